@@ -1,0 +1,808 @@
+// C ABI of libersj (see include/ersj.h): argument validation, the state
+// machine build -> count -> plan -> fill, device memory ownership, and the
+// host-side choices (grid dimensions and widths, fp32 classification band).
+#include "ersj.h"
+#include "ersj_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+using namespace ersj;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+enum State { kNone = 0, kBuilt = 1, kCounted = 2, kPlanned = 3 };
+
+class DeviceGuard {
+public:
+    explicit DeviceGuard(int dev) : ok_(false)
+    {
+        if (hipGetDevice(&prev_) == hipSuccess) ok_ = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard()
+    {
+        if (ok_) (void)hipSetDevice(prev_);
+    }
+    bool ok() const { return ok_; }
+
+private:
+    int prev_ = 0;
+    bool ok_;
+};
+
+}  // namespace
+
+struct ersj_index {
+    int device = 0;
+    int state = kNone;
+    ersj_options opt{};
+    int64_t n = 0;
+    int32_t d = 0, nb = 0;
+    double eps = 0.0, e64 = 0.0;
+    float tlo = 0.0f, thi = 0.0f;
+    GridParams gp{};
+    std::vector<int32_t> perm, pinv;
+
+    std::map<void *, size_t> live;
+    uint64_t bytes = 0;
+
+    // index
+    float4 *xs = nullptr;
+    uint32_t *orig = nullptr;
+    int32_t *d_pinv = nullptr;
+    int64_t M = 0;
+    uint32_t *cell_start = nullptr;
+    uint64_t *cell_key = nullptr;
+    uint32_t *lo_bits = nullptr, *hi_bits = nullptr;
+    // count pass
+    uint32_t *rstart = nullptr, *rpref = nullptr, *nrng = nullptr;
+    uint32_t umax = 0;
+    int64_t T = 0;
+    Tile *tiles = nullptr;
+    uint64_t *toff = nullptr, *coff = nullptr;
+    uint64_t total_cand = 0, total_words = 0;
+    // plan
+    int32_t nbatch = 0;
+    std::vector<uint32_t> hb;
+    std::vector<uint64_t> hrows, hwords, hcands;
+    uint64_t maxw = 0, maxrows = 0;
+    uint32_t *order = nullptr;
+    // fill
+    uint64_t *mask = nullptr;
+    uint64_t mask_cap = 0;
+    Boundary *blist = nullptr;
+    uint64_t bcap = 0;
+    unsigned long long *counters = nullptr;  // [0] boundary count, [1] re-check in
+    uint32_t *rowcnt = nullptr;
+    uint64_t *roff = nullptr, *rscan = nullptr;
+    uint64_t rows_cap = 0;
+    int32_t ready_batch = -1;
+    uint64_t ready_pairs = 0;
+    // stats
+    uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0;
+    double ms_build = 0, ms_count = 0, ms_plan = 0, ms_refine = 0, ms_recheck = 0, ms_expand = 0;
+    int64_t refine_launches = 0;
+    uint64_t refined_cand = 0;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    int32_t kernel_used = ERSJ_REFINE_DIRECT;
+};
+
+namespace {
+
+int hip_fail(hipError_t e, const char *what)
+{
+    (void)hipGetLastError();
+    if (e == hipErrorOutOfMemory) return fail(ERSJ_ERR_OOM, "%s: %s", what, hipGetErrorString(e));
+    return fail(ERSJ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPC(expr, what)                                  \
+    do {                                                  \
+        hipError_t e__ = (expr);                          \
+        if (e__ != hipSuccess) return hip_fail(e__, what); \
+    } while (0)
+
+#define TRY(expr)                  \
+    do {                           \
+        int r__ = (expr);          \
+        if (r__ != ERSJ_OK) return r__; \
+    } while (0)
+
+template <typename T>
+int dalloc(ersj_index *h, T **p, size_t count, const char *what)
+{
+    size_t bytes = count * sizeof(T);
+    if (bytes == 0) bytes = 8;
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (h->opt.max_device_bytes && h->bytes + bytes > h->opt.max_device_bytes)
+        return fail(ERSJ_ERR_OOM, "%s: %zu bytes would exceed max_device_bytes (%llu in use, cap %llu)",
+                    what, bytes, (unsigned long long)h->bytes,
+                    (unsigned long long)h->opt.max_device_bytes);
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ERSJ_ERR_OOM, "%s: hipMalloc(%zu) failed: %s", what, bytes, hipGetErrorString(e));
+    }
+    h->live[q] = bytes;
+    h->bytes += bytes;
+    *p = (T *)q;
+    return ERSJ_OK;
+}
+
+template <typename T>
+void dfree(ersj_index *h, T *&p)
+{
+    if (!p) return;
+    auto it = h->live.find((void *)p);
+    if (it != h->live.end()) {
+        h->bytes -= it->second;
+        h->live.erase(it);
+    }
+    (void)hipFree((void *)p);
+    p = nullptr;
+}
+
+// Temporaries of one call, released on every exit path.
+struct Scratch {
+    ersj_index *h;
+    std::vector<void **> ptrs;
+    explicit Scratch(ersj_index *hh) : h(hh) {}
+    template <typename T>
+    int get(T **p, size_t count, const char *what)
+    {
+        *p = nullptr;
+        int r = dalloc(h, p, count, what);
+        if (r == ERSJ_OK) ptrs.push_back((void **)p);
+        return r;
+    }
+    ~Scratch()
+    {
+        for (void **p : ptrs) dfree(h, *p);
+    }
+};
+
+double gamma_n(double n, double u) { return n * u / (1.0 - n * u); }
+
+float round_down_f32(double v)
+{
+    if (v >= (double)FLT_MAX) return FLT_MAX;
+    float f = (float)v;
+    if ((double)f > v) f = std::nextafter(f, -INFINITY);
+    return f;
+}
+
+float round_up_f32(double v)
+{
+    if (v > (double)FLT_MAX) return INFINITY;
+    float f = (float)v;
+    if ((double)f < v) f = std::nextafter(f, INFINITY);
+    return f;
+}
+
+// fp32 thresholds.  For an fp32 squared distance s computed in any order
+// (d_pad terms, each a rounded difference squared and accumulated with one
+// rounding per step) |s - S| <= g32 * S, and the binary64 reference obeys
+// |D64 - S| <= g64 * S, where S is the exact squared distance.  Hence
+// s <= E(1 - 2(g32 + g64)) implies D64 <= E and s > E(1 + 2(g32 + g64))
+// implies D64 > E (the factor 2 leaves room for the rounding of the
+// thresholds themselves).  Below 2^-90 fp32 underflow breaks the relative
+// bound on the "in" side, so nothing is accepted without the re-check there.
+void thresholds(ersj_index *h)
+{
+    const double E = h->e64;
+    if (std::isinf(E)) {
+        h->tlo = INFINITY;
+        h->thi = INFINITY;
+        return;
+    }
+    const int dpad = h->nb * 4;
+    const double g32 = gamma_n(dpad + 2, std::ldexp(1.0, -24));
+    const double g64 = gamma_n(h->d + 2, std::ldexp(1.0, -53));
+    const double delta = 2.0 * (g32 + g64);
+    h->thi = std::max(round_up_f32(E * (1.0 + delta)), (float)std::ldexp(1.0, -80));
+    if (E < std::ldexp(1.0, -90)) h->tlo = -1.0f;
+    else h->tlo = round_down_f32(E * (1.0 - delta));
+}
+
+int sync(hipStream_t s, const char *what)
+{
+    HIPC(hipStreamSynchronize(s), what);
+    return ERSJ_OK;
+}
+
+void timer_start(ersj_index *h, hipStream_t s)
+{
+    if (h->opt.timing) (void)hipEventRecord(h->ev[0], s);
+}
+
+double timer_stop(ersj_index *h, hipStream_t s)
+{
+    if (!h->opt.timing) return 0.0;
+    float ms = 0.0f;
+    (void)hipEventRecord(h->ev[1], s);
+    (void)hipEventSynchronize(h->ev[1]);
+    (void)hipEventElapsedTime(&ms, h->ev[0], h->ev[1]);
+    return ms;
+}
+
+int ceil_log2(uint64_t v)
+{
+    int b = 0;
+    while ((1ull << b) < v) ++b;
+    return b;
+}
+
+void release_count(ersj_index *h)
+{
+    dfree(h, h->rstart);
+    dfree(h, h->rpref);
+    dfree(h, h->nrng);
+    dfree(h, h->tiles);
+    dfree(h, h->toff);
+    dfree(h, h->coff);
+}
+
+void release_plan(ersj_index *h)
+{
+    dfree(h, h->order);
+    h->hb.clear();
+    h->hrows.clear();
+    h->hwords.clear();
+    h->hcands.clear();
+    h->nbatch = 0;
+    h->ready_batch = -1;
+}
+
+int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
+{
+    const int64_t n = h->n;
+    const int32_t d = h->d;
+    Scratch tmp(h);
+    // A1: per-dimension statistics and the non-finite check.
+    const int64_t T = stats_threads(n, d);
+    double *part = nullptr, *st = nullptr;
+    uint32_t *badp = nullptr;
+    unsigned long long *bad = nullptr;
+    TRY(tmp.get(&part, (size_t)T * 4, "stats"));
+    TRY(tmp.get(&badp, (size_t)T, "stats"));
+    TRY(tmp.get(&st, (size_t)d * 4, "stats"));
+    TRY(tmp.get(&bad, 1, "stats"));
+    HIPC(launch_stats(x, n, d, ld, part, badp, T, st, bad, s), "stats kernels");
+    std::vector<double> hst((size_t)d * 4);
+    unsigned long long hbad = 0;
+    HIPC(hipMemcpyAsync(hst.data(), st, sizeof(double) * d * 4, hipMemcpyDeviceToHost, s), "stats copy");
+    HIPC(hipMemcpyAsync(&hbad, bad, sizeof hbad, hipMemcpyDeviceToHost, s), "stats copy");
+    TRY(sync(s, "stats"));
+    if (hbad) return fail(ERSJ_ERR_INVALID_ARG, "input holds %llu non-finite coordinates", hbad);
+
+    // A2: dimensions by descending variance (ties: lower id first); the first
+    // three are the grid axes.  Cell width >= eps*(1 + 2^-20), widened so no
+    // axis has more than 2^21 cells.
+    h->perm.resize(d);
+    for (int k = 0; k < d; ++k) h->perm[k] = k;
+    std::stable_sort(h->perm.begin(), h->perm.end(),
+                     [&](int a, int b) { return hst[a * 4 + 1] > hst[b * 4 + 1]; });
+    h->pinv.assign(d, 0);
+    for (int j = 0; j < d; ++j) h->pinv[h->perm[j]] = j;
+    GridParams gp{};
+    gp.ndim = std::min(3, d);
+    const double scale = h->opt.cell_width_scale > 1.0 ? h->opt.cell_width_scale : 1.0;
+    int bits = 0;
+    for (int a = 0; a < 3; ++a) {
+        gp.dim[a] = a < gp.ndim ? h->perm[a] : 0;
+        gp.lo[a] = 0.0;
+        gp.w[a] = 1.0;
+        gp.G[a] = 1;
+        if (a >= gp.ndim) continue;
+        const double mn = hst[gp.dim[a] * 4 + 2], mx = hst[gp.dim[a] * 4 + 3];
+        const double range = mx - mn;
+        gp.lo[a] = mn;
+        double w = h->eps * scale * (1.0 + std::ldexp(1.0, -20));
+        w = std::max(w, range / (std::ldexp(1.0, 21) - 1.0));
+        if (!(w > 0.0)) w = 1.0;
+        gp.w[a] = w;
+        double g = std::isinf(w) ? 1.0 : std::floor(range / w) + 1.0;
+        g = std::min(g, std::ldexp(1.0, 21));
+        gp.G[a] = (int32_t)g;
+        bits = std::max(bits, ceil_log2((uint64_t)gp.G[a]));
+    }
+    gp.bits = bits;
+    h->gp = gp;
+
+    // A4-A5: Morton keys of the cells, stable radix sort of (key, row id).
+    uint64_t *k0 = nullptr, *k1 = nullptr, *hist = nullptr, *stmp = nullptr;
+    uint32_t *v1 = nullptr;
+    TRY(tmp.get(&k0, (size_t)n, "keys"));
+    TRY(tmp.get(&k1, (size_t)n, "keys"));
+    TRY(tmp.get(&v1, (size_t)n, "keys"));
+    const size_t hent = radix_hist_entries(n);
+    TRY(tmp.get(&hist, hent, "sort"));
+    TRY(tmp.get(&stmp, std::max(scan_tmp_entries(hent), scan_tmp_entries(n + 1)), "scan"));
+    TRY(dalloc(h, &h->orig, (size_t)n, "orig"));
+    HIPC(launch_keys(x, n, ld, gp, k0, h->orig, s), "keys kernel");
+    HIPC(radix_sort(k0, h->orig, k1, v1, n, 3 * bits, hist, stmp, s), "radix sort");
+
+    // A6: gather into the dimension-blocked, variance-ordered layout.
+    int32_t *dperm = nullptr;
+    TRY(tmp.get(&dperm, (size_t)d, "perm"));
+    HIPC(hipMemcpyAsync(dperm, h->perm.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "perm copy");
+    TRY(dalloc(h, &h->xs, (size_t)h->nb * n, "points"));
+    HIPC(launch_gather(x, n, d, ld, h->orig, dperm, h->xs, s), "gather kernel");
+    TRY(dalloc(h, &h->d_pinv, (size_t)d, "pinv"));
+    HIPC(hipMemcpyAsync(h->d_pinv, h->pinv.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "pinv copy");
+
+    // A7: cells = runs of equal keys; their boxes on the grid axes.
+    uint32_t *flags = nullptr;
+    uint64_t *cid = nullptr;
+    TRY(tmp.get(&flags, (size_t)n, "cells"));
+    TRY(tmp.get(&cid, (size_t)n + 1, "cells"));
+    HIPC(launch_cell_flags(k0, n, flags, s), "cell flags");
+    HIPC(scan_u32(flags, cid, n, stmp, s), "cell scan");
+    uint64_t M = 0;
+    HIPC(hipMemcpyAsync(&M, cid + n, sizeof M, hipMemcpyDeviceToHost, s), "cell count copy");
+    TRY(sync(s, "cells"));
+    h->M = (int64_t)M;
+    TRY(dalloc(h, &h->cell_start, (size_t)M + 1, "cells"));
+    TRY(dalloc(h, &h->cell_key, (size_t)M, "cells"));
+    TRY(dalloc(h, &h->lo_bits, (size_t)M * 3, "cells"));
+    TRY(dalloc(h, &h->hi_bits, (size_t)M * 3, "cells"));
+    HIPC(launch_cell_scatter(k0, flags, cid, n, h->cell_start, h->cell_key, s), "cell scatter");
+    HIPC(launch_cell_aabb(h->xs, cid, n, (int64_t)M, h->lo_bits, h->hi_bits, s), "cell boxes");
+    TRY(sync(s, "build"));
+    thresholds(h);
+    return ERSJ_OK;
+}
+
+int do_count(ersj_index *h, hipStream_t s)
+{
+    release_count(h);
+    release_plan(h);
+    const int64_t M = h->M;
+    Scratch tmp(h);
+    uint32_t *tpc = nullptr;
+    unsigned int *umax = nullptr;
+    uint64_t *tbase = nullptr, *stmp = nullptr, *words = nullptr, *cands = nullptr;
+    TRY(dalloc(h, &h->rstart, (size_t)M * kMaxRanges, "ranges"));
+    TRY(dalloc(h, &h->rpref, (size_t)M * (kMaxRanges + 1), "ranges"));
+    TRY(dalloc(h, &h->nrng, (size_t)M, "ranges"));
+    TRY(tmp.get(&tpc, (size_t)M, "tiles"));
+    TRY(tmp.get(&umax, 1, "tiles"));
+    TRY(tmp.get(&tbase, (size_t)M + 1, "tiles"));
+    TRY(tmp.get(&stmp, scan_tmp_entries(std::max<int64_t>(M, h->n) + 1), "scan"));
+    // Box pruning: drop neighbour cell B if its box lower distance to A's box
+    // exceeds eps.  Computed in binary64 with relative error below 8u; the
+    // margin keeps every pair with D64 <= E64 (|D64 - S| <= g64*S).
+    const double pf = 1.0 + std::max(std::ldexp(1.0, -40), 16.0 * (h->d + 2) * std::ldexp(1.0, -53));
+    const double prune_e2 = std::isinf(h->e64) ? INFINITY : h->e64 * pf;
+    HIPC(launch_stencil(h->cell_key, h->cell_start, h->lo_bits, h->hi_bits, M, h->gp, prune_e2,
+                        h->rstart, h->rpref, h->nrng, tpc, umax, s), "stencil kernel");
+    HIPC(scan_u32(tpc, tbase, M, stmp, s), "tile scan");
+    uint64_t T = 0;
+    HIPC(hipMemcpyAsync(&T, tbase + M, sizeof T, hipMemcpyDeviceToHost, s), "tile count copy");
+    HIPC(hipMemcpyAsync(&h->umax, umax, sizeof(uint32_t), hipMemcpyDeviceToHost, s), "umax copy");
+    TRY(sync(s, "stencil"));
+    h->T = (int64_t)T;
+    TRY(dalloc(h, &h->tiles, (size_t)T, "tiles"));
+    TRY(dalloc(h, &h->toff, (size_t)T + 1, "tiles"));
+    TRY(dalloc(h, &h->coff, (size_t)T + 1, "tiles"));
+    TRY(tmp.get(&words, (size_t)T, "tiles"));
+    TRY(tmp.get(&cands, (size_t)T, "tiles"));
+    HIPC(launch_tiles(tbase, M, (int64_t)T, h->cell_start, h->rpref, h->nrng, h->tiles, words, cands, s),
+         "tiles kernel");
+    HIPC(scan_u64(words, h->toff, (int64_t)T, stmp, s), "word scan");
+    HIPC(scan_u64(cands, h->coff, (int64_t)T, stmp, s), "candidate scan");
+    HIPC(hipMemcpyAsync(&h->total_words, h->toff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(&h->total_cand, h->coff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
+    TRY(sync(s, "count pass"));
+    return ERSJ_OK;
+}
+
+int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
+{
+    release_plan(h);
+    if (budget_bytes == 0) {
+        size_t fr = 0, tot = 0;
+        HIPC(hipMemGetInfo(&fr, &tot), "hipMemGetInfo");
+        const uint64_t extra = (uint64_t)h->n * 24 + (uint64_t)(1 << 22) * sizeof(Boundary);
+        uint64_t b = (uint64_t)fr / 4 * 3;
+        budget_bytes = b > extra ? b - extra : 8;
+        if (h->opt.max_device_bytes) {
+            const uint64_t room = h->opt.max_device_bytes > h->bytes ? h->opt.max_device_bytes - h->bytes : 0;
+            budget_bytes = std::min<uint64_t>(budget_bytes, room / 4 * 3);
+        }
+    }
+    const uint64_t budget_words = budget_bytes / 8;
+    if (budget_words == 0) return fail(ERSJ_ERR_BUDGET, "budget of %llu bytes holds no mask word",
+                                       (unsigned long long)budget_bytes);
+    Scratch tmp(h);
+    const int64_t T = h->T;
+    uint32_t *bounds = nullptr;
+    uint64_t *rowb = nullptr, *wordb = nullptr, *candb = nullptr, *res = nullptr;
+    TRY(tmp.get(&bounds, (size_t)T + 1, "plan"));
+    TRY(tmp.get(&rowb, (size_t)T + 1, "plan"));
+    TRY(tmp.get(&wordb, (size_t)T + 1, "plan"));
+    TRY(tmp.get(&candb, (size_t)T + 1, "plan"));
+    TRY(tmp.get(&res, 4, "plan"));
+    HIPC(launch_plan(h->toff, h->coff, h->tiles, T, h->n, budget_words, bounds, rowb, wordb, candb, res, s),
+         "plan kernel");
+    uint64_t hres[4];
+    HIPC(hipMemcpyAsync(hres, res, sizeof hres, hipMemcpyDeviceToHost, s), "plan copy");
+    TRY(sync(s, "plan"));
+    if (hres[2]) {
+        const uint64_t t = hres[2] - 1;
+        uint64_t w2[2] = {0, 0};
+        HIPC(hipMemcpy(w2, h->toff + t, sizeof w2, hipMemcpyDeviceToHost), "plan copy");
+        return fail(ERSJ_ERR_BUDGET,
+                    "row tile %llu needs %llu bytes of result mask, more than the budget of %llu bytes",
+                    (unsigned long long)t, (unsigned long long)((w2[1] - w2[0]) * 8),
+                    (unsigned long long)budget_bytes);
+    }
+    const int64_t nbat = (int64_t)hres[0];
+    if (nbat > 0x7fffffff) return fail(ERSJ_ERR_BUDGET, "too many batches (%lld)", (long long)nbat);
+    h->nbatch = (int32_t)nbat;
+    h->maxw = hres[1];
+    h->maxrows = hres[3];
+    h->hb.resize(nbat + 1);
+    h->hrows.resize(nbat + 1);
+    h->hwords.resize(nbat + 1);
+    h->hcands.resize(nbat + 1);
+    HIPC(hipMemcpyAsync(h->hb.data(), bounds, sizeof(uint32_t) * (nbat + 1), hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(h->hrows.data(), rowb, sizeof(uint64_t) * (nbat + 1), hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(h->hwords.data(), wordb, sizeof(uint64_t) * (nbat + 1), hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(h->hcands.data(), candb, sizeof(uint64_t) * (nbat + 1), hipMemcpyDeviceToHost, s), "copy");
+
+    // Launch order of the row tiles: by batch, heaviest cell first.
+    const int ubits = std::max(1, ceil_log2((uint64_t)h->umax + 1));
+    const int bbits = ceil_log2((uint64_t)nbat);
+    uint64_t *k0 = nullptr, *k1 = nullptr, *hist = nullptr, *stmp = nullptr;
+    uint32_t *v1 = nullptr;
+    TRY(dalloc(h, &h->order, (size_t)T, "order"));
+    TRY(tmp.get(&k0, (size_t)T, "order"));
+    TRY(tmp.get(&k1, (size_t)T, "order"));
+    TRY(tmp.get(&v1, (size_t)T, "order"));
+    const size_t hent = radix_hist_entries(T);
+    TRY(tmp.get(&hist, hent, "order"));
+    TRY(tmp.get(&stmp, scan_tmp_entries(hent), "order"));
+    HIPC(launch_order_keys(h->tiles, h->rpref, h->nrng, T, bounds, (int32_t)nbat, ubits, h->umax, k0,
+                           h->order, s), "order keys");
+    HIPC(radix_sort(k0, h->order, k1, v1, T, ubits + bbits, hist, stmp, s), "order sort");
+    TRY(sync(s, "plan"));
+    return ERSJ_OK;
+}
+
+int ensure_fill_buffers(ersj_index *h)
+{
+    if (h->mask_cap < h->maxw) {
+        dfree(h, h->mask);
+        h->mask_cap = 0;
+        TRY(dalloc(h, &h->mask, (size_t)h->maxw, "result mask"));
+        h->mask_cap = h->maxw;
+    }
+    if (h->rows_cap < h->maxrows) {
+        dfree(h, h->rowcnt);
+        dfree(h, h->roff);
+        dfree(h, h->rscan);
+        h->rows_cap = 0;
+        TRY(dalloc(h, &h->rowcnt, (size_t)h->maxrows, "row counts"));
+        TRY(dalloc(h, &h->roff, (size_t)h->maxrows + 1, "row offsets"));
+        TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
+        h->rows_cap = h->maxrows;
+    }
+    if (!h->counters) TRY(dalloc(h, &h->counters, 2, "counters"));
+    if (!h->blist) {
+        uint64_t cap = h->opt.boundary_capacity ? h->opt.boundary_capacity : (1ull << 20);
+        TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
+        h->bcap = cap;
+    }
+    return ERSJ_OK;
+}
+
+int do_refine(ersj_index *h, int32_t b, hipStream_t s)
+{
+    TRY(ensure_fill_buffers(h));
+    const uint32_t t0 = h->hb[b], t1 = h->hb[b + 1];
+    const uint32_t ntiles = t1 - t0;
+    const uint64_t rows = h->hrows[b + 1] - h->hrows[b];
+    RefineArgs a{};
+    a.xs = h->xs;
+    a.n = (uint64_t)h->n;
+    a.nb = h->nb;
+    a.tiles = h->tiles;
+    a.order = h->order;
+    a.ord0 = t0;
+    a.ntiles = ntiles;
+    uint32_t seg = 8192;
+    auto nseg_of = [&](uint32_t sl) { return (h->umax + sl - 1) / sl; };
+    while (seg > 256 && (uint64_t)ntiles * nseg_of(seg) < 8192) seg /= 2;
+    while ((uint64_t)ntiles * nseg_of(seg) > 0x7fffffffull) seg *= 2;
+    a.seg_len = seg;
+    a.nseg = std::max<uint32_t>(1, nseg_of(seg));
+    a.rstart = h->rstart;
+    a.rpref = h->rpref;
+    a.nrng = h->nrng;
+    a.toff = h->toff;
+    a.wbase = h->hwords[b];
+    a.mask = h->mask;
+    a.tlo = h->tlo;
+    a.thi = h->thi;
+    uint64_t bcount = 0;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        a.blist = h->blist;
+        a.bcount = h->counters;
+        a.bcap = h->bcap;
+        HIPC(launch_fill_u64((uint64_t *)h->counters, 0, 2, s), "clear counters");
+        timer_start(h, s);
+        HIPC(launch_refine_direct(a, s), "refine kernel");
+        h->ms_refine += timer_stop(h, s);
+        if (h->opt.timing) {
+            h->refine_launches += 1;
+            h->refined_cand += h->hcands[b + 1] - h->hcands[b];
+        }
+        HIPC(hipMemcpyAsync(&bcount, h->counters, sizeof bcount, hipMemcpyDeviceToHost, s), "copy");
+        TRY(sync(s, "refine"));
+        if (bcount <= h->bcap) break;
+        // The boundary list overflowed: grow it and refine the batch again
+        // (every mask word is rewritten, so the first result is discarded).
+        dfree(h, h->blist);
+        h->bcap = 0;
+        const uint64_t cap = bcount + bcount / 4 + 1024;
+        TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
+        h->bcap = cap;
+    }
+    if (bcount > h->bcap) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
+    timer_start(h, s);
+    HIPC(launch_recheck(h->blist, bcount, h->xs, (uint64_t)h->n, h->d, h->d_pinv, h->e64, h->mask,
+                        h->counters + 1, s), "re-check kernel");
+    h->ms_recheck += timer_stop(h, s);
+    timer_start(h, s);
+    HIPC(launch_rowcount(h->tiles, t0, ntiles, h->toff, a.wbase, h->hrows[b], h->mask, h->rowcnt, s),
+         "row count kernel");
+    HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
+    uint64_t tot = 0, nin = 0;
+    HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(&nin, h->counters + 1, sizeof nin, hipMemcpyDeviceToHost, s), "copy");
+    TRY(sync(s, "row count"));
+    h->ms_expand += timer_stop(h, s);
+    h->last_cand = h->hcands[b + 1] - h->hcands[b];
+    h->last_bnd = bcount;
+    h->last_in = nin;
+    h->ready_batch = b;
+    h->ready_pairs = tot;
+    h->last_pairs = tot;
+    return ERSJ_OK;
+}
+
+}  // namespace
+
+// =================================================================== ABI ==
+extern "C" {
+
+void ersj_default_options(ersj_options *opt)
+{
+    if (!opt) return;
+    std::memset(opt, 0, sizeof *opt);
+    opt->struct_size = sizeof *opt;
+    opt->refine_kernel = ERSJ_REFINE_AUTO;
+    opt->cell_width_scale = 1.0;
+}
+
+const char *ersj_last_error(void) { return g_err.c_str(); }
+
+void ersj_free(ersj_index *h)
+{
+    if (!h) return;
+    DeviceGuard g(h->device);
+    for (auto &kv : h->live) (void)hipFree(kv.first);
+    h->live.clear();
+    for (hipEvent_t &e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    delete h;
+}
+
+int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double eps,
+                     const ersj_options *opt, void *stream, ersj_index **out)
+{
+    g_err.clear();
+    if (!out) return fail(ERSJ_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!d_x) return fail(ERSJ_ERR_INVALID_ARG, "d_x is NULL");
+    if (n < 1 || n > 0xffffffffll) return fail(ERSJ_ERR_INVALID_ARG, "n = %lld outside [1, 2^32-1]", (long long)n);
+    if (d < 1 || d > kMaxDim) return fail(ERSJ_ERR_INVALID_ARG, "d = %d outside [1, %d]", d, kMaxDim);
+    if (ld < d) return fail(ERSJ_ERR_INVALID_ARG, "ld = %lld < d = %d", (long long)ld, d);
+    if (ld > (int64_t)1 << 40) return fail(ERSJ_ERR_INVALID_ARG, "ld = %lld too large", (long long)ld);
+    if (std::isnan(eps) || eps < 0.0) return fail(ERSJ_ERR_INVALID_ARG, "eps must be >= 0 (got %g)", eps);
+    ersj_options o;
+    ersj_default_options(&o);
+    if (opt) {
+        if (opt->struct_size < offsetof(ersj_options, timing) || opt->struct_size > sizeof o)
+            return fail(ERSJ_ERR_INVALID_ARG, "options.struct_size = %u not supported", opt->struct_size);
+        std::memcpy(&o, opt, opt->struct_size);
+        o.struct_size = sizeof o;
+        if (!(o.cell_width_scale >= 0.0) || std::isinf(o.cell_width_scale))
+            return fail(ERSJ_ERR_INVALID_ARG, "cell_width_scale must be finite and >= 0");
+        if (o.refine_kernel < ERSJ_REFINE_AUTO || o.refine_kernel > ERSJ_REFINE_MFMA)
+            return fail(ERSJ_ERR_INVALID_ARG, "unknown refine_kernel %d", o.refine_kernel);
+    }
+    if (o.refine_kernel == ERSJ_REFINE_MFMA)
+        return fail(ERSJ_ERR_INVALID_ARG, "the MFMA refinement kernel is not available in this build");
+    int dev = 0;
+    HIPC(hipGetDevice(&dev), "hipGetDevice");
+    ersj_index *h = new ersj_index();
+    h->device = dev;
+    h->opt = o;
+    h->n = n;
+    h->d = d;
+    h->nb = (d + 3) / 4;
+    h->eps = eps;
+    h->e64 = eps * eps;
+    h->kernel_used = ERSJ_REFINE_DIRECT;
+    hipStream_t s = (hipStream_t)stream;
+    int rc = ERSJ_OK;
+    if (o.timing) {
+        hipError_t e = hipEventCreate(&h->ev[0]);
+        if (e == hipSuccess) e = hipEventCreate(&h->ev[1]);
+        if (e != hipSuccess) rc = hip_fail(e, "hipEventCreate");
+    }
+    if (rc == ERSJ_OK) {
+        timer_start(h, s);
+        rc = do_build(h, d_x, ld, s);
+        h->ms_build += timer_stop(h, s);
+    }
+    if (rc != ERSJ_OK) {
+        std::string keep = g_err;
+        (void)hipStreamSynchronize(s);
+        ersj_free(h);
+        g_err = keep;
+        return rc;
+    }
+    h->state = kBuilt;
+    *out = h;
+    return ERSJ_OK;
+}
+
+int ersj_count_pass(ersj_index *h, uint64_t *total_candidates, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (h->state < kBuilt) return fail(ERSJ_ERR_STATE, "index not built");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    timer_start(h, s);
+    int rc = do_count(h, s);
+    h->ms_count += timer_stop(h, s);
+    if (rc != ERSJ_OK) {
+        h->state = kBuilt;
+        return rc;
+    }
+    h->state = kCounted;
+    if (total_candidates) *total_candidates = h->total_cand;
+    return ERSJ_OK;
+}
+
+int ersj_plan_batches(ersj_index *h, uint64_t budget_bytes, int32_t *n_batches, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!n_batches) return fail(ERSJ_ERR_INVALID_ARG, "n_batches is NULL");
+    if (h->state < kCounted) return fail(ERSJ_ERR_STATE, "count_pass has not run");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    timer_start(h, s);
+    int rc = do_plan(h, budget_bytes, s);
+    h->ms_plan += timer_stop(h, s);
+    if (rc != ERSJ_OK) {
+        release_plan(h);
+        h->state = kCounted;
+        return rc;
+    }
+    h->state = kPlanned;
+    *n_batches = h->nbatch;
+    return ERSJ_OK;
+}
+
+int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t capacity,
+                   uint64_t *n_pairs, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!n_pairs) return fail(ERSJ_ERR_INVALID_ARG, "n_pairs is NULL");
+    if (capacity > 0 && !d_pairs) return fail(ERSJ_ERR_INVALID_ARG, "d_pairs is NULL");
+    if (h->state < kPlanned) return fail(ERSJ_ERR_STATE, "plan_batches has not run");
+    if (batch < 0 || batch >= h->nbatch)
+        return fail(ERSJ_ERR_INVALID_ARG, "batch %d outside [0, %d)", batch, h->nbatch);
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    if (h->ready_batch != batch) {
+        h->ready_batch = -1;
+        int rc = do_refine(h, batch, s);
+        if (rc != ERSJ_OK) return rc;
+    }
+    *n_pairs = h->ready_pairs;
+    if (capacity < h->ready_pairs)
+        return fail(ERSJ_ERR_CAPACITY, "batch %d has %llu pairs, capacity is %llu", batch,
+                    (unsigned long long)h->ready_pairs, (unsigned long long)capacity);
+    if (h->ready_pairs == 0) return ERSJ_OK;
+    const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
+    timer_start(h, s);
+    HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
+                       h->roff, h->rstart, h->rpref, h->nrng, h->orig, d_pairs, s), "expand kernel");
+    h->ms_expand += timer_stop(h, s);
+    return ERSJ_OK;
+}
+
+int ersj_batch_info(const ersj_index *h, int32_t batch, uint64_t *first_row, uint64_t *n_rows,
+                    uint64_t *mask_words)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (h->state < kPlanned) return fail(ERSJ_ERR_STATE, "plan_batches has not run");
+    if (batch < 0 || batch >= h->nbatch)
+        return fail(ERSJ_ERR_INVALID_ARG, "batch %d outside [0, %d)", batch, h->nbatch);
+    if (first_row) *first_row = h->hrows[batch];
+    if (n_rows) *n_rows = h->hrows[batch + 1] - h->hrows[batch];
+    if (mask_words) *mask_words = h->hwords[batch + 1] - h->hwords[batch];
+    return ERSJ_OK;
+}
+
+int ersj_get_stats(const ersj_index *h, ersj_stats *o)
+{
+    g_err.clear();
+    if (!h || !o) return fail(ERSJ_ERR_INVALID_ARG, "NULL argument");
+    std::memset(o, 0, sizeof *o);
+    o->n = h->n;
+    o->d = h->d;
+    for (int a = 0; a < 3; ++a) {
+        o->index_dims[a] = a < h->gp.ndim ? h->gp.dim[a] : -1;
+        o->grid[a] = h->gp.G[a];
+    }
+    o->refine_kernel = h->kernel_used;
+    o->cells = h->M;
+    o->tiles = h->T;
+    o->total_candidates = h->total_cand;
+    o->total_mask_words = h->total_words;
+    o->n_batches = h->nbatch;
+    o->last_batch = h->ready_batch;
+    o->max_batch_words = h->maxw;
+    o->last_batch_candidates = h->last_cand;
+    o->last_batch_pairs = h->last_pairs;
+    o->last_boundary_pairs = h->last_bnd;
+    o->last_recheck_in = h->last_in;
+    o->device_bytes = h->bytes;
+    o->build_ms = h->ms_build;
+    o->count_ms = h->ms_count;
+    o->plan_ms = h->ms_plan;
+    o->refine_ms = h->ms_refine;
+    o->recheck_ms = h->ms_recheck;
+    o->expand_ms = h->ms_expand;
+    o->refine_launches = h->refine_launches;
+    o->refined_candidates = h->refined_cand;
+    return ERSJ_OK;
+}
+
+}  // extern "C"

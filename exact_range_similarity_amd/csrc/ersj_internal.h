@@ -1,0 +1,142 @@
+// Internal declarations of libersj: device data layout and kernel launchers.
+//
+// Device layout of an index (n points, d dims, nb = ceil(d/4) dim blocks):
+//   xs      float4 [nb][n]   point i's permuted dims 4b..4b+3 at xs[b*n + i]
+//                            (dims in descending-variance order, zero padded)
+//   orig    u32 [n]          sorted position -> original row id
+//   cell_*  per non-empty grid cell, in Morton order of the cell coordinates
+//   rstart/rpref             per cell, the candidate ranges of its kept
+//                            neighbour cells (merged when contiguous) and the
+//                            prefix of their lengths: candidate position p of
+//                            the cell maps to point rstart[g] + p - rpref[g]
+//   tiles   Tile [T]         row tiles: up to kTileRows rows of one cell
+//   toff    u64 [T+1]        first mask word of each tile (all batches)
+//   coff    u64 [T+1]        candidates before each tile (sum of rows * U)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ersj {
+
+constexpr int kTileRows = 32;   // query rows per row tile
+constexpr int kMaxRanges = 27;  // 3x3x3 stencil
+constexpr int kMaxDim = 4096;
+
+struct Tile {
+    uint32_t cell;
+    uint32_t row0;
+    uint32_t nrows;
+    uint32_t words;  // 64-bit mask words per row = ceil(U / 64)
+};
+
+// A pair inside the fp32 uncertainty band, re-evaluated in binary64.
+struct Boundary {
+    uint32_t q;      // sorted row of the query
+    uint32_t x;      // sorted row of the candidate
+    uint64_t bit;    // bit address in the batch mask (word * 64 + bit)
+};
+
+struct GridParams {
+    int32_t dim[3];   // original dimension ids of the grid axes
+    double lo[3];
+    double w[3];
+    int32_t G[3];
+    int32_t ndim;     // grid dimensions in use (min(d, 3))
+    int32_t bits;     // Morton bits per dimension
+};
+
+// ---- index construction (k_index.hip) ----
+hipError_t launch_stats(const float *x, int64_t n, int32_t d, int64_t ld, double *partial,
+                        uint32_t *bad_partial, int64_t nthreads, double *out_stats,
+                        unsigned long long *out_bad, hipStream_t s);
+int64_t stats_threads(int64_t n, int32_t d);
+
+hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp,
+                       uint64_t *keys, uint32_t *ids, hipStream_t s);
+
+// LSD radix sort of (key, value) pairs on the low `bits` bits of the keys.
+// Result ends in (k0, v0); k1/v1 are scratch of the same size; hist needs
+// radix_hist_entries(n) u64 and scan_tmp scan_tmp_entries(radix_hist_entries(n)).
+size_t radix_hist_entries(int64_t n);
+hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, int64_t n, int bits,
+                      uint64_t *hist, uint64_t *scan_tmp, hipStream_t s);
+
+hipError_t launch_gather(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
+                         const int32_t *perm, float4 *xs, hipStream_t s);
+
+// Exclusive scan: out[i] = sum in[0..i), out[n] = total.  tmp needs
+// scan_tmp_entries(n) u64.
+size_t scan_tmp_entries(int64_t n);
+hipError_t scan_u32(const uint32_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s);
+hipError_t scan_u64(const uint64_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s);
+
+hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, uint32_t *flags, hipStream_t s);
+hipError_t launch_cell_scatter(const uint64_t *keys, const uint32_t *flags, const uint64_t *cid,
+                               int64_t n, uint32_t *cell_start, uint64_t *cell_key,
+                               hipStream_t s);
+hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, int64_t M,
+                            uint32_t *lo_bits, uint32_t *hi_bits, hipStream_t s);
+
+hipError_t launch_stencil(const uint64_t *cell_key, const uint32_t *cell_start,
+                          const uint32_t *lo_bits, const uint32_t *hi_bits, int64_t M,
+                          const GridParams &gp, double prune_e2, uint32_t *rstart,
+                          uint32_t *rpref, uint32_t *nrng, uint32_t *tiles_per_cell,
+                          unsigned int *umax, hipStream_t s);
+
+hipError_t launch_tiles(const uint64_t *tile_base, int64_t M, int64_t T,
+                        const uint32_t *cell_start, const uint32_t *rpref, const uint32_t *nrng,
+                        Tile *tiles, uint64_t *words, uint64_t *cands, hipStream_t s);
+
+// result = {batches, max batch words, failing tile + 1 (0 = ok), max batch rows}
+hipError_t launch_plan(const uint64_t *toff, const uint64_t *coff, const Tile *tiles, int64_t T,
+                       int64_t n, uint64_t budget_words, uint32_t *bounds, uint64_t *row_bounds,
+                       uint64_t *word_bounds, uint64_t *cand_bounds, uint64_t *result,
+                       hipStream_t s);
+
+hipError_t launch_order_keys(const Tile *tiles, const uint32_t *rpref, const uint32_t *nrng,
+                             int64_t T, const uint32_t *bounds, int32_t nb, int ubits,
+                             uint32_t umax, uint64_t *keys, uint32_t *vals, hipStream_t s);
+
+hipError_t launch_fill_u64(uint64_t *p, uint64_t v, int64_t n, hipStream_t s);
+
+// ---- refinement (k_refine.hip) ----
+struct RefineArgs {
+    const float4 *xs;
+    uint64_t n;
+    int32_t nb;
+    const Tile *tiles;
+    const uint32_t *order;
+    uint32_t ord0;       // first entry of `order` for this batch
+    uint32_t ntiles;     // tiles in this batch
+    uint32_t nseg;       // candidate segments per tile
+    uint32_t seg_len;    // candidates per segment (multiple of 256)
+    const uint32_t *rstart;
+    const uint32_t *rpref;
+    const uint32_t *nrng;
+    const uint64_t *toff;
+    uint64_t wbase;      // first mask word of the batch
+    uint64_t *mask;
+    float tlo, thi;      // fp32 classification thresholds
+    Boundary *blist;
+    unsigned long long *bcount;
+    uint64_t bcap;
+};
+hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
+
+// ---- re-check and compaction (k_expand.hip) ----
+hipError_t launch_recheck(const Boundary *bl, uint64_t cnt, const float4 *xs, uint64_t n,
+                          int32_t d, const int32_t *pinv, double e64, uint64_t *mask,
+                          unsigned long long *nin, hipStream_t s);
+
+hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
+                           uint64_t wbase, uint64_t row_base, const uint64_t *mask,
+                           uint32_t *cnt, hipStream_t s);
+
+hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
+                         uint64_t wbase, uint64_t row_base, const uint64_t *mask,
+                         const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
+                         const uint32_t *nrng, const uint32_t *orig, uint32_t *pairs,
+                         hipStream_t s);
+
+}  // namespace ersj

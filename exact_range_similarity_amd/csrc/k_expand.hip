@@ -1,0 +1,153 @@
+// Boundary re-check and result compaction for gfx950.
+//
+// Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+// Similarity Searches", Sec. IV-F and IV-F1 (Fig. 5): the result mask holds
+// one bit per query/candidate comparison; compaction keeps only the
+// positions of its ones, and each position is turned back into the
+// (query id, point id) pair of Sec. II-A1.
+#include "ersj_internal.h"
+
+namespace ersj {
+
+namespace {
+
+// Binary64 squared distance in the input's own dimension order, every
+// operation separately rounded (no contraction): the exact definition the
+// result set is specified by.  Pairs at or below fl(eps*eps) get their bit.
+__global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t cnt,
+                                                 const float *__restrict__ xsf, uint64_t n,
+                                                 int32_t d, const int32_t *__restrict__ pinv,
+                                                 double e64, uint64_t *__restrict__ mask,
+                                                 unsigned long long *__restrict__ nin)
+{
+#pragma clang fp contract(off)
+    __shared__ int32_t sp[kMaxDim];
+    for (int k = threadIdx.x; k < d; k += blockDim.x) sp[k] = pinv[k];
+    __syncthreads();
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= cnt) return;
+    const Boundary e = bl[i];
+    double s = 0.0;
+    for (int k = 0; k < d; ++k) {
+        const int p = sp[k];
+        const uint64_t off = ((uint64_t)(p >> 2) * n) * 4 + (p & 3);
+        const double a = (double)xsf[off + (uint64_t)e.q * 4];
+        const double b = (double)xsf[off + (uint64_t)e.x * 4];
+        const double t = a - b;
+        const double tt = t * t;
+        s = s + tt;
+    }
+    if (s <= e64) {
+        atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
+        atomicAdd(nin, 1ull);
+    }
+}
+
+// Workgroup per row tile of the batch (index order), wave per row.
+__global__ __launch_bounds__(256) void k_rowcount(const Tile *__restrict__ tiles, uint32_t t0,
+                                                  const uint64_t *__restrict__ toff, uint64_t wbase,
+                                                  uint64_t row_base, const uint64_t *__restrict__ mask,
+                                                  uint32_t *__restrict__ cnt)
+{
+    const uint32_t t = t0 + blockIdx.x;
+    const Tile tl = tiles[t];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t tbase = toff[t] - wbase;
+    for (uint32_t r = wave; r < tl.nrows; r += 4) {
+        const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
+        uint32_t c = 0;
+        for (uint32_t w = lane; w < tl.words; w += 64) c += __popcll(row[w]);
+        for (int o = 32; o > 0; o >>= 1) c += __shfl_down(c, o, 64);
+        if (lane == 0) cnt[tl.row0 + r - row_base] = c;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, uint32_t t0,
+                                                const uint64_t *__restrict__ toff, uint64_t wbase,
+                                                uint64_t row_base, const uint64_t *__restrict__ mask,
+                                                const uint64_t *__restrict__ roff,
+                                                const uint32_t *__restrict__ rstart,
+                                                const uint32_t *__restrict__ rpref,
+                                                const uint32_t *__restrict__ nrng,
+                                                const uint32_t *__restrict__ orig,
+                                                uint32_t *__restrict__ pairs)
+{
+    __shared__ uint32_t s_pref[kMaxRanges + 1];
+    __shared__ uint32_t s_start[kMaxRanges];
+    const uint32_t t = t0 + blockIdx.x;
+    const Tile tl = tiles[t];
+    const uint32_t A = tl.cell;
+    const uint32_t nr = nrng[A];
+    if (threadIdx.x <= kMaxRanges)
+        s_pref[threadIdx.x] = threadIdx.x <= nr ? rpref[(uint64_t)A * (kMaxRanges + 1) + threadIdx.x] : 0xffffffffu;
+    if (threadIdx.x < kMaxRanges) s_start[threadIdx.x] = rstart[(uint64_t)A * kMaxRanges + threadIdx.x];
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t tbase = toff[t] - wbase;
+    for (uint32_t r = wave; r < tl.nrows; r += 4) {
+        const uint32_t q = tl.row0 + r;
+        const uint32_t qid = orig[q];
+        const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
+        uint64_t out = roff[q - row_base];
+        for (uint32_t w0 = 0; w0 < tl.words; w0 += 64) {
+            const uint32_t w = w0 + lane;
+            uint64_t m = w < tl.words ? row[w] : 0ull;
+            const uint32_t pc = __popcll(m);
+            uint32_t inc = pc;
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t v = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += v;
+            }
+            const uint32_t tot = __shfl(inc, 63, 64);
+            uint64_t pos = out + inc - pc;
+            while (m) {
+                const int bit = __ffsll((unsigned long long)m) - 1;
+                m &= m - 1;
+                const uint32_t p = w * 64 + bit;
+                int g = 0;
+                while (g + 1 < (int)nr && p >= s_pref[g + 1]) ++g;
+                const uint32_t x = s_start[g] + (p - s_pref[g]);
+                pairs[2 * pos] = qid;
+                pairs[2 * pos + 1] = orig[x];
+                ++pos;
+            }
+            out += tot;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_recheck(const Boundary *bl, uint64_t cnt, const float4 *xs, uint64_t n, int32_t d,
+                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
+                          hipStream_t s)
+{
+    if (cnt == 0) return hipSuccess;
+    const uint64_t blocks = (cnt + 255) / 256;
+    hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, cnt,
+                       (const float *)xs, n, d, pinv, e64, mask, nin);
+    return hipGetLastError();
+}
+
+hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
+                           uint64_t wbase, uint64_t row_base, const uint64_t *mask, uint32_t *cnt,
+                           hipStream_t s)
+{
+    if (ntiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rowcount, dim3(ntiles), dim3(256), 0, s, tiles, t0, toff, wbase, row_base,
+                       mask, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
+                         uint64_t wbase, uint64_t row_base, const uint64_t *mask,
+                         const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
+                         const uint32_t *nrng, const uint32_t *orig, uint32_t *pairs, hipStream_t s)
+{
+    if (ntiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_expand, dim3(ntiles), dim3(256), 0, s, tiles, t0, toff, wbase, row_base, mask,
+                       roff, rstart, rpref, nrng, orig, pairs);
+    return hipGetLastError();
+}
+
+}  // namespace ersj

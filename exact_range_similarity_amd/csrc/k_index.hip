@@ -1,0 +1,803 @@
+// Index construction kernels for gfx950: per-dimension statistics, grid
+// Morton keys, LSD radix sort, point gather into the dimension-blocked
+// layout, cell boundaries and boxes, the 27-cell stencil with box pruning,
+// row tiles, device-wide scans and the batch planner.
+//
+// Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+// Similarity Searches".  Sec. IV-A picks the indexing dimensions by variance;
+// Sec. IV-B/IV-C group nearby points and store each group contiguously, the
+// groups in Morton order; Sec. IV-D counts candidates per query in a first
+// pass, builds a prefix sum over the counts and accumulates queries into
+// batches whose storage fits the free memory.  Here the groups are the
+// non-empty cells of a uniform grid over three dimensions (a grid index
+// searches the 3^k neighbouring cells, Sec. II-B1) and the box lower bound
+// used to drop neighbour cells is the one of "JZ-tree", Sec. III-B, eq. (15).
+#include "ersj_internal.h"
+
+#include <cmath>
+#include <cfloat>
+
+namespace ersj {
+
+namespace {
+
+constexpr int kBlock = 256;
+
+__device__ __forceinline__ uint64_t spread3(uint64_t x)
+{
+    x &= 0x1fffffull;
+    x = (x | (x << 32)) & 0x1f00000000ffffull;
+    x = (x | (x << 16)) & 0x1f0000ff0000ffull;
+    x = (x | (x << 8)) & 0x100f00f00f00f00full;
+    x = (x | (x << 4)) & 0x10c30c30c30c30c3ull;
+    x = (x | (x << 2)) & 0x1249249249249249ull;
+    return x;
+}
+
+__device__ __forceinline__ uint64_t compact3(uint64_t x)
+{
+    x &= 0x1249249249249249ull;
+    x = (x ^ (x >> 2)) & 0x10c30c30c30c30c3ull;
+    x = (x ^ (x >> 4)) & 0x100f00f00f00f00full;
+    x = (x ^ (x >> 8)) & 0x1f0000ff0000ffull;
+    x = (x ^ (x >> 16)) & 0x1f00000000ffffull;
+    x = (x ^ (x >> 32)) & 0x1fffffull;
+    return x;
+}
+
+// Order-preserving map of a float's bits onto uint32 (for atomic min/max).
+__device__ __forceinline__ uint32_t f2ord(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o)
+{
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    return __uint_as_float(u);
+}
+
+inline unsigned grid_for(int64_t n, int block = kBlock)
+{
+    int64_t g = (n + block - 1) / block;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+// ---------------------------------------------------------------- stats --
+// Thread g owns dimension g % d and rows g/d, g/d + step, ...; the thread
+// count is d*step, so every thread sees a single dimension.
+__global__ __launch_bounds__(kBlock) void k_stats_partial(const float *__restrict__ x, int64_t n,
+                                                          int32_t d, int64_t ld, int64_t T,
+                                                          double *__restrict__ part,
+                                                          uint32_t *__restrict__ badp)
+{
+    int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= T) return;
+    const int32_t k = (int32_t)(g % d);
+    const int64_t step = T / d;
+    const double shift = (double)x[k];
+    double s = 0.0, s2 = 0.0;
+    float mn = FLT_MAX, mx = -FLT_MAX;
+    uint32_t bad = 0;
+    for (int64_t r = g / d; r < n; r += step) {
+        float v = x[r * ld + k];
+        if (!isfinite(v)) {
+            ++bad;
+            continue;
+        }
+        double t = (double)v - shift;
+        s += t;
+        s2 += t * t;
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+    }
+    part[g * 4 + 0] = s;
+    part[g * 4 + 1] = s2;
+    part[g * 4 + 2] = mn;
+    part[g * 4 + 3] = mx;
+    badp[g] = bad;
+}
+
+// One block per dimension: out[k*4 + {0,1,2,3}] = mean, variance, min, max.
+__global__ __launch_bounds__(kBlock) void k_stats_final(const float *__restrict__ x, int64_t n,
+                                                        int32_t d, int64_t T,
+                                                        const double *__restrict__ part,
+                                                        const uint32_t *__restrict__ badp,
+                                                        double *__restrict__ out,
+                                                        unsigned long long *__restrict__ bad_total)
+{
+    __shared__ double ss[kBlock], ss2[kBlock], smn[kBlock], smx[kBlock];
+    __shared__ unsigned long long sb[kBlock];
+    const int32_t k = blockIdx.x;
+    const int64_t step = T / d;
+    double s = 0.0, s2 = 0.0, mn = DBL_MAX, mx = -DBL_MAX;
+    unsigned long long b = 0;
+    for (int64_t j = threadIdx.x; j < step; j += blockDim.x) {
+        int64_t g = j * d + k;
+        s += part[g * 4 + 0];
+        s2 += part[g * 4 + 1];
+        mn = fmin(mn, part[g * 4 + 2]);
+        mx = fmax(mx, part[g * 4 + 3]);
+        b += badp[g];
+    }
+    ss[threadIdx.x] = s;
+    ss2[threadIdx.x] = s2;
+    smn[threadIdx.x] = mn;
+    smx[threadIdx.x] = mx;
+    sb[threadIdx.x] = b;
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            ss[threadIdx.x] += ss[threadIdx.x + w];
+            ss2[threadIdx.x] += ss2[threadIdx.x + w];
+            smn[threadIdx.x] = fmin(smn[threadIdx.x], smn[threadIdx.x + w]);
+            smx[threadIdx.x] = fmax(smx[threadIdx.x], smx[threadIdx.x + w]);
+            sb[threadIdx.x] += sb[threadIdx.x + w];
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const double shift = (double)x[k];
+        const double m = ss[0] / (double)n;
+        out[k * 4 + 0] = shift + m;
+        out[k * 4 + 1] = fmax(0.0, ss2[0] / (double)n - m * m);
+        out[k * 4 + 2] = smn[0];
+        out[k * 4 + 3] = smx[0];
+        atomicAdd(bad_total, sb[0]);
+    }
+}
+
+// ----------------------------------------------------------------- keys --
+// Cell coordinate c = floor((x - lo) / w) in binary64, clamped to [0, G-1].
+// With w >= eps * (1 + 2^-20) two coordinates of a neighbour pair land in
+// cells at most one apart, so the 27-cell stencil is exhaustive.
+__global__ __launch_bounds__(kBlock) void k_keys(const float *__restrict__ x, int64_t n, int64_t ld,
+                                                 GridParams gp, uint64_t *__restrict__ keys,
+                                                 uint32_t *__restrict__ ids)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    uint64_t key = 0;
+    for (int a = 0; a < gp.ndim; ++a) {
+        double v = (double)x[i * ld + gp.dim[a]];
+        double c = floor((v - gp.lo[a]) / gp.w[a]);
+        int64_t ci = 0;
+        if (c > 0.0) ci = c >= (double)(gp.G[a] - 1) ? (int64_t)(gp.G[a] - 1) : (int64_t)c;
+        key |= spread3((uint64_t)ci) << a;
+    }
+    keys[i] = key;
+    ids[i] = (uint32_t)i;
+}
+
+// ----------------------------------------------------------- radix sort --
+constexpr int kRsItems = 16;
+constexpr int kRsTile = kBlock * kRsItems;
+
+__global__ __launch_bounds__(kBlock) void k_radix_hist(const uint64_t *__restrict__ keys, int64_t n,
+                                                       int shift, int64_t nblk,
+                                                       uint64_t *__restrict__ hist)
+{
+    __shared__ uint32_t h[256];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kRsTile;
+    for (int r = 0; r < kRsItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < n) atomicAdd(&h[(keys[i] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * nblk + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter: within a block the items are ranked in input order, round
+// by round (256 items per round), with wave ballots matching equal digits.
+__global__ __launch_bounds__(kBlock) void k_radix_scatter(const uint64_t *__restrict__ kin,
+                                                          const uint32_t *__restrict__ vin,
+                                                          uint64_t *__restrict__ kout,
+                                                          uint32_t *__restrict__ vout, int64_t n,
+                                                          int shift, int64_t nblk,
+                                                          const uint64_t *__restrict__ offs)
+{
+    __shared__ uint64_t s_off[256];
+    __shared__ uint32_t s_wc[4][256];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    s_off[tid] = offs[(int64_t)tid * nblk + blockIdx.x];
+    for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
+    __syncthreads();
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int64_t base = (int64_t)blockIdx.x * kRsTile;
+    for (int r = 0; r < kRsItems; ++r) {
+        const int64_t i = base + r * kBlock + tid;
+        const bool valid = i < n;
+        uint64_t k = 0;
+        uint32_t v = 0;
+        if (valid) {
+            k = kin[i];
+            v = vin[i];
+        }
+        const uint32_t dig = (uint32_t)(k >> shift) & 255u;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (dig >> b) & 1u;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const uint32_t rank = __popcll(peers & lt);
+        if (valid && rank == 0) s_wc[wave][dig] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t pre = 0;
+            for (int w = 0; w < wave; ++w) pre += s_wc[w][dig];
+            const uint64_t pos = s_off[dig] + pre + rank;
+            kout[pos] = k;
+            vout[pos] = v;
+        }
+        __syncthreads();
+        s_off[tid] += (uint64_t)s_wc[0][tid] + s_wc[1][tid] + s_wc[2][tid] + s_wc[3][tid];
+        for (int w = 0; w < 4; ++w) s_wc[w][tid] = 0;
+        __syncthreads();
+    }
+}
+
+// ----------------------------------------------------------------- scan --
+constexpr int kScItems = 16;
+constexpr int kScTile = kBlock * kScItems;
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_scan_reduce(const T *__restrict__ in, int64_t n,
+                                                        uint64_t *__restrict__ bsum)
+{
+    __shared__ uint64_t sw[kBlock / 64];
+    const int64_t base = (int64_t)blockIdx.x * kScTile;
+    uint64_t v = 0;
+    for (int r = 0; r < kScItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < n) v += (uint64_t)in[i];
+    }
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_down(v, o, 64);
+    if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) bsum[blockIdx.x] = sw[0] + sw[1] + sw[2] + sw[3];
+}
+
+// Block-wide exclusive scan of one value per thread; returns the prefix and
+// sets *total.
+__device__ __forceinline__ uint64_t block_excl_scan(uint64_t v, uint64_t *sw, uint64_t *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t inc = v;
+    for (int o = 1; o < 64; o <<= 1) {
+        uint64_t t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) sw[wave] = inc;
+    __syncthreads();
+    uint64_t pre = 0, tot = 0;
+    for (int w = 0; w < kBlock / 64; ++w) {
+        if (w < wave) pre += sw[w];
+        tot += sw[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return pre + inc - v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_scan_top(uint64_t *__restrict__ bsum, int64_t nb)
+{
+    __shared__ uint64_t sw[kBlock / 64];
+    uint64_t carry = 0;
+    for (int64_t s = 0; s < nb; s += kBlock) {
+        int64_t i = s + threadIdx.x;
+        uint64_t v = i < nb ? bsum[i] : 0, tot;
+        uint64_t ex = block_excl_scan(v, sw, &tot);
+        if (i < nb) bsum[i] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) bsum[nb] = carry;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_scan_down(const T *__restrict__ in, int64_t n,
+                                                      const uint64_t *__restrict__ bsum, int64_t nb,
+                                                      uint64_t *__restrict__ out)
+{
+    __shared__ uint64_t st[kScTile];
+    __shared__ uint64_t sw[kBlock / 64];
+    const int64_t base = (int64_t)blockIdx.x * kScTile;
+    for (int r = 0; r < kScItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        st[r * kBlock + threadIdx.x] = i < n ? (uint64_t)in[i] : 0;
+    }
+    __syncthreads();
+    uint64_t loc[kScItems];
+    uint64_t s = 0;
+    for (int j = 0; j < kScItems; ++j) {
+        loc[j] = s;
+        s += st[threadIdx.x * kScItems + j];
+    }
+    uint64_t tot;
+    const uint64_t pre = block_excl_scan(s, sw, &tot) + bsum[blockIdx.x];
+    for (int j = 0; j < kScItems; ++j) st[threadIdx.x * kScItems + j] = pre + loc[j];
+    __syncthreads();
+    for (int r = 0; r < kScItems; ++r) {
+        int64_t i = base + r * kBlock + threadIdx.x;
+        if (i < n) out[i] = st[r * kBlock + threadIdx.x];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = bsum[nb];
+}
+
+template <typename T>
+hipError_t scan_impl(const T *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s)
+{
+    const int64_t nb = (n + kScTile - 1) / kScTile;
+    if (nb == 0) return launch_fill_u64(out, 0, 1, s);
+    hipLaunchKernelGGL(k_scan_reduce<T>, dim3((unsigned)nb), dim3(kBlock), 0, s, in, n, tmp);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(kBlock), 0, s, tmp, nb);
+    hipLaunchKernelGGL(k_scan_down<T>, dim3((unsigned)nb), dim3(kBlock), 0, s, in, n, tmp, nb, out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- gather --
+__global__ __launch_bounds__(kBlock) void k_gather(const float *__restrict__ x, int64_t n, int32_t d,
+                                                   int64_t ld, const uint32_t *__restrict__ orig,
+                                                   const int32_t *__restrict__ perm,
+                                                   float4 *__restrict__ xs)
+{
+    __shared__ int32_t sp[kMaxDim + 4];
+    const int nb = (d + 3) / 4;
+    for (int k = threadIdx.x; k < nb * 4; k += blockDim.x) sp[k] = k < d ? perm[k] : -1;
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const float *row = x + (int64_t)orig[i] * ld;
+    for (int b = 0; b < nb; ++b) {
+        float4 v;
+        v.x = sp[4 * b + 0] >= 0 ? row[sp[4 * b + 0]] : 0.0f;
+        v.y = sp[4 * b + 1] >= 0 ? row[sp[4 * b + 1]] : 0.0f;
+        v.z = sp[4 * b + 2] >= 0 ? row[sp[4 * b + 2]] : 0.0f;
+        v.w = sp[4 * b + 3] >= 0 ? row[sp[4 * b + 3]] : 0.0f;
+        xs[(int64_t)b * n + i] = v;
+    }
+}
+
+// ----------------------------------------------------------------- cells --
+__global__ __launch_bounds__(kBlock) void k_cell_flags(const uint64_t *__restrict__ keys, int64_t n,
+                                                       uint32_t *__restrict__ flags)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    flags[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restrict__ keys,
+                                                         const uint32_t *__restrict__ flags,
+                                                         const uint64_t *__restrict__ cid, int64_t n,
+                                                         uint32_t *__restrict__ cell_start,
+                                                         uint64_t *__restrict__ cell_key)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    if (flags[i]) {
+        cell_start[cid[i]] = (uint32_t)i;
+        cell_key[cid[i]] = keys[i];
+    }
+    if (i == n - 1) cell_start[cid[n]] = (uint32_t)n;
+}
+
+constexpr int kAabbChunk = 64;
+
+__global__ __launch_bounds__(kBlock) void k_cell_aabb(const float4 *__restrict__ xs,
+                                                      const uint64_t *__restrict__ cid, int64_t n,
+                                                      uint32_t *__restrict__ lo_bits,
+                                                      uint32_t *__restrict__ hi_bits)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i0 = c * kAabbChunk;
+    if (i0 >= n) return;
+    const int64_t i1 = i0 + kAabbChunk < n ? i0 + kAabbChunk : n;
+    int64_t cur = -1;
+    uint32_t lo[3], hi[3];
+    for (int64_t i = i0; i <= i1; ++i) {
+        const int64_t cell = i < i1 ? (int64_t)cid[i + 1] - 1 : -2;
+        if (cell != cur) {
+            if (cur >= 0) {
+                for (int a = 0; a < 3; ++a) {
+                    atomicMin(&lo_bits[cur * 3 + a], lo[a]);
+                    atomicMax(&hi_bits[cur * 3 + a], hi[a]);
+                }
+            }
+            cur = cell;
+            for (int a = 0; a < 3; ++a) {
+                lo[a] = 0xffffffffu;
+                hi[a] = 0u;
+            }
+        }
+        if (i < i1) {
+            const float4 v = xs[i];
+            const uint32_t o0 = f2ord(v.x), o1 = f2ord(v.y), o2 = f2ord(v.z);
+            lo[0] = min(lo[0], o0); hi[0] = max(hi[0], o0);
+            lo[1] = min(lo[1], o1); hi[1] = max(hi[1], o1);
+            lo[2] = min(lo[2], o2); hi[2] = max(hi[2], o2);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t *__restrict__ p, uint32_t v, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_fill_u64(uint64_t *__restrict__ p, uint64_t v, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+// --------------------------------------------------------------- stencil --
+__device__ __forceinline__ int64_t find_key(const uint64_t *__restrict__ k, int64_t M, uint64_t key)
+{
+    int64_t lo = 0, hi = M;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) >> 1;
+        if (k[mid] < key) lo = mid + 1;
+        else hi = mid;
+    }
+    return (lo < M && k[lo] == key) ? lo : -1;
+}
+
+// Per cell A: the neighbour cells B (offsets in {-1,0,1}^3) that exist and
+// whose box lower distance to A's box (binary64, over the grid dimensions)
+// does not exceed the pruning threshold.  Kept cells are sorted by index and
+// runs of consecutive cells are merged into one contiguous candidate range.
+__global__ __launch_bounds__(kBlock) void k_stencil(const uint64_t *__restrict__ cell_key,
+                                                    const uint32_t *__restrict__ cell_start,
+                                                    const uint32_t *__restrict__ lo_bits,
+                                                    const uint32_t *__restrict__ hi_bits, int64_t M,
+                                                    GridParams gp, double prune_e2,
+                                                    uint32_t *__restrict__ rstart,
+                                                    uint32_t *__restrict__ rpref,
+                                                    uint32_t *__restrict__ nrng,
+                                                    uint32_t *__restrict__ tiles_per_cell,
+                                                    unsigned int *__restrict__ umax)
+{
+    const int64_t A = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (A >= M) return;
+    const uint64_t key = cell_key[A];
+    int64_t c[3];
+    double alo[3], ahi[3];
+    for (int a = 0; a < 3; ++a) {
+        c[a] = (int64_t)compact3(key >> a);
+        alo[a] = (double)ord2f(lo_bits[A * 3 + a]);
+        ahi[a] = (double)ord2f(hi_bits[A * 3 + a]);
+    }
+    uint32_t kept[kMaxRanges];
+    int nk = 0;
+    for (int s = 0; s < 27; ++s) {
+        const int64_t dlt[3] = {s % 3 - 1, (s / 3) % 3 - 1, s / 9 - 1};
+        uint64_t nkey = 0;
+        bool ok = true;
+        for (int a = 0; a < 3; ++a) {
+            const int64_t v = c[a] + dlt[a];
+            const int64_t G = a < gp.ndim ? gp.G[a] : 1;
+            if (v < 0 || v >= G) ok = false;
+            else nkey |= spread3((uint64_t)v) << a;
+        }
+        if (!ok) continue;
+        const int64_t B = (nkey == key) ? A : find_key(cell_key, M, nkey);
+        if (B < 0) continue;
+        if (B != A) {
+            double dl2 = 0.0;
+            for (int a = 0; a < 3; ++a) {
+                const double blo = (double)ord2f(lo_bits[B * 3 + a]);
+                const double bhi = (double)ord2f(hi_bits[B * 3 + a]);
+                double gap = 0.0;
+                if (blo > ahi[a]) gap = blo - ahi[a];
+                else if (alo[a] > bhi) gap = alo[a] - bhi;
+                dl2 += gap * gap;
+            }
+            if (dl2 > prune_e2) continue;
+        }
+        kept[nk++] = (uint32_t)B;
+    }
+    for (int i = 1; i < nk; ++i) {
+        const uint32_t v = kept[i];
+        int j = i - 1;
+        while (j >= 0 && kept[j] > v) {
+            kept[j + 1] = kept[j];
+            --j;
+        }
+        kept[j + 1] = v;
+    }
+    uint32_t nr = 0, U = 0;
+    uint32_t cur_start = 0, cur_len = 0;
+    for (int i = 0; i < nk; ++i) {
+        const uint32_t st = cell_start[kept[i]], len = cell_start[kept[i] + 1] - st;
+        if (i > 0 && kept[i] == kept[i - 1] + 1) {
+            cur_len += len;
+        } else {
+            if (i > 0) {
+                rstart[A * kMaxRanges + nr] = cur_start;
+                rpref[A * (kMaxRanges + 1) + nr] = U;
+                U += cur_len;
+                ++nr;
+            }
+            cur_start = st;
+            cur_len = len;
+        }
+    }
+    rstart[A * kMaxRanges + nr] = cur_start;
+    rpref[A * (kMaxRanges + 1) + nr] = U;
+    U += cur_len;
+    ++nr;
+    for (int g = nr; g <= kMaxRanges; ++g) rpref[A * (kMaxRanges + 1) + g] = U;
+    for (int g = nr; g < kMaxRanges; ++g) rstart[A * kMaxRanges + g] = 0;
+    nrng[A] = nr;
+    const uint32_t sz = cell_start[A + 1] - cell_start[A];
+    tiles_per_cell[A] = (sz + kTileRows - 1) / kTileRows;
+    atomicMax(umax, U);
+}
+
+// ----------------------------------------------------------------- tiles --
+__global__ __launch_bounds__(kBlock) void k_tiles(const uint64_t *__restrict__ tile_base, int64_t M,
+                                                  int64_t T, const uint32_t *__restrict__ cell_start,
+                                                  const uint32_t *__restrict__ rpref,
+                                                  const uint32_t *__restrict__ nrng,
+                                                  Tile *__restrict__ tiles,
+                                                  uint64_t *__restrict__ words,
+                                                  uint64_t *__restrict__ cands)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    int64_t lo = 0, hi = M;  // largest A with tile_base[A] <= t
+    while (hi - lo > 1) {
+        int64_t mid = (lo + hi) >> 1;
+        if (tile_base[mid] <= (uint64_t)t) lo = mid;
+        else hi = mid;
+    }
+    const int64_t A = lo;
+    const uint32_t j = (uint32_t)(t - (int64_t)tile_base[A]);
+    const uint32_t row0 = cell_start[A] + j * kTileRows;
+    const uint32_t end = cell_start[A + 1];
+    const uint32_t nrows = min((uint32_t)kTileRows, end - row0);
+    const uint32_t U = rpref[A * (kMaxRanges + 1) + nrng[A]];
+    const uint32_t W = (U + 63u) / 64u;
+    Tile tl;
+    tl.cell = (uint32_t)A;
+    tl.row0 = row0;
+    tl.nrows = nrows;
+    tl.words = W;
+    tiles[t] = tl;
+    words[t] = (uint64_t)nrows * W;
+    cands[t] = (uint64_t)nrows * U;
+}
+
+// ------------------------------------------------------------------ plan --
+// Greedy window batching over row tiles in index order: a batch grows while
+// its mask words stay within the budget.  result = {batches, max words,
+// failing tile + 1 (0 = ok)}.
+__global__ void k_plan(const uint64_t *__restrict__ toff, const uint64_t *__restrict__ coff,
+                       const Tile *__restrict__ tiles, int64_t T, int64_t n, uint64_t budget,
+                       uint32_t *__restrict__ bounds, uint64_t *__restrict__ row_bounds,
+                       uint64_t *__restrict__ word_bounds, uint64_t *__restrict__ cand_bounds,
+                       uint64_t *__restrict__ result)
+{
+    if (blockIdx.x != 0 || threadIdx.x != 0) return;
+    int64_t t = 0, nb = 0;
+    uint64_t maxw = 0, err = 0, maxrows = 0;
+    bounds[0] = 0;
+    row_bounds[0] = 0;
+    word_bounds[0] = 0;
+    cand_bounds[0] = 0;
+    while (t < T) {
+        const uint64_t base = toff[t];
+        const uint64_t lim = base + budget < base ? ~0ull : base + budget;
+        int64_t lo = t, hi = T;  // largest t2 in [t, T] with toff[t2] <= lim
+        while (lo < hi) {
+            int64_t mid = (lo + hi + 1) >> 1;
+            if (toff[mid] <= lim) lo = mid;
+            else hi = mid - 1;
+        }
+        if (lo == t) {
+            err = (uint64_t)t + 1;
+            break;
+        }
+        ++nb;
+        bounds[nb] = (uint32_t)lo;
+        row_bounds[nb] = lo < T ? tiles[lo].row0 : (uint64_t)n;
+        word_bounds[nb] = toff[lo];
+        cand_bounds[nb] = coff[lo];
+        maxw = max(maxw, toff[lo] - base);
+        maxrows = max(maxrows, row_bounds[nb] - row_bounds[nb - 1]);
+        t = lo;
+    }
+    result[0] = (uint64_t)nb;
+    result[1] = maxw;
+    result[2] = err;
+    result[3] = maxrows;
+}
+
+// Launch order: by batch, then heaviest cell first (Sec. IV-D: primitives
+// with more intersections are processed first).
+__global__ __launch_bounds__(kBlock) void k_order_keys(const Tile *__restrict__ tiles,
+                                                       const uint32_t *__restrict__ rpref,
+                                                       const uint32_t *__restrict__ nrng, int64_t T,
+                                                       const uint32_t *__restrict__ bounds,
+                                                       int32_t nb, int ubits, uint32_t umax,
+                                                       uint64_t *__restrict__ keys,
+                                                       uint32_t *__restrict__ vals)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    int lo = 0, hi = nb;  // largest b with bounds[b] <= t
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (bounds[mid] <= (uint32_t)t) lo = mid;
+        else hi = mid;
+    }
+    const uint32_t A = tiles[t].cell;
+    const uint32_t U = rpref[(uint64_t)A * (kMaxRanges + 1) + nrng[A]];
+    keys[t] = ((uint64_t)lo << ubits) | (uint64_t)(umax - U);
+    vals[t] = (uint32_t)t;
+}
+
+}  // namespace
+
+// ============================================================ launchers ==
+int64_t stats_threads(int64_t n, int32_t d)
+{
+    int64_t step = 131072 / d;
+    if (step < 1) step = 1;
+    if (step > n) step = n;
+    return step * d;
+}
+
+hipError_t launch_stats(const float *x, int64_t n, int32_t d, int64_t ld, double *partial,
+                        uint32_t *bad_partial, int64_t T, double *out_stats,
+                        unsigned long long *out_bad, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u64, dim3(1), dim3(kBlock), 0, s, (uint64_t *)out_bad, 0ull, 1);
+    hipLaunchKernelGGL(k_stats_partial, dim3(grid_for(T)), dim3(kBlock), 0, s, x, n, d, ld, T,
+                       partial, bad_partial);
+    hipLaunchKernelGGL(k_stats_final, dim3((unsigned)d), dim3(kBlock), 0, s, x, n, d, T, partial,
+                       bad_partial, out_stats, out_bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp, uint64_t *keys,
+                       uint32_t *ids, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, ld, gp, keys, ids);
+    return hipGetLastError();
+}
+
+size_t radix_hist_entries(int64_t n)
+{
+    const int64_t nblk = (n + kRsTile - 1) / kRsTile;
+    return (size_t)(2 * (256 * nblk + 1));  // counts, then their scan
+}
+
+size_t scan_tmp_entries(int64_t n)
+{
+    const int64_t nb = (n + kScTile - 1) / kScTile;
+    return (size_t)(nb + 1);
+}
+
+hipError_t scan_u32(const uint32_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s)
+{
+    return scan_impl<uint32_t>(in, out, n, tmp, s);
+}
+
+hipError_t scan_u64(const uint64_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s)
+{
+    return scan_impl<uint64_t>(in, out, n, tmp, s);
+}
+
+hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, int64_t n, int bits,
+                      uint64_t *hist, uint64_t *scan_tmp, hipStream_t s)
+{
+    const int passes = (bits + 7) / 8;
+    const int64_t nblk = (n + kRsTile - 1) / kRsTile;
+    uint64_t *hs = hist + 256 * nblk + 1;  // scanned offsets live after the counts
+    uint64_t *ki = k0, *ko = k1;
+    uint32_t *vi = v0, *vo = v1;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nblk), dim3(kBlock), 0, s, ki, n, shift, nblk,
+                           hist);
+        hipError_t e = scan_u64(hist, hs, 256 * nblk, scan_tmp, s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, s, ki, vi, ko, vo, n,
+                           shift, nblk, hs);
+        uint64_t *tk = ki; ki = ko; ko = tk;
+        uint32_t *tv = vi; vi = vo; vo = tv;
+    }
+    if (ki != k0) {
+        hipError_t e = hipMemcpyAsync(k0, ki, sizeof(uint64_t) * n, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return e;
+        e = hipMemcpyAsync(v0, vi, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
+                         const int32_t *perm, float4 *xs, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, d, ld, orig, perm, xs);
+    return hipGetLastError();
+}
+
+hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, uint32_t *flags, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_cell_flags, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, n, flags);
+    return hipGetLastError();
+}
+
+hipError_t launch_cell_scatter(const uint64_t *keys, const uint32_t *flags, const uint64_t *cid,
+                               int64_t n, uint32_t *cell_start, uint64_t *cell_key, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_cell_scatter, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, flags, cid, n,
+                       cell_start, cell_key);
+    return hipGetLastError();
+}
+
+hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, int64_t M,
+                            uint32_t *lo_bits, uint32_t *hi_bits, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(3 * M)), dim3(kBlock), 0, s, lo_bits, 0xffffffffu,
+                       3 * M);
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(3 * M)), dim3(kBlock), 0, s, hi_bits, 0u, 3 * M);
+    const int64_t chunks = (n + kAabbChunk - 1) / kAabbChunk;
+    hipLaunchKernelGGL(k_cell_aabb, dim3(grid_for(chunks)), dim3(kBlock), 0, s, xs, cid, n, lo_bits,
+                       hi_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_stencil(const uint64_t *cell_key, const uint32_t *cell_start,
+                          const uint32_t *lo_bits, const uint32_t *hi_bits, int64_t M,
+                          const GridParams &gp, double prune_e2, uint32_t *rstart, uint32_t *rpref,
+                          uint32_t *nrng, uint32_t *tiles_per_cell, unsigned int *umax,
+                          hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(kBlock), 0, s, umax, 0u, 1);
+    hipLaunchKernelGGL(k_stencil, dim3(grid_for(M)), dim3(kBlock), 0, s, cell_key, cell_start,
+                       lo_bits, hi_bits, M, gp, prune_e2, rstart, rpref, nrng, tiles_per_cell, umax);
+    return hipGetLastError();
+}
+
+hipError_t launch_tiles(const uint64_t *tile_base, int64_t M, int64_t T, const uint32_t *cell_start,
+                        const uint32_t *rpref, const uint32_t *nrng, Tile *tiles, uint64_t *words,
+                        uint64_t *cands, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tiles, dim3(grid_for(T)), dim3(kBlock), 0, s, tile_base, M, T, cell_start,
+                       rpref, nrng, tiles, words, cands);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan(const uint64_t *toff, const uint64_t *coff, const Tile *tiles, int64_t T,
+                       int64_t n, uint64_t budget_words, uint32_t *bounds, uint64_t *row_bounds,
+                       uint64_t *word_bounds, uint64_t *cand_bounds, uint64_t *result,
+                       hipStream_t s)
+{
+    hipLaunchKernelGGL(k_plan, dim3(1), dim3(64), 0, s, toff, coff, tiles, T, n, budget_words, bounds,
+                       row_bounds, word_bounds, cand_bounds, result);
+    return hipGetLastError();
+}
+
+hipError_t launch_order_keys(const Tile *tiles, const uint32_t *rpref, const uint32_t *nrng,
+                             int64_t T, const uint32_t *bounds, int32_t nb, int ubits, uint32_t umax,
+                             uint64_t *keys, uint32_t *vals, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_order_keys, dim3(grid_for(T)), dim3(kBlock), 0, s, tiles, rpref, nrng, T,
+                       bounds, nb, ubits, umax, keys, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u64(uint64_t *p, uint64_t v, int64_t n, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n)), dim3(kBlock), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
+}  // namespace ersj

@@ -1,0 +1,176 @@
+/*
+ * ersj.h -- exact epsilon-distance similarity self-join on AMD Instinct
+ * MI355X (gfx950).  C ABI of libersj.so.
+ *
+ * The operation ("RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+ * Similarity Searches", Sec. II-A, Problem Statement): for a dataset D of n
+ * points in d dimensions and a search distance eps, the self-join result R
+ * holds every ordered pair (i, j) of point ids whose Euclidean distance is at
+ * most eps.  Self pairs (i, i) are included (the selectivity of Sec. V-B,
+ * z = (|R| - |D|) / |D|, counts them in |R|), both (i, j) and (j, i) appear,
+ * and each pair appears once.  Results are key-value pairs of two 32-bit ids
+ * (Sec. II-A1).
+ *
+ * Exactness.  A pair belongs to R iff D64(x_i, x_j) <= fl64(eps * eps), where
+ * D64 is the binary64 sum over the input's dimension order of
+ * ((double)x_i[k] - (double)x_j[k])^2, each operation rounded to nearest, no
+ * fused multiply-add.  The library classifies pairs in fp32 with a proven
+ * error band and re-evaluates every pair inside the band with exactly that
+ * binary64 sequence, so the returned set equals this definition bit for bit.
+ *
+ * Pipeline (search-then-refine, Sec. IV): build_index picks the three
+ * highest-variance dimensions (Sec. IV-A), bins points into a uniform grid of
+ * cell width >= eps on them, sorts points by the cells' Morton codes and
+ * stores them contiguously per cell (Sec. IV-C); count_pass finds for every
+ * cell the neighbouring cells that can hold a neighbour and so an upper
+ * bound on every query's candidates (the first pass of the two-pass scheme,
+ * Sec. IV-D); plan_batches cuts the queries into batches whose result masks
+ * fit a memory budget (Sec. IV-D, window batching against free memory);
+ * fill_pass refines one batch into a one-bit-per-candidate result mask
+ * (Sec. IV-E, IV-F) and compacts the mask into pairs (Sec. IV-F1, Fig. 5).
+ *
+ * Conventions for every entry point:
+ *  - d_* pointers are HIP device memory of the current device; h_* and
+ *    plain scalar out-parameters are host memory.
+ *  - stream is a hipStream_t (NULL = the default stream).  All device work
+ *    of a call is ordered on that stream.  Calls that return host values
+ *    synchronise the stream before returning.
+ *  - Return value: ERSJ_OK or a negative ERSJ_ERR_* code; no C++ exception
+ *    crosses the ABI.  After an error, ersj_last_error() returns a message
+ *    (thread-local), and the outputs of that call are unspecified.
+ *  - Arguments are validated before any HIP call is made.
+ *  - A handle may be used from one host thread at a time.
+ */
+#ifndef ERSJ_H
+#define ERSJ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ERSJ_OK = 0,
+    ERSJ_ERR_INVALID_ARG = -1, /* bad pointer, size, eps, or non-finite input */
+    ERSJ_ERR_STATE = -2,       /* call out of order (e.g. fill before plan) */
+    ERSJ_ERR_HIP = -3,         /* HIP runtime error; message names it */
+    ERSJ_ERR_OOM = -4,         /* device allocation failed or max_device_bytes hit */
+    ERSJ_ERR_BUDGET = -5,      /* one row tile's mask exceeds the batch budget */
+    ERSJ_ERR_CAPACITY = -6     /* output buffer too small; *n_pairs = required */
+};
+
+typedef struct ersj_index ersj_index; /* opaque; owns all its device memory */
+
+/* Refinement kernels (Sec. IV-E).  Both return identical pair sets. */
+enum {
+    ERSJ_REFINE_AUTO = 0,   /* library's choice */
+    ERSJ_REFINE_DIRECT = 1, /* fp32 sum of squared differences on the vector ALUs */
+    ERSJ_REFINE_MFMA = 2    /* |q|^2 + |x|^2 - 2 q.x with the dot products on MFMA */
+};
+
+typedef struct ersj_options {
+    uint32_t struct_size;       /* sizeof(ersj_options) of the caller */
+    int32_t refine_kernel;      /* ERSJ_REFINE_* */
+    double cell_width_scale;    /* grid cell width = eps * max(1, scale); default 1 */
+    uint64_t max_device_bytes;  /* cap on library-owned device memory; 0 = none */
+    uint64_t boundary_capacity; /* initial boundary-pair list entries; 0 = default */
+    int32_t timing;             /* nonzero: record HIP events around each phase */
+    int32_t reserved;
+} ersj_options;
+
+typedef struct ersj_stats {
+    int64_t n;                   /* points */
+    int32_t d;                   /* dimensions */
+    int32_t index_dims[3];       /* original ids of the grid dimensions (-1: unused) */
+    int32_t grid[3];             /* cells per grid dimension */
+    int32_t refine_kernel;       /* kernel used (ERSJ_REFINE_DIRECT or _MFMA) */
+    int64_t cells;               /* non-empty grid cells */
+    int64_t tiles;               /* row tiles (up to 32 rows of one cell) */
+    uint64_t total_candidates;   /* sum over queries of the candidate upper bound */
+    uint64_t total_mask_words;   /* 64-bit mask words over all batches */
+    int32_t n_batches;           /* from the last plan_batches */
+    int32_t last_batch;          /* batch of the last fill_pass (-1: none) */
+    uint64_t max_batch_words;    /* largest batch mask in 64-bit words */
+    uint64_t last_batch_candidates; /* candidates refined by the last fill_pass */
+    uint64_t last_batch_pairs;   /* pairs produced by the last fill_pass */
+    uint64_t last_boundary_pairs;/* pairs in the fp32 band, re-checked in fp64 */
+    uint64_t last_recheck_in;    /* of those, pairs found to be neighbours */
+    uint64_t device_bytes;       /* device memory held by the handle */
+    /* phase times in ms, accumulated since build (only with options.timing) */
+    double build_ms, count_ms, plan_ms, refine_ms, recheck_ms, expand_ms;
+    int64_t refine_launches;     /* refine kernel launches timed in refine_ms */
+    uint64_t refined_candidates; /* candidates refined in those launches */
+} ersj_stats;
+
+/* Fill *opt with the defaults (struct_size set). */
+void ersj_default_options(ersj_options *opt);
+
+/*
+ * Build the grid index over d_x (Sec. IV-A to IV-C).
+ *  d_x  : device, n rows of d floats, row r at d_x + r*ld; borrowed only for
+ *         the duration of the call (the stream is synchronised on return).
+ *  n    : 1 <= n <= 2^32 - 1;  d: 1 <= d <= 4096;  ld >= d.
+ *  eps  : >= 0 (may be +inf; NaN rejected).
+ *  opt  : NULL for defaults.
+ *  out  : receives a new handle (freed by ersj_free).
+ * Errors: INVALID_ARG (also for NaN/inf coordinates, detected on the device),
+ *         HIP, OOM.
+ */
+int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double eps,
+                     const ersj_options *opt, void *stream, ersj_index **out);
+
+/*
+ * Count pass (Sec. IV-D, "First Intersection Test" and pass 1): for each
+ * cell keep the neighbouring cells whose boxes can hold a neighbour; every
+ * query's candidate count is the size of its cell's kept cells.
+ *  total_candidates: host out, sum over all queries (may be NULL).
+ * Errors: INVALID_ARG, STATE (index not built), HIP, OOM.
+ */
+int ersj_count_pass(ersj_index *h, uint64_t *total_candidates, void *stream);
+
+/*
+ * Cut the queries (in index order, whole row tiles) into batches whose
+ * result masks (one bit per candidate, Sec. IV-F) fit budget_bytes
+ * (Sec. IV-D: queries are accumulated while the total stays within the
+ * budget).  budget_bytes = 0 uses 3/4 of the device's free memory.
+ *  n_batches: host out.
+ * Errors: INVALID_ARG, STATE (count_pass not run), BUDGET (a single row
+ *         tile's mask exceeds the budget), HIP, OOM.
+ */
+int ersj_plan_batches(ersj_index *h, uint64_t budget_bytes, int32_t *n_batches, void *stream);
+
+/*
+ * Refine batch `batch` and write its result pairs (Sec. IV-E, IV-F).
+ *  d_pairs : device, room for `capacity` pairs of two uint32 (query id,
+ *            point id), original row ids, interleaved; may be NULL when
+ *            capacity is 0.
+ *  n_pairs : host out, the batch's pair count.
+ * The union over all batches is R, each pair once.  Order within a batch is
+ * index order of the query, then candidate order.
+ * If capacity < pair count the call returns CAPACITY with *n_pairs set to the
+ * pair count and writes nothing; calling again for the same batch with a
+ * larger buffer only re-runs the final compaction.
+ * Errors: INVALID_ARG, STATE (plan_batches not run), CAPACITY, HIP, OOM.
+ */
+int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t capacity,
+                   uint64_t *n_pairs, void *stream);
+
+/* Rows covered by a batch (index order) and its mask size.  Host outputs. */
+int ersj_batch_info(const ersj_index *h, int32_t batch, uint64_t *first_row, uint64_t *n_rows,
+                    uint64_t *mask_words);
+
+/* Counters and phase times of the handle (host out). */
+int ersj_get_stats(const ersj_index *h, ersj_stats *out);
+
+/* Release the handle and all device memory it owns.  NULL is a no-op. */
+void ersj_free(ersj_index *h);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *ersj_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ERSJ_H */
