@@ -1,0 +1,201 @@
+"""Benchmark: exact epsilon self-join on one MI355X.
+
+One step is one complete self-join of the workload with its points already
+resident in HBM: build_index, count_pass, plan_batches, and fill_pass of
+every batch (pairs written to device memory).  The default workload is
+N = 1,000,000 points, d = 32, a mixture of 100 isotropic Gaussians
+(sigma = 0.02) with epsilon giving a mean of 64 neighbours per point.
+
+Printed JSON (one line): throughput in candidate distance evaluations per
+second over the whole join, plus the refinement kernel's roofline position
+(its duration measured with HIP events on the stream it runs on) and the CPU
+oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ε-self-join time + candidate dist evals/s and % of HBM/FP32 roofline, 1 GPU"
+FP32_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (256 CUs, 2.4 GHz)
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def load_eps(name):
+    with open(os.path.join(ROOT, "tests", "golden", "eps_configs.json")) as f:
+        return json.load(f)[name]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--budget-frac", type=float, default=0.0,
+                    help="batch budget as a fraction of the total mask (0 = free memory)")
+    ap.add_argument("--refine", type=int, default=0, help="0 auto, 1 direct, 2 mfma")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        log("bench.py: only --gpus 1 is supported (single-GPU self-join; no sharding in this build)")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_range_similarity_amd as ersj
+    from workloads import CONFIGS, make_config, x_digest
+
+    spec = CONFIGS[args.workload]
+    rec = load_eps(args.workload)
+    eps = float.fromhex(rec["eps"])
+    t0 = time.time()
+    X = make_config(args.workload)
+    if x_digest(X) != rec["x_sha256"]:
+        raise SystemExit("generated points differ from the ones epsilon was calibrated on")
+    log(f"[bench] {args.workload}: n={X.shape[0]} d={X.shape[1]} eps={eps!r} "
+        f"(generated in {time.time() - t0:.1f}s)")
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    xt = torch.from_numpy(X).to(dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    budget = 0
+    if args.budget_frac > 0:
+        h = ersj.build_index(xt, eps)
+        ersj.count_pass(h)
+        budget = int(ersj.get_stats(h)["total_mask_words"] * 8 * args.budget_frac)
+        h.free()
+
+    def step(timing):
+        opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine)
+        h = ersj.build_index(xt, eps, opts, stream)
+        ersj.count_pass(h, stream)
+        nb = ersj.plan_batches(h, budget, stream)
+        npairs = 0
+        for part in ersj.iter_batches(h, nb, stream):
+            npairs += part.shape[0]
+            del part
+        st = ersj.get_stats(h)
+        h.free()
+        return npairs, st
+
+    for w in range(args.warmup):
+        npairs, st = step(False)
+        log(f"[bench] warmup {w}: pairs={npairs} batches={st['n_batches']}")
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    stats = []
+    for k in range(args.steps):
+        npairs, st = step(True)
+        stats.append(st)
+        log(f"[bench] step {k}: refine {st['refine_ms']:.2f} ms, pairs {npairs}")
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) / args.steps
+
+    st = stats[-1]
+    cand = st["total_candidates"]
+    d = X.shape[1]
+    launches = sum(s["refine_launches"] for s in stats)
+    refine_ms = sum(s["refine_ms"] for s in stats)
+    refined = sum(s["refined_candidates"] for s in stats)
+    avg_launch_ms = refine_ms / max(1, launches)
+    flops_per_launch = 3.0 * d * refined / max(1, launches)
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    phases = {k: sum(s[k] for s in stats) / args.steps
+              for k in ("build_ms", "count_ms", "plan_ms", "refine_ms", "recheck_ms", "expand_ms")}
+
+    out = {
+        "metric": METRIC,
+        "value": cand / wall,
+        "unit": "candidate dist evals/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {spec.desc}; eps for a mean of {spec.k} neighbours/point",
+            "n": int(X.shape[0]), "d": int(d), "eps": rec["eps"], "k": spec.k, "seed": spec.seed,
+            "batches": st["n_batches"], "budget_bytes": budget,
+            "refine_kernel": {1: "direct", 2: "mfma"}.get(st["refine_kernel"], "?"),
+        },
+        "join_wall_s": wall,
+        "result_pairs": npairs,
+        "result_pairs_per_s": npairs / wall,
+        "candidates": cand,
+        "candidate_fraction_of_n2": cand / float(X.shape[0]) ** 2,
+        "cells": st["cells"],
+        "grid": st["grid"],
+        "boundary_pairs": st["last_boundary_pairs"],
+        "recheck_in": st["last_recheck_in"],
+        "phase_ms": phases,
+        "roofline": {
+            "bound": "alu",
+            "kernel": "k_refine_direct",
+            "achieved": achieved,
+            "peak": FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / FP32_PEAK_TFLOPS,
+            "traffic": None,
+            "flops_per_launch": flops_per_launch,
+            "avg_launch_ms": avg_launch_ms,
+            "launches": launches,
+        },
+    }
+
+    if args.copy_calib:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies done")
+
+    if not args.no_cpu:
+        import oracle
+        rows_probe = 4 * oracle.threads()
+        t = time.perf_counter()
+        oracle.join_rows(X, eps, np.arange(rows_probe))
+        per_row = (time.perf_counter() - t) / rows_probe
+        nrows = int(max(rows_probe, min(X.shape[0], args.cpu_seconds / max(per_row, 1e-9))))
+        log(f"[bench] cpu oracle: {nrows} rows (~{per_row * nrows:.0f}s)")
+        t = time.perf_counter()
+        colptr, _ = oracle.join_rows(X, eps, np.arange(nrows))
+        dt = time.perf_counter() - t
+        evals = nrows * X.shape[0]
+        out["cpu_baseline"] = {
+            "value": evals / dt, "unit": "candidate dist evals/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"rows 0..{nrows - 1} of {args.workload} against all {X.shape[0]} points "
+                      f"(brute force, binary64), {dt:.1f}s",
+            "sample_pairs": int(colptr[-1]),
+            "full_join_s_extrapolated": dt * X.shape[0] / nrows,
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
