@@ -118,8 +118,23 @@ def main():
     refine_ms = sum(s["refine_ms"] for s in stats)
     refined = sum(s["refined_candidates"] for s in stats)
     avg_launch_ms = refine_ms / max(1, launches)
-    flops_per_launch = 3.0 * d * refined / max(1, launches)
+    mfma = st["refine_kernel"] == ersj.REFINE_MFMA
+    # algorithmic flops per candidate: direct form 3d (sub, mul, add per
+    # dimension); expanded form 2d + 3 (the dot product on MFMA plus norms)
+    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
+    flops_per_launch = per_cand * refined / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    kname = "k_refine_mfma" if mfma else "k_refine_direct"
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"{kname.replace('k_', '')}_{args.workload}_traffic.json")
+    if os.path.exists(tfile):
+        import hashlib
+        with open(tfile) as f:
+            trec = json.load(f)
+        with open(os.path.join(ROOT, trec["source"]), "rb") as f:
+            cur = hashlib.sha256(f.read()).hexdigest()
+        if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget:
+            traffic = trec["hbm_bytes_per_launch"]
     phases = {k: sum(s[k] for s in stats) / args.steps
               for k in ("build_ms", "count_ms", "plan_ms", "refine_ms", "recheck_ms", "expand_ms")}
 
@@ -153,13 +168,13 @@ def main():
         "recheck_in": st["last_recheck_in"],
         "phase_ms": phases,
         "roofline": {
-            "bound": "alu",
-            "kernel": "k_refine_direct",
+            "bound": "mfma" if mfma else "alu",
+            "kernel": kname,
             "achieved": achieved,
             "peak": FP32_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / FP32_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
             "flops_per_launch": flops_per_launch,
             "avg_launch_ms": avg_launch_ms,
             "launches": launches,

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <cstdarg>
@@ -62,6 +63,8 @@ struct ersj_index {
     int32_t d = 0, nb = 0;
     double eps = 0.0, e64 = 0.0;
     float tlo = 0.0f, thi = 0.0f;
+    float kp = 1.0f, km = 1.0f;
+    double maxabs = 0.0;
     GridParams gp{};
     std::vector<int32_t> perm, pinv;
 
@@ -227,6 +230,43 @@ void thresholds(ersj_index *h)
     else h->tlo = round_down_f32(E * (1.0 - delta));
 }
 
+// MFMA refinement: dot products of tile-centred coordinates.  Usable when
+// the centred values cannot overflow fp32 (|x'| <= 2 max|x| per coordinate,
+// norms and dots <= 4 d_pad max|x|^2, kept below FLT_MAX / 16) and the
+// query tile fits the LDS.  Band: K = 4 (d_pad + 8) u, twice the
+// 2.02 gamma(d_pad + 2) + 6.1 u that the error analysis needs.
+bool mfma_feasible(const ersj_index *h, const char **why)
+{
+    const double dp = 4.0 * h->nb;
+    if (refine_mfma_lds_bytes(h->nb) > 160 * 1024) {
+        *why = "query tile exceeds the 160 KiB LDS (d too large)";
+        return false;
+    }
+    if (16.0 * dp * h->maxabs * h->maxabs >= 1e38) {
+        *why = "coordinates too large for fp32 norms";
+        return false;
+    }
+    return true;
+}
+
+int choose_kernel(ersj_index *h)
+{
+    const char *why = "";
+    const bool ok = mfma_feasible(h, &why);
+    int k = h->opt.refine_kernel;
+    if (k == ERSJ_REFINE_MFMA && !ok)
+        return fail(ERSJ_ERR_INVALID_ARG, "MFMA refinement not usable for this input: %s", why);
+    if (k == ERSJ_REFINE_AUTO) k = ok ? ERSJ_REFINE_MFMA : ERSJ_REFINE_DIRECT;
+    h->kernel_used = k;
+    if (k == ERSJ_REFINE_MFMA) {
+        const double K = 4.0 * (4.0 * h->nb + 8.0) * std::ldexp(1.0, -24);
+        h->kp = (float)(1.0 + K);
+        h->km = (float)(1.0 - K);
+        HIPC(prepare_refine_mfma(h->nb), "MFMA kernel LDS attribute");
+    }
+    return ERSJ_OK;
+}
+
 int sync(hipStream_t s, const char *what)
 {
     HIPC(hipStreamSynchronize(s), what);
@@ -297,6 +337,9 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     HIPC(hipMemcpyAsync(&hbad, bad, sizeof hbad, hipMemcpyDeviceToHost, s), "stats copy");
     TRY(sync(s, "stats"));
     if (hbad) return fail(ERSJ_ERR_INVALID_ARG, "input holds %llu non-finite coordinates", hbad);
+    h->maxabs = 0.0;
+    for (int k = 0; k < d; ++k)
+        h->maxabs = std::max(h->maxabs, std::max(std::fabs(hst[k * 4 + 2]), std::fabs(hst[k * 4 + 3])));
 
     // A2: dimensions by descending variance (ties: lower id first); the first
     // three are the grid axes.  Cell width >= eps*(1 + 2^-20), widened so no
@@ -373,6 +416,7 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     HIPC(launch_cell_aabb(h->xs, cid, n, (int64_t)M, h->lo_bits, h->hi_bits, s), "cell boxes");
     TRY(sync(s, "build"));
     thresholds(h);
+    TRY(choose_kernel(h));
     return ERSJ_OK;
 }
 
@@ -493,6 +537,20 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
     return ERSJ_OK;
 }
 
+// Boundary-list entries to start with: the caller's choice, else a share of
+// the batch's candidates, raised to the largest list a previous overflow in
+// this process needed (so repeated joins of similar data refine once).
+std::atomic<uint64_t> g_bcap_hint{0};
+
+uint64_t initial_bcap(const ersj_index *h)
+{
+    if (h->opt.boundary_capacity) return h->opt.boundary_capacity;
+    uint64_t maxc = 0;
+    for (int32_t b = 0; b < h->nbatch; ++b) maxc = std::max(maxc, h->hcands[b + 1] - h->hcands[b]);
+    uint64_t cap = std::min<uint64_t>(std::max<uint64_t>(maxc / 4096, 1ull << 20), 1ull << 27);
+    return std::max(cap, g_bcap_hint.load());
+}
+
 int ensure_fill_buffers(ersj_index *h)
 {
     if (h->mask_cap < h->maxw) {
@@ -513,7 +571,7 @@ int ensure_fill_buffers(ersj_index *h)
     }
     if (!h->counters) TRY(dalloc(h, &h->counters, 2, "counters"));
     if (!h->blist) {
-        uint64_t cap = h->opt.boundary_capacity ? h->opt.boundary_capacity : (1ull << 20);
+        const uint64_t cap = initial_bcap(h);
         TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
         h->bcap = cap;
     }
@@ -534,10 +592,15 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.order = h->order;
     a.ord0 = t0;
     a.ntiles = ntiles;
+    const bool mfma = h->kernel_used == ERSJ_REFINE_MFMA;
+    // row sub-blocks: the direct kernel covers 32 rows per work item, the
+    // MFMA kernel 32 per query block it holds
+    a.nsub = (uint32_t)(kTileRows / (mfma ? 32 * refine_mfma_qblocks(h->nb) : 32));
+    const uint64_t rows_items = (uint64_t)ntiles * a.nsub;
     uint32_t seg = 8192;
     auto nseg_of = [&](uint32_t sl) { return (h->umax + sl - 1) / sl; };
-    while (seg > 256 && (uint64_t)ntiles * nseg_of(seg) < 8192) seg /= 2;
-    while ((uint64_t)ntiles * nseg_of(seg) > 0x7fffffffull) seg *= 2;
+    while (seg > 512 && rows_items * nseg_of(seg) < 8192) seg /= 2;
+    while (rows_items * nseg_of(seg) > 0x7fffffffull) seg *= 2;
     a.seg_len = seg;
     a.nseg = std::max<uint32_t>(1, nseg_of(seg));
     a.rstart = h->rstart;
@@ -548,6 +611,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.mask = h->mask;
     a.tlo = h->tlo;
     a.thi = h->thi;
+    a.kp = h->kp;
+    a.km = h->km;
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
         a.blist = h->blist;
@@ -555,7 +620,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
         a.bcap = h->bcap;
         HIPC(launch_fill_u64((uint64_t *)h->counters, 0, 2, s), "clear counters");
         timer_start(h, s);
-        HIPC(launch_refine_direct(a, s), "refine kernel");
+        HIPC(mfma ? launch_refine_mfma(a, s) : launch_refine_direct(a, s), "refine kernel");
         h->ms_refine += timer_stop(h, s);
         if (h->opt.timing) {
             h->refine_launches += 1;
@@ -571,6 +636,11 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
         const uint64_t cap = bcount + bcount / 4 + 1024;
         TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
         h->bcap = cap;
+        if (!h->opt.boundary_capacity) {
+            uint64_t cur = g_bcap_hint.load();
+            while (cur < cap && !g_bcap_hint.compare_exchange_weak(cur, cap)) {
+            }
+        }
     }
     if (bcount > h->bcap) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
@@ -646,8 +716,6 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
         if (o.refine_kernel < ERSJ_REFINE_AUTO || o.refine_kernel > ERSJ_REFINE_MFMA)
             return fail(ERSJ_ERR_INVALID_ARG, "unknown refine_kernel %d", o.refine_kernel);
     }
-    if (o.refine_kernel == ERSJ_REFINE_MFMA)
-        return fail(ERSJ_ERR_INVALID_ARG, "the MFMA refinement kernel is not available in this build");
     int dev = 0;
     HIPC(hipGetDevice(&dev), "hipGetDevice");
     ersj_index *h = new ersj_index();

@@ -19,7 +19,7 @@
 
 namespace ersj {
 
-constexpr int kTileRows = 32;   // query rows per row tile
+constexpr int kTileRows = 128;  // query rows per row tile
 constexpr int kMaxRanges = 27;  // 3x3x3 stencil
 constexpr int kMaxDim = 4096;
 
@@ -100,7 +100,38 @@ hipError_t launch_order_keys(const Tile *tiles, const uint32_t *rpref, const uin
 
 hipError_t launch_fill_u64(uint64_t *p, uint64_t v, int64_t n, hipStream_t s);
 
-// ---- refinement (k_refine.hip) ----
+// ---- refinement (k_refine.hip, k_refine_mfma.hip) ----
+
+// Work item of refinement block b among ntiles * ncol: (tile rank, column),
+// where a column is a (candidate segment, row sub-block) pair.
+// Items come in groups of kGroupTiles consecutive tile ranks, segment-major
+// inside a group, so consecutive items read the same candidate segment.
+// Blocks are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8);
+// the remap hands each XCD runs of kXcdRun consecutive items, so one
+// segment is fetched into one XCD's L2 and reused by kGroupTiles tiles.
+constexpr uint32_t kGroupTiles = 16;
+constexpr uint32_t kXcdRun = 16;
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ void work_item(uint32_t b, uint32_t ntiles, uint32_t nseg, uint32_t *rank,
+                                          uint32_t *seg)
+{
+    const uint64_t B = (uint64_t)ntiles * nseg;  // nseg here counts columns
+    const uint64_t span = (uint64_t)kXcds * kXcdRun;
+    const uint64_t full = B / span * span;
+    uint64_t i = b;
+    if (i < full) {
+        const uint64_t x = i % kXcds, j = i / kXcds;
+        i = (j / kXcdRun) * span + x * kXcdRun + (j % kXcdRun);
+    }
+    const uint64_t gsz = (uint64_t)kGroupTiles * nseg;
+    const uint64_t g = i / gsz, within = i - g * gsz;
+    const uint64_t r0 = g * kGroupTiles;
+    const uint64_t rg = ntiles - r0 < kGroupTiles ? ntiles - r0 : kGroupTiles;
+    *seg = (uint32_t)(within / rg);
+    *rank = (uint32_t)(r0 + within % rg);
+}
+
 struct RefineArgs {
     const float4 *xs;
     uint64_t n;
@@ -110,7 +141,8 @@ struct RefineArgs {
     uint32_t ord0;       // first entry of `order` for this batch
     uint32_t ntiles;     // tiles in this batch
     uint32_t nseg;       // candidate segments per tile
-    uint32_t seg_len;    // candidates per segment (multiple of 256)
+    uint32_t seg_len;    // candidates per segment (multiple of 512)
+    uint32_t nsub;       // row sub-blocks per tile (one work item each)
     const uint32_t *rstart;
     const uint32_t *rpref;
     const uint32_t *nrng;
@@ -118,11 +150,18 @@ struct RefineArgs {
     uint64_t wbase;      // first mask word of the batch
     uint64_t *mask;
     float tlo, thi;      // fp32 classification thresholds
+    float kp, km;        // 1 + K and 1 - K of the MFMA kernel's norm-proportional band
     Boundary *blist;
     unsigned long long *bcount;
     uint64_t bcap;
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
+
+// k_refine_mfma.hip: query blocks of 32 rows per work item (4, 2 or 1)
+int refine_mfma_qblocks(int nb);
+size_t refine_mfma_lds_bytes(int nb);
+hipError_t prepare_refine_mfma(int nb);
+hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
 hipError_t launch_recheck(const Boundary *bl, uint64_t cnt, const float4 *xs, uint64_t n,

@@ -5,9 +5,9 @@
 // sharing the same candidates; coordinates read dimension-major) and
 // Sec. IV-F (one result bit per query/candidate comparison).
 //
-// Work item: (row tile of up to 32 queries of one cell, segment of the
-// cell's candidate list).  A 256-thread workgroup holds 4 waves; wave w owns
-// queries 8w..8w+7 of the tile.  Lane l of a wave owns candidates
+// Work item: (32 rows of a row tile of one cell, segment of the cell's
+// candidate list).  A 256-thread workgroup holds 4 waves; wave w owns
+// queries 8w..8w+7 of those 32 rows.  Lane l of a wave owns candidates
 // c + l + 64j (j = 0..3) of each 256-candidate chunk, so one wave ballot of a
 // comparison yields exactly one 64-bit mask word: bit l <-> candidate
 // 64*word + l.  Query coordinates are wave-uniform (scalar loads); candidate
@@ -34,10 +34,14 @@ constexpr int kChunk = 64 * kCW;
 
 __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
 {
-    const uint32_t wg = blockIdx.x;
-    const uint32_t rk = wg / a.nseg, seg = wg - rk * a.nseg;
+    uint32_t rk, colx;
+    work_item(blockIdx.x, a.ntiles, a.nseg * a.nsub, &rk, &colx);
+    const uint32_t seg = colx / a.nsub, sub = colx - seg * a.nsub;
     const uint32_t t = a.order[a.ord0 + rk];
     const Tile tl = a.tiles[t];
+    const uint32_t r_begin = sub * 32;  // rows of this work item: 32 from r_begin
+    if (r_begin >= tl.nrows) return;
+    const uint32_t srows = min(32u, tl.nrows - r_begin);
     const uint32_t A = tl.cell;
     const uint32_t nr = a.nrng[A];
     const uint32_t *pref_g = a.rpref + (uint64_t)A * (kMaxRanges + 1);
@@ -56,12 +60,12 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const uint32_t kq0 = wave * kQW;
-    if (kq0 >= tl.nrows) return;
+    if (kq0 >= srows) return;
     uint32_t qrow[kQW];
 #pragma unroll
-    for (int k = 0; k < kQW; ++k) qrow[k] = tl.row0 + min(kq0 + k, tl.nrows - 1);
-    const uint32_t nq = min((uint32_t)kQW, tl.nrows - kq0);
-    const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)kq0 * tl.words;
+    for (int k = 0; k < kQW; ++k) qrow[k] = tl.row0 + r_begin + min(kq0 + k, srows - 1);
+    const uint32_t nq = min((uint32_t)kQW, srows - kq0);
+    const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)(r_begin + kq0) * tl.words;
     const uint64_t n = a.n;
     const float4 *__restrict__ xs = a.xs;
     uint64_t *__restrict__ mask = a.mask;
@@ -154,7 +158,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
 
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s)
 {
-    const uint64_t blocks = (uint64_t)a.ntiles * a.nseg;
+    const uint64_t blocks = (uint64_t)a.ntiles * a.nseg * a.nsub;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_refine_direct, dim3((unsigned)blocks), dim3(256), 0, s, a);

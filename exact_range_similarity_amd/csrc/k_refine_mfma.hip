@@ -1,0 +1,449 @@
+// Candidate refinement for gfx950 with the dot products on MFMA.
+//
+// Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+// Similarity Searches", Sec. IV-E (a thread block per group of queries that
+// share their candidates; query and candidate tiles staged in on-chip
+// memory, stored dimension-major) and Sec. IV-F (one result bit per
+// comparison).
+//
+// Squared distances are formed as |q'|^2 + |x'|^2 - 2 q'.x' on coordinates
+// centred on the work item's first query r (q' = q - r, x' = x - r, fp32),
+// with q'.x' from v_mfma_f32_32x32x2f32.
+//
+// Work item: (row tile, candidate segment, row sub-block).  The 256-thread
+// workgroup holds QB query blocks of 32 rows (QB = 4, 2 or 1 with growing
+// d, to fit the query tile in LDS) and 4/QB candidate groups; wave w owns
+// query block w % QB and candidate group w / QB and computes a 32 x 64
+// block per step (two 32x32 accumulators) = one 64-bit mask word per row.
+// A step covers 256/QB candidates; candidates are staged through LDS in
+// slabs of 16 dimensions (double-buffered, loaded one slab ahead, centred
+// and squared once by the loading thread) and read by all QB query blocks.
+//
+// MFMA operands: lanes 0-31 carry dimension block 2s, lanes 32-63 block
+// 2s+1 of the same query/candidate (column = lane % 32); the four components
+// of a float4 feed four k = 2 steps.  The output element of register v in
+// lane l is (row 8*(v/4) + 4*(l/32) + v%4, column l%32).
+//
+// Classification with a norm-proportional band.  With Nq = |q'|^2,
+// Nx = |x'|^2, D = q'.x' (fp32, any summation order) and K = kp - 1:
+//   in   iff  fma(-2, D, kp*Nx) <= tlo - kp*Nq
+//   out  iff  fma(-2, D, km*Nx) >  thi - km*Nq          (km = 1 - K)
+//   else boundary -> exact binary64 re-check.
+// K >= 2.02*gamma(d_pad+2) + 6.1u covers the rounding of the centring, of
+// the norms and dot products, and of these fp32 expressions, so "in" implies
+// D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The host bounds the
+// coordinates so that nothing here overflows; NaN never classifies.
+//
+// Overlap: a step's classification runs in the first slab of the next step,
+// right after that slab's MFMAs are issued, so the vector and scalar
+// instructions co-issue with the matrix pipe.  Mask words collect in LDS and
+// leave as 64-byte row pieces every 512 candidates.
+#include "ersj_internal.h"
+
+#include <utility>
+
+namespace ersj {
+
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
+constexpr int kNB = 4;            // step buffers for norms / candidate ids
+constexpr int kGroupCands = 512;  // candidates per mask-word flush
+
+// Write a wave-uniform 32-bit value into lane L of a VGPR (v_writelane_b32;
+// the lane is an inline constant, the value the one allowed SGPR operand).
+template <int L>
+__device__ __forceinline__ int write_lane(int old, uint32_t val)
+{
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(val), "i"(L));
+    return old;
+}
+
+template <int... E, typename F>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, E...>, F &&f)
+{
+    (f(std::integral_constant<int, E>{}), ...);
+}
+
+__device__ __forceinline__ float4 sub4(float4 a, float4 b)
+{
+    return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+}
+
+template <int QB>
+struct Geometry {
+    static constexpr int NCG = 4 / QB;            // candidate groups
+    static constexpr int QR = 32 * QB;            // query rows per work item
+    static constexpr int SC = 64 * NCG;           // candidates per step
+    static constexpr int SPG = kGroupCands / SC;  // steps per mask-word group
+};
+
+template <int QB>
+struct Lds {
+    float4 *q;          // [nbs][QR] centred queries
+    float4 *r;          // [nbs] reference point
+    float4 *x;          // [2][kSlab][SC] centred candidate slab
+    float *nxp;         // [kNB][kSlab][SC] partial candidate norms of a step
+    uint32_t *xi;       // [kNB][SC] candidate point index of a step
+    float *qin, *qout;  // [QR]
+    uint64_t *words;    // [2][QR][8]
+    uint32_t *pref, *start;
+};
+
+template <int QB>
+size_t lds_bytes(int nbs)
+{
+    using G = Geometry<QB>;
+    return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
+           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)2 * G::QR * 8 * 8 + (2 * kMaxRanges + 1) * 4;
+}
+
+template <int QB>
+__device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
+{
+    using G = Geometry<QB>;
+    Lds<QB> L;
+    L.q = smem;
+    L.r = L.q + nbs * G::QR;
+    L.x = L.r + nbs;
+    L.nxp = (float *)(L.x + 2 * kSlab * G::SC);
+    L.xi = (uint32_t *)(L.nxp + kNB * kSlab * G::SC);
+    L.qin = (float *)(L.xi + kNB * G::SC);
+    L.qout = L.qin + G::QR;
+    L.words = (uint64_t *)(L.qout + G::QR);
+    L.pref = (uint32_t *)(L.words + 2 * G::QR * 8);
+    L.start = L.pref + (kMaxRanges + 1);
+    return L;
+}
+
+template <int QB>
+__global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs a)
+{
+    using G = Geometry<QB>;
+    uint32_t rk, colx;
+    work_item(blockIdx.x, a.ntiles, a.nseg * a.nsub, &rk, &colx);
+    const uint32_t seg = colx / a.nsub, sub = colx - seg * a.nsub;
+    const uint32_t t = a.order[a.ord0 + rk];
+    const Tile tl = a.tiles[t];
+    const uint32_t r_begin = sub * G::QR;
+    if (r_begin >= tl.nrows) return;
+    const uint32_t A = tl.cell;
+    const uint32_t nr = a.nrng[A];
+    const uint32_t *pref_g = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+    const uint32_t U = pref_g[nr];
+    const uint32_t c_begin = seg * a.seg_len;
+    if (c_begin >= U) return;
+    const uint32_t c_end = min(U, c_begin + a.seg_len);
+    const uint32_t nrows = min((uint32_t)G::QR, tl.nrows - r_begin);
+    const uint32_t row0 = tl.row0 + r_begin;
+    const int nb = a.nb;
+    const int nslab = (nb + kSlab - 1) / kSlab;
+    const int nbs = nslab * kSlab;
+
+    extern __shared__ float4 smem[];
+    const Lds<QB> L = carve<QB>(smem, nbs);
+
+    const int tid = threadIdx.x;
+    const uint64_t n = a.n;
+    const float4 *__restrict__ xs = a.xs;
+    uint64_t *__restrict__ mask = a.mask;
+    Boundary *__restrict__ blist = a.blist;
+    unsigned long long *__restrict__ bcount = a.bcount;
+    const uint32_t W = tl.words;
+    const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)r_begin * W;
+
+    if (tid <= kMaxRanges) L.pref[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
+    if (tid < kMaxRanges) L.start[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
+    for (int b = tid; b < nbs; b += 256)
+        L.r[b] = b < nb ? xs[(uint64_t)b * n + row0] : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    for (int e = tid; e < nbs * G::QR; e += 256) {
+        const int b = e / G::QR, i = e - b * G::QR;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (b < nb && (uint32_t)i < nrows) v = sub4(xs[(uint64_t)b * n + row0 + i], L.r[b]);
+        L.q[e] = v;
+    }
+    __syncthreads();
+    for (int i = tid; i < G::QR; i += 256) {
+        float nq = 0.f;
+        for (int b = 0; b < nb; ++b) {
+            const float4 v = L.q[b * G::QR + i];
+            nq = fmaf(v.x, v.x, nq);
+            nq = fmaf(v.y, v.y, nq);
+            nq = fmaf(v.z, v.z, nq);
+            nq = fmaf(v.w, v.w, nq);
+        }
+        const bool live = (uint32_t)i < nrows;
+        L.qin[i] = live ? a.tlo - a.kp * nq : -INFINITY;
+        L.qout[i] = live ? a.thi - a.km * nq : -INFINITY;
+    }
+    __syncthreads();
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 31, hi = lane >> 5;
+    const int qb = wave % QB, cg = wave / QB;
+    const bool active = (uint32_t)(qb * 32) < nrows;  // wave-uniform
+    float qin[16], qout[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int i = qb * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
+        qin[v] = L.qin[i];
+        qout[v] = L.qout[i];
+    }
+    const float kp = a.kp, km = a.km;
+    const uint64_t bcap = a.bcap;
+    const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
+    const uint32_t K = nsteps * (uint32_t)nslab;
+
+    // loader: element m of this thread is (block j = e / SC, candidate c = e % SC), e = tid + 256 m
+    auto cand_index = [&](uint32_t step, int c) -> uint32_t {
+        const uint32_t p = c_begin + step * G::SC + c;
+        const uint32_t pp = p < c_end ? p : c_begin;
+        int g = 0;
+        while (g + 1 < (int)nr && pp >= L.pref[g + 1]) ++g;
+        return L.start[g] + (pp - L.pref[g]);
+    };
+    uint32_t lxi[G::NCG];
+    auto set_cands = [&](uint32_t step) {
+#pragma unroll
+        for (int m = 0; m < G::NCG; ++m) lxi[m] = cand_index(step, (tid + 256 * m) % G::SC);
+    };
+    float4 ld[G::NCG];
+    auto load_slab = [&](int sl) {
+#pragma unroll
+        for (int m = 0; m < G::NCG; ++m) {
+            const int e = tid + 256 * m;
+            const int b = sl * kSlab + e / G::SC;
+            ld[m] = b < nb ? xs[(uint64_t)b * n + lxi[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+
+    set_cands(0);
+    load_slab(0);
+    float nxp[G::NCG];
+#pragma unroll
+    for (int m = 0; m < G::NCG; ++m) nxp[m] = 0.f;
+    floatx16 accC[2], accP[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            accC[tt][v] = 0.f;
+            accP[tt][v] = 0.f;
+        }
+    int pend_group = -1;
+
+    // classification of step s (accumulators in acc): mask words and band pairs
+    auto epilogue = [&](uint32_t s, const floatx16 *acc) {
+        const uint32_t cw = c_begin + s * G::SC + cg * 64;
+        float xin[2], xout[2];
+        uint64_t vmask[2];
+        uint32_t xid[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int cl = cg * 64 + 32 * tt + col;
+            const float *np = L.nxp + (s % kNB) * (kSlab * G::SC);
+            const float nxt = ((np[cl] + np[G::SC + cl]) + np[2 * G::SC + cl]) + np[3 * G::SC + cl];
+            xid[tt] = L.xi[(s % kNB) * G::SC + cl];
+            xin[tt] = kp * nxt;
+            xout[tt] = km * nxt;
+            vmask[tt] = __ballot(cw + 32 * tt + col < c_end);
+        }
+        int wlo = 0, whi = 0;
+        uint64_t anyb = 0;
+        static_for(std::make_integer_sequence<int, 32>{}, [&](auto E) {
+            constexpr int tt = decltype(E)::value / 16, v = decltype(E)::value % 16;
+            constexpr int i0 = (v / 4) * 8 + (v % 4);
+            const float dd = acc[tt][v];
+            const float v1 = fmaf(-2.0f, dd, xin[tt]);
+            const float v2 = fmaf(-2.0f, dd, xout[tt]);
+            const uint64_t bin = __ballot(v1 <= qin[v]) & vmask[tt];
+            const uint64_t bno = __ballot(v2 <= qout[v]) & vmask[tt];
+            anyb |= bno & ~bin;
+            if (tt == 0) {
+                wlo = write_lane<i0>(wlo, (uint32_t)bin);
+                wlo = write_lane<i0 + 4>(wlo, (uint32_t)(bin >> 32));
+            } else {
+                whi = write_lane<i0>(whi, (uint32_t)bin);
+                whi = write_lane<i0 + 4>(whi, (uint32_t)(bin >> 32));
+            }
+        });
+        if (anyb != 0) {
+            // rare: redo the classification for the band pairs and append
+            // them for the binary64 re-check
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float dd = acc[tt][v];
+                    asm volatile("" : "+v"(dd));  // recompute, do not keep masks alive
+                    const bool in = fmaf(-2.0f, dd, xin[tt]) <= qin[v];
+                    const bool nout = fmaf(-2.0f, dd, xout[tt]) <= qout[v];
+                    const bool bd = ((vmask[tt] >> lane) & 1ull) && !in && nout;
+                    const uint64_t bbd = __ballot(bd);
+                    if (bbd == 0) continue;
+                    const uint32_t cnt = __popcll(bbd);
+                    const int first = __ffsll((unsigned long long)bbd) - 1;
+                    unsigned long long base = 0;
+                    if (lane == first) base = atomicAdd(bcount, (unsigned long long)cnt);
+                    base = __shfl(base, first, 64);
+                    if (bd) {
+                        const uint64_t below = lane == 0 ? 0ull : (bbd & (~0ull >> (64 - lane)));
+                        const uint64_t idx = base + __popcll(below);
+                        const uint32_t row = qb * 32 + (v >> 2) * 8 + (v & 3) + 4 * hi;
+                        if (idx < bcap) {
+                            Boundary e;
+                            e.q = row0 + row;
+                            e.x = xid[tt];
+                            e.bit = (mbase + (uint64_t)row * W) * 64 + cw + 32 * tt + col;
+                            blist[idx] = e;
+                        }
+                    }
+                }
+            }
+        }
+        const uint32_t grp = s / G::SPG;
+        if (lane < 32)
+            L.words[(grp & 1) * (G::QR * 8) + (qb * 32 + lane) * 8 + (s % G::SPG) * G::NCG + cg] =
+                ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
+    };
+    auto flush = [&](uint32_t grp) {
+        const uint64_t *sw = L.words + (grp & 1) * (G::QR * 8);
+        for (int e = tid; e < G::QR * 8; e += 256) {
+            const int row = e >> 3, j = e & 7;
+            const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
+            const uint32_t w = c0 >> 6;
+            if ((uint32_t)row < nrows && w < W && c0 < c_end) mask[mbase + (uint64_t)row * W + w] = sw[e];
+        }
+    };
+    auto mfma_slab = [&](const float4 *xb, int sl) {
+#pragma unroll
+        for (int s2 = 0; s2 < kSlab / 2; ++s2) {
+            const int jj = 2 * s2 + hi;
+            const float4 av = L.q[(sl * kSlab + jj) * G::QR + qb * 32 + col];
+            const float4 b0 = xb[jj * G::SC + cg * 64 + col];
+            const float4 b1 = xb[jj * G::SC + cg * 64 + 32 + col];
+            accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, accC[0], 0, 0, 0);
+            accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, accC[1], 0, 0, 0);
+            accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b0.y, accC[0], 0, 0, 0);
+            accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1.y, accC[1], 0, 0, 0);
+            accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b0.z, accC[0], 0, 0, 0);
+            accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b1.z, accC[1], 0, 0, 0);
+            accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b0.w, accC[0], 0, 0, 0);
+            accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, b1.w, accC[1], 0, 0, 0);
+        }
+    };
+
+    for (uint32_t k = 0; k < K; ++k) {
+        const uint32_t step = k / nslab;
+        const int sl = (int)(k - step * nslab);
+        float4 *xb = L.x + (k & 1) * (kSlab * G::SC);
+        // stage the slab: centre on r, accumulate partial norms
+#pragma unroll
+        for (int m = 0; m < G::NCG; ++m) {
+            const int e = tid + 256 * m;
+            const int j = e / G::SC;
+            const float4 c4 = sub4(ld[m], L.r[sl * kSlab + j]);
+            float s2 = nxp[m];
+            s2 = fmaf(c4.x, c4.x, s2);
+            s2 = fmaf(c4.y, c4.y, s2);
+            s2 = fmaf(c4.z, c4.z, s2);
+            s2 = fmaf(c4.w, c4.w, s2);
+            nxp[m] = s2;
+            xb[e] = c4;
+        }
+        if (sl == nslab - 1) {
+#pragma unroll
+            for (int m = 0; m < G::NCG; ++m) {
+                const int e = tid + 256 * m;
+                L.nxp[(step % kNB) * (kSlab * G::SC) + e] = nxp[m];
+                if (e < G::SC) L.xi[(step % kNB) * G::SC + e] = lxi[m];
+                nxp[m] = 0.f;
+            }
+        }
+        __syncthreads();
+        if (pend_group >= 0) {
+            flush((uint32_t)pend_group);
+            pend_group = -1;
+        }
+        if (k + 1 < K) {
+            const int sln = sl + 1 == nslab ? 0 : sl + 1;
+            if (sln == 0) set_cands(step + 1);
+            load_slab(sln);
+        }
+        if (sl == 0) {
+            accP[0] = accC[0];
+            accP[1] = accC[1];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) accC[tt][v] = 0.f;
+        }
+        if (active) {
+            mfma_slab(xb, sl);
+            if (sl == 0 && step > 0) {
+                epilogue(step - 1, accP);
+                // interleave: one MFMA, then vector and scalar work of the epilogue
+                static_for(std::make_integer_sequence<int, 2 * kSlab>{}, [&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x004, 6, 0);
+                });
+            }
+        }
+        if (sl == 0 && step > 0 && ((step - 1) % G::SPG == G::SPG - 1)) pend_group = (int)((step - 1) / G::SPG);
+    }
+    if (active) epilogue(nsteps - 1, accC);
+    __syncthreads();
+    if (pend_group >= 0) flush((uint32_t)pend_group);
+    flush((nsteps - 1) / G::SPG);
+}
+
+}  // namespace
+
+int refine_mfma_qblocks(int nb)
+{
+    const int nbs = (nb + kSlab - 1) / kSlab * kSlab;
+    if (lds_bytes<4>(nbs) <= 64 * 1024) return 4;
+    if (lds_bytes<2>(nbs) <= 80 * 1024) return 2;
+    return 1;
+}
+
+size_t refine_mfma_lds_bytes(int nb)
+{
+    const int nbs = (nb + kSlab - 1) / kSlab * kSlab;
+    switch (refine_mfma_qblocks(nb)) {
+    case 4: return lds_bytes<4>(nbs);
+    case 2: return lds_bytes<2>(nbs);
+    default: return lds_bytes<1>(nbs);
+    }
+}
+
+hipError_t prepare_refine_mfma(int nb)
+{
+    const int bytes = (int)refine_mfma_lds_bytes(nb);
+    switch (refine_mfma_qblocks(nb)) {
+    case 4: return hipFuncSetAttribute((const void *)k_refine_mfma<4>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    case 2: return hipFuncSetAttribute((const void *)k_refine_mfma<2>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    default: return hipFuncSetAttribute((const void *)k_refine_mfma<1>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    }
+}
+
+hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s)
+{
+    const uint64_t blocks = (uint64_t)a.ntiles * a.nseg * a.nsub;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    const size_t bytes = refine_mfma_lds_bytes(a.nb);
+    switch (refine_mfma_qblocks(a.nb)) {
+    case 4: hipLaunchKernelGGL(k_refine_mfma<4>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
+    case 2: hipLaunchKernelGGL(k_refine_mfma<2>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
+    default: hipLaunchKernelGGL(k_refine_mfma<1>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace ersj

@@ -52,9 +52,18 @@ def assert_same_pairs(X, eps, got, want, label=""):
     raise AssertionError(f"{label}: |gpu|={sg.size} |oracle|={sw.size}\n" + "\n".join(lines))
 
 
-def check_against_oracle(X, eps, label="", **kw):
-    say(f"[gpu] {label}: n={X.shape[0]} d={X.shape[1]} eps={eps!r}")
-    got = gpu_pairs(X, eps, **kw)
+KERNELS = (ersj.REFINE_DIRECT, ersj.REFINE_MFMA)
+
+
+def check_against_oracle(X, eps, label="", kernels=KERNELS, **kw):
+    """Both refinement kernels must return exactly the oracle's pair set."""
     want = oracle.selfjoin_pairs(X, eps)
-    assert_same_pairs(X, eps, got, want, label)
+    got = None
+    base = kw.pop("options", None)
+    for k in kernels:
+        say(f"[gpu] {label}: n={X.shape[0]} d={X.shape[1]} eps={eps!r} kernel={k}")
+        opts = ersj.Options.from_buffer_copy(base) if base is not None else ersj.default_options()
+        opts.refine_kernel = k
+        got = gpu_pairs(X, eps, options=opts, **kw)
+        assert_same_pairs(X, eps, got, want, f"{label} kernel={k}")
     return got

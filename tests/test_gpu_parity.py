@@ -90,8 +90,9 @@ def test_eps_zero_duplicates_and_identical_points():
 def test_eps_infinite_and_huge():
     rng = np.random.default_rng(6)
     X = rng.random((700, 9), dtype=np.float32)
-    got = gpu_pairs(X, math.inf)
-    assert got.shape[0] == 700 * 700
+    for k in (ersj.REFINE_DIRECT, ersj.REFINE_MFMA):
+        got = gpu_pairs(X, math.inf, options=ersj.default_options(refine_kernel=k))
+        assert got.shape[0] == 700 * 700
     check_against_oracle(X, 1e30, "eps huge")
     check_against_oracle(X, 1e-30, "eps tiny")
 
@@ -107,8 +108,7 @@ def test_wide_value_ranges():
 def test_strided_rows():
     rng = np.random.default_rng(8)
     X = rng.random((1500, 13), dtype=np.float32)
-    got = gpu_pairs(X, 0.45, ld=16)
-    assert_same_pairs(X, 0.45, got, oracle.selfjoin_pairs(X, 0.45), "ld=16")
+    check_against_oracle(X, 0.45, "ld=16", ld=16)
 
 
 def test_fig3_structure():
@@ -126,6 +126,19 @@ def test_fig5_compaction():
     got = gpu_pairs(fig5_points(), 1.0)
     row = sorted(int(j) for i, j in got.tolist() if i == g["query"])
     assert row == g["compressed"]
+
+
+def test_large_d_and_offset_data():
+    rng = np.random.default_rng(12)
+    X = (rng.random((700, 700)) + 5.0).astype(np.float32)
+    check_against_oracle(X, 10.5, "d=700 offset")
+    Z = (rng.random((300, 2000)) + 5.0).astype(np.float32)
+    check_against_oracle(Z, 17.0, "d=2000 offset", kernels=(ersj.REFINE_DIRECT,))
+    h = ersj.build_index(torch.from_numpy(Z).cuda(), 17.0)
+    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_DIRECT
+    h.free()
+    Y = (rng.standard_normal((2000, 40)) * 0.01 + 100.0).astype(np.float32)
+    check_against_oracle(Y, 0.085, "offset cluster")
 
 
 def test_multi_batch_equals_single_batch():
@@ -204,12 +217,31 @@ def test_non_finite_input_rejected():
     assert e.value.code == ersj.ERR_INVALID_ARG
 
 
-def test_boundary_list_overflow_regrows():
+@pytest.mark.parametrize("kernel", [ersj.REFINE_DIRECT, ersj.REFINE_MFMA])
+def test_boundary_list_overflow_regrows(kernel):
     X = lattice(9, 3)
-    opts = ersj.default_options(boundary_capacity=16)
-    say("[gpu] lattice with a 16-entry boundary list")
+    opts = ersj.default_options(boundary_capacity=16, refine_kernel=kernel)
+    say(f"[gpu] lattice with a 16-entry boundary list, kernel={kernel}")
     got = gpu_pairs(X, 1.0, options=opts)
     assert_same_pairs(X, 1.0, got, oracle.selfjoin_pairs(X, 1.0), "blist regrow")
+
+
+def test_kernel_choice():
+    rng = np.random.default_rng(11)
+    X = rng.random((500, 6), dtype=np.float32)
+    xt = torch.from_numpy(X).cuda()
+    for k in (ersj.REFINE_AUTO, ersj.REFINE_DIRECT, ersj.REFINE_MFMA):
+        h = ersj.build_index(xt, 0.3, ersj.default_options(refine_kernel=k))
+        used = ersj.get_stats(h)["refine_kernel"]
+        h.free()
+        assert used == (ersj.REFINE_MFMA if k == ersj.REFINE_AUTO else k)
+    big = (X * 1e18).astype(np.float32)
+    with pytest.raises(ersj.ErsjError) as e:
+        ersj.build_index(torch.from_numpy(big).cuda(), 1e18, ersj.default_options(refine_kernel=ersj.REFINE_MFMA))
+    assert e.value.code == ersj.ERR_INVALID_ARG
+    h = ersj.build_index(torch.from_numpy(big).cuda(), 1e18)
+    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_DIRECT
+    h.free()
 
 
 def test_deterministic_output_order():
