@@ -34,10 +34,10 @@
 // D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The host bounds the
 // coordinates so that nothing here overflows; NaN never classifies.
 //
-// Overlap: a step's classification runs in the first slab of the next step,
-// right after that slab's MFMAs are issued, so the vector and scalar
-// instructions co-issue with the matrix pipe.  Mask words collect in LDS and
-// leave as 64-byte row pieces every 512 candidates.
+// A step's classification follows its last slab's MFMAs; the two waves that
+// share a SIMD (two workgroups per CU) overlap one's classification with the
+// other's matrix work.  Mask words collect in LDS and leave as 64-byte row
+// pieces every 512 candidates.
 #include "ersj_internal.h"
 
 #include <utility>
@@ -226,21 +226,13 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
     float nxp[G::NCG];
 #pragma unroll
     for (int m = 0; m < G::NCG; ++m) nxp[m] = 0.f;
-    floatx16 accC[2], accP[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            accC[tt][v] = 0.f;
-            accP[tt][v] = 0.f;
-        }
+    floatx16 accC[2];
     int pend_group = -1;
 
     // classification of step s (accumulators in acc): mask words and band pairs
     auto epilogue = [&](uint32_t s, const floatx16 *acc) {
         const uint32_t cw = c_begin + s * G::SC + cg * 64;
         float xin[2], xout[2];
-        uint64_t vmask[2];
         uint32_t xid[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -248,9 +240,12 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             const float *np = L.nxp + (s % kNB) * (kSlab * G::SC);
             const float nxt = ((np[cl] + np[G::SC + cl]) + np[2 * G::SC + cl]) + np[3 * G::SC + cl];
             xid[tt] = L.xi[(s % kNB) * G::SC + cl];
-            xin[tt] = kp * nxt;
-            xout[tt] = km * nxt;
-            vmask[tt] = __ballot(cw + 32 * tt + col < c_end);
+            // candidates past the segment end never classify: a NaN operand
+            // makes both comparisons false (an infinity would not: with an
+            // infinite eps, inf <= inf holds)
+            const bool valid = cw + 32 * tt + col < c_end;
+            xin[tt] = valid ? kp * nxt : __builtin_nanf("");
+            xout[tt] = valid ? km * nxt : __builtin_nanf("");
         }
         int wlo = 0, whi = 0;
         uint64_t anyb = 0;
@@ -260,8 +255,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             const float dd = acc[tt][v];
             const float v1 = fmaf(-2.0f, dd, xin[tt]);
             const float v2 = fmaf(-2.0f, dd, xout[tt]);
-            const uint64_t bin = __ballot(v1 <= qin[v]) & vmask[tt];
-            const uint64_t bno = __ballot(v2 <= qout[v]) & vmask[tt];
+            const uint64_t bin = __ballot(v1 <= qin[v]);
+            const uint64_t bno = __ballot(v2 <= qout[v]);
             anyb |= bno & ~bin;
             if (tt == 0) {
                 wlo = write_lane<i0>(wlo, (uint32_t)bin);
@@ -282,7 +277,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
                     asm volatile("" : "+v"(dd));  // recompute, do not keep masks alive
                     const bool in = fmaf(-2.0f, dd, xin[tt]) <= qin[v];
                     const bool nout = fmaf(-2.0f, dd, xout[tt]) <= qout[v];
-                    const bool bd = ((vmask[tt] >> lane) & 1ull) && !in && nout;
+                    const bool bd = !in && nout;
                     const uint64_t bbd = __ballot(bd);
                     if (bbd == 0) continue;
                     const uint32_t cnt = __popcll(bbd);
@@ -319,15 +314,21 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             if ((uint32_t)row < nrows && w < W && c0 < c_end) mask[mbase + (uint64_t)row * W + w] = sw[e];
         }
     };
-    auto mfma_slab = [&](const float4 *xb, int sl) {
+    auto mfma_slab = [&](const float4 *xb, int sl, bool fresh) {
 #pragma unroll
         for (int s2 = 0; s2 < kSlab / 2; ++s2) {
             const int jj = 2 * s2 + hi;
             const float4 av = L.q[(sl * kSlab + jj) * G::QR + qb * 32 + col];
             const float4 b0 = xb[jj * G::SC + cg * 64 + col];
             const float4 b1 = xb[jj * G::SC + cg * 64 + 32 + col];
-            accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, accC[0], 0, 0, 0);
-            accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, accC[1], 0, 0, 0);
+            if (s2 == 0 && fresh) {
+                const floatx16 z = {};
+                accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, z, 0, 0, 0);
+                accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, z, 0, 0, 0);
+            } else {
+                accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b0.x, accC[0], 0, 0, 0);
+                accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, b1.x, accC[1], 0, 0, 0);
+            }
             accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b0.y, accC[0], 0, 0, 0);
             accC[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, b1.y, accC[1], 0, 0, 0);
             accC[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, b0.z, accC[0], 0, 0, 0);
@@ -374,32 +375,15 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             if (sln == 0) set_cands(step + 1);
             load_slab(sln);
         }
-        if (sl == 0) {
-            accP[0] = accC[0];
-            accP[1] = accC[1];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) accC[tt][v] = 0.f;
-        }
         if (active) {
-            mfma_slab(xb, sl);
-            if (sl == 0 && step > 0) {
-                epilogue(step - 1, accP);
-                // interleave: one MFMA, then vector and scalar work of the epilogue
-                static_for(std::make_integer_sequence<int, 2 * kSlab>{}, [&](auto) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x004, 6, 0);
-                });
-            }
+            if (sl == 0) mfma_slab(xb, sl, true);
+            else mfma_slab(xb, sl, false);
+            if (sl == nslab - 1) epilogue(step, accC);
         }
-        if (sl == 0 && step > 0 && ((step - 1) % G::SPG == G::SPG - 1)) pend_group = (int)((step - 1) / G::SPG);
+        if (sl == nslab - 1 && (step % G::SPG == G::SPG - 1 || step + 1 == nsteps)) pend_group = (int)(step / G::SPG);
     }
-    if (active) epilogue(nsteps - 1, accC);
     __syncthreads();
     if (pend_group >= 0) flush((uint32_t)pend_group);
-    flush((nsteps - 1) / G::SPG);
 }
 
 }  // namespace
