@@ -198,31 +198,69 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
     const uint32_t K = nsteps * (uint32_t)nslab;
 
-    // loader: element m of this thread is (block j = e / SC, candidate c = e % SC), e = tid + 256 m
-    auto cand_index = [&](uint32_t step, int c) -> uint32_t {
-        const uint32_t p = c_begin + step * G::SC + c;
-        const uint32_t pp = p < c_end ? p : c_begin;
+    // loader: element m of this thread is (block j = e / SC, candidate c =
+    // e % SC), e = tid + 256 m.  Its candidate position advances by SC per
+    // step, so the merged range it falls in is tracked incrementally (ranges
+    // are visited in order); positions past the segment end reuse the first
+    // candidate so that every load stays in bounds.
+    uint32_t rg[G::NCG], rnext[G::NCG], roff[G::NCG], lxi[G::NCG];
+    uint32_t idx0;
+    {
         int g = 0;
-        while (g + 1 < (int)nr && pp >= L.pref[g + 1]) ++g;
-        return L.start[g] + (pp - L.pref[g]);
-    };
-    uint32_t lxi[G::NCG];
+        while (g + 1 < (int)nr && c_begin >= L.pref[g + 1]) ++g;
+        idx0 = L.start[g] + (c_begin - L.pref[g]);
+#pragma unroll
+        for (int m = 0; m < G::NCG; ++m) {
+            rg[m] = (uint32_t)g;
+            rnext[m] = g + 1 < (int)nr ? L.pref[g + 1] : 0xffffffffu;
+            roff[m] = L.start[g] - L.pref[g];
+        }
+    }
     auto set_cands = [&](uint32_t step) {
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) lxi[m] = cand_index(step, (tid + 256 * m) % G::SC);
+        for (int m = 0; m < G::NCG; ++m) {
+            const uint32_t p = c_begin + step * G::SC + (uint32_t)((tid + 256 * m) % G::SC);
+            if (p < c_end) {
+                while (p >= rnext[m]) {
+                    const uint32_t g = ++rg[m];
+                    rnext[m] = g + 1 < nr ? L.pref[g + 1] : 0xffffffffu;
+                    roff[m] = L.start[g] - L.pref[g];
+                }
+                lxi[m] = p + roff[m];
+            } else {
+                lxi[m] = idx0;
+            }
+        }
     };
-    float4 ld[G::NCG];
-    auto load_slab = [&](int sl) {
+    // loads run kAhead slabs ahead of the staging
+    constexpr int kAhead = 2;
+    float4 ld[kAhead][G::NCG];
+    uint32_t ldx[kAhead][G::NCG];
+    auto load_slab = [&](int sl, float4 *dst, uint32_t *dx) {
 #pragma unroll
         for (int m = 0; m < G::NCG; ++m) {
             const int e = tid + 256 * m;
             const int b = sl * kSlab + e / G::SC;
-            ld[m] = b < nb ? xs[(uint64_t)b * n + lxi[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            dst[m] = b < nb ? xs[(uint64_t)b * n + lxi[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            dx[m] = lxi[m];
         }
     };
-
+    // load cursor: slab lsl of step lstep
+    uint32_t lstep = 0;
+    int lsl = 0;
+    auto cursor_next = [&]() {
+        if (++lsl == nslab) {
+            lsl = 0;
+            ++lstep;
+            set_cands(lstep);
+        }
+    };
     set_cands(0);
-    load_slab(0);
+#pragma unroll
+    for (int a2 = 0; a2 < kAhead; ++a2) {
+        if ((uint32_t)a2 < K) load_slab(lsl, ld[a2], ldx[a2]);
+        if ((uint32_t)a2 + 1 < K) cursor_next();
+    }
     float nxp[G::NCG];
 #pragma unroll
     for (int m = 0; m < G::NCG; ++m) nxp[m] = 0.f;
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
         for (int m = 0; m < G::NCG; ++m) {
             const int e = tid + 256 * m;
             const int j = e / G::SC;
-            const float4 c4 = sub4(ld[m], L.r[sl * kSlab + j]);
+            const float4 c4 = sub4(ld[0][m], L.r[sl * kSlab + j]);
             float s2 = nxp[m];
             s2 = fmaf(c4.x, c4.x, s2);
             s2 = fmaf(c4.y, c4.y, s2);
@@ -361,7 +399,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             for (int m = 0; m < G::NCG; ++m) {
                 const int e = tid + 256 * m;
                 L.nxp[(step % kNB) * (kSlab * G::SC) + e] = nxp[m];
-                if (e < G::SC) L.xi[(step % kNB) * G::SC + e] = lxi[m];
+                if (e < G::SC) L.xi[(step % kNB) * G::SC + e] = ldx[0][m];
                 nxp[m] = 0.f;
             }
         }
@@ -370,10 +408,17 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             flush((uint32_t)pend_group);
             pend_group = -1;
         }
-        if (k + 1 < K) {
-            const int sln = sl + 1 == nslab ? 0 : sl + 1;
-            if (sln == 0) set_cands(step + 1);
-            load_slab(sln);
+#pragma unroll
+        for (int a2 = 0; a2 + 1 < kAhead; ++a2) {
+#pragma unroll
+            for (int m = 0; m < G::NCG; ++m) {
+                ld[a2][m] = ld[a2 + 1][m];
+                ldx[a2][m] = ldx[a2 + 1][m];
+            }
+        }
+        if (k + kAhead < K) {
+            load_slab(lsl, ld[kAhead - 1], ldx[kAhead - 1]);
+            cursor_next();
         }
         if (active) {
             if (sl == 0) mfma_slab(xb, sl, true);
