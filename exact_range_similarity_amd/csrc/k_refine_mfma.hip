@@ -52,13 +52,16 @@ constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
 constexpr int kNB = 4;            // step buffers for norms / candidate ids
 constexpr int kGroupCands = 512;  // candidates per mask-word flush
 
-// Write a wave-uniform 32-bit value into lane L of a VGPR (v_writelane_b32;
-// the lane is an inline constant, the value the one allowed SGPR operand).
+// v_writelane_b32 through its LLVM intrinsic (clang has no builtin for it):
+// writes a wave-uniform 32-bit value into one lane of a VGPR.  The compiler
+// sees a real instruction and keeps the hazard wait states around it, which
+// an asm statement would hide from it.
+extern "C" __device__ int ersj_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
 template <int L>
 __device__ __forceinline__ int write_lane(int old, uint32_t val)
 {
-    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(val), "i"(L));
-    return old;
+    return ersj_writelane((int)val, L, old);
 }
 
 template <int... E, typename F>
