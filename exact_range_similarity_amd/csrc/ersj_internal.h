@@ -27,8 +27,13 @@ struct Tile {
     uint32_t cell;
     uint32_t row0;
     uint32_t nrows;
-    uint32_t words;  // 64-bit mask words per row = ceil(U / 64)
+    uint32_t words;  // row stride of the mask in 64-bit words: used, rounded up to kRowAlign
+    uint32_t used;   // mask words that hold candidates = ceil(U / 64)
 };
+
+// Mask rows start on 64-byte boundaries, so the refinement's 64-byte row
+// pieces are whole aligned segments.  Words past `used` are never read.
+constexpr uint32_t kRowAlign = 8;
 
 // A pair inside the fp32 uncertainty band, re-evaluated in binary64.
 struct Boundary {

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void k_rowcount(const Tile *__restrict__ tiles
     for (uint32_t r = wave; r < tl.nrows; r += 4) {
         const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
         uint32_t c = 0;
-        for (uint32_t w = lane; w < tl.words; w += 64) c += __popcll(row[w]);
+        for (uint32_t w = lane; w < tl.used; w += 64) c += __popcll(row[w]);
         for (int o = 32; o > 0; o >>= 1) c += __shfl_down(c, o, 64);
         if (lane == 0) cnt[tl.row0 + r - row_base] = c;
     }
@@ -89,9 +89,9 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
         const uint32_t qid = orig[q];
         const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
         uint64_t out = roff[q - row_base];
-        for (uint32_t w0 = 0; w0 < tl.words; w0 += 64) {
+        for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
             const uint32_t w = w0 + lane;
-            uint64_t m = w < tl.words ? row[w] : 0ull;
+            uint64_t m = w < tl.used ? row[w] : 0ull;
             const uint32_t pc = __popcll(m);
             uint32_t inc = pc;
             for (int o = 1; o < 64; o <<= 1) {

@@ -561,12 +561,14 @@ __global__ __launch_bounds__(kBlock) void k_tiles(const uint64_t *__restrict__ t
     const uint32_t end = cell_start[A + 1];
     const uint32_t nrows = min((uint32_t)kTileRows, end - row0);
     const uint32_t U = rpref[A * (kMaxRanges + 1) + nrng[A]];
-    const uint32_t W = (U + 63u) / 64u;
+    const uint32_t used = (U + 63u) / 64u;
+    const uint32_t W = (used + kRowAlign - 1) / kRowAlign * kRowAlign;
     Tile tl;
     tl.cell = (uint32_t)A;
     tl.row0 = row0;
     tl.nrows = nrows;
     tl.words = W;
+    tl.used = used;
     tiles[t] = tl;
     words[t] = (uint64_t)nrows * W;
     cands[t] = (uint64_t)nrows * U;
