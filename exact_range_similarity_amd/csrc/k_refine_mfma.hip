@@ -309,15 +309,17 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
         });
         if (anyb != 0) {
             // rare: redo the classification for the band pairs and append
-            // them for the binary64 re-check
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
+            // them for the binary64 re-check.  Rolled loops (indexed reads
+            // of one accumulator vector, thresholds re-read from LDS) keep
+            // this path from setting the kernel's register budget.
+            const floatx16 a0 = acc[0], a1 = acc[1];
+            auto band_tile = [&](const floatx16 &at, int tt) __attribute__((always_inline)) {
+#pragma unroll 1
                 for (int v = 0; v < 16; ++v) {
-                    float dd = acc[tt][v];
-                    asm volatile("" : "+v"(dd));  // recompute, do not keep masks alive
-                    const bool in = fmaf(-2.0f, dd, xin[tt]) <= qin[v];
-                    const bool nout = fmaf(-2.0f, dd, xout[tt]) <= qout[v];
+                    const float dd = at[v];
+                    const int row = qb * 32 + (v >> 2) * 8 + (v & 3) + 4 * hi;
+                    const bool in = fmaf(-2.0f, dd, xin[tt]) <= L.qin[row];
+                    const bool nout = fmaf(-2.0f, dd, xout[tt]) <= L.qout[row];
                     const bool bd = !in && nout;
                     const uint64_t bbd = __ballot(bd);
                     if (bbd == 0) continue;
@@ -329,7 +331,6 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
                     if (bd) {
                         const uint64_t below = lane == 0 ? 0ull : (bbd & (~0ull >> (64 - lane)));
                         const uint64_t idx = base + __popcll(below);
-                        const uint32_t row = qb * 32 + (v >> 2) * 8 + (v & 3) + 4 * hi;
                         if (idx < bcap) {
                             Boundary e;
                             e.q = row0 + row;
@@ -339,7 +340,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
                         }
                     }
                 }
-            }
+            };
+            band_tile(a0, 0);
+            band_tile(a1, 1);
         }
         const uint32_t grp = s / G::SPG;
         if (lane < 32)
