@@ -16,7 +16,7 @@
 // query block w % QB and candidate group w / QB and computes a 32 x 64
 // block per step (two 32x32 accumulators) = one 64-bit mask word per row.
 // A step covers 256/QB candidates; candidates are staged through LDS in
-// slabs of 16 dimensions (double-buffered, loaded one slab ahead, centred
+// slabs of 16 dimensions (double-buffered, loaded two slabs ahead, centred
 // and squared once by the loading thread) and read by all QB query blocks.
 //
 // MFMA operands: lanes 0-31 carry dimension block 2s, lanes 32-63 block
@@ -34,10 +34,11 @@
 // D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The host bounds the
 // coordinates so that nothing here overflows; NaN never classifies.
 //
-// A step's classification follows its last slab's MFMAs; the two waves that
-// share a SIMD (two workgroups per CU) overlap one's classification with the
-// other's matrix work.  Mask words collect in LDS and leave as 64-byte row
-// pieces every 512 candidates.
+// A step's classification follows its last slab's MFMAs; the waves that
+// share a SIMD overlap one's classification with another's matrix work.
+// With QB = 4 the kernel stays within 128 VGPRs and, up to d = 32, 40 KiB of
+// LDS, so four workgroups fit a CU.  Mask words collect in LDS and leave as
+// aligned 64-byte row pieces every 512 candidates.
 #include "ersj_internal.h"
 
 #include <utility>
@@ -49,7 +50,7 @@ namespace {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
-constexpr int kNB = 4;            // step buffers for norms / candidate ids
+constexpr int kNB = 2;            // step buffers for norms / candidate ids
 constexpr int kGroupCands = 512;  // candidates per mask-word flush
 
 // v_writelane_b32 through its LLVM intrinsic (clang has no builtin for it):
@@ -91,7 +92,7 @@ struct Lds {
     float *nxp;         // [kNB][kSlab][SC] partial candidate norms of a step
     uint32_t *xi;       // [kNB][SC] candidate point index of a step
     float *qin, *qout;  // [QR]
-    uint64_t *words;    // [2][QR][8]
+    uint64_t *words;    // [QR][8] mask words of the current 512-candidate group
     uint32_t *pref, *start;
 };
 
@@ -100,7 +101,7 @@ size_t lds_bytes(int nbs)
 {
     using G = Geometry<QB>;
     return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
-           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)2 * G::QR * 8 * 8 + (2 * kMaxRanges + 1) * 4;
+           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)G::QR * 8 * 8 + (2 * kMaxRanges + 1) * 4;
 }
 
 template <int QB>
@@ -116,13 +117,13 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     L.qin = (float *)(L.xi + kNB * G::SC);
     L.qout = L.qin + G::QR;
     L.words = (uint64_t *)(L.qout + G::QR);
-    L.pref = (uint32_t *)(L.words + 2 * G::QR * 8);
+    L.pref = (uint32_t *)(L.words + G::QR * 8);
     L.start = L.pref + (kMaxRanges + 1);
     return L;
 }
 
 template <int QB>
-__global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs a)
+__global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs a)
 {
     using G = Geometry<QB>;
     uint32_t rk, colx;
@@ -189,13 +190,6 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
     const int col = lane & 31, hi = lane >> 5;
     const int qb = wave % QB, cg = wave / QB;
     const bool active = (uint32_t)(qb * 32) < nrows;  // wave-uniform
-    float qin[16], qout[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int i = qb * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
-        qin[v] = L.qin[i];
-        qout[v] = L.qout[i];
-    }
     const float kp = a.kp, km = a.km;
     const uint64_t bcap = a.bcap;
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
@@ -290,14 +284,25 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
         }
         int wlo = 0, whi = 0;
         uint64_t anyb = 0;
+        // row thresholds come from LDS four rows at a time (rows
+        // 8t + 4hi .. +3 of the query block for registers 4t .. 4t+3)
+        const float4 *qin4 = (const float4 *)L.qin + qb * 8 + hi;
+        const float4 *qout4 = (const float4 *)L.qout + qb * 8 + hi;
+        float4 qi = make_float4(0.f, 0.f, 0.f, 0.f), qo = qi;
         static_for(std::make_integer_sequence<int, 32>{}, [&](auto E) {
-            constexpr int tt = decltype(E)::value / 16, v = decltype(E)::value % 16;
+            constexpr int v = decltype(E)::value / 2, tt = decltype(E)::value % 2;
             constexpr int i0 = (v / 4) * 8 + (v % 4);
+            if (v % 4 == 0 && tt == 0) {
+                qi = qin4[(v / 4) * 2];
+                qo = qout4[(v / 4) * 2];
+            }
+            const float qiv = v % 4 == 0 ? qi.x : v % 4 == 1 ? qi.y : v % 4 == 2 ? qi.z : qi.w;
+            const float qov = v % 4 == 0 ? qo.x : v % 4 == 1 ? qo.y : v % 4 == 2 ? qo.z : qo.w;
             const float dd = acc[tt][v];
             const float v1 = fmaf(-2.0f, dd, xin[tt]);
             const float v2 = fmaf(-2.0f, dd, xout[tt]);
-            const uint64_t bin = __ballot(v1 <= qin[v]);
-            const uint64_t bno = __ballot(v2 <= qout[v]);
+            const uint64_t bin = __ballot(v1 <= qiv);
+            const uint64_t bno = __ballot(v2 <= qov);
             anyb |= bno & ~bin;
             if (tt == 0) {
                 wlo = write_lane<i0>(wlo, (uint32_t)bin);
@@ -344,13 +349,12 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
             band_tile(a0, 0);
             band_tile(a1, 1);
         }
-        const uint32_t grp = s / G::SPG;
         if (lane < 32)
-            L.words[(grp & 1) * (G::QR * 8) + (qb * 32 + lane) * 8 + (s % G::SPG) * G::NCG + cg] =
+            L.words[(qb * 32 + lane) * 8 + (s % G::SPG) * G::NCG + cg] =
                 ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
     };
     auto flush = [&](uint32_t grp) {
-        const uint64_t *sw = L.words + (grp & 1) * (G::QR * 8);
+        const uint64_t *sw = L.words;
         for (int e = tid; e < G::QR * 8; e += 256) {
             const int row = e >> 3, j = e & 7;
             const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
@@ -411,8 +415,12 @@ __global__ __launch_bounds__(256, QB == 4 ? 2 : 1) void k_refine_mfma(RefineArgs
         }
         __syncthreads();
         if (pend_group >= 0) {
+            // the group buffer is reused by the next group: with one slab
+            // per step this step's classification follows in this same
+            // iteration, so wait for the whole flush first
             flush((uint32_t)pend_group);
             pend_group = -1;
+            if (nslab == 1) __syncthreads();
         }
 #pragma unroll
         for (int a2 = 0; a2 + 1 < kAhead; ++a2) {
