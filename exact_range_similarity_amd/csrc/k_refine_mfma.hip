@@ -233,14 +233,21 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     constexpr int kAhead = 2;
     float4 ld[kAhead][G::NCG];
     uint32_t ldx[kAhead][G::NCG];
+    // element offset of the next load: block b = lsl * kSlab + j of the
+    // candidate, i.e. b * n + index, advanced by kSlab * n within a step
+    uint64_t loff[G::NCG];
+    const uint64_t slab_stride = (uint64_t)kSlab * n;
     auto load_slab = [&](int sl, float4 *dst, uint32_t *dx) {
 #pragma unroll
         for (int m = 0; m < G::NCG; ++m) {
-            const int e = tid + 256 * m;
-            const int b = sl * kSlab + e / G::SC;
-            dst[m] = b < nb ? xs[(uint64_t)b * n + lxi[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int b = sl * kSlab + (tid + 256 * m) / G::SC;
+            dst[m] = b < nb ? xs[loff[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
             dx[m] = lxi[m];
         }
+    };
+    auto restart_offsets = [&]() {
+#pragma unroll
+        for (int m = 0; m < G::NCG; ++m) loff[m] = (uint64_t)((tid + 256 * m) / G::SC) * n + lxi[m];
     };
     // load cursor: slab lsl of step lstep
     uint32_t lstep = 0;
@@ -250,9 +257,14 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             lsl = 0;
             ++lstep;
             set_cands(lstep);
+            restart_offsets();
+        } else {
+#pragma unroll
+            for (int m = 0; m < G::NCG; ++m) loff[m] += slab_stride;
         }
     };
     set_cands(0);
+    restart_offsets();
 #pragma unroll
     for (int a2 = 0; a2 < kAhead; ++a2) {
         if ((uint32_t)a2 < K) load_slab(lsl, ld[a2], ldx[a2]);
@@ -386,9 +398,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
     };
 
+    uint32_t step = 0;
+    int sl = 0;
     for (uint32_t k = 0; k < K; ++k) {
-        const uint32_t step = k / nslab;
-        const int sl = (int)(k - step * nslab);
         float4 *xb = L.x + (k & 1) * (kSlab * G::SC);
         // stage the slab: centre on r, accumulate partial norms
 #pragma unroll
@@ -440,6 +452,10 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             if (sl == nslab - 1) epilogue(step, accC);
         }
         if (sl == nslab - 1 && (step % G::SPG == G::SPG - 1 || step + 1 == nsteps)) pend_group = (int)(step / G::SPG);
+        if (++sl == nslab) {
+            sl = 0;
+            ++step;
+        }
     }
     __syncthreads();
     if (pend_group >= 0) flush((uint32_t)pend_group);
