@@ -301,27 +301,42 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         const float4 *qin4 = (const float4 *)L.qin + qb * 8 + hi;
         const float4 *qout4 = (const float4 *)L.qout + qb * 8 + hi;
         float4 qi = make_float4(0.f, 0.f, 0.f, 0.f), qo = qi;
-        static_for(std::make_integer_sequence<int, 32>{}, [&](auto E) {
-            constexpr int v = decltype(E)::value / 2, tt = decltype(E)::value % 2;
-            constexpr int i0 = (v / 4) * 8 + (v % 4);
-            if (v % 4 == 0 && tt == 0) {
-                qi = qin4[(v / 4) * 2];
-                qo = qout4[(v / 4) * 2];
-            }
-            const float qiv = v % 4 == 0 ? qi.x : v % 4 == 1 ? qi.y : v % 4 == 2 ? qi.z : qi.w;
-            const float qov = v % 4 == 0 ? qo.x : v % 4 == 1 ? qo.y : v % 4 == 2 ? qo.z : qo.w;
-            const float dd = acc[tt][v];
-            const float v1 = fmaf(-2.0f, dd, xin[tt]);
-            const float v2 = fmaf(-2.0f, dd, xout[tt]);
-            const uint64_t bin = __ballot(v1 <= qiv);
-            const uint64_t bno = __ballot(v2 <= qov);
-            anyb |= bno & ~bin;
+        // Groups of four registers (rows 8g .. 8g+3 and 8g+4 .. 8g+7 of a
+        // tile).  "In" implies "not out" exactly (fl(kp*Nx) >= fl(km*Nx) and
+        // qin <= qout under monotone rounding), so a group whose pairs are
+        // all "out" - most of them - needs only the four "out" tests; its
+        // mask half-words stay zero.
+        static_for(std::make_integer_sequence<int, 8>{}, [&](auto E) {
+            constexpr int g = decltype(E)::value / 2, tt = decltype(E)::value % 2;
             if (tt == 0) {
-                wlo = write_lane<i0>(wlo, (uint32_t)bin);
-                wlo = write_lane<i0 + 4>(wlo, (uint32_t)(bin >> 32));
-            } else {
-                whi = write_lane<i0>(whi, (uint32_t)bin);
-                whi = write_lane<i0 + 4>(whi, (uint32_t)(bin >> 32));
+                qi = qin4[g * 2];
+                qo = qout4[g * 2];
+            }
+            uint64_t bno[4];
+            uint64_t anyno = 0;
+            static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
+                constexpr int j = decltype(J)::value;
+                const float qov = j == 0 ? qo.x : j == 1 ? qo.y : j == 2 ? qo.z : qo.w;
+                const float v2 = fmaf(-2.0f, acc[tt][4 * g + j], xout[tt]);
+                bno[j] = __ballot(v2 <= qov);
+                anyno |= bno[j];
+            });
+            if (anyno != 0) {
+                static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    constexpr int i0 = 8 * g + j;
+                    const float qiv = j == 0 ? qi.x : j == 1 ? qi.y : j == 2 ? qi.z : qi.w;
+                    const float v1 = fmaf(-2.0f, acc[tt][4 * g + j], xin[tt]);
+                    const uint64_t bin = __ballot(v1 <= qiv);
+                    anyb |= bno[j] & ~bin;
+                    if (tt == 0) {
+                        wlo = write_lane<i0>(wlo, (uint32_t)bin);
+                        wlo = write_lane<i0 + 4>(wlo, (uint32_t)(bin >> 32));
+                    } else {
+                        whi = write_lane<i0>(whi, (uint32_t)bin);
+                        whi = write_lane<i0 + 4>(whi, (uint32_t)(bin >> 32));
+                    }
+                });
             }
         });
         if (anyb != 0) {
