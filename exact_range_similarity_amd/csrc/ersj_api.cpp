@@ -97,7 +97,8 @@ struct ersj_index {
     uint64_t mask_cap = 0;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;
-    unsigned long long *counters = nullptr;  // [0] boundary count, [1] re-check in
+    unsigned long long *counters = nullptr;  // band sub-list counters, then re-check hits
+    uint64_t *lpref = nullptr;               // [kBandLists + 1] prefix, [2] kept / max count
     uint32_t *rowcnt = nullptr;
     uint64_t *roff = nullptr, *rscan = nullptr;
     uint64_t rows_cap = 0;
@@ -569,7 +570,8 @@ int ensure_fill_buffers(ersj_index *h)
         TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
         h->rows_cap = h->maxrows;
     }
-    if (!h->counters) TRY(dalloc(h, &h->counters, 2, "counters"));
+    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)kBandLists * kBandStride + 1, "counters"));
+    if (!h->lpref) TRY(dalloc(h, &h->lpref, (size_t)kBandLists + 3, "band list prefix"));
     if (!h->blist) {
         const uint64_t cap = initial_bcap(h);
         TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
@@ -613,12 +615,16 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.thi = h->thi;
     a.kp = h->kp;
     a.km = h->km;
+    const size_t ncount = (size_t)kBandLists * kBandStride + 1;
+    unsigned long long *const hits = h->counters + (size_t)kBandLists * kBandStride;
+    uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
+        const uint64_t lcap = h->bcap / kBandLists;
         a.blist = h->blist;
         a.bcount = h->counters;
-        a.bcap = h->bcap;
-        HIPC(launch_fill_u64((uint64_t *)h->counters, 0, 2, s), "clear counters");
+        a.lcap = lcap;
+        HIPC(launch_fill_u64((uint64_t *)h->counters, 0, (int64_t)ncount, s), "clear counters");
         timer_start(h, s);
         HIPC(mfma ? launch_refine_mfma(a, s) : launch_refine_direct(a, s), "refine kernel");
         h->ms_refine += timer_stop(h, s);
@@ -626,14 +632,17 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
             h->refine_launches += 1;
             h->refined_cand += h->hcands[b + 1] - h->hcands[b];
         }
-        HIPC(hipMemcpyAsync(&bcount, h->counters, sizeof bcount, hipMemcpyDeviceToHost, s), "copy");
+        HIPC(launch_band_prefix(h->counters, lcap, h->lpref, h->lpref + kBandLists + 1, s), "band prefix");
+        HIPC(hipMemcpyAsync(bres, h->lpref + kBandLists + 1, sizeof bres, hipMemcpyDeviceToHost, s), "copy");
         TRY(sync(s, "refine"));
-        if (bcount <= h->bcap) break;
-        // The boundary list overflowed: grow it and refine the batch again
-        // (every mask word is rewritten, so the first result is discarded).
+        bcount = bres[0];
+        if (bres[1] <= lcap) break;
+        // A band sub-list overflowed: grow them all and refine the batch
+        // again (every mask word is rewritten, so the first result is
+        // discarded).
         dfree(h, h->blist);
         h->bcap = 0;
-        const uint64_t cap = bcount + bcount / 4 + 1024;
+        const uint64_t cap = (bres[1] + bres[1] / 4 + 64) * kBandLists;
         TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
         h->bcap = cap;
         if (!h->opt.boundary_capacity) {
@@ -642,10 +651,10 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
             }
         }
     }
-    if (bcount > h->bcap) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
+    if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
-    HIPC(launch_recheck(h->blist, bcount, h->xs, (uint64_t)h->n, h->d, h->d_pinv, h->e64, h->mask,
-                        h->counters + 1, s), "re-check kernel");
+    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->d,
+                        h->d_pinv, h->e64, h->mask, hits, s), "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
     HIPC(launch_rowcount(h->tiles, t0, ntiles, h->toff, a.wbase, h->hrows[b], h->mask, h->rowcnt, s),
@@ -653,7 +662,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
     uint64_t tot = 0, nin = 0;
     HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
-    HIPC(hipMemcpyAsync(&nin, h->counters + 1, sizeof nin, hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(&nin, hits, sizeof nin, hipMemcpyDeviceToHost, s), "copy");
     TRY(sync(s, "row count"));
     h->ms_expand += timer_stop(h, s);
     h->last_cand = h->hcands[b + 1] - h->hcands[b];

@@ -137,6 +137,22 @@ __device__ __forceinline__ void work_item(uint32_t b, uint32_t ntiles, uint32_t 
     *rank = (uint32_t)(r0 + within % rg);
 }
 
+// Band pairs go to kBandLists sub-lists, picked by workgroup, each with its
+// own counter on its own 128-byte line: one counter for the whole grid made
+// the appends contend on a single address.  Workgroup b uses sub-list
+// b % kBandLists, so each sub-list is served by one XCD's L2.
+constexpr uint32_t kBandLists = 256;
+constexpr uint32_t kBandStride = 16;  // u64 words between two counters
+
+__device__ __forceinline__ unsigned long long *band_counter(unsigned long long *bcount)
+{
+    return bcount + (uint64_t)(blockIdx.x % kBandLists) * kBandStride;
+}
+__device__ __forceinline__ Boundary *band_list(Boundary *blist, uint64_t lcap)
+{
+    return blist + (uint64_t)(blockIdx.x % kBandLists) * lcap;
+}
+
 struct RefineArgs {
     const float4 *xs;
     uint64_t n;
@@ -156,9 +172,9 @@ struct RefineArgs {
     uint64_t *mask;
     float tlo, thi;      // fp32 classification thresholds
     float kp, km;        // 1 + K and 1 - K of the MFMA kernel's norm-proportional band
-    Boundary *blist;
-    unsigned long long *bcount;
-    uint64_t bcap;
+    Boundary *blist;              // kBandLists sub-lists of lcap entries each
+    unsigned long long *bcount;   // sub-list c's counter at bcount[c * kBandStride]
+    uint64_t lcap;                // entries per sub-list
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
 
@@ -169,9 +185,14 @@ hipError_t prepare_refine_mfma(int nb);
 hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
-hipError_t launch_recheck(const Boundary *bl, uint64_t cnt, const float4 *xs, uint64_t n,
-                          int32_t d, const int32_t *pinv, double e64, uint64_t *mask,
-                          unsigned long long *nin, hipStream_t s);
+// Band-list bookkeeping after a refinement launch: out[0] = entries kept
+// (each sub-list's count, clipped to lcap), out[1] = the largest unclipped
+// count, lpref[0..kBandLists] = exclusive prefix of the kept counts.
+hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, uint64_t *lpref,
+                              uint64_t *out, hipStream_t s);
+hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
+                          const float4 *xs, uint64_t n, int32_t d, const int32_t *pinv, double e64,
+                          uint64_t *mask, unsigned long long *nin, hipStream_t s);
 
 hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
                            uint64_t wbase, uint64_t row_base, const uint64_t *mask,

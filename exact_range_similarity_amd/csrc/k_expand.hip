@@ -11,10 +11,40 @@ namespace ersj {
 
 namespace {
 
+// One workgroup of kBandLists threads: keep min(count, lcap) entries of each
+// band sub-list, prefix them, and report the total kept and the largest
+// count (a count above lcap means the lists must grow).
+__global__ __launch_bounds__(kBandLists) void k_band_prefix(const unsigned long long *__restrict__ bcount,
+                                                            uint64_t lcap, uint64_t *__restrict__ lpref,
+                                                            uint64_t *__restrict__ out)
+{
+    __shared__ uint64_t sc[kBandLists];
+    __shared__ uint64_t sm[kBandLists];
+    const uint32_t t = threadIdx.x;
+    const uint64_t c = bcount[(uint64_t)t * kBandStride];
+    sc[t] = c < lcap ? c : lcap;
+    sm[t] = c;
+    __syncthreads();
+    if (t == 0) {
+        uint64_t run = 0, mx = 0;
+        for (uint32_t i = 0; i < kBandLists; ++i) {
+            lpref[i] = run;
+            run += sc[i];
+            mx = sm[i] > mx ? sm[i] : mx;
+        }
+        lpref[kBandLists] = run;
+        out[0] = run;
+        out[1] = mx;
+    }
+}
+
 // Binary64 squared distance in the input's own dimension order, every
 // operation separately rounded (no contraction): the exact definition the
 // result set is specified by.  Pairs at or below fl(eps*eps) get their bit.
-__global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t cnt,
+// Entry i of the kept band pairs lives in sub-list c (lpref[c] <= i <
+// lpref[c+1]) at offset i - lpref[c].
+__global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t lcap,
+                                                 const uint64_t *__restrict__ lpref, uint64_t cnt,
                                                  const float *__restrict__ xsf, uint64_t n,
                                                  int32_t d, const int32_t *__restrict__ pinv,
                                                  double e64, uint64_t *__restrict__ mask,
@@ -22,25 +52,39 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
 {
 #pragma clang fp contract(off)
     __shared__ int32_t sp[kMaxDim];
+    __shared__ uint64_t spref[kBandLists + 1];
     for (int k = threadIdx.x; k < d; k += blockDim.x) sp[k] = pinv[k];
+    for (uint32_t k = threadIdx.x; k <= kBandLists; k += blockDim.x) spref[k] = lpref[k];
     __syncthreads();
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= cnt) return;
-    const Boundary e = bl[i];
-    double s = 0.0;
-    for (int k = 0; k < d; ++k) {
-        const int p = sp[k];
-        const uint64_t off = ((uint64_t)(p >> 2) * n) * 4 + (p & 3);
-        const double a = (double)xsf[off + (uint64_t)e.q * 4];
-        const double b = (double)xsf[off + (uint64_t)e.x * 4];
-        const double t = a - b;
-        const double tt = t * t;
-        s = s + tt;
+    bool hit = false;
+    if (i < cnt) {
+        uint32_t lo = 0, hi = kBandLists;  // largest c with spref[c] <= i
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (spref[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const Boundary e = bl[(uint64_t)lo * lcap + (i - spref[lo])];
+        double s = 0.0;
+        for (int k = 0; k < d; ++k) {
+            const int p = sp[k];
+            const uint64_t off = ((uint64_t)(p >> 2) * n) * 4 + (p & 3);
+            const double a = (double)xsf[off + (uint64_t)e.q * 4];
+            const double b = (double)xsf[off + (uint64_t)e.x * 4];
+            const double t = a - b;
+            const double tt = t * t;
+            s = s + tt;
+        }
+        if (s <= e64) {
+            atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
+            hit = true;
+        }
     }
-    if (s <= e64) {
-        atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
-        atomicAdd(nin, 1ull);
-    }
+    // one counter update per wave
+    const uint64_t hits = __ballot(hit);
+    if (hits != 0 && (threadIdx.x & 63) == (uint32_t)(__ffsll((unsigned long long)hits) - 1))
+        atomicAdd(nin, (unsigned long long)__popcll(hits));
 }
 
 // Workgroup per row tile of the batch (index order), wave per row.
@@ -118,13 +162,20 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
 
 }  // namespace
 
-hipError_t launch_recheck(const Boundary *bl, uint64_t cnt, const float4 *xs, uint64_t n, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
-                          hipStream_t s)
+hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, uint64_t *lpref,
+                              uint64_t *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_band_prefix, dim3(1), dim3(kBandLists), 0, s, bcount, lcap, lpref, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
+                          const float4 *xs, uint64_t n, int32_t d, const int32_t *pinv, double e64,
+                          uint64_t *mask, unsigned long long *nin, hipStream_t s)
 {
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
-    hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, cnt,
+    hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt,
                        (const float *)xs, n, d, pinv, e64, mask, nin);
     return hipGetLastError();
 }

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     const uint64_t n = a.n;
     const float4 *__restrict__ xs = a.xs;
     uint64_t *__restrict__ mask = a.mask;
-    Boundary *__restrict__ blist = a.blist;
-    unsigned long long *__restrict__ bcount = a.bcount;
+    Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
+    unsigned long long *__restrict__ bcount = band_counter(a.bcount);
 
     for (uint32_t c = c_begin; c < c_end; c += kChunk) {
         uint32_t xi[kCW];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
                     if (bd) {
                         const uint64_t below = lane == 0 ? 0ull : (wb & (~0ull >> (64 - lane)));
                         const uint64_t idx = base + __popcll(below);
-                        if (idx < a.bcap) {
+                        if (idx < a.lcap) {
                             Boundary e;
                             e.q = qrow[k];
                             e.x = xi[j];

@@ -153,8 +153,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const uint64_t n = a.n;
     const float4 *__restrict__ xs = a.xs;
     uint64_t *__restrict__ mask = a.mask;
-    Boundary *__restrict__ blist = a.blist;
-    unsigned long long *__restrict__ bcount = a.bcount;
+    Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
+    unsigned long long *__restrict__ bcount = band_counter(a.bcount);
     const uint32_t W = tl.words;
     const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)r_begin * W;
 
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const int qb = wave % QB, cg = wave / QB;
     const bool active = (uint32_t)(qb * 32) < nrows;  // wave-uniform
     const float kp = a.kp, km = a.km;
-    const uint64_t bcap = a.bcap;
+    const uint64_t bcap = a.lcap;
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
     const uint32_t K = nsteps * (uint32_t)nslab;
 

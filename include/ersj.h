@@ -74,7 +74,8 @@ typedef struct ersj_options {
     int32_t refine_kernel;      /* ERSJ_REFINE_* */
     double cell_width_scale;    /* grid cell width = eps * max(1, scale); default 1 */
     uint64_t max_device_bytes;  /* cap on library-owned device memory; 0 = none */
-    uint64_t boundary_capacity; /* initial boundary-pair list entries; 0 = default */
+    uint64_t boundary_capacity; /* initial boundary-pair list entries over all 256 sub-lists (grown and
+                                   the batch refined again on overflow); 0 = default */
     int32_t timing;             /* nonzero: record HIP events around each phase */
     int32_t reserved;
 } ersj_options;
