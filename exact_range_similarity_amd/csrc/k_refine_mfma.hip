@@ -82,6 +82,7 @@ struct Geometry {
     static constexpr int QR = 32 * QB;            // query rows per work item
     static constexpr int SC = 64 * NCG;           // candidates per step
     static constexpr int SPG = kGroupCands / SC;  // steps per mask-word group
+    static constexpr int EPT = kSlab * SC / 256;   // slab elements staged per thread
 };
 
 template <int QB>
@@ -122,7 +123,7 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     return L;
 }
 
-template <int QB>
+template <int QB, int NS>
 __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs a)
 {
     using G = Geometry<QB>;
@@ -143,7 +144,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const uint32_t nrows = min((uint32_t)G::QR, tl.nrows - r_begin);
     const uint32_t row0 = tl.row0 + r_begin;
     const int nb = a.nb;
-    const int nslab = (nb + kSlab - 1) / kSlab;
+    // slabs per step: a compile-time constant when NS > 0 (d <= 16, d <= 32)
+    const int nslab = NS > 0 ? NS : (nb + kSlab - 1) / kSlab;
     const int nbs = nslab * kSlab;
 
     extern __shared__ float4 smem[];
@@ -200,14 +202,14 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     // step, so the merged range it falls in is tracked incrementally (ranges
     // are visited in order); positions past the segment end reuse the first
     // candidate so that every load stays in bounds.
-    uint32_t rg[G::NCG], rnext[G::NCG], roff[G::NCG], lxi[G::NCG];
+    uint32_t rg[G::EPT], rnext[G::EPT], roff[G::EPT], lxi[G::EPT];
     uint32_t idx0;
     {
         int g = 0;
         while (g + 1 < (int)nr && c_begin >= L.pref[g + 1]) ++g;
         idx0 = L.start[g] + (c_begin - L.pref[g]);
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) {
+        for (int m = 0; m < G::EPT; ++m) {
             rg[m] = (uint32_t)g;
             rnext[m] = g + 1 < (int)nr ? L.pref[g + 1] : 0xffffffffu;
             roff[m] = L.start[g] - L.pref[g];
@@ -215,7 +217,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     }
     auto set_cands = [&](uint32_t step) {
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) {
+        for (int m = 0; m < G::EPT; ++m) {
             const uint32_t p = c_begin + step * G::SC + (uint32_t)((tid + 256 * m) % G::SC);
             if (p < c_end) {
                 while (p >= rnext[m]) {
@@ -231,15 +233,15 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     };
     // loads run kAhead slabs ahead of the staging
     constexpr int kAhead = 2;
-    float4 ld[kAhead][G::NCG];
-    uint32_t ldx[kAhead][G::NCG];
+    float4 ld[kAhead][G::EPT];
+    uint32_t ldx[kAhead][G::EPT];
     // element offset of the next load: block b = lsl * kSlab + j of the
     // candidate, i.e. b * n + index, advanced by kSlab * n within a step
-    uint64_t loff[G::NCG];
+    uint64_t loff[G::EPT];
     const uint64_t slab_stride = (uint64_t)kSlab * n;
     auto load_slab = [&](int sl, float4 *dst, uint32_t *dx) {
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) {
+        for (int m = 0; m < G::EPT; ++m) {
             const int b = sl * kSlab + (tid + 256 * m) / G::SC;
             dst[m] = b < nb ? xs[loff[m]] : make_float4(0.f, 0.f, 0.f, 0.f);
             dx[m] = lxi[m];
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     };
     auto restart_offsets = [&]() {
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) loff[m] = (uint64_t)((tid + 256 * m) / G::SC) * n + lxi[m];
+        for (int m = 0; m < G::EPT; ++m) loff[m] = (uint64_t)((tid + 256 * m) / G::SC) * n + lxi[m];
     };
     // load cursor: slab lsl of step lstep
     uint32_t lstep = 0;
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             restart_offsets();
         } else {
 #pragma unroll
-            for (int m = 0; m < G::NCG; ++m) loff[m] += slab_stride;
+            for (int m = 0; m < G::EPT; ++m) loff[m] += slab_stride;
         }
     };
     set_cands(0);
@@ -270,9 +272,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         if ((uint32_t)a2 < K) load_slab(lsl, ld[a2], ldx[a2]);
         if ((uint32_t)a2 + 1 < K) cursor_next();
     }
-    float nxp[G::NCG];
+    float nxp[G::EPT];
 #pragma unroll
-    for (int m = 0; m < G::NCG; ++m) nxp[m] = 0.f;
+    for (int m = 0; m < G::EPT; ++m) nxp[m] = 0.f;
     floatx16 accC[2];
     int pend_group = -1;
 
@@ -285,7 +287,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         for (int tt = 0; tt < 2; ++tt) {
             const int cl = cg * 64 + 32 * tt + col;
             const float *np = L.nxp + (s % kNB) * (kSlab * G::SC);
-            const float nxt = ((np[cl] + np[G::SC + cl]) + np[2 * G::SC + cl]) + np[3 * G::SC + cl];
+            float nxt = np[cl];
+#pragma unroll
+            for (int j = 1; j < kSlab; ++j) nxt += np[j * G::SC + cl];
             xid[tt] = L.xi[(s % kNB) * G::SC + cl];
             // candidates past the segment end never classify: a NaN operand
             // makes both comparisons false (an infinity would not: with an
@@ -413,13 +417,16 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
     };
 
-    uint32_t step = 0;
-    int sl = 0;
-    for (uint32_t k = 0; k < K; ++k) {
+    // One slab: stage it, barrier, flush a finished mask-word group, issue
+    // the loads kAhead slabs ahead, MFMAs, and the step's classification
+    // after its last slab.  With NS > 0 the slab index is a constant and
+    // every per-slab condition folds.
+    auto slab_iter = [&](uint32_t k, uint32_t step, auto SLC) __attribute__((always_inline)) {
+        const int sl = SLC;
         float4 *xb = L.x + (k & 1) * (kSlab * G::SC);
         // stage the slab: centre on r, accumulate partial norms
 #pragma unroll
-        for (int m = 0; m < G::NCG; ++m) {
+        for (int m = 0; m < G::EPT; ++m) {
             const int e = tid + 256 * m;
             const int j = e / G::SC;
             const float4 c4 = sub4(ld[0][m], L.r[sl * kSlab + j]);
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
         if (sl == nslab - 1) {
 #pragma unroll
-            for (int m = 0; m < G::NCG; ++m) {
+            for (int m = 0; m < G::EPT; ++m) {
                 const int e = tid + 256 * m;
                 L.nxp[(step % kNB) * (kSlab * G::SC) + e] = nxp[m];
                 if (e < G::SC) L.xi[(step % kNB) * G::SC + e] = ldx[0][m];
@@ -452,14 +459,26 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
 #pragma unroll
         for (int a2 = 0; a2 + 1 < kAhead; ++a2) {
 #pragma unroll
-            for (int m = 0; m < G::NCG; ++m) {
+            for (int m = 0; m < G::EPT; ++m) {
                 ld[a2][m] = ld[a2 + 1][m];
                 ldx[a2][m] = ldx[a2 + 1][m];
             }
         }
         if (k + kAhead < K) {
-            load_slab(lsl, ld[kAhead - 1], ldx[kAhead - 1]);
-            cursor_next();
+            if constexpr (NS > 0) {
+                // the slab loaded now and the one after it are known here
+                load_slab((sl + kAhead) % NS, ld[kAhead - 1], ldx[kAhead - 1]);
+                if ((sl + kAhead + 1) % NS == 0) {
+                    set_cands(step + (uint32_t)((sl + kAhead + 1) / NS));
+                    restart_offsets();
+                } else {
+#pragma unroll
+                    for (int m = 0; m < G::EPT; ++m) loff[m] += slab_stride;
+                }
+            } else {
+                load_slab(lsl, ld[kAhead - 1], ldx[kAhead - 1]);
+                cursor_next();
+            }
         }
         if (active) {
             if (sl == 0) mfma_slab(xb, sl, true);
@@ -467,9 +486,20 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             if (sl == nslab - 1) epilogue(step, accC);
         }
         if (sl == nslab - 1 && (step % G::SPG == G::SPG - 1 || step + 1 == nsteps)) pend_group = (int)(step / G::SPG);
-        if (++sl == nslab) {
-            sl = 0;
-            ++step;
+    };
+    if constexpr (NS > 0) {
+        for (uint32_t step = 0; step < nsteps; ++step)
+            static_for(std::make_integer_sequence<int, NS>{},
+                       [&](auto S) __attribute__((always_inline)) { slab_iter(step * NS + S, step, S); });
+    } else {
+        uint32_t step = 0;
+        int sl = 0;
+        for (uint32_t k = 0; k < K; ++k) {
+            slab_iter(k, step, sl);
+            if (++sl == nslab) {
+                sl = 0;
+                ++step;
+            }
         }
     }
     __syncthreads();
@@ -496,14 +526,29 @@ size_t refine_mfma_lds_bytes(int nb)
     }
 }
 
+namespace {
+
+// kernel instance for nb dimension blocks: query blocks per workgroup and
+// slabs per step (1 and 2 are compiled as constants)
+const void *mfma_kernel(int nb)
+{
+    const int nslab = (nb + kSlab - 1) / kSlab;
+    switch (refine_mfma_qblocks(nb)) {
+    case 4:
+        if (nslab == 1) return (const void *)k_refine_mfma<4, 1>;
+        if (nslab == 2) return (const void *)k_refine_mfma<4, 2>;
+        return (const void *)k_refine_mfma<4, 0>;
+    case 2: return (const void *)k_refine_mfma<2, 0>;
+    default: return (const void *)k_refine_mfma<1, 0>;
+    }
+}
+
+}  // namespace
+
 hipError_t prepare_refine_mfma(int nb)
 {
-    const int bytes = (int)refine_mfma_lds_bytes(nb);
-    switch (refine_mfma_qblocks(nb)) {
-    case 4: return hipFuncSetAttribute((const void *)k_refine_mfma<4>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    case 2: return hipFuncSetAttribute((const void *)k_refine_mfma<2>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    default: return hipFuncSetAttribute((const void *)k_refine_mfma<1>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    }
+    return hipFuncSetAttribute(mfma_kernel(nb), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)refine_mfma_lds_bytes(nb));
 }
 
 hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s)
@@ -512,12 +557,9 @@ hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s)
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     const size_t bytes = refine_mfma_lds_bytes(a.nb);
-    switch (refine_mfma_qblocks(a.nb)) {
-    case 4: hipLaunchKernelGGL(k_refine_mfma<4>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
-    case 2: hipLaunchKernelGGL(k_refine_mfma<2>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
-    default: hipLaunchKernelGGL(k_refine_mfma<1>, dim3((unsigned)blocks), dim3(256), bytes, s, a); break;
-    }
-    return hipGetLastError();
+    RefineArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel(mfma_kernel(a.nb), dim3((unsigned)blocks), dim3(256), params, bytes, s);
 }
 
 }  // namespace ersj
