@@ -26,7 +26,8 @@
  *   - both (i,j) and (j,i) are reported, and (i,i) for every i.
  *
  * Every routine scans all candidate points in index order, so neighbour
- * lists come out sorted by point id.
+ * lists come out sorted by point id.  orc_semijoin_rows does the same for
+ * a query set distinct from the dataset (the semi-join of Sec. II-A).
  */
 #include <math.h>
 #include <stdint.h>
@@ -34,7 +35,7 @@
 #include <string.h>
 #include <omp.h>
 
-#define ORC_VERSION 1
+#define ORC_VERSION 2
 
 int orc_version(void) { return ORC_VERSION; }
 
@@ -88,6 +89,41 @@ int orc_join_rows(const float *X, int64_t n, int64_t d, int64_t ld, double eps,
         uint64_t c = 0, at = cols ? colptr[r] : 0;
         for (int64_t j = 0; j < n; ++j) {
             if (orc_d64(xi, X + j * ld, d) <= e64) {
+                if (cols) cols[at + c] = (uint32_t)j;
+                ++c;
+            }
+        }
+        if (counts) counts[r] = c;
+    }
+    return 0;
+}
+
+/*
+ * Semi-join (Sec. II-A: the query set Q distinct from the dataset D; the pair
+ * (q_j, p_i) is in the result iff dist(p_i, q_j) <= eps): neighbour lists of
+ * selected query rows of Q (all when rows == NULL) over all n points of X.
+ * Same two phases, return codes and canonical D64 (query first, point
+ * second) as orc_join_rows; with Q == X it is the self-join.
+ */
+int orc_semijoin_rows(const float *Q, int64_t nq, int64_t ldq, const float *X, int64_t n,
+                      int64_t ld, int64_t d, double eps, const int64_t *rows, int64_t nrows,
+                      uint64_t *counts, uint32_t *cols, const uint64_t *colptr)
+{
+    int rc = check_inputs(X, n, d, ld, eps);
+    if (rc) return rc;
+    rc = check_inputs(Q, nq, d, ldq, eps);
+    if (rc) return rc;
+    if (!rows) nrows = nq;
+    if (nrows < 0 || (!cols && !counts) || (cols && !colptr)) return -1;
+    const double e64 = orc_e64(eps);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        if (i < 0 || i >= nq) continue;
+        const float *qi = Q + i * ldq;
+        uint64_t c = 0, at = cols ? colptr[r] : 0;
+        for (int64_t j = 0; j < n; ++j) {
+            if (orc_d64(qi, X + j * ld, d) <= e64) {
                 if (cols) cols[at + c] = (uint32_t)j;
                 ++c;
             }

@@ -43,6 +43,10 @@ def _load():
     lib.orc_join_rows.restype = ctypes.c_int
     lib.orc_join_rows.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_double, _i64p, ctypes.c_int64, _u64p, _u32p, _u64p]
+    lib.orc_semijoin_rows.restype = ctypes.c_int
+    lib.orc_semijoin_rows.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, _f32p, ctypes.c_int64,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_double, _i64p,
+                                      ctypes.c_int64, _u64p, _u32p, _u64p]
     lib.orc_band_count.restype = ctypes.c_int64
     lib.orc_band_count.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64]
@@ -126,6 +130,42 @@ def join_rows(X, eps, rows=None):
         if rc != 0:
             raise ValueError(f"oracle rejected the input (code {rc})")
     return colptr, cols
+
+
+def semijoin_rows(Q, X, eps, rows=None):
+    """Neighbour lists in X of the query rows ``rows`` of Q (all if None), as
+    CSR (colptr, cols); cols ascending.  RT-HiSS Sec. II-A, the semi-join."""
+    Q = _as_x(Q)
+    X = _as_x(X)
+    nq, d = Q.shape
+    n, dx = X.shape
+    if d != dx:
+        raise ValueError("Q and X differ in dimension")
+    lib = _load()
+    r, rp = _rows_arg(rows)
+    nrows = nq if r is None else r.size
+    counts = np.zeros(nrows, dtype=np.uint64)
+    rc = lib.orc_semijoin_rows(_ptr(Q, _f32p), nq, d, _ptr(X, _f32p), n, d, d, float(eps), rp, nrows,
+                               _ptr(counts, _u64p), None, None)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the input (code {rc})")
+    colptr = np.zeros(nrows + 1, dtype=np.uint64)
+    np.cumsum(counts, out=colptr[1:])
+    cols = np.empty(int(colptr[-1]), dtype=np.uint32)
+    if cols.size:
+        rc = lib.orc_semijoin_rows(_ptr(Q, _f32p), nq, d, _ptr(X, _f32p), n, d, d, float(eps), rp, nrows,
+                                   None, _ptr(cols, _u32p), _ptr(colptr, _u64p))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the input (code {rc})")
+    return colptr, cols
+
+
+def semijoin_pairs(Q, X, eps):
+    """All (j, i) with D64(q_j, x_i) <= fl(eps*eps) (query id, point id), uint32 [|R|, 2], sorted."""
+    colptr, cols = semijoin_rows(Q, X, eps)
+    counts = np.diff(colptr).astype(np.int64)
+    q = np.repeat(np.arange(counts.size, dtype=np.uint32), counts)
+    return np.stack([q, cols], axis=1)
 
 
 def selfjoin_pairs(X, eps):
