@@ -58,7 +58,8 @@ class Stats(ctypes.Structure):
                 ("build_ms", ctypes.c_double), ("count_ms", ctypes.c_double),
                 ("plan_ms", ctypes.c_double), ("refine_ms", ctypes.c_double),
                 ("recheck_ms", ctypes.c_double), ("expand_ms", ctypes.c_double),
-                ("refine_launches", ctypes.c_int64), ("refined_candidates", ctypes.c_uint64)]
+                ("refine_launches", ctypes.c_int64), ("refined_candidates", ctypes.c_uint64),
+                ("n_queries", ctypes.c_int64)]
 
     def as_dict(self):
         out = {}
@@ -69,8 +70,9 @@ class Stats(ctypes.Structure):
 
 
 _lib = None
-SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_count_pass", "ersj_plan_batches",
-           "ersj_fill_pass", "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error")
+SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",
+           "ersj_plan_batches", "ersj_fill_pass", "ersj_batch_info", "ersj_get_stats", "ersj_free",
+           "ersj_last_error")
 
 
 def lib():
@@ -88,6 +90,7 @@ def lib():
     L.ersj_default_options.restype = None
     L.ersj_build_index.argtypes = [vp, i64, i32, i64, dbl, ctypes.POINTER(Options), vp,
                                    ctypes.POINTER(vp)]
+    L.ersj_set_queries.argtypes = [vp, vp, i64, i64, vp]
     L.ersj_count_pass.argtypes = [vp, ctypes.POINTER(u64), vp]
     L.ersj_plan_batches.argtypes = [vp, u64, ctypes.POINTER(i32), vp]
     L.ersj_fill_pass.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
@@ -98,8 +101,8 @@ def lib():
     L.ersj_free.restype = None
     L.ersj_last_error.argtypes = []
     L.ersj_last_error.restype = ctypes.c_char_p
-    for f in ("ersj_build_index", "ersj_count_pass", "ersj_plan_batches", "ersj_fill_pass",
-              "ersj_batch_info", "ersj_get_stats"):
+    for f in ("ersj_build_index", "ersj_set_queries", "ersj_count_pass", "ersj_plan_batches",
+              "ersj_fill_pass", "ersj_batch_info", "ersj_get_stats"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -157,6 +160,25 @@ def build_index(x: torch.Tensor, eps: float, options: Options = None, stream=Non
     _check(lib().ersj_build_index(ctypes.c_void_p(x.data_ptr()), n, d, x.stride(0), float(eps), opt,
                                   _stream(stream), ctypes.byref(out)))
     return Index(out.value, n, d)
+
+
+def _rows_tensor(x, what):
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.dim() != 2:
+        raise TypeError(f"{what} must be a 2-D torch.float32 tensor")
+    if not x.is_cuda:
+        raise TypeError(f"{what} must live on the GPU")
+    if x.stride(1) != 1:
+        raise ValueError(f"{what} rows must be contiguous (stride(1) == 1)")
+
+
+def set_queries(h: Index, q: torch.Tensor, stream=None):
+    """``ersj_set_queries``: make the float32 [nq, d] CUDA tensor ``q`` the query
+    rows of a semi-join against the indexed points."""
+    _rows_tensor(q, "q")
+    if q.shape[1] != h.d:
+        raise ValueError(f"q has {q.shape[1]} columns, the index {h.d}")
+    _check(lib().ersj_set_queries(h.handle, ctypes.c_void_p(q.data_ptr()), q.shape[0], q.stride(0),
+                                  _stream(stream)))
 
 
 def count_pass(h: Index, stream=None) -> int:
@@ -235,6 +257,25 @@ def self_join(x: torch.Tensor, eps: float, budget_bytes: int = 0, options: Optio
     """All pairs within eps of the rows of ``x``: list of per-batch [m, 2] int32 tensors."""
     h = build_index(x, eps, options, stream)
     try:
+        count_pass(h, stream)
+        nb = plan_batches(h, budget_bytes, stream)
+        parts = list(iter_batches(h, nb, stream))
+    except Exception:
+        h.free()
+        raise
+    if return_index:
+        return parts, h
+    h.free()
+    return parts
+
+
+def semi_join(q: torch.Tensor, x: torch.Tensor, eps: float, budget_bytes: int = 0,
+              options: Options = None, stream=None, return_index: bool = False):
+    """All (query row of ``q``, row of ``x``) pairs within eps: list of per-batch
+    [m, 2] int32 tensors (RT-HiSS Sec. II-A, the semi-join)."""
+    h = build_index(x, eps, options, stream)
+    try:
+        set_queries(h, q, stream)
         count_pass(h, stream)
         nb = plan_batches(h, budget_bytes, stream)
         parts = list(iter_batches(h, nb, stream))

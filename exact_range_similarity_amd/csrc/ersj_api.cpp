@@ -79,6 +79,18 @@ struct ersj_index {
     uint32_t *cell_start = nullptr;
     uint64_t *cell_key = nullptr;
     uint32_t *lo_bits = nullptr, *hi_bits = nullptr;
+    // query rows: the points themselves for the self-join (these alias the
+    // arrays above), a separate set binned into the same grid after
+    // ersj_set_queries (the semi-join)
+    bool semi = false;
+    int64_t nq = 0;
+    float4 *xq = nullptr;
+    uint32_t *qorig = nullptr;
+    int64_t Mq = 0;
+    uint32_t *qcell_start = nullptr;
+    uint64_t *qcell_key = nullptr;
+    uint32_t *qlo_bits = nullptr, *qhi_bits = nullptr;
+    double maxabs_q = 0.0;
     // count pass
     uint32_t *rstart = nullptr, *rpref = nullptr, *nrng = nullptr;
     uint32_t umax = 0;
@@ -243,7 +255,8 @@ bool mfma_feasible(const ersj_index *h, const char **why)
         *why = "query tile exceeds the 160 KiB LDS (d too large)";
         return false;
     }
-    if (16.0 * dp * h->maxabs * h->maxabs >= 1e38) {
+    const double m = std::max(h->maxabs, h->maxabs_q);  // points and query rows
+    if (16.0 * dp * m * m >= 1e38) {
         *why = "coordinates too large for fp32 norms";
         return false;
     }
@@ -317,12 +330,68 @@ void release_plan(ersj_index *h)
     h->ready_batch = -1;
 }
 
-int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
+// Rows binned into the grid (A4-A7): Morton keys of their cells (clamped as
+// points or as queries), stable radix sort, gather into the
+// dimension-blocked variance-ordered layout, runs of equal keys = cells and
+// their boxes on the grid axes.
+struct Binned {
+    float4 *xs = nullptr;
+    uint32_t *orig = nullptr;
+    int64_t M = 0;
+    uint32_t *cell_start = nullptr;
+    uint64_t *cell_key = nullptr;
+    uint32_t *lo_bits = nullptr, *hi_bits = nullptr;
+};
+
+int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries, Binned *out, hipStream_t s)
 {
-    const int64_t n = h->n;
     const int32_t d = h->d;
     Scratch tmp(h);
-    // A1: per-dimension statistics and the non-finite check.
+    uint64_t *k0 = nullptr, *k1 = nullptr, *hist = nullptr, *stmp = nullptr;
+    uint32_t *v1 = nullptr;
+    TRY(tmp.get(&k0, (size_t)n, "keys"));
+    TRY(tmp.get(&k1, (size_t)n, "keys"));
+    TRY(tmp.get(&v1, (size_t)n, "keys"));
+    const size_t hent = radix_hist_entries(n);
+    TRY(tmp.get(&hist, hent, "sort"));
+    TRY(tmp.get(&stmp, std::max(scan_tmp_entries(hent), scan_tmp_entries(n + 1)), "scan"));
+    TRY(dalloc(h, &out->orig, (size_t)n, "orig"));
+    HIPC(launch_keys(x, n, ld, h->gp, queries, k0, out->orig, s), "keys kernel");
+    HIPC(radix_sort(k0, out->orig, k1, v1, n, 3 * h->gp.bits, hist, stmp, s), "radix sort");
+
+    int32_t *dperm = nullptr;
+    TRY(tmp.get(&dperm, (size_t)d, "perm"));
+    HIPC(hipMemcpyAsync(dperm, h->perm.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "perm copy");
+    TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
+    HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
+
+    uint32_t *flags = nullptr;
+    uint64_t *cid = nullptr;
+    TRY(tmp.get(&flags, (size_t)n, "cells"));
+    TRY(tmp.get(&cid, (size_t)n + 1, "cells"));
+    HIPC(launch_cell_flags(k0, n, flags, s), "cell flags");
+    HIPC(scan_u32(flags, cid, n, stmp, s), "cell scan");
+    uint64_t M = 0;
+    HIPC(hipMemcpyAsync(&M, cid + n, sizeof M, hipMemcpyDeviceToHost, s), "cell count copy");
+    TRY(sync(s, "cells"));
+    out->M = (int64_t)M;
+    TRY(dalloc(h, &out->cell_start, (size_t)M + 1, "cells"));
+    TRY(dalloc(h, &out->cell_key, (size_t)M, "cells"));
+    TRY(dalloc(h, &out->lo_bits, (size_t)M * 3, "cells"));
+    TRY(dalloc(h, &out->hi_bits, (size_t)M * 3, "cells"));
+    HIPC(launch_cell_scatter(k0, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
+    HIPC(launch_cell_aabb(out->xs, cid, n, (int64_t)M, out->lo_bits, out->hi_bits, s), "cell boxes");
+    TRY(sync(s, "bin"));
+    return ERSJ_OK;
+}
+
+// A1 for any row set: per-dimension statistics (binary64) and the count of
+// non-finite coordinates; returns the statistics on the host.
+int row_stats(ersj_index *h, const float *x, int64_t n, int64_t ld, std::vector<double> *hst,
+              hipStream_t s)
+{
+    const int32_t d = h->d;
+    Scratch tmp(h);
     const int64_t T = stats_threads(n, d);
     double *part = nullptr, *st = nullptr;
     uint32_t *badp = nullptr;
@@ -332,19 +401,49 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     TRY(tmp.get(&st, (size_t)d * 4, "stats"));
     TRY(tmp.get(&bad, 1, "stats"));
     HIPC(launch_stats(x, n, d, ld, part, badp, T, st, bad, s), "stats kernels");
-    std::vector<double> hst((size_t)d * 4);
+    hst->assign((size_t)d * 4, 0.0);
     unsigned long long hbad = 0;
-    HIPC(hipMemcpyAsync(hst.data(), st, sizeof(double) * d * 4, hipMemcpyDeviceToHost, s), "stats copy");
+    HIPC(hipMemcpyAsync(hst->data(), st, sizeof(double) * d * 4, hipMemcpyDeviceToHost, s), "stats copy");
     HIPC(hipMemcpyAsync(&hbad, bad, sizeof hbad, hipMemcpyDeviceToHost, s), "stats copy");
     TRY(sync(s, "stats"));
     if (hbad) return fail(ERSJ_ERR_INVALID_ARG, "input holds %llu non-finite coordinates", hbad);
-    h->maxabs = 0.0;
-    for (int k = 0; k < d; ++k)
-        h->maxabs = std::max(h->maxabs, std::max(std::fabs(hst[k * 4 + 2]), std::fabs(hst[k * 4 + 3])));
+    return ERSJ_OK;
+}
+
+double max_abs(const std::vector<double> &hst, int32_t d)
+{
+    double m = 0.0;
+    for (int k = 0; k < d; ++k) m = std::max(m, std::max(std::fabs(hst[k * 4 + 2]), std::fabs(hst[k * 4 + 3])));
+    return m;
+}
+
+// The self-join's query rows are the points.
+void alias_queries(ersj_index *h)
+{
+    h->semi = false;
+    h->nq = h->n;
+    h->xq = h->xs;
+    h->qorig = h->orig;
+    h->Mq = h->M;
+    h->qcell_start = h->cell_start;
+    h->qcell_key = h->cell_key;
+    h->qlo_bits = h->lo_bits;
+    h->qhi_bits = h->hi_bits;
+    h->maxabs_q = h->maxabs;
+}
+
+int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
+{
+    const int64_t n = h->n;
+    const int32_t d = h->d;
+    // A1: per-dimension statistics and the non-finite check.
+    std::vector<double> hst;
+    TRY(row_stats(h, x, n, ld, &hst, s));
+    h->maxabs = max_abs(hst, d);
 
     // A2: dimensions by descending variance (ties: lower id first); the first
     // three are the grid axes.  Cell width >= eps*(1 + 2^-20), widened so no
-    // axis has more than 2^21 cells.
+    // axis has more than 2^21 - 2 cells (stored coordinates run to G + 1).
     h->perm.resize(d);
     for (int k = 0; k < d; ++k) h->perm[k] = k;
     std::stable_sort(h->perm.begin(), h->perm.end(),
@@ -354,7 +453,8 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     GridParams gp{};
     gp.ndim = std::min(3, d);
     const double scale = h->opt.cell_width_scale > 1.0 ? h->opt.cell_width_scale : 1.0;
-    int bits = 0;
+    const double gmax = std::ldexp(1.0, 21) - 2.0;
+    int bits = 1;
     for (int a = 0; a < 3; ++a) {
         gp.dim[a] = a < gp.ndim ? h->perm[a] : 0;
         gp.lo[a] = 0.0;
@@ -365,67 +465,77 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
         const double range = mx - mn;
         gp.lo[a] = mn;
         double w = h->eps * scale * (1.0 + std::ldexp(1.0, -20));
-        w = std::max(w, range / (std::ldexp(1.0, 21) - 1.0));
+        w = std::max(w, range / (gmax - 1.0));
         if (!(w > 0.0)) w = 1.0;
         gp.w[a] = w;
         double g = std::isinf(w) ? 1.0 : std::floor(range / w) + 1.0;
-        g = std::min(g, std::ldexp(1.0, 21));
+        g = std::min(g, gmax);
         gp.G[a] = (int32_t)g;
-        bits = std::max(bits, ceil_log2((uint64_t)gp.G[a]));
+        bits = std::max(bits, ceil_log2((uint64_t)gp.G[a] + 2));
     }
     gp.bits = bits;
     h->gp = gp;
 
-    // A4-A5: Morton keys of the cells, stable radix sort of (key, row id).
-    uint64_t *k0 = nullptr, *k1 = nullptr, *hist = nullptr, *stmp = nullptr;
-    uint32_t *v1 = nullptr;
-    TRY(tmp.get(&k0, (size_t)n, "keys"));
-    TRY(tmp.get(&k1, (size_t)n, "keys"));
-    TRY(tmp.get(&v1, (size_t)n, "keys"));
-    const size_t hent = radix_hist_entries(n);
-    TRY(tmp.get(&hist, hent, "sort"));
-    TRY(tmp.get(&stmp, std::max(scan_tmp_entries(hent), scan_tmp_entries(n + 1)), "scan"));
-    TRY(dalloc(h, &h->orig, (size_t)n, "orig"));
-    HIPC(launch_keys(x, n, ld, gp, k0, h->orig, s), "keys kernel");
-    HIPC(radix_sort(k0, h->orig, k1, v1, n, 3 * bits, hist, stmp, s), "radix sort");
-
-    // A6: gather into the dimension-blocked, variance-ordered layout.
-    int32_t *dperm = nullptr;
-    TRY(tmp.get(&dperm, (size_t)d, "perm"));
-    HIPC(hipMemcpyAsync(dperm, h->perm.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "perm copy");
-    TRY(dalloc(h, &h->xs, (size_t)h->nb * n, "points"));
-    HIPC(launch_gather(x, n, d, ld, h->orig, dperm, h->xs, s), "gather kernel");
+    // A4-A7 for the points.
+    Binned b;
+    TRY(bin_rows(h, x, n, ld, false, &b, s));
+    h->xs = b.xs;
+    h->orig = b.orig;
+    h->M = b.M;
+    h->cell_start = b.cell_start;
+    h->cell_key = b.cell_key;
+    h->lo_bits = b.lo_bits;
+    h->hi_bits = b.hi_bits;
     TRY(dalloc(h, &h->d_pinv, (size_t)d, "pinv"));
     HIPC(hipMemcpyAsync(h->d_pinv, h->pinv.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "pinv copy");
-
-    // A7: cells = runs of equal keys; their boxes on the grid axes.
-    uint32_t *flags = nullptr;
-    uint64_t *cid = nullptr;
-    TRY(tmp.get(&flags, (size_t)n, "cells"));
-    TRY(tmp.get(&cid, (size_t)n + 1, "cells"));
-    HIPC(launch_cell_flags(k0, n, flags, s), "cell flags");
-    HIPC(scan_u32(flags, cid, n, stmp, s), "cell scan");
-    uint64_t M = 0;
-    HIPC(hipMemcpyAsync(&M, cid + n, sizeof M, hipMemcpyDeviceToHost, s), "cell count copy");
-    TRY(sync(s, "cells"));
-    h->M = (int64_t)M;
-    TRY(dalloc(h, &h->cell_start, (size_t)M + 1, "cells"));
-    TRY(dalloc(h, &h->cell_key, (size_t)M, "cells"));
-    TRY(dalloc(h, &h->lo_bits, (size_t)M * 3, "cells"));
-    TRY(dalloc(h, &h->hi_bits, (size_t)M * 3, "cells"));
-    HIPC(launch_cell_scatter(k0, flags, cid, n, h->cell_start, h->cell_key, s), "cell scatter");
-    HIPC(launch_cell_aabb(h->xs, cid, n, (int64_t)M, h->lo_bits, h->hi_bits, s), "cell boxes");
     TRY(sync(s, "build"));
+    alias_queries(h);
     thresholds(h);
     TRY(choose_kernel(h));
     return ERSJ_OK;
+}
+
+// Semi-join query rows (Sec. II-A): statistics for the non-finite check and
+// the coordinate bound, then the same binning as the points, into the
+// points' grid.
+int do_queries(ersj_index *h, const float *q, int64_t nq, int64_t ldq, hipStream_t s)
+{
+    std::vector<double> hst;
+    TRY(row_stats(h, q, nq, ldq, &hst, s));
+    Binned b;
+    TRY(bin_rows(h, q, nq, ldq, true, &b, s));
+    h->semi = true;
+    h->nq = nq;
+    h->xq = b.xs;
+    h->qorig = b.orig;
+    h->Mq = b.M;
+    h->qcell_start = b.cell_start;
+    h->qcell_key = b.cell_key;
+    h->qlo_bits = b.lo_bits;
+    h->qhi_bits = b.hi_bits;
+    h->maxabs_q = max_abs(hst, h->d);
+    TRY(choose_kernel(h));
+    return ERSJ_OK;
+}
+
+void release_queries(ersj_index *h)
+{
+    if (h->semi) {
+        dfree(h, h->xq);
+        dfree(h, h->qorig);
+        dfree(h, h->qcell_start);
+        dfree(h, h->qcell_key);
+        dfree(h, h->qlo_bits);
+        dfree(h, h->qhi_bits);
+    }
+    alias_queries(h);
 }
 
 int do_count(ersj_index *h, hipStream_t s)
 {
     release_count(h);
     release_plan(h);
-    const int64_t M = h->M;
+    const int64_t M = h->Mq;  // cells of the query rows
     Scratch tmp(h);
     uint32_t *tpc = nullptr;
     unsigned int *umax = nullptr;
@@ -436,14 +546,16 @@ int do_count(ersj_index *h, hipStream_t s)
     TRY(tmp.get(&tpc, (size_t)M, "tiles"));
     TRY(tmp.get(&umax, 1, "tiles"));
     TRY(tmp.get(&tbase, (size_t)M + 1, "tiles"));
-    TRY(tmp.get(&stmp, scan_tmp_entries(std::max<int64_t>(M, h->n) + 1), "scan"));
+    TRY(tmp.get(&stmp, scan_tmp_entries(std::max<int64_t>(M, h->nq) + 1), "scan"));
     // Box pruning: drop neighbour cell B if its box lower distance to A's box
     // exceeds eps.  Computed in binary64 with relative error below 8u; the
     // margin keeps every pair with D64 <= E64 (|D64 - S| <= g64*S).
     const double pf = 1.0 + std::max(std::ldexp(1.0, -40), 16.0 * (h->d + 2) * std::ldexp(1.0, -53));
     const double prune_e2 = std::isinf(h->e64) ? INFINITY : h->e64 * pf;
-    HIPC(launch_stencil(h->cell_key, h->cell_start, h->lo_bits, h->hi_bits, M, h->gp, prune_e2,
-                        h->rstart, h->rpref, h->nrng, tpc, umax, s), "stencil kernel");
+    const CellSet home{h->qcell_key, h->qcell_start, h->qlo_bits, h->qhi_bits, h->Mq};
+    const CellSet target{h->cell_key, h->cell_start, h->lo_bits, h->hi_bits, h->M};
+    HIPC(launch_stencil(home, target, h->gp, prune_e2, h->rstart, h->rpref, h->nrng, tpc, umax, s),
+         "stencil kernel");
     HIPC(scan_u32(tpc, tbase, M, stmp, s), "tile scan");
     uint64_t T = 0;
     HIPC(hipMemcpyAsync(&T, tbase + M, sizeof T, hipMemcpyDeviceToHost, s), "tile count copy");
@@ -455,7 +567,7 @@ int do_count(ersj_index *h, hipStream_t s)
     TRY(dalloc(h, &h->coff, (size_t)T + 1, "tiles"));
     TRY(tmp.get(&words, (size_t)T, "tiles"));
     TRY(tmp.get(&cands, (size_t)T, "tiles"));
-    HIPC(launch_tiles(tbase, M, (int64_t)T, h->cell_start, h->rpref, h->nrng, h->tiles, words, cands, s),
+    HIPC(launch_tiles(tbase, M, (int64_t)T, h->qcell_start, h->rpref, h->nrng, h->tiles, words, cands, s),
          "tiles kernel");
     HIPC(scan_u64(words, h->toff, (int64_t)T, stmp, s), "word scan");
     HIPC(scan_u64(cands, h->coff, (int64_t)T, stmp, s), "candidate scan");
@@ -471,7 +583,7 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
     if (budget_bytes == 0) {
         size_t fr = 0, tot = 0;
         HIPC(hipMemGetInfo(&fr, &tot), "hipMemGetInfo");
-        const uint64_t extra = (uint64_t)h->n * 24 + (uint64_t)(1 << 22) * sizeof(Boundary);
+        const uint64_t extra = (uint64_t)h->nq * 24 + (uint64_t)(1 << 22) * sizeof(Boundary);
         uint64_t b = (uint64_t)fr / 4 * 3;
         budget_bytes = b > extra ? b - extra : 8;
         if (h->opt.max_device_bytes) {
@@ -491,7 +603,7 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
     TRY(tmp.get(&wordb, (size_t)T + 1, "plan"));
     TRY(tmp.get(&candb, (size_t)T + 1, "plan"));
     TRY(tmp.get(&res, 4, "plan"));
-    HIPC(launch_plan(h->toff, h->coff, h->tiles, T, h->n, budget_words, bounds, rowb, wordb, candb, res, s),
+    HIPC(launch_plan(h->toff, h->coff, h->tiles, T, h->nq, budget_words, bounds, rowb, wordb, candb, res, s),
          "plan kernel");
     uint64_t hres[4];
     HIPC(hipMemcpyAsync(hres, res, sizeof hres, hipMemcpyDeviceToHost, s), "plan copy");
@@ -589,6 +701,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     RefineArgs a{};
     a.xs = h->xs;
     a.n = (uint64_t)h->n;
+    a.xq = h->xq;
+    a.nqr = (uint64_t)h->nq;
     a.nb = h->nb;
     a.tiles = h->tiles;
     a.order = h->order;
@@ -653,8 +767,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     }
     if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
-    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->d,
-                        h->d_pinv, h->e64, h->mask, hits, s), "re-check kernel");
+    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->xq,
+                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, hits, s), "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
     HIPC(launch_rowcount(h->tiles, t0, ntiles, h->toff, a.wbase, h->hrows[b], h->mask, h->rowcnt, s),
@@ -760,6 +874,42 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
     return ERSJ_OK;
 }
 
+int ersj_set_queries(ersj_index *h, const float *d_q, int64_t nq, int64_t ldq, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!d_q) return fail(ERSJ_ERR_INVALID_ARG, "d_q is NULL");
+    if (nq < 1 || nq > 0xffffffffll)
+        return fail(ERSJ_ERR_INVALID_ARG, "nq = %lld outside [1, 2^32-1]", (long long)nq);
+    if (ldq < h->d) return fail(ERSJ_ERR_INVALID_ARG, "ldq = %lld < d = %d", (long long)ldq, h->d);
+    if (ldq > (int64_t)1 << 40) return fail(ERSJ_ERR_INVALID_ARG, "ldq = %lld too large", (long long)ldq);
+    if (h->state < kBuilt) return fail(ERSJ_ERR_STATE, "index not built");
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    // whatever was counted or planned belongs to the previous query rows
+    release_plan(h);
+    release_count(h);
+    h->nbatch = 0;
+    h->ready_batch = -1;
+    h->total_cand = h->total_words = 0;
+    h->T = 0;
+    h->state = kBuilt;
+    release_queries(h);
+    timer_start(h, s);
+    int rc = do_queries(h, d_q, nq, ldq, s);
+    h->ms_build += timer_stop(h, s);
+    if (rc != ERSJ_OK) {
+        std::string keep = g_err;
+        (void)hipStreamSynchronize(s);
+        release_queries(h);
+        (void)choose_kernel(h);
+        g_err = keep;
+        return rc;
+    }
+    return ERSJ_OK;
+}
+
 int ersj_count_pass(ersj_index *h, uint64_t *total_candidates, void *stream)
 {
     g_err.clear();
@@ -828,7 +978,8 @@ int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t cap
     const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
     timer_start(h, s);
     HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
-                       h->roff, h->rstart, h->rpref, h->nrng, h->orig, d_pairs, s), "expand kernel");
+                       h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
+         "expand kernel");
     h->ms_expand += timer_stop(h, s);
     return ERSJ_OK;
 }
@@ -853,6 +1004,7 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     if (!h || !o) return fail(ERSJ_ERR_INVALID_ARG, "NULL argument");
     std::memset(o, 0, sizeof *o);
     o->n = h->n;
+    o->n_queries = h->nq;
     o->d = h->d;
     for (int a = 0; a < 3; ++a) {
         o->index_dims[a] = a < h->gp.ndim ? h->gp.dim[a] : -1;

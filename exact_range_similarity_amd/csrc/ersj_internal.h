@@ -48,7 +48,7 @@ struct GridParams {
     double w[3];
     int32_t G[3];
     int32_t ndim;     // grid dimensions in use (min(d, 3))
-    int32_t bits;     // Morton bits per dimension
+    int32_t bits;     // Morton bits per dimension (coordinates 0 .. G + 1)
 };
 
 // ---- index construction (k_index.hip) ----
@@ -57,7 +57,12 @@ hipError_t launch_stats(const float *x, int64_t n, int32_t d, int64_t ld, double
                         unsigned long long *out_bad, hipStream_t s);
 int64_t stats_threads(int64_t n, int32_t d);
 
-hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp,
+// Morton keys of the cells; cell coordinates are stored plus one, so that a
+// query of a semi-join one cell outside the points' grid (coordinate -1 or G)
+// still has a key.  Points clamp to [0, G-1], queries (`queries` set) to
+// [-1, G]: a query further out has no neighbour, and the clamp only adds
+// candidates that refinement rejects.
+hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp, bool queries,
                        uint64_t *keys, uint32_t *ids, hipStream_t s);
 
 // LSD radix sort of (key, value) pairs on the low `bits` bits of the keys.
@@ -83,11 +88,17 @@ hipError_t launch_cell_scatter(const uint64_t *keys, const uint32_t *flags, cons
 hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, int64_t M,
                             uint32_t *lo_bits, uint32_t *hi_bits, hipStream_t s);
 
-hipError_t launch_stencil(const uint64_t *cell_key, const uint32_t *cell_start,
-                          const uint32_t *lo_bits, const uint32_t *hi_bits, int64_t M,
-                          const GridParams &gp, double prune_e2, uint32_t *rstart,
-                          uint32_t *rpref, uint32_t *nrng, uint32_t *tiles_per_cell,
-                          unsigned int *umax, hipStream_t s);
+// Cells of the query rows (home: the points themselves for the self-join)
+// against the cells of the points (target).
+struct CellSet {
+    const uint64_t *key;
+    const uint32_t *start;
+    const uint32_t *lo_bits, *hi_bits;
+    int64_t M;
+};
+hipError_t launch_stencil(const CellSet &home, const CellSet &target, const GridParams &gp,
+                          double prune_e2, uint32_t *rstart, uint32_t *rpref, uint32_t *nrng,
+                          uint32_t *tiles_per_cell, unsigned int *umax, hipStream_t s);
 
 hipError_t launch_tiles(const uint64_t *tile_base, int64_t M, int64_t T,
                         const uint32_t *cell_start, const uint32_t *rpref, const uint32_t *nrng,
@@ -154,8 +165,10 @@ __device__ __forceinline__ Boundary *band_list(Boundary *blist, uint64_t lcap)
 }
 
 struct RefineArgs {
-    const float4 *xs;
+    const float4 *xs;    // points (candidates), dimension-blocked
     uint64_t n;
+    const float4 *xq;    // query rows, same layout (== xs for the self-join)
+    uint64_t nqr;
     int32_t nb;
     const Tile *tiles;
     const uint32_t *order;
@@ -191,8 +204,9 @@ hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s);
 hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, uint64_t *lpref,
                               uint64_t *out, hipStream_t s);
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float4 *xs, uint64_t n, int32_t d, const int32_t *pinv, double e64,
-                          uint64_t *mask, unsigned long long *nin, hipStream_t s);
+                          const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
+                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
+                          hipStream_t s);
 
 hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
                            uint64_t wbase, uint64_t row_base, const uint64_t *mask,
@@ -201,7 +215,7 @@ hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, cons
 hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
                          uint64_t wbase, uint64_t row_base, const uint64_t *mask,
                          const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
-                         const uint32_t *nrng, const uint32_t *orig, uint32_t *pairs,
-                         hipStream_t s);
+                         const uint32_t *nrng, const uint32_t *qorig, const uint32_t *orig,
+                         uint32_t *pairs, hipStream_t s);
 
 }  // namespace ersj

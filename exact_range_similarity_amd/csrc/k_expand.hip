@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kBandLists) void k_band_prefix(const unsigned long 
 __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t lcap,
                                                  const uint64_t *__restrict__ lpref, uint64_t cnt,
                                                  const float *__restrict__ xsf, uint64_t n,
+                                                 const float *__restrict__ xqf, uint64_t nqr,
                                                  int32_t d, const int32_t *__restrict__ pinv,
                                                  double e64, uint64_t *__restrict__ mask,
                                                  unsigned long long *__restrict__ nin)
@@ -69,9 +70,8 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         double s = 0.0;
         for (int k = 0; k < d; ++k) {
             const int p = sp[k];
-            const uint64_t off = ((uint64_t)(p >> 2) * n) * 4 + (p & 3);
-            const double a = (double)xsf[off + (uint64_t)e.q * 4];
-            const double b = (double)xsf[off + (uint64_t)e.x * 4];
+            const double a = (double)xqf[((uint64_t)(p >> 2) * nqr + e.q) * 4 + (p & 3)];
+            const double b = (double)xsf[((uint64_t)(p >> 2) * n + e.x) * 4 + (p & 3)];
             const double t = a - b;
             const double tt = t * t;
             s = s + tt;
@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                                                 const uint32_t *__restrict__ rstart,
                                                 const uint32_t *__restrict__ rpref,
                                                 const uint32_t *__restrict__ nrng,
+                                                const uint32_t *__restrict__ qorig,
                                                 const uint32_t *__restrict__ orig,
                                                 uint32_t *__restrict__ pairs)
 {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     const uint64_t tbase = toff[t] - wbase;
     for (uint32_t r = wave; r < tl.nrows; r += 4) {
         const uint32_t q = tl.row0 + r;
-        const uint32_t qid = orig[q];
+        const uint32_t qid = qorig[q];
         const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
         uint64_t out = roff[q - row_base];
         for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
@@ -170,13 +171,14 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 }
 
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float4 *xs, uint64_t n, int32_t d, const int32_t *pinv, double e64,
-                          uint64_t *mask, unsigned long long *nin, hipStream_t s)
+                          const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
+                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
+                          hipStream_t s)
 {
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
     hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt,
-                       (const float *)xs, n, d, pinv, e64, mask, nin);
+                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, nin);
     return hipGetLastError();
 }
 
@@ -193,11 +195,12 @@ hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, cons
 hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
                          uint64_t wbase, uint64_t row_base, const uint64_t *mask,
                          const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
-                         const uint32_t *nrng, const uint32_t *orig, uint32_t *pairs, hipStream_t s)
+                         const uint32_t *nrng, const uint32_t *qorig, const uint32_t *orig,
+                         uint32_t *pairs, hipStream_t s)
 {
     if (ntiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_expand, dim3(ntiles), dim3(256), 0, s, tiles, t0, toff, wbase, row_base, mask,
-                       roff, rstart, rpref, nrng, orig, pairs);
+                       roff, rstart, rpref, nrng, qorig, orig, pairs);
     return hipGetLastError();
 }
 

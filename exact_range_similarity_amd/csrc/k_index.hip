@@ -148,11 +148,12 @@ __global__ __launch_bounds__(kBlock) void k_stats_final(const float *__restrict_
 }
 
 // ----------------------------------------------------------------- keys --
-// Cell coordinate c = floor((x - lo) / w) in binary64, clamped to [0, G-1].
-// With w >= eps * (1 + 2^-20) two coordinates of a neighbour pair land in
-// cells at most one apart, so the 27-cell stencil is exhaustive.
+// Cell coordinate c = floor((x - lo) / w) in binary64, clamped to [0, G-1]
+// for points and to [-1, G] for semi-join queries, stored as c + 1.  With
+// w >= eps * (1 + 2^-20) two coordinates of a neighbour pair land in cells at
+// most one apart, so the 27-cell stencil is exhaustive.
 __global__ __launch_bounds__(kBlock) void k_keys(const float *__restrict__ x, int64_t n, int64_t ld,
-                                                 GridParams gp, uint64_t *__restrict__ keys,
+                                                 GridParams gp, int queries, uint64_t *__restrict__ keys,
                                                  uint32_t *__restrict__ ids)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -161,9 +162,13 @@ __global__ __launch_bounds__(kBlock) void k_keys(const float *__restrict__ x, in
     for (int a = 0; a < gp.ndim; ++a) {
         double v = (double)x[i * ld + gp.dim[a]];
         double c = floor((v - gp.lo[a]) / gp.w[a]);
-        int64_t ci = 0;
-        if (c > 0.0) ci = c >= (double)(gp.G[a] - 1) ? (int64_t)(gp.G[a] - 1) : (int64_t)c;
-        key |= spread3((uint64_t)ci) << a;
+        const double cmin = queries ? -1.0 : 0.0;
+        const double cmax = queries ? (double)gp.G[a] : (double)(gp.G[a] - 1);
+        int64_t ci;
+        if (!(c > cmin)) ci = (int64_t)cmin;  // also NaN-free: x is finite
+        else if (c >= cmax) ci = (int64_t)cmax;
+        else ci = (int64_t)c;
+        key |= spread3((uint64_t)(ci + 1)) << a;
     }
     keys[i] = key;
     ids[i] = (uint32_t)i;
@@ -446,30 +451,29 @@ __device__ __forceinline__ int64_t find_key(const uint64_t *__restrict__ k, int6
     return (lo < M && k[lo] == key) ? lo : -1;
 }
 
-// Per cell A: the neighbour cells B (offsets in {-1,0,1}^3) that exist and
-// whose box lower distance to A's box (binary64, over the grid dimensions)
-// does not exceed the pruning threshold.  Kept cells are sorted by index and
-// runs of consecutive cells are merged into one contiguous candidate range.
-__global__ __launch_bounds__(kBlock) void k_stencil(const uint64_t *__restrict__ cell_key,
-                                                    const uint32_t *__restrict__ cell_start,
-                                                    const uint32_t *__restrict__ lo_bits,
-                                                    const uint32_t *__restrict__ hi_bits, int64_t M,
-                                                    GridParams gp, double prune_e2,
-                                                    uint32_t *__restrict__ rstart,
+// Per home cell A (a cell of the query rows; of the points for the
+// self-join): the target cells B (cells of the points) at offsets in
+// {-1,0,1}^3 that exist and whose box lower distance to A's box (binary64,
+// over the grid dimensions) does not exceed the pruning threshold.  Kept
+// cells are sorted by index and runs of consecutive cells are merged into one
+// contiguous candidate range.  A query cell with no kept cell gets one empty
+// range (U = 0).
+__global__ __launch_bounds__(kBlock) void k_stencil(CellSet home, CellSet target, GridParams gp,
+                                                    double prune_e2, uint32_t *__restrict__ rstart,
                                                     uint32_t *__restrict__ rpref,
                                                     uint32_t *__restrict__ nrng,
                                                     uint32_t *__restrict__ tiles_per_cell,
                                                     unsigned int *__restrict__ umax)
 {
     const int64_t A = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (A >= M) return;
-    const uint64_t key = cell_key[A];
+    if (A >= home.M) return;
+    const uint64_t key = home.key[A];
     int64_t c[3];
     double alo[3], ahi[3];
     for (int a = 0; a < 3; ++a) {
         c[a] = (int64_t)compact3(key >> a);
-        alo[a] = (double)ord2f(lo_bits[A * 3 + a]);
-        ahi[a] = (double)ord2f(hi_bits[A * 3 + a]);
+        alo[a] = (double)ord2f(home.lo_bits[A * 3 + a]);
+        ahi[a] = (double)ord2f(home.hi_bits[A * 3 + a]);
     }
     uint32_t kept[kMaxRanges];
     int nk = 0;
@@ -479,25 +483,24 @@ __global__ __launch_bounds__(kBlock) void k_stencil(const uint64_t *__restrict__
         bool ok = true;
         for (int a = 0; a < 3; ++a) {
             const int64_t v = c[a] + dlt[a];
-            const int64_t G = a < gp.ndim ? gp.G[a] : 1;
+            // stored coordinates run 0 .. G + 1 on a grid axis, 0 elsewhere
+            const int64_t G = a < gp.ndim ? (int64_t)gp.G[a] + 2 : 1;
             if (v < 0 || v >= G) ok = false;
             else nkey |= spread3((uint64_t)v) << a;
         }
         if (!ok) continue;
-        const int64_t B = (nkey == key) ? A : find_key(cell_key, M, nkey);
+        const int64_t B = find_key(target.key, target.M, nkey);
         if (B < 0) continue;
-        if (B != A) {
-            double dl2 = 0.0;
-            for (int a = 0; a < 3; ++a) {
-                const double blo = (double)ord2f(lo_bits[B * 3 + a]);
-                const double bhi = (double)ord2f(hi_bits[B * 3 + a]);
-                double gap = 0.0;
-                if (blo > ahi[a]) gap = blo - ahi[a];
-                else if (alo[a] > bhi) gap = alo[a] - bhi;
-                dl2 += gap * gap;
-            }
-            if (dl2 > prune_e2) continue;
+        double dl2 = 0.0;
+        for (int a = 0; a < 3; ++a) {
+            const double blo = (double)ord2f(target.lo_bits[B * 3 + a]);
+            const double bhi = (double)ord2f(target.hi_bits[B * 3 + a]);
+            double gap = 0.0;
+            if (blo > ahi[a]) gap = blo - ahi[a];
+            else if (alo[a] > bhi) gap = alo[a] - bhi;
+            dl2 += gap * gap;
         }
+        if (dl2 > prune_e2) continue;
         kept[nk++] = (uint32_t)B;
     }
     for (int i = 1; i < nk; ++i) {
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void k_stencil(const uint64_t *__restrict__
     uint32_t nr = 0, U = 0;
     uint32_t cur_start = 0, cur_len = 0;
     for (int i = 0; i < nk; ++i) {
-        const uint32_t st = cell_start[kept[i]], len = cell_start[kept[i] + 1] - st;
+        const uint32_t st = target.start[kept[i]], len = target.start[kept[i] + 1] - st;
         if (i > 0 && kept[i] == kept[i - 1] + 1) {
             cur_len += len;
         } else {
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(kBlock) void k_stencil(const uint64_t *__restrict__
     for (int g = nr; g <= kMaxRanges; ++g) rpref[A * (kMaxRanges + 1) + g] = U;
     for (int g = nr; g < kMaxRanges; ++g) rstart[A * kMaxRanges + g] = 0;
     nrng[A] = nr;
-    const uint32_t sz = cell_start[A + 1] - cell_start[A];
+    const uint32_t sz = home.start[A + 1] - home.start[A];
     tiles_per_cell[A] = (sz + kTileRows - 1) / kTileRows;
     atomicMax(umax, U);
 }
@@ -666,10 +669,11 @@ hipError_t launch_stats(const float *x, int64_t n, int32_t d, int64_t ld, double
     return hipGetLastError();
 }
 
-hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp, uint64_t *keys,
-                       uint32_t *ids, hipStream_t s)
+hipError_t launch_keys(const float *x, int64_t n, int64_t ld, const GridParams &gp, bool queries,
+                       uint64_t *keys, uint32_t *ids, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, ld, gp, keys, ids);
+    hipLaunchKernelGGL(k_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, ld, gp, (int)queries, keys,
+                       ids);
     return hipGetLastError();
 }
 
@@ -756,15 +760,14 @@ hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, in
     return hipGetLastError();
 }
 
-hipError_t launch_stencil(const uint64_t *cell_key, const uint32_t *cell_start,
-                          const uint32_t *lo_bits, const uint32_t *hi_bits, int64_t M,
-                          const GridParams &gp, double prune_e2, uint32_t *rstart, uint32_t *rpref,
-                          uint32_t *nrng, uint32_t *tiles_per_cell, unsigned int *umax,
-                          hipStream_t s)
+hipError_t launch_stencil(const CellSet &home, const CellSet &target, const GridParams &gp,
+                          double prune_e2, uint32_t *rstart, uint32_t *rpref, uint32_t *nrng,
+                          uint32_t *tiles_per_cell, unsigned int *umax, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(kBlock), 0, s, umax, 0u, 1);
-    hipLaunchKernelGGL(k_stencil, dim3(grid_for(M)), dim3(kBlock), 0, s, cell_key, cell_start,
-                       lo_bits, hi_bits, M, gp, prune_e2, rstart, rpref, nrng, tiles_per_cell, umax);
+    if (home.M == 0) return hipGetLastError();
+    hipLaunchKernelGGL(k_stencil, dim3(grid_for(home.M)), dim3(kBlock), 0, s, home, target, gp, prune_e2,
+                       rstart, rpref, nrng, tiles_per_cell, umax);
     return hipGetLastError();
 }
 

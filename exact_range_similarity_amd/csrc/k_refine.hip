@@ -68,6 +68,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)(r_begin + kq0) * tl.words;
     const uint64_t n = a.n;
     const float4 *__restrict__ xs = a.xs;
+    const float4 *__restrict__ xq = a.xq;  // query rows (the points themselves in a self-join)
     uint64_t *__restrict__ mask = a.mask;
     Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
     unsigned long long *__restrict__ bcount = band_counter(a.bcount);
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
             for (int j = 0; j < kCW; ++j) xv4[j] = xb[xi[j]];
 #pragma unroll
             for (int k = 0; k < kQW; ++k) {
-                const float4 q = xb[qrow[k]];
+                const float4 q = xq[(uint64_t)b * a.nqr + qrow[k]];
 #pragma unroll
                 for (int j = 0; j < kCW; ++j) {
                     float t0 = q.x - xv4[j].x;

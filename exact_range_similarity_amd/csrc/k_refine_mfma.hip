@@ -154,6 +154,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const int tid = threadIdx.x;
     const uint64_t n = a.n;
     const float4 *__restrict__ xs = a.xs;
+    const float4 *__restrict__ xq = a.xq;  // query rows (the points themselves in a self-join)
+    const uint64_t nqr = a.nqr;
     uint64_t *__restrict__ mask = a.mask;
     Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
     unsigned long long *__restrict__ bcount = band_counter(a.bcount);
@@ -163,12 +165,12 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     if (tid <= kMaxRanges) L.pref[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
     if (tid < kMaxRanges) L.start[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
     for (int b = tid; b < nbs; b += 256)
-        L.r[b] = b < nb ? xs[(uint64_t)b * n + row0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        L.r[b] = b < nb ? xq[(uint64_t)b * nqr + row0] : make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
     for (int e = tid; e < nbs * G::QR; e += 256) {
         const int b = e / G::QR, i = e - b * G::QR;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (b < nb && (uint32_t)i < nrows) v = sub4(xs[(uint64_t)b * n + row0 + i], L.r[b]);
+        if (b < nb && (uint32_t)i < nrows) v = sub4(xq[(uint64_t)b * nqr + row0 + i], L.r[b]);
         L.q[e] = v;
     }
     __syncthreads();

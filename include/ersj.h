@@ -87,7 +87,7 @@ typedef struct ersj_stats {
     int32_t grid[3];             /* cells per grid dimension */
     int32_t refine_kernel;       /* kernel used (ERSJ_REFINE_DIRECT or _MFMA) */
     int64_t cells;               /* non-empty grid cells */
-    int64_t tiles;               /* row tiles (up to 32 rows of one cell) */
+    int64_t tiles;               /* row tiles (up to 128 query rows of one cell) */
     uint64_t total_candidates;   /* sum over queries of the candidate upper bound */
     uint64_t total_mask_words;   /* 64-bit mask words over all batches */
     int32_t n_batches;           /* from the last plan_batches */
@@ -102,6 +102,7 @@ typedef struct ersj_stats {
     double build_ms, count_ms, plan_ms, refine_ms, recheck_ms, expand_ms;
     int64_t refine_launches;     /* refine kernel launches timed in refine_ms */
     uint64_t refined_candidates; /* candidates refined in those launches */
+    int64_t n_queries;           /* query rows: n for the self-join, nq after ersj_set_queries */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */
@@ -120,6 +121,25 @@ void ersj_default_options(ersj_options *opt);
  */
 int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double eps,
                      const ersj_options *opt, void *stream, ersj_index **out);
+
+/*
+ * Semi-join (Sec. II-A: a query set Q distinct from the dataset D, the pair
+ * (q_j, p_i) in the result iff dist(p_i, q_j) <= eps; Sec. IV-D, Fig. 3(d):
+ * a query's candidates are the points of the index cells around it).  Bins
+ * the nq query rows into the index's grid; count_pass, plan_batches and
+ * fill_pass then work on these queries and fill_pass returns pairs (query
+ * row id in d_q, point id).  Without this call the queries are the points
+ * (the self-join).  Calling it again replaces the queries; either way the
+ * previous count and plan are discarded.
+ *  d_q : device, nq rows of d floats (d of the index), row r at d_q + r*ldq;
+ *        borrowed for the duration of the call (the stream is synchronised).
+ *  nq  : 1 <= nq <= 2^32 - 1;  ldq >= d.
+ * Errors: INVALID_ARG (also non-finite coordinates, and an explicitly chosen
+ *         MFMA kernel that the query coordinates make unusable), STATE (index
+ *         not built), HIP, OOM.  On error the handle is back in the self-join
+ *         state, built and not counted.
+ */
+int ersj_set_queries(ersj_index *h, const float *d_q, int64_t nq, int64_t ldq, void *stream);
 
 /*
  * Count pass (Sec. IV-D, "First Intersection Test" and pass 1): for each
