@@ -12,6 +12,10 @@ second over the whole join, plus the refinement kernel's roofline position
 oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu]
+                    [--mode semijoin [--nq NQ]]
+
+``--mode semijoin`` joins a separate query set (the workload's cluster
+structure, rows from another seed; RT-HiSS Sec. II-A) against the points.
 """
 import argparse
 import json
@@ -50,6 +54,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--mode", choices=("selfjoin", "semijoin"), default="selfjoin",
+                    help="semijoin: a separate query set from the workload's structure")
+    ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -60,7 +67,7 @@ def main():
     import numpy as np
     import torch
     import exact_range_similarity_amd as ersj
-    from workloads import CONFIGS, make_config, x_digest
+    from workloads import CONFIGS, make_config, make_queries, x_digest
 
     spec = CONFIGS[args.workload]
     rec = load_eps(args.workload)
@@ -74,12 +81,21 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     xt = torch.from_numpy(X).to(dev)
+    semi = args.mode == "semijoin"
+    Q, qt = X, None
+    if semi:
+        nq = args.nq if args.nq > 0 else X.shape[0]
+        Q = make_queries(args.workload, nq, spec.seed + 1000, X.shape[0])
+        qt = torch.from_numpy(Q).to(dev)
+        log(f"[bench] semi-join: {nq} queries from the workload's structure (seed {spec.seed + 1000})")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     budget = 0
     if args.budget_frac > 0:
         h = ersj.build_index(xt, eps)
+        if semi:
+            ersj.set_queries(h, qt)
         ersj.count_pass(h)
         budget = int(ersj.get_stats(h)["total_mask_words"] * 8 * args.budget_frac)
         h.free()
@@ -87,6 +103,8 @@ def main():
     def step(timing):
         opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine)
         h = ersj.build_index(xt, eps, opts, stream)
+        if semi:
+            ersj.set_queries(h, qt, stream)
         ersj.count_pass(h, stream)
         nb = ersj.plan_batches(h, budget, stream)
         npairs = 0
@@ -133,7 +151,7 @@ def main():
             trec = json.load(f)
         with open(os.path.join(ROOT, trec["source"]), "rb") as f:
             cur = hashlib.sha256(f.read()).hexdigest()
-        if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget:
+        if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget and not semi:
             traffic = trec["hbm_bytes_per_launch"]
     phases = {k: sum(s[k] for s in stats) / args.steps
               for k in ("build_ms", "count_ms", "plan_ms", "refine_ms", "recheck_ms", "expand_ms")}
@@ -152,7 +170,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {spec.desc}; eps for a mean of {spec.k} neighbours/point",
+            "workload": (f"{args.workload}: {spec.desc}; eps for a mean of {spec.k} neighbours/point"
+                         + (f"; semi-join of {Q.shape[0]} queries drawn from the same structure"
+                            if semi else "")),
+            "mode": args.mode, "n_queries": int(Q.shape[0]),
             "n": int(X.shape[0]), "d": int(d), "eps": rec["eps"], "k": spec.k, "seed": spec.seed,
             "batches": st["n_batches"], "budget_bytes": budget,
             "refine_kernel": {1: "direct", 2: "mfma"}.get(st["refine_kernel"], "?"),
@@ -191,23 +212,28 @@ def main():
 
     if not args.no_cpu:
         import oracle
+        def cpu_rows(rows):
+            if semi:
+                return oracle.semijoin_rows(Q, X, eps, rows)
+            return oracle.join_rows(X, eps, rows)
+
         rows_probe = 4 * oracle.threads()
         t = time.perf_counter()
-        oracle.join_rows(X, eps, np.arange(rows_probe))
+        cpu_rows(np.arange(rows_probe))
         per_row = (time.perf_counter() - t) / rows_probe
-        nrows = int(max(rows_probe, min(X.shape[0], args.cpu_seconds / max(per_row, 1e-9))))
+        nrows = int(max(rows_probe, min(Q.shape[0], args.cpu_seconds / max(per_row, 1e-9))))
         log(f"[bench] cpu oracle: {nrows} rows (~{per_row * nrows:.0f}s)")
         t = time.perf_counter()
-        colptr, _ = oracle.join_rows(X, eps, np.arange(nrows))
+        colptr, _ = cpu_rows(np.arange(nrows))
         dt = time.perf_counter() - t
         evals = nrows * X.shape[0]
         out["cpu_baseline"] = {
             "value": evals / dt, "unit": "candidate dist evals/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"rows 0..{nrows - 1} of {args.workload} against all {X.shape[0]} points "
-                      f"(brute force, binary64), {dt:.1f}s",
+            "sample": f"{'query ' if semi else ''}rows 0..{nrows - 1} of {args.workload} against all "
+                      f"{X.shape[0]} points (brute force, binary64), {dt:.1f}s",
             "sample_pairs": int(colptr[-1]),
-            "full_join_s_extrapolated": dt * X.shape[0] / nrows,
+            "full_join_s_extrapolated": dt * Q.shape[0] / nrows,
         }
     print(json.dumps(out), flush=True)
 

@@ -64,3 +64,18 @@ def test_eps_table_complete(name):
     assert rec["n"] == CONFIGS[name].n and rec["d"] == CONFIGS[name].d
     eps = float.fromhex(rec["eps"])
     assert math.isfinite(eps) and eps > 0
+
+
+def test_query_sets_share_the_structure_of_the_points():
+    from workloads import make_queries
+    for name in CONFIGS:
+        Q1 = make_queries(name, 3000, 11, 20000)
+        Q2 = make_queries(name, 3000, 11, 20000)
+        assert Q1.dtype == np.float32 and Q1.shape == (3000, CONFIGS[name].d) and Q1.flags.c_contiguous
+        assert np.array_equal(Q1, Q2)
+        assert not np.array_equal(Q1, make_queries(name, 3000, 12, 20000))
+    # same cluster centres as the points: every clustered query lies near some point
+    X = make_config("c2", 20000)
+    Q = make_queries("c2", 200, 11, 20000)
+    d2 = ((Q[:, None, :].astype(np.float64) - X[None, :, :]) ** 2).sum(-1).min(axis=1)
+    assert np.all(d2 < 0.05)

@@ -132,6 +132,54 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
     raise ValueError(f"unknown workload kind {spec.kind}")
 
 
+def make_queries(name: str, nq: int, seed: int, n_points: int = None) -> np.ndarray:
+    """A query set for a semi-join against ``make_config(name, n_points)``: the
+    same structure (cluster centres, per-cluster scales: the generator's first
+    draws from the workload's seed) with rows, labels and noise drawn from
+    ``seed``.  float32 [nq, d], C-contiguous."""
+    spec = CONFIGS[name]
+    n_points = spec.n if n_points is None else int(n_points)
+    nq = int(nq)
+    if nq < 1:
+        raise ValueError("nq must be positive")
+    d = spec.d
+    rs = np.random.default_rng(spec.seed)  # structure, drawn as make_config draws it
+    rng = np.random.default_rng(seed)
+    if spec.kind == "uniform":
+        return rng.random((nq, d), dtype=np.float32)
+    nc = _scaled_clusters(spec, n_points)
+    Q = np.empty((nq, d), dtype=np.float32)
+    if spec.kind in ("gauss_iso", "gauss_aniso", "mix_bg"):
+        C = rs.random((nc, d))
+        S = None
+        if spec.kind == "gauss_aniso":
+            S = np.exp(rs.uniform(math.log(spec.sig_lo), math.log(spec.sig_hi), (nc, d)))
+        ncl = int(round(spec.frac * nq)) if spec.kind == "mix_bg" else nq
+        L = rng.integers(0, nc, ncl)
+        for s0 in range(0, ncl, _CHUNK):
+            e = min(ncl, s0 + _CHUNK)
+            sc = S[L[s0:e]] if S is not None else spec.sigma
+            Q[s0:e] = C[L[s0:e]] + sc * rng.standard_normal((e - s0, d))
+        for s0 in range(ncl, nq, _CHUNK):
+            e = min(nq, s0 + _CHUNK)
+            Q[s0:e] = rng.random((e - s0, d))
+        if spec.kind == "mix_bg":
+            Q = np.ascontiguousarray(Q[rng.permutation(nq)])
+        return Q
+    if spec.kind == "embed":
+        C = rs.standard_normal((nc, d))
+        C /= np.linalg.norm(C, axis=1, keepdims=True)
+        L = rng.integers(0, nc, nq)
+        scale = spec.noise / math.sqrt(d)
+        for s0 in range(0, nq, _CHUNK):
+            e = min(nq, s0 + _CHUNK)
+            Y = C[L[s0:e]] + scale * rng.standard_normal((e - s0, d))
+            Y /= np.linalg.norm(Y, axis=1, keepdims=True)
+            Q[s0:e] = Y
+        return Q
+    raise ValueError(f"unknown workload kind {spec.kind}")
+
+
 def lattice(m: int, d: int, spacing: float = 1.0) -> np.ndarray:
     """All points of the integer box {0..m-1}^d times ``spacing``, row-major enumeration."""
     axes = [np.arange(m, dtype=np.float64)] * d
