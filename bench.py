@@ -57,6 +57,8 @@ def main():
     ap.add_argument("--mode", choices=("selfjoin", "semijoin"), default="selfjoin",
                     help="semijoin: a separate query set from the workload's structure")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
+    ap.add_argument("--no-host", action="store_true",
+                    help="skip the timing of the join delivered to pinned host memory")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -201,6 +203,36 @@ def main():
             "launches": launches,
         },
     }
+
+    if not args.no_host:
+        # The same join with every batch delivered to pinned host memory
+        # (fill_pass_host: batch b's copy overlaps batch b+1's refinement).
+        # Reported beside the device-resident figure, never as `value`.
+        host_buf = torch.empty((npairs + 1024, 2), dtype=torch.int32, pin_memory=True)
+
+        def host_step():
+            h = ersj.build_index(xt, eps, ersj.default_options(refine_kernel=args.refine), stream)
+            if semi:
+                ersj.set_queries(h, qt, stream)
+            ersj.count_pass(h, stream)
+            nb = ersj.plan_batches(h, budget, stream)
+            got = ersj.join_to_host(h, nb, host_buf, stream)
+            h.free()
+            return got.shape[0], nb
+
+        host_step()
+        torch.cuda.synchronize()
+        t0h = time.perf_counter()
+        for _ in range(args.steps):
+            hp, hnb = host_step()
+        torch.cuda.synchronize()
+        hwall = (time.perf_counter() - t0h) / args.steps
+        out["host_delivery"] = {
+            "ms_per_step": hwall * 1e3, "pairs": hp, "batches": hnb,
+            "pair_bytes_per_s": hp * 8 / hwall,
+            "note": "join + copy of every pair into pinned host memory; PCIe/xGMI-inclusive, not `value`",
+        }
+        log(f"[bench] host delivery: {hwall * 1e3:.1f} ms per step ({hnb} batches)")
 
     if args.copy_calib:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)

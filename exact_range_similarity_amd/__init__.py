@@ -71,8 +71,8 @@ class Stats(ctypes.Structure):
 
 _lib = None
 SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",
-           "ersj_plan_batches", "ersj_fill_pass", "ersj_batch_info", "ersj_get_stats", "ersj_free",
-           "ersj_last_error")
+           "ersj_plan_batches", "ersj_fill_pass", "ersj_fill_pass_host", "ersj_host_sync",
+           "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error")
 
 
 def lib():
@@ -94,6 +94,8 @@ def lib():
     L.ersj_count_pass.argtypes = [vp, ctypes.POINTER(u64), vp]
     L.ersj_plan_batches.argtypes = [vp, u64, ctypes.POINTER(i32), vp]
     L.ersj_fill_pass.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
+    L.ersj_fill_pass_host.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
+    L.ersj_host_sync.argtypes = [vp]
     L.ersj_batch_info.argtypes = [vp, i32, ctypes.POINTER(u64), ctypes.POINTER(u64),
                                   ctypes.POINTER(u64)]
     L.ersj_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
@@ -102,7 +104,8 @@ def lib():
     L.ersj_last_error.argtypes = []
     L.ersj_last_error.restype = ctypes.c_char_p
     for f in ("ersj_build_index", "ersj_set_queries", "ersj_count_pass", "ersj_plan_batches",
-              "ersj_fill_pass", "ersj_batch_info", "ersj_get_stats"):
+              "ersj_fill_pass", "ersj_fill_pass_host", "ersj_host_sync", "ersj_batch_info",
+              "ersj_get_stats"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
     return L
@@ -217,6 +220,67 @@ def fill_pass(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = 
         raise err
     _check(rc)
     return npairs.value
+
+
+def fill_pass_host(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = None,
+                   stream=None) -> int:
+    """``ersj_fill_pass_host``: refine batch ``batch`` and start copying its pairs
+    into ``pairs``, an int32 CPU tensor (pinned for an asynchronous copy) viewed
+    as [capacity, 2] uint32 ids.  The pairs are there after ``host_sync``.
+    Raises ErsjError(CAPACITY) with ``.required`` when it is too small."""
+    npairs = ctypes.c_uint64()
+    if pairs is None:
+        ptr, cap = None, 0
+    else:
+        if pairs.dtype != torch.int32 or pairs.is_cuda or not pairs.is_contiguous():
+            raise TypeError("pairs must be a contiguous int32 CPU tensor")
+        ptr = ctypes.c_void_p(pairs.data_ptr())
+        cap = pairs.numel() // 2 if capacity is None else int(capacity)
+        if cap * 2 > pairs.numel():
+            raise ValueError("capacity exceeds the tensor")
+    rc = lib().ersj_fill_pass_host(h.handle, int(batch), ptr, cap, ctypes.byref(npairs), _stream(stream))
+    if rc == ERR_CAPACITY:
+        err = ErsjError(rc, lib().ersj_last_error().decode(errors="replace"))
+        err.required = npairs.value
+        raise err
+    _check(rc)
+    return npairs.value
+
+
+def host_sync(h: Index):
+    _check(lib().ersj_host_sync(h.handle))
+
+
+def join_to_host(h: Index, n_batches: int, out: torch.Tensor = None, stream=None):
+    """Deliver every batch into host memory, each batch's copy overlapping the
+    next batch's refinement.  ``out``: an int32 CPU tensor [capacity, 2],
+    pinned, filled batch after batch (allocated, pinned, when None; it must
+    hold all pairs).  Returns the [|R|, 2] view of it with the pairs."""
+    counts, at = [], 0
+    if out is None:
+        parts = []
+        for b in range(n_batches):
+            try:
+                m = fill_pass_host(h, b, None, 0, stream)
+            except ErsjError as e:
+                if e.code != ERR_CAPACITY:
+                    raise
+                m = e.required
+            buf = torch.empty((m, 2), dtype=torch.int32, pin_memory=True)
+            if m:
+                fill_pass_host(h, b, buf, m, stream)
+            parts.append(buf)
+        host_sync(h)
+        if not parts:
+            return torch.empty((0, 2), dtype=torch.int32)
+        return parts[0] if len(parts) == 1 else torch.cat(parts)
+    for b in range(n_batches):
+        view = out[at:]
+        m = fill_pass_host(h, b, view, view.shape[0], stream)
+        counts.append(m)
+        at += m
+    host_sync(h)
+    return out[:at]
 
 
 def batch_info(h: Index, batch: int):

@@ -123,6 +123,14 @@ struct ersj_index {
     uint64_t refined_cand = 0;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t kernel_used = ERSJ_REFINE_DIRECT;
+    // host delivery: two device staging buffers, alternated by batch, drained
+    // into the caller's host memory on a copy stream of its own
+    hipStream_t copy_stream = nullptr;
+    uint32_t *stage[2] = {nullptr, nullptr};
+    uint64_t stage_cap[2] = {0, 0};
+    hipEvent_t expanded[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
+    bool copy_pending[2] = {false, false};
+    double ms_deliver = 0;  // host time waiting in ersj_host_sync
 };
 
 namespace {
@@ -788,6 +796,29 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     return ERSJ_OK;
 }
 
+int expand_batch(ersj_index *h, int32_t batch, uint32_t *d_pairs, hipStream_t s)
+{
+    const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
+    timer_start(h, s);
+    HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
+                       h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
+         "expand kernel");
+    h->ms_expand += timer_stop(h, s);
+    return ERSJ_OK;
+}
+
+// Copy stream (default priority) and its events, created on first use.
+int ensure_delivery(ersj_index *h)
+{
+    if (h->copy_stream) return ERSJ_OK;
+    HIPC(hipStreamCreateWithFlags(&h->copy_stream, hipStreamNonBlocking), "copy stream");
+    for (int k = 0; k < 2; ++k) {
+        HIPC(hipEventCreateWithFlags(&h->expanded[k], hipEventDisableTiming), "delivery event");
+        HIPC(hipEventCreateWithFlags(&h->copied[k], hipEventDisableTiming), "delivery event");
+    }
+    return ERSJ_OK;
+}
+
 }  // namespace
 
 // =================================================================== ABI ==
@@ -808,6 +839,15 @@ void ersj_free(ersj_index *h)
 {
     if (!h) return;
     DeviceGuard g(h->device);
+    if (h->copy_stream) {
+        // staging buffers may still be draining into host memory
+        (void)hipStreamSynchronize(h->copy_stream);
+        (void)hipStreamDestroy(h->copy_stream);
+        for (int k = 0; k < 2; ++k) {
+            if (h->expanded[k]) (void)hipEventDestroy(h->expanded[k]);
+            if (h->copied[k]) (void)hipEventDestroy(h->copied[k]);
+        }
+    }
     for (auto &kv : h->live) (void)hipFree(kv.first);
     h->live.clear();
     for (hipEvent_t &e : h->ev)
@@ -975,12 +1015,66 @@ int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t cap
         return fail(ERSJ_ERR_CAPACITY, "batch %d has %llu pairs, capacity is %llu", batch,
                     (unsigned long long)h->ready_pairs, (unsigned long long)capacity);
     if (h->ready_pairs == 0) return ERSJ_OK;
-    const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
-    timer_start(h, s);
-    HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
-                       h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
-         "expand kernel");
-    h->ms_expand += timer_stop(h, s);
+    return expand_batch(h, batch, d_pairs, s);
+}
+
+int ersj_fill_pass_host(ersj_index *h, int32_t batch, uint32_t *host_pairs, uint64_t capacity,
+                        uint64_t *n_pairs, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!n_pairs) return fail(ERSJ_ERR_INVALID_ARG, "n_pairs is NULL");
+    if (capacity > 0 && !host_pairs) return fail(ERSJ_ERR_INVALID_ARG, "host_pairs is NULL");
+    if (h->state < kPlanned) return fail(ERSJ_ERR_STATE, "plan_batches has not run");
+    if (batch < 0 || batch >= h->nbatch)
+        return fail(ERSJ_ERR_INVALID_ARG, "batch %d outside [0, %d)", batch, h->nbatch);
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    if (h->ready_batch != batch) {
+        h->ready_batch = -1;
+        int rc = do_refine(h, batch, s);
+        if (rc != ERSJ_OK) return rc;
+    }
+    *n_pairs = h->ready_pairs;
+    if (capacity < h->ready_pairs)
+        return fail(ERSJ_ERR_CAPACITY, "batch %d has %llu pairs, capacity is %llu", batch,
+                    (unsigned long long)h->ready_pairs, (unsigned long long)capacity);
+    if (h->ready_pairs == 0) return ERSJ_OK;
+    TRY(ensure_delivery(h));
+    const int k = batch & 1;
+    if (h->stage_cap[k] < h->ready_pairs) {
+        // the buffer may still be draining a batch two back
+        if (h->copy_pending[k]) HIPC(hipEventSynchronize(h->copied[k]), "delivery wait");
+        h->copy_pending[k] = false;
+        dfree(h, h->stage[k]);
+        h->stage_cap[k] = 0;
+        const uint64_t cap = h->ready_pairs + h->ready_pairs / 8 + 1024;
+        TRY(dalloc(h, &h->stage[k], (size_t)cap * 2, "delivery staging"));
+        h->stage_cap[k] = cap;
+    }
+    // expand into staging buffer k after its previous copy has drained, then
+    // copy it out on the copy stream while the caller's stream moves on
+    if (h->copy_pending[k]) HIPC(hipStreamWaitEvent(s, h->copied[k], 0), "delivery order");
+    TRY(expand_batch(h, batch, h->stage[k], s));
+    HIPC(hipEventRecord(h->expanded[k], s), "delivery event");
+    HIPC(hipStreamWaitEvent(h->copy_stream, h->expanded[k], 0), "delivery order");
+    HIPC(hipMemcpyAsync(host_pairs, h->stage[k], sizeof(uint32_t) * 2 * h->ready_pairs, hipMemcpyDeviceToHost,
+                        h->copy_stream), "delivery copy");
+    HIPC(hipEventRecord(h->copied[k], h->copy_stream), "delivery event");
+    h->copy_pending[k] = true;
+    return ERSJ_OK;
+}
+
+int ersj_host_sync(ersj_index *h)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!h->copy_stream) return ERSJ_OK;
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    HIPC(hipStreamSynchronize(h->copy_stream), "delivery sync");
+    h->copy_pending[0] = h->copy_pending[1] = false;
     return ERSJ_OK;
 }
 

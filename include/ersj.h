@@ -177,6 +177,27 @@ int ersj_plan_batches(ersj_index *h, uint64_t budget_bytes, int32_t *n_batches, 
 int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t capacity,
                    uint64_t *n_pairs, void *stream);
 
+/*
+ * fill_pass with delivery to host memory (the pages' response time includes
+ * the results' transfer to the host, Sec. IV-D and V): the batch is refined
+ * and compacted on `stream` into one of two device staging buffers
+ * (alternating by batch), and copied into host_pairs on a copy stream of the
+ * handle's own, so the copy of batch b overlaps the refinement of batch b+1.
+ * Returns once the copy is enqueued: host_pairs is complete only after
+ * ersj_host_sync.  host_pairs should be pinned (hipHostMalloc, or a torch
+ * tensor with pin_memory=True) for the copy to run asynchronously; pageable
+ * memory works but copies synchronously.  The caller keeps host_pairs alive
+ * until ersj_host_sync (or ersj_free) returns.  Pair layout, CAPACITY and the
+ * other errors as for ersj_fill_pass; the staging buffers are allocated on
+ * demand.
+ */
+int ersj_fill_pass_host(ersj_index *h, int32_t batch, uint32_t *host_pairs, uint64_t capacity,
+                        uint64_t *n_pairs, void *stream);
+
+/* Wait until every copy started by ersj_fill_pass_host has landed in host
+ * memory.  Errors: INVALID_ARG, HIP. */
+int ersj_host_sync(ersj_index *h);
+
 /* Rows covered by a batch (index order) and its mask size.  Host outputs. */
 int ersj_batch_info(const ersj_index *h, int32_t batch, uint64_t *first_row, uint64_t *n_rows,
                     uint64_t *mask_words);
