@@ -56,6 +56,8 @@ def main():
                     help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--mode", choices=("selfjoin", "semijoin"), default="selfjoin",
                     help="semijoin: a separate query set from the workload's structure")
+    ap.add_argument("--grid-reach", type=int, default=1, choices=(1, 2),
+                    help="2: cells of width eps/2 and a 5x5x5 stencil (fewer candidates)")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
     ap.add_argument("--no-host", action="store_true",
                     help="skip the timing of the join delivered to pinned host memory")
@@ -103,7 +105,8 @@ def main():
         h.free()
 
     def step(timing):
-        opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine)
+        opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine,
+                                    grid_reach=args.grid_reach)
         h = ersj.build_index(xt, eps, opts, stream)
         if semi:
             ersj.set_queries(h, qt, stream)
@@ -153,7 +156,8 @@ def main():
             trec = json.load(f)
         with open(os.path.join(ROOT, trec["source"]), "rb") as f:
             cur = hashlib.sha256(f.read()).hexdigest()
-        if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget and not semi:
+        if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget and not semi \
+                and args.grid_reach == 1:
             traffic = trec["hbm_bytes_per_launch"]
     phases = {k: sum(s[k] for s in stats) / args.steps
               for k in ("build_ms", "count_ms", "plan_ms", "refine_ms", "recheck_ms", "expand_ms")}
@@ -177,7 +181,7 @@ def main():
                             if semi else "")),
             "mode": args.mode, "n_queries": int(Q.shape[0]),
             "n": int(X.shape[0]), "d": int(d), "eps": rec["eps"], "k": spec.k, "seed": spec.seed,
-            "batches": st["n_batches"], "budget_bytes": budget,
+            "batches": st["n_batches"], "budget_bytes": budget, "grid_reach": args.grid_reach,
             "refine_kernel": {1: "direct", 2: "mfma"}.get(st["refine_kernel"], "?"),
         },
         "join_wall_s": wall,

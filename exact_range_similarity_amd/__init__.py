@@ -43,7 +43,7 @@ class Options(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("refine_kernel", ctypes.c_int32),
                 ("cell_width_scale", ctypes.c_double), ("max_device_bytes", ctypes.c_uint64),
                 ("boundary_capacity", ctypes.c_uint64), ("timing", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("grid_reach", ctypes.c_int32), ("block_prune", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -59,7 +59,8 @@ class Stats(ctypes.Structure):
                 ("plan_ms", ctypes.c_double), ("refine_ms", ctypes.c_double),
                 ("recheck_ms", ctypes.c_double), ("expand_ms", ctypes.c_double),
                 ("refine_launches", ctypes.c_int64), ("refined_candidates", ctypes.c_uint64),
-                ("n_queries", ctypes.c_int64)]
+                ("n_queries", ctypes.c_int64), ("last_skipped", ctypes.c_uint64),
+                ("skipped_candidates", ctypes.c_uint64)]
 
     def as_dict(self):
         out = {}
@@ -196,6 +197,16 @@ def plan_batches(h: Index, budget_bytes: int = 0, stream=None) -> int:
     return nb.value
 
 
+def _capacity_error(rc: int, required: int) -> ErsjError:
+    # built here, not in the raising frame: an exception held in a local of
+    # the frame that raises it forms a reference cycle through its traceback,
+    # which would keep the caller's frames (and their output tensors) alive
+    # until the garbage collector runs
+    err = ErsjError(rc, lib().ersj_last_error().decode(errors="replace"))
+    err.required = required
+    return err
+
+
 def fill_pass(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = None,
               stream=None) -> int:
     """Run ``ersj_fill_pass``; returns the batch's pair count.
@@ -215,9 +226,7 @@ def fill_pass(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = 
             raise ValueError("capacity exceeds the tensor")
     rc = lib().ersj_fill_pass(h.handle, int(batch), ptr, cap, ctypes.byref(npairs), _stream(stream))
     if rc == ERR_CAPACITY:
-        err = ErsjError(rc, lib().ersj_last_error().decode(errors="replace"))
-        err.required = npairs.value
-        raise err
+        raise _capacity_error(rc, npairs.value)
     _check(rc)
     return npairs.value
 
@@ -240,9 +249,7 @@ def fill_pass_host(h: Index, batch: int, pairs: torch.Tensor = None, capacity: i
             raise ValueError("capacity exceeds the tensor")
     rc = lib().ersj_fill_pass_host(h.handle, int(batch), ptr, cap, ctypes.byref(npairs), _stream(stream))
     if rc == ERR_CAPACITY:
-        err = ErsjError(rc, lib().ersj_last_error().decode(errors="replace"))
-        err.required = npairs.value
-        raise err
+        raise _capacity_error(rc, npairs.value)
     _check(rc)
     return npairs.value
 

@@ -63,6 +63,7 @@ struct ersj_index {
     int32_t d = 0, nb = 0;
     double eps = 0.0, e64 = 0.0;
     float tlo = 0.0f, thi = 0.0f;
+    float tbox = INFINITY;  // block box test threshold (inf: off)
     float kp = 1.0f, km = 1.0f;
     double maxabs = 0.0;
     GridParams gp{};
@@ -117,10 +118,10 @@ struct ersj_index {
     int32_t ready_batch = -1;
     uint64_t ready_pairs = 0;
     // stats
-    uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0;
+    uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0, last_skip = 0;
     double ms_build = 0, ms_count = 0, ms_plan = 0, ms_refine = 0, ms_recheck = 0, ms_expand = 0;
     int64_t refine_launches = 0;
-    uint64_t refined_cand = 0;
+    uint64_t refined_cand = 0, skipped_cand = 0;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t kernel_used = ERSJ_REFINE_DIRECT;
     // host delivery: two device staging buffers, alternated by batch, drained
@@ -249,6 +250,12 @@ void thresholds(ersj_index *h)
     h->thi = std::max(round_up_f32(E * (1.0 + delta)), (float)std::ldexp(1.0, -80));
     if (E < std::ldexp(1.0, -90)) h->tlo = -1.0f;
     else h->tlo = round_down_f32(E * (1.0 - delta));
+    // Block box test: the fp32 sum of three squared box gaps (gaps rounded
+    // once, then up to three more roundings) is at most (1 + u)^5 times the
+    // exact sum, which bounds the squared distance of every pair in the two
+    // boxes from below; D64 is within gamma(d + 1) of the exact distance.
+    // Above E (1 + 2^-20) the whole block is therefore out.
+    h->tbox = h->opt.block_prune < 0 ? INFINITY : round_up_f32(E * (1.0 + std::ldexp(1.0, -20)));
 }
 
 // MFMA refinement: dot products of tile-centred coordinates.  Usable when
@@ -365,7 +372,7 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     TRY(tmp.get(&stmp, std::max(scan_tmp_entries(hent), scan_tmp_entries(n + 1)), "scan"));
     TRY(dalloc(h, &out->orig, (size_t)n, "orig"));
     HIPC(launch_keys(x, n, ld, h->gp, queries, k0, out->orig, s), "keys kernel");
-    HIPC(radix_sort(k0, out->orig, k1, v1, n, 3 * h->gp.bits, hist, stmp, s), "radix sort");
+    HIPC(radix_sort(k0, out->orig, k1, v1, n, 3 * (h->gp.bits + h->gp.sub), hist, stmp, s), "radix sort");
 
     int32_t *dperm = nullptr;
     TRY(tmp.get(&dperm, (size_t)d, "perm"));
@@ -377,7 +384,7 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     uint64_t *cid = nullptr;
     TRY(tmp.get(&flags, (size_t)n, "cells"));
     TRY(tmp.get(&cid, (size_t)n + 1, "cells"));
-    HIPC(launch_cell_flags(k0, n, flags, s), "cell flags");
+    HIPC(launch_cell_flags(k0, n, 3 * h->gp.sub, flags, s), "cell flags");
     HIPC(scan_u32(flags, cid, n, stmp, s), "cell scan");
     uint64_t M = 0;
     HIPC(hipMemcpyAsync(&M, cid + n, sizeof M, hipMemcpyDeviceToHost, s), "cell count copy");
@@ -387,7 +394,7 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     TRY(dalloc(h, &out->cell_key, (size_t)M, "cells"));
     TRY(dalloc(h, &out->lo_bits, (size_t)M * 3, "cells"));
     TRY(dalloc(h, &out->hi_bits, (size_t)M * 3, "cells"));
-    HIPC(launch_cell_scatter(k0, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
+    HIPC(launch_cell_scatter(k0, 3 * h->gp.sub, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
     HIPC(launch_cell_aabb(out->xs, cid, n, (int64_t)M, out->lo_bits, out->hi_bits, s), "cell boxes");
     TRY(sync(s, "bin"));
     return ERSJ_OK;
@@ -460,6 +467,7 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     for (int j = 0; j < d; ++j) h->pinv[h->perm[j]] = j;
     GridParams gp{};
     gp.ndim = std::min(3, d);
+    gp.reach = h->opt.grid_reach > 0 ? h->opt.grid_reach : 1;
     const double scale = h->opt.cell_width_scale > 1.0 ? h->opt.cell_width_scale : 1.0;
     const double gmax = std::ldexp(1.0, 21) - 2.0;
     int bits = 1;
@@ -472,7 +480,7 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
         const double mn = hst[gp.dim[a] * 4 + 2], mx = hst[gp.dim[a] * 4 + 3];
         const double range = mx - mn;
         gp.lo[a] = mn;
-        double w = h->eps * scale * (1.0 + std::ldexp(1.0, -20));
+        double w = h->eps * scale * (1.0 + std::ldexp(1.0, -20)) / gp.reach;
         w = std::max(w, range / (gmax - 1.0));
         if (!(w > 0.0)) w = 1.0;
         gp.w[a] = w;
@@ -482,6 +490,10 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
         bits = std::max(bits, ceil_log2((uint64_t)gp.G[a] + 2));
     }
     gp.bits = bits;
+    // rows within a cell follow a Morton curve over 8 x 8 x 8 sub-cells (fewer
+    // when the grid is near its 2^21 cap), so a block of consecutive rows is
+    // spatially compact and its bounding box prunes refinement work
+    gp.sub = std::min(3, 21 - bits);
     h->gp = gp;
 
     // A4-A7 for the points.
@@ -690,7 +702,7 @@ int ensure_fill_buffers(ersj_index *h)
         TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
         h->rows_cap = h->maxrows;
     }
-    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)kBandLists * kBandStride + 1, "counters"));
+    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)kBandLists * kBandStride + 2, "counters"));
     if (!h->lpref) TRY(dalloc(h, &h->lpref, (size_t)kBandLists + 3, "band list prefix"));
     if (!h->blist) {
         const uint64_t cap = initial_bcap(h);
@@ -737,8 +749,11 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.thi = h->thi;
     a.kp = h->kp;
     a.km = h->km;
-    const size_t ncount = (size_t)kBandLists * kBandStride + 1;
+    const size_t ncount = (size_t)kBandLists * kBandStride + 2;
     unsigned long long *const hits = h->counters + (size_t)kBandLists * kBandStride;
+    unsigned long long *const skipped = hits + 1;
+    a.tbox = h->tbox;
+    a.skipped = skipped;
     uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -782,14 +797,16 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     HIPC(launch_rowcount(h->tiles, t0, ntiles, h->toff, a.wbase, h->hrows[b], h->mask, h->rowcnt, s),
          "row count kernel");
     HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
-    uint64_t tot = 0, nin = 0;
+    uint64_t tot = 0, hs[2] = {0, 0};  // pairs; re-check hits, skipped comparisons
     HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
-    HIPC(hipMemcpyAsync(&nin, hits, sizeof nin, hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(hs, hits, sizeof hs, hipMemcpyDeviceToHost, s), "copy");
     TRY(sync(s, "row count"));
     h->ms_expand += timer_stop(h, s);
     h->last_cand = h->hcands[b + 1] - h->hcands[b];
     h->last_bnd = bcount;
-    h->last_in = nin;
+    h->last_in = hs[0];
+    h->last_skip = hs[1];
+    if (h->opt.timing) h->skipped_cand += hs[1];
     h->ready_batch = b;
     h->ready_pairs = tot;
     h->last_pairs = tot;
@@ -878,6 +895,10 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
             return fail(ERSJ_ERR_INVALID_ARG, "cell_width_scale must be finite and >= 0");
         if (o.refine_kernel < ERSJ_REFINE_AUTO || o.refine_kernel > ERSJ_REFINE_MFMA)
             return fail(ERSJ_ERR_INVALID_ARG, "unknown refine_kernel %d", o.refine_kernel);
+        if (o.grid_reach < 0 || o.grid_reach > kMaxGridReach)
+            return fail(ERSJ_ERR_INVALID_ARG, "grid_reach must be 0, 1 or 2 (got %d)", o.grid_reach);
+        if (o.block_prune < -1 || o.block_prune > 1)
+            return fail(ERSJ_ERR_INVALID_ARG, "block_prune must be -1, 0 or 1 (got %d)", o.block_prune);
     }
     int dev = 0;
     HIPC(hipGetDevice(&dev), "hipGetDevice");
@@ -1125,6 +1146,8 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     o->expand_ms = h->ms_expand;
     o->refine_launches = h->refine_launches;
     o->refined_candidates = h->refined_cand;
+    o->last_skipped = h->last_skip;
+    o->skipped_candidates = h->skipped_cand;
     return ERSJ_OK;
 }
 

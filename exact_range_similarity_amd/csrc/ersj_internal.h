@@ -20,7 +20,23 @@
 namespace ersj {
 
 constexpr int kTileRows = 128;  // query rows per row tile
-constexpr int kMaxRanges = 27;  // 3x3x3 stencil
+// Candidate ranges per cell: at most one per stencil cell, (2R+1)^3 for grid
+// reach R <= 2 (cell width eps/R, stencil of 5x5x5 cells at R = 2).
+constexpr int kMaxGridReach = 2;
+constexpr int kMaxRanges = (2 * kMaxGridReach + 1) * (2 * kMaxGridReach + 1) * (2 * kMaxGridReach + 1);
+
+// Range g holding candidate position p: the largest g < nr with pref[g] <= p
+// (pref[0] = 0, ascending).
+__device__ __forceinline__ int range_of(const uint32_t *pref, uint32_t nr, uint32_t p)
+{
+    int lo = 0, hi = (int)nr;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pref[mid] <= p) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
 constexpr int kMaxDim = 4096;
 
 struct Tile {
@@ -49,6 +65,9 @@ struct GridParams {
     int32_t G[3];
     int32_t ndim;     // grid dimensions in use (min(d, 3))
     int32_t bits;     // Morton bits per dimension (coordinates 0 .. G + 1)
+    int32_t reach;    // stencil reach R: cell width >= eps / R, offsets in [-R, R]^3
+    int32_t sub;      // sub-cell bits per axis: rows within a cell ordered by a 2^sub-per-axis
+                      // Morton key (bits + sub <= 21); the cell key is the row key >> 3*sub
 };
 
 // ---- index construction (k_index.hip) ----
@@ -81,8 +100,8 @@ size_t scan_tmp_entries(int64_t n);
 hipError_t scan_u32(const uint32_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s);
 hipError_t scan_u64(const uint64_t *in, uint64_t *out, int64_t n, uint64_t *tmp, hipStream_t s);
 
-hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, uint32_t *flags, hipStream_t s);
-hipError_t launch_cell_scatter(const uint64_t *keys, const uint32_t *flags, const uint64_t *cid,
+hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, int shift, uint32_t *flags, hipStream_t s);
+hipError_t launch_cell_scatter(const uint64_t *keys, int shift, const uint32_t *flags, const uint64_t *cid,
                                int64_t n, uint32_t *cell_start, uint64_t *cell_key,
                                hipStream_t s);
 hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, int64_t M,
@@ -188,6 +207,9 @@ struct RefineArgs {
     Boundary *blist;              // kBandLists sub-lists of lcap entries each
     unsigned long long *bcount;   // sub-list c's counter at bcount[c * kBandStride]
     uint64_t lcap;                // entries per sub-list
+    float tbox;                   // a query block and a candidate group whose boxes on the three
+                                  // grid axes have fp32 gap^2 sum > tbox hold no pair (inf: off)
+    unsigned long long *skipped;  // comparisons decided by that box test alone
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
 

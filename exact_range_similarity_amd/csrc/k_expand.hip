@@ -149,8 +149,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 const int bit = __ffsll((unsigned long long)m) - 1;
                 m &= m - 1;
                 const uint32_t p = w * 64 + bit;
-                int g = 0;
-                while (g + 1 < (int)nr && p >= s_pref[g + 1]) ++g;
+                const int g = range_of(s_pref, nr, p);
                 const uint32_t x = s_start[g] + (p - s_pref[g]);
                 pairs[2 * pos] = qid;
                 pairs[2 * pos + 1] = orig[x];

@@ -148,27 +148,41 @@ __global__ __launch_bounds__(kBlock) void k_stats_final(const float *__restrict_
 }
 
 // ----------------------------------------------------------------- keys --
-// Cell coordinate c = floor((x - lo) / w) in binary64, clamped to [0, G-1]
-// for points and to [-1, G] for semi-join queries, stored as c + 1.  With
-// w >= eps * (1 + 2^-20) two coordinates of a neighbour pair land in cells at
-// most one apart, so the 27-cell stencil is exhaustive.
+// Cell coordinate c = floor(t), t = (x - lo) / w in binary64, clamped to
+// [0, G-1] for points and to [-1, G] for semi-join queries, stored as c + 1.
+// With w >= eps * (1 + 2^-20) / R two coordinates of a neighbour pair land in
+// cells at most R apart, so the (2R+1)^3 stencil is exhaustive.  The row key
+// interleaves c + 1 followed by the sub-cell coordinate floor(t * 2^sub) -
+// c * 2^sub (exact: scaling by a power of two), so rows sort by cell and,
+// within a cell, along a finer Morton curve; a clamped coordinate takes the
+// sub-cell at its clamped end.
 __global__ __launch_bounds__(kBlock) void k_keys(const float *__restrict__ x, int64_t n, int64_t ld,
                                                  GridParams gp, int queries, uint64_t *__restrict__ keys,
                                                  uint32_t *__restrict__ ids)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
+    const int64_t nsub = (int64_t)1 << gp.sub;
     uint64_t key = 0;
     for (int a = 0; a < gp.ndim; ++a) {
-        double v = (double)x[i * ld + gp.dim[a]];
-        double c = floor((v - gp.lo[a]) / gp.w[a]);
+        const double v = (double)x[i * ld + gp.dim[a]];
+        const double t = (v - gp.lo[a]) / gp.w[a];
+        const double c = floor(t);
         const double cmin = queries ? -1.0 : 0.0;
         const double cmax = queries ? (double)gp.G[a] : (double)(gp.G[a] - 1);
-        int64_t ci;
-        if (!(c > cmin)) ci = (int64_t)cmin;  // also NaN-free: x is finite
-        else if (c >= cmax) ci = (int64_t)cmax;
-        else ci = (int64_t)c;
-        key |= spread3((uint64_t)(ci + 1)) << a;
+        int64_t ci, si;
+        if (!(c > cmin)) {  // also NaN-free: x is finite
+            ci = (int64_t)cmin;
+            si = c < cmin ? 0 : (int64_t)(floor(t * (double)nsub) - c * (double)nsub);
+        } else if (c >= cmax) {
+            ci = (int64_t)cmax;
+            si = c > cmax ? nsub - 1 : (int64_t)(floor(t * (double)nsub) - c * (double)nsub);
+        } else {
+            ci = (int64_t)c;
+            si = (int64_t)(floor(t * (double)nsub) - c * (double)nsub);
+        }
+        si = si < 0 ? 0 : (si >= nsub ? nsub - 1 : si);
+        key |= spread3((uint64_t)(((ci + 1) << gp.sub) | si)) << a;
     }
     keys[i] = key;
     ids[i] = (uint32_t)i;
@@ -366,15 +380,16 @@ __global__ __launch_bounds__(kBlock) void k_gather(const float *__restrict__ x, 
 }
 
 // ----------------------------------------------------------------- cells --
+// cells are runs of equal row keys >> shift (the sub-cell bits dropped)
 __global__ __launch_bounds__(kBlock) void k_cell_flags(const uint64_t *__restrict__ keys, int64_t n,
-                                                       uint32_t *__restrict__ flags)
+                                                       int shift, uint32_t *__restrict__ flags)
 {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    flags[i] = (i == 0 || keys[i] != keys[i - 1]) ? 1u : 0u;
+    flags[i] = (i == 0 || (keys[i] >> shift) != (keys[i - 1] >> shift)) ? 1u : 0u;
 }
 
-__global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restrict__ keys,
+__global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restrict__ keys, int shift,
                                                          const uint32_t *__restrict__ flags,
                                                          const uint64_t *__restrict__ cid, int64_t n,
                                                          uint32_t *__restrict__ cell_start,
@@ -384,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restr
     if (i >= n) return;
     if (flags[i]) {
         cell_start[cid[i]] = (uint32_t)i;
-        cell_key[cid[i]] = keys[i];
+        cell_key[cid[i]] = keys[i] >> shift;
     }
     if (i == n - 1) cell_start[cid[n]] = (uint32_t)n;
 }
@@ -453,7 +468,7 @@ __device__ __forceinline__ int64_t find_key(const uint64_t *__restrict__ k, int6
 
 // Per home cell A (a cell of the query rows; of the points for the
 // self-join): the target cells B (cells of the points) at offsets in
-// {-1,0,1}^3 that exist and whose box lower distance to A's box (binary64,
+// [-R, R]^3 (R = 1: the 27-cell stencil) that exist and whose box lower distance to A's box (binary64,
 // over the grid dimensions) does not exceed the pruning threshold.  Kept
 // cells are sorted by index and runs of consecutive cells are merged into one
 // contiguous candidate range.  A query cell with no kept cell gets one empty
@@ -477,8 +492,10 @@ __global__ __launch_bounds__(kBlock) void k_stencil(CellSet home, CellSet target
     }
     uint32_t kept[kMaxRanges];
     int nk = 0;
-    for (int s = 0; s < 27; ++s) {
-        const int64_t dlt[3] = {s % 3 - 1, (s / 3) % 3 - 1, s / 9 - 1};
+    const int R = gp.reach, span = 2 * gp.reach + 1;
+    const int nst = span * span * span;
+    for (int s = 0; s < nst; ++s) {
+        const int64_t dlt[3] = {s % span - R, (s / span) % span - R, s / (span * span) - R};
         uint64_t nkey = 0;
         bool ok = true;
         for (int a = 0; a < 3; ++a) {
@@ -734,16 +751,16 @@ hipError_t launch_gather(const float *x, int64_t n, int32_t d, int64_t ld, const
     return hipGetLastError();
 }
 
-hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, uint32_t *flags, hipStream_t s)
+hipError_t launch_cell_flags(const uint64_t *keys, int64_t n, int shift, uint32_t *flags, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cell_flags, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, n, flags);
+    hipLaunchKernelGGL(k_cell_flags, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, n, shift, flags);
     return hipGetLastError();
 }
 
-hipError_t launch_cell_scatter(const uint64_t *keys, const uint32_t *flags, const uint64_t *cid,
+hipError_t launch_cell_scatter(const uint64_t *keys, int shift, const uint32_t *flags, const uint64_t *cid,
                                int64_t n, uint32_t *cell_start, uint64_t *cell_key, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_cell_scatter, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, flags, cid, n,
+    hipLaunchKernelGGL(k_cell_scatter, dim3(grid_for(n)), dim3(kBlock), 0, s, keys, shift, flags, cid, n,
                        cell_start, cell_key);
     return hipGetLastError();
 }

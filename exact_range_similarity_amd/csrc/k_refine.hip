@@ -81,8 +81,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
             const uint32_t p = c + lane + 64 * j;
             xv[j] = p < c_end;
             const uint32_t pp = xv[j] ? p : c_begin;
-            int g = 0;
-            while (g + 1 < (int)nr && pp >= s_pref[g + 1]) ++g;
+            const int g = range_of(s_pref, nr, pp);
             xi[j] = s_start[g] + (pp - s_pref[g]);
         }
         float acc[kQW][kCW];

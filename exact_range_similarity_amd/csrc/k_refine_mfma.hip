@@ -34,6 +34,14 @@
 // D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The host bounds the
 // coordinates so that nothing here overflows; NaN never classifies.
 //
+// Block pruning: rows within a cell follow a fine Morton order, so a query
+// block and a 64-candidate group are compact on the three grid axes (the
+// first three dimensions of the layout).  When the gap between their
+// bounding boxes there already exceeds eps (squared gaps summed in fp32 >
+// tbox, a bound that covers the rounding), the wave skips the group's
+// MFMAs and classification and writes zero mask words.  The candidate box
+// is reduced by the loading wave while it stages the first slab of a step.
+//
 // A step's classification follows its last slab's MFMAs; the waves that
 // share a SIMD overlap one's classification with another's matrix work.
 // With QB = 4 the kernel stays within 128 VGPRs and, up to d = 32, 40 KiB of
@@ -76,6 +84,29 @@ __device__ __forceinline__ float4 sub4(float4 a, float4 b)
     return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
 }
 
+// lo = min, hi = max of (x, y, z) over the 64 lanes, in every lane
+__device__ __forceinline__ void wave_box(float4 &lo, float4 &hi)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
+        lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
+        lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
+        hi.x = fmaxf(hi.x, __shfl_xor(hi.x, o, 64));
+        hi.y = fmaxf(hi.y, __shfl_xor(hi.y, o, 64));
+        hi.z = fmaxf(hi.z, __shfl_xor(hi.z, o, 64));
+    }
+}
+
+// fp32 sum of squared gaps between two boxes on the grid axes
+__device__ __forceinline__ float box_gap2(const float *alo, const float *ahi, float4 blo, float4 bhi)
+{
+    const float gx = fmaxf(0.f, fmaxf(blo.x - ahi[0], alo[0] - bhi.x));
+    const float gy = fmaxf(0.f, fmaxf(blo.y - ahi[1], alo[1] - bhi.y));
+    const float gz = fmaxf(0.f, fmaxf(blo.z - ahi[2], alo[2] - bhi.z));
+    return gx * gx + gy * gy + gz * gz;
+}
+
 template <int QB>
 struct Geometry {
     static constexpr int NCG = 4 / QB;            // candidate groups
@@ -94,6 +125,7 @@ struct Lds {
     uint32_t *xi;       // [kNB][SC] candidate point index of a step
     float *qin, *qout;  // [QR]
     uint64_t *words;    // [QR][8] mask words of the current 512-candidate group
+    float4 *cbox;       // [kNB][NCG][2] lo, hi of each candidate group of a step
     uint32_t *pref, *start;
 };
 
@@ -102,7 +134,8 @@ size_t lds_bytes(int nbs)
 {
     using G = Geometry<QB>;
     return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
-           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)G::QR * 8 * 8 + (2 * kMaxRanges + 1) * 4;
+           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)G::QR * 8 * 8 +
+           (size_t)kNB * G::NCG * 2 * 16 + (2 * kMaxRanges + 1) * 4;
 }
 
 template <int QB>
@@ -118,7 +151,8 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     L.qin = (float *)(L.xi + kNB * G::SC);
     L.qout = L.qin + G::QR;
     L.words = (uint64_t *)(L.qout + G::QR);
-    L.pref = (uint32_t *)(L.words + G::QR * 8);
+    L.cbox = (float4 *)(L.words + G::QR * 8);
+    L.pref = (uint32_t *)(L.cbox + kNB * G::NCG * 2);
     L.start = L.pref + (kMaxRanges + 1);
     return L;
 }
@@ -194,6 +228,24 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const int col = lane & 31, hi = lane >> 5;
     const int qb = wave % QB, cg = wave / QB;
     const bool active = (uint32_t)(qb * 32) < nrows;  // wave-uniform
+    // the wave's query block box on the grid axes (raw coordinates, valid
+    // rows only), held wave-uniform
+    float qlo[3], qhi[3];
+    {
+        const uint32_t i = (uint32_t)(qb * 32 + (lane & 31));
+        float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), hi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
+        if (i < nrows) {
+            lo = xq[row0 + i];
+            hi = lo;
+        }
+        wave_box(lo, hi);
+        qlo[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.x)));
+        qlo[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.y)));
+        qlo[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.z)));
+        qhi[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.x)));
+        qhi[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.y)));
+        qhi[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.z)));
+    }
     const float kp = a.kp, km = a.km;
     const uint64_t bcap = a.lcap;
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
@@ -207,8 +259,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     uint32_t rg[G::EPT], rnext[G::EPT], roff[G::EPT], lxi[G::EPT];
     uint32_t idx0;
     {
-        int g = 0;
-        while (g + 1 < (int)nr && c_begin >= L.pref[g + 1]) ++g;
+        const int g = range_of(L.pref, nr, c_begin);
         idx0 = L.start[g] + (c_begin - L.pref[g]);
 #pragma unroll
         for (int m = 0; m < G::EPT; ++m) {
@@ -279,6 +330,10 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     for (int m = 0; m < G::EPT; ++m) nxp[m] = 0.f;
     floatx16 accC[2];
     int pend_group = -1;
+    bool far = false;       // this wave skips the current step
+    uint64_t nskip = 0;     // comparisons this wave skipped
+    const float tbox = a.tbox;
+    const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
 
     // classification of step s (accumulators in acc): mask words and band pairs
     auto epilogue = [&](uint32_t s, const floatx16 *acc) {
@@ -419,11 +474,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
     };
 
-    // One slab: stage it, barrier, flush a finished mask-word group, issue
-    // the loads kAhead slabs ahead, MFMAs, and the step's classification
-    // after its last slab.  With NS > 0 the slab index is a constant and
-    // every per-slab condition folds.
-    auto slab_iter = [&](uint32_t k, uint32_t step, auto SLC) __attribute__((always_inline)) {
+    // One slab: stage it, barrier, decide the step's block test (first
+    // slab), flush a finished mask-word group and issue the loads kAhead
+    // slabs ahead.  Returns the staged buffer.  With NS > 0 the slab index is
+    // a constant and every per-slab condition folds.
+    auto stage = [&](uint32_t k, uint32_t step, auto SLC) __attribute__((always_inline)) {
         const int sl = SLC;
         float4 *xb = L.x + (k & 1) * (kSlab * G::SC);
         // stage the slab: centre on r, accumulate partial norms
@@ -440,6 +495,19 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             nxp[m] = s2;
             xb[e] = c4;
         }
+        if (sl == 0 && (tid >> 6) < G::NCG) {
+            // element 0 of the first NCG waves is block 0 (the grid axes) of
+            // candidate tid of the step: reduce each group's box
+            const bool valid = c_begin + step * G::SC + (uint32_t)tid < c_end;
+            float4 lo = valid ? ld[0][0] : make_float4(INFINITY, INFINITY, INFINITY, 0.f);
+            float4 hi = valid ? ld[0][0] : make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
+            wave_box(lo, hi);
+            if ((tid & 63) == 0) {
+                float4 *cb = L.cbox + ((step % kNB) * G::NCG + (tid >> 6)) * 2;
+                cb[0] = lo;
+                cb[1] = hi;
+            }
+        }
         if (sl == nslab - 1) {
 #pragma unroll
             for (int m = 0; m < G::EPT; ++m) {
@@ -450,6 +518,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             }
         }
         __syncthreads();
+        if (sl == 0) {
+            const float4 *cb = L.cbox + ((step % kNB) * G::NCG + cg) * 2;
+            const float g2 = box_gap2(qlo, qhi, cb[0], cb[1]);
+            far = !active || __builtin_amdgcn_readfirstlane((int)(g2 > tbox)) != 0;
+        }
         if (pend_group >= 0) {
             // the group buffer is reused by the next group: with one slab
             // per step this step's classification follows in this same
@@ -482,30 +555,47 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 cursor_next();
             }
         }
-        if (active) {
-            if (sl == 0) mfma_slab(xb, sl, true);
-            else mfma_slab(xb, sl, false);
-            if (sl == nslab - 1) epilogue(step, accC);
-        }
-        if (sl == nslab - 1 && (step % G::SPG == G::SPG - 1 || step + 1 == nsteps)) pend_group = (int)(step / G::SPG);
+        return xb;
     };
-    if constexpr (NS > 0) {
-        for (uint32_t step = 0; step < nsteps; ++step)
-            static_for(std::make_integer_sequence<int, NS>{},
-                       [&](auto S) __attribute__((always_inline)) { slab_iter(step * NS + S, step, S); });
-    } else {
-        uint32_t step = 0;
-        int sl = 0;
-        for (uint32_t k = 0; k < K; ++k) {
-            slab_iter(k, step, sl);
-            if (++sl == nslab) {
-                sl = 0;
-                ++step;
+    // a skipped (or inactive) wave's step: zero mask words, no band pairs
+    auto skip_step = [&](uint32_t step) __attribute__((always_inline)) {
+        const uint32_t cw = c_begin + step * G::SC + cg * 64;
+        nskip += (uint64_t)qrows * (cw < c_end ? min(64u, c_end - cw) : 0u);
+        if (lane < 32) L.words[(qb * 32 + lane) * 8 + (step % G::SPG) * G::NCG + cg] = 0ull;
+    };
+    // Each step branches once on the block test, so the accumulators are
+    // never live across steps; both branches stage the same slabs and meet
+    // the same barriers.
+    for (uint32_t step = 0; step < nsteps; ++step) {
+        const uint32_t k0 = step * (uint32_t)nslab;
+        float4 *xb0 = stage(k0, step, std::integral_constant<int, 0>{});
+        if (!far) {
+            mfma_slab(xb0, 0, true);
+            if constexpr (NS > 0) {
+                static_for(std::make_integer_sequence<int, NS - 1>{}, [&](auto S) __attribute__((always_inline)) {
+                    constexpr int sl = decltype(S)::value + 1;
+                    mfma_slab(stage(k0 + sl, step, std::integral_constant<int, sl>{}), sl, false);
+                });
+            } else {
+                for (int sl = 1; sl < nslab; ++sl) mfma_slab(stage(k0 + sl, step, sl), sl, false);
             }
+            epilogue(step, accC);
+        } else {
+            if constexpr (NS > 0) {
+                static_for(std::make_integer_sequence<int, NS - 1>{}, [&](auto S) __attribute__((always_inline)) {
+                    constexpr int sl = decltype(S)::value + 1;
+                    stage(k0 + sl, step, std::integral_constant<int, sl>{});
+                });
+            } else {
+                for (int sl = 1; sl < nslab; ++sl) stage(k0 + sl, step, sl);
+            }
+            skip_step(step);
         }
+        if (step % G::SPG == G::SPG - 1 || step + 1 == nsteps) pend_group = (int)(step / G::SPG);
     }
     __syncthreads();
     if (pend_group >= 0) flush((uint32_t)pend_group);
+    if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
 }
 
 }  // namespace

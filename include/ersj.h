@@ -77,7 +77,12 @@ typedef struct ersj_options {
     uint64_t boundary_capacity; /* initial boundary-pair list entries over all 256 sub-lists (grown and
                                    the batch refined again on overflow); 0 = default */
     int32_t timing;             /* nonzero: record HIP events around each phase */
-    int32_t reserved;
+    int32_t grid_reach;         /* 0 or 1: cells of width >= eps and the 27-cell stencil; 2: cells of
+                                   width >= eps/2 and a 5x5x5 stencil, fewer candidates (tighter
+                                   pruning, more cells) with the same result */
+    int32_t block_prune;        /* 0 or 1: a 32-query block and a 64-candidate group whose bounding
+                                   boxes on the grid axes are farther apart than eps skip their
+                                   distance computations (MFMA kernel); -1: off.  Same result. */
 } ersj_options;
 
 typedef struct ersj_stats {
@@ -103,6 +108,8 @@ typedef struct ersj_stats {
     int64_t refine_launches;     /* refine kernel launches timed in refine_ms */
     uint64_t refined_candidates; /* candidates refined in those launches */
     int64_t n_queries;           /* query rows: n for the self-join, nq after ersj_set_queries */
+    uint64_t last_skipped;       /* comparisons of the last fill_pass decided by the block box test */
+    uint64_t skipped_candidates; /* the same, over the launches timed in refine_ms */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */

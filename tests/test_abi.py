@@ -57,6 +57,9 @@ def test_build_rejects_bad_options():
     assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
     o = ersj.default_options(cell_width_scale=float("nan"))
     assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
+    for reach in (-1, 3):
+        o = ersj.default_options(grid_reach=reach)
+        assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
 
 
 def test_null_handle_paths():
@@ -85,3 +88,44 @@ def test_hip_failure_without_a_device():
     rc, out = build()
     assert rc in (ersj.ERR_HIP, ersj.ERR_OOM)
     assert out.value is None
+
+
+def test_capacity_error_leaves_no_reference_cycle(monkeypatch):
+    # A CAPACITY result raises ErsjError with .required; the exception must
+    # not form a cycle that keeps the caller's frame (and the output tensors
+    # it holds) alive until a garbage collection.
+    import gc
+    import weakref
+
+    class FakeLib:
+        def ersj_fill_pass(self, handle, batch, ptr, cap, npairs_ref, stream):
+            npairs_ref._obj.value = 12345
+            return ersj.ERR_CAPACITY
+
+        def ersj_last_error(self):
+            return b"capacity"
+
+    class FakeIndex:
+        handle = None
+
+    class Sentinel:
+        pass
+
+    monkeypatch.setattr(ersj, "lib", lambda: FakeLib())
+    monkeypatch.setattr(ersj, "_stream", lambda stream: None)
+
+    def caller():
+        held = Sentinel()
+        ref = weakref.ref(held)
+        try:
+            ersj.fill_pass(FakeIndex(), 0, None, 0)
+        except ersj.ErsjError as e:
+            assert e.code == ersj.ERR_CAPACITY and e.required == 12345
+        return ref
+
+    gc.disable()
+    try:
+        ref = caller()
+        assert ref() is None
+    finally:
+        gc.enable()

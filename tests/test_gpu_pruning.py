@@ -1,0 +1,126 @@
+"""Tighter pruning keeps the oracle's pair set exactly.
+
+The finer grid (grid_reach = 2: cells of width eps/2, 5x5x5 stencil) with
+both refinement kernels, never with more candidates than the default grid;
+and the block box test of the MFMA kernel (on by default, compared here with
+it switched off): it must skip work on clustered data and change nothing.
+Cases: random data with ragged sizes, clustered workload shapes, lattices
+with pairs exactly at eps (cell walls at multiples of eps/2, box gaps of
+exactly eps), eps = 0, and the semi-join."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_range_similarity_amd as ersj
+import oracle
+from workloads import lattice, make_config, make_queries
+
+from gpu_util import KERNELS, check_against_oracle, keys_of, say
+
+pytestmark = pytest.mark.gpu
+FINE = ersj.default_options(grid_reach=2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ersj.lib()
+
+
+def candidates(X, eps, reach):
+    h = ersj.build_index(torch.from_numpy(X).cuda(), eps, ersj.default_options(grid_reach=reach))
+    total = ersj.count_pass(h)
+    st = ersj.get_stats(h)
+    h.free()
+    return total, st["cells"]
+
+
+@pytest.mark.parametrize("n,d", [(1, 3), (257, 5), (2000, 2), (3001, 9), (1500, 40)])
+def test_random(n, d):
+    rng = np.random.default_rng(n + 100 * d)
+    X = rng.random((n, d), dtype=np.float32)
+    for eps in (0.05 * math.sqrt(d), 0.3 * math.sqrt(d)):
+        check_against_oracle(X, eps, f"reach 2 random n={n} d={d}", options=FINE)
+
+
+@pytest.mark.parametrize("name,n", [("c2", 20000), ("c4", 30011), ("c3", 8000)])
+def test_workload_shapes_and_fewer_candidates(name, n):
+    X = make_config(name, n)
+    eps, _, _ = oracle.calibrate_eps(X, min(1000, n), 32)
+    check_against_oracle(X, eps, f"reach 2 {name} n={n}", options=FINE)
+    c1, m1 = candidates(X, eps, 1)
+    c2, m2 = candidates(X, eps, 2)
+    say(f"[gpu] {name} n={n}: candidates {c1} -> {c2}, cells {m1} -> {m2}")
+    assert c2 <= c1 and m2 >= m1
+
+
+@pytest.mark.parametrize("m,d", [(9, 2), (6, 3)])
+def test_lattice_pairs_at_eps(m, d):
+    X = lattice(m, d)
+    for eps in (1.0, math.nextafter(1.0, 0.0), 2.0, math.sqrt(2.0), 0.5):
+        check_against_oracle(X, eps, f"reach 2 lattice m={m} d={d}", options=FINE)
+
+
+def test_eps_zero_and_infinite():
+    rng = np.random.default_rng(61)
+    base = rng.random((40, 4), dtype=np.float32)
+    X = np.repeat(base, 3, axis=0)
+    check_against_oracle(X, 0.0, "reach 2 eps = 0", options=FINE)
+    for k in KERNELS:
+        got = ersj.pairs_to_numpy(ersj.self_join(torch.from_numpy(base).cuda(), math.inf,
+                                                 options=ersj.default_options(grid_reach=2,
+                                                                              refine_kernel=k)))
+        assert got.shape[0] == 40 * 40
+
+
+def test_semi_join_with_the_finer_grid():
+    X = make_config("c2", 15000)
+    Q = make_queries("c2", 4000, 7, 15000)
+    eps = 0.11
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    for k in KERNELS:
+        opts = ersj.default_options(grid_reach=2, refine_kernel=k)
+        parts = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts)
+        got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+        assert np.array_equal(got, want)
+
+
+def _mfma_join(X, eps, **opt):
+    h = ersj.build_index(torch.from_numpy(X).cuda(), eps,
+                         ersj.default_options(refine_kernel=ersj.REFINE_MFMA, timing=1, **opt))
+    ersj.count_pass(h)
+    nb = ersj.plan_batches(h, 0)
+    parts = list(ersj.iter_batches(h, nb))
+    st = ersj.get_stats(h)
+    h.free()
+    return np.sort(keys_of(ersj.pairs_to_numpy(parts))), st
+
+
+@pytest.mark.parametrize("name,n,reach", [("c2", 40000, 1), ("c2", 40000, 2), ("c4", 30011, 1),
+                                          ("c3", 9000, 1)])
+def test_block_prune_skips_work_and_changes_nothing(name, n, reach):
+    X = make_config(name, n)
+    eps, _, _ = oracle.calibrate_eps(X, min(1000, n), 32)
+    want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
+    on, st_on = _mfma_join(X, eps, grid_reach=reach)
+    off, st_off = _mfma_join(X, eps, grid_reach=reach, block_prune=-1)
+    say(f"[gpu] {name} n={n} reach={reach}: skipped {st_on['skipped_candidates']} of "
+        f"{st_on['refined_candidates']} comparisons")
+    assert np.array_equal(on, want) and np.array_equal(off, want)
+    assert st_off["skipped_candidates"] == 0
+    assert 0 < st_on["skipped_candidates"] < st_on["refined_candidates"]
+    assert st_on["last_skipped"] == st_on["skipped_candidates"]  # one batch
+
+
+@pytest.mark.parametrize("m,d", [(9, 2), (6, 3), (5, 4)])
+def test_block_prune_lattice_at_eps(m, d):
+    # integer lattices: many box gaps equal eps exactly; eps just below an
+    # integer distance puts the threshold between lattice distances
+    X = lattice(m, d)
+    for eps in (1.0, math.nextafter(1.0, 0.0), 2.0, math.nextafter(2.0, 3.0), 3.0):
+        want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
+        got, st = _mfma_join(X, eps)
+        assert np.array_equal(got, want), (m, d, eps)
