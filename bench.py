@@ -58,6 +58,8 @@ def main():
                     help="semijoin: a separate query set from the workload's structure")
     ap.add_argument("--grid-reach", type=int, default=1, choices=(1, 2),
                     help="2: cells of width eps/2 and a 5x5x5 stencil (fewer candidates)")
+    ap.add_argument("--no-block-prune", action="store_true",
+                    help="switch off the MFMA kernel's query-block/candidate-group box test")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
     ap.add_argument("--no-host", action="store_true",
                     help="skip the timing of the join delivered to pinned host memory")
@@ -106,7 +108,8 @@ def main():
 
     def step(timing):
         opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine,
-                                    grid_reach=args.grid_reach)
+                                    grid_reach=args.grid_reach,
+                                    block_prune=-1 if args.no_block_prune else 0)
         h = ersj.build_index(xt, eps, opts, stream)
         if semi:
             ersj.set_queries(h, qt, stream)
@@ -140,12 +143,16 @@ def main():
     launches = sum(s["refine_launches"] for s in stats)
     refine_ms = sum(s["refine_ms"] for s in stats)
     refined = sum(s["refined_candidates"] for s in stats)
+    skipped = sum(s["skipped_candidates"] for s in stats)
+    # comparisons the kernel computed: the block box test decides the rest
+    # without a distance, so they carry no flops
+    evaluated = refined - skipped
     avg_launch_ms = refine_ms / max(1, launches)
     mfma = st["refine_kernel"] == ersj.REFINE_MFMA
     # algorithmic flops per candidate: direct form 3d (sub, mul, add per
     # dimension); expanded form 2d + 3 (the dot product on MFMA plus norms)
     per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
-    flops_per_launch = per_cand * refined / max(1, launches)
+    flops_per_launch = per_cand * evaluated / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
     kname = "k_refine_mfma" if mfma else "k_refine_direct"
     traffic = None
@@ -157,7 +164,7 @@ def main():
         with open(os.path.join(ROOT, trec["source"]), "rb") as f:
             cur = hashlib.sha256(f.read()).hexdigest()
         if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget and not semi \
-                and args.grid_reach == 1:
+                and args.grid_reach == 1 and not args.no_block_prune:
             traffic = trec["hbm_bytes_per_launch"]
     phases = {k: sum(s[k] for s in stats) / args.steps
               for k in ("build_ms", "count_ms", "plan_ms", "refine_ms", "recheck_ms", "expand_ms")}
@@ -182,6 +189,7 @@ def main():
             "mode": args.mode, "n_queries": int(Q.shape[0]),
             "n": int(X.shape[0]), "d": int(d), "eps": rec["eps"], "k": spec.k, "seed": spec.seed,
             "batches": st["n_batches"], "budget_bytes": budget, "grid_reach": args.grid_reach,
+            "block_prune": not args.no_block_prune,
             "refine_kernel": {1: "direct", 2: "mfma"}.get(st["refine_kernel"], "?"),
         },
         "join_wall_s": wall,
@@ -189,6 +197,7 @@ def main():
         "result_pairs_per_s": npairs / wall,
         "candidates": cand,
         "candidate_fraction_of_n2": cand / float(X.shape[0]) ** 2,
+        "evaluated_fraction": evaluated / max(1, refined),
         "cells": st["cells"],
         "grid": st["grid"],
         "boundary_pairs": st["last_boundary_pairs"],

@@ -37,6 +37,34 @@ __device__ __forceinline__ int range_of(const uint32_t *pref, uint32_t nr, uint3
     }
     return lo;
 }
+
+// Block box test.  Rows within a cell follow a fine Morton order, so a few
+// consecutive rows (queries, or candidates of a cell's list) are compact on
+// the three grid axes, which are the first three dimensions of the layout.
+// wave_box: lo = min, hi = max of (x, y, z) over the 64 lanes, in every lane.
+__device__ __forceinline__ void wave_box(float4 &lo, float4 &hi)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
+        lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
+        lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
+        hi.x = fmaxf(hi.x, __shfl_xor(hi.x, o, 64));
+        hi.y = fmaxf(hi.y, __shfl_xor(hi.y, o, 64));
+        hi.z = fmaxf(hi.z, __shfl_xor(hi.z, o, 64));
+    }
+}
+
+// fp32 sum of squared gaps between two boxes on the grid axes.  Compared
+// with RefineArgs::tbox, which covers its rounding: above it no pair of
+// points in the two boxes is within eps.
+__device__ __forceinline__ float box_gap2(const float *alo, const float *ahi, float4 blo, float4 bhi)
+{
+    const float gx = fmaxf(0.f, fmaxf(blo.x - ahi[0], alo[0] - bhi.x));
+    const float gy = fmaxf(0.f, fmaxf(blo.y - ahi[1], alo[1] - bhi.y));
+    const float gz = fmaxf(0.f, fmaxf(blo.z - ahi[2], alo[2] - bhi.z));
+    return gx * gx + gy * gy + gz * gz;
+}
 constexpr int kMaxDim = 4096;
 
 struct Tile {

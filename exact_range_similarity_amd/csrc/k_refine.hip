@@ -22,6 +22,11 @@
 //                         binary64 by the re-check kernel.
 // tlo and thi come from a forward error bound that holds for any summation
 // order, so the dimension order used here (by variance) is free.
+//
+// Block pruning: before a chunk, the wave compares the bounding box of its
+// 8 queries with that of the chunk's 256 candidates on the three grid axes
+// (block 0 of the layout); when their squared gap exceeds tbox no pair in
+// them is a neighbour, and the wave writes zero words without computing.
 #include "ersj_internal.h"
 
 namespace ersj {
@@ -73,6 +78,24 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
     unsigned long long *__restrict__ bcount = band_counter(a.bcount);
 
+    // the wave's query box on the grid axes (rows past srows repeat the last)
+    float qlo[3], qhi[3];
+    {
+        const float4 q0 = xq[qrow[0]];
+        qlo[0] = qhi[0] = q0.x;
+        qlo[1] = qhi[1] = q0.y;
+        qlo[2] = qhi[2] = q0.z;
+#pragma unroll
+        for (int k = 1; k < kQW; ++k) {
+            const float4 q = xq[qrow[k]];
+            qlo[0] = fminf(qlo[0], q.x); qhi[0] = fmaxf(qhi[0], q.x);
+            qlo[1] = fminf(qlo[1], q.y); qhi[1] = fmaxf(qhi[1], q.y);
+            qlo[2] = fminf(qlo[2], q.z); qhi[2] = fmaxf(qhi[2], q.z);
+        }
+    }
+    const float tbox = a.tbox;
+    uint64_t nskip = 0;
+
     for (uint32_t c = c_begin; c < c_end; c += kChunk) {
         uint32_t xi[kCW];
         bool xv[kCW];
@@ -83,6 +106,29 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
             const uint32_t pp = xv[j] ? p : c_begin;
             const int g = range_of(s_pref, nr, pp);
             xi[j] = s_start[g] + (pp - s_pref[g]);
+        }
+        {
+            float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), hi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
+#pragma unroll
+            for (int j = 0; j < kCW; ++j) {
+                if (xv[j]) {
+                    const float4 v = xs[xi[j]];
+                    lo.x = fminf(lo.x, v.x); hi.x = fmaxf(hi.x, v.x);
+                    lo.y = fminf(lo.y, v.y); hi.y = fmaxf(hi.y, v.y);
+                    lo.z = fminf(lo.z, v.z); hi.z = fmaxf(hi.z, v.z);
+                }
+            }
+            wave_box(lo, hi);
+            const float g2 = box_gap2(qlo, qhi, lo, hi);
+            if (__builtin_amdgcn_readfirstlane((int)(g2 > tbox)) != 0) {
+                nskip += (uint64_t)nq * min((uint32_t)kChunk, c_end - c);
+                if (lane < kQW * kCW) {
+                    const int k = lane / kCW, j = lane % kCW;
+                    const uint32_t w = (c >> 6) + j;
+                    if ((uint32_t)k < nq && w < tl.words) mask[mbase + (uint64_t)k * tl.words + w] = 0ull;
+                }
+                continue;
+            }
         }
         float acc[kQW][kCW];
 #pragma unroll
@@ -152,6 +198,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
                 mask[mbase + (uint64_t)k * tl.words + w0 + j] = myword;
         }
     }
+    if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
 }
 
 }  // namespace

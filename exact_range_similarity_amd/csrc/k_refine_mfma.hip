@@ -84,29 +84,6 @@ __device__ __forceinline__ float4 sub4(float4 a, float4 b)
     return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
 }
 
-// lo = min, hi = max of (x, y, z) over the 64 lanes, in every lane
-__device__ __forceinline__ void wave_box(float4 &lo, float4 &hi)
-{
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
-        lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
-        lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
-        hi.x = fmaxf(hi.x, __shfl_xor(hi.x, o, 64));
-        hi.y = fmaxf(hi.y, __shfl_xor(hi.y, o, 64));
-        hi.z = fmaxf(hi.z, __shfl_xor(hi.z, o, 64));
-    }
-}
-
-// fp32 sum of squared gaps between two boxes on the grid axes
-__device__ __forceinline__ float box_gap2(const float *alo, const float *ahi, float4 blo, float4 bhi)
-{
-    const float gx = fmaxf(0.f, fmaxf(blo.x - ahi[0], alo[0] - bhi.x));
-    const float gy = fmaxf(0.f, fmaxf(blo.y - ahi[1], alo[1] - bhi.y));
-    const float gz = fmaxf(0.f, fmaxf(blo.z - ahi[2], alo[2] - bhi.z));
-    return gx * gx + gy * gy + gz * gz;
-}
-
 template <int QB>
 struct Geometry {
     static constexpr int NCG = 4 / QB;            // candidate groups
@@ -453,6 +430,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     auto mfma_slab = [&](const float4 *xb, int sl, bool fresh) {
 #pragma unroll
         for (int s2 = 0; s2 < kSlab / 2; ++s2) {
+            // block pairs past the last dimension block are zero padding
+            if (s2 > 0 && sl * kSlab + 2 * s2 >= nb) break;
             const int jj = 2 * s2 + hi;
             const float4 av = L.q[(sl * kSlab + jj) * G::QR + qb * 32 + col];
             const float4 b0 = xb[jj * G::SC + cg * 64 + col];

@@ -80,9 +80,10 @@ typedef struct ersj_options {
     int32_t grid_reach;         /* 0 or 1: cells of width >= eps and the 27-cell stencil; 2: cells of
                                    width >= eps/2 and a 5x5x5 stencil, fewer candidates (tighter
                                    pruning, more cells) with the same result */
-    int32_t block_prune;        /* 0 or 1: a 32-query block and a 64-candidate group whose bounding
-                                   boxes on the grid axes are farther apart than eps skip their
-                                   distance computations (MFMA kernel); -1: off.  Same result. */
+    int32_t block_prune;        /* 0 or 1: a block of queries and a group of candidates (MFMA kernel:
+                                   32 x 64, direct kernel: 8 x 256) whose bounding boxes on the grid
+                                   axes are farther apart than eps skip their distance computations
+                                   and get zero mask bits; -1: off.  Same result. */
 } ersj_options;
 
 typedef struct ersj_stats {

@@ -2,7 +2,7 @@
 
 The finer grid (grid_reach = 2: cells of width eps/2, 5x5x5 stencil) with
 both refinement kernels, never with more candidates than the default grid;
-and the block box test of the MFMA kernel (on by default, compared here with
+and the block box test of both kernels (on by default, compared here with
 it switched off): it must skip work on clustered data and change nothing.
 Cases: random data with ragged sizes, clustered workload shapes, lattices
 with pairs exactly at eps (cell walls at multiples of eps/2, box gaps of
@@ -88,9 +88,9 @@ def test_semi_join_with_the_finer_grid():
         assert np.array_equal(got, want)
 
 
-def _mfma_join(X, eps, **opt):
+def _join(X, eps, kernel=ersj.REFINE_MFMA, **opt):
     h = ersj.build_index(torch.from_numpy(X).cuda(), eps,
-                         ersj.default_options(refine_kernel=ersj.REFINE_MFMA, timing=1, **opt))
+                         ersj.default_options(refine_kernel=kernel, timing=1, **opt))
     ersj.count_pass(h)
     nb = ersj.plan_batches(h, 0)
     parts = list(ersj.iter_batches(h, nb))
@@ -99,16 +99,17 @@ def _mfma_join(X, eps, **opt):
     return np.sort(keys_of(ersj.pairs_to_numpy(parts))), st
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name,n,reach", [("c2", 40000, 1), ("c2", 40000, 2), ("c4", 30011, 1),
                                           ("c3", 9000, 1)])
-def test_block_prune_skips_work_and_changes_nothing(name, n, reach):
+def test_block_prune_skips_work_and_changes_nothing(name, n, reach, kernel):
     X = make_config(name, n)
     eps, _, _ = oracle.calibrate_eps(X, min(1000, n), 32)
     want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
-    on, st_on = _mfma_join(X, eps, grid_reach=reach)
-    off, st_off = _mfma_join(X, eps, grid_reach=reach, block_prune=-1)
-    say(f"[gpu] {name} n={n} reach={reach}: skipped {st_on['skipped_candidates']} of "
-        f"{st_on['refined_candidates']} comparisons")
+    on, st_on = _join(X, eps, kernel, grid_reach=reach)
+    off, st_off = _join(X, eps, kernel, grid_reach=reach, block_prune=-1)
+    say(f"[gpu] {name} n={n} reach={reach} kernel={kernel}: skipped "
+        f"{st_on['skipped_candidates']} of {st_on['refined_candidates']} comparisons")
     assert np.array_equal(on, want) and np.array_equal(off, want)
     assert st_off["skipped_candidates"] == 0
     assert 0 < st_on["skipped_candidates"] < st_on["refined_candidates"]
@@ -122,5 +123,6 @@ def test_block_prune_lattice_at_eps(m, d):
     X = lattice(m, d)
     for eps in (1.0, math.nextafter(1.0, 0.0), 2.0, math.nextafter(2.0, 3.0), 3.0):
         want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
-        got, st = _mfma_join(X, eps)
-        assert np.array_equal(got, want), (m, d, eps)
+        for k in KERNELS:
+            got, st = _join(X, eps, k)
+            assert np.array_equal(got, want), (m, d, eps, k)
