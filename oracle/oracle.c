@@ -28,6 +28,8 @@
  * Every routine scans all candidate points in index order, so neighbour
  * lists come out sorted by point id.  orc_semijoin_rows does the same for
  * a query set distinct from the dataset (the semi-join of Sec. II-A).
+ * orc_knn gives the exact k nearest neighbours (Sec. VI), ranked by the same
+ * canonical D64, ties by the smaller point id.
  */
 #include <math.h>
 #include <stdint.h>
@@ -35,7 +37,7 @@
 #include <string.h>
 #include <omp.h>
 
-#define ORC_VERSION 2
+#define ORC_VERSION 3
 
 int orc_version(void) { return ORC_VERSION; }
 
@@ -236,4 +238,66 @@ int orc_calibrate(const float *X, int64_t n, int64_t d, int64_t ld, int64_t nq, 
     *out_b = b;
     free(pool); free(sizes); free(roots); free(flat);
     return ok ? 0 : 1;
+}
+
+/* ---- exact k nearest neighbours -------------------------------------------
+ * Sec. VI recasts the k-nearest-neighbours search as distance similarity
+ * searches whose radius grows until a query has k neighbours, which gives
+ * the exact kNN.  The oracle computes that result from its definition: for
+ * each selected query row, every one of the n points is ranked by the key
+ * (D64(query, point), point id) ascending, and the first k keys are the
+ * answer.  With Q == X the query itself is its own first neighbour (D64 = 0)
+ * unless an identical point has a smaller id, just as the self-join counts
+ * self pairs.
+ *   ids  : [nrows][k] point ids, ascending key
+ *   d64s : [nrows][k] their D64 (may be NULL)
+ * Returns 0, -1 on bad arguments (also k < 1 or k > n), -2 if an input
+ * holds a non-finite value, -3 if memory runs out.
+ */
+typedef struct {
+    double d;
+    uint32_t j;
+} orc_ranked;
+
+static int orc_ranked_cmp(const void *pa, const void *pb)
+{
+    const orc_ranked *a = (const orc_ranked *)pa, *b = (const orc_ranked *)pb;
+    if (a->d < b->d) return -1;
+    if (a->d > b->d) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+int orc_knn(const float *Q, int64_t nq, int64_t ldq, const float *X, int64_t n, int64_t ld,
+            int64_t d, int64_t k, const int64_t *rows, int64_t nrows, uint32_t *ids, double *d64s)
+{
+    int rc = check_inputs(X, n, d, ld, 0.0);
+    if (rc) return rc;
+    rc = check_inputs(Q, nq, d, ldq, 0.0);
+    if (rc) return rc;
+    if (!rows) nrows = nq;
+    if (nrows < 0 || !ids || k < 1 || k > n || n > (int64_t)UINT32_MAX) return -1;
+    int oom = 0;
+#pragma omp parallel reduction(| : oom)
+    {
+        orc_ranked *all = (orc_ranked *)malloc(sizeof(orc_ranked) * (size_t)n);
+        if (!all) oom = 1;
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!all) continue;
+            const int64_t i = rows ? rows[r] : r;
+            if (i < 0 || i >= nq) continue;
+            const float *qi = Q + i * ldq;
+            for (int64_t j = 0; j < n; ++j) {
+                all[j].d = orc_d64(qi, X + j * ld, d);
+                all[j].j = (uint32_t)j;
+            }
+            qsort(all, (size_t)n, sizeof(orc_ranked), orc_ranked_cmp);
+            for (int64_t t = 0; t < k; ++t) {
+                ids[r * k + t] = all[t].j;
+                if (d64s) d64s[r * k + t] = all[t].d;
+            }
+        }
+        free(all);
+    }
+    return oom ? -3 : 0;
 }

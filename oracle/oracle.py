@@ -50,6 +50,10 @@ def _load():
     lib.orc_band_count.restype = ctypes.c_int64
     lib.orc_band_count.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64]
+    lib.orc_knn.restype = ctypes.c_int
+    lib.orc_knn.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, _f32p, ctypes.c_int64,
+                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p, ctypes.c_int64,
+                            _u32p, _dblp]
     lib.orc_calibrate.restype = ctypes.c_int
     lib.orc_calibrate.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _dblp, _dblp]
@@ -174,6 +178,33 @@ def selfjoin_pairs(X, eps):
     counts = np.diff(colptr).astype(np.int64)
     q = np.repeat(np.arange(counts.size, dtype=np.uint32), counts)
     return np.stack([q, cols], axis=1)
+
+
+def knn_rows(Q, X, k: int, rows=None):
+    """Exact k nearest neighbours in X of the query rows ``rows`` of Q (all if
+    None), RT-HiSS Sec. VI: every point ranked by (D64, point id) ascending,
+    the first k.  Returns (ids uint32 [nrows, k], d64 float64 [nrows, k])."""
+    Q = _as_x(Q)
+    X = _as_x(X)
+    nq, d = Q.shape
+    n, dx = X.shape
+    if d != dx:
+        raise ValueError("Q and X differ in dimension")
+    r, rp = _rows_arg(rows)
+    nrows = nq if r is None else r.size
+    ids = np.zeros((nrows, int(k)), dtype=np.uint32)
+    dist = np.zeros((nrows, int(k)), dtype=np.float64)
+    rc = _load().orc_knn(_ptr(Q, _f32p), nq, d, _ptr(X, _f32p), n, d, d, int(k), rp, nrows,
+                         _ptr(ids, _u32p), _ptr(dist, _dblp))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the input (code {rc})")
+    return ids, dist
+
+
+def knn(X, k: int, rows=None):
+    """Self kNN: the query rows are the points themselves (each its own first
+    neighbour unless an identical point has a smaller id)."""
+    return knn_rows(X, X, k, rows)
 
 
 def band_count(X, eps, rel=1e-6, rows=None) -> int:
