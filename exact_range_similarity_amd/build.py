@@ -19,11 +19,11 @@ LIB = os.path.join(HERE, "libersj.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_expand.hip", "ersj_api.cpp"]
+SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_expand.hip", "k_knn.hip", "ersj_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result", "-Wno-unused-command-line-argument"]
-DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
+DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast-honor-pragmas"]
 
 
 def _compile(src: str, verbose: bool) -> str:

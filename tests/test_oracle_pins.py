@@ -251,3 +251,15 @@ def test_rejects_bad_input():
     X[2, 1] = np.inf
     with pytest.raises(ValueError):
         oracle.join_rows(X, 1.0)
+
+
+def test_oracle_d64_is_unfused():
+    """For pairs where a fused multiply-add accumulation rounds differently,
+    the oracle returns the canonical (separately rounded) value and decides
+    the pair at fl(eps^2) accordingly."""
+    from fused_pairs import canonical_d64, discriminating_pairs
+    for a, b, eps, inside in discriminating_pairs(40, 7, 5):
+        assert oracle.d64(a, b) == canonical_d64(a, b)
+        X = np.stack([a, b])
+        got = {tuple(p) for p in oracle.selfjoin_pairs(X, eps).tolist()}
+        assert ((0, 1) in got) == inside and ((1, 0) in got) == inside
