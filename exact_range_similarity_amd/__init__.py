@@ -71,9 +71,26 @@ class Stats(ctypes.Structure):
 
 
 _lib = None
+KNN_MAX_ROUNDS = 41
+
+
+class KnnInfo(ctypes.Structure):
+    _fields_ = [("rounds", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("eps", ctypes.c_double * KNN_MAX_ROUNDS), ("queries", ctypes.c_int64 * KNN_MAX_ROUNDS),
+                ("candidates", ctypes.c_uint64 * KNN_MAX_ROUNDS),
+                ("dim_estimate", ctypes.c_double * KNN_MAX_ROUNDS),
+                ("total_candidates", ctypes.c_uint64)]
+
+    def as_dict(self):
+        r = self.rounds
+        return {"rounds": r, "eps": list(self.eps[:r]), "queries": list(self.queries[:r]),
+                "candidates": list(self.candidates[:r]), "dim_estimate": list(self.dim_estimate[:r]),
+                "total_candidates": self.total_candidates}
+
+
 SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",
            "ersj_plan_batches", "ersj_fill_pass", "ersj_fill_pass_host", "ersj_host_sync",
-           "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error")
+           "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error", "ersj_knn")
 
 
 def lib():
@@ -101,6 +118,8 @@ def lib():
                                   ctypes.POINTER(u64)]
     L.ersj_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     L.ersj_free.argtypes = [vp]
+    L.ersj_knn.argtypes = [vp, i64, i32, i64, vp, i64, i64, i32, dbl, dbl, ctypes.POINTER(Options),
+                           vp, vp, ctypes.POINTER(KnnInfo), vp]
     L.ersj_free.restype = None
     L.ersj_last_error.argtypes = []
     L.ersj_last_error.restype = ctypes.c_char_p
@@ -357,6 +376,33 @@ def semi_join(q: torch.Tensor, x: torch.Tensor, eps: float, budget_bytes: int = 
         return parts, h
     h.free()
     return parts
+
+
+def knn(x: torch.Tensor, k: int, eps0: float, q: torch.Tensor = None, growth: float = 0.0,
+        options: Options = None, stream=None, with_dist: bool = True):
+    """Exact k nearest neighbours (``ersj_knn``; RT-HiSS Sec. VI, growing
+    similarity searches): for each row of ``q`` (the rows of ``x`` when None),
+    the k rows of ``x`` with the smallest canonical binary64 squared distance,
+    ties to the smaller row.  Returns (ids int32 [nq, k] holding uint32 row
+    numbers, D64 float64 [nq, k] or None, info dict)."""
+    _rows_tensor(x, "x")
+    nq, ldq, qp = 0, 0, None
+    if q is not None:
+        _rows_tensor(q, "q")
+        if q.shape[1] != x.shape[1]:
+            raise ValueError(f"q has {q.shape[1]} columns, x {x.shape[1]}")
+        nq, ldq, qp = q.shape[0], q.stride(0), ctypes.c_void_p(q.data_ptr())
+    rows = nq if q is not None else x.shape[0]
+    ids = torch.empty((rows, int(k)), dtype=torch.int32, device=x.device)
+    dist = torch.empty((rows, int(k)), dtype=torch.float64, device=x.device) if with_dist else None
+    info = KnnInfo()
+    _check(lib().ersj_knn(ctypes.c_void_p(x.data_ptr()), x.shape[0], x.shape[1], x.stride(0), qp, nq, ldq,
+                          int(k), float(eps0), float(growth),
+                          ctypes.byref(options) if options is not None else None,
+                          ctypes.c_void_p(ids.data_ptr()),
+                          ctypes.c_void_p(dist.data_ptr()) if dist is not None else None,
+                          ctypes.byref(info), _stream(stream)))
+    return ids, dist, info.as_dict()
 
 
 def pairs_to_numpy(parts):

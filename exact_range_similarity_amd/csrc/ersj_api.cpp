@@ -836,6 +836,80 @@ int ensure_delivery(ersj_index *h)
     return ERSJ_OK;
 }
 
+// ---- exact kNN driver -------------------------------------------------
+
+// Device memory of one ersj_knn call (not tied to an index handle).
+struct DevBuf {
+    void *p = nullptr;
+    DevBuf() = default;
+    DevBuf(const DevBuf &) = delete;
+    DevBuf &operator=(const DevBuf &) = delete;
+    ~DevBuf()
+    {
+        if (p) (void)hipFree(p);
+    }
+    int get(size_t bytes, const char *what)
+    {
+        if (p) return ERSJ_OK;
+        const hipError_t e = hipMalloc(&p, bytes ? bytes : 1);
+        if (e != hipSuccess) {
+            p = nullptr;
+            (void)hipGetLastError();
+            return fail(ERSJ_ERR_OOM, "cannot allocate %zu bytes for %s", bytes, what);
+        }
+        return ERSJ_OK;
+    }
+    template <typename T>
+    T *as() const
+    {
+        return (T *)p;
+    }
+};
+
+struct IndexGuard {
+    ersj_index *h = nullptr;
+    ~IndexGuard();
+};
+
+constexpr int kKnnFiniteRounds = ERSJ_KNN_MAX_ROUNDS - 1;
+
+// Next radius factor from the queries that stayed short of k neighbours:
+// query q had c_q neighbours within eps, np_q of them at a positive distance,
+// and over those the sum L_q of log(eps / rho).  Pooled over the queries,
+// m = sum np / sum L is the maximum-likelihood local dimension of Levina and
+// Bickel (counts growing like radius^m).  Neighbours at distance zero count
+// toward k at any radius, so query q needs the radius times
+// ((k - (c_q - np_q)) / np_q)^(1/m).  The factor is the 95th percentile of
+// that need within [1.01, 4]; it is 4 when most queries have no neighbour at
+// a positive distance yet (the radius is still below the neighbour scale)
+// or when nothing can be estimated.
+double knn_factor(int k, const std::vector<uint32_t> &packed, const std::vector<double> &lsum,
+                  double *dim)
+{
+    double sn = 0.0, sl = 0.0;
+    size_t none = 0;
+    for (size_t i = 0; i < packed.size(); ++i) {
+        const uint32_t np = packed[i] >> 16;
+        sn += (double)np;
+        sl += lsum[i];
+        none += np == 0;
+    }
+    *dim = 0.0;
+    if (!(sn > 0.0 && sl > 0.0)) return 4.0;
+    const double m = sn / sl;
+    *dim = m;
+    if (2 * none > packed.size()) return 4.0;
+    std::vector<double> need(packed.size());
+    for (size_t i = 0; i < packed.size(); ++i) {
+        const double c = (double)(packed[i] & 0xffffu), np = (double)(packed[i] >> 16);
+        need[i] = std::pow(((double)k - (c - np)) / std::max(0.5, np), 1.0 / m);
+    }
+    const size_t at = std::min(need.size() - 1, (size_t)std::ceil(0.95 * (double)need.size()) - 1);
+    std::nth_element(need.begin(), need.begin() + at, need.end());
+    const double f = need[at];
+    return std::isfinite(f) ? std::min(4.0, std::max(1.01, f)) : 4.0;
+}
+
 }  // namespace
 
 // =================================================================== ABI ==
@@ -1151,4 +1225,137 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     return ERSJ_OK;
 }
 
+int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_q, int64_t nq,
+             int64_t ldq, int32_t k, double eps0, double growth, const ersj_options *opt,
+             uint32_t *d_ids, double *d_dist2, ersj_knn_info *info, void *stream)
+{
+    g_err.clear();
+    if (!d_x) return fail(ERSJ_ERR_INVALID_ARG, "d_x is NULL");
+    if (!d_ids) return fail(ERSJ_ERR_INVALID_ARG, "d_ids is NULL");
+    if (n < 1 || n > 0xffffffffll) return fail(ERSJ_ERR_INVALID_ARG, "n = %lld outside [1, 2^32-1]", (long long)n);
+    if (d < 1 || d > kMaxDim) return fail(ERSJ_ERR_INVALID_ARG, "d = %d outside [1, %d]", d, kMaxDim);
+    if (ld < d) return fail(ERSJ_ERR_INVALID_ARG, "ld = %lld < d = %d", (long long)ld, d);
+    if (d_q) {
+        if (nq < 1 || nq > 0xffffffffll)
+            return fail(ERSJ_ERR_INVALID_ARG, "nq = %lld outside [1, 2^32-1]", (long long)nq);
+        if (ldq < d) return fail(ERSJ_ERR_INVALID_ARG, "ldq = %lld < d = %d", (long long)ldq, d);
+    } else {
+        nq = n;
+        ldq = ld;
+    }
+    const int64_t kmax = std::min<int64_t>(n, knn_max_k());
+    if (k < 1 || k > kmax) return fail(ERSJ_ERR_INVALID_ARG, "k = %d outside [1, %lld]", k, (long long)kmax);
+    if (!(eps0 > 0.0)) return fail(ERSJ_ERR_INVALID_ARG, "eps0 must be > 0 (got %g)", eps0);
+    if (!(growth == 0.0 || (growth > 1.0 && std::isfinite(growth))))
+        return fail(ERSJ_ERR_INVALID_ARG, "growth must be 0 or a finite factor > 1 (got %g)", growth);
+    if (info) std::memset(info, 0, sizeof *info);
+    hipStream_t s = (hipStream_t)stream;
+    const float *qsrc = d_q ? d_q : d_x;
+
+    DevBuf idx[2], nbrs, lsum, counter, qrows;
+    TRY(idx[0].get(sizeof(uint32_t) * (size_t)nq, "kNN query lists"));
+    TRY(idx[1].get(sizeof(uint32_t) * (size_t)nq, "kNN query lists"));
+    TRY(nbrs.get(sizeof(uint32_t) * (size_t)nq, "kNN counts"));
+    TRY(lsum.get(sizeof(double) * (size_t)nq, "kNN counts"));
+    TRY(counter.get(sizeof(uint32_t), "kNN counter"));
+    int cur = 0;  // idx[cur] lists the round's queries (round 0: all, in order)
+    int64_t m = nq;
+    double eps = eps0;
+    uint64_t total = 0;
+    int round = 0;
+    while (m > 0) {
+        if (round >= kKnnFiniteRounds) eps = INFINITY;
+        const float *qb = qsrc;
+        int64_t lq = ldq;
+        if (round > 0) {
+            TRY(qrows.get(sizeof(float) * (size_t)nq * (size_t)d, "kNN query rows"));
+            HIPC(launch_gather_rows(qsrc, ldq, idx[cur].as<uint32_t>(), (uint64_t)m, d, qrows.as<float>(), s),
+                 "kNN gather kernel");
+            qb = qrows.as<float>();
+            lq = d;
+        }
+        IndexGuard g;
+        TRY(ersj_build_index(d_x, n, d, ld, eps, opt, stream, &g.h));
+        TRY(ersj_set_queries(g.h, qb, m, lq, stream));
+        uint64_t cand = 0;
+        TRY(ersj_count_pass(g.h, &cand, stream));
+        int32_t nbatch = 0;
+        TRY(ersj_plan_batches(g.h, 0, &nbatch, stream));
+        ersj_index *h = g.h;
+        DeviceGuard dg(h->device);
+        if (!dg.ok()) return fail(ERSJ_ERR_HIP, "cannot select the index's device");
+        HIPC(hipMemsetAsync(counter.p, 0, sizeof(uint32_t), s), "clear kNN counter");
+        KnnArgs a{};
+        a.tiles = h->tiles;
+        a.toff = h->toff;
+        a.rpref = h->rpref;
+        a.rstart = h->rstart;
+        a.nrng = h->nrng;
+        a.orig = h->orig;
+        a.qorig = h->qorig;
+        a.qmap = round > 0 ? idx[cur].as<uint32_t>() : nullptr;
+        a.qbase = qb;
+        a.ldq = lq;
+        a.x = d_x;
+        a.ld = ld;
+        a.d = d;
+        a.k = (uint32_t)k;
+        a.e64 = h->e64;
+        a.next = idx[1 - cur].as<uint32_t>();
+        a.next_count = counter.as<uint32_t>();
+        a.next_nbrs = nbrs.as<uint32_t>();
+        a.next_lsum = lsum.as<double>();
+        a.ids = d_ids;
+        a.dist = d_dist2;
+        for (int32_t b = 0; b < nbatch; ++b) {
+            h->ready_batch = -1;
+            TRY(do_refine(h, b, s));
+            a.t0 = h->hb[b];
+            a.wbase = h->hwords[b];
+            a.row_base = h->hrows[b];
+            a.mask = h->mask;
+            a.rowcnt = h->rowcnt;
+            HIPC(launch_knn_select(a, h->hb[b + 1] - h->hb[b], s), "kNN select kernel");
+        }
+        uint32_t left = 0;
+        HIPC(hipMemcpyAsync(&left, counter.p, sizeof left, hipMemcpyDeviceToHost, s), "copy");
+        HIPC(hipStreamSynchronize(s), "kNN round");
+        total += cand;
+        double dim = 0.0, next = eps;
+        if (left > 0) {
+            if (std::isinf(eps))
+                return fail(ERSJ_ERR_HIP, "%u queries short of k neighbours at an infinite radius", left);
+            double f = growth;
+            if (growth == 0.0) {
+                std::vector<uint32_t> hn(left);
+                std::vector<double> hl(left);
+                HIPC(hipMemcpy(hn.data(), nbrs.p, sizeof(uint32_t) * left, hipMemcpyDeviceToHost), "copy");
+                HIPC(hipMemcpy(hl.data(), lsum.p, sizeof(double) * left, hipMemcpyDeviceToHost), "copy");
+                f = knn_factor(k, hn, hl, &dim);
+            }
+            next = eps * f;
+            if (!(next > eps) || std::isinf(next)) next = INFINITY;
+        }
+        if (info && round < ERSJ_KNN_MAX_ROUNDS) {
+            info->eps[round] = eps;
+            info->queries[round] = m;
+            info->candidates[round] = cand;
+            info->dim_estimate[round] = dim;
+        }
+        ++round;
+        m = left;
+        cur = 1 - cur;
+        eps = next;
+    }
+    if (info) {
+        info->rounds = round;
+        info->total_candidates = total;
+    }
+    return ERSJ_OK;
+}
+
 }  // extern "C"
+
+namespace {
+IndexGuard::~IndexGuard() { ersj_free(h); }
+}  // namespace

@@ -241,6 +241,38 @@ struct RefineArgs {
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
 
+// ---- exact kNN (k_knn.hip) ----
+struct KnnArgs {
+    const Tile *tiles;
+    uint32_t t0;                 // first tile of the batch (index order)
+    const uint64_t *toff;
+    uint64_t wbase;              // first mask word of the batch
+    uint64_t row_base;           // first query row of the batch
+    const uint64_t *mask;
+    const uint32_t *rowcnt;      // neighbours per row of the batch
+    const uint32_t *rpref, *rstart, *nrng;
+    const uint32_t *orig;        // sorted point -> input row
+    const uint32_t *qorig;       // index-order query row -> row of qbase
+    const uint32_t *qmap;        // row of qbase -> query id of the search (NULL: identity)
+    const float *qbase;          // the round's query rows, row-major
+    int64_t ldq;
+    const float *x;              // the points, row-major, input dimension order
+    int64_t ld;
+    int32_t d;
+    uint32_t k;
+    double e64;                  // the round's fl(eps^2)
+    uint32_t *next;              // queries left for the next round
+    uint32_t *next_count;
+    uint32_t *next_nbrs;         // their neighbour count c at this radius, | (terms << 16)
+    double *next_lsum;           // sum of log(eps / dist) over the neighbours at dist > 0 (terms)
+    uint32_t *ids;               // [nq][k]
+    double *dist;                // [nq][k] or NULL
+};
+int knn_max_k();
+hipError_t launch_knn_select(const KnnArgs &a, uint32_t ntiles, hipStream_t s);
+hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, uint64_t m, int32_t d,
+                              float *out, hipStream_t s);
+
 // k_refine_mfma.hip: query blocks of 32 rows per work item (4, 2 or 1)
 int refine_mfma_qblocks(int nb);
 size_t refine_mfma_lds_bytes(int nb);

@@ -1,0 +1,304 @@
+// Exact k nearest neighbours from a similarity-search round, for gfx950.
+//
+// Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+// Similarity Searches", Sec. VI: the k-nearest-neighbours search becomes a
+// sequence of distance similarity searches whose radius grows until every
+// query has k neighbours; with the index on three dimensions this still
+// gives the exact kNN.  After a round's batch is refined (its result mask
+// final, Sec. IV-F), each query row with at least k neighbours holds its k
+// nearest among them: every point closer than the k-th neighbour is within
+// the round's radius.  Rows with fewer go to the next round.
+//
+// Ranking key of a neighbour: (D64, point id), D64 the canonical binary64
+// squared distance (sum over the input's own dimension order of the squared
+// differences, each operation rounded, no fused multiply-add).  D64 >= 0, so
+// its bit pattern orders like its value, and the 96-bit key (D64 bits, id)
+// is unique within a row.
+//
+// A row with fewer than k neighbours also reports its count and the sum of
+// log(eps / dist) over its neighbours at a positive distance: with the
+// counts, the maximum-likelihood estimate of the local dimension m of
+// Levina and Bickel ("Maximum likelihood estimation of intrinsic
+// dimension", 2004) is (number of terms) / (sum), from which the host sizes
+// the next radius (a count growing like radius^m).
+//
+// Workgroup per row tile, wave per row.  A row with at most kCap neighbours
+// gathers their keys into the wave's LDS area and sorts them (bitonic);
+// a longer row finds the k-th smallest key by a radix select over 8-bit
+// digits (twelve passes, each recomputing the keys from the mask), then
+// gathers the k keys at or below it and sorts those.  No pair list is
+// written to memory.
+#include "ersj_internal.h"
+
+namespace ersj {
+
+namespace {
+
+constexpr int kCap = 1024;  // keys a wave sorts in LDS (also the largest k)
+constexpr int kWaves = 4;
+
+struct KnnLds {
+    uint64_t hi[kWaves][kCap];   // D64 bits
+    uint32_t lo[kWaves][kCap];   // point id
+    uint32_t hist[kWaves][256];
+    uint32_t pref[kMaxRanges + 1];
+    uint32_t start[kMaxRanges];
+};
+
+__device__ __forceinline__ bool key_less(uint64_t ah, uint32_t al, uint64_t bh, uint32_t bl)
+{
+    return ah < bh || (ah == bh && al < bl);
+}
+
+// digit p (0 = most significant) of the 96-bit key
+__device__ __forceinline__ uint32_t key_digit(uint64_t h, uint32_t l, int p)
+{
+    return p < 8 ? (uint32_t)(h >> (56 - 8 * p)) & 255u : (l >> (24 - 8 * (p - 8))) & 255u;
+}
+
+// the digits above p of the key equal those of the prefix
+__device__ __forceinline__ bool key_match(uint64_t h, uint32_t l, uint64_t ph, uint32_t pl, int p)
+{
+    if (p == 0) return true;
+    if (p <= 8) return (h >> (64 - 8 * p)) == (ph >> (64 - 8 * p));
+    return h == ph && (l >> (32 - 8 * (p - 8))) == (pl >> (32 - 8 * (p - 8)));
+}
+
+// sort hi/lo[0, S) ascending by key; S a power of two, one wave
+__device__ void wave_bitonic(uint64_t *hi, uint32_t *lo, int S, int lane)
+{
+    for (int size = 2; size <= S; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = lane; i < (S >> 1); i += 64) {
+                const int a = 2 * i - (i & (stride - 1));
+                const int b = a + stride;
+                const bool up = (a & size) == 0;
+                const uint64_t ah = hi[a], bh = hi[b];
+                const uint32_t al = lo[a], bl = lo[b];
+                if (key_less(bh, bl, ah, al) == up) {
+                    hi[a] = bh;
+                    lo[a] = bl;
+                    hi[b] = ah;
+                    lo[b] = al;
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        }
+    }
+}
+
+// Canonical D64 of two rows in the input's dimension order: each difference,
+// square and sum rounded on its own (the pragma sits in this body because a
+// lambda body does not take it from the enclosing function).
+__device__ __forceinline__ double canonical_d64(const float *__restrict__ q, const float *__restrict__ x, int d)
+{
+#pragma clang fp contract(off)
+    double s = 0.0;
+    for (int j = 0; j < d; ++j) {
+        const double u = (double)q[j] - (double)x[j];
+        const double uu = u * u;
+        s = s + uu;
+    }
+    return s;
+}
+
+__device__ __forceinline__ uint32_t pow2_at_least(uint32_t v)
+{
+    uint32_t s = 1;
+    while (s < v) s <<= 1;
+    return s;
+}
+
+__global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
+{
+    __shared__ KnnLds L;
+    const uint32_t t = a.t0 + blockIdx.x;
+    const Tile tl = a.tiles[t];
+    const uint32_t A = tl.cell;
+    const uint32_t nr = a.nrng[A];
+    if (threadIdx.x <= kMaxRanges)
+        L.pref[threadIdx.x] = threadIdx.x <= nr ? a.rpref[(uint64_t)A * (kMaxRanges + 1) + threadIdx.x] : 0xffffffffu;
+    if (threadIdx.x < kMaxRanges) L.start[threadIdx.x] = a.rstart[(uint64_t)A * kMaxRanges + threadIdx.x];
+    __syncthreads();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    uint64_t *const ehi = L.hi[wave];
+    uint32_t *const elo = L.lo[wave];
+    uint32_t *const hist = L.hist[wave];
+    const uint32_t k = a.k;
+    const int32_t d = a.d;
+    const uint64_t tbase = a.toff[t] - a.wbase;
+
+    for (uint32_t r = wave; r < tl.nrows; r += kWaves) {
+        const uint32_t q = tl.row0 + r;
+        const uint32_t c = a.rowcnt[q - a.row_base];
+        const uint32_t qid = a.qorig[q];                   // row of the round's query array
+        const uint32_t oq = a.qmap ? a.qmap[qid] : qid;    // query id of the whole search
+        const float *qrow = a.qbase + (uint64_t)qid * a.ldq;
+        const uint64_t *row = a.mask + tbase + (uint64_t)r * tl.words;
+
+        // Calls f(valid, hi, lo) once per lane and step while the row's set
+        // bits last: each valid lane holds one neighbour's key.
+        auto for_each = [&](auto &&f) __attribute__((always_inline)) {
+            for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
+                const uint32_t w = w0 + lane;
+                uint64_t m = w < tl.used ? row[w] : 0ull;
+                while (__ballot(m != 0) != 0) {
+                    const bool valid = m != 0;
+                    uint64_t kh = ~0ull;
+                    uint32_t kl = ~0u;
+                    if (valid) {
+                        const int bit = __ffsll((unsigned long long)m) - 1;
+                        m &= m - 1;
+                        const uint32_t p = w * 64 + bit;
+                        const int g = range_of(L.pref, nr, p);
+                        const uint32_t pid = a.orig[L.start[g] + (p - L.pref[g])];
+                        const double s = canonical_d64(qrow, a.x + (uint64_t)pid * a.ld, d);
+                        kh = (uint64_t)__double_as_longlong(s);
+                        kl = pid;
+                    }
+                    f(valid, kh, kl);
+                }
+            }
+        };
+        // append the valid lanes' keys at ehi/elo[*n ...]
+        auto append = [&](bool valid, uint64_t kh, uint32_t kl, uint32_t &n) __attribute__((always_inline)) {
+            const uint64_t b = __ballot(valid);
+            const uint32_t below = __popcll(b & ((1ull << lane) - 1ull));
+            if (valid && n + below < (uint32_t)kCap) {
+                ehi[n + below] = kh;
+                elo[n + below] = kl;
+            }
+            n += __popcll(b);
+        };
+
+        if (c < k) {
+            // too few: report the query with what the next radius needs
+            double ls = 0.0;
+            uint32_t np = 0;
+            for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                const double dd = __longlong_as_double((long long)kh);
+                if (v && dd > 0.0) {
+                    ls += 0.5 * log(a.e64 / dd);
+                    ++np;
+                }
+            });
+            for (int o = 32; o > 0; o >>= 1) {
+                ls += __shfl_xor(ls, o, 64);
+                np += __shfl_xor(np, o, 64);
+            }
+            if (lane == 0) {
+                const uint32_t pos = atomicAdd(a.next_count, 1u);
+                a.next[pos] = oq;
+                a.next_nbrs[pos] = c | (np << 16);  // both below 2^16 (c < k <= 1024)
+                a.next_lsum[pos] = np > 0 ? ls : 0.0;
+            }
+            continue;
+        }
+        uint32_t nsel = 0;
+        if (c <= (uint32_t)kCap) {
+            for_each([&](bool v, uint64_t kh, uint32_t kl) { append(v, kh, kl, nsel); });
+        } else {
+            // radix select of the k-th smallest key, 8 bits per pass
+            uint64_t ph = 0;
+            uint32_t pl = 0, rank = k - 1;
+            for (int p = 0; p < 12; ++p) {
+                for (int i = lane; i < 256; i += 64) hist[i] = 0;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                    if (v && key_match(kh, kl, ph, pl, p)) atomicAdd(&hist[key_digit(kh, kl, p)], 1u);
+                });
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                // bucket holding the rank: lane l sums buckets 4l .. 4l+3
+                uint32_t h4[4], s4 = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    h4[j] = hist[4 * lane + j];
+                    s4 += h4[j];
+                }
+                uint32_t inc = s4;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t v = __shfl_up(inc, o, 64);
+                    if (lane >= o) inc += v;
+                }
+                const uint32_t exc = inc - s4;
+                const bool mine = exc <= rank && rank < inc;
+                const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+                uint32_t dig = 0, before = exc;
+                if (mine) {
+                    uint32_t run = exc;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (rank >= run && rank < run + h4[j]) {
+                            dig = 4 * lane + j;
+                            before = run;
+                        }
+                        run += h4[j];
+                    }
+                }
+                dig = __shfl(dig, owner, 64);
+                before = __shfl(before, owner, 64);
+                rank -= before;
+                if (p < 8) ph |= (uint64_t)dig << (56 - 8 * p);
+                else pl |= dig << (24 - 8 * (p - 8));
+            }
+            // the k keys at or below the k-th smallest
+            for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                append(v && !key_less(ph, pl, kh, kl), kh, kl, nsel);
+            });
+        }
+        nsel = min(nsel, (uint32_t)kCap);
+        const uint32_t S = pow2_at_least(nsel);
+        for (uint32_t i = nsel + lane; i < S; i += 64) {
+            ehi[i] = ~0ull;
+            elo[i] = ~0u;
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        wave_bitonic(ehi, elo, (int)S, lane);
+        for (uint32_t i = lane; i < k; i += 64) {
+            a.ids[(uint64_t)oq * k + i] = elo[i];
+            if (a.dist) a.dist[(uint64_t)oq * k + i] = __longlong_as_double((long long)ehi[i]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+}
+
+// rows idx[i] of a row-major array, packed: out[i * d + j] = q[idx[i] * ldq + j]
+__global__ __launch_bounds__(256) void k_gather_rows(const float *__restrict__ q, int64_t ldq,
+                                                     const uint32_t *__restrict__ idx, uint64_t m,
+                                                     int32_t d, float *__restrict__ out)
+{
+    const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= m * (uint64_t)d) return;
+    const uint64_t i = e / (uint64_t)d, j = e - i * (uint64_t)d;
+    out[e] = q[(uint64_t)idx[i] * ldq + j];
+}
+
+}  // namespace
+
+int knn_max_k() { return kCap; }
+
+hipError_t launch_knn_select(const KnnArgs &a, uint32_t ntiles, hipStream_t s)
+{
+    if (ntiles == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_knn_select, dim3(ntiles), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, uint64_t m, int32_t d,
+                              float *out, hipStream_t s)
+{
+    const uint64_t total = m * (uint64_t)d;
+    if (total == 0) return hipSuccess;
+    const uint64_t blocks = (total + 255) / 256;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)blocks), dim3(256), 0, s, q, ldq, idx, m, d, out);
+    return hipGetLastError();
+}
+
+}  // namespace ersj

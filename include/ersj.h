@@ -206,6 +206,54 @@ int ersj_fill_pass_host(ersj_index *h, int32_t batch, uint32_t *host_pairs, uint
  * memory.  Errors: INVALID_ARG, HIP. */
 int ersj_host_sync(ersj_index *h);
 
+/*
+ * Exact k nearest neighbours by growing similarity searches (Sec. VI: the
+ * kNN problem recast as distance similarity searches whose radius grows until
+ * k neighbours are found, which stays exact with three indexed dimensions).
+ * The k nearest neighbours of a query are the k points with the smallest
+ * D64 (the canonical binary64 squared distance of the join), ties broken by
+ * the smaller point id.
+ *  d_x, n, d, ld : the points, as for ersj_build_index.
+ *  d_q, nq, ldq  : device query rows (row-major, d floats each); d_q = NULL
+ *                  searches the points themselves (nq and ldq are ignored): a
+ *                  point is then its own first neighbour unless an identical
+ *                  point has a smaller id.  Query rows borrowed for the call.
+ *  k             : 1 <= k <= min(n, 1024).
+ *  eps0          : radius of the first round, > 0 (+inf: one round in which
+ *                  every point is a candidate).
+ *  growth        : > 1: each round multiplies the radius by it; 0: the next
+ *                  radius is estimated from the queries still short of k
+ *                  neighbours (their counts and, pooled, the maximum-likelihood
+ *                  local dimension of Levina and Bickel), factor in [1.01, 4].
+ *  opt           : as for ersj_build_index (NULL: defaults).
+ *  d_ids         : device [nq][k] uint32, row q = its neighbours' input row
+ *                  numbers, nearest first.
+ *  d_dist2       : device [nq][k] double, their D64 values, or NULL.
+ *  info          : host out (may be NULL).
+ * Round r searches only the queries that still lack k neighbours, as a
+ * semi-join against the points with its own index; a query with c >= k
+ * neighbours takes the k smallest keys among them (every closer point lies
+ * within the radius).  After 40 rounds, or once the radius overflows, the
+ * radius becomes +inf, where every query has all n points as neighbours, so
+ * the search always ends.  No pair list is written: each round needs the
+ * memory of a semi-join's index and result mask.
+ * Errors: INVALID_ARG (also non-finite coordinates), HIP, OOM, BUDGET.
+ */
+#define ERSJ_KNN_MAX_ROUNDS 41
+typedef struct ersj_knn_info {
+    int32_t rounds;                             /* rounds run */
+    int32_t reserved;
+    double eps[ERSJ_KNN_MAX_ROUNDS];            /* radius of round r */
+    int64_t queries[ERSJ_KNN_MAX_ROUNDS];       /* queries searched in round r */
+    uint64_t candidates[ERSJ_KNN_MAX_ROUNDS];   /* candidates refined in round r */
+    double dim_estimate[ERSJ_KNN_MAX_ROUNDS];   /* local dimension estimated after round r (0: none) */
+    uint64_t total_candidates;
+} ersj_knn_info;
+
+int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_q, int64_t nq,
+             int64_t ldq, int32_t k, double eps0, double growth, const ersj_options *opt,
+             uint32_t *d_ids, double *d_dist2, ersj_knn_info *info, void *stream);
+
 /* Rows covered by a batch (index order) and its mask size.  Host outputs. */
 int ersj_batch_info(const ersj_index *h, int32_t batch, uint64_t *first_row, uint64_t *n_rows,
                     uint64_t *mask_words);

@@ -75,6 +75,22 @@ def test_null_handle_paths():
     L.ersj_free(None)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(ids=None), dict(n=0), dict(d=0), dict(ld=2), dict(k=0), dict(k=11),
+    dict(k=1025, n=2000), dict(eps0=0.0), dict(eps0=-1.0), dict(eps0=float("nan")),
+    dict(growth=1.0), dict(growth=0.5), dict(growth=float("inf")), dict(q=FAKE, nq=0),
+    dict(q=FAKE, nq=5, ldq=2),
+])
+def test_knn_rejects_bad_arguments(kw):
+    a = dict(x=FAKE, n=10, d=3, ld=3, q=None, nq=0, ldq=0, k=3, eps0=1.0, growth=0.0, ids=FAKE)
+    a.update(kw)
+    info = ersj.KnnInfo()
+    rc = ersj.lib().ersj_knn(a["x"], a["n"], a["d"], a["ld"], a["q"], a["nq"], a["ldq"], a["k"],
+                             a["eps0"], a["growth"], None, a["ids"], None, ctypes.byref(info), None)
+    assert rc == ersj.ERR_INVALID_ARG
+    assert ersj.lib().ersj_last_error()
+
+
 def test_error_message_is_per_call():
     rc, _ = build(d=0)
     assert rc == ersj.ERR_INVALID_ARG
