@@ -16,6 +16,9 @@ oracle timed on a bounded sample of the same workload.
 
 ``--mode semijoin`` joins a separate query set (the workload's cluster
 structure, rows from another seed; RT-HiSS Sec. II-A) against the points.
+``--mode knn`` finds the exact k nearest neighbours of every point (RT-HiSS
+Sec. VI, growing similarity searches from the workload's epsilon); its line
+reports queries per second instead.
 """
 import argparse
 import json
@@ -54,8 +57,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--mode", choices=("selfjoin", "semijoin"), default="selfjoin",
-                    help="semijoin: a separate query set from the workload's structure")
+    ap.add_argument("--mode", choices=("selfjoin", "semijoin", "knn"), default="selfjoin",
+                    help="semijoin: a separate query set from the workload's structure; "
+                         "knn: exact k nearest neighbours of every point")
+    ap.add_argument("--k", type=int, default=0, help="kNN: neighbours per query (0 = the workload's k)")
+    ap.add_argument("--eps0-scale", type=float, default=1.0,
+                    help="kNN: first radius as a multiple of the workload's epsilon")
+    ap.add_argument("--growth", type=float, default=0.0, help="kNN: radius factor (0 = estimated)")
     ap.add_argument("--grid-reach", type=int, default=1, choices=(1, 2),
                     help="2: cells of width eps/2 and a 5x5x5 stencil (fewer candidates)")
     ap.add_argument("--no-block-prune", action="store_true",
@@ -96,6 +104,9 @@ def main():
         log(f"[bench] semi-join: {nq} queries from the workload's structure (seed {spec.seed + 1000})")
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    if args.mode == "knn":
+        run_knn(args, spec, rec, eps, X, xt, stream)
+        return
 
     budget = 0
     if args.budget_frac > 0:
@@ -279,6 +290,94 @@ def main():
                       f"{X.shape[0]} points (brute force, binary64), {dt:.1f}s",
             "sample_pairs": int(colptr[-1]),
             "full_join_s_extrapolated": dt * Q.shape[0] / nrows,
+        }
+    print(json.dumps(out), flush=True)
+
+
+def run_knn(args, spec, rec, eps, X, xt, stream):
+    """One step = exact kNN of every point (ersj_knn) from eps0 = scale * eps."""
+    import numpy as np
+    import torch
+    import exact_range_similarity_amd as ersj
+
+    k = args.k if args.k > 0 else spec.k
+    eps0 = eps * args.eps0_scale
+    opts = ersj.default_options(timing=1, refine_kernel=args.refine, grid_reach=args.grid_reach,
+                                block_prune=-1 if args.no_block_prune else 0)
+    ids = None
+    for w in range(args.warmup):
+        ids, _, info = ersj.knn(xt, k, eps0, growth=args.growth, options=opts, stream=stream)
+        log(f"[bench] knn warmup {w}: rounds {info['rounds']} queries {info['queries']}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    infos = []
+    for step in range(args.steps):
+        ids, dist, info = ersj.knn(xt, k, eps0, growth=args.growth, options=opts, stream=stream)
+        infos.append(info)
+        log(f"[bench] knn step {step}: rounds {info['rounds']} refine {info['refine_ms']:.2f} ms "
+            f"select {info['select_ms']:.2f} ms")
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    info = infos[-1]
+    n, d = X.shape
+    refine_ms = sum(i["refine_ms"] for i in infos)
+    launches = sum(i["refine_launches"] for i in infos)
+    computed = sum(i["computed_candidates"] for i in infos)
+    mfma = args.refine != 1
+    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
+    avg_launch_ms = refine_ms / max(1, launches)
+    flops_per_launch = per_cand * computed / max(1, launches)
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    phases = {key: sum(i[key] for i in infos) / args.steps
+              for key in ("index_ms", "refine_ms", "recheck_ms", "select_ms")}
+    out = {
+        "metric": f"exact kNN queries/s (k={k}), 1 GPU",
+        "value": n / wall,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {spec.desc}; exact kNN of every point, k={k}, first "
+                               f"radius {args.eps0_scale} x the workload's eps",
+                   "mode": "knn", "n": int(n), "d": int(d), "k": int(k), "eps0": eps0.hex(),
+                   "growth": args.growth, "grid_reach": args.grid_reach,
+                   "block_prune": not args.no_block_prune},
+        "rounds": info["rounds"],
+        "queries_per_round": info["queries"],
+        "eps_per_round": info["eps"],
+        "dim_estimate": info["dim_estimate"],
+        "candidates": info["total_candidates"],
+        "phase_ms": phases,
+        "roofline": {
+            "bound": "mfma" if mfma else "alu",
+            "kernel": "k_refine_mfma" if mfma else "k_refine_direct",
+            "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+            "flops_per_launch": flops_per_launch, "avg_launch_ms": avg_launch_ms, "launches": launches,
+        },
+    }
+    if not args.no_cpu:
+        import oracle
+        probe = 2 * oracle.threads()
+        t = time.perf_counter()
+        oracle.knn(X, k, np.arange(probe))
+        per_row = (time.perf_counter() - t) / probe
+        nrows = int(max(probe, min(n, args.cpu_seconds / max(per_row, 1e-9))))
+        t = time.perf_counter()
+        want, _ = oracle.knn(X, k, np.arange(nrows))
+        dt = time.perf_counter() - t
+        got = ids[:nrows].cpu().numpy().view(np.uint32)
+        out["cpu_baseline"] = {
+            "value": nrows / dt, "unit": "queries/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"rows 0..{nrows - 1} of {args.workload}: every point ranked (brute force, "
+                      f"binary64, sort), {dt:.1f}s",
+            "sample_matches_gpu": bool(np.array_equal(got, want)),
         }
     print(json.dumps(out), flush=True)
 

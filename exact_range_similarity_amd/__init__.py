@@ -79,13 +79,19 @@ class KnnInfo(ctypes.Structure):
                 ("eps", ctypes.c_double * KNN_MAX_ROUNDS), ("queries", ctypes.c_int64 * KNN_MAX_ROUNDS),
                 ("candidates", ctypes.c_uint64 * KNN_MAX_ROUNDS),
                 ("dim_estimate", ctypes.c_double * KNN_MAX_ROUNDS),
-                ("total_candidates", ctypes.c_uint64)]
+                ("total_candidates", ctypes.c_uint64), ("index_ms", ctypes.c_double),
+                ("refine_ms", ctypes.c_double), ("recheck_ms", ctypes.c_double),
+                ("select_ms", ctypes.c_double), ("refine_launches", ctypes.c_int64),
+                ("computed_candidates", ctypes.c_uint64)]
 
     def as_dict(self):
-        r = self.rounds
-        return {"rounds": r, "eps": list(self.eps[:r]), "queries": list(self.queries[:r]),
+        r = min(self.rounds, KNN_MAX_ROUNDS)
+        return {"rounds": self.rounds, "eps": list(self.eps[:r]), "queries": list(self.queries[:r]),
                 "candidates": list(self.candidates[:r]), "dim_estimate": list(self.dim_estimate[:r]),
-                "total_candidates": self.total_candidates}
+                "total_candidates": self.total_candidates, "index_ms": self.index_ms,
+                "refine_ms": self.refine_ms, "recheck_ms": self.recheck_ms, "select_ms": self.select_ms,
+                "refine_launches": self.refine_launches,
+                "computed_candidates": self.computed_candidates}
 
 
 SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",

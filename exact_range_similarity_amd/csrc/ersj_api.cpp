@@ -877,37 +877,39 @@ constexpr int kKnnFiniteRounds = ERSJ_KNN_MAX_ROUNDS - 1;
 // query q had c_q neighbours within eps, np_q of them at a positive distance,
 // and over those the sum L_q of log(eps / rho).  Pooled over the queries,
 // m = sum np / sum L is the maximum-likelihood local dimension of Levina and
-// Bickel (counts growing like radius^m).  Neighbours at distance zero count
-// toward k at any radius, so query q needs the radius times
-// ((k - (c_q - np_q)) / np_q)^(1/m).  The factor is the 95th percentile of
-// that need within [1.01, 4]; it is 4 when most queries have no neighbour at
-// a positive distance yet (the radius is still below the neighbour scale)
-// or when nothing can be estimated.
-double knn_factor(int k, const std::vector<uint32_t> &packed, const std::vector<double> &lsum,
-                  double *dim)
+// Bickel (counts growing like radius^m), kept within [1, d]; with no
+// neighbour at a positive distance anywhere, m = d (the local dimension
+// cannot exceed the ambient one, so this grows the radius most cautiously).
+// Neighbours at distance zero count toward k at any radius, so query q needs
+// the radius times ((k - (c_q - np_q)) / max(np_q, 1/2))^(1/m), and passes
+// the `cap` neighbours a row ranks in on-chip memory at (cap / c_q)^(1/m).
+// The factor is the 95th percentile of the need, but no more than the 10th
+// percentile of the cap factor (so few rows take the slower ranking path),
+// within [lo, 4].
+double knn_factor(int k, int cap, double lo, int d, const std::vector<uint32_t> &packed,
+                  const std::vector<double> &lsum, double *dim)
 {
     double sn = 0.0, sl = 0.0;
-    size_t none = 0;
     for (size_t i = 0; i < packed.size(); ++i) {
-        const uint32_t np = packed[i] >> 16;
-        sn += (double)np;
+        sn += (double)(packed[i] >> 16);
         sl += lsum[i];
-        none += np == 0;
     }
-    *dim = 0.0;
-    if (!(sn > 0.0 && sl > 0.0)) return 4.0;
-    const double m = sn / sl;
+    double m = (sn > 0.0 && sl > 0.0) ? sn / sl : (double)d;
+    m = std::min((double)d, std::max(1.0, m));
     *dim = m;
-    if (2 * none > packed.size()) return 4.0;
-    std::vector<double> need(packed.size());
-    for (size_t i = 0; i < packed.size(); ++i) {
+    const size_t q = packed.size();
+    std::vector<double> need(q), room(q);
+    for (size_t i = 0; i < q; ++i) {
         const double c = (double)(packed[i] & 0xffffu), np = (double)(packed[i] >> 16);
         need[i] = std::pow(((double)k - (c - np)) / std::max(0.5, np), 1.0 / m);
+        room[i] = std::pow((double)cap / std::max(1.0, c), 1.0 / m);
     }
-    const size_t at = std::min(need.size() - 1, (size_t)std::ceil(0.95 * (double)need.size()) - 1);
-    std::nth_element(need.begin(), need.begin() + at, need.end());
-    const double f = need[at];
-    return std::isfinite(f) ? std::min(4.0, std::max(1.01, f)) : 4.0;
+    const size_t a = std::min(q - 1, (size_t)std::ceil(0.95 * (double)q) - 1);
+    std::nth_element(need.begin(), need.begin() + a, need.end());
+    const size_t b = (size_t)std::floor(0.10 * (double)(q - 1));
+    std::nth_element(room.begin(), room.begin() + b, room.end());
+    const double f = std::min(need[a], room[b]);
+    return std::isfinite(f) ? std::min(4.0, std::max(lo, f)) : 4.0;
 }
 
 }  // namespace
@@ -1307,6 +1309,7 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
         a.next_lsum = lsum.as<double>();
         a.ids = d_ids;
         a.dist = d_dist2;
+        double select_ms = 0.0;
         for (int32_t b = 0; b < nbatch; ++b) {
             h->ready_batch = -1;
             TRY(do_refine(h, b, s));
@@ -1315,7 +1318,17 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
             a.row_base = h->hrows[b];
             a.mask = h->mask;
             a.rowcnt = h->rowcnt;
+            timer_start(h, s);
             HIPC(launch_knn_select(a, h->hb[b + 1] - h->hb[b], s), "kNN select kernel");
+            select_ms += timer_stop(h, s);
+        }
+        if (info && h->opt.timing) {
+            info->index_ms += h->ms_build + h->ms_count + h->ms_plan;
+            info->refine_ms += h->ms_refine;
+            info->recheck_ms += h->ms_recheck + h->ms_expand;
+            info->select_ms += select_ms;
+            info->refine_launches += h->refine_launches;
+            info->computed_candidates += h->refined_cand - h->skipped_cand;
         }
         uint32_t left = 0;
         HIPC(hipMemcpyAsync(&left, counter.p, sizeof left, hipMemcpyDeviceToHost, s), "copy");
@@ -1331,7 +1344,9 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
                 std::vector<double> hl(left);
                 HIPC(hipMemcpy(hn.data(), nbrs.p, sizeof(uint32_t) * left, hipMemcpyDeviceToHost), "copy");
                 HIPC(hipMemcpy(hl.data(), lsum.p, sizeof(double) * left, hipMemcpyDeviceToHost), "copy");
-                f = knn_factor(k, hn, hl, &dim);
+                // the floor rises after 20 rounds so that the radius keeps
+                // growing geometrically toward the unbounded final round
+                f = knn_factor(k, knn_max_k(), round < 20 ? 1.02 : 2.0, d, hn, hl, &dim);
             }
             next = eps * f;
             if (!(next > eps) || std::isinf(next)) next = INFINITY;

@@ -23,11 +23,13 @@
 // the next radius (a count growing like radius^m).
 //
 // Workgroup per row tile, wave per row.  A row with at most kCap neighbours
-// gathers their keys into the wave's LDS area and sorts them (bitonic);
-// a longer row finds the k-th smallest key by a radix select over 8-bit
-// digits (twelve passes, each recomputing the keys from the mask), then
-// gathers the k keys at or below it and sorts those.  No pair list is
-// written to memory.
+// gathers their keys into the wave's LDS area and sorts them (bitonic).  A
+// longer row first narrows the keys with a histogram of D64 / E64 (one or
+// two counting passes, then a gathering pass of at most kCap keys); when
+// ties crowd a bucket, or the radius is infinite, an exact radix select over
+// 8-bit digits of the key (twelve passes) finds the k-th smallest key and
+// the k keys at or below it are gathered.  Every pass recomputes the keys
+// from the mask: no pair list is written to memory.
 #include "ersj_internal.h"
 
 namespace ersj {
@@ -41,6 +43,8 @@ struct KnnLds {
     uint64_t hi[kWaves][kCap];   // D64 bits
     uint32_t lo[kWaves][kCap];   // point id
     uint32_t hist[kWaves][256];
+    uint64_t words[kWaves][64];  // a 64-word chunk of the row's mask
+    uint32_t before[kWaves][64]; // set bits in the chunk's earlier words
     uint32_t pref[kMaxRanges + 1];
     uint32_t start[kMaxRanges];
 };
@@ -103,6 +107,25 @@ __device__ __forceinline__ double canonical_d64(const float *__restrict__ q, con
     return s;
 }
 
+// position of the r-th (0-based) set bit of w; r < popcount(w)
+__device__ __forceinline__ int nth_set_bit(uint64_t w, uint32_t r)
+{
+    int pos = 0;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+        const uint64_t low = (1ull << sh) - 1ull;
+        const uint32_t c = __popcll(w & low);
+        if (r >= c) {
+            r -= c;
+            w >>= sh;
+            pos += sh;
+        } else {
+            w &= low;
+        }
+    }
+    return pos;
+}
+
 __device__ __forceinline__ uint32_t pow2_at_least(uint32_t v)
 {
     uint32_t s = 1;
@@ -125,6 +148,8 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
     uint64_t *const ehi = L.hi[wave];
     uint32_t *const elo = L.lo[wave];
     uint32_t *const hist = L.hist[wave];
+    uint64_t *const cw = L.words[wave];
+    uint32_t *const cb = L.before[wave];
     const uint32_t k = a.k;
     const int32_t d = a.d;
     const uint64_t tbase = a.toff[t] - a.wbase;
@@ -137,20 +162,41 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
         const float *qrow = a.qbase + (uint64_t)qid * a.ldq;
         const uint64_t *row = a.mask + tbase + (uint64_t)r * tl.words;
 
-        // Calls f(valid, hi, lo) once per lane and step while the row's set
-        // bits last: each valid lane holds one neighbour's key.
+        // Calls f(valid, hi, lo) once per lane and step until every set bit
+        // of the row has been visited; each valid lane holds one neighbour's
+        // key.  A 64-word chunk of the mask is staged in LDS with its bit
+        // prefix, and the chunk's set bits are dealt to the lanes in turn,
+        // so dense words do not serialise the distance work on one lane.
         auto for_each = [&](auto &&f) __attribute__((always_inline)) {
             for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
                 const uint32_t w = w0 + lane;
-                uint64_t m = w < tl.used ? row[w] : 0ull;
-                while (__ballot(m != 0) != 0) {
-                    const bool valid = m != 0;
+                const uint64_t m = w < tl.used ? row[w] : 0ull;
+                const uint32_t pc = __popcll(m);
+                uint32_t inc = pc;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t v = __shfl_up(inc, o, 64);
+                    if (lane >= o) inc += v;
+                }
+                const uint32_t total = __shfl(inc, 63, 64);
+                if (total == 0) continue;
+                cw[lane] = m;
+                cb[lane] = inc - pc;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                for (uint32_t j0 = 0; j0 < total; j0 += 64) {
+                    const uint32_t j = j0 + lane;
+                    const bool valid = j < total;
                     uint64_t kh = ~0ull;
                     uint32_t kl = ~0u;
                     if (valid) {
-                        const int bit = __ffsll((unsigned long long)m) - 1;
-                        m &= m - 1;
-                        const uint32_t p = w * 64 + bit;
+                        int lo = 0, hi = 63;  // the last word with cb[word] <= j
+                        while (lo < hi) {
+                            const int mid = (lo + hi + 1) >> 1;
+                            if (cb[mid] <= j) lo = mid;
+                            else hi = mid - 1;
+                        }
+                        const uint32_t p = (w0 + lo) * 64 + nth_set_bit(cw[lo], j - cb[lo]);
                         const int g = range_of(L.pref, nr, p);
                         const uint32_t pid = a.orig[L.start[g] + (p - L.pref[g])];
                         const double s = canonical_d64(qrow, a.x + (uint64_t)pid * a.ld, d);
@@ -159,6 +205,8 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
                     }
                     f(valid, kh, kl);
                 }
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
         };
         // append the valid lanes' keys at ehi/elo[*n ...]
@@ -199,19 +247,12 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
         if (c <= (uint32_t)kCap) {
             for_each([&](bool v, uint64_t kh, uint32_t kl) { append(v, kh, kl, nsel); });
         } else {
-            // radix select of the k-th smallest key, 8 bits per pass
-            uint64_t ph = 0;
-            uint32_t pl = 0, rank = k - 1;
-            for (int p = 0; p < 12; ++p) {
-                for (int i = lane; i < 256; i += 64) hist[i] = 0;
+            // The bucket of hist holding rank (0-based): its index, the count
+            // in the buckets before it, and that count plus its own.
+            auto pick = [&](uint32_t rank, uint32_t &dig, uint32_t &before, uint32_t &through)
+                            __attribute__((always_inline)) {
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                for_each([&](bool v, uint64_t kh, uint32_t kl) {
-                    if (v && key_match(kh, kl, ph, pl, p)) atomicAdd(&hist[key_digit(kh, kl, p)], 1u);
-                });
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                // bucket holding the rank: lane l sums buckets 4l .. 4l+3
                 uint32_t h4[4], s4 = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -227,28 +268,98 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
                 const uint32_t exc = inc - s4;
                 const bool mine = exc <= rank && rank < inc;
                 const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
-                uint32_t dig = 0, before = exc;
+                uint32_t dg = 0, bf = exc, th = exc;
                 if (mine) {
                     uint32_t run = exc;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (rank >= run && rank < run + h4[j]) {
-                            dig = 4 * lane + j;
-                            before = run;
+                            dg = 4 * lane + j;
+                            bf = run;
+                            th = run + h4[j];
                         }
                         run += h4[j];
                     }
                 }
-                dig = __shfl(dig, owner, 64);
-                before = __shfl(before, owner, 64);
-                rank -= before;
-                if (p < 8) ph |= (uint64_t)dig << (56 - 8 * p);
-                else pl |= dig << (24 - 8 * (p - 8));
+                dig = __shfl(dg, owner, 64);
+                before = __shfl(bf, owner, 64);
+                through = __shfl(th, owner, 64);
+            };
+            auto clear_hist = [&]() __attribute__((always_inline)) {
+                for (int i = lane; i < 256; i += 64) hist[i] = 0;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            };
+            bool done = false;
+            // Value buckets: u = 256 D64 / E64 is monotone in D64 and, with
+            // every neighbour at D64 <= E64, within [0, 256]; keys of equal
+            // D64 share a bucket.  Usually one counting pass finds a bucket
+            // prefix holding the k smallest keys and at most kCap keys in
+            // all, and a second pass gathers it; a crowded bucket is split
+            // once more into 256 sub-buckets.
+            if (a.e64 > 0.0 && a.e64 <= 1.0e300) {
+                const double sc = 256.0 / a.e64;
+                auto ubin = [&](uint64_t kh, double &u) __attribute__((always_inline)) {
+                    u = __longlong_as_double((long long)kh) * sc;
+                    return u >= 255.0 ? 255u : (uint32_t)u;
+                };
+                auto sub = [&](double u, uint32_t b0) __attribute__((always_inline)) {
+                    const double v = (u - (double)b0) * 256.0;
+                    return v >= 255.0 ? 255u : (uint32_t)v;
+                };
+                clear_hist();
+                for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                    double u;
+                    if (v) atomicAdd(&hist[ubin(kh, u)], 1u);
+                });
+                uint32_t b0, before0, through0;
+                pick(k - 1, b0, before0, through0);
+                if (through0 <= (uint32_t)kCap) {
+                    for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                        double u;
+                        append(v && ubin(kh, u) <= b0, kh, kl, nsel);
+                    });
+                    done = true;
+                } else {
+                    clear_hist();
+                    for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                        double u;
+                        if (v && ubin(kh, u) == b0) atomicAdd(&hist[sub(u, b0)], 1u);
+                    });
+                    uint32_t b1, before1, through1;
+                    pick(k - 1 - before0, b1, before1, through1);
+                    if (before0 + through1 <= (uint32_t)kCap) {
+                        for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                            double u;
+                            const uint32_t b = ubin(kh, u);
+                            append(v && (b < b0 || (b == b0 && sub(u, b0) <= b1)), kh, kl, nsel);
+                        });
+                        done = true;
+                    }
+                }
             }
-            // the k keys at or below the k-th smallest
-            for_each([&](bool v, uint64_t kh, uint32_t kl) {
-                append(v && !key_less(ph, pl, kh, kl), kh, kl, nsel);
-            });
+            if (!done) {
+                // exact radix select of the k-th smallest 96-bit key, 8 bits
+                // per pass (crowded ties, or an infinite radius)
+                uint64_t ph = 0;
+                uint32_t pl = 0, rank = k - 1;
+                for (int p = 0; p < 12; ++p) {
+                    clear_hist();
+                    for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                        if (v && key_match(kh, kl, ph, pl, p)) atomicAdd(&hist[key_digit(kh, kl, p)], 1u);
+                    });
+                    uint32_t dig, before, through;
+                    pick(rank, dig, before, through);
+                    rank -= before;
+                    if (p < 8) ph |= (uint64_t)dig << (56 - 8 * p);
+                    else pl |= dig << (24 - 8 * (p - 8));
+                }
+                // the k keys at or below the k-th smallest
+                nsel = 0;
+                for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                    append(v && !key_less(ph, pl, kh, kl), kh, kl, nsel);
+                });
+            }
         }
         nsel = min(nsel, (uint32_t)kCap);
         const uint32_t S = pow2_at_least(nsel);

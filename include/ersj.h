@@ -224,7 +224,10 @@ int ersj_host_sync(ersj_index *h);
  *  growth        : > 1: each round multiplies the radius by it; 0: the next
  *                  radius is estimated from the queries still short of k
  *                  neighbours (their counts and, pooled, the maximum-likelihood
- *                  local dimension of Levina and Bickel), factor in [1.01, 4].
+ *                  local dimension of Levina and Bickel, d when nothing can
+ *                  be estimated): enough for 95% of them, held back so that
+ *                  no more than 10% are predicted to exceed 1024 neighbours,
+ *                  factor in [1.02, 4] ([2, 4] after 20 rounds).
  *  opt           : as for ersj_build_index (NULL: defaults).
  *  d_ids         : device [nq][k] uint32, row q = its neighbours' input row
  *                  numbers, nearest first.
@@ -248,6 +251,13 @@ typedef struct ersj_knn_info {
     uint64_t candidates[ERSJ_KNN_MAX_ROUNDS];   /* candidates refined in round r */
     double dim_estimate[ERSJ_KNN_MAX_ROUNDS];   /* local dimension estimated after round r (0: none) */
     uint64_t total_candidates;
+    /* with options.timing (ms, summed over rounds; HIP events on the stream) */
+    double index_ms;                            /* index builds, query binning, counts, plans */
+    double refine_ms;                           /* refinement kernel launches */
+    double recheck_ms;                          /* binary64 re-check and per-row counts */
+    double select_ms;                           /* ranking kernel */
+    int64_t refine_launches;
+    uint64_t computed_candidates;               /* candidates refined minus those the box test decided */
 } ersj_knn_info;
 
 int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_q, int64_t nq,

@@ -128,6 +128,20 @@ def test_more_than_1024_neighbours_and_limits():
     assert dist is None and np.array_equal(ids, oracle.knn(Y, 17)[0])
 
 
+def test_large_rows_through_each_narrowing_level():
+    # 1-D uniform points: about 40,000 neighbours per query, a sixteenth of
+    # them in the first value bucket, so the bucket is split once more
+    rng = np.random.default_rng(74)
+    X = rng.random((200000, 1), dtype=np.float32)
+    check(X, 10, 0.1, rows=np.arange(0, 200000, 4001), label="sub-buckets",
+          kernels=(ersj.REFINE_MFMA,))
+    # 3,000 copies of one point: every bucket holds them all (D64 = 0), so the
+    # exact radix select over (D64, id) decides, ranking the copies by id
+    Y = np.concatenate([rng.random((500, 3), dtype=np.float32),
+                        np.repeat(np.float32([[0.5, 0.5, 0.5]]), 3000, axis=0)])
+    check(Y, 700, 0.2, rows=np.arange(0, 3500, 53), label="tied bucket")
+
+
 def test_bad_arguments_raise():
     x = torch.zeros((10, 3), dtype=torch.float32, device="cuda")
     for k, eps0, growth in ((0, 1.0, 0.0), (11, 1.0, 0.0), (3, 0.0, 0.0), (3, float("nan"), 0.0),
