@@ -754,6 +754,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     unsigned long long *const skipped = hits + 1;
     a.tbox = h->tbox;
     a.skipped = skipped;
+    a.rowcnt = h->rowcnt;
+    a.row_base = h->hrows[b];
     uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -762,6 +764,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
         a.bcount = h->counters;
         a.lcap = lcap;
         HIPC(launch_fill_u64((uint64_t *)h->counters, 0, (int64_t)ncount, s), "clear counters");
+        HIPC(launch_fill_u32(h->rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
         HIPC(mfma ? launch_refine_mfma(a, s) : launch_refine_direct(a, s), "refine kernel");
         h->ms_refine += timer_stop(h, s);
@@ -791,11 +794,10 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
     HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->xq,
-                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, hits, s), "re-check kernel");
+                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, hits, h->rowcnt, h->hrows[b], s),
+         "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
-    HIPC(launch_rowcount(h->tiles, t0, ntiles, h->toff, a.wbase, h->hrows[b], h->mask, h->rowcnt, s),
-         "row count kernel");
     HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
     uint64_t tot = 0, hs[2] = {0, 0};  // pairs; re-check hits, skipped comparisons
     HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");

@@ -162,6 +162,7 @@ hipError_t launch_order_keys(const Tile *tiles, const uint32_t *rpref, const uin
                              uint32_t umax, uint64_t *keys, uint32_t *vals, hipStream_t s);
 
 hipError_t launch_fill_u64(uint64_t *p, uint64_t v, int64_t n, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
 
 // ---- refinement (k_refine.hip, k_refine_mfma.hip) ----
 
@@ -238,6 +239,8 @@ struct RefineArgs {
     float tbox;                   // a query block and a candidate group whose boxes on the three
                                   // grid axes have fp32 gap^2 sum > tbox hold no pair (inf: off)
     unsigned long long *skipped;  // comparisons decided by that box test alone
+    uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
+    uint64_t row_base;            // first query row of the batch
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
 
@@ -287,12 +290,9 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
                               uint64_t *out, hipStream_t s);
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
                           const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
+                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s);
 
-hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
-                           uint64_t wbase, uint64_t row_base, const uint64_t *mask,
-                           uint32_t *cnt, hipStream_t s);
 
 hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
                          uint64_t wbase, uint64_t row_base, const uint64_t *mask,

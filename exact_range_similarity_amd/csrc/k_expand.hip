@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
                                                  const float *__restrict__ xqf, uint64_t nqr,
                                                  int32_t d, const int32_t *__restrict__ pinv,
                                                  double e64, uint64_t *__restrict__ mask,
-                                                 unsigned long long *__restrict__ nin)
+                                                 unsigned long long *__restrict__ nin,
+                                                 uint32_t *__restrict__ rowcnt, uint64_t row_base)
 {
 #pragma clang fp contract(off)
     __shared__ int32_t sp[kMaxDim];
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         }
         if (s <= e64) {
             atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
+            atomicAdd(&rowcnt[e.q - row_base], 1u);
             hit = true;
         }
     }
@@ -87,25 +89,30 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         atomicAdd(nin, (unsigned long long)__popcll(hits));
 }
 
-// Workgroup per row tile of the batch (index order), wave per row.
-__global__ __launch_bounds__(256) void k_rowcount(const Tile *__restrict__ tiles, uint32_t t0,
-                                                  const uint64_t *__restrict__ toff, uint64_t wbase,
-                                                  uint64_t row_base, const uint64_t *__restrict__ mask,
-                                                  uint32_t *__restrict__ cnt)
+// position of the r-th (0-based) set bit of w; r < popcount(w)
+__device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
 {
-    const uint32_t t = t0 + blockIdx.x;
-    const Tile tl = tiles[t];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const uint64_t tbase = toff[t] - wbase;
-    for (uint32_t r = wave; r < tl.nrows; r += 4) {
-        const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
-        uint32_t c = 0;
-        for (uint32_t w = lane; w < tl.used; w += 64) c += __popcll(row[w]);
-        for (int o = 32; o > 0; o >>= 1) c += __shfl_down(c, o, 64);
-        if (lane == 0) cnt[tl.row0 + r - row_base] = c;
+    int pos = 0;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+        const uint64_t low = (1ull << sh) - 1ull;
+        const uint32_t c = __popcll(w & low);
+        if (r >= c) {
+            r -= c;
+            w >>= sh;
+            pos += sh;
+        } else {
+            w &= low;
+        }
     }
+    return pos;
 }
 
+// Workgroup per row tile of the batch, wave per row.  A 64-word chunk of the
+// row's mask is staged in LDS with its bit prefix, and its set bits are dealt
+// to the lanes in turn (lane j takes the chunk's set bits j, j + 64, ...), so
+// the pairs of a dense word are written by 64 lanes at once and each wave's
+// stores are consecutive.
 __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, uint32_t t0,
                                                 const uint64_t *__restrict__ toff, uint64_t wbase,
                                                 uint64_t row_base, const uint64_t *__restrict__ mask,
@@ -119,6 +126,8 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
 {
     __shared__ uint32_t s_pref[kMaxRanges + 1];
     __shared__ uint32_t s_start[kMaxRanges];
+    __shared__ uint64_t s_words[4][64];
+    __shared__ uint32_t s_before[4][64];
     const uint32_t t = t0 + blockIdx.x;
     const Tile tl = tiles[t];
     const uint32_t A = tl.cell;
@@ -128,6 +137,8 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     if (threadIdx.x < kMaxRanges) s_start[threadIdx.x] = rstart[(uint64_t)A * kMaxRanges + threadIdx.x];
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint64_t *const cw = s_words[wave];
+    uint32_t *const cb = s_before[wave];
     const uint64_t tbase = toff[t] - wbase;
     for (uint32_t r = wave; r < tl.nrows; r += 4) {
         const uint32_t q = tl.row0 + r;
@@ -136,26 +147,36 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
         uint64_t out = roff[q - row_base];
         for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
             const uint32_t w = w0 + lane;
-            uint64_t m = w < tl.used ? row[w] : 0ull;
+            const uint64_t m = w < tl.used ? row[w] : 0ull;
             const uint32_t pc = __popcll(m);
             uint32_t inc = pc;
             for (int o = 1; o < 64; o <<= 1) {
                 const uint32_t v = __shfl_up(inc, o, 64);
                 if (lane >= o) inc += v;
             }
-            const uint32_t tot = __shfl(inc, 63, 64);
-            uint64_t pos = out + inc - pc;
-            while (m) {
-                const int bit = __ffsll((unsigned long long)m) - 1;
-                m &= m - 1;
-                const uint32_t p = w * 64 + bit;
+            const uint32_t total = __shfl(inc, 63, 64);
+            if (total == 0) continue;
+            cw[lane] = m;
+            cb[lane] = inc - pc;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            for (uint32_t j = lane; j < total; j += 64) {
+                int lo = 0, hi = 63;  // the last word with cb[word] <= j
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (cb[mid] <= j) lo = mid;
+                    else hi = mid - 1;
+                }
+                const uint32_t p = (w0 + lo) * 64 + nth_bit(cw[lo], j - cb[lo]);
                 const int g = range_of(s_pref, nr, p);
                 const uint32_t x = s_start[g] + (p - s_pref[g]);
+                const uint64_t pos = out + j;
                 pairs[2 * pos] = qid;
                 pairs[2 * pos + 1] = orig[x];
-                ++pos;
             }
-            out += tot;
+            out += total;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
 }
@@ -172,22 +193,13 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
                           const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
                           const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
-                          hipStream_t s)
+                          uint32_t *rowcnt, uint64_t row_base, hipStream_t s)
 {
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
     hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt,
-                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, nin);
-    return hipGetLastError();
-}
-
-hipError_t launch_rowcount(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
-                           uint64_t wbase, uint64_t row_base, const uint64_t *mask, uint32_t *cnt,
-                           hipStream_t s)
-{
-    if (ntiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_rowcount, dim3(ntiles), dim3(256), 0, s, tiles, t0, toff, wbase, row_base,
-                       mask, cnt);
+                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, nin, rowcnt,
+                       row_base);
     return hipGetLastError();
 }
 

@@ -816,6 +816,13 @@ hipError_t launch_order_keys(const Tile *tiles, const uint32_t *rpref, const uin
     return hipGetLastError();
 }
 
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(n)), dim3(kBlock), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_u64(uint64_t *p, uint64_t v, int64_t n, hipStream_t s)
 {
     hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n)), dim3(kBlock), 0, s, p, v, n);

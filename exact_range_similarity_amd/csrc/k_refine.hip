@@ -95,6 +95,7 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     }
     const float tbox = a.tbox;
     uint64_t nskip = 0;
+    uint32_t mycnt = 0;  // bits set in this lane's mask words (lane = query k * 4 + word j)
 
     for (uint32_t c = c_begin; c < c_end; c += kChunk) {
         uint32_t xi[kCW];
@@ -194,11 +195,19 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
         }
         if (lane < kQW * kCW) {
             const int k = lane / kCW, j = lane % kCW;
-            if ((uint32_t)k < nq && w0 + j < tl.words)
+            if ((uint32_t)k < nq && w0 + j < tl.words) {
                 mask[mbase + (uint64_t)k * tl.words + w0 + j] = myword;
+                mycnt += __popcll(myword);
+            }
         }
     }
     if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
+    // the rows' neighbour counts (the binary64 re-check adds the band's):
+    // the kCW lanes of a query sum their words' counts
+    mycnt += __shfl_down(mycnt, 2, kCW);
+    mycnt += __shfl_down(mycnt, 1, kCW);
+    if (lane < kQW * kCW && lane % kCW == 0 && (uint32_t)(lane / kCW) < nq && mycnt != 0)
+        atomicAdd(&a.rowcnt[tl.row0 + r_begin + kq0 + (uint32_t)(lane / kCW) - a.row_base], mycnt);
 }
 
 }  // namespace

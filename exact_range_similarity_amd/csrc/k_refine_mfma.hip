@@ -101,6 +101,7 @@ struct Lds {
     float *nxp;         // [kNB][kSlab][SC] partial candidate norms of a step
     uint32_t *xi;       // [kNB][SC] candidate point index of a step
     float *qin, *qout;  // [QR]
+    uint32_t *rcnt;     // [QR] mask bits set per row by this work item
     uint64_t *words;    // [QR][8] mask words of the current 512-candidate group
     float4 *cbox;       // [kNB][NCG][2] lo, hi of each candidate group of a step
     uint32_t *pref, *start;
@@ -111,7 +112,7 @@ size_t lds_bytes(int nbs)
 {
     using G = Geometry<QB>;
     return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
-           (size_t)kNB * G::SC * 4 + (size_t)2 * G::QR * 4 + (size_t)G::QR * 8 * 8 +
+           (size_t)kNB * G::SC * 4 + (size_t)3 * G::QR * 4 + (size_t)G::QR * 8 * 8 +
            (size_t)kNB * G::NCG * 2 * 16 + (2 * kMaxRanges + 1) * 4;
 }
 
@@ -127,7 +128,8 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     L.xi = (uint32_t *)(L.nxp + kNB * kSlab * G::SC);
     L.qin = (float *)(L.xi + kNB * G::SC);
     L.qout = L.qin + G::QR;
-    L.words = (uint64_t *)(L.qout + G::QR);
+    L.rcnt = (uint32_t *)(L.qout + G::QR);
+    L.words = (uint64_t *)(L.rcnt + G::QR);
     L.cbox = (float4 *)(L.words + G::QR * 8);
     L.pref = (uint32_t *)(L.cbox + kNB * G::NCG * 2);
     L.start = L.pref + (kMaxRanges + 1);
@@ -197,6 +199,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         const bool live = (uint32_t)i < nrows;
         L.qin[i] = live ? a.tlo - a.kp * nq : -INFINITY;
         L.qout[i] = live ? a.thi - a.km * nq : -INFINITY;
+        L.rcnt[i] = 0;
     }
     __syncthreads();
 
@@ -424,7 +427,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             const int row = e >> 3, j = e & 7;
             const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
             const uint32_t w = c0 >> 6;
-            if ((uint32_t)row < nrows && w < W && c0 < c_end) mask[mbase + (uint64_t)row * W + w] = sw[e];
+            if ((uint32_t)row < nrows && w < W && c0 < c_end) {
+                mask[mbase + (uint64_t)row * W + w] = sw[e];
+                const uint32_t pc = __popcll(sw[e]);
+                if (pc != 0) atomicAdd(&L.rcnt[row], pc);
+            }
         }
     };
     auto mfma_slab = [&](const float4 *xb, int sl, bool fresh) {
@@ -575,6 +582,10 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     __syncthreads();
     if (pend_group >= 0) flush((uint32_t)pend_group);
     if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
+    // the rows' neighbour counts (the binary64 re-check adds the band's)
+    __syncthreads();
+    for (int i = tid; i < (int)nrows; i += 256)
+        if (L.rcnt[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], L.rcnt[i]);
 }
 
 }  // namespace
