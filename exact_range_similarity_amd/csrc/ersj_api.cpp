@@ -99,6 +99,8 @@ struct ersj_index {
     Tile *tiles = nullptr;
     uint64_t *toff = nullptr, *coff = nullptr;
     uint64_t total_cand = 0, total_words = 0;
+    float4 *cbox = nullptr;           // block box test: box of each 64-candidate chunk of each cell's list
+    uint64_t *chunk_base = nullptr;   // first chunk of each cell
     // plan
     int32_t nbatch = 0;
     std::vector<uint32_t> hb;
@@ -332,6 +334,8 @@ void release_count(ersj_index *h)
     dfree(h, h->tiles);
     dfree(h, h->toff);
     dfree(h, h->coff);
+    dfree(h, h->cbox);
+    dfree(h, h->chunk_base);
 }
 
 void release_plan(ersj_index *h)
@@ -593,6 +597,20 @@ int do_count(ersj_index *h, hipStream_t s)
     HIPC(scan_u64(cands, h->coff, (int64_t)T, stmp, s), "candidate scan");
     HIPC(hipMemcpyAsync(&h->total_words, h->toff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(&h->total_cand, h->coff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
+    if (h->kernel_used == ERSJ_REFINE_MFMA && std::isfinite(h->tbox)) {
+        // boxes of each cell list's 64-candidate chunks for the block box test
+        uint32_t *ccnt = nullptr;
+        TRY(tmp.get(&ccnt, (size_t)M, "chunk boxes"));
+        TRY(dalloc(h, &h->chunk_base, (size_t)M + 1, "chunk boxes"));
+        HIPC(launch_chunk_counts(h->rpref, h->nrng, M, ccnt, s), "chunk count kernel");
+        HIPC(scan_u32(ccnt, h->chunk_base, M, stmp, s), "chunk scan");
+        uint64_t nchunks = 0;
+        HIPC(hipMemcpyAsync(&nchunks, h->chunk_base + M, sizeof nchunks, hipMemcpyDeviceToHost, s), "copy");
+        TRY(sync(s, "chunk count"));
+        TRY(dalloc(h, &h->cbox, (size_t)nchunks * 2 + 2, "chunk boxes"));
+        HIPC(launch_chunk_boxes(h->chunk_base, M, nchunks, h->rstart, h->rpref, h->nrng, h->xs, h->cbox, s),
+             "chunk box kernel");
+    }
     TRY(sync(s, "count pass"));
     return ERSJ_OK;
 }
@@ -756,6 +774,9 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.skipped = skipped;
     a.rowcnt = h->rowcnt;
     a.row_base = h->hrows[b];
+    a.cbox = h->cbox;
+    a.chunk_base = h->chunk_base;
+    if (mfma && !h->cbox) a.tbox = INFINITY;  // no chunk boxes: no block test
     uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {

@@ -143,6 +143,11 @@ struct CellSet {
     const uint32_t *lo_bits, *hi_bits;
     int64_t M;
 };
+hipError_t launch_chunk_counts(const uint32_t *rpref, const uint32_t *nrng, int64_t M, uint32_t *cnt,
+                               hipStream_t s);
+hipError_t launch_chunk_boxes(const uint64_t *base, int64_t M, uint64_t nchunks, const uint32_t *rstart,
+                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, float4 *cbox,
+                              hipStream_t s);
 hipError_t launch_stencil(const CellSet &home, const CellSet &target, const GridParams &gp,
                           double prune_e2, uint32_t *rstart, uint32_t *rpref, uint32_t *nrng,
                           uint32_t *tiles_per_cell, unsigned int *umax, hipStream_t s);
@@ -238,6 +243,9 @@ struct RefineArgs {
     uint64_t lcap;                // entries per sub-list
     float tbox;                   // a query block and a candidate group whose boxes on the three
                                   // grid axes have fp32 gap^2 sum > tbox hold no pair (inf: off)
+    const float4 *cbox;           // MFMA kernel, tbox finite: lo, hi on the grid axes of each
+                                  // 64-candidate chunk of each cell's candidate list
+    const uint64_t *chunk_base;   // first chunk of each cell
     unsigned long long *skipped;  // comparisons decided by that box test alone
     uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
     uint64_t row_base;            // first query row of the batch

@@ -559,6 +559,55 @@ __global__ __launch_bounds__(kBlock) void k_stencil(CellSet home, CellSet target
 }
 
 // ----------------------------------------------------------------- tiles --
+// ------------------------------------------------------- chunk boxes --
+// Chunks of 64 consecutive positions of each cell's candidate list: counts
+// per cell, then the box of each chunk's points on the grid axes (block 0
+// of the layout), for the refinement's block box test.
+__global__ __launch_bounds__(kBlock) void k_chunk_counts(const uint32_t *__restrict__ rpref,
+                                                         const uint32_t *__restrict__ nrng, int64_t M,
+                                                         uint32_t *__restrict__ cnt)
+{
+    const int64_t A = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (A >= M) return;
+    const uint32_t U = rpref[(uint64_t)A * (kMaxRanges + 1) + nrng[A]];
+    cnt[A] = (U + 63) / 64;
+}
+
+// Wave per chunk: the chunk's cell A is the last with base[A] <= chunk.
+__global__ __launch_bounds__(256) void k_chunk_boxes(const uint64_t *__restrict__ base, int64_t M,
+                                                     uint64_t nchunks, const uint32_t *__restrict__ rstart,
+                                                     const uint32_t *__restrict__ rpref,
+                                                     const uint32_t *__restrict__ nrng,
+                                                     const float4 *__restrict__ xs, float4 *__restrict__ cbox)
+{
+    const uint64_t ch = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (ch >= nchunks) return;  // whole wave
+    int64_t lo = 0, hi = M - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (base[mid] <= ch) lo = mid;
+        else hi = mid - 1;
+    }
+    const int64_t A = lo;
+    const uint32_t *pref = rpref + (uint64_t)A * (kMaxRanges + 1);
+    const uint32_t nr = nrng[A];
+    const uint32_t U = pref[nr];
+    const uint32_t p = (uint32_t)(ch - base[A]) * 64 + (uint32_t)lane;
+    float4 blo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), bhi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
+    if (p < U) {
+        const int g = range_of(pref, nr, p);
+        const float4 v = xs[rstart[(uint64_t)A * kMaxRanges + g] + (p - pref[g])];
+        blo = v;
+        bhi = v;
+    }
+    wave_box(blo, bhi);
+    if (lane == 0) {
+        cbox[2 * ch] = blo;
+        cbox[2 * ch + 1] = bhi;
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void k_tiles(const uint64_t *__restrict__ tile_base, int64_t M,
                                                   int64_t T, const uint32_t *__restrict__ cell_start,
                                                   const uint32_t *__restrict__ rpref,
@@ -774,6 +823,26 @@ hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, in
     const int64_t chunks = (n + kAabbChunk - 1) / kAabbChunk;
     hipLaunchKernelGGL(k_cell_aabb, dim3(grid_for(chunks)), dim3(kBlock), 0, s, xs, cid, n, lo_bits,
                        hi_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_counts(const uint32_t *rpref, const uint32_t *nrng, int64_t M, uint32_t *cnt,
+                               hipStream_t s)
+{
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_chunk_counts, dim3(grid_for(M)), dim3(kBlock), 0, s, rpref, nrng, M, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_boxes(const uint64_t *base, int64_t M, uint64_t nchunks, const uint32_t *rstart,
+                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, float4 *cbox,
+                              hipStream_t s)
+{
+    if (nchunks == 0) return hipSuccess;
+    const uint64_t blocks = (nchunks + 3) / 4;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_chunk_boxes, dim3((unsigned)blocks), dim3(256), 0, s, base, M, nchunks, rstart, rpref,
+                       nrng, xs, cbox);
     return hipGetLastError();
 }
 

@@ -38,9 +38,11 @@
 // block and a 64-candidate group are compact on the three grid axes (the
 // first three dimensions of the layout).  When the gap between their
 // bounding boxes there already exceeds eps (squared gaps summed in fp32 >
-// tbox, a bound that covers the rounding), the wave skips the group's
-// MFMAs and classification and writes zero mask words.  The candidate box
-// is reduced by the loading wave while it stages the first slab of a step.
+// tbox, a bound that covers the rounding), the pair of them holds no
+// neighbour.  Each wave tests all its steps against the candidate groups'
+// boxes (precomputed per 64-candidate chunk after the count pass) before
+// the loop: steps that every wave passes are dropped (no loads, no staging,
+// zero mask words), and in the others a wave skips its own far steps.
 //
 // A step's classification follows its last slab's MFMAs; the waves that
 // share a SIMD overlap one's classification with another's matrix work.
@@ -60,6 +62,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
 constexpr int kNB = 2;            // step buffers for norms / candidate ids
 constexpr int kGroupCands = 512;  // candidates per mask-word flush
+constexpr int kMaxSteps = 128;    // steps of a segment the block box test covers (8192 / 64)
 
 // v_writelane_b32 through its LLVM intrinsic (clang has no builtin for it):
 // writes a wave-uniform 32-bit value into one lane of a VGPR.  The compiler
@@ -103,7 +106,8 @@ struct Lds {
     float *qin, *qout;  // [QR]
     uint32_t *rcnt;     // [QR] mask bits set per row by this work item
     uint64_t *words;    // [QR][8] mask words of the current 512-candidate group
-    float4 *cbox;       // [kNB][NCG][2] lo, hi of each candidate group of a step
+    uint32_t *far;      // [4 waves][4] steps (bit s) each wave skips
+    uint32_t *live;     // [kMaxSteps] steps some wave computes, ascending
     uint32_t *pref, *start;
 };
 
@@ -113,7 +117,7 @@ size_t lds_bytes(int nbs)
     using G = Geometry<QB>;
     return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
            (size_t)kNB * G::SC * 4 + (size_t)3 * G::QR * 4 + (size_t)G::QR * 8 * 8 +
-           (size_t)kNB * G::NCG * 2 * 16 + (2 * kMaxRanges + 1) * 4;
+           (size_t)(16 + kMaxSteps) * 4 + (2 * kMaxRanges + 1) * 4;
 }
 
 template <int QB>
@@ -130,8 +134,9 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     L.qout = L.qin + G::QR;
     L.rcnt = (uint32_t *)(L.qout + G::QR);
     L.words = (uint64_t *)(L.rcnt + G::QR);
-    L.cbox = (float4 *)(L.words + G::QR * 8);
-    L.pref = (uint32_t *)(L.cbox + kNB * G::NCG * 2);
+    L.far = (uint32_t *)(L.words + G::QR * 8);
+    L.live = L.far + 16;
+    L.pref = L.live + kMaxSteps;
     L.start = L.pref + (kMaxRanges + 1);
     return L;
 }
@@ -201,6 +206,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         L.qout[i] = live ? a.thi - a.km * nq : -INFINITY;
         L.rcnt[i] = 0;
     }
+    for (int e = tid; e < G::QR * 8; e += 256) L.words[e] = 0ull;
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -229,7 +235,66 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const float kp = a.kp, km = a.km;
     const uint64_t bcap = a.lcap;
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
-    const uint32_t K = nsteps * (uint32_t)nslab;
+    const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
+    const float tbox = a.tbox;
+
+    // Block box test of every step up front: the wave's query box against
+    // its candidate group's box (precomputed per 64-candidate chunk of the
+    // cell's list).  Steps that every wave skips are dropped from the loop
+    // (no loads, no staging); the wave skips its own far steps among the
+    // rest.  Segments longer than kMaxSteps steps are not tested.
+    const bool tested = tbox < INFINITY && nsteps <= (uint32_t)kMaxSteps;
+    uint32_t far0 = 0, far1 = 0, far2 = 0, far3 = 0;
+    uint64_t nskip = 0;  // comparisons this wave skipped
+    if (tested) {
+        const uint64_t cb0 = a.chunk_base[A] + (c_begin >> 6) + (uint32_t)cg;
+        for (uint32_t st = 0; st < nsteps; ++st) {
+            const uint32_t gs = c_begin + st * G::SC + cg * 64;
+            uint32_t bit = 1;
+            if (active && gs < c_end) {
+                const float4 *cb = a.cbox + 2 * (cb0 + st * (uint32_t)(G::SC / 64));
+                bit = __builtin_amdgcn_readfirstlane((int)(box_gap2(qlo, qhi, cb[0], cb[1]) > tbox));
+            }
+            if (bit) {
+                const uint32_t m = 1u << (st & 31);
+                if (st < 32) far0 |= m;
+                else if (st < 64) far1 |= m;
+                else if (st < 96) far2 |= m;
+                else far3 |= m;
+                if (gs < c_end) nskip += (uint64_t)qrows * min(64u, c_end - gs);
+            }
+        }
+    }
+    auto wave_far = [&](uint32_t st) __attribute__((always_inline)) {
+        const uint32_t w = st < 32 ? far0 : st < 64 ? far1 : st < 96 ? far2 : far3;
+        return ((w >> (st & 31)) & 1u) != 0;
+    };
+    uint32_t nlive = nsteps;
+    if (tested) {
+        if (lane == 0) {
+            L.far[wave * 4 + 0] = far0;
+            L.far[wave * 4 + 1] = far1;
+            L.far[wave * 4 + 2] = far2;
+            L.far[wave * 4 + 3] = far3;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t c = 0;
+            for (uint32_t st = 0; st < nsteps; ++st) {
+                const uint32_t i = st >> 5, m = 1u << (st & 31);
+                if (!(L.far[i] & L.far[4 + i] & L.far[8 + i] & L.far[12 + i] & m)) L.live[c++] = st;
+            }
+            L.far[0] = c;  // read back below, after the barrier
+        }
+        __syncthreads();
+        nlive = __builtin_amdgcn_readfirstlane(L.far[0]);
+    }
+    // step of live index i (i = nlive: past the segment, loads nothing new)
+    auto live_step = [&](uint32_t i) __attribute__((always_inline)) {
+        if (i >= nlive) return nsteps;
+        return tested ? L.live[i] : i;
+    };
+    const uint32_t K = nlive * (uint32_t)nslab;
 
     // loader: element m of this thread is (block j = e / SC, candidate c =
     // e % SC), e = tid + 256 m.  Its candidate position advances by SC per
@@ -291,14 +356,14 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         if (++lsl == nslab) {
             lsl = 0;
             ++lstep;
-            set_cands(lstep);
+            set_cands(live_step(lstep));
             restart_offsets();
         } else {
 #pragma unroll
             for (int m = 0; m < G::EPT; ++m) loff[m] += slab_stride;
         }
     };
-    set_cands(0);
+    set_cands(live_step(0));
     restart_offsets();
 #pragma unroll
     for (int a2 = 0; a2 < kAhead; ++a2) {
@@ -309,25 +374,23 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
 #pragma unroll
     for (int m = 0; m < G::EPT; ++m) nxp[m] = 0.f;
     floatx16 accC[2];
-    int pend_group = -1;
-    bool far = false;       // this wave skips the current step
-    uint64_t nskip = 0;     // comparisons this wave skipped
-    const float tbox = a.tbox;
-    const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
+    int pend_group = -1;            // group whose words wait in L.words
+    uint32_t pend_next = 0;         // next group with a live step (groups between are zero)
+    const uint32_t ngroups = (nsteps + G::SPG - 1) / G::SPG;
 
     // classification of step s (accumulators in acc): mask words and band pairs
-    auto epilogue = [&](uint32_t s, const floatx16 *acc) {
+    auto epilogue = [&](uint32_t s, uint32_t bi, const floatx16 *acc) {
         const uint32_t cw = c_begin + s * G::SC + cg * 64;
         float xin[2], xout[2];
         uint32_t xid[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int cl = cg * 64 + 32 * tt + col;
-            const float *np = L.nxp + (s % kNB) * (kSlab * G::SC);
+            const float *np = L.nxp + (bi % kNB) * (kSlab * G::SC);
             float nxt = np[cl];
 #pragma unroll
             for (int j = 1; j < kSlab; ++j) nxt += np[j * G::SC + cl];
-            xid[tt] = L.xi[(s % kNB) * G::SC + cl];
+            xid[tt] = L.xi[(bi % kNB) * G::SC + cl];
             // candidates past the segment end never classify: a NaN operand
             // makes both comparisons false (an infinity would not: with an
             // infinite eps, inf <= inf holds)
@@ -422,7 +485,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
     };
     auto flush = [&](uint32_t grp) {
-        const uint64_t *sw = L.words;
+        uint64_t *sw = L.words;
         for (int e = tid; e < G::QR * 8; e += 256) {
             const int row = e >> 3, j = e & 7;
             const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
@@ -431,6 +494,18 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 mask[mbase + (uint64_t)row * W + w] = sw[e];
                 const uint32_t pc = __popcll(sw[e]);
                 if (pc != 0) atomicAdd(&L.rcnt[row], pc);
+            }
+            sw[e] = 0ull;  // words of steps the next group skips stay zero
+        }
+    };
+    // groups without a live step: zero words
+    auto zero_groups = [&](uint32_t g0, uint32_t g1) {
+        for (uint32_t g = g0; g < g1; ++g) {
+            for (int e = tid; e < G::QR * 8; e += 256) {
+                const int row = e >> 3, j = e & 7;
+                const uint32_t c0 = c_begin + g * kGroupCands + 64 * j;
+                const uint32_t w = c0 >> 6;
+                if ((uint32_t)row < nrows && w < W && c0 < c_end) mask[mbase + (uint64_t)row * W + w] = 0ull;
             }
         }
     };
@@ -464,7 +539,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     // slab), flush a finished mask-word group and issue the loads kAhead
     // slabs ahead.  Returns the staged buffer.  With NS > 0 the slab index is
     // a constant and every per-slab condition folds.
-    auto stage = [&](uint32_t k, uint32_t step, auto SLC) __attribute__((always_inline)) {
+    auto stage = [&](uint32_t k, uint32_t bi, auto SLC) __attribute__((always_inline)) {
         const int sl = SLC;
         float4 *xb = L.x + (k & 1) * (kSlab * G::SC);
         // stage the slab: centre on r, accumulate partial norms
@@ -481,39 +556,22 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             nxp[m] = s2;
             xb[e] = c4;
         }
-        if (sl == 0 && (tid >> 6) < G::NCG) {
-            // element 0 of the first NCG waves is block 0 (the grid axes) of
-            // candidate tid of the step: reduce each group's box
-            const bool valid = c_begin + step * G::SC + (uint32_t)tid < c_end;
-            float4 lo = valid ? ld[0][0] : make_float4(INFINITY, INFINITY, INFINITY, 0.f);
-            float4 hi = valid ? ld[0][0] : make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
-            wave_box(lo, hi);
-            if ((tid & 63) == 0) {
-                float4 *cb = L.cbox + ((step % kNB) * G::NCG + (tid >> 6)) * 2;
-                cb[0] = lo;
-                cb[1] = hi;
-            }
-        }
         if (sl == nslab - 1) {
 #pragma unroll
             for (int m = 0; m < G::EPT; ++m) {
                 const int e = tid + 256 * m;
-                L.nxp[(step % kNB) * (kSlab * G::SC) + e] = nxp[m];
-                if (e < G::SC) L.xi[(step % kNB) * G::SC + e] = ldx[0][m];
+                L.nxp[(bi % kNB) * (kSlab * G::SC) + e] = nxp[m];
+                if (e < G::SC) L.xi[(bi % kNB) * G::SC + e] = ldx[0][m];
                 nxp[m] = 0.f;
             }
         }
         __syncthreads();
-        if (sl == 0) {
-            const float4 *cb = L.cbox + ((step % kNB) * G::NCG + cg) * 2;
-            const float g2 = box_gap2(qlo, qhi, cb[0], cb[1]);
-            far = !active || __builtin_amdgcn_readfirstlane((int)(g2 > tbox)) != 0;
-        }
         if (pend_group >= 0) {
             // the group buffer is reused by the next group: with one slab
             // per step this step's classification follows in this same
             // iteration, so wait for the whole flush first
             flush((uint32_t)pend_group);
+            zero_groups((uint32_t)pend_group + 1, pend_next);
             pend_group = -1;
             if (nslab == 1) __syncthreads();
         }
@@ -530,7 +588,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 // the slab loaded now and the one after it are known here
                 load_slab((sl + kAhead) % NS, ld[kAhead - 1], ldx[kAhead - 1]);
                 if ((sl + kAhead + 1) % NS == 0) {
-                    set_cands(step + (uint32_t)((sl + kAhead + 1) / NS));
+                    set_cands(live_step(bi + (uint32_t)((sl + kAhead + 1) / NS)));
                     restart_offsets();
                 } else {
 #pragma unroll
@@ -543,44 +601,49 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
         return xb;
     };
-    // a skipped (or inactive) wave's step: zero mask words, no band pairs
-    auto skip_step = [&](uint32_t step) __attribute__((always_inline)) {
-        const uint32_t cw = c_begin + step * G::SC + cg * 64;
-        nskip += (uint64_t)qrows * (cw < c_end ? min(64u, c_end - cw) : 0u);
-        if (lane < 32) L.words[(qb * 32 + lane) * 8 + (step % G::SPG) * G::NCG + cg] = 0ull;
-    };
-    // Each step branches once on the block test, so the accumulators are
-    // never live across steps; both branches stage the same slabs and meet
-    // the same barriers.
-    for (uint32_t step = 0; step < nsteps; ++step) {
-        const uint32_t k0 = step * (uint32_t)nslab;
-        float4 *xb0 = stage(k0, step, std::integral_constant<int, 0>{});
-        if (!far) {
+    // groups before the first live step hold no neighbour
+    zero_groups(0, nlive > 0 ? live_step(0) / G::SPG : ngroups);
+    // Each live step branches once on the wave's own test, so the
+    // accumulators are never live across steps; both branches stage the same
+    // slabs and meet the same barriers.
+    for (uint32_t bi = 0; bi < nlive; ++bi) {
+        const uint32_t step = __builtin_amdgcn_readfirstlane(live_step(bi));
+        const uint32_t k0 = bi * (uint32_t)nslab;
+        float4 *xb0 = stage(k0, bi, std::integral_constant<int, 0>{});
+        if (active && !wave_far(step)) {
             mfma_slab(xb0, 0, true);
             if constexpr (NS > 0) {
                 static_for(std::make_integer_sequence<int, NS - 1>{}, [&](auto S) __attribute__((always_inline)) {
                     constexpr int sl = decltype(S)::value + 1;
-                    mfma_slab(stage(k0 + sl, step, std::integral_constant<int, sl>{}), sl, false);
+                    mfma_slab(stage(k0 + sl, bi, std::integral_constant<int, sl>{}), sl, false);
                 });
             } else {
-                for (int sl = 1; sl < nslab; ++sl) mfma_slab(stage(k0 + sl, step, sl), sl, false);
+                for (int sl = 1; sl < nslab; ++sl) mfma_slab(stage(k0 + sl, bi, sl), sl, false);
             }
-            epilogue(step, accC);
+            epilogue(step, bi, accC);
         } else {
             if constexpr (NS > 0) {
                 static_for(std::make_integer_sequence<int, NS - 1>{}, [&](auto S) __attribute__((always_inline)) {
                     constexpr int sl = decltype(S)::value + 1;
-                    stage(k0 + sl, step, std::integral_constant<int, sl>{});
+                    stage(k0 + sl, bi, std::integral_constant<int, sl>{});
                 });
             } else {
-                for (int sl = 1; sl < nslab; ++sl) stage(k0 + sl, step, sl);
+                for (int sl = 1; sl < nslab; ++sl) stage(k0 + sl, bi, sl);
             }
-            skip_step(step);
         }
-        if (step % G::SPG == G::SPG - 1 || step + 1 == nsteps) pend_group = (int)(step / G::SPG);
+        // flush the group after its last live step (at the next barrier)
+        const uint32_t g = step / G::SPG;
+        const uint32_t gn = bi + 1 < nlive ? live_step(bi + 1) / G::SPG : ngroups;
+        if (gn != g) {
+            pend_group = (int)g;
+            pend_next = gn;
+        }
     }
     __syncthreads();
-    if (pend_group >= 0) flush((uint32_t)pend_group);
+    if (pend_group >= 0) {
+        flush((uint32_t)pend_group);
+        zero_groups((uint32_t)pend_group + 1, pend_next);
+    }
     if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
     // the rows' neighbour counts (the binary64 re-check adds the band's)
     __syncthreads();
