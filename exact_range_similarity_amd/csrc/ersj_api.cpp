@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -157,18 +158,111 @@ int hip_fail(hipError_t e, const char *what)
         if (r__ != ERSJ_OK) return r__; \
     } while (0)
 
+// Device memory pool, per device, shared by all handles of the process.
+// Released blocks are kept and handed out again for a request of the same
+// rounded size, which spares a repeated join the hipMalloc and the
+// device-synchronising hipFree of every buffer.  A released block may still
+// be in use by work enqueued before its release, so it is reused only after a
+// device-wide synchronisation (the guarantee hipFree gave).  When hipMalloc
+// fails the pool frees what it holds and tries again; it keeps at most half
+// of the device's memory.
+struct PoolBlock {
+    void *p;
+    size_t bytes;
+    bool ready;  // released before the last device synchronisation
+};
+struct DevicePool {
+    std::vector<PoolBlock> blocks;
+    size_t cached = 0, cap = 0;
+};
+std::mutex g_pool_mu;
+std::map<int, DevicePool> g_pools;
+
+size_t pool_round(size_t b)
+{
+    const size_t big = (size_t)2 << 20;
+    return b <= ((size_t)1 << 20) ? (b + 255) & ~(size_t)255 : (b + big - 1) & ~(big - 1);
+}
+
+DevicePool &pool_of(int dev)
+{
+    DevicePool &pl = g_pools[dev];
+    if (pl.cap == 0) {
+        size_t fr = 0, tot = 0;
+        pl.cap = hipMemGetInfo(&fr, &tot) == hipSuccess ? tot / 2 : ((size_t)1 << 30);
+        (void)hipGetLastError();
+    }
+    return pl;
+}
+
+hipError_t pool_get(int dev, size_t bytes, void **out)
+{
+    {
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        DevicePool &pl = pool_of(dev);
+        for (int pass = 0; pass < 2; ++pass) {
+            for (size_t i = 0; i < pl.blocks.size(); ++i) {
+                if (pl.blocks[i].bytes == bytes && pl.blocks[i].ready) {
+                    *out = pl.blocks[i].p;
+                    pl.cached -= bytes;
+                    pl.blocks.erase(pl.blocks.begin() + (long)i);
+                    return hipSuccess;
+                }
+            }
+            bool pending = false;
+            for (const PoolBlock &b : pl.blocks) pending |= b.bytes == bytes && !b.ready;
+            if (!pending) break;
+            // a block of this size awaits the work enqueued before its release
+            if (hipDeviceSynchronize() != hipSuccess) break;
+            for (PoolBlock &b : pl.blocks) b.ready = true;
+        }
+    }
+    hipError_t e = hipMalloc(out, bytes);
+    if (e == hipSuccess) return e;
+    (void)hipGetLastError();
+    {
+        std::lock_guard<std::mutex> lk(g_pool_mu);
+        DevicePool &pl = pool_of(dev);
+        if (pl.blocks.empty()) return e;
+        (void)hipDeviceSynchronize();
+        for (const PoolBlock &b : pl.blocks) (void)hipFree(b.p);
+        pl.blocks.clear();
+        pl.cached = 0;
+    }
+    return hipMalloc(out, bytes);
+}
+
+void pool_put(int dev, void *p, size_t bytes)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    DevicePool &pl = pool_of(dev);
+    if (pl.cached + bytes > pl.cap) {
+        (void)hipFree(p);
+        return;
+    }
+    pl.blocks.push_back(PoolBlock{p, bytes, false});
+    pl.cached += bytes;
+}
+
+// bytes the pool holds for the device (free for this library's reuse)
+size_t pool_cached(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    return pool_of(dev).cached;
+}
+
 template <typename T>
 int dalloc(ersj_index *h, T **p, size_t count, const char *what)
 {
     size_t bytes = count * sizeof(T);
     if (bytes == 0) bytes = 8;
-    bytes = (bytes + 255) & ~(size_t)255;
+    bytes = pool_round(bytes);
     if (h->opt.max_device_bytes && h->bytes + bytes > h->opt.max_device_bytes)
         return fail(ERSJ_ERR_OOM, "%s: %zu bytes would exceed max_device_bytes (%llu in use, cap %llu)",
                     what, bytes, (unsigned long long)h->bytes,
                     (unsigned long long)h->opt.max_device_bytes);
     void *q = nullptr;
-    hipError_t e = hipMalloc(&q, bytes);
+    hipError_t e = pool_get(h->device, bytes, &q);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(ERSJ_ERR_OOM, "%s: hipMalloc(%zu) failed: %s", what, bytes, hipGetErrorString(e));
@@ -186,9 +280,11 @@ void dfree(ersj_index *h, T *&p)
     auto it = h->live.find((void *)p);
     if (it != h->live.end()) {
         h->bytes -= it->second;
+        pool_put(h->device, (void *)p, it->second);
         h->live.erase(it);
+    } else {
+        (void)hipFree((void *)p);
     }
-    (void)hipFree((void *)p);
     p = nullptr;
 }
 
@@ -621,6 +717,7 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
     if (budget_bytes == 0) {
         size_t fr = 0, tot = 0;
         HIPC(hipMemGetInfo(&fr, &tot), "hipMemGetInfo");
+        fr += pool_cached(h->device);  // blocks this library keeps for reuse
         const uint64_t extra = (uint64_t)h->nq * 24 + (uint64_t)(1 << 22) * sizeof(Boundary);
         uint64_t b = (uint64_t)fr / 4 * 3;
         budget_bytes = b > extra ? b - extra : 8;
@@ -964,7 +1061,7 @@ void ersj_free(ersj_index *h)
             if (h->copied[k]) (void)hipEventDestroy(h->copied[k]);
         }
     }
-    for (auto &kv : h->live) (void)hipFree(kv.first);
+    for (auto &kv : h->live) pool_put(h->device, kv.first, kv.second);
     h->live.clear();
     for (hipEvent_t &e : h->ev)
         if (e) (void)hipEventDestroy(e);
