@@ -110,6 +110,7 @@ struct ersj_index {
     uint32_t *order = nullptr;
     // fill
     uint64_t *mask = nullptr;
+    uint8_t *gflag = nullptr;  // per 4 mask words (256 candidates): any bit set
     uint64_t mask_cap = 0;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;
@@ -726,7 +727,8 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
             budget_bytes = std::min<uint64_t>(budget_bytes, room / 4 * 3);
         }
     }
-    const uint64_t budget_words = budget_bytes / 8;
+    // a mask word costs 8 bytes plus a quarter byte of unit flags
+    const uint64_t budget_words = budget_bytes / 33 * 4;
     if (budget_words == 0) return fail(ERSJ_ERR_BUDGET, "budget of %llu bytes holds no mask word",
                                        (unsigned long long)budget_bytes);
     Scratch tmp(h);
@@ -803,8 +805,10 @@ int ensure_fill_buffers(ersj_index *h)
 {
     if (h->mask_cap < h->maxw) {
         dfree(h, h->mask);
+        dfree(h, h->gflag);
         h->mask_cap = 0;
         TRY(dalloc(h, &h->mask, (size_t)h->maxw, "result mask"));
+        TRY(dalloc(h, &h->gflag, (size_t)(h->maxw / 4 + 64), "mask unit flags"));
         h->mask_cap = h->maxw;
     }
     if (h->rows_cap < h->maxrows) {
@@ -873,6 +877,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.row_base = h->hrows[b];
     a.cbox = h->cbox;
     a.chunk_base = h->chunk_base;
+    a.gflag = h->gflag;
     if (mfma && !h->cbox) a.tbox = INFINITY;  // no chunk boxes: no block test
     uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
@@ -912,7 +917,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
     HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->xq,
-                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, hits, h->rowcnt, h->hrows[b], s),
+                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, h->gflag, hits, h->rowcnt,
+                        h->hrows[b], s),
          "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
@@ -938,7 +944,7 @@ int expand_batch(ersj_index *h, int32_t batch, uint32_t *d_pairs, hipStream_t s)
     const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
     timer_start(h, s);
     HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
-                       h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
+                       h->gflag, h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
          "expand kernel");
     h->ms_expand += timer_stop(h, s);
     return ERSJ_OK;

@@ -247,6 +247,7 @@ struct RefineArgs {
                                   // 64-candidate chunk of each cell's candidate list
     const uint64_t *chunk_base;   // first chunk of each cell
     unsigned long long *skipped;  // comparisons decided by that box test alone
+    uint8_t *gflag;               // per 4 mask words (aligned): 1 if any bit is set, else 0
     uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
     uint64_t row_base;            // first query row of the batch
 };
@@ -298,12 +299,13 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
                               uint64_t *out, hipStream_t s);
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
                           const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
+                          const int32_t *pinv, double e64, uint64_t *mask, uint8_t *gflag,
+                          unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s);
 
 
 hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
-                         uint64_t wbase, uint64_t row_base, const uint64_t *mask,
+                         uint64_t wbase, uint64_t row_base, const uint64_t *mask, const uint8_t *gflag,
                          const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
                          const uint32_t *nrng, const uint32_t *qorig, const uint32_t *orig,
                          uint32_t *pairs, hipStream_t s);

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
                                                  const float *__restrict__ xqf, uint64_t nqr,
                                                  int32_t d, const int32_t *__restrict__ pinv,
                                                  double e64, uint64_t *__restrict__ mask,
+                                                 uint8_t *__restrict__ gflag,
                                                  unsigned long long *__restrict__ nin,
                                                  uint32_t *__restrict__ rowcnt, uint64_t row_base)
 {
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         }
         if (s <= e64) {
             atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
+            gflag[e.bit >> 8] = 1;  // its 4-word unit now holds a bit
             atomicAdd(&rowcnt[e.q - row_base], 1u);
             hit = true;
         }
@@ -108,14 +110,17 @@ __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
     return pos;
 }
 
-// Workgroup per row tile of the batch, wave per row.  A 64-word chunk of the
-// row's mask is staged in LDS with its bit prefix, and its set bits are dealt
-// to the lanes in turn (lane j takes the chunk's set bits j, j + 64, ...), so
-// the pairs of a dense word are written by 64 lanes at once and each wave's
-// stores are consecutive.
+// Workgroup per row tile of the batch, wave per row.  The row's unit flags
+// (one per 4 mask words) are read 64 at a time; the words of up to 16
+// flagged units are staged in LDS with their bit prefix and their set bits
+// are dealt to the lanes in turn (lane j takes the staged set bits j,
+// j + 64, ...), so only flagged words are read, the pairs of a dense word
+// are written by 64 lanes at once, and each wave's stores are consecutive.
+// Pairs come out in candidate order.
 __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, uint32_t t0,
                                                 const uint64_t *__restrict__ toff, uint64_t wbase,
                                                 uint64_t row_base, const uint64_t *__restrict__ mask,
+                                                const uint8_t *__restrict__ gflag,
                                                 const uint64_t *__restrict__ roff,
                                                 const uint32_t *__restrict__ rstart,
                                                 const uint32_t *__restrict__ rpref,
@@ -127,6 +132,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     __shared__ uint32_t s_pref[kMaxRanges + 1];
     __shared__ uint32_t s_start[kMaxRanges];
     __shared__ uint64_t s_words[4][64];
+    __shared__ uint32_t s_widx[4][64];
     __shared__ uint32_t s_before[4][64];
     const uint32_t t = t0 + blockIdx.x;
     const Tile tl = tiles[t];
@@ -138,45 +144,60 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     __syncthreads();
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     uint64_t *const cw = s_words[wave];
+    uint32_t *const ci = s_widx[wave];
     uint32_t *const cb = s_before[wave];
     const uint64_t tbase = toff[t] - wbase;
+    const uint32_t nunits = (tl.used + 3) / 4;
     for (uint32_t r = wave; r < tl.nrows; r += 4) {
         const uint32_t q = tl.row0 + r;
         const uint32_t qid = qorig[q];
-        const uint64_t *row = mask + tbase + (uint64_t)r * tl.words;
+        const uint64_t rw = tbase + (uint64_t)r * tl.words;  // first word of the row (a multiple of 8)
+        const uint64_t *row = mask + rw;
+        const uint8_t *frow = gflag + (rw >> 2);
         uint64_t out = roff[q - row_base];
-        for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
-            const uint32_t w = w0 + lane;
-            const uint64_t m = w < tl.used ? row[w] : 0ull;
-            const uint32_t pc = __popcll(m);
-            uint32_t inc = pc;
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t v = __shfl_up(inc, o, 64);
-                if (lane >= o) inc += v;
-            }
-            const uint32_t total = __shfl(inc, 63, 64);
-            if (total == 0) continue;
-            cw[lane] = m;
-            cb[lane] = inc - pc;
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            for (uint32_t j = lane; j < total; j += 64) {
-                int lo = 0, hi = 63;  // the last word with cb[word] <= j
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (cb[mid] <= j) lo = mid;
-                    else hi = mid - 1;
+        for (uint32_t u0 = 0; u0 < nunits; u0 += 64) {
+            uint64_t nz = __ballot(u0 + lane < nunits && frow[u0 + lane] != 0);
+            while (nz != 0) {
+                const uint32_t cnt = min(16u, (uint32_t)__popcll(nz));
+                const uint32_t slot = (uint32_t)lane >> 2;
+                uint64_t m = 0ull;
+                uint32_t wi = 0;
+                if (slot < cnt) {
+                    wi = (u0 + (uint32_t)nth_bit(nz, slot)) * 4 + (lane & 3);
+                    m = wi < tl.used ? row[wi] : 0ull;
                 }
-                const uint32_t p = (w0 + lo) * 64 + nth_bit(cw[lo], j - cb[lo]);
-                const int g = range_of(s_pref, nr, p);
-                const uint32_t x = s_start[g] + (p - s_pref[g]);
-                const uint64_t pos = out + j;
-                pairs[2 * pos] = qid;
-                pairs[2 * pos + 1] = orig[x];
+                for (uint32_t i = 0; i < cnt; ++i) nz &= nz - 1;
+                const uint32_t pc = __popcll(m);
+                uint32_t inc = pc;
+                for (int o = 1; o < 64; o <<= 1) {
+                    const uint32_t v = __shfl_up(inc, o, 64);
+                    if (lane >= o) inc += v;
+                }
+                const uint32_t total = __shfl(inc, 63, 64);
+                if (total == 0) continue;
+                cw[lane] = m;
+                ci[lane] = wi;
+                cb[lane] = inc - pc;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                for (uint32_t j = lane; j < total; j += 64) {
+                    int lo = 0, hi = 63;  // the last staged word with cb[word] <= j
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (cb[mid] <= j) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    const uint32_t p = ci[lo] * 64 + nth_bit(cw[lo], j - cb[lo]);
+                    const int g = range_of(s_pref, nr, p);
+                    const uint32_t x = s_start[g] + (p - s_pref[g]);
+                    const uint64_t pos = out + j;
+                    pairs[2 * pos] = qid;
+                    pairs[2 * pos + 1] = orig[x];
+                }
+                out += total;
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
-            out += total;
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         }
     }
 }
@@ -192,26 +213,26 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
                           const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, unsigned long long *nin,
-                          uint32_t *rowcnt, uint64_t row_base, hipStream_t s)
+                          const int32_t *pinv, double e64, uint64_t *mask, uint8_t *gflag,
+                          unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base, hipStream_t s)
 {
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
     hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt,
-                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, nin, rowcnt,
-                       row_base);
+                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, gflag, nin,
+                       rowcnt, row_base);
     return hipGetLastError();
 }
 
 hipError_t launch_expand(const Tile *tiles, uint32_t t0, uint32_t ntiles, const uint64_t *toff,
-                         uint64_t wbase, uint64_t row_base, const uint64_t *mask,
+                         uint64_t wbase, uint64_t row_base, const uint64_t *mask, const uint8_t *gflag,
                          const uint64_t *roff, const uint32_t *rstart, const uint32_t *rpref,
                          const uint32_t *nrng, const uint32_t *qorig, const uint32_t *orig,
                          uint32_t *pairs, hipStream_t s)
 {
     if (ntiles == 0) return hipSuccess;
     hipLaunchKernelGGL(k_expand, dim3(ntiles), dim3(256), 0, s, tiles, t0, toff, wbase, row_base, mask,
-                       roff, rstart, rpref, nrng, qorig, orig, pairs);
+                       gflag, roff, rstart, rpref, nrng, qorig, orig, pairs);
     return hipGetLastError();
 }
 

@@ -127,6 +127,8 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
                     const int k = lane / kCW, j = lane % kCW;
                     const uint32_t w = (c >> 6) + j;
                     if ((uint32_t)k < nq && w < tl.words) mask[mbase + (uint64_t)k * tl.words + w] = 0ull;
+                    // the chunk's 4 words are one flag unit
+                    if (j == 0 && (uint32_t)k < nq && w < tl.words) a.gflag[(mbase + (uint64_t)k * tl.words + w) >> 2] = 0;
                 }
                 continue;
             }
@@ -193,12 +195,17 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
                 }
             }
         }
-        if (lane < kQW * kCW) {
+        {
             const int k = lane / kCW, j = lane % kCW;
-            if ((uint32_t)k < nq && w0 + j < tl.words) {
+            const bool ok = lane < kQW * kCW && (uint32_t)k < nq && w0 + j < tl.words;
+            if (ok) {
                 mask[mbase + (uint64_t)k * tl.words + w0 + j] = myword;
                 mycnt += __popcll(myword);
             }
+            // the chunk's 4 words of a query are one flag unit (lanes 4k .. 4k+3)
+            const uint64_t nzb = __ballot(ok && myword != 0);
+            if (lane < kQW * kCW && j == 0 && (uint32_t)k < nq && w0 < tl.words)
+                a.gflag[(mbase + (uint64_t)k * tl.words + w0) >> 2] = ((nzb >> lane) & 0xfull) ? 1 : 0;
         }
     }
     if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);

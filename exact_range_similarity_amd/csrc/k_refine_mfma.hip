@@ -484,17 +484,26 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             L.words[(qb * 32 + lane) * 8 + (s % G::SPG) * G::NCG + cg] =
                 ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
     };
+    // unit flags: the 4 words of a unit sit in 4 consecutive lanes (e & 7
+    // = j, units j 0-3 and 4-7 of a row); the first lane of the unit writes
+    auto unit_flag = [&](int row, int j, uint32_t w, bool ok, bool nz) __attribute__((always_inline)) {
+        const uint64_t b = __ballot(nz);
+        if (ok && (j & 3) == 0) a.gflag[(mbase + (uint64_t)row * W + w) >> 2] = ((b >> (lane & ~3)) & 0xfull) ? 1 : 0;
+    };
     auto flush = [&](uint32_t grp) {
         uint64_t *sw = L.words;
         for (int e = tid; e < G::QR * 8; e += 256) {
             const int row = e >> 3, j = e & 7;
             const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
             const uint32_t w = c0 >> 6;
-            if ((uint32_t)row < nrows && w < W && c0 < c_end) {
-                mask[mbase + (uint64_t)row * W + w] = sw[e];
-                const uint32_t pc = __popcll(sw[e]);
+            const bool ok = (uint32_t)row < nrows && w < W && c0 < c_end;
+            const uint64_t v = sw[e];
+            if (ok) {
+                mask[mbase + (uint64_t)row * W + w] = v;
+                const uint32_t pc = __popcll(v);
                 if (pc != 0) atomicAdd(&L.rcnt[row], pc);
             }
+            unit_flag(row, j, w, ok, ok && v != 0);
             sw[e] = 0ull;  // words of steps the next group skips stay zero
         }
     };
@@ -505,7 +514,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 const int row = e >> 3, j = e & 7;
                 const uint32_t c0 = c_begin + g * kGroupCands + 64 * j;
                 const uint32_t w = c0 >> 6;
-                if ((uint32_t)row < nrows && w < W && c0 < c_end) mask[mbase + (uint64_t)row * W + w] = 0ull;
+                const bool ok = (uint32_t)row < nrows && w < W && c0 < c_end;
+                if (ok) mask[mbase + (uint64_t)row * W + w] = 0ull;
+                unit_flag(row, j, w, ok, false);
             }
         }
     };
