@@ -1443,6 +1443,7 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
             a.wbase = h->hwords[b];
             a.row_base = h->hrows[b];
             a.mask = h->mask;
+            a.gflag = h->gflag;
             a.rowcnt = h->rowcnt;
             timer_start(h, s);
             HIPC(launch_knn_select(a, h->hb[b + 1] - h->hb[b], s), "kNN select kernel");

@@ -261,6 +261,7 @@ struct KnnArgs {
     uint64_t wbase;              // first mask word of the batch
     uint64_t row_base;           // first query row of the batch
     const uint64_t *mask;
+    const uint8_t *gflag;        // per 4 mask words: any bit set
     const uint32_t *rowcnt;      // neighbours per row of the batch
     const uint32_t *rpref, *rstart, *nrng;
     const uint32_t *orig;        // sorted point -> input row

@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     uint32_t *const cb = s_before[wave];
     const uint64_t tbase = toff[t] - wbase;
     const uint32_t nunits = (tl.used + 3) / 4;
+    const bool al8 = ((uintptr_t)pairs & 7u) == 0;  // a pair in one 8-byte store
     for (uint32_t r = wave; r < tl.nrows; r += 4) {
         const uint32_t q = tl.row0 + r;
         const uint32_t qid = qorig[q];
@@ -191,8 +192,12 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                     const int g = range_of(s_pref, nr, p);
                     const uint32_t x = s_start[g] + (p - s_pref[g]);
                     const uint64_t pos = out + j;
-                    pairs[2 * pos] = qid;
-                    pairs[2 * pos + 1] = orig[x];
+                    if (al8) {
+                        ((uint2 *)pairs)[pos] = make_uint2(qid, orig[x]);
+                    } else {
+                        pairs[2 * pos] = qid;
+                        pairs[2 * pos + 1] = orig[x];
+                    }
                 }
                 out += total;
                 __builtin_amdgcn_wave_barrier();

@@ -43,8 +43,9 @@ struct KnnLds {
     uint64_t hi[kWaves][kCap];   // D64 bits
     uint32_t lo[kWaves][kCap];   // point id
     uint32_t hist[kWaves][256];
-    uint64_t words[kWaves][64];  // a 64-word chunk of the row's mask
-    uint32_t before[kWaves][64]; // set bits in the chunk's earlier words
+    uint64_t words[kWaves][64];  // staged mask words of the row
+    uint32_t widx[kWaves][64];   // their word index in the row
+    uint32_t before[kWaves][64]; // set bits in the earlier staged words
     uint32_t pref[kMaxRanges + 1];
     uint32_t start[kMaxRanges];
 };
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
     uint32_t *const elo = L.lo[wave];
     uint32_t *const hist = L.hist[wave];
     uint64_t *const cw = L.words[wave];
+    uint32_t *const ci = L.widx[wave];
     uint32_t *const cb = L.before[wave];
     const uint32_t k = a.k;
     const int32_t d = a.d;
@@ -161,52 +163,67 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
         const uint32_t oq = a.qmap ? a.qmap[qid] : qid;    // query id of the whole search
         const float *qrow = a.qbase + (uint64_t)qid * a.ldq;
         const uint64_t *row = a.mask + tbase + (uint64_t)r * tl.words;
+        const uint8_t *frow = a.gflag + ((tbase + (uint64_t)r * tl.words) >> 2);
 
         // Calls f(valid, hi, lo) once per lane and step until every set bit
         // of the row has been visited; each valid lane holds one neighbour's
-        // key.  A 64-word chunk of the mask is staged in LDS with its bit
-        // prefix, and the chunk's set bits are dealt to the lanes in turn,
-        // so dense words do not serialise the distance work on one lane.
+        // key.  The row's unit flags (one per 4 mask words) are read 64 at a
+        // time; the words of up to 16 flagged units are staged in LDS with
+        // their bit prefix, and their set bits are dealt to the lanes in
+        // turn, so only flagged words are read and dense words do not
+        // serialise the distance work on one lane.
         auto for_each = [&](auto &&f) __attribute__((always_inline)) {
-            for (uint32_t w0 = 0; w0 < tl.used; w0 += 64) {
-                const uint32_t w = w0 + lane;
-                const uint64_t m = w < tl.used ? row[w] : 0ull;
-                const uint32_t pc = __popcll(m);
-                uint32_t inc = pc;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t v = __shfl_up(inc, o, 64);
-                    if (lane >= o) inc += v;
-                }
-                const uint32_t total = __shfl(inc, 63, 64);
-                if (total == 0) continue;
-                cw[lane] = m;
-                cb[lane] = inc - pc;
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                for (uint32_t j0 = 0; j0 < total; j0 += 64) {
-                    const uint32_t j = j0 + lane;
-                    const bool valid = j < total;
-                    uint64_t kh = ~0ull;
-                    uint32_t kl = ~0u;
-                    if (valid) {
-                        int lo = 0, hi = 63;  // the last word with cb[word] <= j
-                        while (lo < hi) {
-                            const int mid = (lo + hi + 1) >> 1;
-                            if (cb[mid] <= j) lo = mid;
-                            else hi = mid - 1;
-                        }
-                        const uint32_t p = (w0 + lo) * 64 + nth_set_bit(cw[lo], j - cb[lo]);
-                        const int g = range_of(L.pref, nr, p);
-                        const uint32_t pid = a.orig[L.start[g] + (p - L.pref[g])];
-                        const double s = canonical_d64(qrow, a.x + (uint64_t)pid * a.ld, d);
-                        kh = (uint64_t)__double_as_longlong(s);
-                        kl = pid;
+            const uint32_t nunits = (tl.used + 3) / 4;
+            for (uint32_t u0 = 0; u0 < nunits; u0 += 64) {
+                uint64_t nz = __ballot(u0 + lane < nunits && frow[u0 + lane] != 0);
+                while (nz != 0) {
+                    const uint32_t cnt = min(16u, (uint32_t)__popcll(nz));
+                    const uint32_t slot = (uint32_t)lane >> 2;
+                    uint64_t m = 0ull;
+                    uint32_t wi = 0;
+                    if (slot < cnt) {
+                        wi = (u0 + (uint32_t)nth_set_bit(nz, slot)) * 4 + (lane & 3);
+                        m = wi < tl.used ? row[wi] : 0ull;
                     }
-                    f(valid, kh, kl);
+                    for (uint32_t i = 0; i < cnt; ++i) nz &= nz - 1;
+                    const uint32_t pc = __popcll(m);
+                    uint32_t inc = pc;
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const uint32_t v = __shfl_up(inc, o, 64);
+                        if (lane >= o) inc += v;
+                    }
+                    const uint32_t total = __shfl(inc, 63, 64);
+                    if (total == 0) continue;
+                    cw[lane] = m;
+                    ci[lane] = wi;
+                    cb[lane] = inc - pc;
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    for (uint32_t j0 = 0; j0 < total; j0 += 64) {
+                        const uint32_t j = j0 + lane;
+                        const bool valid = j < total;
+                        uint64_t kh = ~0ull;
+                        uint32_t kl = ~0u;
+                        if (valid) {
+                            int lo = 0, hi = 63;  // the last staged word with cb[word] <= j
+                            while (lo < hi) {
+                                const int mid = (lo + hi + 1) >> 1;
+                                if (cb[mid] <= j) lo = mid;
+                                else hi = mid - 1;
+                            }
+                            const uint32_t p = ci[lo] * 64 + nth_set_bit(cw[lo], j - cb[lo]);
+                            const int g = range_of(L.pref, nr, p);
+                            const uint32_t pid = a.orig[L.start[g] + (p - L.pref[g])];
+                            const double s = canonical_d64(qrow, a.x + (uint64_t)pid * a.ld, d);
+                            kh = (uint64_t)__double_as_longlong(s);
+                            kl = pid;
+                        }
+                        f(valid, kh, kl);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
                 }
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
         };
         // append the valid lanes' keys at ehi/elo[*n ...]
