@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "ε-self-join time + candidate dist evals/s and % of HBM/FP32 roofline, 1 GPU"
 FP32_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (256 CUs, 2.4 GHz)
+FP16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix peak
 HBM_PEAK_GBS = 8000.0
 
 
@@ -159,15 +160,22 @@ def main():
     # without a distance, so they carry no flops
     evaluated = refined - skipped
     avg_launch_ms = refine_ms / max(1, launches)
-    mfma = st["refine_kernel"] == ersj.REFINE_MFMA
-    # algorithmic flops per candidate: direct form 3d (sub, mul, add per
-    # dimension); expanded form 2d + 3 (the dot product on MFMA plus norms)
-    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
+    kern = st["refine_kernel"]
+    mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
+    f16 = kern == ersj.REFINE_MFMA16
+    # flops per computed candidate: direct form 3d (sub, mul, add per
+    # dimension); expanded form 2d + 3 (the dot product on MFMA plus norms);
+    # split-fp16 form 6d + 3 (three fp16 products per dimension on MFMA)
+    per_cand = (6.0 * d + 3.0) if f16 else (2.0 * d + 3.0) if mfma else 3.0 * d
     flops_per_launch = per_cand * evaluated / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
-    kname = "k_refine_mfma" if mfma else "k_refine_direct"
+    peak = FP16_PEAK_TFLOPS if f16 else FP32_PEAK_TFLOPS
+    # the same launch priced as fp32 work (2d + 3 flops per candidate)
+    fp32_equiv = (2.0 * d + 3.0) * evaluated / max(1, launches) / (avg_launch_ms * 1e-3) / 1e12
+    kname = "k_refine_mfma" if mfma else "k_refine_direct"  # one kernel template, both MFMA forms
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"{kname.replace('k_', '')}_{args.workload}_traffic.json")
+    form = kname.replace("k_", "") + ("16" if f16 else "")
+    tfile = os.path.join(ROOT, "profiles", f"{form}_{args.workload}_traffic.json")
     if os.path.exists(tfile):
         import hashlib
         with open(tfile) as f:
@@ -191,7 +199,7 @@ def main():
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16x3/f32" if f16 else "f32",
         "data": "synthetic",
         "config": {
             "workload": (f"{args.workload}: {spec.desc}; eps for a mean of {spec.k} neighbours/point"
@@ -201,7 +209,7 @@ def main():
             "n": int(X.shape[0]), "d": int(d), "eps": rec["eps"], "k": spec.k, "seed": spec.seed,
             "batches": st["n_batches"], "budget_bytes": budget, "grid_reach": args.grid_reach,
             "block_prune": not args.no_block_prune,
-            "refine_kernel": {1: "direct", 2: "mfma"}.get(st["refine_kernel"], "?"),
+            "refine_kernel": {1: "direct", 2: "mfma", 3: "mfma16"}.get(kern, "?"),
         },
         "join_wall_s": wall,
         "result_pairs": npairs,
@@ -217,10 +225,13 @@ def main():
         "roofline": {
             "bound": "mfma" if mfma else "alu",
             "kernel": kname,
+            "mfma_dtype": "f16 (hi/lo split), f32 accumulate" if f16 else "f32" if mfma else None,
             "achieved": achieved,
-            "peak": FP32_PEAK_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / FP32_PEAK_TFLOPS,
+            "frac": achieved / peak,
+            "fp32_equivalent": {"achieved": fp32_equiv, "peak": FP32_PEAK_TFLOPS,
+                                "frac": fp32_equiv / FP32_PEAK_TFLOPS} if f16 else None,
             "traffic": traffic,
             "flops_per_launch": flops_per_launch,
             "avg_launch_ms": avg_launch_ms,
@@ -323,11 +334,14 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
     refine_ms = sum(i["refine_ms"] for i in infos)
     launches = sum(i["refine_launches"] for i in infos)
     computed = sum(i["computed_candidates"] for i in infos)
-    mfma = args.refine != 1
-    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
+    kern = info["refine_kernel"]
+    mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
+    f16 = kern == ersj.REFINE_MFMA16
+    per_cand = (6.0 * d + 3.0) if f16 else (2.0 * d + 3.0) if mfma else 3.0 * d
     avg_launch_ms = refine_ms / max(1, launches)
     flops_per_launch = per_cand * computed / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    peak = FP16_PEAK_TFLOPS if f16 else FP32_PEAK_TFLOPS
     phases = {key: sum(i[key] for i in infos) / args.steps
               for key in ("index_ms", "refine_ms", "recheck_ms", "select_ms")}
     out = {
@@ -341,7 +355,7 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16x3/f32" if f16 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {spec.desc}; exact kNN of every point, k={k}, first "
                                f"radius {args.eps0_scale} x the workload's eps",
@@ -357,8 +371,9 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
         "roofline": {
             "bound": "mfma" if mfma else "alu",
             "kernel": "k_refine_mfma" if mfma else "k_refine_direct",
-            "achieved": achieved, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / FP32_PEAK_TFLOPS, "traffic": None,
+            "mfma_dtype": "f16 (hi/lo split), f32 accumulate" if f16 else "f32" if mfma else None,
+            "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": None,
             "flops_per_launch": flops_per_launch, "avg_launch_ms": avg_launch_ms, "launches": launches,
         },
     }

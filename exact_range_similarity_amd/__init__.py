@@ -28,6 +28,7 @@ ERR_CAPACITY = -6
 REFINE_AUTO = 0
 REFINE_DIRECT = 1
 REFINE_MFMA = 2
+REFINE_MFMA16 = 3
 
 _NAMES = {0: "OK", -1: "INVALID_ARG", -2: "STATE", -3: "HIP", -4: "OOM", -5: "BUDGET",
           -6: "CAPACITY"}
@@ -75,7 +76,7 @@ KNN_MAX_ROUNDS = 41
 
 
 class KnnInfo(ctypes.Structure):
-    _fields_ = [("rounds", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("rounds", ctypes.c_int32), ("refine_kernel", ctypes.c_int32),
                 ("eps", ctypes.c_double * KNN_MAX_ROUNDS), ("queries", ctypes.c_int64 * KNN_MAX_ROUNDS),
                 ("candidates", ctypes.c_uint64 * KNN_MAX_ROUNDS),
                 ("dim_estimate", ctypes.c_double * KNN_MAX_ROUNDS),
@@ -86,7 +87,7 @@ class KnnInfo(ctypes.Structure):
 
     def as_dict(self):
         r = min(self.rounds, KNN_MAX_ROUNDS)
-        return {"rounds": self.rounds, "eps": list(self.eps[:r]), "queries": list(self.queries[:r]),
+        return {"rounds": self.rounds, "refine_kernel": self.refine_kernel, "eps": list(self.eps[:r]), "queries": list(self.queries[:r]),
                 "candidates": list(self.candidates[:r]), "dim_estimate": list(self.dim_estimate[:r]),
                 "total_candidates": self.total_candidates, "index_ms": self.index_ms,
                 "refine_ms": self.refine_ms, "recheck_ms": self.recheck_ms, "select_ms": self.select_ms,

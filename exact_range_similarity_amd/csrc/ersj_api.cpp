@@ -66,6 +66,7 @@ struct ersj_index {
     float tlo = 0.0f, thi = 0.0f;
     float tbox = INFINITY;  // block box test threshold (inf: off)
     float kp = 1.0f, km = 1.0f;
+    float s16 = 1.0f, tlo16 = 0.0f, thi16 = 0.0f, tabs = 0.0f;  // split-fp16 form (scaled domain)
     double maxabs = 0.0;
     GridParams gp{};
     std::vector<int32_t> perm, pinv;
@@ -377,21 +378,79 @@ bool mfma_feasible(const ersj_index *h, const char **why)
     return true;
 }
 
+// Split-fp16 MFMA form, classified in a scaled domain.  Centred coordinates
+// v (|v| <= M = 2 max|x|) are multiplied by s = 2^(14 - ceil(log2 M)), exact
+// in fp32 (|v s| <= 2^15 < 65504), and split into hi = fl16(v s) and
+// lo = fl16(v s - hi): v s = hi + lo + e, |e| <= 2^-22 |v s| + 2^-25 (the
+// 2^-25 covers subnormal parts).  Then s^2 q'x' = hi.hi + hi.lo + lo.hi + r
+// with |r| <= 3 * 2^-22 |s^2 q'x'| plus absolute terms below
+// 2^-25 (|q's| + |x's|) * 1.01 per dimension.  The fp16 products are exact in
+// fp32; each k = 16 MFMA adds 16 products and the accumulator, 17 additions,
+// each taken to err by less than one ulp (2u): 34u per instruction (a probe
+// of v_mfma_f32_32x32x16_f16 on the GPU measured at most 22.3u of
+// sum |ab| + |c|); the band charges 36u for each of the 3 ceil(d_pad / 16)
+// instructions of a tile, on top of the fp32 kernel's K.  With
+// sum |q'_k x'_k| <= (Nq + Nx) / 2 the relative part fits the
+// norm-proportional band.  Norms come from the scaled coordinates and the
+// thresholds are those of fl(eps^2) s^2 (s^2 a power of two, so the rounding
+// analysis of the fp32 thresholds carries over); the absolute part, at most
+// 2^-24 d_pad M s 1.02 in s^2 D, is charged twice over as tabs on both
+// thresholds.  Admitted while s is a normal fp32 power of two.
+bool mfma16_setup(ersj_index *h)
+{
+    const double M = 2.0 * std::max(h->maxabs, h->maxabs_q);
+    int e = 14;
+    if (M > 0.0) {
+        int ex = 0;
+        std::frexp(M, &ex);  // M < 2^ex
+        e = 14 - ex;
+    }
+    if (e < -120 || e > 120) return false;
+    const double s = std::ldexp(1.0, e);
+    const double dpad = 4.0 * h->nb;
+    const int nslab = (h->nb + 3) / 4;
+    const double u = std::ldexp(1.0, -24);
+    const double K = 4.0 * (dpad + 8.0) * u + 3.0 * std::ldexp(1.0, -22) + 36.0 * u * 3.0 * nslab * 1.01;
+    h->kp = (float)(1.0 + K);
+    h->km = (float)(1.0 - K);
+    h->s16 = (float)s;
+    h->tabs = round_up_f32(4.0 * u * dpad * (M * s) * 1.02);
+    // thresholds of fl(eps^2) s^2, by the same rules as the fp32 ones
+    const double E = h->e64 * s * s;
+    if (std::isinf(E)) {
+        h->tlo16 = h->tlo == INFINITY ? INFINITY : FLT_MAX;
+        h->thi16 = INFINITY;
+    } else {
+        const double g32 = gamma_n(dpad + 2, u);
+        const double g64 = gamma_n(h->d + 2, std::ldexp(1.0, -53));
+        const double delta = 2.0 * (g32 + g64);
+        h->thi16 = std::max(round_up_f32(E * (1.0 + delta)), (float)std::ldexp(1.0, -80));
+        h->tlo16 = E < std::ldexp(1.0, -90) ? -1.0f : round_down_f32(E * (1.0 - delta));
+    }
+    return true;
+}
+
 int choose_kernel(ersj_index *h)
 {
     const char *why = "";
     const bool ok = mfma_feasible(h, &why);
     int k = h->opt.refine_kernel;
-    if (k == ERSJ_REFINE_MFMA && !ok)
+    if ((k == ERSJ_REFINE_MFMA || k == ERSJ_REFINE_MFMA16) && !ok)
         return fail(ERSJ_ERR_INVALID_ARG, "MFMA refinement not usable for this input: %s", why);
-    if (k == ERSJ_REFINE_AUTO) k = ok ? ERSJ_REFINE_MFMA : ERSJ_REFINE_DIRECT;
+    if (k == ERSJ_REFINE_AUTO) {
+        // the split-fp16 form where its scale fits, else fp32 MFMA, else direct
+        k = !ok ? ERSJ_REFINE_DIRECT : mfma16_setup(h) ? ERSJ_REFINE_MFMA16 : ERSJ_REFINE_MFMA;
+    } else if (k == ERSJ_REFINE_MFMA16 && !mfma16_setup(h)) {
+        return fail(ERSJ_ERR_INVALID_ARG, "split-fp16 refinement not usable: coordinate scale out of range");
+    }
     h->kernel_used = k;
     if (k == ERSJ_REFINE_MFMA) {
         const double K = 4.0 * (4.0 * h->nb + 8.0) * std::ldexp(1.0, -24);
         h->kp = (float)(1.0 + K);
         h->km = (float)(1.0 - K);
-        HIPC(prepare_refine_mfma(h->nb), "MFMA kernel LDS attribute");
+        HIPC(prepare_refine_mfma(h->nb, false), "MFMA kernel LDS attribute");
     }
+    if (k == ERSJ_REFINE_MFMA16) HIPC(prepare_refine_mfma(h->nb, true), "MFMA kernel LDS attribute");
     return ERSJ_OK;
 }
 
@@ -694,7 +753,7 @@ int do_count(ersj_index *h, hipStream_t s)
     HIPC(scan_u64(cands, h->coff, (int64_t)T, stmp, s), "candidate scan");
     HIPC(hipMemcpyAsync(&h->total_words, h->toff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(&h->total_cand, h->coff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
-    if (h->kernel_used == ERSJ_REFINE_MFMA && std::isfinite(h->tbox)) {
+    if ((h->kernel_used == ERSJ_REFINE_MFMA || h->kernel_used == ERSJ_REFINE_MFMA16) && std::isfinite(h->tbox)) {
         // boxes of each cell list's 64-candidate chunks for the block box test
         uint32_t *ccnt = nullptr;
         TRY(tmp.get(&ccnt, (size_t)M, "chunk boxes"));
@@ -847,7 +906,8 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.order = h->order;
     a.ord0 = t0;
     a.ntiles = ntiles;
-    const bool mfma = h->kernel_used == ERSJ_REFINE_MFMA;
+    const bool f16 = h->kernel_used == ERSJ_REFINE_MFMA16;
+    const bool mfma = h->kernel_used == ERSJ_REFINE_MFMA || f16;
     // row sub-blocks: the direct kernel covers 32 rows per work item, the
     // MFMA kernel 32 per query block it holds
     a.nsub = (uint32_t)(kTileRows / (mfma ? 32 * refine_mfma_qblocks(h->nb) : 32));
@@ -868,6 +928,12 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.thi = h->thi;
     a.kp = h->kp;
     a.km = h->km;
+    a.s16 = h->s16;
+    a.tabs = h->tabs;
+    if (f16) {
+        a.tlo = h->tlo16;
+        a.thi = h->thi16;
+    }
     const size_t ncount = (size_t)kBandLists * kBandStride + 2;
     unsigned long long *const hits = h->counters + (size_t)kBandLists * kBandStride;
     unsigned long long *const skipped = hits + 1;
@@ -889,7 +955,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
         HIPC(launch_fill_u64((uint64_t *)h->counters, 0, (int64_t)ncount, s), "clear counters");
         HIPC(launch_fill_u32(h->rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
-        HIPC(mfma ? launch_refine_mfma(a, s) : launch_refine_direct(a, s), "refine kernel");
+        HIPC(mfma ? launch_refine_mfma(a, f16, s) : launch_refine_direct(a, s), "refine kernel");
         h->ms_refine += timer_stop(h, s);
         if (h->opt.timing) {
             h->refine_launches += 1;
@@ -1095,7 +1161,7 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
         o.struct_size = sizeof o;
         if (!(o.cell_width_scale >= 0.0) || std::isinf(o.cell_width_scale))
             return fail(ERSJ_ERR_INVALID_ARG, "cell_width_scale must be finite and >= 0");
-        if (o.refine_kernel < ERSJ_REFINE_AUTO || o.refine_kernel > ERSJ_REFINE_MFMA)
+        if (o.refine_kernel < ERSJ_REFINE_AUTO || o.refine_kernel > ERSJ_REFINE_MFMA16)
             return fail(ERSJ_ERR_INVALID_ARG, "unknown refine_kernel %d", o.refine_kernel);
         if (o.grid_reach < 0 || o.grid_reach > kMaxGridReach)
             return fail(ERSJ_ERR_INVALID_ARG, "grid_reach must be 0, 1 or 2 (got %d)", o.grid_reach);
@@ -1449,6 +1515,7 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
             HIPC(launch_knn_select(a, h->hb[b + 1] - h->hb[b], s), "kNN select kernel");
             select_ms += timer_stop(h, s);
         }
+        if (info) info->refine_kernel = h->kernel_used;
         if (info && h->opt.timing) {
             info->index_ms += h->ms_build + h->ms_count + h->ms_plan;
             info->refine_ms += h->ms_refine;

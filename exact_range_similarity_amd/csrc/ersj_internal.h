@@ -238,6 +238,9 @@ struct RefineArgs {
     uint64_t *mask;
     float tlo, thi;      // fp32 classification thresholds
     float kp, km;        // 1 + K and 1 - K of the MFMA kernel's norm-proportional band
+    float s16;           // split-fp16 form: power-of-two scale of the centred coordinates
+                         // (tlo, thi are then the scaled thresholds)
+    float tabs;          // absolute widening of its thresholds (fp16 subnormal parts)
     Boundary *blist;              // kBandLists sub-lists of lcap entries each
     unsigned long long *bcount;   // sub-list c's counter at bcount[c * kBandStride]
     uint64_t lcap;                // entries per sub-list
@@ -289,8 +292,8 @@ hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, 
 // k_refine_mfma.hip: query blocks of 32 rows per work item (4, 2 or 1)
 int refine_mfma_qblocks(int nb);
 size_t refine_mfma_lds_bytes(int nb);
-hipError_t prepare_refine_mfma(int nb);
-hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s);
+hipError_t prepare_refine_mfma(int nb, bool f16);
+hipError_t launch_refine_mfma(const RefineArgs &a, bool f16, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
 // Band-list bookkeeping after a refinement launch: out[0] = entries kept

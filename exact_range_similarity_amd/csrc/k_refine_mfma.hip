@@ -58,6 +58,26 @@ namespace ersj {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float4 scale4(float4 v, float s)
+{
+    return make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
+}
+
+// Split of a (scaled) coordinate block into fp16 high and low parts:
+// hi = fl16(v), lo = fl16(v - hi) (the difference is exact in fp32).
+__device__ __forceinline__ void split16(float4 v, half4 &hi, half4 &lo)
+{
+    const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const _Float16 h = (_Float16)a[i];
+        hi[i] = h;
+        lo[i] = (_Float16)(a[i] - (float)h);
+    }
+}
 
 constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
 constexpr int kNB = 2;            // step buffers for norms / candidate ids
@@ -141,7 +161,7 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     return L;
 }
 
-template <int QB, int NS>
+template <int QB, int NS, bool F16>
 __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs a)
 {
     using G = Geometry<QB>;
@@ -189,21 +209,37 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         const int b = e / G::QR, i = e - b * G::QR;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
         if (b < nb && (uint32_t)i < nrows) v = sub4(xq[(uint64_t)b * nqr + row0 + i], L.r[b]);
-        L.q[e] = v;
+        if constexpr (F16) {
+            // slab sl = b / kSlab holds [hi k 0-7, hi k 8-15, lo k 0-7, lo k 8-15][row]
+            const int sl = b / kSlab, j = b % kSlab;
+            half4 h, l;
+            split16(scale4(v, a.s16), h, l);
+            ((half4 *)&L.q[(sl * kSlab + j / 2) * G::QR + i])[j & 1] = h;
+            ((half4 *)&L.q[(sl * kSlab + 2 + j / 2) * G::QR + i])[j & 1] = l;
+        } else {
+            L.q[e] = v;
+        }
     }
     __syncthreads();
     for (int i = tid; i < G::QR; i += 256) {
         float nq = 0.f;
         for (int b = 0; b < nb; ++b) {
-            const float4 v = L.q[b * G::QR + i];
+            float4 v;
+            if constexpr (F16) {
+                v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if ((uint32_t)i < nrows) v = scale4(sub4(xq[(uint64_t)b * nqr + row0 + i], L.r[b]), a.s16);
+            } else {
+                v = L.q[b * G::QR + i];
+            }
             nq = fmaf(v.x, v.x, nq);
             nq = fmaf(v.y, v.y, nq);
             nq = fmaf(v.z, v.z, nq);
             nq = fmaf(v.w, v.w, nq);
         }
         const bool live = (uint32_t)i < nrows;
-        L.qin[i] = live ? a.tlo - a.kp * nq : -INFINITY;
-        L.qout[i] = live ? a.thi - a.km * nq : -INFINITY;
+        const float tabs = F16 ? a.tabs : 0.f;
+        L.qin[i] = live ? a.tlo - a.kp * nq - tabs : -INFINITY;
+        L.qout[i] = live ? a.thi - a.km * nq + tabs : -INFINITY;
         L.rcnt[i] = 0;
     }
     for (int e = tid; e < G::QR * 8; e += 256) L.words[e] = 0ull;
@@ -233,6 +269,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         qhi[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.z)));
     }
     const float kp = a.kp, km = a.km;
+    // the split-fp16 form classifies in the scaled domain (coordinates, norms
+    // and thresholds multiplied by s, s^2 and s^2; host-side thresholds)
+    const float neg2 = -2.0f;
     const uint64_t bcap = a.lcap;
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
     const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
@@ -421,7 +460,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
                 constexpr int j = decltype(J)::value;
                 const float qov = j == 0 ? qo.x : j == 1 ? qo.y : j == 2 ? qo.z : qo.w;
-                const float v2 = fmaf(-2.0f, acc[tt][4 * g + j], xout[tt]);
+                const float v2 = fmaf(neg2, acc[tt][4 * g + j], xout[tt]);
                 bno[j] = __ballot(v2 <= qov);
                 anyno |= bno[j];
             });
@@ -430,7 +469,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                     constexpr int j = decltype(J)::value;
                     constexpr int i0 = 8 * g + j;
                     const float qiv = j == 0 ? qi.x : j == 1 ? qi.y : j == 2 ? qi.z : qi.w;
-                    const float v1 = fmaf(-2.0f, acc[tt][4 * g + j], xin[tt]);
+                    const float v1 = fmaf(neg2, acc[tt][4 * g + j], xin[tt]);
                     const uint64_t bin = __ballot(v1 <= qiv);
                     anyb |= bno[j] & ~bin;
                     if (tt == 0) {
@@ -454,8 +493,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
                 for (int v = 0; v < 16; ++v) {
                     const float dd = at[v];
                     const int row = qb * 32 + (v >> 2) * 8 + (v & 3) + 4 * hi;
-                    const bool in = fmaf(-2.0f, dd, xin[tt]) <= L.qin[row];
-                    const bool nout = fmaf(-2.0f, dd, xout[tt]) <= L.qout[row];
+                    const bool in = fmaf(neg2, dd, xin[tt]) <= L.qin[row];
+                    const bool nout = fmaf(neg2, dd, xout[tt]) <= L.qout[row];
                     const bool bd = !in && nout;
                     const uint64_t bbd = __ballot(bd);
                     if (bbd == 0) continue;
@@ -521,6 +560,26 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         }
     };
     auto mfma_slab = [&](const float4 *xb, int sl, bool fresh) {
+        if constexpr (F16) {
+            // one k = 16 step: hi.hi + hi.lo + lo.hi (lo.lo is below the band)
+            const half8 ah = *(const half8 *)&L.q[(sl * kSlab + hi) * G::QR + qb * 32 + col];
+            const half8 al = *(const half8 *)&L.q[(sl * kSlab + 2 + hi) * G::QR + qb * 32 + col];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int cc = cg * 64 + 32 * tt + col;
+                const half8 bh = *(const half8 *)&xb[hi * G::SC + cc];
+                const half8 bl = *(const half8 *)&xb[(2 + hi) * G::SC + cc];
+                if (fresh) {
+                    const floatx16 z = {};
+                    accC[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, z, 0, 0, 0);
+                } else {
+                    accC[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, accC[tt], 0, 0, 0);
+                }
+                accC[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, accC[tt], 0, 0, 0);
+                accC[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, accC[tt], 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int s2 = 0; s2 < kSlab / 2; ++s2) {
             // block pairs past the last dimension block are zero padding
@@ -558,14 +617,24 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         for (int m = 0; m < G::EPT; ++m) {
             const int e = tid + 256 * m;
             const int j = e / G::SC;
-            const float4 c4 = sub4(ld[0][m], L.r[sl * kSlab + j]);
+            const float4 c4 = F16 ? scale4(sub4(ld[0][m], L.r[sl * kSlab + j]), a.s16)
+                                  : sub4(ld[0][m], L.r[sl * kSlab + j]);
             float s2 = nxp[m];
             s2 = fmaf(c4.x, c4.x, s2);
             s2 = fmaf(c4.y, c4.y, s2);
             s2 = fmaf(c4.z, c4.z, s2);
             s2 = fmaf(c4.w, c4.w, s2);
             nxp[m] = s2;
-            xb[e] = c4;
+            if constexpr (F16) {
+                // [hi k 0-7, hi k 8-15, lo k 0-7, lo k 8-15][candidate]
+                const int c = e - j * G::SC;
+                half4 h, l;
+                split16(c4, h, l);
+                ((half4 *)&xb[(j / 2) * G::SC + c])[j & 1] = h;
+                ((half4 *)&xb[(2 + j / 2) * G::SC + c])[j & 1] = l;
+            } else {
+                xb[e] = c4;
+            }
         }
         if (sl == nslab - 1) {
 #pragma unroll
@@ -686,28 +755,34 @@ namespace {
 
 // kernel instance for nb dimension blocks: query blocks per workgroup and
 // slabs per step (1 and 2 are compiled as constants)
-const void *mfma_kernel(int nb)
+template <bool F16>
+const void *mfma_kernel_t(int nb)
 {
     const int nslab = (nb + kSlab - 1) / kSlab;
     switch (refine_mfma_qblocks(nb)) {
     case 4:
-        if (nslab == 1) return (const void *)k_refine_mfma<4, 1>;
-        if (nslab == 2) return (const void *)k_refine_mfma<4, 2>;
-        return (const void *)k_refine_mfma<4, 0>;
-    case 2: return (const void *)k_refine_mfma<2, 0>;
-    default: return (const void *)k_refine_mfma<1, 0>;
+        if (nslab == 1) return (const void *)k_refine_mfma<4, 1, F16>;
+        if (nslab == 2) return (const void *)k_refine_mfma<4, 2, F16>;
+        return (const void *)k_refine_mfma<4, 0, F16>;
+    case 2: return (const void *)k_refine_mfma<2, 0, F16>;
+    default: return (const void *)k_refine_mfma<1, 0, F16>;
     }
+}
+
+const void *mfma_kernel(int nb, bool f16)
+{
+    return f16 ? mfma_kernel_t<true>(nb) : mfma_kernel_t<false>(nb);
 }
 
 }  // namespace
 
-hipError_t prepare_refine_mfma(int nb)
+hipError_t prepare_refine_mfma(int nb, bool f16)
 {
-    return hipFuncSetAttribute(mfma_kernel(nb), hipFuncAttributeMaxDynamicSharedMemorySize,
+    return hipFuncSetAttribute(mfma_kernel(nb, f16), hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)refine_mfma_lds_bytes(nb));
 }
 
-hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s)
+hipError_t launch_refine_mfma(const RefineArgs &a, bool f16, hipStream_t s)
 {
     const uint64_t blocks = (uint64_t)a.ntiles * a.nseg * a.nsub;
     if (blocks == 0) return hipSuccess;
@@ -715,7 +790,7 @@ hipError_t launch_refine_mfma(const RefineArgs &a, hipStream_t s)
     const size_t bytes = refine_mfma_lds_bytes(a.nb);
     RefineArgs args = a;
     void *params[] = {&args};
-    return hipLaunchKernel(mfma_kernel(a.nb), dim3((unsigned)blocks), dim3(256), params, bytes, s);
+    return hipLaunchKernel(mfma_kernel(a.nb, f16), dim3((unsigned)blocks), dim3(256), params, bytes, s);
 }
 
 }  // namespace ersj

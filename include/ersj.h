@@ -64,9 +64,12 @@ typedef struct ersj_index ersj_index; /* opaque; owns all its device memory */
 
 /* Refinement kernels (Sec. IV-E).  Both return identical pair sets. */
 enum {
-    ERSJ_REFINE_AUTO = 0,   /* library's choice */
+    ERSJ_REFINE_AUTO = 0,   /* library's choice: MFMA16 where admissible, else MFMA, else DIRECT */
     ERSJ_REFINE_DIRECT = 1, /* fp32 sum of squared differences on the vector ALUs */
-    ERSJ_REFINE_MFMA = 2    /* |q|^2 + |x|^2 - 2 q.x with the dot products on MFMA */
+    ERSJ_REFINE_MFMA = 2,   /* |q|^2 + |x|^2 - 2 q.x with the dot products on MFMA */
+    ERSJ_REFINE_MFMA16 = 3  /* the same with each centred coordinate split into fp16 high and low
+                               parts (hi.hi + hi.lo + lo.hi on fp16 MFMA, fp32 accumulation) and a
+                               correspondingly wider band */
 };
 
 typedef struct ersj_options {
@@ -245,7 +248,7 @@ int ersj_host_sync(ersj_index *h);
 #define ERSJ_KNN_MAX_ROUNDS 41
 typedef struct ersj_knn_info {
     int32_t rounds;                             /* rounds run */
-    int32_t reserved;
+    int32_t refine_kernel;                      /* ERSJ_REFINE_* used (last round) */
     double eps[ERSJ_KNN_MAX_ROUNDS];            /* radius of round r */
     int64_t queries[ERSJ_KNN_MAX_ROUNDS];       /* queries searched in round r */
     uint64_t candidates[ERSJ_KNN_MAX_ROUNDS];   /* candidates refined in round r */

@@ -52,7 +52,7 @@ def assert_same_pairs(X, eps, got, want, label=""):
     raise AssertionError(f"{label}: |gpu|={sg.size} |oracle|={sw.size}\n" + "\n".join(lines))
 
 
-KERNELS = (ersj.REFINE_DIRECT, ersj.REFINE_MFMA)
+KERNELS = (ersj.REFINE_DIRECT, ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
 
 
 def check_against_oracle(X, eps, label="", kernels=KERNELS, **kw):
