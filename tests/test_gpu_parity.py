@@ -17,7 +17,7 @@ import exact_range_similarity_amd as ersj
 import oracle
 from workloads import CONFIGS, fig3_points, fig5_points, lattice, make_config
 
-from gpu_util import assert_same_pairs, check_against_oracle, gpu_pairs, keys_of, say
+from gpu_util import KERNELS, assert_same_pairs, check_against_oracle, gpu_pairs, keys_of, say
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -90,7 +90,7 @@ def test_eps_zero_duplicates_and_identical_points():
 def test_eps_infinite_and_huge():
     rng = np.random.default_rng(6)
     X = rng.random((700, 9), dtype=np.float32)
-    for k in (ersj.REFINE_DIRECT, ersj.REFINE_MFMA):
+    for k in KERNELS:
         got = gpu_pairs(X, math.inf, options=ersj.default_options(refine_kernel=k))
         assert got.shape[0] == 700 * 700
     check_against_oracle(X, 1e30, "eps huge")
@@ -217,7 +217,7 @@ def test_non_finite_input_rejected():
     assert e.value.code == ersj.ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("kernel", [ersj.REFINE_DIRECT, ersj.REFINE_MFMA])
+@pytest.mark.parametrize("kernel", KERNELS)
 def test_boundary_list_overflow_regrows(kernel):
     X = lattice(9, 3)
     opts = ersj.default_options(boundary_capacity=16, refine_kernel=kernel)
@@ -230,15 +230,16 @@ def test_kernel_choice():
     rng = np.random.default_rng(11)
     X = rng.random((500, 6), dtype=np.float32)
     xt = torch.from_numpy(X).cuda()
-    for k in (ersj.REFINE_AUTO, ersj.REFINE_DIRECT, ersj.REFINE_MFMA):
+    for k in (ersj.REFINE_AUTO,) + KERNELS:
         h = ersj.build_index(xt, 0.3, ersj.default_options(refine_kernel=k))
         used = ersj.get_stats(h)["refine_kernel"]
         h.free()
-        assert used == (ersj.REFINE_MFMA if k == ersj.REFINE_AUTO else k)
+        assert used == (ersj.REFINE_MFMA16 if k == ersj.REFINE_AUTO else k)
     big = (X * 1e18).astype(np.float32)
-    with pytest.raises(ersj.ErsjError) as e:
-        ersj.build_index(torch.from_numpy(big).cuda(), 1e18, ersj.default_options(refine_kernel=ersj.REFINE_MFMA))
-    assert e.value.code == ersj.ERR_INVALID_ARG
+    for k in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16):
+        with pytest.raises(ersj.ErsjError) as e:
+            ersj.build_index(torch.from_numpy(big).cuda(), 1e18, ersj.default_options(refine_kernel=k))
+        assert e.value.code == ersj.ERR_INVALID_ARG
     h = ersj.build_index(torch.from_numpy(big).cuda(), 1e18)
     assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_DIRECT
     h.free()

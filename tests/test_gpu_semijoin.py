@@ -163,7 +163,7 @@ def test_large_query_coordinates_choose_the_direct_kernel():
     Q[7] = np.float32(1e19)
     x = torch.from_numpy(X).cuda()
     h = ersj.build_index(x, 0.4)
-    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_MFMA
+    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_MFMA16
     ersj.set_queries(h, torch.from_numpy(Q).cuda())
     assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_DIRECT
     ersj.count_pass(h)
