@@ -53,7 +53,7 @@ def main():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--budget-frac", type=float, default=0.0,
                     help="batch budget as a fraction of the total mask (0 = free memory)")
-    ap.add_argument("--refine", type=int, default=0, help="0 auto, 1 direct, 2 mfma")
+    ap.add_argument("--refine", type=int, default=0, help="0 auto, 1 direct, 2 fp32 MFMA, 3 split-fp16 MFMA")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calib", action="store_true",

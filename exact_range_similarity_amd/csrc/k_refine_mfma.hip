@@ -7,8 +7,13 @@
 // comparison).
 //
 // Squared distances are formed as |q'|^2 + |x'|^2 - 2 q'.x' on coordinates
-// centred on the work item's first query r (q' = q - r, x' = x - r, fp32),
-// with q'.x' from v_mfma_f32_32x32x2f32.
+// centred on the work item's first query r (q' = q - r, x' = x - r, fp32).
+// F16 = false: q'.x' from v_mfma_f32_32x32x2f32.  F16 = true (split form):
+// the centred coordinates are multiplied by a power of two s that keeps
+// them below 2^14 and split into fp16 parts h + l (l = fl16(v - h)); the
+// dot product h.h + h.l + l.h takes three v_mfma_f32_32x32x16_f16 per slab
+// with fp32 accumulation, and norms and thresholds live in the same scaled
+// domain (the host scales the thresholds by s^2).
 //
 // Work item: (row tile, candidate segment, row sub-block).  The 256-thread
 // workgroup holds QB query blocks of 32 rows (QB = 4, 2 or 1 with growing
@@ -21,7 +26,9 @@
 //
 // MFMA operands: lanes 0-31 carry dimension block 2s, lanes 32-63 block
 // 2s+1 of the same query/candidate (column = lane % 32); the four components
-// of a float4 feed four k = 2 steps.  The output element of register v in
+// of a float4 feed four k = 2 steps.  Split form: lane l carries row (or
+// column) l % 32 and the eight k = 8*(l/32) .. 8*(l/32)+7 of the slab's high
+// (or low) halves.  The output element of register v in
 // lane l is (row 8*(v/4) + 4*(l/32) + v%4, column l%32).
 //
 // Classification with a norm-proportional band.  With Nq = |q'|^2,
@@ -31,7 +38,10 @@
 //   else boundary -> exact binary64 re-check.
 // K >= 2.02*gamma(d_pad+2) + 6.1u covers the rounding of the centring, of
 // the norms and dot products, and of these fp32 expressions, so "in" implies
-// D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The host bounds the
+// D64 <= fl(eps^2) and "out" implies D64 > fl(eps^2).  The split form's K
+// adds the dropped l.l product, the split residues and the fp16 MFMA's
+// accumulation error, and both sides move by an absolute term tabs for
+// parts in fp16's subnormal range.  The host bounds the
 // coordinates so that nothing here overflows; NaN never classifies.
 //
 // Block pruning: rows within a cell follow a fine Morton order, so a query
