@@ -59,62 +59,21 @@
 // With QB = 4 the kernel stays within 128 VGPRs and, up to d = 32, 40 KiB of
 // LDS, so four workgroups fit a CU.  Mask words collect in LDS and leave as
 // aligned 64-byte row pieces every 512 candidates.
-#include "ersj_internal.h"
-
-#include <utility>
+#include "refine_mfma_common.h"
 
 namespace ersj {
 
 namespace {
 
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+constexpr int kNB = 2;  // step buffers for norms / candidate ids
 
-__device__ __forceinline__ float4 scale4(float4 v, float s)
+// Load registers of a slab: its own with a constant slab count (S is the
+// slab's integral_constant), else the front of the shifted queue.
+template <int NS, class S>
+__device__ constexpr int slab_slot()
 {
-    return make_float4(v.x * s, v.y * s, v.z * s, v.w * s);
-}
-
-// Split of a (scaled) coordinate block into fp16 high and low parts:
-// hi = fl16(v), lo = fl16(v - hi) (the difference is exact in fp32).
-__device__ __forceinline__ void split16(float4 v, half4 &hi, half4 &lo)
-{
-    const float a[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const _Float16 h = (_Float16)a[i];
-        hi[i] = h;
-        lo[i] = (_Float16)(a[i] - (float)h);
-    }
-}
-
-constexpr int kSlab = 4;          // dimension blocks (16 dims) per LDS slab
-constexpr int kNB = 2;            // step buffers for norms / candidate ids
-constexpr int kGroupCands = 512;  // candidates per mask-word flush
-constexpr int kMaxSteps = 128;    // steps of a segment the block box test covers (8192 / 64)
-
-// v_writelane_b32 through its LLVM intrinsic (clang has no builtin for it):
-// writes a wave-uniform 32-bit value into one lane of a VGPR.  The compiler
-// sees a real instruction and keeps the hazard wait states around it, which
-// an asm statement would hide from it.
-extern "C" __device__ int ersj_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
-
-template <int L>
-__device__ __forceinline__ int write_lane(int old, uint32_t val)
-{
-    return ersj_writelane((int)val, L, old);
-}
-
-template <int... E, typename F>
-__device__ __forceinline__ void static_for(std::integer_sequence<int, E...>, F &&f)
-{
-    (f(std::integral_constant<int, E>{}), ...);
-}
-
-__device__ __forceinline__ float4 sub4(float4 a, float4 b)
-{
-    return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+    if constexpr (NS > 0) return S::value;
+    else return 0;
 }
 
 template <int QB>
@@ -205,8 +164,6 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const float4 *__restrict__ xq = a.xq;  // query rows (the points themselves in a self-join)
     const uint64_t nqr = a.nqr;
     uint64_t *__restrict__ mask = a.mask;
-    Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
-    unsigned long long *__restrict__ bcount = band_counter(a.bcount);
     const uint32_t W = tl.words;
     const uint64_t mbase = a.toff[t] - a.wbase + (uint64_t)r_begin * W;
 
@@ -281,8 +238,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const float kp = a.kp, km = a.km;
     // the split-fp16 form classifies in the scaled domain (coordinates, norms
     // and thresholds multiplied by s, s^2 and s^2; host-side thresholds)
-    const float neg2 = -2.0f;
-    const uint64_t bcap = a.lcap;
+    const BandSink bsink{band_list(a.blist, a.lcap), band_counter(a.bcount), a.lcap, row0, mbase, W};
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
     const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
     const float tbox = a.tbox;
@@ -378,8 +334,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             }
         }
     };
-    // loads run kAhead slabs ahead of the staging
-    constexpr int kAhead = 2;
+    // Loads run kAhead slabs ahead of the staging.  With a constant slab
+    // count the slab of a step has its own load registers (ld[sl]), loaded
+    // one step ahead: a register is never copied while its load is in
+    // flight, which would make the wave wait for that load at once.
+    constexpr int kAhead = NS > 0 ? NS : 2;
     float4 ld[kAhead][G::EPT];
     uint32_t ldx[kAhead][G::EPT];
     // element offset of the next load: block b = lsl * kSlab + j of the
@@ -447,91 +406,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             xin[tt] = valid ? kp * nxt : __builtin_nanf("");
             xout[tt] = valid ? km * nxt : __builtin_nanf("");
         }
-        int wlo = 0, whi = 0;
-        uint64_t anyb = 0;
-        // row thresholds come from LDS four rows at a time (rows
-        // 8t + 4hi .. +3 of the query block for registers 4t .. 4t+3)
-        const float4 *qin4 = (const float4 *)L.qin + qb * 8 + hi;
-        const float4 *qout4 = (const float4 *)L.qout + qb * 8 + hi;
-        float4 qi = make_float4(0.f, 0.f, 0.f, 0.f), qo = qi;
-        // Groups of four registers (rows 8g .. 8g+3 and 8g+4 .. 8g+7 of a
-        // tile).  "In" implies "not out" exactly (fl(kp*Nx) >= fl(km*Nx) and
-        // qin <= qout under monotone rounding), so a group whose pairs are
-        // all "out" - most of them - needs only the four "out" tests; its
-        // mask half-words stay zero.
-        static_for(std::make_integer_sequence<int, 8>{}, [&](auto E) {
-            constexpr int g = decltype(E)::value / 2, tt = decltype(E)::value % 2;
-            if (tt == 0) {
-                qi = qin4[g * 2];
-                qo = qout4[g * 2];
-            }
-            uint64_t bno[4];
-            uint64_t anyno = 0;
-            static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
-                constexpr int j = decltype(J)::value;
-                const float qov = j == 0 ? qo.x : j == 1 ? qo.y : j == 2 ? qo.z : qo.w;
-                const float v2 = fmaf(neg2, acc[tt][4 * g + j], xout[tt]);
-                bno[j] = __ballot(v2 <= qov);
-                anyno |= bno[j];
-            });
-            if (anyno != 0) {
-                static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
-                    constexpr int j = decltype(J)::value;
-                    constexpr int i0 = 8 * g + j;
-                    const float qiv = j == 0 ? qi.x : j == 1 ? qi.y : j == 2 ? qi.z : qi.w;
-                    const float v1 = fmaf(neg2, acc[tt][4 * g + j], xin[tt]);
-                    const uint64_t bin = __ballot(v1 <= qiv);
-                    anyb |= bno[j] & ~bin;
-                    if (tt == 0) {
-                        wlo = write_lane<i0>(wlo, (uint32_t)bin);
-                        wlo = write_lane<i0 + 4>(wlo, (uint32_t)(bin >> 32));
-                    } else {
-                        whi = write_lane<i0>(whi, (uint32_t)bin);
-                        whi = write_lane<i0 + 4>(whi, (uint32_t)(bin >> 32));
-                    }
-                });
-            }
-        });
-        if (anyb != 0) {
-            // rare: redo the classification for the band pairs and append
-            // them for the binary64 re-check.  Rolled loops (indexed reads
-            // of one accumulator vector, thresholds re-read from LDS) keep
-            // this path from setting the kernel's register budget.
-            const floatx16 a0 = acc[0], a1 = acc[1];
-            auto band_tile = [&](const floatx16 &at, int tt) __attribute__((always_inline)) {
-#pragma unroll 1
-                for (int v = 0; v < 16; ++v) {
-                    const float dd = at[v];
-                    const int row = qb * 32 + (v >> 2) * 8 + (v & 3) + 4 * hi;
-                    const bool in = fmaf(neg2, dd, xin[tt]) <= L.qin[row];
-                    const bool nout = fmaf(neg2, dd, xout[tt]) <= L.qout[row];
-                    const bool bd = !in && nout;
-                    const uint64_t bbd = __ballot(bd);
-                    if (bbd == 0) continue;
-                    const uint32_t cnt = __popcll(bbd);
-                    const int first = __ffsll((unsigned long long)bbd) - 1;
-                    unsigned long long base = 0;
-                    if (lane == first) base = atomicAdd(bcount, (unsigned long long)cnt);
-                    base = __shfl(base, first, 64);
-                    if (bd) {
-                        const uint64_t below = lane == 0 ? 0ull : (bbd & (~0ull >> (64 - lane)));
-                        const uint64_t idx = base + __popcll(below);
-                        if (idx < bcap) {
-                            Boundary e;
-                            e.q = row0 + row;
-                            e.x = xid[tt];
-                            e.bit = (mbase + (uint64_t)row * W) * 64 + cw + 32 * tt + col;
-                            blist[idx] = e;
-                        }
-                    }
-                }
-            };
-            band_tile(a0, 0);
-            band_tile(a1, 1);
-        }
-        if (lane < 32)
-            L.words[(qb * 32 + lane) * 8 + (s % G::SPG) * G::NCG + cg] =
-                ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
+        classify_block(acc, xin, xout, L.qin, L.qout, qb, lane, cw, bsink, [&](int tt) { return xid[tt]; },
+                       L.words + (qb * 32 + (lane & 31)) * 8 + (s % G::SPG) * G::NCG + cg);
     };
     // unit flags: the 4 words of a unit sit in 4 consecutive lanes (e & 7
     // = j, units j 0-3 and 4-7 of a row); the first lane of the unit writes
@@ -627,8 +503,9 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         for (int m = 0; m < G::EPT; ++m) {
             const int e = tid + 256 * m;
             const int j = e / G::SC;
-            const float4 c4 = F16 ? scale4(sub4(ld[0][m], L.r[sl * kSlab + j]), a.s16)
-                                  : sub4(ld[0][m], L.r[sl * kSlab + j]);
+            constexpr int li = slab_slot<NS, decltype(SLC)>();
+            const float4 c4 = F16 ? scale4(sub4(ld[li][m], L.r[sl * kSlab + j]), a.s16)
+                                  : sub4(ld[li][m], L.r[sl * kSlab + j]);
             float s2 = nxp[m];
             s2 = fmaf(c4.x, c4.x, s2);
             s2 = fmaf(c4.y, c4.y, s2);
@@ -651,7 +528,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             for (int m = 0; m < G::EPT; ++m) {
                 const int e = tid + 256 * m;
                 L.nxp[(bi % kNB) * (kSlab * G::SC) + e] = nxp[m];
-                if (e < G::SC) L.xi[(bi % kNB) * G::SC + e] = ldx[0][m];
+                if (e < G::SC) L.xi[(bi % kNB) * G::SC + e] = ldx[slab_slot<NS, decltype(SLC)>()][m];
                 nxp[m] = 0.f;
             }
         }
@@ -665,18 +542,22 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             pend_group = -1;
             if (nslab == 1) __syncthreads();
         }
+        if constexpr (NS == 0) {
 #pragma unroll
-        for (int a2 = 0; a2 + 1 < kAhead; ++a2) {
+            for (int a2 = 0; a2 + 1 < kAhead; ++a2) {
 #pragma unroll
-            for (int m = 0; m < G::EPT; ++m) {
-                ld[a2][m] = ld[a2 + 1][m];
-                ldx[a2][m] = ldx[a2 + 1][m];
+                for (int m = 0; m < G::EPT; ++m) {
+                    ld[a2][m] = ld[a2 + 1][m];
+                    ldx[a2][m] = ldx[a2 + 1][m];
+                }
             }
         }
         if (k + kAhead < K) {
             if constexpr (NS > 0) {
-                // the slab loaded now and the one after it are known here
-                load_slab((sl + kAhead) % NS, ld[kAhead - 1], ldx[kAhead - 1]);
+                // this slab of the next step, into the registers just staged;
+                // the slab after it is known here
+                constexpr int li = slab_slot<NS, decltype(SLC)>();
+                load_slab(li, ld[li], ldx[li]);
                 if ((sl + kAhead + 1) % NS == 0) {
                     set_cands(live_step(bi + (uint32_t)((sl + kAhead + 1) / NS)));
                     restart_offsets();
