@@ -94,6 +94,7 @@ struct Lds {
     uint32_t *xi;       // [kNB][SC] candidate point index of a step
     float *qin, *qout;  // [QR]
     uint32_t *rcnt;     // [QR] mask bits set per row by this work item
+    float *nqmax;       // [QB] largest query norm of each query block
     uint64_t *words;    // [QR][8] mask words of the current 512-candidate group
     uint32_t *far;      // [4 waves][4] steps (bit s) each wave skips
     uint32_t *live;     // [kMaxSteps] steps some wave computes, ascending
@@ -105,7 +106,7 @@ size_t lds_bytes(int nbs)
 {
     using G = Geometry<QB>;
     return (size_t)nbs * (G::QR + 1) * 16 + (size_t)2 * kSlab * G::SC * 16 + (size_t)kNB * kSlab * G::SC * 4 +
-           (size_t)kNB * G::SC * 4 + (size_t)3 * G::QR * 4 + (size_t)G::QR * 8 * 8 +
+           (size_t)kNB * G::SC * 4 + (size_t)3 * G::QR * 4 + (size_t)QB * 4 + (size_t)G::QR * 8 * 8 +
            (size_t)(16 + kMaxSteps) * 4 + (2 * kMaxRanges + 1) * 4;
 }
 
@@ -122,7 +123,8 @@ __device__ __forceinline__ Lds<QB> carve(float4 *smem, int nbs)
     L.qin = (float *)(L.xi + kNB * G::SC);
     L.qout = L.qin + G::QR;
     L.rcnt = (uint32_t *)(L.qout + G::QR);
-    L.words = (uint64_t *)(L.rcnt + G::QR);
+    L.nqmax = (float *)(L.rcnt + G::QR);
+    L.words = (uint64_t *)(L.nqmax + QB);
     L.far = (uint32_t *)(L.words + G::QR * 8);
     L.live = L.far + 16;
     L.pref = L.live + kMaxSteps;
@@ -208,6 +210,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         L.qin[i] = live ? a.tlo - a.kp * nq - tabs : -INFINITY;
         L.qout[i] = live ? a.thi - a.km * nq + tabs : -INFINITY;
         L.rcnt[i] = 0;
+        // the largest norm of each 32-row query block (rows past nrows: 0)
+        float m = live ? nq : 0.f;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if ((i & 31) == 0) L.nqmax[i >> 5] = m;
     }
     for (int e = tid; e < G::QR * 8; e += 256) L.words[e] = 0ull;
     __syncthreads();
@@ -238,6 +245,27 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const float kp = a.kp, km = a.km;
     // the split-fp16 form classifies in the scaled domain (coordinates, norms
     // and thresholds multiplied by s, s^2 and s^2; host-side thresholds)
+    //
+    // Norm test of a candidate column against the wave's query block: with
+    // v the centred (scaled) fp32 coordinates and N their computed norms,
+    // |v_x - v_q| >= |v_x| - |v_q|, and the centring moves |v_x - v_q| by at
+    // most u (|v_x| + |v_q|) from s |x - q|.  With g = gamma of the terms in
+    // a norm (|N - |v|^2| <= g |v|^2), a candidate with
+    //   N_x > tn = ((sqrt(max N_q) + sqrt(thi)) c1)^2 c2,
+    //   c1 = 1 + g + 2^-18, c2 = 1 + 2 g + 2^-16,
+    // has s |x - q| > sqrt(thi) for every row of the block, so it is out
+    // there: c1^2 c2 exceeds the 1 + 3 g + 5 u the bounds need by more than
+    // the rounding of the square roots, sums and products that form tn, and
+    // thi already covers the binary64 definition.  A 32-candidate half whose
+    // columns are all such skips its classification (its bits stay zero).
+    // thi = inf gives tn = inf: no skip.
+    const float tn = [&]() {
+        const float nt = 4.0f * (float)nb + 4.0f;  // terms (and additions) in a norm
+        const float g = nt * 0x1p-24f / (1.0f - nt * 0x1p-24f);
+        const float c1 = 1.0f + g + 0x1p-18f, c2 = 1.0f + 2.0f * g + 0x1p-16f;
+        const float sq = sqrtf(L.nqmax[qb]) * c1, st = sqrtf(a.thi) * c1;
+        return ((sq + st) * (sq + st)) * c2;
+    }();
     const BandSink bsink{band_list(a.blist, a.lcap), band_counter(a.bcount), a.lcap, row0, mbase, W};
     const uint32_t nsteps = (c_end - c_begin + G::SC - 1) / G::SC;
     const uint32_t qrows = active ? min(32u, nrows - (uint32_t)(qb * 32)) : 0u;
@@ -391,6 +419,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         const uint32_t cw = c_begin + s * G::SC + cg * 64;
         float xin[2], xout[2];
         uint32_t xid[2];
+        uint32_t live = 0;  // halves to classify
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int cl = cg * 64 + 32 * tt + col;
@@ -405,9 +434,11 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             const bool valid = cw + 32 * tt + col < c_end;
             xin[tt] = valid ? kp * nxt : __builtin_nanf("");
             xout[tt] = valid ? km * nxt : __builtin_nanf("");
+            if (__ballot(!(nxt > tn)) != 0) live |= 1u << tt;  // a column not decided by its norm
         }
-        classify_block(acc, xin, xout, L.qin, L.qout, qb, lane, cw, bsink, [&](int tt) { return xid[tt]; },
-                       L.words + (qb * 32 + (lane & 31)) * 8 + (s % G::SPG) * G::NCG + cg);
+        if (live != 0)
+            classify_block(acc, xin, xout, L.qin, L.qout, qb, lane, cw, live, bsink, [&](int tt) { return xid[tt]; },
+                           L.words + (qb * 32 + (lane & 31)) * 8 + (s % G::SPG) * G::NCG + cg);
     };
     // unit flags: the 4 words of a unit sit in 4 consecutive lanes (e & 7
     // = j, units j 0-3 and 4-7 of a row); the first lane of the unit writes

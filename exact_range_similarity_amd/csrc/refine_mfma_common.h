@@ -1,7 +1,6 @@
-// Device helpers shared by the MFMA refinement kernels (k_refine_mfma.hip,
-// k_refine_staged.hip): operand types, the fp16 split, and the
-// classification of a wave's 32 x 64 block of squared distances into result
-// mask bits and band pairs.
+// Device helpers of the MFMA refinement kernel (k_refine_mfma.hip): operand
+// types, the fp16 split, and the classification of a wave's 32 x 64 block of
+// squared distances into result mask bits and band pairs.
 //
 // Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
 // Similarity Searches", Sec. IV-E (refinement of a group of queries against
@@ -84,11 +83,14 @@ struct BandSink {
 // "In" pairs become mask bits: lane r < 32 of the wave gets row r's 64-bit
 // word, stored to *wdst.  Pairs neither in nor out are appended to the band
 // list for the binary64 re-check; xid(tt) gives the point index of the
-// lane's column (called only for band pairs).
+// lane's column (called only for band pairs).  Only the 32-candidate halves
+// tt with bit tt of live_tt set are classified (wave-uniform): the others
+// are known to hold no neighbour and keep zero bits.
 template <class XidFn>
 __device__ __forceinline__ void classify_block(const floatx16 *acc, const float (&xin)[2], const float (&xout)[2],
                                                const float *qin, const float *qout, int qb, int lane,
-                                               uint32_t cw, const BandSink &bs, XidFn &&xid, uint64_t *wdst)
+                                               uint32_t cw, uint32_t live_tt, const BandSink &bs, XidFn &&xid,
+                                               uint64_t *wdst)
 {
     const int col = lane & 31, hi = lane >> 5;
     const float neg2 = -2.0f;
@@ -110,6 +112,7 @@ __device__ __forceinline__ void classify_block(const floatx16 *acc, const float 
             qi = qin4[g * 2];
             qo = qout4[g * 2];
         }
+        if (!(live_tt & (1u << tt))) return;
         uint64_t bno[4];
         uint64_t anyno = 0;
         static_for(std::make_integer_sequence<int, 4>{}, [&](auto J) {
@@ -171,8 +174,8 @@ __device__ __forceinline__ void classify_block(const floatx16 *acc, const float 
                 }
             }
         };
-        band_tile(a0, 0);
-        band_tile(a1, 1);
+        if (live_tt & 1u) band_tile(a0, 0);
+        if (live_tt & 2u) band_tile(a1, 1);
     }
     if (lane < 32) *wdst = ((uint64_t)(uint32_t)whi << 32) | (uint64_t)(uint32_t)wlo;
 }

@@ -126,3 +126,27 @@ def test_block_prune_lattice_at_eps(m, d):
         for k in KERNELS:
             got, st = _join(X, eps, k)
             assert np.array_equal(got, want), (m, d, eps, k)
+
+
+def test_norm_test_on_clusters_apart_off_the_grid_axes():
+    # Two point families share the grid cells but sit in opposite corners of
+    # them (so their query blocks are pure and the box test keeps them
+    # paired) and 3 apart on a fourth axis: the refinement's norm test
+    # decides their cross products.  Partners of the first family one unit up
+    # on that axis are exactly eps = 1 away; every coordinate is a multiple of
+    # 1/16, so all distances are exact.
+    rng = np.random.default_rng(71)
+    n = 1500
+    cell = rng.integers(0, 8, size=(n, 3)).astype(np.float32)
+    fine = rng.integers(0, 2, size=(n, 3)).astype(np.float32) / 16
+    A = np.zeros((n, 8), np.float32)
+    A[:, :3] = cell + fine
+    B = A.copy()
+    B[:, :3] += np.float32(14 / 16)
+    B[:, 3] = 3.0
+    C = A[: n // 3].copy()
+    C[:, 3] = 1.0
+    X = np.concatenate([A, B, C])
+    X = X[rng.permutation(len(X))]
+    check_against_oracle(X, 1.0, "families apart on a fourth axis")
+    check_against_oracle(X, math.nextafter(1.0, 0.0), "families apart, eps just below 1")
