@@ -110,9 +110,10 @@ __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
     return pos;
 }
 
-// Workgroup per row tile of the batch, wave per row.  The row's unit flags
-// (one per 4 mask words) are read 64 at a time; the words of up to 16
-// flagged units are staged in LDS with their bit prefix and their set bits
+// Workgroup per row tile of the batch, wave per row.  A row's unit flags
+// (one per 4 mask words) are read 256 at a time, four independent loads per
+// lane, and the flagged units are listed in LDS in order; then the words of
+// up to 16 listed units are staged with their bit prefix and their set bits
 // are dealt to the lanes in turn (lane j takes the staged set bits j,
 // j + 64, ...), so only flagged words are read, the pairs of a dense word
 // are written by 64 lanes at once, and each wave's stores are consecutive.
@@ -129,11 +130,13 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                                                 const uint32_t *__restrict__ orig,
                                                 uint32_t *__restrict__ pairs)
 {
+    constexpr uint32_t kChunk = 256;  // unit flags scanned per pass
     __shared__ uint32_t s_pref[kMaxRanges + 1];
     __shared__ uint32_t s_start[kMaxRanges];
     __shared__ uint64_t s_words[4][64];
     __shared__ uint32_t s_widx[4][64];
     __shared__ uint32_t s_before[4][64];
+    __shared__ uint32_t s_units[4][kChunk];
     const uint32_t t = t0 + blockIdx.x;
     const Tile tl = tiles[t];
     const uint32_t A = tl.cell;
@@ -146,6 +149,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     uint64_t *const cw = s_words[wave];
     uint32_t *const ci = s_widx[wave];
     uint32_t *const cb = s_before[wave];
+    uint32_t *const lu = s_units[wave];
     const uint64_t tbase = toff[t] - wbase;
     const uint32_t nunits = (tl.used + 3) / 4;
     const bool al8 = ((uintptr_t)pairs & 7u) == 0;  // a pair in one 8-byte store
@@ -156,18 +160,33 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
         const uint64_t *row = mask + rw;
         const uint8_t *frow = gflag + (rw >> 2);
         uint64_t out = roff[q - row_base];
-        for (uint32_t u0 = 0; u0 < nunits; u0 += 64) {
-            uint64_t nz = __ballot(u0 + lane < nunits && frow[u0 + lane] != 0);
-            while (nz != 0) {
-                const uint32_t cnt = min(16u, (uint32_t)__popcll(nz));
+        for (uint32_t c0 = 0; c0 < nunits; c0 += kChunk) {
+            // the chunk's flags, four independent loads per lane, then the
+            // flagged units listed in order
+            uint8_t f[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t u = c0 + 64 * k + lane;
+                f[k] = u < nunits ? frow[u] : 0;
+            }
+            uint32_t nf = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint64_t nz = __ballot(f[k] != 0);
+                if (f[k] != 0) lu[nf + __popcll(nz & ((1ull << lane) - 1ull))] = c0 + 64 * k + lane;
+                nf += __popcll(nz);
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            for (uint32_t i0 = 0; i0 < nf; i0 += 16) {
+                const uint32_t cnt = min(16u, nf - i0);
                 const uint32_t slot = (uint32_t)lane >> 2;
                 uint64_t m = 0ull;
                 uint32_t wi = 0;
                 if (slot < cnt) {
-                    wi = (u0 + (uint32_t)nth_bit(nz, slot)) * 4 + (lane & 3);
+                    wi = lu[i0 + slot] * 4 + (lane & 3);
                     m = wi < tl.used ? row[wi] : 0ull;
                 }
-                for (uint32_t i = 0; i < cnt; ++i) nz &= nz - 1;
                 const uint32_t pc = __popcll(m);
                 uint32_t inc = pc;
                 for (int o = 1; o < 64; o <<= 1) {
