@@ -76,8 +76,8 @@ struct ersj_index {
 
     // index
     float4 *xs = nullptr;
+    float *xr = nullptr;  // the same rows in sorted order, input dimension order, row-major
     uint32_t *orig = nullptr;
-    int32_t *d_pinv = nullptr;
     int64_t M = 0;
     uint32_t *cell_start = nullptr;
     uint64_t *cell_key = nullptr;
@@ -88,6 +88,7 @@ struct ersj_index {
     bool semi = false;
     int64_t nq = 0;
     float4 *xq = nullptr;
+    float *xqr = nullptr;
     uint32_t *qorig = nullptr;
     int64_t Mq = 0;
     uint32_t *qcell_start = nullptr;
@@ -511,6 +512,7 @@ void release_plan(ersj_index *h)
 // their boxes on the grid axes.
 struct Binned {
     float4 *xs = nullptr;
+    float *xr = nullptr;
     uint32_t *orig = nullptr;
     int64_t M = 0;
     uint32_t *cell_start = nullptr;
@@ -539,6 +541,10 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     HIPC(hipMemcpyAsync(dperm, h->perm.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "perm copy");
     TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
     HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
+    // row-major copy in sorted order for the binary64 re-check, which sums
+    // in the input's dimension order
+    TRY(dalloc(h, &out->xr, (size_t)n * d, "rows"));
+    HIPC(launch_gather_rows(x, ld, out->orig, (uint64_t)n, d, out->xr, s), "row gather kernel");
 
     uint32_t *flags = nullptr;
     uint64_t *cid = nullptr;
@@ -598,6 +604,7 @@ void alias_queries(ersj_index *h)
     h->semi = false;
     h->nq = h->n;
     h->xq = h->xs;
+    h->xqr = h->xr;
     h->qorig = h->orig;
     h->Mq = h->M;
     h->qcell_start = h->cell_start;
@@ -660,14 +667,13 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     Binned b;
     TRY(bin_rows(h, x, n, ld, false, &b, s));
     h->xs = b.xs;
+    h->xr = b.xr;
     h->orig = b.orig;
     h->M = b.M;
     h->cell_start = b.cell_start;
     h->cell_key = b.cell_key;
     h->lo_bits = b.lo_bits;
     h->hi_bits = b.hi_bits;
-    TRY(dalloc(h, &h->d_pinv, (size_t)d, "pinv"));
-    HIPC(hipMemcpyAsync(h->d_pinv, h->pinv.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "pinv copy");
     TRY(sync(s, "build"));
     alias_queries(h);
     thresholds(h);
@@ -687,6 +693,7 @@ int do_queries(ersj_index *h, const float *q, int64_t nq, int64_t ldq, hipStream
     h->semi = true;
     h->nq = nq;
     h->xq = b.xs;
+    h->xqr = b.xr;
     h->qorig = b.orig;
     h->Mq = b.M;
     h->qcell_start = b.cell_start;
@@ -702,6 +709,7 @@ void release_queries(ersj_index *h)
 {
     if (h->semi) {
         dfree(h, h->xq);
+        dfree(h, h->xqr);
         dfree(h, h->qorig);
         dfree(h, h->qcell_start);
         dfree(h, h->qcell_key);
@@ -880,7 +888,7 @@ int ensure_fill_buffers(ersj_index *h)
         TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
         h->rows_cap = h->maxrows;
     }
-    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)kBandLists * kBandStride + 2, "counters"));
+    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)(kBandLists + 2 * kHitSlots) * kBandStride, "counters"));
     if (!h->lpref) TRY(dalloc(h, &h->lpref, (size_t)kBandLists + 3, "band list prefix"));
     if (!h->blist) {
         const uint64_t cap = initial_bcap(h);
@@ -934,9 +942,10 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
         a.tlo = h->tlo16;
         a.thi = h->thi16;
     }
-    const size_t ncount = (size_t)kBandLists * kBandStride + 2;
+    // band sub-list counters, re-check hit slots, skipped-comparison slots
+    const size_t ncount = (size_t)(kBandLists + 2 * kHitSlots) * kBandStride;
     unsigned long long *const hits = h->counters + (size_t)kBandLists * kBandStride;
-    unsigned long long *const skipped = hits + 1;
+    unsigned long long *const skipped = hits + (size_t)kHitSlots * kBandStride;
     a.tbox = h->tbox;
     a.skipped = skipped;
     a.rowcnt = h->rowcnt;
@@ -982,17 +991,22 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     }
     if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
-    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xs, (uint64_t)h->n, h->xq,
-                        (uint64_t)h->nq, h->d, h->d_pinv, h->e64, h->mask, h->gflag, hits, h->rowcnt,
+    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xr, h->xqr, h->d, h->e64,
+                        h->mask, h->gflag, hits, h->rowcnt,
                         h->hrows[b], s),
          "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
     HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
-    uint64_t tot = 0, hs[2] = {0, 0};  // pairs; re-check hits, skipped comparisons
+    uint64_t tot = 0;  // pairs
+    uint64_t hs[2 * kHitSlots * kBandStride];  // re-check hit slots, skipped-comparison slots
     HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(hs, hits, sizeof hs, hipMemcpyDeviceToHost, s), "copy");
     TRY(sync(s, "row count"));
+    for (uint32_t k = 1; k < kHitSlots; ++k) hs[0] += hs[k * kBandStride];
+    uint64_t skip = 0;
+    for (uint32_t k = 0; k < kHitSlots; ++k) skip += hs[(kHitSlots + k) * kBandStride];
+    hs[1] = skip;
     h->ms_expand += timer_stop(h, s);
     h->last_cand = h->hcands[b + 1] - h->hcands[b];
     h->last_bnd = bcount;

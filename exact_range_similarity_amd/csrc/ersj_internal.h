@@ -207,6 +207,11 @@ __device__ __forceinline__ void work_item(uint32_t b, uint32_t ntiles, uint32_t 
 // b % kBandLists, so each sub-list is served by one XCD's L2.
 constexpr uint32_t kBandLists = 256;
 constexpr uint32_t kBandStride = 16;  // u64 words between two counters
+// The re-check's hits and the refinement's skipped comparisons are counted
+// in kHitSlots counters each (workgroup b adds to slot b % kHitSlots,
+// kBandStride words apart), summed on the host: one counter for the whole
+// grid serialised c4's 1.6 M re-check additions.
+constexpr uint32_t kHitSlots = 32;
 
 __device__ __forceinline__ unsigned long long *band_counter(unsigned long long *bcount)
 {
@@ -249,7 +254,7 @@ struct RefineArgs {
     const float4 *cbox;           // MFMA kernel, tbox finite: lo, hi on the grid axes of each
                                   // 64-candidate chunk of each cell's candidate list
     const uint64_t *chunk_base;   // first chunk of each cell
-    unsigned long long *skipped;  // comparisons decided by that box test alone
+    unsigned long long *skipped;  // comparisons decided by that box test alone (kHitSlots slots)
     uint8_t *gflag;               // per 4 mask words (aligned): 1 if any bit is set, else 0
     uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
     uint64_t row_base;            // first query row of the batch
@@ -301,10 +306,11 @@ hipError_t launch_refine_mfma(const RefineArgs &a, bool f16, hipStream_t s);
 // count, lpref[0..kBandLists] = exclusive prefix of the kept counts.
 hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, uint64_t *lpref,
                               uint64_t *out, hipStream_t s);
+// xr, xqr: points and query rows in sorted order, input dimension order,
+// row-major (d floats per row).
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, uint8_t *gflag,
-                          unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
+                          const float *xr, const float *xqr, int32_t d, double e64, uint64_t *mask,
+                          uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s);
 
 

@@ -41,23 +41,23 @@ __global__ __launch_bounds__(kBandLists) void k_band_prefix(const unsigned long 
 // Binary64 squared distance in the input's own dimension order, every
 // operation separately rounded (no contraction): the exact definition the
 // result set is specified by.  Pairs at or below fl(eps*eps) get their bit.
-// Entry i of the kept band pairs lives in sub-list c (lpref[c] <= i <
-// lpref[c+1]) at offset i - lpref[c].
+// Both rows are read from row-major copies in sorted order (a row's d
+// floats are contiguous: a few cache lines per pair).  Entry i of the kept
+// band pairs lives in sub-list c (lpref[c] <= i < lpref[c+1]) at offset
+// i - lpref[c].
 __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t lcap,
                                                  const uint64_t *__restrict__ lpref, uint64_t cnt,
-                                                 const float *__restrict__ xsf, uint64_t n,
-                                                 const float *__restrict__ xqf, uint64_t nqr,
-                                                 int32_t d, const int32_t *__restrict__ pinv,
-                                                 double e64, uint64_t *__restrict__ mask,
+                                                 const float *__restrict__ xr, const float *__restrict__ xqr,
+                                                 int32_t d, double e64, uint64_t *__restrict__ mask,
                                                  uint8_t *__restrict__ gflag,
                                                  unsigned long long *__restrict__ nin,
                                                  uint32_t *__restrict__ rowcnt, uint64_t row_base)
 {
 #pragma clang fp contract(off)
-    __shared__ int32_t sp[kMaxDim];
     __shared__ uint64_t spref[kBandLists + 1];
-    for (int k = threadIdx.x; k < d; k += blockDim.x) sp[k] = pinv[k];
+    __shared__ uint32_t s_hits;
     for (uint32_t k = threadIdx.x; k <= kBandLists; k += blockDim.x) spref[k] = lpref[k];
+    if (threadIdx.x == 0) s_hits = 0;
     __syncthreads();
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     bool hit = false;
@@ -69,11 +69,12 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
             else hi = mid;
         }
         const Boundary e = bl[(uint64_t)lo * lcap + (i - spref[lo])];
+        const float *qa = xqr + (uint64_t)e.q * (uint64_t)d;
+        const float *xb = xr + (uint64_t)e.x * (uint64_t)d;
         double s = 0.0;
         for (int k = 0; k < d; ++k) {
-            const int p = sp[k];
-            const double a = (double)xqf[((uint64_t)(p >> 2) * nqr + e.q) * 4 + (p & 3)];
-            const double b = (double)xsf[((uint64_t)(p >> 2) * n + e.x) * 4 + (p & 3)];
+            const double a = (double)qa[k];
+            const double b = (double)xb[k];
             const double t = a - b;
             const double tt = t * t;
             s = s + tt;
@@ -85,10 +86,13 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
             hit = true;
         }
     }
-    // one counter update per wave
+    // one counter update per workgroup, into its slot
     const uint64_t hits = __ballot(hit);
     if (hits != 0 && (threadIdx.x & 63) == (uint32_t)(__ffsll((unsigned long long)hits) - 1))
-        atomicAdd(nin, (unsigned long long)__popcll(hits));
+        atomicAdd(&s_hits, (uint32_t)__popcll(hits));
+    __syncthreads();
+    if (threadIdx.x == 0 && s_hits != 0)
+        atomicAdd(&nin[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], (unsigned long long)s_hits);
 }
 
 // position of the r-th (0-based) set bit of w; r < popcount(w)
@@ -236,15 +240,14 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 }
 
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float4 *xs, uint64_t n, const float4 *xq, uint64_t nqr, int32_t d,
-                          const int32_t *pinv, double e64, uint64_t *mask, uint8_t *gflag,
-                          unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base, hipStream_t s)
+                          const float *xr, const float *xqr, int32_t d, double e64, uint64_t *mask,
+                          uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
+                          hipStream_t s)
 {
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
-    hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt,
-                       (const float *)xs, n, (const float *)xq, nqr, d, pinv, e64, mask, gflag, nin,
-                       rowcnt, row_base);
+    hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt, xr, xqr,
+                       d, e64, mask, gflag, nin, rowcnt, row_base);
     return hipGetLastError();
 }
 

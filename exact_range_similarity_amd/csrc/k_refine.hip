@@ -208,7 +208,8 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
                 a.gflag[(mbase + (uint64_t)k * tl.words + w0) >> 2] = ((nzb >> lane) & 0xfull) ? 1 : 0;
         }
     }
-    if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
+    if (nskip != 0 && lane == 0)
+        atomicAdd(&a.skipped[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], (unsigned long long)nskip);
     // the rows' neighbour counts (the binary64 re-check adds the band's):
     // the kCW lanes of a query sum their words' counts
     mycnt += __shfl_down(mycnt, 2, kCW);

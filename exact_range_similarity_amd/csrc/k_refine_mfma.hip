@@ -646,7 +646,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
         flush((uint32_t)pend_group);
         zero_groups((uint32_t)pend_group + 1, pend_next);
     }
-    if (nskip != 0 && lane == 0) atomicAdd(a.skipped, (unsigned long long)nskip);
+    if (nskip != 0 && lane == 0)
+        atomicAdd(&a.skipped[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], (unsigned long long)nskip);
     // the rows' neighbour counts (the binary64 re-check adds the band's)
     __syncthreads();
     for (int i = tid; i < (int)nrows; i += 256)
