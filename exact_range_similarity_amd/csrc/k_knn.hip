@@ -48,6 +48,11 @@ struct KnnLds {
     uint32_t before[kWaves][64]; // set bits in the earlier staged words
     uint32_t pref[kMaxRanges + 1];
     uint32_t start[kMaxRanges];
+    // the tile's rows short of k neighbours, appended to the next round's
+    // list with one counter update per workgroup
+    uint32_t nshort;
+    uint32_t soq[kTileRows], snb[kTileRows];
+    double sls[kTileRows];
 };
 
 __device__ __forceinline__ bool key_less(uint64_t ah, uint32_t al, uint64_t bh, uint32_t bl)
@@ -144,6 +149,7 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
     if (threadIdx.x <= kMaxRanges)
         L.pref[threadIdx.x] = threadIdx.x <= nr ? a.rpref[(uint64_t)A * (kMaxRanges + 1) + threadIdx.x] : 0xffffffffu;
     if (threadIdx.x < kMaxRanges) L.start[threadIdx.x] = a.rstart[(uint64_t)A * kMaxRanges + threadIdx.x];
+    if (threadIdx.x == 0) L.nshort = 0;
     __syncthreads();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     uint64_t *const ehi = L.hi[wave];
@@ -253,10 +259,10 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
                 np += __shfl_xor(np, o, 64);
             }
             if (lane == 0) {
-                const uint32_t pos = atomicAdd(a.next_count, 1u);
-                a.next[pos] = oq;
-                a.next_nbrs[pos] = c | (np << 16);  // both below 2^16 (c < k <= 1024)
-                a.next_lsum[pos] = np > 0 ? ls : 0.0;
+                const uint32_t pos = atomicAdd(&L.nshort, 1u);
+                L.soq[pos] = oq;
+                L.snb[pos] = c | (np << 16);  // both below 2^16 (c < k <= 1024)
+                L.sls[pos] = np > 0 ? ls : 0.0;
             }
             continue;
         }
@@ -393,6 +399,18 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
         }
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    __syncthreads();
+    const uint32_t ns = L.nshort;
+    if (ns != 0) {
+        __shared__ uint32_t s_base;
+        if (threadIdx.x == 0) s_base = atomicAdd(a.next_count, ns);
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < ns; i += blockDim.x) {
+            a.next[s_base + i] = L.soq[i];
+            a.next_nbrs[s_base + i] = L.snb[i];
+            a.next_lsum[s_base + i] = L.sls[i];
+        }
     }
 }
 
