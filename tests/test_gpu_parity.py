@@ -266,3 +266,7 @@ def test_stats_are_consistent():
     assert st["total_candidates"] >= total
     assert st["refine_launches"] >= 1 and st["refine_ms"] > 0
     assert sorted(st["index_dims"]) == sorted(set(st["index_dims"]))
+    # counters summed over their per-workgroup slots
+    assert 0 <= st["last_recheck_in"] <= st["last_boundary_pairs"]
+    assert 0 <= st["last_skipped"] <= st["last_batch_candidates"]
+    assert st["skipped_candidates"] == st["last_skipped"]  # one batch
