@@ -79,3 +79,14 @@ def test_query_sets_share_the_structure_of_the_points():
     Q = make_queries("c2", 200, 11, 20000)
     d2 = ((Q[:, None, :].astype(np.float64) - X[None, :, :]) ** 2).sum(-1).min(axis=1)
     assert np.all(d2 < 0.05)
+
+
+def test_smoke_input_calibrates():
+    """The smoke case's epsilon gives queries 0..499 a whole number of
+    neighbours per query (target 32, or a neighbouring target where 32 falls
+    on a tie), and more than one pair per query."""
+    import __graft_entry__ as entry
+    X, eps = entry.smoke_input()
+    colptr, _ = oracle.join_rows(X, eps, np.arange(500))
+    total = int(colptr[-1]) - 500
+    assert total % 500 == 0 and 30 <= total // 500 <= 34
