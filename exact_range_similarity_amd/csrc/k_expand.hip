@@ -114,14 +114,45 @@ __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
     return pos;
 }
 
-// Workgroup per row tile of the batch, wave per row.  A row's unit flags
-// (one per 4 mask words) are read 256 at a time, four independent loads per
-// lane, and the flagged units are listed in LDS in order; then the words of
-// up to 16 listed units are staged with their bit prefix and their set bits
-// are dealt to the lanes in turn (lane j takes the staged set bits j,
-// j + 64, ...), so only flagged words are read, the pairs of a dense word
-// are written by 64 lanes at once, and each wave's stores are consecutive.
-// Pairs come out in candidate order.
+// Workgroup per row tile of the batch, all 256 threads on one pass at a
+// time, so that a tile costs a few memory round trips rather than a few per
+// row.  The tile's unit flags (one byte per 4 mask words; its rows' flag
+// bytes are consecutive, words / 4 per row) are read 4 KiB per pass, four
+// independent loads per thread, and the flagged units are listed in LDS in
+// row-then-unit order.  The listed units are then taken 64 at a time: each
+// thread loads one of their 256 words, a workgroup prefix sum of the words'
+// bit counts places every set bit, and the bits are dealt to the threads in
+// turn (thread i takes bits i, i + 256, ...).  A row's pairs fill its output
+// range in candidate order; its next output position is kept in LDS from one
+// batch of units to the next.
+constexpr uint32_t kFlagPass = 4096;   // flag bytes read per pass
+constexpr uint32_t kUnitBatch = 64;    // listed units expanded per batch (256 words)
+static_assert(kTileRows < 255, "rows of a tile are held in bytes (0xff: no row)");
+
+// Exclusive prefix sum of v over the workgroup's 256 threads in thread
+// order; *total gets the sum.  wtot: 4 words of LDS.  Ends with a barrier.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *wtot, uint32_t *total)
+{
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+    }
+    if (lane == 63) wtot[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t t = wtot[w];
+        before += w < wave ? t : 0u;
+        all += t;
+    }
+    *total = all;
+    return before + inc - v;
+}
+
 __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, uint32_t t0,
                                                 const uint64_t *__restrict__ toff, uint64_t wbase,
                                                 uint64_t row_base, const uint64_t *__restrict__ mask,
@@ -134,98 +165,137 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                                                 const uint32_t *__restrict__ orig,
                                                 uint32_t *__restrict__ pairs)
 {
-    constexpr uint32_t kChunk = 256;  // unit flags scanned per pass
     __shared__ uint32_t s_pref[kMaxRanges + 1];
     __shared__ uint32_t s_start[kMaxRanges];
-    __shared__ uint64_t s_words[4][64];
-    __shared__ uint32_t s_widx[4][64];
-    __shared__ uint32_t s_before[4][64];
-    __shared__ uint32_t s_units[4][kChunk];
+    __shared__ uint16_t s_list[kFlagPass];   // pass-relative byte offsets of flagged units
+    __shared__ uint32_t s_ftot[16];          // flagged bytes per (load k, wave)
+    __shared__ uint32_t s_wtot[4];
+    __shared__ uint64_t s_word[256];
+    __shared__ uint32_t s_excl[256];
+    __shared__ uint32_t s_wi[256];
+    __shared__ uint8_t s_row[256];
+    __shared__ uint64_t s_rpos[kTileRows];   // next output position of each row
+    __shared__ uint64_t s_rbase[kTileRows];  // output position of the batch's bit 0, per row
+    __shared__ uint32_t s_qid[kTileRows];
     const uint32_t t = t0 + blockIdx.x;
     const Tile tl = tiles[t];
     const uint32_t A = tl.cell;
     const uint32_t nr = nrng[A];
-    if (threadIdx.x <= kMaxRanges)
-        s_pref[threadIdx.x] = threadIdx.x <= nr ? rpref[(uint64_t)A * (kMaxRanges + 1) + threadIdx.x] : 0xffffffffu;
-    if (threadIdx.x < kMaxRanges) s_start[threadIdx.x] = rstart[(uint64_t)A * kMaxRanges + threadIdx.x];
-    __syncthreads();
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    uint64_t *const cw = s_words[wave];
-    uint32_t *const ci = s_widx[wave];
-    uint32_t *const cb = s_before[wave];
-    uint32_t *const lu = s_units[wave];
-    const uint64_t tbase = toff[t] - wbase;
-    const uint32_t nunits = (tl.used + 3) / 4;
+    const uint32_t tid = threadIdx.x;
+    if (tid <= kMaxRanges) s_pref[tid] = tid <= nr ? rpref[(uint64_t)A * (kMaxRanges + 1) + tid] : 0xffffffffu;
+    if (tid < kMaxRanges) s_start[tid] = rstart[(uint64_t)A * kMaxRanges + tid];
+    if (tid < tl.nrows) {
+        const uint32_t q = tl.row0 + tid;
+        s_qid[tid] = qorig[q];
+        s_rpos[tid] = roff[q - row_base];
+    }
+    const int wave = tid >> 6, lane = tid & 63;
+    const uint64_t tbase = toff[t] - wbase;         // first word of the tile (a multiple of 8)
+    const uint64_t fb = tbase >> 2;                  // its first flag byte
+    const uint32_t fstride = tl.words >> 2;          // flag bytes per row
+    const uint32_t nunits = (tl.used + 3) >> 2;      // units that hold candidates
+    const uint64_t nbytes = (uint64_t)tl.nrows * fstride;  // below 2^32 (rows <= kTileRows)
+    if (nbytes == 0) return;                           // uniform: no barrier passed yet
+    const uint32_t *gf32 = (const uint32_t *)gflag;  // 4-byte loads from the aligned dword below fb
+    const uint64_t d0 = fb >> 2, d1 = (fb + nbytes + 3) >> 2;
     const bool al8 = ((uintptr_t)pairs & 7u) == 0;  // a pair in one 8-byte store
-    for (uint32_t r = wave; r < tl.nrows; r += 4) {
-        const uint32_t q = tl.row0 + r;
-        const uint32_t qid = qorig[q];
-        const uint64_t rw = tbase + (uint64_t)r * tl.words;  // first word of the row (a multiple of 8)
-        const uint64_t *row = mask + rw;
-        const uint8_t *frow = gflag + (rw >> 2);
-        uint64_t out = roff[q - row_base];
-        for (uint32_t c0 = 0; c0 < nunits; c0 += kChunk) {
-            // the chunk's flags, four independent loads per lane, then the
-            // flagged units listed in order
-            uint8_t f[4];
+    const uint64_t below = (1ull << lane) - 1ull;
+    __syncthreads();
+    for (uint64_t c = d0; c < d1; c += kFlagPass / 4) {
+        // flag dwords c + 256 k + tid; byte b of dword di is tile byte
+        // 4 di + b - fb, listed if non-zero, inside the tile and on a unit
+        // that holds candidates
+        uint32_t f[4], fm[4], cnt[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t u = c0 + 64 * k + lane;
-                f[k] = u < nunits ? frow[u] : 0;
-            }
-            uint32_t nf = 0;
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t di = c + 256 * k + tid;
+            f[k] = di < d1 ? gf32[di] : 0u;
+        }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint64_t nz = __ballot(f[k] != 0);
-                if (f[k] != 0) lu[nf + __popcll(nz & ((1ull << lane) - 1ull))] = c0 + 64 * k + lane;
-                nf += __popcll(nz);
+        for (int k = 0; k < 4; ++k) {
+            uint32_t m = 0;
+            if (f[k] != 0u) {
+                const uint64_t di = c + 256 * k + tid;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int64_t o = (int64_t)(4 * di + b) - (int64_t)fb;
+                    if (((f[k] >> (8 * b)) & 0xffu) != 0u && o >= 0 && (uint64_t)o < nbytes &&
+                        (uint32_t)o % fstride < nunits)
+                        m |= 1u << b;
+                }
             }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            for (uint32_t i0 = 0; i0 < nf; i0 += 16) {
-                const uint32_t cnt = min(16u, nf - i0);
-                const uint32_t slot = (uint32_t)lane >> 2;
-                uint64_t m = 0ull;
-                uint32_t wi = 0;
-                if (slot < cnt) {
-                    wi = lu[i0 + slot] * 4 + (lane & 3);
-                    m = wi < tl.used ? row[wi] : 0ull;
-                }
-                const uint32_t pc = __popcll(m);
-                uint32_t inc = pc;
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t v = __shfl_up(inc, o, 64);
-                    if (lane >= o) inc += v;
-                }
-                const uint32_t total = __shfl(inc, 63, 64);
-                if (total == 0) continue;
-                cw[lane] = m;
-                ci[lane] = wi;
-                cb[lane] = inc - pc;
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                for (uint32_t j = lane; j < total; j += 64) {
-                    int lo = 0, hi = 63;  // the last staged word with cb[word] <= j
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (cb[mid] <= j) lo = mid;
-                        else hi = mid - 1;
-                    }
-                    const uint32_t p = ci[lo] * 64 + nth_bit(cw[lo], j - cb[lo]);
-                    const int g = range_of(s_pref, nr, p);
-                    const uint32_t x = s_start[g] + (p - s_pref[g]);
-                    const uint64_t pos = out + j;
-                    if (al8) {
-                        ((uint2 *)pairs)[pos] = make_uint2(qid, orig[x]);
-                    } else {
-                        pairs[2 * pos] = qid;
-                        pairs[2 * pos + 1] = orig[x];
-                    }
-                }
-                out += total;
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            fm[k] = m;
+            cnt[k] = __popc(m);
+        }
+        // order: load k, then wave, lane, byte; counts 0..4 in three bit planes
+        uint32_t pre[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint64_t b0 = __ballot(cnt[k] & 1u), b1 = __ballot(cnt[k] & 2u), b2 = __ballot(cnt[k] & 4u);
+            pre[k] = __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
+            if (lane == 0) s_ftot[4 * k + wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+        }
+        __syncthreads();
+        uint32_t nl = 0, base[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if (w == wave) base[k] = nl;
+                nl += s_ftot[4 * k + w];
             }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t i = base[k] + pre[k];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (fm[k] & (1u << b)) s_list[i++] = (uint16_t)(4 * (256 * k + tid) + b);
+        }
+        __syncthreads();
+        for (uint32_t i0 = 0; i0 < nl; i0 += kUnitBatch) {
+            // thread tid: word tid & 3 of listed unit i0 + tid / 4
+            const uint32_t e = i0 + (tid >> 2);
+            uint64_t m = 0ull;
+            uint32_t wi = 0, row = 0xffu;
+            if (e < nl) {
+                const uint32_t o = (uint32_t)(4 * c + s_list[e] - fb);
+                row = o / fstride;
+                wi = (o - row * fstride) * 4 + (tid & 3);
+                if (wi < tl.used) m = mask[tbase + (uint64_t)row * tl.words + wi];
+            }
+            const uint32_t pc = __popcll(m);
+            s_row[tid] = (uint8_t)row;
+            uint32_t total;
+            const uint32_t excl = block_excl_scan(pc, s_wtot, &total);
+            const bool first = row != 0xffu && (tid == 0 || s_row[tid - 1] != row);
+            const bool last = row != 0xffu && (tid == 255 || s_row[tid + 1] != row);
+            s_word[tid] = m;
+            s_excl[tid] = excl;
+            s_wi[tid] = wi;
+            if (first) s_rbase[row] = s_rpos[row] - excl;
+            __syncthreads();
+            if (last) s_rpos[row] = s_rbase[row] + excl + pc;
+            for (uint32_t j = tid; j < total; j += 256) {
+                int lo = 0, hi = 255;  // the last slot with s_excl[slot] <= j
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_excl[mid] <= j) lo = mid;
+                    else hi = mid - 1;
+                }
+                const uint32_t p = s_wi[lo] * 64 + nth_bit(s_word[lo], j - s_excl[lo]);
+                const int g = range_of(s_pref, nr, p);
+                const uint32_t x = s_start[g] + (p - s_pref[g]);
+                const uint32_t r = s_row[lo];
+                const uint64_t pos = s_rbase[r] + j;
+                if (al8) {
+                    ((uint2 *)pairs)[pos] = make_uint2(s_qid[r], orig[x]);
+                } else {
+                    pairs[2 * pos] = s_qid[r];
+                    pairs[2 * pos + 1] = orig[x];
+                }
+            }
+            __syncthreads();
         }
     }
 }
