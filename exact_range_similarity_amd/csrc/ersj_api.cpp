@@ -77,6 +77,7 @@ struct ersj_index {
     // index
     float4 *xs = nullptr;
     float *xr = nullptr;  // the same rows in sorted order, input dimension order, row-major
+                          // (stride recheck_stride(d), zero-padded)
     uint32_t *orig = nullptr;
     int64_t M = 0;
     uint32_t *cell_start = nullptr;
@@ -543,8 +544,8 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
     // row-major copy in sorted order for the binary64 re-check, which sums
     // in the input's dimension order
-    TRY(dalloc(h, &out->xr, (size_t)n * d, "rows"));
-    HIPC(launch_gather_rows(x, ld, out->orig, (uint64_t)n, d, out->xr, s), "row gather kernel");
+    TRY(dalloc(h, &out->xr, (size_t)n * recheck_stride(d), "rows"));
+    HIPC(launch_gather_rows(x, ld, out->orig, (uint64_t)n, d, recheck_stride(d), out->xr, s), "row gather kernel");
 
     uint32_t *flags = nullptr;
     uint64_t *cid = nullptr;
@@ -991,7 +992,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     }
     if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
     timer_start(h, s);
-    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xr, h->xqr, h->d, h->e64,
+    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xr, h->xqr, h->d, recheck_stride(h->d), h->e64,
                         h->mask, h->gflag, hits, h->rowcnt,
                         h->hrows[b], s),
          "re-check kernel");
@@ -1477,7 +1478,7 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
         int64_t lq = ldq;
         if (round > 0) {
             TRY(qrows.get(sizeof(float) * (size_t)nq * (size_t)d, "kNN query rows"));
-            HIPC(launch_gather_rows(qsrc, ldq, idx[cur].as<uint32_t>(), (uint64_t)m, d, qrows.as<float>(), s),
+            HIPC(launch_gather_rows(qsrc, ldq, idx[cur].as<uint32_t>(), (uint64_t)m, d, d, qrows.as<float>(), s),
                  "kNN gather kernel");
             qb = qrows.as<float>();
             lq = d;

@@ -291,8 +291,13 @@ struct KnnArgs {
 };
 int knn_max_k();
 hipError_t launch_knn_select(const KnnArgs &a, uint32_t ntiles, hipStream_t s);
+// out row i (stride ldo >= d; columns d .. ldo-1 zero) = q row idx[i]
 hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, uint64_t m, int32_t d,
-                              float *out, hipStream_t s);
+                              int32_t ldo, float *out, hipStream_t s);
+
+// row stride of the row-major copies read by the re-check: d rounded up to
+// four floats, so that a row is read in 16-byte pieces
+inline int32_t recheck_stride(int32_t d) { return (d + 3) & ~3; }
 
 // k_refine_mfma.hip: query blocks of 32 rows per work item (4, 2 or 1)
 int refine_mfma_qblocks(int nb);
@@ -309,7 +314,7 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 // xr, xqr: points and query rows in sorted order, input dimension order,
 // row-major (d floats per row).
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float *xr, const float *xqr, int32_t d, double e64, uint64_t *mask,
+                          const float *xr, const float *xqr, int32_t d, int32_t ldr, double e64, uint64_t *mask,
                           uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s);
 

@@ -41,14 +41,15 @@ __global__ __launch_bounds__(kBandLists) void k_band_prefix(const unsigned long 
 // Binary64 squared distance in the input's own dimension order, every
 // operation separately rounded (no contraction): the exact definition the
 // result set is specified by.  Pairs at or below fl(eps*eps) get their bit.
-// Both rows are read from row-major copies in sorted order (a row's d
-// floats are contiguous: a few cache lines per pair).  Entry i of the kept
+// Both rows are read from row-major copies in sorted order, rows ldr
+// floats apart (ldr: d rounded up to 4), in 16-byte pieces: a row's d floats
+// are contiguous, a few cache lines and d / 4 loads per pair.  Entry i of the kept
 // band pairs lives in sub-list c (lpref[c] <= i < lpref[c+1]) at offset
 // i - lpref[c].
 __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t lcap,
                                                  const uint64_t *__restrict__ lpref, uint64_t cnt,
                                                  const float *__restrict__ xr, const float *__restrict__ xqr,
-                                                 int32_t d, double e64, uint64_t *__restrict__ mask,
+                                                 int32_t d, int32_t ldr, double e64, uint64_t *__restrict__ mask,
                                                  uint8_t *__restrict__ gflag,
                                                  unsigned long long *__restrict__ nin,
                                                  uint32_t *__restrict__ rowcnt, uint64_t row_base)
@@ -69,15 +70,20 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
             else hi = mid;
         }
         const Boundary e = bl[(uint64_t)lo * lcap + (i - spref[lo])];
-        const float *qa = xqr + (uint64_t)e.q * (uint64_t)d;
-        const float *xb = xr + (uint64_t)e.x * (uint64_t)d;
+        const float4 *qa = (const float4 *)(xqr + (uint64_t)e.q * (uint64_t)ldr);
+        const float4 *xb = (const float4 *)(xr + (uint64_t)e.x * (uint64_t)ldr);
         double s = 0.0;
-        for (int k = 0; k < d; ++k) {
-            const double a = (double)qa[k];
-            const double b = (double)xb[k];
-            const double t = a - b;
-            const double tt = t * t;
-            s = s + tt;
+        for (int k4 = 0; 4 * k4 < d; ++k4) {
+            const float4 qv = qa[k4], xv = xb[k4];
+            const float qc[4] = {qv.x, qv.y, qv.z, qv.w}, xc[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (4 * k4 + c < d) {
+                    const double t = (double)qc[c] - (double)xc[c];
+                    const double tt = t * t;
+                    s = s + tt;
+                }
+            }
         }
         if (s <= e64) {
             atomicOr((unsigned long long *)&mask[e.bit >> 6], 1ull << (e.bit & 63));
@@ -310,14 +316,15 @@ hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, u
 }
 
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
-                          const float *xr, const float *xqr, int32_t d, double e64, uint64_t *mask,
+                          const float *xr, const float *xqr, int32_t d, int32_t ldr, double e64, uint64_t *mask,
                           uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s)
 {
+    if (ldr < d || (ldr & 3) != 0) return hipErrorInvalidValue;
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
     hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt, xr, xqr,
-                       d, e64, mask, gflag, nin, rowcnt, row_base);
+                       d, ldr, e64, mask, gflag, nin, rowcnt, row_base);
     return hipGetLastError();
 }
 

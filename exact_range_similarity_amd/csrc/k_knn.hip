@@ -417,12 +417,12 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
 // rows idx[i] of a row-major array, packed: out[i * d + j] = q[idx[i] * ldq + j]
 __global__ __launch_bounds__(256) void k_gather_rows(const float *__restrict__ q, int64_t ldq,
                                                      const uint32_t *__restrict__ idx, uint64_t m,
-                                                     int32_t d, float *__restrict__ out)
+                                                     int32_t d, int32_t ldo, float *__restrict__ out)
 {
     const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= m * (uint64_t)d) return;
-    const uint64_t i = e / (uint64_t)d, j = e - i * (uint64_t)d;
-    out[e] = q[(uint64_t)idx[i] * ldq + j];
+    if (e >= m * (uint64_t)ldo) return;
+    const uint64_t i = e / (uint64_t)ldo, j = e - i * (uint64_t)ldo;
+    out[e] = j < (uint64_t)d ? q[(uint64_t)idx[i] * ldq + j] : 0.0f;
 }
 
 }  // namespace
@@ -437,13 +437,14 @@ hipError_t launch_knn_select(const KnnArgs &a, uint32_t ntiles, hipStream_t s)
 }
 
 hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, uint64_t m, int32_t d,
-                              float *out, hipStream_t s)
+                              int32_t ldo, float *out, hipStream_t s)
 {
-    const uint64_t total = m * (uint64_t)d;
+    if (ldo < d) return hipErrorInvalidValue;
+    const uint64_t total = m * (uint64_t)ldo;
     if (total == 0) return hipSuccess;
     const uint64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)blocks), dim3(256), 0, s, q, ldq, idx, m, d, out);
+    hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)blocks), dim3(256), 0, s, q, ldq, idx, m, d, ldo, out);
     return hipGetLastError();
 }
 
