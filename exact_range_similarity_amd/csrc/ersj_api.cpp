@@ -1503,10 +1503,9 @@ int ersj_knn(const float *d_x, int64_t n, int32_t d, int64_t ld, const float *d_
         a.orig = h->orig;
         a.qorig = h->qorig;
         a.qmap = round > 0 ? idx[cur].as<uint32_t>() : nullptr;
-        a.qbase = qb;
-        a.ldq = lq;
-        a.x = d_x;
-        a.ld = ld;
+        a.xr = h->xr;
+        a.xqr = h->xqr;
+        a.ldr = recheck_stride(d);
         a.d = d;
         a.k = (uint32_t)k;
         a.e64 = h->e64;

@@ -273,12 +273,11 @@ struct KnnArgs {
     const uint32_t *rowcnt;      // neighbours per row of the batch
     const uint32_t *rpref, *rstart, *nrng;
     const uint32_t *orig;        // sorted point -> input row
-    const uint32_t *qorig;       // index-order query row -> row of qbase
-    const uint32_t *qmap;        // row of qbase -> query id of the search (NULL: identity)
-    const float *qbase;          // the round's query rows, row-major
-    int64_t ldq;
-    const float *x;              // the points, row-major, input dimension order
-    int64_t ld;
+    const uint32_t *qorig;       // index-order query row -> row of the round's query array
+    const uint32_t *qmap;        // row of the round's query array -> query id of the search (NULL: identity)
+    const float *xr;             // the points in sorted order, row-major, input dimension order
+    const float *xqr;            // the round's queries likewise (sorted query order)
+    int32_t ldr;                 // row stride of both: recheck_stride(d)
     int32_t d;
     uint32_t k;
     double e64;                  // the round's fl(eps^2)

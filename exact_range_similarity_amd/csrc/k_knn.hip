@@ -100,15 +100,24 @@ __device__ void wave_bitonic(uint64_t *hi, uint32_t *lo, int S, int lane)
 
 // Canonical D64 of two rows in the input's dimension order: each difference,
 // square and sum rounded on its own (the pragma sits in this body because a
-// lambda body does not take it from the enclosing function).
-__device__ __forceinline__ double canonical_d64(const float *__restrict__ q, const float *__restrict__ x, int d)
+// lambda body does not take it from the enclosing function).  The rows are
+// 16-byte aligned and zero-padded to a multiple of four floats; only the
+// first d are summed.
+__device__ __forceinline__ double canonical_d64(const float4 *__restrict__ q, const float4 *__restrict__ x, int d)
 {
 #pragma clang fp contract(off)
     double s = 0.0;
-    for (int j = 0; j < d; ++j) {
-        const double u = (double)q[j] - (double)x[j];
-        const double uu = u * u;
-        s = s + uu;
+    for (int j4 = 0; 4 * j4 < d; ++j4) {
+        const float4 qv = q[j4], xv = x[j4];
+        const float qc[4] = {qv.x, qv.y, qv.z, qv.w}, xc[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (4 * j4 + c < d) {
+                const double u = (double)qc[c] - (double)xc[c];
+                const double uu = u * u;
+                s = s + uu;
+            }
+        }
     }
     return s;
 }
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
         const uint32_t c = a.rowcnt[q - a.row_base];
         const uint32_t qid = a.qorig[q];                   // row of the round's query array
         const uint32_t oq = a.qmap ? a.qmap[qid] : qid;    // query id of the whole search
-        const float *qrow = a.qbase + (uint64_t)qid * a.ldq;
+        const float4 *qrow = (const float4 *)(a.xqr + (uint64_t)q * a.ldr);
         const uint64_t *row = a.mask + tbase + (uint64_t)r * tl.words;
         const uint8_t *frow = a.gflag + ((tbase + (uint64_t)r * tl.words) >> 2);
 
@@ -220,8 +229,9 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
                             }
                             const uint32_t p = ci[lo] * 64 + nth_set_bit(cw[lo], j - cb[lo]);
                             const int g = range_of(L.pref, nr, p);
-                            const uint32_t pid = a.orig[L.start[g] + (p - L.pref[g])];
-                            const double s = canonical_d64(qrow, a.x + (uint64_t)pid * a.ld, d);
+                            const uint32_t sx = L.start[g] + (p - L.pref[g]);  // sorted point
+                            const uint32_t pid = a.orig[sx];
+                            const double s = canonical_d64(qrow, (const float4 *)(a.xr + (uint64_t)sx * a.ldr), d);
                             kh = (uint64_t)__double_as_longlong(s);
                             kl = pid;
                         }
