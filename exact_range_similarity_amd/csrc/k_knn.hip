@@ -277,65 +277,102 @@ __global__ __launch_bounds__(256) void k_knn_select(KnnArgs a)
             continue;
         }
         uint32_t nsel = 0;
-        if (c <= (uint32_t)kCap) {
-            for_each([&](bool v, uint64_t kh, uint32_t kl) { append(v, kh, kl, nsel); });
-        } else {
-            // The bucket of hist holding rank (0-based): its index, the count
-            // in the buckets before it, and that count plus its own.
-            auto pick = [&](uint32_t rank, uint32_t &dig, uint32_t &before, uint32_t &through)
-                            __attribute__((always_inline)) {
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                uint32_t h4[4], s4 = 0;
+        // The bucket of hist holding rank (0-based): its index, the count
+        // in the buckets before it, and that count plus its own.
+        auto pick = [&](uint32_t rank, uint32_t &dig, uint32_t &before, uint32_t &through)
+                        __attribute__((always_inline)) {
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            uint32_t h4[4], s4 = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h4[j] = hist[4 * lane + j];
+                s4 += h4[j];
+            }
+            uint32_t inc = s4;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t v = __shfl_up(inc, o, 64);
+                if (lane >= o) inc += v;
+            }
+            const uint32_t exc = inc - s4;
+            const bool mine = exc <= rank && rank < inc;
+            const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
+            uint32_t dg = 0, bf = exc, th = exc;
+            if (mine) {
+                uint32_t run = exc;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    h4[j] = hist[4 * lane + j];
-                    s4 += h4[j];
-                }
-                uint32_t inc = s4;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const uint32_t v = __shfl_up(inc, o, 64);
-                    if (lane >= o) inc += v;
-                }
-                const uint32_t exc = inc - s4;
-                const bool mine = exc <= rank && rank < inc;
-                const int owner = __ffsll((unsigned long long)__ballot(mine)) - 1;
-                uint32_t dg = 0, bf = exc, th = exc;
-                if (mine) {
-                    uint32_t run = exc;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (rank >= run && rank < run + h4[j]) {
-                            dg = 4 * lane + j;
-                            bf = run;
-                            th = run + h4[j];
-                        }
-                        run += h4[j];
+                    if (rank >= run && rank < run + h4[j]) {
+                        dg = 4 * lane + j;
+                        bf = run;
+                        th = run + h4[j];
                     }
+                    run += h4[j];
                 }
-                dig = __shfl(dg, owner, 64);
-                before = __shfl(bf, owner, 64);
-                through = __shfl(th, owner, 64);
-            };
-            auto clear_hist = [&]() __attribute__((always_inline)) {
-                for (int i = lane; i < 256; i += 64) hist[i] = 0;
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            };
+            }
+            dig = __shfl(dg, owner, 64);
+            before = __shfl(bf, owner, 64);
+            through = __shfl(th, owner, 64);
+        };
+        auto clear_hist = [&]() __attribute__((always_inline)) {
+            for (int i = lane; i < 256; i += 64) hist[i] = 0;
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        };
+        // value buckets: u = 256 D64 / E64 is monotone in D64 and, with
+        // every neighbour at D64 <= E64, within [0, 256]; keys of equal D64
+        // share a bucket
+        const bool bucketed = a.e64 > 0.0 && a.e64 <= 1.0e300;
+        const double sc = bucketed ? 256.0 / a.e64 : 0.0;
+        auto ubin = [&](uint64_t kh, double &u) __attribute__((always_inline)) {
+            u = __longlong_as_double((long long)kh) * sc;
+            return u >= 255.0 ? 255u : (uint32_t)u;
+        };
+        if (c <= (uint32_t)kCap) {
+            // all keys into LDS; with more than 2k of them, a histogram taken
+            // on the way finds the bucket prefix that holds the k smallest,
+            // and only that prefix is kept for the sort
+            const bool cut = bucketed && c > 2 * k;
+            if (cut) clear_hist();
+            for_each([&](bool v, uint64_t kh, uint32_t kl) {
+                append(v, kh, kl, nsel);
+                double u;
+                if (cut && v) atomicAdd(&hist[ubin(kh, u)], 1u);
+            });
+            if (cut) {
+                uint32_t b0, before0, through0;
+                pick(k - 1, b0, before0, through0);
+                // in-place compaction in order: a chunk is read before it is
+                // written, and writes land at or below the chunk's start
+                const uint32_t ntot = min(nsel, (uint32_t)kCap);
+                uint32_t m = 0;
+                for (uint32_t j0 = 0; j0 < ntot; j0 += 64) {
+                    const uint32_t j = j0 + lane;
+                    uint64_t kh = 0;
+                    uint32_t kl = 0;
+                    bool keep = false;
+                    if (j < ntot) {
+                        kh = ehi[j];
+                        kl = elo[j];
+                        double u;
+                        keep = ubin(kh, u) <= b0;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                    append(keep, kh, kl, m);
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                }
+                nsel = m;
+            }
+        } else {
             bool done = false;
-            // Value buckets: u = 256 D64 / E64 is monotone in D64 and, with
-            // every neighbour at D64 <= E64, within [0, 256]; keys of equal
-            // D64 share a bucket.  Usually one counting pass finds a bucket
-            // prefix holding the k smallest keys and at most kCap keys in
-            // all, and a second pass gathers it; a crowded bucket is split
-            // once more into 256 sub-buckets.
-            if (a.e64 > 0.0 && a.e64 <= 1.0e300) {
-                const double sc = 256.0 / a.e64;
-                auto ubin = [&](uint64_t kh, double &u) __attribute__((always_inline)) {
-                    u = __longlong_as_double((long long)kh) * sc;
-                    return u >= 255.0 ? 255u : (uint32_t)u;
-                };
+            // Usually one counting pass over the value buckets finds a
+            // bucket prefix holding the k smallest keys and at most kCap
+            // keys in all, and a second pass gathers it; a crowded bucket is
+            // split once more into 256 sub-buckets.
+            if (bucketed) {
                 auto sub = [&](double u, uint32_t b0) __attribute__((always_inline)) {
                     const double v = (u - (double)b0) * 256.0;
                     return v >= 255.0 ? 255u : (uint32_t)v;
