@@ -5,7 +5,8 @@ the same order and the same binary64 D64 values.
 Cases: random and clustered data over several rounds (adaptive and fixed
 growth), ties (integer lattices, duplicated points), query sets distinct from
 the points (cell centres, queries far outside the data), rows with more than
-1024 neighbours (the radix-select path), the largest k, k = n, an infinite
+1024 neighbours (the radix-select path), rows cut to the bucket prefix
+holding their k smallest keys, the largest k, k = n, an infinite
 first radius, and both refinement kernels.
 """
 import math
@@ -140,6 +141,18 @@ def test_large_rows_through_each_narrowing_level():
     Y = np.concatenate([rng.random((500, 3), dtype=np.float32),
                         np.repeat(np.float32([[0.5, 0.5, 0.5]]), 3000, axis=0)])
     check(Y, 700, 0.2, rows=np.arange(0, 3500, 53), label="tied bucket")
+
+
+def test_rows_cut_to_their_bucket_prefix_before_the_sort():
+    # uniform 3-D points: a first radius giving each row a few hundred
+    # neighbours, more than 2k of them but at most the 1024 keys a wave
+    # holds, so the keys are cut to the value-bucket prefix holding the k
+    # smallest before the sort (58%, 86% and 67% of the sampled rows)
+    rng = np.random.default_rng(75)
+    X = rng.random((20000, 3), dtype=np.float32)
+    check(X, 100, 0.14, rows=np.arange(0, 20000, 37), label="cut, k = 100")
+    check(X, 150, 0.19, rows=np.arange(0, 20000, 41), label="cut, k = 150")
+    check(X, 128, 0.16, rows=np.arange(0, 20000, 43), label="cut, k = 128")
 
 
 def test_bad_arguments_raise():
