@@ -23,8 +23,10 @@
 // the next radius (a count growing like radius^m).
 //
 // Workgroup per row tile, wave per row.  A row with at most kCap neighbours
-// gathers their keys into the wave's LDS area and sorts them (bitonic).  A
-// longer row first narrows the keys with a histogram of D64 / E64 (one or
+// gathers their keys into the wave's LDS area and sorts them (bitonic); with
+// more than 2k of them, a histogram of D64 / E64 taken while they are
+// gathered picks the bucket prefix holding the k smallest, and only that
+// prefix is sorted.  A longer row first narrows the keys with a histogram of D64 / E64 (one or
 // two counting passes, then a gathering pass of at most kCap keys); when
 // ties crowd a bucket, or the radius is infinite, an exact radix select over
 // 8-bit digits of the key (twelve passes) finds the k-th smallest key and
