@@ -173,6 +173,36 @@ def test_multi_batch_equals_single_batch():
     assert np.array_equal(ref, np.sort(keys_of(want)))
 
 
+def test_pairs_buffer_aligned_to_four_bytes_only():
+    # the output starts one int32 into its allocation: pairs are stored as
+    # two 4-byte words instead of one 8-byte word; the word before the
+    # output and the one after it stay untouched
+    X = make_config("c2", 6000)
+    eps, _, _ = oracle.calibrate_eps(X, 600, 64)
+    xt = torch.from_numpy(X).cuda()
+    h = ersj.build_index(xt, eps)
+    try:
+        ersj.count_pass(h)
+        nb = ersj.plan_batches(h, 0)
+        assert nb == 1
+        try:
+            m = ersj.fill_pass(h, 0, None, 0)
+        except ersj.ErsjError as e:
+            m = e.required
+        buf = torch.full((2 * m + 2,), -7, dtype=torch.int32, device="cuda")
+        view = buf[1:2 * m + 1]
+        assert view.data_ptr() % 8 == 4
+        assert ersj.fill_pass(h, 0, view, m) == m
+        torch.cuda.synchronize()
+        out = buf.cpu().numpy()
+    finally:
+        h.free()
+    assert out[0] == -7 and out[-1] == -7
+    got = out[1:-1].view(np.uint32).reshape(m, 2)
+    say(f"[gpu] 4-byte aligned output: {m} pairs")
+    assert_same_pairs(X, eps, got, oracle.selfjoin_pairs(X, eps), "4-byte aligned output")
+
+
 def test_capacity_and_budget_errors():
     rng = np.random.default_rng(9)
     X = rng.random((4000, 8), dtype=np.float32)
