@@ -583,11 +583,18 @@ __global__ __launch_bounds__(256) void k_chunk_boxes(const uint64_t *__restrict_
     const uint64_t ch = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (ch >= nchunks) return;  // whole wave
-    int64_t lo = 0, hi = M - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (base[mid] <= ch) lo = mid;
-        else hi = mid - 1;
+    // the last A in [lo, lo + len) with base[A] <= ch (base[lo] <= ch holds
+    // throughout): each round the 64 lanes test evenly spaced cells and the
+    // last one that passes starts the next, 64 times shorter, interval
+    int64_t lo = 0, len = M;
+    while (len > 1) {
+        const int64_t step = (len + 63) / 64;
+        const int64_t j = lo + (int64_t)lane * step;
+        const uint64_t b = __ballot(j < lo + len && base[j] <= ch);
+        const int64_t t = 63 - __clzll((long long)b);  // lane 0 always passes
+        const int64_t nlo = lo + t * step;
+        len = min(step, lo + len - nlo);
+        lo = nlo;
     }
     const int64_t A = lo;
     const uint32_t *pref = rpref + (uint64_t)A * (kMaxRanges + 1);
