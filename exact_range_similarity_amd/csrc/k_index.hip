@@ -473,15 +473,23 @@ __device__ __forceinline__ int64_t find_key(const uint64_t *__restrict__ k, int6
 // cells are sorted by index and runs of consecutive cells are merged into one
 // contiguous candidate range.  A query cell with no kept cell gets one empty
 // range (U = 0).
-__global__ __launch_bounds__(kBlock) void k_stencil(CellSet home, CellSet target, GridParams gp,
-                                                    double prune_e2, uint32_t *__restrict__ rstart,
-                                                    uint32_t *__restrict__ rpref,
-                                                    uint32_t *__restrict__ nrng,
-                                                    uint32_t *__restrict__ tiles_per_cell,
-                                                    unsigned int *__restrict__ umax)
+// A wave per home cell: lane s takes stencil offset s (and s + 64, ...), so
+// the binary searches for the neighbour keys run side by side; the kept
+// cells are listed in LDS and one lane sorts and merges them.
+__global__ __launch_bounds__(256) void k_stencil(CellSet home, CellSet target, GridParams gp,
+                                                 double prune_e2, uint32_t *__restrict__ rstart,
+                                                 uint32_t *__restrict__ rpref,
+                                                 uint32_t *__restrict__ nrng,
+                                                 uint32_t *__restrict__ tiles_per_cell,
+                                                 unsigned int *__restrict__ umax)
 {
-    const int64_t A = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (A >= home.M) return;
+    __shared__ uint32_t s_kept[4][kMaxRanges];
+    __shared__ uint32_t s_rs[4][kMaxRanges];
+    __shared__ uint32_t s_rp[4][kMaxRanges + 1];
+    __shared__ uint32_t s_nr[4];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t A = (int64_t)blockIdx.x * 4 + wave;
+    if (A >= home.M) return;  // whole wave; no workgroup barrier follows
     const uint64_t key = home.key[A];
     int64_t c[3];
     double alo[3], ahi[3];
@@ -490,72 +498,94 @@ __global__ __launch_bounds__(kBlock) void k_stencil(CellSet home, CellSet target
         alo[a] = (double)ord2f(home.lo_bits[A * 3 + a]);
         ahi[a] = (double)ord2f(home.hi_bits[A * 3 + a]);
     }
-    uint32_t kept[kMaxRanges];
-    int nk = 0;
+    uint32_t *const kept = s_kept[wave];
+    uint32_t nk = 0;
     const int R = gp.reach, span = 2 * gp.reach + 1;
     const int nst = span * span * span;
-    for (int s = 0; s < nst; ++s) {
-        const int64_t dlt[3] = {s % span - R, (s / span) % span - R, s / (span * span) - R};
-        uint64_t nkey = 0;
-        bool ok = true;
-        for (int a = 0; a < 3; ++a) {
-            const int64_t v = c[a] + dlt[a];
-            // stored coordinates run 0 .. G + 1 on a grid axis, 0 elsewhere
-            const int64_t G = a < gp.ndim ? (int64_t)gp.G[a] + 2 : 1;
-            if (v < 0 || v >= G) ok = false;
-            else nkey |= spread3((uint64_t)v) << a;
-        }
-        if (!ok) continue;
-        const int64_t B = find_key(target.key, target.M, nkey);
-        if (B < 0) continue;
-        double dl2 = 0.0;
-        for (int a = 0; a < 3; ++a) {
-            const double blo = (double)ord2f(target.lo_bits[B * 3 + a]);
-            const double bhi = (double)ord2f(target.hi_bits[B * 3 + a]);
-            double gap = 0.0;
-            if (blo > ahi[a]) gap = blo - ahi[a];
-            else if (alo[a] > bhi) gap = alo[a] - bhi;
-            dl2 += gap * gap;
-        }
-        if (dl2 > prune_e2) continue;
-        kept[nk++] = (uint32_t)B;
-    }
-    for (int i = 1; i < nk; ++i) {
-        const uint32_t v = kept[i];
-        int j = i - 1;
-        while (j >= 0 && kept[j] > v) {
-            kept[j + 1] = kept[j];
-            --j;
-        }
-        kept[j + 1] = v;
-    }
-    uint32_t nr = 0, U = 0;
-    uint32_t cur_start = 0, cur_len = 0;
-    for (int i = 0; i < nk; ++i) {
-        const uint32_t st = target.start[kept[i]], len = target.start[kept[i] + 1] - st;
-        if (i > 0 && kept[i] == kept[i - 1] + 1) {
-            cur_len += len;
-        } else {
-            if (i > 0) {
-                rstart[A * kMaxRanges + nr] = cur_start;
-                rpref[A * (kMaxRanges + 1) + nr] = U;
-                U += cur_len;
-                ++nr;
+    for (int s0 = 0; s0 < nst; s0 += 64) {
+        const int s = s0 + lane;
+        bool keep = false;
+        uint32_t Bk = 0;
+        if (s < nst) {
+            const int64_t dlt[3] = {s % span - R, (s / span) % span - R, s / (span * span) - R};
+            uint64_t nkey = 0;
+            bool ok = true;
+            for (int a = 0; a < 3; ++a) {
+                const int64_t v = c[a] + dlt[a];
+                // stored coordinates run 0 .. G + 1 on a grid axis, 0 elsewhere
+                const int64_t G = a < gp.ndim ? (int64_t)gp.G[a] + 2 : 1;
+                if (v < 0 || v >= G) ok = false;
+                else nkey |= spread3((uint64_t)v) << a;
             }
-            cur_start = st;
-            cur_len = len;
+            const int64_t B = ok ? find_key(target.key, target.M, nkey) : -1;
+            if (B >= 0) {
+                double dl2 = 0.0;
+                for (int a = 0; a < 3; ++a) {
+                    const double blo = (double)ord2f(target.lo_bits[B * 3 + a]);
+                    const double bhi = (double)ord2f(target.hi_bits[B * 3 + a]);
+                    double gap = 0.0;
+                    if (blo > ahi[a]) gap = blo - ahi[a];
+                    else if (alo[a] > bhi) gap = alo[a] - bhi;
+                    dl2 += gap * gap;
+                }
+                keep = !(dl2 > prune_e2);
+                Bk = (uint32_t)B;
+            }
         }
+        const uint64_t bk = __ballot(keep);
+        if (keep) kept[nk + __popcll(bk & ((1ull << lane) - 1ull))] = Bk;
+        nk += __popcll(bk);
     }
-    rstart[A * kMaxRanges + nr] = cur_start;
-    rpref[A * (kMaxRanges + 1) + nr] = U;
-    U += cur_len;
-    ++nr;
-    for (int g = nr; g <= kMaxRanges; ++g) rpref[A * (kMaxRanges + 1) + g] = U;
-    for (int g = nr; g < kMaxRanges; ++g) rstart[A * kMaxRanges + g] = 0;
-    nrng[A] = nr;
-    const uint32_t sz = home.start[A + 1] - home.start[A];
-    tiles_per_cell[A] = (sz + kTileRows - 1) / kTileRows;
-    atomicMax(umax, U);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint32_t *const rs = s_rs[wave];
+    uint32_t *const rp = s_rp[wave];
+    if (lane == 0) {
+        for (uint32_t i = 1; i < nk; ++i) {
+            const uint32_t v = kept[i];
+            int j = (int)i - 1;
+            while (j >= 0 && kept[j] > v) {
+                kept[j + 1] = kept[j];
+                --j;
+            }
+            kept[j + 1] = v;
+        }
+        uint32_t nr = 0, U = 0;
+        uint32_t cur_start = 0, cur_len = 0;
+        for (uint32_t i = 0; i < nk; ++i) {
+            const uint32_t st = target.start[kept[i]], len = target.start[kept[i] + 1] - st;
+            if (i > 0 && kept[i] == kept[i - 1] + 1) {
+                cur_len += len;
+            } else {
+                if (i > 0) {
+                    rs[nr] = cur_start;
+                    rp[nr] = U;
+                    U += cur_len;
+                    ++nr;
+                }
+                cur_start = st;
+                cur_len = len;
+            }
+        }
+        rs[nr] = cur_start;
+        rp[nr] = U;
+        U += cur_len;
+        ++nr;
+        rp[nr] = U;  // nr <= kMaxRanges
+        s_nr[wave] = nr;
+        nrng[A] = nr;
+        const uint32_t sz = home.start[A + 1] - home.start[A];
+        tiles_per_cell[A] = (sz + kTileRows - 1) / kTileRows;
+        atomicMax(umax, U);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const uint32_t nr = s_nr[wave];
+    const uint32_t U = rp[nr];
+    for (int g = lane; g <= kMaxRanges; g += 64) {
+        rpref[A * (kMaxRanges + 1) + g] = (uint32_t)g < nr ? rp[g] : U;
+        if (g < kMaxRanges) rstart[A * kMaxRanges + g] = (uint32_t)g < nr ? rs[g] : 0u;
+    }
 }
 
 // ----------------------------------------------------------------- tiles --
@@ -859,7 +889,8 @@ hipError_t launch_stencil(const CellSet &home, const CellSet &target, const Grid
 {
     hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(kBlock), 0, s, umax, 0u, 1);
     if (home.M == 0) return hipGetLastError();
-    hipLaunchKernelGGL(k_stencil, dim3(grid_for(home.M)), dim3(kBlock), 0, s, home, target, gp, prune_e2,
+    if ((home.M + 3) / 4 > 0x7fffffffll) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_stencil, dim3((unsigned)((home.M + 3) / 4)), dim3(256), 0, s, home, target, gp, prune_e2,
                        rstart, rpref, nrng, tiles_per_cell, umax);
     return hipGetLastError();
 }
