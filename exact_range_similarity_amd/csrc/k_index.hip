@@ -404,42 +404,93 @@ __global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restr
     if (i == n - 1) cell_start[cid[n]] = (uint32_t)n;
 }
 
-constexpr int kAabbChunk = 64;
+constexpr int kAabbSteps = 8;  // 64-point steps per wave
 
+// A wave per 512 consecutive sorted points, 64 at a time (coalesced loads).
+// While a step's 64 points share the running cell, each lane keeps its own
+// bounds; when the cell changes the wave reduces them and one lane merges
+// them into the cell's box by atomic min/max.  A step that straddles a cell
+// boundary (a few per cell) merges every point on its own.
 __global__ __launch_bounds__(kBlock) void k_cell_aabb(const float4 *__restrict__ xs,
                                                       const uint64_t *__restrict__ cid, int64_t n,
                                                       uint32_t *__restrict__ lo_bits,
                                                       uint32_t *__restrict__ hi_bits)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t i0 = c * kAabbChunk;
-    if (i0 >= n) return;
-    const int64_t i1 = i0 + kAabbChunk < n ? i0 + kAabbChunk : n;
-    int64_t cur = -1;
+    const int lane = threadIdx.x & 63;
+    const int64_t i0 = ((int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6)) * (64 * kAabbSteps);
+    if (i0 >= n) return;  // whole wave
+    int64_t cur = -1;     // wave-uniform
     uint32_t lo[3], hi[3];
-    for (int64_t i = i0; i <= i1; ++i) {
-        const int64_t cell = i < i1 ? (int64_t)cid[i + 1] - 1 : -2;
-        if (cell != cur) {
-            if (cur >= 0) {
+    auto reset = [&]() {
+        for (int a = 0; a < 3; ++a) {
+            lo[a] = 0xffffffffu;
+            hi[a] = 0u;
+        }
+    };
+    auto flush = [&]() {
+        for (int a = 0; a < 3; ++a) {
+            for (int o = 1; o < 64; o <<= 1) {
+                lo[a] = min(lo[a], (uint32_t)__shfl_xor((int)lo[a], o, 64));
+                hi[a] = max(hi[a], (uint32_t)__shfl_xor((int)hi[a], o, 64));
+            }
+        }
+        if (lane == 0) {
+            for (int a = 0; a < 3; ++a) {
+                atomicMin(&lo_bits[cur * 3 + a], lo[a]);
+                atomicMax(&hi_bits[cur * 3 + a], hi[a]);
+            }
+        }
+    };
+    reset();
+    // every step's loads first, so that they are in flight together
+    int64_t cellv[kAabbSteps];
+    float4 xv[kAabbSteps];
+#pragma unroll
+    for (int j = 0; j < kAabbSteps; ++j) {
+        const int64_t i = i0 + 64 * j + lane;
+        cellv[j] = i < n ? (int64_t)cid[i + 1] - 1 : -1;
+        xv[j] = i < n ? xs[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kAabbSteps; ++j) {
+        const int64_t i = i0 + 64 * j + lane;
+        if (i0 + 64 * j >= n) break;  // uniform
+        const bool valid = i < n;
+        const int64_t cell = cellv[j];
+        uint32_t o[3] = {0u, 0u, 0u};
+        if (valid) {
+            o[0] = f2ord(xv[j].x);
+            o[1] = f2ord(xv[j].y);
+            o[2] = f2ord(xv[j].z);
+        }
+        const int64_t c0 = __shfl(cell, 0, 64);
+        const bool same = __ballot(valid && cell == c0) == __ballot(true);
+        if (same && c0 == cur) {
+            for (int a = 0; a < 3; ++a) {
+                lo[a] = min(lo[a], o[a]);
+                hi[a] = max(hi[a], o[a]);
+            }
+            continue;
+        }
+        if (cur >= 0) flush();
+        reset();
+        if (same) {
+            cur = c0;
+            for (int a = 0; a < 3; ++a) {
+                lo[a] = o[a];
+                hi[a] = o[a];
+            }
+        } else {
+            cur = -1;
+            if (valid) {
                 for (int a = 0; a < 3; ++a) {
-                    atomicMin(&lo_bits[cur * 3 + a], lo[a]);
-                    atomicMax(&hi_bits[cur * 3 + a], hi[a]);
+                    atomicMin(&lo_bits[cell * 3 + a], o[a]);
+                    atomicMax(&hi_bits[cell * 3 + a], o[a]);
                 }
             }
-            cur = cell;
-            for (int a = 0; a < 3; ++a) {
-                lo[a] = 0xffffffffu;
-                hi[a] = 0u;
-            }
-        }
-        if (i < i1) {
-            const float4 v = xs[i];
-            const uint32_t o0 = f2ord(v.x), o1 = f2ord(v.y), o2 = f2ord(v.z);
-            lo[0] = min(lo[0], o0); hi[0] = max(hi[0], o0);
-            lo[1] = min(lo[1], o1); hi[1] = max(hi[1], o1);
-            lo[2] = min(lo[2], o2); hi[2] = max(hi[2], o2);
         }
     }
+    if (cur >= 0) flush();
 }
 
 __global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t *__restrict__ p, uint32_t v, int64_t n)
@@ -857,8 +908,8 @@ hipError_t launch_cell_aabb(const float4 *xs, const uint64_t *cid, int64_t n, in
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(3 * M)), dim3(kBlock), 0, s, lo_bits, 0xffffffffu,
                        3 * M);
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(3 * M)), dim3(kBlock), 0, s, hi_bits, 0u, 3 * M);
-    const int64_t chunks = (n + kAabbChunk - 1) / kAabbChunk;
-    hipLaunchKernelGGL(k_cell_aabb, dim3(grid_for(chunks)), dim3(kBlock), 0, s, xs, cid, n, lo_bits,
+    const int64_t waves = (n + 64 * kAabbSteps - 1) / (64 * kAabbSteps);
+    hipLaunchKernelGGL(k_cell_aabb, dim3(grid_for(waves, kBlock / 64)), dim3(kBlock), 0, s, xs, cid, n, lo_bits,
                        hi_bits);
     return hipGetLastError();
 }
