@@ -6,6 +6,6 @@ shares no code with the GPU library.
 """
 from .oracle import (  # noqa: F401
     available, d64, e64, join_rows, selfjoin_pairs, semijoin_rows, semijoin_pairs, band_count,
-    calibrate_bounds, knn_rows, knn,
+    calibrate_bounds, knn_rows, knn, mix64, digest_rows, digest_all,
     calibrate_eps, version, threads,
 )

@@ -29,7 +29,10 @@
  * lists come out sorted by point id.  orc_semijoin_rows does the same for
  * a query set distinct from the dataset (the semi-join of Sec. II-A).
  * orc_knn gives the exact k nearest neighbours (Sec. VI), ranked by the same
- * canonical D64, ties by the smaller point id.
+ * canonical D64, ties by the smaller point id.  orc_digest_rows and
+ * orc_digest_all summarise neighbour lists too long to keep (a count and a
+ * fingerprint per row, plus the pairs near the threshold) for the full-size
+ * comparisons.
  */
 #include <math.h>
 #include <stdint.h>
@@ -37,7 +40,7 @@
 #include <string.h>
 #include <omp.h>
 
-#define ORC_VERSION 3
+#define ORC_VERSION 4
 
 int orc_version(void) { return ORC_VERSION; }
 
@@ -154,6 +157,121 @@ int64_t orc_band_count(const float *X, int64_t n, int64_t d, int64_t ld, double 
             if (fabs(orc_d64(X + i * ld, X + j * ld, d) - e64) <= w) ++total;
     }
     return total;
+}
+
+/* ---- neighbour-list fingerprints -------------------------------------------
+ * For joins too large to hold as pair lists, each row's neighbour set N(i) is
+ * summarised by its size and a fingerprint h_i = sum over j in N(i) of
+ * mix64(j), modulo 2^64.  mix64 is the output function of the splitmix64
+ * generator (state advanced by the golden-ratio constant 0x9e3779b97f4a7c15,
+ * then two xor-shift-multiply rounds), a bijection on 64-bit words, so a
+ * missing, extra or wrong neighbour changes h_i except with probability
+ * about 2^-64.  The fingerprint belongs to the checking, not to the join.
+ */
+uint64_t orc_mix64(uint64_t j)
+{
+    uint64_t z = j + 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+/*
+ * Per selected row r (all rows when rows == NULL), i = rows[r]:
+ *   counts[r]  = |N(i)|, N(i) = { j : D64(x_i, x_j) <= E64 };
+ *   digests[r] = sum of mix64(j) over N(i), mod 2^64;
+ *   band[r]    = |{ j : |D64(x_i, x_j) - E64| <= rel * E64 }|  (band may be NULL).
+ * One pass over all n points per row.  Returns 0, -1, -2 as orc_join_rows.
+ */
+int orc_digest_rows(const float *X, int64_t n, int64_t d, int64_t ld, double eps, double rel,
+                    const int64_t *rows, int64_t nrows, uint32_t *counts, uint64_t *digests,
+                    uint32_t *band)
+{
+    int rc = check_inputs(X, n, d, ld, eps);
+    if (rc) return rc;
+    if (!rows) nrows = n;
+    if (nrows < 0 || !counts || !digests || !(rel >= 0.0)) return -1;
+    const double e64 = orc_e64(eps), w = rel * e64;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows ? rows[r] : r;
+        uint32_t c = 0, nb = 0;
+        uint64_t h = 0;
+        if (i >= 0 && i < n) {
+            for (int64_t j = 0; j < n; ++j) {
+                const double s = orc_d64(X + i * ld, X + j * ld, d);
+                if (s <= e64) {
+                    ++c;
+                    h += orc_mix64((uint64_t)j);
+                }
+                if (fabs(s - e64) <= w) ++nb;
+            }
+        }
+        counts[r] = c;
+        digests[r] = h;
+        if (band) band[r] = nb;
+    }
+    return 0;
+}
+
+/*
+ * The same three arrays for every row of the self-join (length n), with each
+ * unordered pair evaluated once: D64(x_i, x_j) and D64(x_j, x_i) are the
+ * same binary64 value (each difference is the negation of the other, exactly,
+ * so the squares and their running sums agree), so the pair (i, j), j > i,
+ * counts for row i and, mirrored, for row j.  Each thread accumulates into
+ * arrays of its own, summed at the end.  Returns 0, -1, -2 (bad input),
+ * -3 (out of host memory).
+ */
+int orc_digest_all(const float *X, int64_t n, int64_t d, int64_t ld, double eps, double rel,
+                   uint32_t *counts, uint64_t *digests, uint32_t *band)
+{
+    int rc = check_inputs(X, n, d, ld, eps);
+    if (rc) return rc;
+    if (!counts || !digests || !band || !(rel >= 0.0)) return -1;
+    const double e64 = orc_e64(eps), w = rel * e64;
+    memset(counts, 0, sizeof(uint32_t) * (size_t)n);
+    memset(digests, 0, sizeof(uint64_t) * (size_t)n);
+    memset(band, 0, sizeof(uint32_t) * (size_t)n);
+    int oom = 0;
+#pragma omp parallel reduction(| : oom)
+    {
+        uint32_t *lc = (uint32_t *)calloc((size_t)n, sizeof(uint32_t));
+        uint32_t *lb = (uint32_t *)calloc((size_t)n, sizeof(uint32_t));
+        uint64_t *lh = (uint64_t *)calloc((size_t)n, sizeof(uint64_t));
+        const int ok = lc && lb && lh;
+        if (!ok) oom = 1;
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t i = 0; i < n; ++i) {
+            if (!ok) continue;
+            const uint64_t mi = orc_mix64((uint64_t)i);
+            for (int64_t j = i; j < n; ++j) {
+                const double s = orc_d64(X + i * ld, X + j * ld, d);
+                const int in = s <= e64, bd = fabs(s - e64) <= w;
+                if (!in && !bd) continue;
+                lc[i] += (uint32_t)in;
+                lb[i] += (uint32_t)bd;
+                if (in) lh[i] += orc_mix64((uint64_t)j);
+                if (j != i) {
+                    lc[j] += (uint32_t)in;
+                    lb[j] += (uint32_t)bd;
+                    if (in) lh[j] += mi;
+                }
+            }
+        }
+#pragma omp critical
+        if (ok) {
+            for (int64_t i = 0; i < n; ++i) {
+                counts[i] += lc[i];
+                band[i] += lb[i];
+                digests[i] += lh[i];
+            }
+        }
+        free(lc);
+        free(lb);
+        free(lh);
+    }
+    return oom ? -3 : 0;
 }
 
 /* ---- epsilon calibration ------------------------------------------------

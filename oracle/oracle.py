@@ -50,6 +50,14 @@ def _load():
     lib.orc_band_count.restype = ctypes.c_int64
     lib.orc_band_count.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    ctypes.c_double, ctypes.c_double, _i64p, ctypes.c_int64]
+    lib.orc_mix64.restype = ctypes.c_uint64
+    lib.orc_mix64.argtypes = [ctypes.c_uint64]
+    lib.orc_digest_rows.restype = ctypes.c_int
+    lib.orc_digest_rows.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                    ctypes.c_double, _i64p, ctypes.c_int64, _u32p, _u64p, _u32p]
+    lib.orc_digest_all.restype = ctypes.c_int
+    lib.orc_digest_all.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                   ctypes.c_double, _u32p, _u64p, _u32p]
     lib.orc_knn.restype = ctypes.c_int
     lib.orc_knn.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int64, _f32p, ctypes.c_int64,
                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i64p, ctypes.c_int64,
@@ -208,6 +216,9 @@ def knn(X, k: int, rows=None):
 
 
 def band_count(X, eps, rel=1e-6, rows=None) -> int:
+    """Ordered pairs (row, j) with |D64 - E64| <= rel * E64 over the selected
+    rows (all if None): the pairs a reduced-precision classifier cannot
+    decide without the exact binary64 test."""
     X = _as_x(X)
     n, d = X.shape
     r, rp = _rows_arg(rows)
@@ -216,6 +227,43 @@ def band_count(X, eps, rel=1e-6, rows=None) -> int:
     if v < 0:
         raise ValueError("oracle rejected the input")
     return int(v)
+
+
+def mix64(j: int) -> int:
+    """The splitmix64 output function of j (neighbour-list fingerprints)."""
+    return int(_load().orc_mix64(int(j) & 0xffffffffffffffff))
+
+
+def digest_rows(X, eps, rows=None, rel=1e-6):
+    """Per selected row (all if None): (count, fingerprint, band) as uint32,
+    uint64, uint32 arrays; fingerprint = sum of mix64(j) over the row's
+    neighbours mod 2^64, band = points with |D64 - E64| <= rel * E64."""
+    X = _as_x(X)
+    n, d = X.shape
+    r, rp = _rows_arg(rows)
+    nrows = n if r is None else r.size
+    cnt = np.zeros(nrows, dtype=np.uint32)
+    dig = np.zeros(nrows, dtype=np.uint64)
+    band = np.zeros(nrows, dtype=np.uint32)
+    rc = _load().orc_digest_rows(_ptr(X, _f32p), n, d, d, float(eps), float(rel), rp, nrows,
+                                 _ptr(cnt, _u32p), _ptr(dig, _u64p), _ptr(band, _u32p))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the input (code {rc})")
+    return cnt, dig, band
+
+
+def digest_all(X, eps, rel=1e-6):
+    """digest_rows for every row, each unordered pair evaluated once (mirrored)."""
+    X = _as_x(X)
+    n, d = X.shape
+    cnt = np.zeros(n, dtype=np.uint32)
+    dig = np.zeros(n, dtype=np.uint64)
+    band = np.zeros(n, dtype=np.uint32)
+    rc = _load().orc_digest_all(_ptr(X, _f32p), n, d, d, float(eps), float(rel),
+                                _ptr(cnt, _u32p), _ptr(dig, _u64p), _ptr(band, _u32p))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the input (code {rc})")
+    return cnt, dig, band
 
 
 def calibrate_bounds(X, nq: int, k: int):

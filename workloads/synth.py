@@ -77,6 +77,17 @@ def _normal_rows(rng, n, d):
 
 def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
     """Points of workload ``name`` as a C-contiguous float32 [n, d] array."""
+    return _generate(name, n, seed)[0]
+
+
+def make_config_labels(name: str, n: int = None, seed: int = None):
+    """(points, labels): the array of ``make_config`` and, per row, the index
+    of the cluster it was drawn from (int32; -1 for uniform rows and for the
+    background of the mixture)."""
+    return _generate(name, n, seed)
+
+
+def _generate(name: str, n: int = None, seed: int = None):
     spec = CONFIGS[name]
     n = spec.n if n is None else int(n)
     seed = spec.seed if seed is None else int(seed)
@@ -85,7 +96,7 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
     rng = np.random.default_rng(seed)
     d = spec.d
     if spec.kind == "uniform":
-        return rng.random((n, d), dtype=np.float32)
+        return rng.random((n, d), dtype=np.float32), np.full(n, -1, dtype=np.int32)
     nc = _scaled_clusters(spec, n)
     if spec.kind == "gauss_iso":
         C = rng.random((nc, d))
@@ -94,7 +105,7 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
         for s in range(0, n, _CHUNK):
             e = min(n, s + _CHUNK)
             X[s:e] = C[L[s:e]] + spec.sigma * rng.standard_normal((e - s, d))
-        return X
+        return X, L.astype(np.int32)
     if spec.kind == "gauss_aniso":
         C = rng.random((nc, d))
         S = np.exp(rng.uniform(math.log(spec.sig_lo), math.log(spec.sig_hi), (nc, d)))
@@ -103,7 +114,7 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
         for s in range(0, n, _CHUNK):
             e = min(n, s + _CHUNK)
             X[s:e] = C[L[s:e]] + S[L[s:e]] * rng.standard_normal((e - s, d))
-        return X
+        return X, L.astype(np.int32)
     if spec.kind == "mix_bg":
         ncl = int(round(spec.frac * n))
         C = rng.random((nc, d))
@@ -116,7 +127,9 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
             e = min(n, s + _CHUNK)
             X[s:e] = rng.random((e - s, d))
         perm = rng.permutation(n)
-        return np.ascontiguousarray(X[perm])
+        lab = np.full(n, -1, dtype=np.int32)
+        lab[:ncl] = L
+        return np.ascontiguousarray(X[perm]), lab[perm]
     if spec.kind == "embed":
         C = rng.standard_normal((nc, d))
         C /= np.linalg.norm(C, axis=1, keepdims=True)
@@ -128,7 +141,7 @@ def make_config(name: str, n: int = None, seed: int = None) -> np.ndarray:
             Y = C[L[s:e]] + scale * rng.standard_normal((e - s, d))
             Y /= np.linalg.norm(Y, axis=1, keepdims=True)
             X[s:e] = Y
-        return X
+        return X, L.astype(np.int32)
     raise ValueError(f"unknown workload kind {spec.kind}")
 
 
