@@ -24,6 +24,8 @@ ERR_HIP = -3
 ERR_OOM = -4
 ERR_BUDGET = -5
 ERR_CAPACITY = -6
+ERR_SCRATCH = -7
+ERR_INTERNAL = -8
 
 REFINE_AUTO = 0
 REFINE_DIRECT = 1
@@ -31,7 +33,11 @@ REFINE_MFMA = 2
 REFINE_MFMA16 = 3
 
 _NAMES = {0: "OK", -1: "INVALID_ARG", -2: "STATE", -3: "HIP", -4: "OOM", -5: "BUDGET",
-          -6: "CAPACITY"}
+          -6: "CAPACITY", -7: "SCRATCH", -8: "INTERNAL"}
+
+# ERSJ_NOALLOC_SCRATCH_BYTES / ERSJ_NOALLOC_MASK_BUDGET of include/ersj.h
+NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_MASK_BUDGET = 48 << 20
 
 
 class ErsjError(RuntimeError):
@@ -96,7 +102,8 @@ class KnnInfo(ctypes.Structure):
 
 
 SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",
-           "ersj_plan_batches", "ersj_fill_pass", "ersj_fill_pass_host", "ersj_host_sync",
+           "ersj_plan_batches", "ersj_fill_pass", "ersj_fill_pass_host", "ersj_fill_pass_noalloc",
+           "ersj_host_sync",
            "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error", "ersj_knn")
 
 
@@ -120,6 +127,7 @@ def lib():
     L.ersj_plan_batches.argtypes = [vp, u64, ctypes.POINTER(i32), vp]
     L.ersj_fill_pass.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
     L.ersj_fill_pass_host.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
+    L.ersj_fill_pass_noalloc.argtypes = [vp, i32, vp, u64, ctypes.POINTER(u64), vp]
     L.ersj_host_sync.argtypes = [vp]
     L.ersj_batch_info.argtypes = [vp, i32, ctypes.POINTER(u64), ctypes.POINTER(u64),
                                   ctypes.POINTER(u64)]
@@ -131,7 +139,8 @@ def lib():
     L.ersj_last_error.argtypes = []
     L.ersj_last_error.restype = ctypes.c_char_p
     for f in ("ersj_build_index", "ersj_set_queries", "ersj_count_pass", "ersj_plan_batches",
-              "ersj_fill_pass", "ersj_fill_pass_host", "ersj_host_sync", "ersj_batch_info",
+              "ersj_fill_pass", "ersj_fill_pass_host", "ersj_fill_pass_noalloc", "ersj_host_sync",
+              "ersj_batch_info",
               "ersj_get_stats"):
         getattr(L, f).restype = ctypes.c_int
     _lib = L
@@ -251,6 +260,29 @@ def fill_pass(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = 
         if cap * 2 > pairs.numel():
             raise ValueError("capacity exceeds the tensor")
     rc = lib().ersj_fill_pass(h.handle, int(batch), ptr, cap, ctypes.byref(npairs), _stream(stream))
+    if rc == ERR_CAPACITY:
+        raise _capacity_error(rc, npairs.value)
+    _check(rc)
+    return npairs.value
+
+
+def fill_pass_noalloc(h: Index, batch: int, pairs: torch.Tensor = None, capacity: int = None,
+                      stream=None) -> int:
+    """``ersj_fill_pass_noalloc``: ``fill_pass`` with the batch's working memory
+    taken from the library's fixed device scratch (no device allocation).
+    Raises ErsjError(SCRATCH) when the batch does not fit it, and
+    ErsjError(CAPACITY) with ``.required`` when ``pairs`` is too small."""
+    npairs = ctypes.c_uint64()
+    if pairs is None:
+        ptr, cap = None, 0
+    else:
+        if pairs.dtype != torch.int32 or not pairs.is_cuda or not pairs.is_contiguous():
+            raise TypeError("pairs must be a contiguous int32 CUDA tensor")
+        ptr = ctypes.c_void_p(pairs.data_ptr())
+        cap = pairs.numel() // 2 if capacity is None else int(capacity)
+        if cap * 2 > pairs.numel():
+            raise ValueError("capacity exceeds the tensor")
+    rc = lib().ersj_fill_pass_noalloc(h.handle, int(batch), ptr, cap, ctypes.byref(npairs), _stream(stream))
     if rc == ERR_CAPACITY:
         raise _capacity_error(rc, npairs.value)
     _check(rc)

@@ -19,7 +19,8 @@ LIB = os.path.join(HERE, "libersj.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_expand.hip", "k_knn.hip", "ersj_api.cpp"]
+SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_expand.hip", "k_knn.hip", "k_scratch.hip",
+           "ersj_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result", "-Wno-unused-command-line-argument"]

@@ -899,9 +899,41 @@ int ensure_fill_buffers(ersj_index *h)
     return ERSJ_OK;
 }
 
-int do_refine(ersj_index *h, int32_t b, hipStream_t s)
+// Working memory of one batch's refinement, re-check and compaction: the
+// handle's own buffers (ensure_fill_buffers), or carved from the fixed device
+// scratch of the allocation-free entry point.
+struct FillBufs {
+    uint64_t *mask = nullptr;
+    uint8_t *gflag = nullptr;
+    Boundary *blist = nullptr;
+    uint64_t bcap = 0;                         // band-list entries over all sub-lists
+    unsigned long long *counters = nullptr;    // band sub-list counters, then re-check hit slots
+    uint64_t *lpref = nullptr;
+    uint32_t *rowcnt = nullptr;
+    uint64_t *roff = nullptr, *rscan = nullptr;
+    bool grow = false;                         // band list may be reallocated on overflow
+};
+
+FillBufs handle_bufs(ersj_index *h)
 {
-    TRY(ensure_fill_buffers(h));
+    FillBufs fb;
+    fb.mask = h->mask;
+    fb.gflag = h->gflag;
+    fb.blist = h->blist;
+    fb.bcap = h->bcap;
+    fb.counters = h->counters;
+    fb.lpref = h->lpref;
+    fb.rowcnt = h->rowcnt;
+    fb.roff = h->roff;
+    fb.rscan = h->rscan;
+    fb.grow = true;
+    return fb;
+}
+
+// Refine batch b into fb: mask words, band pairs re-checked in binary64, row
+// counts and their offsets; *pairs = the batch's pair count.
+int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t *pairs)
+{
     const uint32_t t0 = h->hb[b], t1 = h->hb[b + 1];
     const uint32_t ntiles = t1 - t0;
     const uint64_t rows = h->hrows[b + 1] - h->hrows[b];
@@ -932,7 +964,7 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     a.nrng = h->nrng;
     a.toff = h->toff;
     a.wbase = h->hwords[b];
-    a.mask = h->mask;
+    a.mask = fb.mask;
     a.tlo = h->tlo;
     a.thi = h->thi;
     a.kp = h->kp;
@@ -945,25 +977,25 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     }
     // band sub-list counters, re-check hit slots, skipped-comparison slots
     const size_t ncount = (size_t)(kBandLists + 2 * kHitSlots) * kBandStride;
-    unsigned long long *const hits = h->counters + (size_t)kBandLists * kBandStride;
+    unsigned long long *const hits = fb.counters + (size_t)kBandLists * kBandStride;
     unsigned long long *const skipped = hits + (size_t)kHitSlots * kBandStride;
     a.tbox = h->tbox;
     a.skipped = skipped;
-    a.rowcnt = h->rowcnt;
+    a.rowcnt = fb.rowcnt;
     a.row_base = h->hrows[b];
     a.cbox = h->cbox;
     a.chunk_base = h->chunk_base;
-    a.gflag = h->gflag;
+    a.gflag = fb.gflag;
     if (mfma && !h->cbox) a.tbox = INFINITY;  // no chunk boxes: no block test
     uint64_t bres[2] = {0, 0};  // kept band pairs, largest sub-list count
     uint64_t bcount = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
-        const uint64_t lcap = h->bcap / kBandLists;
-        a.blist = h->blist;
-        a.bcount = h->counters;
+        const uint64_t lcap = fb.bcap / kBandLists;
+        a.blist = fb.blist;
+        a.bcount = fb.counters;
         a.lcap = lcap;
-        HIPC(launch_fill_u64((uint64_t *)h->counters, 0, (int64_t)ncount, s), "clear counters");
-        HIPC(launch_fill_u32(h->rowcnt, 0, (int64_t)rows, s), "clear row counts");
+        HIPC(launch_fill_u64((uint64_t *)fb.counters, 0, (int64_t)ncount, s), "clear counters");
+        HIPC(launch_fill_u32(fb.rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
         HIPC(mfma ? launch_refine_mfma(a, f16, s) : launch_refine_direct(a, s), "refine kernel");
         h->ms_refine += timer_stop(h, s);
@@ -971,37 +1003,44 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
             h->refine_launches += 1;
             h->refined_cand += h->hcands[b + 1] - h->hcands[b];
         }
-        HIPC(launch_band_prefix(h->counters, lcap, h->lpref, h->lpref + kBandLists + 1, s), "band prefix");
-        HIPC(hipMemcpyAsync(bres, h->lpref + kBandLists + 1, sizeof bres, hipMemcpyDeviceToHost, s), "copy");
+        HIPC(launch_band_prefix(fb.counters, lcap, fb.lpref, fb.lpref + kBandLists + 1, s), "band prefix");
+        HIPC(hipMemcpyAsync(bres, fb.lpref + kBandLists + 1, sizeof bres, hipMemcpyDeviceToHost, s), "copy");
         TRY(sync(s, "refine"));
         bcount = bres[0];
         if (bres[1] <= lcap) break;
         // A band sub-list overflowed: grow them all and refine the batch
         // again (every mask word is rewritten, so the first result is
         // discarded).
+        const uint64_t cap = (bres[1] + bres[1] / 4 + 64) * kBandLists;
+        if (!fb.grow)
+            return fail(ERSJ_ERR_SCRATCH,
+                        "batch %d: %llu band pairs in one sub-list, the fixed scratch holds %llu per sub-list",
+                        b, (unsigned long long)bres[1], (unsigned long long)lcap);
         dfree(h, h->blist);
         h->bcap = 0;
-        const uint64_t cap = (bres[1] + bres[1] / 4 + 64) * kBandLists;
         TRY(dalloc(h, &h->blist, (size_t)cap, "boundary list"));
         h->bcap = cap;
+        fb.blist = h->blist;
+        fb.bcap = cap;
         if (!h->opt.boundary_capacity) {
             uint64_t cur = g_bcap_hint.load();
             while (cur < cap && !g_bcap_hint.compare_exchange_weak(cur, cap)) {
             }
         }
     }
-    if (bres[1] > h->bcap / kBandLists) return fail(ERSJ_ERR_HIP, "boundary list overflow persisted");
+    if (bres[1] > fb.bcap / kBandLists)
+        return fail(ERSJ_ERR_INTERNAL, "band sub-list still overflows after growing it (%llu > %llu)",
+                    (unsigned long long)bres[1], (unsigned long long)(fb.bcap / kBandLists));
     timer_start(h, s);
-    HIPC(launch_recheck(h->blist, h->bcap / kBandLists, h->lpref, bcount, h->xr, h->xqr, h->d, recheck_stride(h->d), h->e64,
-                        h->mask, h->gflag, hits, h->rowcnt,
-                        h->hrows[b], s),
+    HIPC(launch_recheck(fb.blist, fb.bcap / kBandLists, fb.lpref, bcount, h->xr, h->xqr, h->d, recheck_stride(h->d),
+                        h->e64, fb.mask, fb.gflag, hits, fb.rowcnt, h->hrows[b], s),
          "re-check kernel");
     h->ms_recheck += timer_stop(h, s);
     timer_start(h, s);
-    HIPC(scan_u32(h->rowcnt, h->roff, (int64_t)rows, h->rscan, s), "row scan");
+    HIPC(scan_u32(fb.rowcnt, fb.roff, (int64_t)rows, fb.rscan, s), "row scan");
     uint64_t tot = 0;  // pairs
     uint64_t hs[2 * kHitSlots * kBandStride];  // re-check hit slots, skipped-comparison slots
-    HIPC(hipMemcpyAsync(&tot, h->roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
+    HIPC(hipMemcpyAsync(&tot, fb.roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(hs, hits, sizeof hs, hipMemcpyDeviceToHost, s), "copy");
     TRY(sync(s, "row count"));
     for (uint32_t k = 1; k < kHitSlots; ++k) hs[0] += hs[k * kBandStride];
@@ -1014,20 +1053,81 @@ int do_refine(ersj_index *h, int32_t b, hipStream_t s)
     h->last_in = hs[0];
     h->last_skip = hs[1];
     if (h->opt.timing) h->skipped_cand += hs[1];
+    h->last_pairs = tot;
+    *pairs = tot;
+    return ERSJ_OK;
+}
+
+// Refine batch b into the handle's own buffers (kept for a CAPACITY retry).
+int do_refine(ersj_index *h, int32_t b, hipStream_t s)
+{
+    TRY(ensure_fill_buffers(h));
+    FillBufs fb = handle_bufs(h);
+    uint64_t tot = 0;
+    TRY(refine_into(h, b, s, fb, &tot));
     h->ready_batch = b;
     h->ready_pairs = tot;
-    h->last_pairs = tot;
+    return ERSJ_OK;
+}
+
+
+int expand_into(ersj_index *h, int32_t batch, uint32_t *d_pairs, const FillBufs &fb, hipStream_t s)
+{
+    const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
+    timer_start(h, s);
+    HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], fb.mask,
+                       fb.gflag, fb.roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
+         "expand kernel");
+    h->ms_expand += timer_stop(h, s);
     return ERSJ_OK;
 }
 
 int expand_batch(ersj_index *h, int32_t batch, uint32_t *d_pairs, hipStream_t s)
 {
-    const uint32_t t0 = h->hb[batch], t1 = h->hb[batch + 1];
-    timer_start(h, s);
-    HIPC(launch_expand(h->tiles, t0, t1 - t0, h->toff, h->hwords[batch], h->hrows[batch], h->mask,
-                       h->gflag, h->roff, h->rstart, h->rpref, h->nrng, h->qorig, h->orig, d_pairs, s),
-         "expand kernel");
-    h->ms_expand += timer_stop(h, s);
+    return expand_into(h, batch, d_pairs, handle_bufs(h), s);
+}
+
+// The allocation-free fill pass carves every buffer of a batch from the
+// fixed device scratch (256-byte aligned pieces): mask words, unit flags,
+// row counts, row offsets and their scan temporaries, counters, the band
+// prefix, and the band list in what remains.
+int noalloc_bufs(ersj_index *h, int32_t b, FillBufs *fb)
+{
+    void *base = nullptr;
+    HIPC(noalloc_scratch(h->device, &base), "address of the fixed scratch");
+    const uint64_t words = h->hwords[b + 1] - h->hwords[b];
+    const uint64_t rows = h->hrows[b + 1] - h->hrows[b];
+    uint64_t off = 0;
+    auto take = [&](uint64_t bytes) {
+        const uint64_t at = off;
+        off += (bytes + 255) & ~(uint64_t)255;
+        return at;
+    };
+    const uint64_t o_mask = take(words * 8);
+    const uint64_t o_flag = take(words / 4 + 64);
+    const uint64_t o_rcnt = take(rows * 4);
+    const uint64_t o_roff = take((rows + 1) * 8);
+    const uint64_t o_scan = take(scan_tmp_entries((int64_t)rows + 1) * 8);
+    const uint64_t o_cnt = take((uint64_t)(kBandLists + 2 * kHitSlots) * kBandStride * 8);
+    const uint64_t o_lpref = take((uint64_t)(kBandLists + 3) * 8);
+    const uint64_t min_band = (uint64_t)kBandLists * 64 * sizeof(Boundary);
+    if (off + min_band > kNoallocScratchBytes)
+        return fail(ERSJ_ERR_SCRATCH,
+                    "batch %d needs %llu bytes of working memory (%llu mask words, %llu rows) plus a band list, "
+                    "more than the %llu bytes of the fixed scratch; plan smaller batches",
+                    b, (unsigned long long)off, (unsigned long long)words, (unsigned long long)rows,
+                    (unsigned long long)kNoallocScratchBytes);
+    char *p = (char *)base;
+    fb->mask = (uint64_t *)(p + o_mask);
+    fb->gflag = (uint8_t *)(p + o_flag);
+    fb->rowcnt = (uint32_t *)(p + o_rcnt);
+    fb->roff = (uint64_t *)(p + o_roff);
+    fb->rscan = (uint64_t *)(p + o_scan);
+    fb->counters = (unsigned long long *)(p + o_cnt);
+    fb->lpref = (uint64_t *)(p + o_lpref);
+    fb->blist = (Boundary *)(p + off);
+    fb->bcap = (kNoallocScratchBytes - off) / sizeof(Boundary) / kBandLists * kBandLists;
+    fb->grow = false;
     return ERSJ_OK;
 }
 
@@ -1368,6 +1468,31 @@ int ersj_fill_pass_host(ersj_index *h, int32_t batch, uint32_t *host_pairs, uint
     HIPC(hipEventRecord(h->copied[k], h->copy_stream), "delivery event");
     h->copy_pending[k] = true;
     return ERSJ_OK;
+}
+
+int ersj_fill_pass_noalloc(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t capacity,
+                           uint64_t *n_pairs, void *stream)
+{
+    g_err.clear();
+    if (!h) return fail(ERSJ_ERR_INVALID_ARG, "handle is NULL");
+    if (!n_pairs) return fail(ERSJ_ERR_INVALID_ARG, "n_pairs is NULL");
+    if (capacity > 0 && !d_pairs) return fail(ERSJ_ERR_INVALID_ARG, "d_pairs is NULL");
+    if (h->state < kPlanned) return fail(ERSJ_ERR_STATE, "plan_batches has not run");
+    if (batch < 0 || batch >= h->nbatch)
+        return fail(ERSJ_ERR_INVALID_ARG, "batch %d outside [0, %d)", batch, h->nbatch);
+    DeviceGuard g(h->device);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select the handle's device");
+    hipStream_t s = (hipStream_t)stream;
+    FillBufs fb;
+    TRY(noalloc_bufs(h, batch, &fb));
+    uint64_t tot = 0;
+    TRY(refine_into(h, batch, s, fb, &tot));
+    *n_pairs = tot;
+    if (capacity < tot)
+        return fail(ERSJ_ERR_CAPACITY, "batch %d has %llu pairs, capacity is %llu", batch,
+                    (unsigned long long)tot, (unsigned long long)capacity);
+    if (tot == 0) return ERSJ_OK;
+    return expand_into(h, batch, d_pairs, fb, s);
 }
 
 int ersj_host_sync(ersj_index *h)

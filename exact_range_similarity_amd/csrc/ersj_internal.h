@@ -294,6 +294,12 @@ hipError_t launch_knn_select(const KnnArgs &a, uint32_t ntiles, hipStream_t s);
 hipError_t launch_gather_rows(const float *q, int64_t ldq, const uint32_t *idx, uint64_t m, int32_t d,
                               int32_t ldo, float *out, hipStream_t s);
 
+// Fixed device scratch of the allocation-free fill pass (k_scratch.hip):
+// kNoallocScratchBytes per device; *out = this device's address of it
+// (looked up on the first call for the device, which must be current).
+constexpr uint64_t kNoallocScratchBytes = (uint64_t)64 << 20;
+hipError_t noalloc_scratch(int dev, void **out);
+
 // row stride of the row-major copies read by the re-check: d rounded up to
 // four floats, so that a row is read in 16-byte pieces
 inline int32_t recheck_stride(int32_t d) { return (d + 3) & ~3; }

@@ -57,7 +57,9 @@ enum {
     ERSJ_ERR_HIP = -3,         /* HIP runtime error; message names it */
     ERSJ_ERR_OOM = -4,         /* device allocation failed or max_device_bytes hit */
     ERSJ_ERR_BUDGET = -5,      /* one row tile's mask exceeds the batch budget */
-    ERSJ_ERR_CAPACITY = -6     /* output buffer too small; *n_pairs = required */
+    ERSJ_ERR_CAPACITY = -6,    /* output buffer too small; *n_pairs = required */
+    ERSJ_ERR_SCRATCH = -7,     /* ersj_fill_pass_noalloc: the batch does not fit the fixed scratch */
+    ERSJ_ERR_INTERNAL = -8     /* an invariant of the library failed (message names it) */
 };
 
 typedef struct ersj_index ersj_index; /* opaque; owns all its device memory */
@@ -204,6 +206,31 @@ int ersj_fill_pass(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t cap
  */
 int ersj_fill_pass_host(ersj_index *h, int32_t batch, uint32_t *host_pairs, uint64_t capacity,
                         uint64_t *n_pairs, void *stream);
+
+/*
+ * ersj_fill_pass for callers that cannot allocate device memory (code that
+ * must not call hipMalloc, such as work prepared for stream capture, tight
+ * serving loops, or harnesses that forbid allocation).  Same arguments,
+ * result and errors as ersj_fill_pass, but the batch's working memory (its
+ * result mask and unit flags, row counts and offsets, counters and band
+ * list) comes from a fixed device array of ERSJ_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends; the call
+ * allocates nothing.  The caller still provides d_pairs.
+ *  - A batch whose working memory exceeds the scratch is rejected with
+ *    ERSJ_ERR_SCRATCH before any device work: plan with
+ *    budget_bytes <= ERSJ_NOALLOC_MASK_BUDGET (mask words cost 8.25 bytes,
+ *    and the rows of a batch 20 bytes each on top).  A band list that
+ *    outgrows what remains of the scratch is ERSJ_ERR_SCRATCH as well.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (each call clears what it needs): calls that overlap
+ *    on one GPU, from any thread, handle or stream, race.
+ *  - On CAPACITY a retry refines the batch again (nothing is kept between
+ *    calls).  The handle's own buffers and ersj_fill_pass are untouched.
+ */
+#define ERSJ_NOALLOC_SCRATCH_BYTES ((uint64_t)64 << 20)
+#define ERSJ_NOALLOC_MASK_BUDGET ((uint64_t)48 << 20)
+int ersj_fill_pass_noalloc(ersj_index *h, int32_t batch, uint32_t *d_pairs, uint64_t capacity,
+                           uint64_t *n_pairs, void *stream);
 
 /* Wait until every copy started by ersj_fill_pass_host has landed in host
  * memory.  Errors: INVALID_ARG, HIP. */

@@ -69,6 +69,7 @@ def test_null_handle_paths():
     assert L.ersj_count_pass(None, ctypes.byref(u), None) == ersj.ERR_INVALID_ARG
     assert L.ersj_plan_batches(None, 0, ctypes.byref(i), None) == ersj.ERR_INVALID_ARG
     assert L.ersj_fill_pass(None, 0, None, 0, ctypes.byref(u), None) == ersj.ERR_INVALID_ARG
+    assert L.ersj_fill_pass_noalloc(None, 0, None, 0, ctypes.byref(u), None) == ersj.ERR_INVALID_ARG
     assert L.ersj_batch_info(None, 0, None, None, None) == ersj.ERR_INVALID_ARG
     assert L.ersj_get_stats(None, None) == ersj.ERR_INVALID_ARG
     assert L.ersj_set_queries(None, FAKE, 10, 4, None) == ersj.ERR_INVALID_ARG
