@@ -2,14 +2,18 @@
 
 One step is one complete self-join of the workload with its points already
 resident in HBM: build_index, count_pass, plan_batches, and fill_pass of
-every batch (pairs written to device memory).  The default workload is
-N = 1,000,000 points, d = 32, a mixture of 100 isotropic Gaussians
-(sigma = 0.02) with epsilon giving a mean of 64 neighbours per point.
+every batch (pairs written to device memory).  The default workload is the
+largest single-GPU one: N = 10,000,000 points, d = 18, 70% in 500 Gaussian
+clusters (sigma = 0.01) and 30% uniform background, epsilon giving a mean of
+256 neighbours per point.
 
-Printed JSON (one line): throughput in candidate distance evaluations per
-second over the whole join, plus the refinement kernel's roofline position
-(its duration measured with HIP events on the stream it runs on) and the CPU
-oracle timed on a bounded sample of the same workload.
+Printed JSON (one line): throughput in distance evaluations computed per
+second over the whole join (the candidates the count pass produced, minus
+those the block box test settled without a distance), the refinement
+kernel's roofline position (its duration measured with HIP events on the
+stream it runs on), and the CPU oracle timed on a bounded sample of the same
+workload.  The sample rows are also compared with the GPU's, and the pairs
+whose binary64 squared distance lies within 1e-6 eps^2 of eps^2 counted.
 
     python bench.py [--steps K] [--warmup W] [--workload c2] [--no-cpu]
                     [--mode semijoin [--nq NQ]]
@@ -32,6 +36,7 @@ if ROOT not in sys.path:
 
 METRIC = "ε-self-join time + candidate dist evals/s and % of HBM/FP32 roofline, 1 GPU"
 FP32_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak (256 CUs, 2.4 GHz)
+BAND_REL = 1e-6            # threshold band reported beside the result
 FP16_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16 matrix peak
 HBM_PEAK_GBS = 8000.0
 
@@ -50,7 +55,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="c4")
     ap.add_argument("--budget-frac", type=float, default=0.0,
                     help="batch budget as a fraction of the total mask (0 = free memory)")
     ap.add_argument("--refine", type=int, default=0, help="0 auto, 1 direct, 2 fp32 MFMA, 3 split-fp16 MFMA")
@@ -163,15 +168,24 @@ def main():
     kern = st["refine_kernel"]
     mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
     f16 = kern == ersj.REFINE_MFMA16
-    # flops per computed candidate: direct form 3d (sub, mul, add per
-    # dimension); expanded form 2d + 3 (the dot product on MFMA plus norms);
-    # split-fp16 form 6d + 3 (three fp16 products per dimension on MFMA)
-    per_cand = (6.0 * d + 3.0) if f16 else (2.0 * d + 3.0) if mfma else 3.0 * d
+    # algorithmic flops per computed candidate: 2d + 3 for the expanded
+    # form (a d-term dot product and the combination with the two norms),
+    # 3d for the direct form (difference, square, sum per dimension); the
+    # split-fp16 form executes three fp16 products per dimension but is
+    # priced, like the others, by the work the distance needs
+    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
     flops_per_launch = per_cand * evaluated / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    # against the peak of the dtype the contraction runs in
     peak = FP16_PEAK_TFLOPS if f16 else FP32_PEAK_TFLOPS
-    # the same launch priced as fp32 work (2d + 3 flops per candidate)
     fp32_equiv = (2.0 * d + 3.0) * evaluated / max(1, launches) / (avg_launch_ms * 1e-3) / 1e12
+    # algorithmic HBM bytes of a launch: its result mask written once, and
+    # the candidate and query rows read once (dimension-blocked, d padded to
+    # a multiple of four)
+    dpad = (d + 3) // 4 * 4
+    mask_bytes = 8.0 * st["total_mask_words"] / max(1, st["n_batches"])
+    hbm_bytes = mask_bytes + 4.0 * dpad * (X.shape[0] + (Q.shape[0] if semi else 0))
+    hbm_gbs = hbm_bytes / (avg_launch_ms * 1e-3) / 1e9
     kname = "k_refine_mfma" if mfma else "k_refine_direct"  # one kernel template, both MFMA forms
     traffic = None
     form = kname.replace("k_", "") + ("16" if f16 else "")
@@ -190,7 +204,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": cand / wall,
+        "value": evaluated / args.steps / wall,
         "unit": "candidate dist evals/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -214,7 +228,10 @@ def main():
         "join_wall_s": wall,
         "result_pairs": npairs,
         "result_pairs_per_s": npairs / wall,
+        "value_note": "distance evaluations computed per second of whole-join wall time; the count pass's "
+                      "candidates minus those the block box test settled without a distance",
         "candidates": cand,
+        "candidates_per_s": cand / wall,
         "candidate_fraction_of_n2": cand / float(X.shape[0]) ** 2,
         "evaluated_fraction": evaluated / max(1, refined),
         "cells": st["cells"],
@@ -230,8 +247,11 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
+            "flops_per_candidate": per_cand,
             "fp32_equivalent": {"achieved": fp32_equiv, "peak": FP32_PEAK_TFLOPS,
                                 "frac": fp32_equiv / FP32_PEAK_TFLOPS} if f16 else None,
+            "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
+                    "algorithmic_bytes_per_launch": hbm_bytes},
             "traffic": traffic,
             "flops_per_launch": flops_per_launch,
             "avg_launch_ms": avg_launch_ms,
@@ -291,18 +311,70 @@ def main():
         nrows = int(max(rows_probe, min(Q.shape[0], args.cpu_seconds / max(per_row, 1e-9))))
         log(f"[bench] cpu oracle: {nrows} rows (~{per_row * nrows:.0f}s)")
         t = time.perf_counter()
-        colptr, _ = cpu_rows(np.arange(nrows))
+        colptr, cols = cpu_rows(np.arange(nrows))
         dt = time.perf_counter() - t
         evals = nrows * X.shape[0]
         out["cpu_baseline"] = {
             "value": evals / dt, "unit": "candidate dist evals/s", "cores": oracle.threads(),
+            "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{'query ' if semi else ''}rows 0..{nrows - 1} of {args.workload} against all "
-                      f"{X.shape[0]} points (brute force, binary64), {dt:.1f}s",
+                      f"{X.shape[0]} points (brute force, binary64, every pair evaluated), {dt:.1f}s",
             "sample_pairs": int(colptr[-1]),
             "full_join_s_extrapolated": dt * Q.shape[0] / nrows,
         }
+        # the GPU's pairs of the same rows, from one more (untimed) join
+        mism = sample_mismatches(args, ersj, xt, qt, eps, budget, stream, nrows, colptr, cols)
+        band = None if semi else oracle.band_count(X, eps, BAND_REL, np.arange(nrows))
+        out["threshold_band"] = {
+            "rel": BAND_REL, "sample_rows": nrows,
+            "oracle_band_pairs": band,
+            "gpu_pairs_differing_from_oracle": mism,
+            "note": "pairs of the sample rows with |D64 - fl(eps^2)| <= 1e-6 fl(eps^2) (binary64), and GPU pairs "
+                    "of those rows that differ from the oracle's after the binary64 re-check",
+        }
     print(json.dumps(out), flush=True)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def sample_mismatches(args, ersj, xt, qt, eps, budget, stream, nrows, colptr, cols):
+    """Pairs of query rows 0..nrows-1 in which one more GPU join (default
+    options of the timed run) differs from the oracle's neighbour lists."""
+    import numpy as np
+    import torch
+    opts = ersj.default_options(refine_kernel=args.refine, grid_reach=args.grid_reach,
+                                block_prune=-1 if args.no_block_prune else 0)
+    h = ersj.build_index(xt, eps, opts, stream)
+    if qt is not None:
+        ersj.set_queries(h, qt, stream)
+    ersj.count_pass(h, stream)
+    nb = ersj.plan_batches(h, budget, stream)
+    keep = []
+    for part in ersj.iter_batches(h, nb, stream):
+        for s0 in range(0, part.shape[0], 1 << 27):  # torch indexing stays below 2^31 elements
+            blk = part[s0:s0 + (1 << 27)]
+            q = blk[:, 0].to(torch.int64) & 0xffffffff
+            sel = q < nrows
+            if bool(sel.any()):
+                x = blk[:, 1].to(torch.int64)[sel] & 0xffffffff
+                keep.append(((q[sel] << 32) | x).cpu())
+        del part
+    h.free()
+    got = np.sort(torch.cat(keep).numpy()) if keep else np.zeros(0, dtype=np.int64)
+    counts = np.diff(colptr).astype(np.int64)
+    rows = np.repeat(np.arange(nrows, dtype=np.int64), counts)
+    want = np.sort((rows << 32) | cols.astype(np.int64))
+    return int(np.setxor1d(got, want).size)
 
 
 def run_knn(args, spec, rec, eps, X, xt, stream):
@@ -337,7 +409,7 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
     kern = info["refine_kernel"]
     mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
     f16 = kern == ersj.REFINE_MFMA16
-    per_cand = (6.0 * d + 3.0) if f16 else (2.0 * d + 3.0) if mfma else 3.0 * d
+    per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
     avg_launch_ms = refine_ms / max(1, launches)
     flops_per_launch = per_cand * computed / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
