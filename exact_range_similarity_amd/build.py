@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libersj.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_expand.hip", "k_knn.hip", "k_scratch.hip",
+SOURCES = ["k_index.hip", "k_refine.hip", "k_refine_mfma.hip", "k_refine_m16.hip", "k_refine_g16.hip", "k_expand.hip", "k_knn.hip", "k_scratch.hip",
            "ersj_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

@@ -131,6 +131,12 @@ struct ersj_index {
     uint64_t refined_cand = 0, skipped_cand = 0;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t kernel_used = ERSJ_REFINE_DIRECT;
+    bool use_m16 = false;  // split-fp16 form on the whole-tile kernel (33 <= d <= 64)
+    bool use_g16 = false;  // split-fp16 form on operands prepared per point (d > 64)
+    std::vector<double> mean;  // per input dimension (binary64 statistics of the points)
+    float4 *tref = nullptr;  // per row tile: reference point of the MFMA kernels' centring
+    uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
+    float *n16 = nullptr, *n16q = nullptr;
     // host delivery: two device staging buffers, alternated by batch, drained
     // into the caller's host memory on a copy stream of its own
     hipStream_t copy_stream = nullptr;
@@ -365,19 +371,24 @@ void thresholds(ersj_index *h)
 // norms and dots <= 4 d_pad max|x|^2, kept below FLT_MAX / 16) and the
 // query tile fits the LDS.  Band: K = 4 (d_pad + 8) u, twice the
 // 2.02 gamma(d_pad + 2) + 6.1 u that the error analysis needs.
-bool mfma_feasible(const ersj_index *h, const char **why)
+bool coords_feasible(const ersj_index *h, const char **why)
 {
     const double dp = 4.0 * h->nb;
-    if (refine_mfma_lds_bytes(h->nb) > 160 * 1024) {
-        *why = "query tile exceeds the 160 KiB LDS (d too large)";
-        return false;
-    }
     const double m = std::max(h->maxabs, h->maxabs_q);  // points and query rows
     if (16.0 * dp * m * m >= 1e38) {
         *why = "coordinates too large for fp32 norms";
         return false;
     }
     return true;
+}
+
+bool mfma_feasible(const ersj_index *h, const char **why)
+{
+    if (refine_mfma_lds_bytes(h->nb) > 160 * 1024) {
+        *why = "query tile exceeds the 160 KiB LDS (d too large)";
+        return false;
+    }
+    return coords_feasible(h, why);
 }
 
 // Split-fp16 MFMA form, classified in a scaled domain.  Centred coordinates
@@ -436,12 +447,19 @@ int choose_kernel(ersj_index *h)
 {
     const char *why = "";
     const bool ok = mfma_feasible(h, &why);
+    // above 64 dimensions the split form runs on prepared operands, whose
+    // LDS use does not grow with d: only the coordinate range limits it
+    const char *why16 = "";
+    const bool ok16 = h->nb > 16 ? coords_feasible(h, &why16) : ok;
+    if (h->nb <= 16) why16 = why;
     int k = h->opt.refine_kernel;
-    if ((k == ERSJ_REFINE_MFMA || k == ERSJ_REFINE_MFMA16) && !ok)
+    if (k == ERSJ_REFINE_MFMA && !ok)
         return fail(ERSJ_ERR_INVALID_ARG, "MFMA refinement not usable for this input: %s", why);
+    if (k == ERSJ_REFINE_MFMA16 && !ok16)
+        return fail(ERSJ_ERR_INVALID_ARG, "MFMA refinement not usable for this input: %s", why16);
     if (k == ERSJ_REFINE_AUTO) {
         // the split-fp16 form where its scale fits, else fp32 MFMA, else direct
-        k = !ok ? ERSJ_REFINE_DIRECT : mfma16_setup(h) ? ERSJ_REFINE_MFMA16 : ERSJ_REFINE_MFMA;
+        k = ok16 && mfma16_setup(h) ? ERSJ_REFINE_MFMA16 : ok ? ERSJ_REFINE_MFMA : ERSJ_REFINE_DIRECT;
     } else if (k == ERSJ_REFINE_MFMA16 && !mfma16_setup(h)) {
         return fail(ERSJ_ERR_INVALID_ARG, "split-fp16 refinement not usable: coordinate scale out of range");
     }
@@ -452,7 +470,11 @@ int choose_kernel(ersj_index *h)
         h->km = (float)(1.0 - K);
         HIPC(prepare_refine_mfma(h->nb, false), "MFMA kernel LDS attribute");
     }
-    if (k == ERSJ_REFINE_MFMA16) HIPC(prepare_refine_mfma(h->nb, true), "MFMA kernel LDS attribute");
+    h->use_m16 = k == ERSJ_REFINE_MFMA16 && refine_m16_supported(h->nb);
+    h->use_g16 = k == ERSJ_REFINE_MFMA16 && h->nb > 16;
+    if (h->use_m16) HIPC(prepare_refine_m16(h->nb), "MFMA kernel LDS attribute");
+    else if (h->use_g16) HIPC(prepare_refine_g16(), "MFMA kernel LDS attribute");
+    else if (k == ERSJ_REFINE_MFMA16) HIPC(prepare_refine_mfma(h->nb, true), "MFMA kernel LDS attribute");
     return ERSJ_OK;
 }
 
@@ -484,8 +506,20 @@ int ceil_log2(uint64_t v)
     return b;
 }
 
+void release_prepared(ersj_index *h)
+{
+    if (h->p16q != h->p16) dfree(h, h->p16q);
+    if (h->n16q != h->n16) dfree(h, h->n16q);
+    h->p16q = nullptr;
+    h->n16q = nullptr;
+    dfree(h, h->p16);
+    dfree(h, h->n16);
+}
+
 void release_count(ersj_index *h)
 {
+    release_prepared(h);
+    dfree(h, h->tref);
     dfree(h, h->rstart);
     dfree(h, h->rpref);
     dfree(h, h->nrng);
@@ -623,6 +657,8 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     std::vector<double> hst;
     TRY(row_stats(h, x, n, ld, &hst, s));
     h->maxabs = max_abs(hst, d);
+    h->mean.resize(d);
+    for (int k = 0; k < d; ++k) h->mean[k] = hst[k * 4 + 0];
 
     // A2: dimensions by descending variance (ties: lower id first); the first
     // three are the grid axes.  Cell width >= eps*(1 + 2^-20), widened so no
@@ -720,6 +756,33 @@ void release_queries(ersj_index *h)
     alias_queries(h);
 }
 
+// Split-fp16 operands of the points and the query rows for k_refine_g16:
+// centred on the points' per-dimension mean r (fp32, in the layout's
+// variance order; padded dimensions 0), scaled by s16, split, with norms.
+int prepare_operands(ersj_index *h, hipStream_t s)
+{
+    const int nb = h->nb, ns = (nb + 3) / 4;
+    std::vector<float> nrs((size_t)nb * 4, 0.0f);
+    for (int j = 0; j < h->d; ++j) nrs[j] = -((float)h->mean[h->perm[j]] * h->s16);
+    Scratch tmp(h);
+    float4 *dnrs = nullptr;
+    TRY(tmp.get(&dnrs, (size_t)nb, "operand preparation"));
+    HIPC(hipMemcpyAsync(dnrs, nrs.data(), sizeof(float) * nrs.size(), hipMemcpyHostToDevice, s), "copy");
+    TRY(dalloc(h, &h->p16, (size_t)ns * 4 * (size_t)h->n, "prepared operands"));
+    TRY(dalloc(h, &h->n16, (size_t)h->n, "prepared operands"));
+    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->p16, h->n16, s), "operand preparation");
+    if (h->semi) {
+        TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->nq, "prepared operands"));
+        TRY(dalloc(h, &h->n16q, (size_t)h->nq, "prepared operands"));
+        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->p16q, h->n16q, s), "operand preparation");
+    } else {
+        h->p16q = h->p16;
+        h->n16q = h->n16;
+    }
+    TRY(sync(s, "operand preparation"));  // the host copy of nrs and dnrs must outlive the kernels
+    return ERSJ_OK;
+}
+
 int do_count(ersj_index *h, hipStream_t s)
 {
     release_count(h);
@@ -775,6 +838,12 @@ int do_count(ersj_index *h, hipStream_t s)
         TRY(dalloc(h, &h->cbox, (size_t)nchunks * 2 + 2, "chunk boxes"));
         HIPC(launch_chunk_boxes(h->chunk_base, M, nchunks, h->rstart, h->rpref, h->nrng, h->xs, h->cbox, s),
              "chunk box kernel");
+    }
+    if (h->use_g16) TRY(prepare_operands(h, s));
+    if ((h->kernel_used == ERSJ_REFINE_MFMA || h->kernel_used == ERSJ_REFINE_MFMA16) && !h->use_g16) {
+        // per-tile reference points of the MFMA kernels' centring
+        TRY(dalloc(h, &h->tref, (size_t)h->T * h->nb, "tile references"));
+        HIPC(launch_tile_ref(h->tiles, h->T, h->xq, (uint64_t)h->nq, h->nb, h->tref, s), "tile reference kernel");
     }
     TRY(sync(s, "count pass"));
     return ERSJ_OK;
@@ -951,7 +1020,12 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     const bool mfma = h->kernel_used == ERSJ_REFINE_MFMA || f16;
     // row sub-blocks: the direct kernel covers 32 rows per work item, the
     // MFMA kernel 32 per query block it holds
-    a.nsub = (uint32_t)(kTileRows / (mfma ? 32 * refine_mfma_qblocks(h->nb) : 32));
+    a.nsub = h->use_m16 || h->use_g16 ? 1u : (uint32_t)(kTileRows / (mfma ? 32 * refine_mfma_qblocks(h->nb) : 32));
+    a.p16 = h->p16;
+    a.p16q = h->p16q;
+    a.n16 = h->n16;
+    a.n16q = h->n16q;
+    a.tref = h->tref;
     const uint64_t rows_items = (uint64_t)ntiles * a.nsub;
     uint32_t seg = 8192;
     auto nseg_of = [&](uint32_t sl) { return (h->umax + sl - 1) / sl; };
@@ -997,7 +1071,11 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         HIPC(launch_fill_u64((uint64_t *)fb.counters, 0, (int64_t)ncount, s), "clear counters");
         HIPC(launch_fill_u32(fb.rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
-        HIPC(mfma ? launch_refine_mfma(a, f16, s) : launch_refine_direct(a, s), "refine kernel");
+        HIPC(h->use_g16   ? launch_refine_g16(a, s)
+             : h->use_m16 ? launch_refine_m16(a, s)
+             : mfma       ? launch_refine_mfma(a, f16, s)
+                          : launch_refine_direct(a, s),
+             "refine kernel");
         h->ms_refine += timer_stop(h, s);
         if (h->opt.timing) {
             h->refine_launches += 1;

@@ -156,6 +156,12 @@ hipError_t launch_tiles(const uint64_t *tile_base, int64_t M, int64_t T,
                         const uint32_t *cell_start, const uint32_t *rpref, const uint32_t *nrng,
                         Tile *tiles, uint64_t *words, uint64_t *cands, hipStream_t s);
 
+// Per row tile t: tref[t * nb + b] = per-dimension lower median of up to 32
+// of the tile's query rows spread evenly over it (block b of the
+// dimension-blocked layout xq, nq rows)
+hipError_t launch_tile_ref(const Tile *tiles, int64_t T, const float4 *xq, uint64_t nq, int nb, float4 *tref,
+                           hipStream_t s);
+
 // result = {batches, max batch words, failing tile + 1 (0 = ok), max batch rows}
 hipError_t launch_plan(const uint64_t *toff, const uint64_t *coff, const Tile *tiles, int64_t T,
                        int64_t n, uint64_t budget_words, uint32_t *bounds, uint64_t *row_bounds,
@@ -258,6 +264,13 @@ struct RefineArgs {
     uint8_t *gflag;               // per 4 mask words (aligned): 1 if any bit is set, else 0
     uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
     uint64_t row_base;            // first query row of the batch
+    // split-fp16 operands prepared once per point (k_refine_g16): points and
+    // query rows, [slabs][4 parts][rows] x 16 bytes, and their norms
+    const uint4 *p16, *p16q;
+    const float *n16, *n16q;
+    // MFMA kernels that centre per row tile: reference of tile t at
+    // tref[t * nb .. t * nb + nb - 1] (the first query row of the tile when NULL)
+    const float4 *tref;
 };
 hipError_t launch_refine_direct(const RefineArgs &a, hipStream_t s);
 
@@ -309,6 +322,20 @@ int refine_mfma_qblocks(int nb);
 size_t refine_mfma_lds_bytes(int nb);
 hipError_t prepare_refine_mfma(int nb, bool f16);
 hipError_t launch_refine_mfma(const RefineArgs &a, bool f16, hipStream_t s);
+
+// k_refine_m16.hip: split-fp16 refinement for nb <= 16 (d <= 64), one row
+// tile per work item (nsub = 1), seg_len a multiple of 512 and <= 8192
+bool refine_m16_supported(int nb);
+hipError_t prepare_refine_m16(int nb);
+hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
+
+// k_refine_g16.hip: split-fp16 refinement for nb > 16 on operands prepared by
+// launch_prep16 (rows of xs centred by -nrs / s, scaled by s, split; P needs
+// ceil(nb / 4) * 4 * n uint4, N n floats); nsub = 1, seg_len a multiple of 512
+hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, uint4 *P, float *N,
+                         hipStream_t st);
+hipError_t prepare_refine_g16();
+hipError_t launch_refine_g16(const RefineArgs &a, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
 // Band-list bookkeeping after a refinement launch: out[0] = entries kept

@@ -735,6 +735,46 @@ __global__ __launch_bounds__(kBlock) void k_tiles(const uint64_t *__restrict__ t
 // Greedy window batching over row tiles in index order: a batch grows while
 // its mask words stay within the budget.  result = {batches, max words,
 // failing tile + 1 (0 = ok)}.
+// Reference point of each row tile for the MFMA refinement's centring: per
+// dimension the lower median of up to 32 of the tile's rows, taken evenly
+// spread over it (rows i m / 32).  Any fp32 point serves the error analysis;
+// a median keeps the rows' norms about it small when most of the tile's rows
+// lie in one cluster, whatever its first row is.  One workgroup per tile;
+// each thread ranks one sampled row's value in one dimension among the
+// samples (ties by sample index), eight dimensions per pass.
+constexpr int kRefSamples = 32;
+
+__global__ __launch_bounds__(256) void k_tile_ref(const Tile *__restrict__ tiles, const float4 *__restrict__ xq,
+                                                  uint64_t nq, int nb, float4 *__restrict__ tref)
+{
+    __shared__ float vals[8][kRefSamples];
+    const uint32_t t = blockIdx.x;
+    const Tile tl = tiles[t];
+    const int m = (int)min((uint32_t)kTileRows, tl.nrows);
+    const int ms = min(m, kRefSamples);
+    const int tid = threadIdx.x;
+    const int i = tid & (kRefSamples - 1), dd = tid >> 5;  // sample, dimension of the pass
+    const int med = (ms - 1) / 2;
+    for (int b0 = 0; b0 < nb; b0 += 2) {
+        const int b = b0 + (dd >> 2), c = dd & 3;
+        __syncthreads();
+        if (i < ms && b < nb) {
+            const float4 v = xq[(uint64_t)b * nq + tl.row0 + (uint32_t)(i * m / ms)];
+            vals[dd][i] = c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+        }
+        __syncthreads();
+        if (i < ms && b < nb) {
+            const float v = vals[dd][i];
+            int rank = 0;
+            for (int j = 0; j < ms; ++j) {
+                const float w = vals[dd][j];
+                rank += (w < v) || (w == v && j < i);
+            }
+            if (rank == med) ((float *)&tref[(uint64_t)t * nb + b])[c] = v;
+        }
+    }
+}
+
 __global__ void k_plan(const uint64_t *__restrict__ toff, const uint64_t *__restrict__ coff,
                        const Tile *__restrict__ tiles, int64_t T, int64_t n, uint64_t budget,
                        uint32_t *__restrict__ bounds, uint64_t *__restrict__ row_bounds,
@@ -952,6 +992,15 @@ hipError_t launch_tiles(const uint64_t *tile_base, int64_t M, int64_t T, const u
 {
     hipLaunchKernelGGL(k_tiles, dim3(grid_for(T)), dim3(kBlock), 0, s, tile_base, M, T, cell_start,
                        rpref, nrng, tiles, words, cands);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_ref(const Tile *tiles, int64_t T, const float4 *xq, uint64_t nq, int nb, float4 *tref,
+                           hipStream_t s)
+{
+    if (T == 0) return hipSuccess;
+    if (T > 0x7fffffffll) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_tile_ref, dim3((unsigned)T), dim3(256), 0, s, tiles, xq, nq, nb, tref);
     return hipGetLastError();
 }
 

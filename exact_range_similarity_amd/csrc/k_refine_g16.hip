@@ -1,0 +1,358 @@
+// Candidate refinement for gfx950, split-fp16 form on MFMA, for more than 64
+// dimensions, with operands prepared once per point.
+//
+// Method: "RT-HiSS: Ray Tracing Accelerated High Dimensional Vector
+// Similarity Searches", Sec. IV-E (a thread block per group of queries that
+// share their candidates, staged through on-chip memory) and Sec. IV-F (one
+// result bit per comparison).
+//
+// The split-fp16 arithmetic of k_refine_mfma.hip with one reference point
+// for all pairs, the per-dimension mean r of the points (fp32): every point
+// and query row is centred and scaled once, v = fl((x - r) s) (computed as
+// fma(x, s, -(r s)), the same value while r s is exact), split into fp16
+// halves and stored with its fp32 norm |v|^2 (k_prep16).  The band analysis
+// of the split form holds for any fp32 reference shared by the two points of
+// a pair; a single one pays off when the data lie around a common centre (for
+// unit-norm rows the norms are about 1, less than the squared distance
+// between two rows), and in high dimension it takes the centring and
+// splitting out of the refinement loop, whose arithmetic is then the matrix
+// products alone.
+//
+// Work item: (row tile of up to 128 query rows of one cell, segment of the
+// cell's candidate list), in steps of 256 candidates.  Wave w computes rows
+// 64 (w % 2) .. +63 against candidates 128 (w / 2) .. +127 of a step: two
+// 32-row blocks times four 32-candidate groups, eight 32 x 32 accumulators.
+// The step runs over the 16-dimension slabs; each slab's fp16 halves of the
+// tile's rows (8 KiB) and of the step's candidates (16 KiB) are copied from
+// HBM into one of two LDS buffers while the previous slab's 24 MFMAs per wave
+// run: one barrier per slab.  After the last slab the accumulators are
+// classified (classify_block, same band and thresholds as k_refine_mfma) and
+// mask words leave every 512 candidates as aligned 64-byte row pieces.
+#include "refine_mfma_common.h"
+
+namespace ersj {
+
+namespace {
+
+constexpr int kRowsG = 128;                         // query rows per work item
+constexpr int kStepG = 256;                         // candidates per step
+constexpr int kGroupStepsG = kGroupCands / kStepG;  // steps per 512-candidate word group
+constexpr int kMaxStepsG = 8192 / kStepG;
+
+struct G16 {
+    static constexpr size_t A = 0;                                        // [2][4][kRowsG] x 16 B
+    static constexpr size_t B = A + (size_t)2 * 4 * kRowsG * 16;           // [2][4][kStepG] x 16 B
+    static constexpr size_t XI = B + (size_t)2 * 4 * kStepG * 16;          // [2][kStepG] u32
+    static constexpr size_t NX = XI + (size_t)2 * kStepG * 4;              // [2][kStepG] f32
+    static constexpr size_t QIN = NX + (size_t)2 * kStepG * 4;             // [kRowsG] f32
+    static constexpr size_t QOUT = QIN + (size_t)kRowsG * 4;
+    static constexpr size_t RCNT = QOUT + (size_t)kRowsG * 4;             // [kRowsG] u32
+    static constexpr size_t PREF = RCNT + (size_t)kRowsG * 4;             // [kMaxRanges + 1] u32
+    static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;  // [kMaxRanges] u32
+    static constexpr size_t WORDS = (START + (size_t)kMaxRanges * 4 + 63) & ~(size_t)63;  // [2][kRowsG][8] u64
+    static constexpr size_t BYTES = WORDS + (size_t)2 * kRowsG * 8 * 8;
+};
+
+// Operands of one point set: centred, scaled, split, in slab-major parts
+// (part 0: high halves of a slab's dimensions 0-7, 1: high 8-15, 2 and 3:
+// the low halves), and the norms.
+__global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, uint64_t n, int nb, int ns,
+                                                const float4 *__restrict__ nrs, float s, uint4 *__restrict__ P,
+                                                float *__restrict__ N)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float nrm = 0.f;
+    for (int sl = 0; sl < ns; ++sl) {
+        half8 h0, h1, l0, l1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int b = sl * 4 + j;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (b < nb) {
+                const float4 x = xs[(uint64_t)b * n + i];
+                const float4 r = nrs[b];
+                v = make_float4(fmaf(x.x, s, r.x), fmaf(x.y, s, r.y), fmaf(x.z, s, r.z), fmaf(x.w, s, r.w));
+            }
+            nrm = fmaf(v.x, v.x, nrm);
+            nrm = fmaf(v.y, v.y, nrm);
+            nrm = fmaf(v.z, v.z, nrm);
+            nrm = fmaf(v.w, v.w, nrm);
+            half4 hh, ll;
+            split16(v, hh, ll);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (j < 2) {
+                    h0[(j & 1) * 4 + k] = hh[k];
+                    l0[(j & 1) * 4 + k] = ll[k];
+                } else {
+                    h1[(j & 1) * 4 + k] = hh[k];
+                    l1[(j & 1) * 4 + k] = ll[k];
+                }
+            }
+        }
+        P[((uint64_t)sl * 4 + 0) * n + i] = *(const uint4 *)&h0;
+        P[((uint64_t)sl * 4 + 1) * n + i] = *(const uint4 *)&h1;
+        P[((uint64_t)sl * 4 + 2) * n + i] = *(const uint4 *)&l0;
+        P[((uint64_t)sl * 4 + 3) * n + i] = *(const uint4 *)&l1;
+    }
+    N[i] = nrm;
+}
+
+__global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
+{
+    using G = G16;
+    uint32_t rk, colx;
+    work_item(blockIdx.x, a.ntiles, a.nseg, &rk, &colx);
+    const uint32_t seg = colx;
+    const uint32_t t = a.order[a.ord0 + rk];
+    const Tile tl = a.tiles[t];
+    const uint32_t A = tl.cell;
+    const uint32_t nr = a.nrng[A];
+    const uint32_t *pref_g = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+    const uint32_t U = pref_g[nr];
+    const uint32_t c_begin = seg * a.seg_len;
+    if (c_begin >= U) return;
+    const uint32_t c_end = min(U, c_begin + a.seg_len);
+    const uint32_t nrows = min((uint32_t)kRowsG, tl.nrows);
+    const uint32_t row0 = tl.row0;
+    const int ns = (a.nb + 3) / 4;
+
+    extern __shared__ __align__(16) unsigned char smemg[];
+    uint4 *const LA = (uint4 *)(smemg + G::A);
+    uint4 *const LB = (uint4 *)(smemg + G::B);
+    uint32_t *const LXI = (uint32_t *)(smemg + G::XI);
+    float *const LNX = (float *)(smemg + G::NX);
+    float *const LQIN = (float *)(smemg + G::QIN);
+    float *const LQOUT = (float *)(smemg + G::QOUT);
+    uint32_t *const LRCNT = (uint32_t *)(smemg + G::RCNT);
+    uint32_t *const LPREF = (uint32_t *)(smemg + G::PREF);
+    uint32_t *const LSTART = (uint32_t *)(smemg + G::START);
+    uint64_t *const LWORDS = (uint64_t *)(smemg + G::WORDS);
+
+    const int tid = threadIdx.x;
+    const uint64_t n = a.n, nqr = a.nqr;
+    const uint4 *__restrict__ P = a.p16;
+    const uint4 *__restrict__ PQ = a.p16q;
+    const float *__restrict__ NP = a.n16;
+    uint64_t *__restrict__ mask = a.mask;
+    const uint32_t W = tl.words;
+    const uint64_t mbase = a.toff[t] - a.wbase;
+
+    if (tid <= kMaxRanges) LPREF[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
+    if (tid < kMaxRanges) LSTART[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
+    if (tid < kRowsG) {
+        const bool valid = (uint32_t)tid < nrows;
+        const float nq = valid ? a.n16q[row0 + tid] : 0.f;
+        LQIN[tid] = valid ? a.tlo - a.kp * nq - a.tabs : -INFINITY;
+        LQOUT[tid] = valid ? a.thi - a.km * nq + a.tabs : -INFINITY;
+        LRCNT[tid] = 0;
+    }
+    for (int e = tid; e < 2 * kRowsG * 8; e += 256) LWORDS[e] = 0ull;
+    __syncthreads();
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int col = lane & 31, hi = lane >> 5;
+    const int rh = wave & 1, cg = wave >> 1;
+    const bool do0 = (uint32_t)(rh * 64) < nrows, do1 = (uint32_t)(rh * 64 + 32) < nrows;
+    const uint32_t nsteps = (c_end - c_begin + kStepG - 1) / kStepG;  // <= kMaxStepsG
+    const uint32_t units = nsteps * (uint32_t)ns;
+    const BandSink bsink{band_list(a.blist, a.lcap), band_counter(a.bcount), a.lcap, row0, mbase, W};
+
+    // loader: lane l of wave w copies part w of query rows l and 64 + l, and
+    // all four parts of candidate 64 w + l of the step
+    const uint32_t qa = row0 + min((uint32_t)lane, nrows - 1), qb2 = row0 + min((uint32_t)(64 + lane), nrows - 1);
+    uint32_t g_u = 0;
+    const uint32_t idx0 = [&]() {
+        const int g = range_of(LPREF, nr, c_begin);
+        return LSTART[g] + (c_begin - LPREF[g]);
+    }();
+    auto cand_index = [&](uint32_t st) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t P0 = c_begin + st * kStepG;
+        while (P0 >= (uint32_t)__builtin_amdgcn_readfirstlane(LPREF[g_u + 1])) ++g_u;
+        const uint32_t p = P0 + (uint32_t)(wave * 64 + lane);
+        if (p >= c_end) return idx0;
+        uint32_t g = g_u;
+        const uint32_t nxt = __builtin_amdgcn_readfirstlane(LPREF[g_u + 1]);
+        if (P0 + kStepG > nxt) {
+            while (p >= LPREF[g + 1]) ++g;
+        }
+        return LSTART[g] - LPREF[g] + p;
+    };
+    uint4 ra0, ra1, rb[4];
+    uint32_t ci = idx0;
+    float cn = 0.f;
+    auto issue = [&](uint32_t u) __attribute__((always_inline)) {
+        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
+        if (sl == 0) {
+            ci = cand_index(st);
+            cn = NP[ci];
+        }
+        ra0 = PQ[((uint64_t)sl * 4 + wave) * nqr + qa];
+        ra1 = PQ[((uint64_t)sl * 4 + wave) * nqr + qb2];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rb[p] = P[((uint64_t)sl * 4 + p) * n + ci];
+    };
+    auto deposit = [&](uint32_t u) __attribute__((always_inline)) {
+        const int buf = (int)(u & 1);
+        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
+        uint4 *la = LA + (size_t)buf * 4 * kRowsG;
+        uint4 *lb = LB + (size_t)buf * 4 * kStepG;
+        la[wave * kRowsG + lane] = ra0;
+        la[wave * kRowsG + 64 + lane] = ra1;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) lb[p * kStepG + wave * 64 + lane] = rb[p];
+        if (sl == 0) {
+            LXI[(st & 1) * kStepG + wave * 64 + lane] = ci;
+            LNX[(st & 1) * kStepG + wave * 64 + lane] = cn;
+        }
+    };
+
+    floatx16 acc[2][4];
+    auto mma = [&](int buf, bool fresh) __attribute__((always_inline)) {
+        const uint4 *la = LA + (size_t)buf * 4 * kRowsG;
+        const uint4 *lb = LB + (size_t)buf * 4 * kStepG;
+        half8 ah[2], al[2], bh[4], bl[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = rh * 64 + i * 32 + col;
+            ah[i] = *(const half8 *)&la[hi * kRowsG + r];
+            al[i] = *(const half8 *)&la[(2 + hi) * kRowsG + r];
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int c = cg * 128 + tt * 32 + col;
+            bh[tt] = *(const half8 *)&lb[hi * kStepG + c];
+            bl[tt] = *(const half8 *)&lb[(2 + hi) * kStepG + c];
+        }
+        const floatx16 z = {};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (!(i == 0 ? do0 : do1)) continue;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], fresh ? z : acc[i][tt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (!(i == 0 ? do0 : do1)) continue;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bl[tt], acc[i][tt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (!(i == 0 ? do0 : do1)) continue;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bh[tt], acc[i][tt], 0, 0, 0);
+        }
+    };
+
+    int wsel = 0;  // group buffer of the current 512-candidate group (toggles at each flush)
+    auto classify = [&](uint32_t st) __attribute__((always_inline)) {
+        uint64_t *wg = LWORDS + (size_t)wsel * kRowsG * 8;
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+            const uint32_t cw = c_begin + st * kStepG + cg * 128 + w2 * 64;
+            float xin[2], xout[2];
+            uint32_t xid[2];
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const int cl = cg * 128 + w2 * 64 + t2 * 32 + col;
+                const float nx = LNX[(st & 1) * kStepG + cl];
+                xid[t2] = LXI[(st & 1) * kStepG + cl];
+                const bool valid = cw + 32 * t2 + col < c_end;
+                xin[t2] = valid ? a.kp * nx : __builtin_nanf("");
+                xout[t2] = valid ? a.km * nx : __builtin_nanf("");
+            }
+            const int wi = (int)(st % kGroupStepsG) * 4 + cg * 2 + w2;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (!(i == 0 ? do0 : do1)) continue;
+                const int qb = rh * 2 + i;
+                classify_block(&acc[i][w2 * 2], xin, xout, LQIN, LQOUT, qb, lane, cw, 3u, bsink,
+                               [&](int t2) { return xid[t2]; }, wg + (qb * 32 + col) * 8 + wi);
+            }
+        }
+    };
+    auto unit_flag = [&](int row, int j, uint32_t w, bool ok, bool nz) __attribute__((always_inline)) {
+        const uint64_t b = __ballot(nz);
+        if (ok && (j & 3) == 0) a.gflag[(mbase + (uint64_t)row * W + w) >> 2] = ((b >> (lane & ~3)) & 0xfull) ? 1 : 0;
+    };
+    auto flush = [&](uint32_t grp) __attribute__((always_inline)) {
+        uint64_t *sw = LWORDS + (size_t)wsel * kRowsG * 8;
+        for (int e = tid; e < kRowsG * 8; e += 256) {
+            const int row = e >> 3, j = e & 7;
+            const uint32_t c0 = c_begin + grp * kGroupCands + 64 * j;
+            const uint32_t w = c0 >> 6;
+            const bool ok = (uint32_t)row < nrows && w < W && c0 < c_end;
+            const uint64_t v = sw[e];
+            if (ok) {
+                mask[mbase + (uint64_t)row * W + w] = v;
+                const uint32_t pc = __popcll(v);
+                if (pc != 0) atomicAdd(&LRCNT[row], pc);
+            }
+            unit_flag(row, j, w, ok, ok && v != 0);
+            sw[e] = 0ull;
+        }
+    };
+
+    if (units > 0) {
+        issue(0);
+        deposit(0);
+    }
+    __syncthreads();
+    for (uint32_t u = 0; u < units; ++u) {
+        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
+        const bool more = u + 1 < units;
+        if (more) issue(u + 1);
+        if (do0 || do1) {
+            mma((int)(u & 1), sl == 0);
+            if (sl + 1 == (uint32_t)ns) classify(st);
+        }
+        if (more) deposit(u + 1);
+        __syncthreads();
+        if (sl + 1 == (uint32_t)ns && (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps)) {
+            flush(st / kGroupStepsG);
+            wsel ^= 1;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < (int)nrows; i += 256)
+        if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
+}
+
+}  // namespace
+
+hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, uint4 *P, float *N,
+                         hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const int ns = (nb + 3) / 4;
+    const uint64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, P, N);
+    return hipGetLastError();
+}
+
+hipError_t prepare_refine_g16()
+{
+    return hipFuncSetAttribute((const void *)k_refine_g16, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)G16::BYTES);
+}
+
+hipError_t launch_refine_g16(const RefineArgs &a, hipStream_t s)
+{
+    if (a.seg_len % kGroupCands != 0 || a.seg_len / kStepG > (uint32_t)kMaxStepsG) return hipErrorInvalidValue;
+    if (!a.p16 || !a.p16q || !a.n16 || !a.n16q) return hipErrorInvalidValue;
+    const uint64_t blocks = (uint64_t)a.ntiles * a.nseg;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    RefineArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel((const void *)k_refine_g16, dim3((unsigned)blocks), dim3(256), params, G16::BYTES, s);
+}
+
+}  // namespace ersj

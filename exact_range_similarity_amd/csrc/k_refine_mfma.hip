@@ -7,7 +7,9 @@
 // comparison).
 //
 // Squared distances are formed as |q'|^2 + |x'|^2 - 2 q'.x' on coordinates
-// centred on the work item's first query r (q' = q - r, x' = x - r, fp32).
+// centred on a reference point r of the row tile (q' = q - r, x' = x - r,
+// fp32): the per-dimension median of the tile's rows (k_tile_ref), or the
+// work item's first query row.
 // F16 = false: q'.x' from v_mfma_f32_32x32x2f32.  F16 = true (split form):
 // the centred coordinates are multiplied by a power of two s that keeps
 // them below 2^14 and split into fp16 parts h + l (l = fl16(v - h)); the
@@ -172,7 +174,8 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     if (tid <= kMaxRanges) L.pref[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
     if (tid < kMaxRanges) L.start[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
     for (int b = tid; b < nbs; b += 256)
-        L.r[b] = b < nb ? xq[(uint64_t)b * nqr + row0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        L.r[b] = b >= nb ? make_float4(0.f, 0.f, 0.f, 0.f) : a.tref ? a.tref[(uint64_t)t * nb + b]
+                                                                     : xq[(uint64_t)b * nqr + row0];
     __syncthreads();
     for (int e = tid; e < nbs * G::QR; e += 256) {
         const int b = e / G::QR, i = e - b * G::QR;

@@ -61,7 +61,7 @@ def check(X, k, eps0, Q=None, rows=None, label="", **kw):
     return info
 
 
-@pytest.mark.parametrize("n,d,k", [(3001, 5, 1), (3001, 5, 7), (2500, 12, 64), (700, 40, 33)])
+@pytest.mark.parametrize("n,d,k", [(3001, 5, 1), (3001, 5, 7), (2500, 12, 64), (700, 40, 33), (900, 100, 20)])
 def test_random_adaptive(n, d, k):
     rng = np.random.default_rng(n + d + k)
     X = rng.random((n, d), dtype=np.float32)

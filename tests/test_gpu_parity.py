@@ -132,11 +132,16 @@ def test_large_d_and_offset_data():
     rng = np.random.default_rng(12)
     X = (rng.random((700, 700)) + 5.0).astype(np.float32)
     check_against_oracle(X, 10.5, "d=700 offset")
+    # at d = 2000 the fp32 MFMA form's query tile exceeds the LDS; the split
+    # form runs on operands prepared per point and is the automatic choice
     Z = (rng.random((300, 2000)) + 5.0).astype(np.float32)
-    check_against_oracle(Z, 17.0, "d=2000 offset", kernels=(ersj.REFINE_DIRECT,))
+    check_against_oracle(Z, 17.0, "d=2000 offset", kernels=(ersj.REFINE_DIRECT, ersj.REFINE_MFMA16))
     h = ersj.build_index(torch.from_numpy(Z).cuda(), 17.0)
-    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_DIRECT
+    assert ersj.get_stats(h)["refine_kernel"] == ersj.REFINE_MFMA16
     h.free()
+    with pytest.raises(ersj.ErsjError) as e:
+        ersj.build_index(torch.from_numpy(Z).cuda(), 17.0, ersj.default_options(refine_kernel=ersj.REFINE_MFMA))
+    assert e.value.code == ersj.ERR_INVALID_ARG
     Y = (rng.standard_normal((2000, 40)) * 0.01 + 100.0).astype(np.float32)
     check_against_oracle(Y, 0.085, "offset cluster")
 

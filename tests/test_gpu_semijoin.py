@@ -50,7 +50,8 @@ def check(Q, X, eps, label, kernels=KERNELS, budget=0):
 
 
 @pytest.mark.parametrize("nq,n,d", [(1, 500, 4), (700, 3000, 8), (4000, 2500, 16), (2100, 6000, 33),
-                                    (300, 300, 2), (513, 777, 1), (900, 1200, 3)])
+                                    (300, 300, 2), (513, 777, 1), (900, 1200, 3), (1500, 2000, 48),
+                                    (600, 900, 100), (257, 300, 200)])
 def test_random_queries(nq, n, d):
     rng = np.random.default_rng(nq * 7 + n + d)
     X = rng.random((n, d), dtype=np.float32)
