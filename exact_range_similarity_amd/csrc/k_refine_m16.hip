@@ -16,10 +16,12 @@
 //
 // Work decomposition (what differs from k_refine_mfma):
 //  - A workgroup (4 waves) takes one whole row tile (up to 128 query rows
-//    of a cell) and a segment of the cell's candidate list, in steps of 128
-//    candidates.  Wave w computes rows 64 (w % 2) .. +63 against candidates
-//    64 (w / 2) .. +63 of each step: two 32-row query blocks times two
-//    32-candidate halves, four 32 x 32 accumulators, 4096 pairs per step.
+//    of a cell) and a segment of the cell's candidate list.  Each wave
+//    holds QBW 32-row query blocks (QBW = 2: rows 64 (w % 2) .. +63 against
+//    candidates 64 (w / 2) .. +63 of a 128-candidate step, four 32 x 32
+//    accumulators; QBW = 1: rows 32 w .. +31 against the 64 candidates of a
+//    step, two accumulators and few enough registers for four waves per
+//    SIMD).
 //  - The query blocks' fp16 halves stay in registers for the whole work
 //    item (the MFMA A operands), so LDS carries only candidates.
 //  - A step's candidates are staged whole (all slabs) into one of two LDS
@@ -38,37 +40,42 @@ namespace ersj {
 
 namespace {
 
-constexpr int kRows = 128;                      // query rows per work item (one tile)
-constexpr int kStep = 128;                      // candidates per step
-constexpr int kGroupSteps = kGroupCands / kStep;  // steps per 512-candidate mask-word group
-constexpr int kMaxSteps16 = 8192 / kStep;       // steps of the longest segment
+constexpr int kRows = 128;  // query rows per work item (one tile)
 
-template <int NS>
+template <int NS, int QBW>
 struct M16 {
+    static constexpr int RW = 4 / QBW;          // waves per candidate group (row groups)
+    static constexpr int CG = QBW;              // candidate groups of 64 per step
+    static constexpr int STEP = 64 * CG;        // candidates per step
+    static constexpr int TPC = 256 / STEP;      // staging threads per candidate
     static constexpr int NBS = 4 * NS;          // float4 blocks per candidate (padded)
-    static constexpr int PER = NBS / 2;         // blocks staged per thread (two threads per candidate)
+    static constexpr int PER = NBS / TPC;       // blocks staged per thread
+    static constexpr int GS = kGroupCands / STEP;  // steps per 512-candidate mask-word group
+    static constexpr int MAXST = 8192 / STEP;   // steps of the longest segment
+    static constexpr int FW = MAXST / 64;       // 64-bit words of a step bit set
     static constexpr int WB = NS >= 4 ? 1 : 2;  // mask-word group buffers
     // LDS layout (bytes)
-    static constexpr size_t X = 0;                                         // [2][NS][4][kStep] x 16 B
-    static constexpr size_t NXP = X + (size_t)2 * NS * 4 * kStep * 16;      // [2][2][kStep] f32
-    static constexpr size_t XI = NXP + (size_t)2 * 2 * kStep * 4;           // [2][kStep] u32
-    static constexpr size_t NRS = XI + (size_t)2 * kStep * 4;               // [NBS] float4: -(r s)
+    static constexpr size_t X = 0;                                         // [2][NS][4][STEP] x 16 B
+    static constexpr size_t NXP = X + (size_t)2 * NS * 4 * STEP * 16;       // [2][TPC][STEP] f32
+    static constexpr size_t XI = NXP + (size_t)2 * TPC * STEP * 4;          // [2][STEP] u32
+    static constexpr size_t NRS = XI + (size_t)2 * STEP * 4;                // [NBS] float4: -(r s)
     static constexpr size_t QIN = NRS + (size_t)NBS * 16;                   // [kRows] f32
     static constexpr size_t QOUT = QIN + (size_t)kRows * 4;
     static constexpr size_t RCNT = QOUT + (size_t)kRows * 4;               // [kRows] u32
     static constexpr size_t NQMAX = RCNT + (size_t)kRows * 4;               // [4] f32
-    static constexpr size_t FAR = NQMAX + 16;                               // [4 waves] u64
-    static constexpr size_t LIVE = FAR + 4 * 8;                             // [kMaxSteps16] u32 (+1)
-    static constexpr size_t PREF = LIVE + (size_t)(kMaxSteps16 + 4) * 4;    // [kMaxRanges + 1] u32
+    static constexpr size_t FAR = NQMAX + 16;                               // [4 waves][FW] u64
+    static constexpr size_t LIVE = FAR + (size_t)4 * FW * 8;                // [MAXST] u32, count at MAXST + 1
+    static constexpr size_t PREF = LIVE + (size_t)(MAXST + 4) * 4;          // [kMaxRanges + 1] u32
     static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;    // [kMaxRanges] u32
     static constexpr size_t WORDS = (START + (size_t)kMaxRanges * 4 + 63) & ~(size_t)63;  // [WB][kRows][8] u64
     static constexpr size_t BYTES = WORDS + (size_t)WB * kRows * 8 * 8;
 };
 
-template <int NS>
-__global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
+template <int NS, int QBW>
+__global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs a)
 {
-    using G = M16<NS>;
+    using G = M16<NS, QBW>;
+    constexpr int kStep = G::STEP, kGroupSteps = G::GS, kMaxSteps16 = G::MAXST;
     uint32_t rk, colx;
     work_item(blockIdx.x, a.ntiles, a.nseg, &rk, &colx);
     const uint32_t seg = colx;
@@ -121,19 +128,23 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
     }
     if (tid < kRows) LRCNT[tid] = 0;
     for (int e = tid; e < G::WB * kRows * 8; e += 256) LWORDS[e] = 0ull;
+    // dimension blocks past nb are zero padding: staged as zeros once here
+    // and never written again
+    for (int e = tid; e < 2 * NS * 4 * kStep; e += 256) LX[e] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int col = lane & 31, hi = lane >> 5;
-    const int rh = wave & 1, cg = wave >> 1;  // row half, candidate group
+    const int rh = wave % G::RW, cg = wave / G::RW;  // row group, candidate group
+    const int rbase = rh * 32 * QBW;                 // first row of the wave's query blocks
 
     // ---- query blocks: fp16 halves in registers, norms, thresholds ----
-    half8 ah[2][NS], al[2][NS];
-    float qnorm[2];
+    half8 ah[QBW][NS], al[QBW][NS];
+    float qnorm[QBW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const uint32_t r = (uint32_t)(rh * 64 + i * 32 + col);
+    for (int i = 0; i < QBW; ++i) {
+        const uint32_t r = (uint32_t)(rbase + i * 32 + col);
         const bool valid = r < nrows;
         float nq = 0.f;
 #pragma unroll
@@ -168,25 +179,25 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
     // thresholds of the rows (lanes 0-31 of the waves of column group 0)
     if (cg == 0 && hi == 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = rh * 64 + i * 32 + col;
+        for (int i = 0; i < QBW; ++i) {
+            const int r = rbase + i * 32 + col;
             const bool valid = qnorm[i] >= 0.f;
             LQIN[r] = valid ? a.tlo - a.kp * qnorm[i] - a.tabs : -INFINITY;
             LQOUT[r] = valid ? a.thi - a.km * qnorm[i] + a.tabs : -INFINITY;
             float m = valid ? qnorm[i] : 0.f;
 #pragma unroll
             for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 32));
-            if (col == 0) LNQMAX[rh * 2 + i] = m;
+            if (col == 0) LNQMAX[r >> 5] = m;
         }
     }
 
     // ---- block box test of every step, up front ----
-    // the wave's two query blocks' boxes on the grid axes (lanes 0-31: block 0,
-    // lanes 32-63: block 1), made wave-uniform
-    float qlo[2][3], qhi[2][3];
-    uint32_t qrows[2];
+    // the wave's query blocks' boxes on the grid axes (lanes 0-31: block 0,
+    // lanes 32-63: block 1 if the wave holds two), made wave-uniform
+    float qlo[QBW][3], qhi[QBW][3];
+    uint32_t qrows[QBW];
     {
-        const uint32_t r = (uint32_t)(rh * 64 + hi * 32 + col);
+        const uint32_t r = (uint32_t)(rbase + (QBW == 2 ? hi : 0) * 32 + col);
         float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), up = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
         if (r < nrows) {
             lo = xq[row0 + r];
@@ -202,64 +213,81 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
             up.z = fmaxf(up.z, __shfl_xor(up.z, o, 64));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < QBW; ++i) {
             qlo[i][0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.x), i * 32));
             qlo[i][1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.y), i * 32));
             qlo[i][2] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.z), i * 32));
             qhi[i][0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.x), i * 32));
             qhi[i][1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.y), i * 32));
             qhi[i][2] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.z), i * 32));
-            const int rb = rh * 64 + i * 32;
+            const int rb = rbase + i * 32;
             qrows[i] = (uint32_t)rb < nrows ? min(32u, nrows - (uint32_t)rb) : 0u;
         }
     }
     const uint32_t nsteps = (c_end - c_begin + kStep - 1) / kStep;  // <= kMaxSteps16
     const float tbox = a.tbox;
     const bool tested = tbox < INFINITY;
-    // far0 / far1: steps in which query block 0 / 1 of this wave holds no
-    // neighbour (box test) or no row; the wave skips a step when both are set
-    uint64_t far0 = 0, far1 = 0;
+    // far[i]: steps (bit st) in which query block i of this wave holds no
+    // neighbour (box test) or no row; the wave skips a step when all are set
+    uint64_t far[QBW][G::FW];
+#pragma unroll
+    for (int i = 0; i < QBW; ++i)
+#pragma unroll
+        for (int f = 0; f < G::FW; ++f) far[i][f] = 0;
     uint64_t nskip = 0;
     {
         const uint64_t cb0 = tested ? a.chunk_base[A] : 0;
         for (uint32_t st = 0; st < nsteps; ++st) {
             const uint32_t gs = c_begin + st * kStep + cg * 64;
-            const uint64_t m = 1ull << st;
-            if (gs >= c_end) {
-                far0 |= m;
-                far1 |= m;
-                continue;
-            }
-            const uint32_t ncol = min(64u, c_end - gs);
-            bool f0 = qrows[0] == 0, f1 = qrows[1] == 0;
-            if (tested && !(f0 && f1)) {
+            const uint64_t m = 1ull << (st & 63);
+            const int fw = (int)(st >> 6);
+            bool f[QBW];
+#pragma unroll
+            for (int i = 0; i < QBW; ++i) f[i] = gs >= c_end || qrows[i] == 0;
+            if (tested && gs < c_end) {
+                const uint32_t ncol = min(64u, c_end - gs);
                 const float4 *cb = a.cbox + 2 * (cb0 + (gs >> 6));
                 const float4 blo = cb[0], bhi = cb[1];
-                if (!f0 && box_gap2(qlo[0], qhi[0], blo, bhi) > tbox) {
-                    f0 = true;
-                    nskip += (uint64_t)qrows[0] * ncol;
-                }
-                if (!f1 && box_gap2(qlo[1], qhi[1], blo, bhi) > tbox) {
-                    f1 = true;
-                    nskip += (uint64_t)qrows[1] * ncol;
+#pragma unroll
+                for (int i = 0; i < QBW; ++i) {
+                    if (!f[i] && box_gap2(qlo[i], qhi[i], blo, bhi) > tbox) {
+                        f[i] = true;
+                        nskip += (uint64_t)qrows[i] * ncol;
+                    }
                 }
             }
-            if (f0) far0 |= m;
-            if (f1) far1 |= m;
+#pragma unroll
+            for (int i = 0; i < QBW; ++i)
+#pragma unroll
+                for (int w2 = 0; w2 < G::FW; ++w2)
+                    if (f[i] && w2 == fw) far[i][w2] |= m;
         }
     }
     // far bits are wave-uniform (computed from uniform values); make it explicit
-    far0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(far0 >> 32)) << 32) |
-           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)far0);
-    far1 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(far1 >> 32)) << 32) |
-           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)far1);
-    if (lane == 0) LFAR[wave] = far0 & far1;
+#pragma unroll
+    for (int i = 0; i < QBW; ++i)
+#pragma unroll
+        for (int w2 = 0; w2 < G::FW; ++w2)
+            far[i][w2] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(far[i][w2] >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)far[i][w2]);
+    if (lane == 0) {
+#pragma unroll
+        for (int w2 = 0; w2 < G::FW; ++w2) {
+            uint64_t all = ~0ull;
+#pragma unroll
+            for (int i = 0; i < QBW; ++i) all &= far[i][w2];
+            LFAR[wave * G::FW + w2] = all;
+        }
+    }
     __syncthreads();
     if (tid == 0) {
-        const uint64_t all = LFAR[0] & LFAR[1] & LFAR[2] & LFAR[3];
         uint32_t c = 0;
-        for (uint32_t st = 0; st < nsteps; ++st)
-            if (!((all >> st) & 1ull)) LLIVE[c++] = st;
+        for (uint32_t st = 0; st < nsteps; ++st) {
+            const int w2 = (int)(st >> 6);
+            const uint64_t all = LFAR[0 * G::FW + w2] & LFAR[1 * G::FW + w2] & LFAR[2 * G::FW + w2] &
+                                 LFAR[3 * G::FW + w2];
+            if (!((all >> (st & 63)) & 1ull)) LLIVE[c++] = st;
+        }
         LLIVE[kMaxSteps16 + 1] = c;
     }
     __syncthreads();
@@ -267,22 +295,22 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
     const uint32_t ngroups = (nsteps + kGroupSteps - 1) / kGroupSteps;
 
     // ---- the norm test's bound per query block (see k_refine_mfma) ----
-    float tn[2];
+    float tn[QBW];
     {
         const float nt = 4.0f * (float)nb + 4.0f;
         const float g = nt * 0x1p-24f / (1.0f - nt * 0x1p-24f);
         const float c1 = 1.0f + g + 0x1p-18f, c2 = 1.0f + 2.0f * g + 0x1p-16f;
         const float st = sqrtf(a.thi) * c1;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const float sq = sqrtf(LNQMAX[rh * 2 + i]) * c1;
+        for (int i = 0; i < QBW; ++i) {
+            const float sq = sqrtf(LNQMAX[(rbase >> 5) + i]) * c1;
             tn[i] = ((sq + st) * (sq + st)) * c2;
         }
     }
     const BandSink bsink{band_list(a.blist, a.lcap), band_counter(a.bcount), a.lcap, row0, mbase, W};
 
-    // ---- loader: thread t stages candidate c = t % 128, blocks h + 2 m ----
-    const int lc = tid & (kStep - 1), lh = tid >> 7;
+    // ---- loader: thread t stages candidate c = t % STEP, blocks h + TPC m ----
+    const int lc = tid % kStep, lh = tid / kStep;
     uint32_t g_u = 0;  // range of the step's first position (wave-uniform, advances)
     const uint32_t idx0 = [&]() {
         const int g = range_of(LPREF, nr, c_begin);
@@ -306,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
         ldi = cand_index(st);
 #pragma unroll
         for (int m = 0; m < G::PER; ++m) {
-            const int b = lh + 2 * m;
+            const int b = lh + G::TPC * m;
             ld[m] = b < nb ? xs[(uint64_t)b * n + ldi] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
@@ -315,12 +343,12 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
         unsigned char *xb = (unsigned char *)(LX + (size_t)buf * NS * 4 * kStep);
 #pragma unroll
         for (int m = 0; m < G::PER; ++m) {
-            const int b = lh + 2 * m;
+            const int b = lh + G::TPC * m;  // wave-uniform
+            if (b >= nb) continue;
             const float4 nr4 = LNRS[b];
             const float4 x = ld[m];
-            float4 v = make_float4(fmaf(x.x, s16, nr4.x), fmaf(x.y, s16, nr4.y), fmaf(x.z, s16, nr4.z),
-                                   fmaf(x.w, s16, nr4.w));
-            if (b >= nb) v = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 v = make_float4(fmaf(x.x, s16, nr4.x), fmaf(x.y, s16, nr4.y), fmaf(x.z, s16, nr4.z),
+                                         fmaf(x.w, s16, nr4.w));
             s2 = fmaf(v.x, v.x, s2);
             s2 = fmaf(v.y, v.y, s2);
             s2 = fmaf(v.z, v.z, s2);
@@ -332,55 +360,43 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
             *(half4 *)(xb + ((size_t)(sl * 4 + p) * kStep + lc) * 16 + o) = hh;
             *(half4 *)(xb + ((size_t)(sl * 4 + 2 + p) * kStep + lc) * 16 + o) = ll;
         }
-        LNXP[(buf * 2 + lh) * kStep + lc] = s2;
+        LNXP[(buf * G::TPC + lh) * kStep + lc] = s2;
         if (lh == 0) LXI[buf * kStep + lc] = ldi;
     };
 
-    floatx16 acc[2][2];
-    auto mma = [&](int buf, bool do0, bool do1) __attribute__((always_inline)) {
+    floatx16 acc[QBW][2];
+    auto mma = [&](int buf, const bool (&dq)[QBW]) __attribute__((always_inline)) {
         const uint4 *xb = LX + (size_t)buf * NS * 4 * kStep;
         const int c0 = cg * 64 + col;
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
-            const half8 bh0 = *(const half8 *)&xb[(sl * 4 + hi) * kStep + c0];
-            const half8 bh1 = *(const half8 *)&xb[(sl * 4 + hi) * kStep + c0 + 32];
-            const half8 bl0 = *(const half8 *)&xb[(sl * 4 + 2 + hi) * kStep + c0];
-            const half8 bl1 = *(const half8 *)&xb[(sl * 4 + 2 + hi) * kStep + c0 + 32];
-            if (sl == 0) {
-                const floatx16 z = {};
-                if (do0) {
-                    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][0], bh0, z, 0, 0, 0);
-                    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][0], bh1, z, 0, 0, 0);
-                }
-                if (do1) {
-                    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][0], bh0, z, 0, 0, 0);
-                    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][0], bh1, z, 0, 0, 0);
-                }
-            } else {
-                if (do0) {
-                    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][sl], bh0, acc[0][0], 0, 0, 0);
-                    acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][sl], bh1, acc[0][1], 0, 0, 0);
-                }
-                if (do1) {
-                    acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][sl], bh0, acc[1][0], 0, 0, 0);
-                    acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][sl], bh1, acc[1][1], 0, 0, 0);
-                }
+            const half8 bh[2] = {*(const half8 *)&xb[(sl * 4 + hi) * kStep + c0],
+                                 *(const half8 *)&xb[(sl * 4 + hi) * kStep + c0 + 32]};
+            const half8 bl[2] = {*(const half8 *)&xb[(sl * 4 + 2 + hi) * kStep + c0],
+                                 *(const half8 *)&xb[(sl * 4 + 2 + hi) * kStep + c0 + 32]};
+            const floatx16 z = {};
+            // three products, each accumulator touched every 2 QBW instructions
+#pragma unroll
+            for (int i = 0; i < QBW; ++i) {
+                if (!dq[i]) continue;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i][sl], bh[tt], sl == 0 ? z : acc[i][tt],
+                                                                        0, 0, 0);
             }
-            if (do0) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][sl], bl0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][sl], bl1, acc[0][1], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < QBW; ++i) {
+                if (!dq[i]) continue;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i][sl], bl[tt], acc[i][tt], 0, 0, 0);
             }
-            if (do1) {
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][sl], bl0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][sl], bl1, acc[1][1], 0, 0, 0);
-            }
-            if (do0) {
-                acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[0][sl], bh0, acc[0][0], 0, 0, 0);
-                acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[0][sl], bh1, acc[0][1], 0, 0, 0);
-            }
-            if (do1) {
-                acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[1][sl], bh0, acc[1][0], 0, 0, 0);
-                acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[1][sl], bh1, acc[1][1], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < QBW; ++i) {
+                if (!dq[i]) continue;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i][sl], bh[tt], acc[i][tt], 0, 0, 0);
             }
         }
     };
@@ -391,30 +407,33 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
     // two live steps are zero and take no buffer).
     int wsel = 0;
     // classification of live step st (buffer buf) into the group buffer
-    auto epilogue = [&](uint32_t st, int buf, bool do0, bool do1) __attribute__((always_inline)) {
+    auto epilogue = [&](uint32_t st, int buf, const bool (&dq)[QBW]) __attribute__((always_inline)) {
         const uint32_t cw = c_begin + st * kStep + cg * 64;
         float xin[2], xout[2], nxt[2];
         uint32_t xid[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const int cl = cg * 64 + 32 * tt + col;
-            nxt[tt] = LNXP[(buf * 2) * kStep + cl] + LNXP[(buf * 2 + 1) * kStep + cl];
+            float nsum = LNXP[(buf * G::TPC) * kStep + cl];
+#pragma unroll
+            for (int k = 1; k < G::TPC; ++k) nsum += LNXP[(buf * G::TPC + k) * kStep + cl];
+            nxt[tt] = nsum;
             xid[tt] = LXI[buf * kStep + cl];
             const bool valid = cw + 32 * tt + col < c_end;
             xin[tt] = valid ? a.kp * nxt[tt] : __builtin_nanf("");
             xout[tt] = valid ? a.km * nxt[tt] : __builtin_nanf("");
         }
         uint64_t *wg = LWORDS + (size_t)wsel * kRows * 8;
-        const int wi = (int)(st % kGroupSteps) * 2 + cg;
+        const int wi = (int)(st % kGroupSteps) * G::CG + cg;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (!(i == 0 ? do0 : do1)) continue;
+        for (int i = 0; i < QBW; ++i) {
+            if (!dq[i]) continue;
             uint32_t live = 0;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
                 if (__ballot(!(nxt[tt] > tn[i])) != 0) live |= 1u << tt;
             if (live == 0) continue;
-            const int qb = rh * 2 + i;
+            const int qb = (rbase >> 5) + i;
             classify_block(acc[i], xin, xout, LQIN, LQOUT, qb, lane, cw, live, bsink,
                            [&](int tt) { return xid[tt]; }, wg + (qb * 32 + col) * 8 + wi);
         }
@@ -468,10 +487,20 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
         const bool more = bi + 1 < nlive;
         const uint32_t st_next = more ? __builtin_amdgcn_readfirstlane(LLIVE[bi + 1]) : nsteps;
         if (more) issue(st_next);
-        const bool do0 = !((far0 >> st) & 1ull), do1 = !((far1 >> st) & 1ull);
-        if (do0 || do1) {
-            mma(buf, do0, do1);
-            epilogue(st, buf, do0, do1);
+        bool dq[QBW];
+        bool any = false;
+#pragma unroll
+        for (int i = 0; i < QBW; ++i) {
+            uint64_t fw = 0;
+#pragma unroll
+            for (int w2 = 0; w2 < G::FW; ++w2)
+                if ((int)(st >> 6) == w2) fw = far[i][w2];
+            dq[i] = !((fw >> (st & 63)) & 1ull);
+            any |= dq[i];
+        }
+        if (any) {
+            mma(buf, dq);
+            epilogue(st, buf, dq);
         }
         if (more) stage(buf ^ 1);
         __syncthreads();
@@ -492,13 +521,17 @@ __global__ __launch_bounds__(256, 2) void k_refine_m16(RefineArgs a)
         if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
 }
 
+// one query block per wave up to two slabs (four waves per SIMD), two from
+// three slabs on (the query halves fill the registers anyway)
+constexpr int qbw_of(int ns) { return ns <= 2 ? 1 : 2; }
+
 const void *m16_kernel(int ns)
 {
     switch (ns) {
-    case 1: return (const void *)k_refine_m16<1>;
-    case 2: return (const void *)k_refine_m16<2>;
-    case 3: return (const void *)k_refine_m16<3>;
-    case 4: return (const void *)k_refine_m16<4>;
+    case 1: return (const void *)k_refine_m16<1, 1>;
+    case 2: return (const void *)k_refine_m16<2, 1>;
+    case 3: return (const void *)k_refine_m16<3, 2>;
+    case 4: return (const void *)k_refine_m16<4, 2>;
     default: return nullptr;
     }
 }
@@ -506,20 +539,22 @@ const void *m16_kernel(int ns)
 size_t m16_lds(int ns)
 {
     switch (ns) {
-    case 1: return M16<1>::BYTES;
-    case 2: return M16<2>::BYTES;
-    case 3: return M16<3>::BYTES;
-    case 4: return M16<4>::BYTES;
+    case 1: return M16<1, 1>::BYTES;
+    case 2: return M16<2, 1>::BYTES;
+    case 3: return M16<3, 2>::BYTES;
+    case 4: return M16<4, 2>::BYTES;
     default: return 0;
     }
 }
+
+uint32_t m16_step(int ns) { return (uint32_t)(64 * qbw_of(ns)); }
 
 }  // namespace
 
 // Used for three and four slabs (33 to 64 dimensions).  With one or two
 // slabs its two waves per SIMD (179 registers) hide load latency worse than
 // k_refine_mfma's four, which is then faster (c2: 9.3 against 13.4 ms).
-bool refine_m16_supported(int nb) { return nb > 8 && nb <= 16; }
+bool refine_m16_supported(int nb) { return nb >= 1 && nb <= 16; }
 
 hipError_t prepare_refine_m16(int nb)
 {
@@ -534,7 +569,8 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s)
     const int ns = (a.nb + 3) / 4;
     const void *k = m16_kernel(ns);
     if (!k) return hipErrorInvalidValue;
-    if (a.seg_len % kStep != 0 || a.seg_len / kStep > (uint32_t)kMaxSteps16) return hipErrorInvalidValue;
+    if (a.seg_len % kGroupCands != 0 || a.seg_len > 8192u || a.seg_len % m16_step(ns) != 0)
+        return hipErrorInvalidValue;
     const uint64_t blocks = (uint64_t)a.ntiles * a.nseg;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
