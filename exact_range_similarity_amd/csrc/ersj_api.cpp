@@ -363,7 +363,7 @@ void thresholds(ersj_index *h)
     // exact sum, which bounds the squared distance of every pair in the two
     // boxes from below; D64 is within gamma(d + 1) of the exact distance.
     // Above E (1 + 2^-20) the whole block is therefore out.
-    h->tbox = h->opt.block_prune < 0 ? INFINITY : round_up_f32(E * (1.0 + std::ldexp(1.0, -20)));
+    h->tbox = h->opt.block_prune < 0 ? INFINITY : round_up_f32(E * (1.0 + std::ldexp(1.0, -20)) + std::ldexp(1.0, -140));
 }
 
 // MFMA refinement: dot products of tile-centred coordinates.  Usable when
@@ -825,7 +825,8 @@ int do_count(ersj_index *h, hipStream_t s)
     HIPC(scan_u64(cands, h->coff, (int64_t)T, stmp, s), "candidate scan");
     HIPC(hipMemcpyAsync(&h->total_words, h->toff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(&h->total_cand, h->coff + T, sizeof(uint64_t), hipMemcpyDeviceToHost, s), "copy");
-    if ((h->kernel_used == ERSJ_REFINE_MFMA || h->kernel_used == ERSJ_REFINE_MFMA16) && std::isfinite(h->tbox)) {
+    if ((h->kernel_used == ERSJ_REFINE_MFMA || h->kernel_used == ERSJ_REFINE_MFMA16) && !h->use_g16 &&
+        std::isfinite(h->tbox)) {
         // boxes of each cell list's 64-candidate chunks for the block box test
         uint32_t *ccnt = nullptr;
         TRY(tmp.get(&ccnt, (size_t)M, "chunk boxes"));
@@ -835,8 +836,12 @@ int do_count(ersj_index *h, hipStream_t s)
         uint64_t nchunks = 0;
         HIPC(hipMemcpyAsync(&nchunks, h->chunk_base + M, sizeof nchunks, hipMemcpyDeviceToHost, s), "copy");
         TRY(sync(s, "chunk count"));
-        TRY(dalloc(h, &h->cbox, (size_t)nchunks * 2 + 2, "chunk boxes"));
-        HIPC(launch_chunk_boxes(h->chunk_base, M, nchunks, h->rstart, h->rpref, h->nrng, h->xs, h->cbox, s),
+        float4 *pbox = nullptr;
+        TRY(tmp.get(&pbox, (size_t)((h->n + 7) / 8 + 1) * 2 * kBoxBlocks, "point boxes"));
+        HIPC(launch_point_boxes(h->xs, (uint64_t)h->n, h->nb, pbox, s), "point box kernel");
+        TRY(dalloc(h, &h->cbox, (size_t)(nchunks + 1) * 2 * kBoxBlocks, "chunk boxes"));
+        HIPC(launch_chunk_boxes(h->chunk_base, M, nchunks, h->rstart, h->rpref, h->nrng, h->xs, (uint64_t)h->n,
+                                h->nb, pbox, h->cbox, s),
              "chunk box kernel");
     }
     if (h->use_g16) TRY(prepare_operands(h, s));

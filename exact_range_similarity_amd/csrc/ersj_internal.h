@@ -65,6 +65,41 @@ __device__ __forceinline__ float box_gap2(const float *alo, const float *ahi, fl
     const float gz = fmaxf(0.f, fmaxf(blo.z - ahi[2], alo[2] - bhi.z));
     return gx * gx + gy * gy + gz * gz;
 }
+
+// Candidate-chunk boxes cover the first kBoxBlocks float4 blocks of the
+// variance-ordered layout (dimensions 0-7; zero padding where d is
+// smaller): chunk ch has lo, hi of block b at cbox[(ch * kBoxBlocks + b) * 2
+// + 0, 1].  The refinement's box test sums the squared gaps of all 8
+// dimensions: a term takes one rounded difference and one rounded square,
+// (1 + u)^3, and at most 7 rounded additions follow it, so the fp32 sum is
+// within (1 + u)^10 < 1 + 2^-20 of the exact one (u = 2^-24), plus less than
+// 2^-146 where squares underflow; RefineArgs::tbox covers both.
+constexpr int kBoxBlocks = 2;
+
+__device__ __forceinline__ float gap4(float4 alo, float4 ahi, float4 blo, float4 bhi, float acc)
+{
+    const float gx = fmaxf(0.f, fmaxf(blo.x - ahi.x, alo.x - bhi.x));
+    const float gy = fmaxf(0.f, fmaxf(blo.y - ahi.y, alo.y - bhi.y));
+    const float gz = fmaxf(0.f, fmaxf(blo.z - ahi.z, alo.z - bhi.z));
+    const float gw = fmaxf(0.f, fmaxf(blo.w - ahi.w, alo.w - bhi.w));
+    return acc + gx * gx + gy * gy + gz * gz + gw * gw;
+}
+
+// lo = min, hi = max of all four components over the 64 lanes, in every lane
+__device__ __forceinline__ void wave_box4(float4 &lo, float4 &hi)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
+        lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
+        lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
+        lo.w = fminf(lo.w, __shfl_xor(lo.w, o, 64));
+        hi.x = fmaxf(hi.x, __shfl_xor(hi.x, o, 64));
+        hi.y = fmaxf(hi.y, __shfl_xor(hi.y, o, 64));
+        hi.z = fmaxf(hi.z, __shfl_xor(hi.z, o, 64));
+        hi.w = fmaxf(hi.w, __shfl_xor(hi.w, o, 64));
+    }
+}
 constexpr int kMaxDim = 4096;
 
 struct Tile {
@@ -145,9 +180,14 @@ struct CellSet {
 };
 hipError_t launch_chunk_counts(const uint32_t *rpref, const uint32_t *nrng, int64_t M, uint32_t *cnt,
                                hipStream_t s);
+// pbox: box of every 8 consecutive sorted points over the first kBoxBlocks
+// blocks of xs (n points, nb blocks; ceil(n / 8) groups, layout as cbox);
+// cbox: exact box of every 64-candidate chunk of every cell's candidate
+// list, from the group boxes and the points of partial groups
+hipError_t launch_point_boxes(const float4 *xs, uint64_t n, int nb, float4 *pbox, hipStream_t s);
 hipError_t launch_chunk_boxes(const uint64_t *base, int64_t M, uint64_t nchunks, const uint32_t *rstart,
-                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, float4 *cbox,
-                              hipStream_t s);
+                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, uint64_t n, int nb,
+                              const float4 *pbox, float4 *cbox, hipStream_t s);
 hipError_t launch_stencil(const CellSet &home, const CellSet &target, const GridParams &gp,
                           double prune_e2, uint32_t *rstart, uint32_t *rpref, uint32_t *nrng,
                           uint32_t *tiles_per_cell, unsigned int *umax, hipStream_t s);
@@ -255,10 +295,10 @@ struct RefineArgs {
     Boundary *blist;              // kBandLists sub-lists of lcap entries each
     unsigned long long *bcount;   // sub-list c's counter at bcount[c * kBandStride]
     uint64_t lcap;                // entries per sub-list
-    float tbox;                   // a query block and a candidate group whose boxes on the three
-                                  // grid axes have fp32 gap^2 sum > tbox hold no pair (inf: off)
-    const float4 *cbox;           // MFMA kernel, tbox finite: lo, hi on the grid axes of each
-                                  // 64-candidate chunk of each cell's candidate list
+    float tbox;                   // a query block and a candidate chunk whose boxes have an fp32
+                                  // gap^2 sum > tbox hold no pair (inf: off)
+    const float4 *cbox;           // MFMA kernels, tbox finite: box of each 64-candidate chunk of
+                                  // each cell's candidate list (kBoxBlocks blocks, see above)
     const uint64_t *chunk_base;   // first chunk of each cell
     unsigned long long *skipped;  // comparisons decided by that box test alone (kHitSlots slots)
     uint8_t *gflag;               // per 4 mask words (aligned): 1 if any bit is set, else 0

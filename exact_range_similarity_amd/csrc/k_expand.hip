@@ -259,17 +259,27 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 if (fm[k] & (1u << b)) s_list[i++] = (uint16_t)(4 * (256 * k + tid) + b);
         }
         __syncthreads();
-        for (uint32_t i0 = 0; i0 < nl; i0 += kUnitBatch) {
-            // thread tid: word tid & 3 of listed unit i0 + tid / 4
+        // thread tid: word tid & 3 of listed unit i0 + tid / 4; the next
+        // batch's word is loaded while this batch's bits are expanded
+        auto load_word = [&](uint32_t i0, uint64_t *m, uint32_t *wi, uint32_t *row) __attribute__((always_inline)) {
             const uint32_t e = i0 + (tid >> 2);
-            uint64_t m = 0ull;
-            uint32_t wi = 0, row = 0xffu;
+            *m = 0ull;
+            *wi = 0;
+            *row = 0xffu;
             if (e < nl) {
                 const uint32_t o = (uint32_t)(4 * c + s_list[e] - fb);
-                row = o / fstride;
-                wi = (o - row * fstride) * 4 + (tid & 3);
-                if (wi < tl.used) m = mask[tbase + (uint64_t)row * tl.words + wi];
+                *row = o / fstride;
+                *wi = (o - *row * fstride) * 4 + (tid & 3);
+                if (*wi < tl.used) *m = mask[tbase + (uint64_t)*row * tl.words + *wi];
             }
+        };
+        uint64_t m_next = 0ull;
+        uint32_t wi_next = 0, row_next = 0xffu;
+        if (nl > 0) load_word(0, &m_next, &wi_next, &row_next);
+        for (uint32_t i0 = 0; i0 < nl; i0 += kUnitBatch) {
+            const uint64_t m = m_next;
+            const uint32_t wi = wi_next, row = row_next;
+            if (i0 + kUnitBatch < nl) load_word(i0 + kUnitBatch, &m_next, &wi_next, &row_next);
             const uint32_t pc = __popcll(m);
             s_row[tid] = (uint8_t)row;
             uint32_t total;
@@ -282,7 +292,9 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
             if (first) s_rbase[row] = s_rpos[row] - excl;
             __syncthreads();
             if (last) s_rpos[row] = s_rbase[row] + excl + pc;
-            for (uint32_t j = tid; j < total; j += 256) {
+            // bit j of the batch -> (output position, query id, point); two
+            // bits per thread at a time, so two gathers of orig are in flight
+            auto locate = [&](uint32_t j, uint64_t *pos, uint32_t *qid, uint32_t *x) __attribute__((always_inline)) {
                 int lo = 0, hi = 255;  // the last slot with s_excl[slot] <= j
                 while (lo < hi) {
                     const int mid = (lo + hi + 1) >> 1;
@@ -291,15 +303,29 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 }
                 const uint32_t p = s_wi[lo] * 64 + nth_bit(s_word[lo], j - s_excl[lo]);
                 const int g = range_of(s_pref, nr, p);
-                const uint32_t x = s_start[g] + (p - s_pref[g]);
+                *x = s_start[g] + (p - s_pref[g]);
                 const uint32_t r = s_row[lo];
-                const uint64_t pos = s_rbase[r] + j;
+                *qid = s_qid[r];
+                *pos = s_rbase[r] + j;
+            };
+            auto put = [&](uint64_t pos, uint32_t qid, uint32_t id) __attribute__((always_inline)) {
                 if (al8) {
-                    ((uint2 *)pairs)[pos] = make_uint2(s_qid[r], orig[x]);
+                    ((uint2 *)pairs)[pos] = make_uint2(qid, id);
                 } else {
-                    pairs[2 * pos] = s_qid[r];
-                    pairs[2 * pos + 1] = orig[x];
+                    pairs[2 * pos] = qid;
+                    pairs[2 * pos + 1] = id;
                 }
+            };
+            for (uint32_t j = tid; j < total; j += 512) {
+                uint64_t pa, pb = 0;
+                uint32_t qa, xa, qb = 0, xb = 0;
+                const bool two = j + 256 < total;
+                locate(j, &pa, &qa, &xa);
+                if (two) locate(j + 256, &pb, &qb, &xb);
+                const uint32_t ia = orig[xa];
+                const uint32_t ib = two ? orig[xb] : 0u;
+                put(pa, qa, ia);
+                if (two) put(pb, qb, ib);
             }
             __syncthreads();
         }

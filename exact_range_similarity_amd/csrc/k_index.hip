@@ -642,8 +642,8 @@ __global__ __launch_bounds__(256) void k_stencil(CellSet home, CellSet target, G
 // ----------------------------------------------------------------- tiles --
 // ------------------------------------------------------- chunk boxes --
 // Chunks of 64 consecutive positions of each cell's candidate list: counts
-// per cell, then the box of each chunk's points on the grid axes (block 0
-// of the layout), for the refinement's block box test.
+// per cell, then the box of each chunk's points over the first kBoxBlocks
+// layout blocks, for the refinement's block box test.
 __global__ __launch_bounds__(kBlock) void k_chunk_counts(const uint32_t *__restrict__ rpref,
                                                          const uint32_t *__restrict__ nrng, int64_t M,
                                                          uint32_t *__restrict__ cnt)
@@ -654,46 +654,80 @@ __global__ __launch_bounds__(kBlock) void k_chunk_counts(const uint32_t *__restr
     cnt[A] = (U + 63) / 64;
 }
 
-// Wave per chunk: the chunk's cell A is the last with base[A] <= chunk.
+// Box of every 8 consecutive sorted points (the last group may be short)
+// over the first kBoxBlocks layout blocks: a thread per group and block.
+__global__ __launch_bounds__(256) void k_point_boxes(const float4 *__restrict__ xs, uint64_t n, int nb,
+                                                     uint64_t ngroups, float4 *__restrict__ pbox)
+{
+    const uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t k = g / kBoxBlocks;
+    const int b = (int)(g % kBoxBlocks);
+    if (k >= ngroups) return;
+    float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+    if (b < nb) {
+        const float4 *x = xs + (uint64_t)b * n;
+        const uint64_t e = min(n, k * 8 + 8);
+        lo = x[k * 8];
+        hi = lo;
+        for (uint64_t j = k * 8 + 1; j < e; ++j) {
+            const float4 v = x[j];
+            lo = make_float4(fminf(lo.x, v.x), fminf(lo.y, v.y), fminf(lo.z, v.z), fminf(lo.w, v.w));
+            hi = make_float4(fmaxf(hi.x, v.x), fmaxf(hi.y, v.y), fmaxf(hi.z, v.z), fmaxf(hi.w, v.w));
+        }
+    }
+    pbox[(k * kBoxBlocks + b) * 2] = lo;
+    pbox[(k * kBoxBlocks + b) * 2 + 1] = hi;
+}
+
+// Box of each 64-candidate chunk of each cell's candidate list, exact: a
+// thread per chunk and layout block.  The chunk's cell is the last A with
+// base[A] <= chunk (binary search over the per-cell chunk prefix); its
+// candidates are pieces of the cell's point ranges, and each piece is
+// covered by the boxes of the 8-point groups that lie wholly inside it plus
+// the points of its partial groups at either end.
 __global__ __launch_bounds__(256) void k_chunk_boxes(const uint64_t *__restrict__ base, int64_t M,
                                                      uint64_t nchunks, const uint32_t *__restrict__ rstart,
                                                      const uint32_t *__restrict__ rpref,
                                                      const uint32_t *__restrict__ nrng,
-                                                     const float4 *__restrict__ xs, float4 *__restrict__ cbox)
+                                                     const float4 *__restrict__ xs, uint64_t n, int nb,
+                                                     const float4 *__restrict__ pbox, float4 *__restrict__ cbox)
 {
-    const uint64_t ch = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (ch >= nchunks) return;  // whole wave
-    // the last A in [lo, lo + len) with base[A] <= ch (base[lo] <= ch holds
-    // throughout): each round the 64 lanes test evenly spaced cells and the
-    // last one that passes starts the next, 64 times shorter, interval
-    int64_t lo = 0, len = M;
-    while (len > 1) {
-        const int64_t step = (len + 63) / 64;
-        const int64_t j = lo + (int64_t)lane * step;
-        const uint64_t b = __ballot(j < lo + len && base[j] <= ch);
-        const int64_t t = 63 - __clzll((long long)b);  // lane 0 always passes
-        const int64_t nlo = lo + t * step;
-        len = min(step, lo + len - nlo);
-        lo = nlo;
+    const uint64_t gid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t ch = gid / kBoxBlocks;
+    const int b = (int)(gid % kBoxBlocks);
+    if (ch >= nchunks) return;
+    float4 blo = make_float4(0.f, 0.f, 0.f, 0.f), bhi = blo;
+    if (b < nb) {
+        int64_t lo = 0, hi = M;  // the last A with base[A] <= ch
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (base[mid] <= ch) lo = mid;
+            else hi = mid;
+        }
+        const int64_t A = lo;
+        const uint32_t *pref = rpref + (uint64_t)A * (kMaxRanges + 1);
+        const uint32_t *start = rstart + (uint64_t)A * kMaxRanges;
+        const uint32_t nr = nrng[A];
+        const uint32_t U = pref[nr];
+        const uint32_t p0 = (uint32_t)(ch - base[A]) * 64, p1 = min(U, p0 + 64);
+        const float4 *x = xs + (uint64_t)b * n;
+        blo = make_float4(INFINITY, INFINITY, INFINITY, INFINITY);
+        bhi = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        auto add = [&](float4 l, float4 h) __attribute__((always_inline)) {
+            blo = make_float4(fminf(blo.x, l.x), fminf(blo.y, l.y), fminf(blo.z, l.z), fminf(blo.w, l.w));
+            bhi = make_float4(fmaxf(bhi.x, h.x), fmaxf(bhi.y, h.y), fmaxf(bhi.z, h.z), fmaxf(bhi.w, h.w));
+        };
+        for (int g = range_of(pref, nr, p0); g < (int)nr && pref[g] < p1; ++g) {
+            uint32_t j = start[g] + (max(p0, pref[g]) - pref[g]);
+            const uint32_t e = start[g] + (min(p1, pref[g + 1]) - pref[g]);  // exclusive, > j
+            for (; j < e && (j & 7u); ++j) add(x[j], x[j]);
+            for (; j + 8 <= e; j += 8)
+                add(pbox[((uint64_t)(j >> 3) * kBoxBlocks + b) * 2], pbox[((uint64_t)(j >> 3) * kBoxBlocks + b) * 2 + 1]);
+            for (; j < e; ++j) add(x[j], x[j]);
+        }
     }
-    const int64_t A = lo;
-    const uint32_t *pref = rpref + (uint64_t)A * (kMaxRanges + 1);
-    const uint32_t nr = nrng[A];
-    const uint32_t U = pref[nr];
-    const uint32_t p = (uint32_t)(ch - base[A]) * 64 + (uint32_t)lane;
-    float4 blo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), bhi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
-    if (p < U) {
-        const int g = range_of(pref, nr, p);
-        const float4 v = xs[rstart[(uint64_t)A * kMaxRanges + g] + (p - pref[g])];
-        blo = v;
-        bhi = v;
-    }
-    wave_box(blo, bhi);
-    if (lane == 0) {
-        cbox[2 * ch] = blo;
-        cbox[2 * ch + 1] = bhi;
-    }
+    cbox[(ch * kBoxBlocks + b) * 2] = blo;
+    cbox[(ch * kBoxBlocks + b) * 2 + 1] = bhi;
 }
 
 __global__ __launch_bounds__(kBlock) void k_tiles(const uint64_t *__restrict__ tile_base, int64_t M,
@@ -962,15 +996,25 @@ hipError_t launch_chunk_counts(const uint32_t *rpref, const uint32_t *nrng, int6
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_boxes(const uint64_t *base, int64_t M, uint64_t nchunks, const uint32_t *rstart,
-                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, float4 *cbox,
-                              hipStream_t s)
+hipError_t launch_point_boxes(const float4 *xs, uint64_t n, int nb, float4 *pbox, hipStream_t s)
 {
-    if (nchunks == 0) return hipSuccess;
-    const uint64_t blocks = (nchunks + 3) / 4;
+    const uint64_t ng = (n + 7) / 8;
+    const uint64_t blocks = (ng * kBoxBlocks + 255) / 256;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_point_boxes, dim3((unsigned)blocks), dim3(256), 0, s, xs, n, nb, ng, pbox);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_boxes(const uint64_t *base, int64_t M, uint64_t nchunks, const uint32_t *rstart,
+                              const uint32_t *rpref, const uint32_t *nrng, const float4 *xs, uint64_t n, int nb,
+                              const float4 *pbox, float4 *cbox, hipStream_t s)
+{
+    const uint64_t blocks = (nchunks * kBoxBlocks + 255) / 256;
+    if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(k_chunk_boxes, dim3((unsigned)blocks), dim3(256), 0, s, base, M, nchunks, rstart, rpref,
-                       nrng, xs, cbox);
+                       nrng, xs, n, nb, pbox, cbox);
     return hipGetLastError();
 }
 

@@ -6,6 +6,11 @@
 // share their candidates, candidates staged through on-chip memory) and
 // Sec. IV-F (one result bit per comparison).
 //
+// Block box test over dimensions 0-7 of the variance-ordered layout (the
+// grid axes and the next ones), not only the grid axes: a cell's stencil
+// often holds clusters that are close on the grid axes and far apart on the
+// others.
+//
 // Arithmetic and classification are those of the split-fp16 form of
 // k_refine_mfma.hip: coordinates centred on the tile's reference point r and
 // scaled by the power of two s (computed as fma(x, s, -(r s)), which equals
@@ -52,7 +57,7 @@ struct M16 {
     static constexpr int PER = NBS / TPC;       // blocks staged per thread
     static constexpr int GS = kGroupCands / STEP;  // steps per 512-candidate mask-word group
     static constexpr int MAXST = 8192 / STEP;   // steps of the longest segment
-    static constexpr int FW = MAXST / 64;       // 64-bit words of a step bit set
+    static constexpr int FW = MAXST / 64;       // 64-bit words of a step bit set (MAXST * CG = 128)
     static constexpr int WB = NS >= 4 ? 1 : 2;  // mask-word group buffers
     // LDS layout (bytes)
     static constexpr size_t X = 0;                                         // [2][NS][4][STEP] x 16 B
@@ -63,8 +68,10 @@ struct M16 {
     static constexpr size_t QOUT = QIN + (size_t)kRows * 4;
     static constexpr size_t RCNT = QOUT + (size_t)kRows * 4;               // [kRows] u32
     static constexpr size_t NQMAX = RCNT + (size_t)kRows * 4;               // [4] f32
-    static constexpr size_t FAR = NQMAX + 16;                               // [4 waves][FW] u64
-    static constexpr size_t LIVE = FAR + (size_t)4 * FW * 8;                // [MAXST] u32, count at MAXST + 1
+    static constexpr size_t QBOX = NQMAX + 16;                              // [4 blocks][kBoxBlocks][2] float4
+    static constexpr size_t FARU = QBOX + (size_t)4 * kBoxBlocks * 2 * 16;  // [128] u32: far bits per chunk
+    static constexpr size_t LLB = FARU + (size_t)128 * 4;                   // [2] u64: live-step ballots
+    static constexpr size_t LIVE = LLB + 16;                                // [MAXST] u32, count at MAXST + 1
     static constexpr size_t PREF = LIVE + (size_t)(MAXST + 4) * 4;          // [kMaxRanges + 1] u32
     static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;    // [kMaxRanges] u32
     static constexpr size_t WORDS = (START + (size_t)kMaxRanges * 4 + 63) & ~(size_t)63;  // [WB][kRows][8] u64
@@ -101,7 +108,9 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
     float *const LQOUT = (float *)(smem16 + G::QOUT);
     uint32_t *const LRCNT = (uint32_t *)(smem16 + G::RCNT);
     float *const LNQMAX = (float *)(smem16 + G::NQMAX);
-    uint64_t *const LFAR = (uint64_t *)(smem16 + G::FAR);
+    float4 *const LQBOX = (float4 *)(smem16 + G::QBOX);
+    uint32_t *const LFARU = (uint32_t *)(smem16 + G::FARU);
+    uint64_t *const LLB = (uint64_t *)(smem16 + G::LLB);
     uint32_t *const LLIVE = (uint32_t *)(smem16 + G::LIVE);
     uint32_t *const LPREF = (uint32_t *)(smem16 + G::PREF);
     uint32_t *const LSTART = (uint32_t *)(smem16 + G::START);
@@ -192,103 +201,119 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
     }
 
     // ---- block box test of every step, up front ----
-    // the wave's query blocks' boxes on the grid axes (lanes 0-31: block 0,
-    // lanes 32-63: block 1 if the wave holds two), made wave-uniform
-    float qlo[QBW][3], qhi[QBW][3];
-    uint32_t qrows[QBW];
+    // Each wave writes its query blocks' boxes over the first kBoxBlocks
+    // layout blocks (dimensions 0-7: the grid axes and the next
+    // highest-variance ones) to LDS; then thread u tests the segment's
+    // 64-candidate chunk u against all four query blocks of the tile (bit q of
+    // LFARU[u]: block q holds no neighbour there, or no row), and the waves
+    // read their step bits and the live steps back with ballots.
     {
         const uint32_t r = (uint32_t)(rbase + (QBW == 2 ? hi : 0) * 32 + col);
-        float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), up = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
-        if (r < nrows) {
-            lo = xq[row0 + r];
-            up = lo;
-        }
 #pragma unroll
-        for (int o = 1; o < 32; o <<= 1) {
-            lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
-            lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
-            lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
-            up.x = fmaxf(up.x, __shfl_xor(up.x, o, 64));
-            up.y = fmaxf(up.y, __shfl_xor(up.y, o, 64));
-            up.z = fmaxf(up.z, __shfl_xor(up.z, o, 64));
-        }
+        for (int b = 0; b < kBoxBlocks; ++b) {
+            float4 lo = make_float4(INFINITY, INFINITY, INFINITY, INFINITY);
+            float4 up = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (r < nrows) {
+                lo = b < nb ? xq[(uint64_t)b * nqr + row0 + r] : make_float4(0.f, 0.f, 0.f, 0.f);
+                up = lo;
+            }
 #pragma unroll
-        for (int i = 0; i < QBW; ++i) {
-            qlo[i][0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.x), i * 32));
-            qlo[i][1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.y), i * 32));
-            qlo[i][2] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo.z), i * 32));
-            qhi[i][0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.x), i * 32));
-            qhi[i][1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.y), i * 32));
-            qhi[i][2] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(up.z), i * 32));
-            const int rb = rbase + i * 32;
-            qrows[i] = (uint32_t)rb < nrows ? min(32u, nrows - (uint32_t)rb) : 0u;
+            for (int o = 1; o < 32; o <<= 1) {
+                lo.x = fminf(lo.x, __shfl_xor(lo.x, o, 64));
+                lo.y = fminf(lo.y, __shfl_xor(lo.y, o, 64));
+                lo.z = fminf(lo.z, __shfl_xor(lo.z, o, 64));
+                lo.w = fminf(lo.w, __shfl_xor(lo.w, o, 64));
+                up.x = fmaxf(up.x, __shfl_xor(up.x, o, 64));
+                up.y = fmaxf(up.y, __shfl_xor(up.y, o, 64));
+                up.z = fmaxf(up.z, __shfl_xor(up.z, o, 64));
+                up.w = fmaxf(up.w, __shfl_xor(up.w, o, 64));
+            }
+            // lane 0 (and lane 32 for a second block) holds its block's box
+            if (col == 0 && (QBW == 2 || hi == 0)) {
+                const int q = (rbase >> 5) + (QBW == 2 ? hi : 0);
+                LQBOX[(q * kBoxBlocks + b) * 2] = lo;
+                LQBOX[(q * kBoxBlocks + b) * 2 + 1] = up;
+            }
         }
     }
     const uint32_t nsteps = (c_end - c_begin + kStep - 1) / kStep;  // <= kMaxSteps16
+    const uint32_t nunits = nsteps * G::CG;                         // <= 128 chunks
     const float tbox = a.tbox;
     const bool tested = tbox < INFINITY;
-    // far[i]: steps (bit st) in which query block i of this wave holds no
-    // neighbour (box test) or no row; the wave skips a step when all are set
-    uint64_t far[QBW][G::FW];
+    __syncthreads();
+    uint32_t nskip = 0;  // comparisons the box test settles (<= 8192 per chunk)
+    if ((uint32_t)tid < 128u) {
+        const uint32_t u = (uint32_t)tid;
+        const uint32_t gs = c_begin + u * 64;
+        uint32_t fm = 0xfu;
+        if (u < nunits && gs < c_end) {
+            const uint32_t ncol = min(64u, c_end - gs);
+            float4 blo[kBoxBlocks], bhi[kBoxBlocks];
+            if (tested) {
+                const float4 *cb = a.cbox + 2 * kBoxBlocks * (a.chunk_base[A] + (gs >> 6));
 #pragma unroll
-    for (int i = 0; i < QBW; ++i)
-#pragma unroll
-        for (int f = 0; f < G::FW; ++f) far[i][f] = 0;
-    uint64_t nskip = 0;
-    {
-        const uint64_t cb0 = tested ? a.chunk_base[A] : 0;
-        for (uint32_t st = 0; st < nsteps; ++st) {
-            const uint32_t gs = c_begin + st * kStep + cg * 64;
-            const uint64_t m = 1ull << (st & 63);
-            const int fw = (int)(st >> 6);
-            bool f[QBW];
-#pragma unroll
-            for (int i = 0; i < QBW; ++i) f[i] = gs >= c_end || qrows[i] == 0;
-            if (tested && gs < c_end) {
-                const uint32_t ncol = min(64u, c_end - gs);
-                const float4 *cb = a.cbox + 2 * (cb0 + (gs >> 6));
-                const float4 blo = cb[0], bhi = cb[1];
-#pragma unroll
-                for (int i = 0; i < QBW; ++i) {
-                    if (!f[i] && box_gap2(qlo[i], qhi[i], blo, bhi) > tbox) {
-                        f[i] = true;
-                        nskip += (uint64_t)qrows[i] * ncol;
-                    }
+                for (int b = 0; b < kBoxBlocks; ++b) {
+                    blo[b] = cb[2 * b];
+                    bhi[b] = cb[2 * b + 1];
                 }
             }
+            fm = 0;
 #pragma unroll
-            for (int i = 0; i < QBW; ++i)
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t rb = (uint32_t)q * 32;
+                const uint32_t qr = rb < nrows ? min(32u, nrows - rb) : 0u;
+                bool far_q = qr == 0;
+                if (!far_q && tested) {
+                    float g2 = 0.f;
 #pragma unroll
-                for (int w2 = 0; w2 < G::FW; ++w2)
-                    if (f[i] && w2 == fw) far[i][w2] |= m;
+                    for (int b = 0; b < kBoxBlocks; ++b)
+                        g2 = gap4(LQBOX[(q * kBoxBlocks + b) * 2], LQBOX[(q * kBoxBlocks + b) * 2 + 1], blo[b], bhi[b], g2);
+                    if (g2 > tbox) {
+                        far_q = true;
+                        nskip += qr * ncol;
+                    }
+                }
+                fm |= (uint32_t)far_q << q;
+            }
         }
-    }
-    // far bits are wave-uniform (computed from uniform values); make it explicit
+        LFARU[u] = fm;
 #pragma unroll
-    for (int i = 0; i < QBW; ++i)
-#pragma unroll
-        for (int w2 = 0; w2 < G::FW; ++w2)
-            far[i][w2] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(far[i][w2] >> 32)) << 32) |
-                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)far[i][w2]);
-    if (lane == 0) {
-#pragma unroll
-        for (int w2 = 0; w2 < G::FW; ++w2) {
-            uint64_t all = ~0ull;
-#pragma unroll
-            for (int i = 0; i < QBW; ++i) all &= far[i][w2];
-            LFAR[wave * G::FW + w2] = all;
-        }
+        for (int o = 1; o < 64; o <<= 1) nskip += __shfl_xor(nskip, o, 64);
     }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t c = 0;
-        for (uint32_t st = 0; st < nsteps; ++st) {
-            const int w2 = (int)(st >> 6);
-            const uint64_t all = LFAR[0 * G::FW + w2] & LFAR[1 * G::FW + w2] & LFAR[2 * G::FW + w2] &
-                                 LFAR[3 * G::FW + w2];
-            if (!((all >> (st & 63)) & 1ull)) LLIVE[c++] = st;
+    // the wave's step bits: block i far at step st (lanes take steps w2 64 + lane)
+    uint64_t far[QBW][G::FW];
+#pragma unroll
+    for (int i = 0; i < QBW; ++i) {
+        const int q = (rbase >> 5) + i;
+#pragma unroll
+        for (int w2 = 0; w2 < G::FW; ++w2) {
+            const uint32_t st = (uint32_t)(w2 * 64 + lane);
+            const bool f = st >= nsteps || ((LFARU[st * G::CG + cg] >> q) & 1u);
+            far[i][w2] = __ballot(f);
         }
-        LLIVE[kMaxSteps16 + 1] = c;
+    }
+    // live steps: some block of some candidate group is not far
+    if ((uint32_t)tid < 128u) {
+        const uint32_t st = (uint32_t)tid;
+        bool live = false;
+        if (st < nsteps) {
+            uint32_t all = 0xfu;
+#pragma unroll
+            for (int c = 0; c < G::CG; ++c) all &= LFARU[st * G::CG + c];
+            live = all != 0xfu;
+        }
+        const uint64_t bl = __ballot(live);
+        if (lane == 0) LLB[wave] = bl;
+    }
+    __syncthreads();
+    if ((uint32_t)tid < 128u) {
+        const uint32_t st = (uint32_t)tid;
+        const uint64_t b0 = LLB[0], b1 = LLB[1];
+        const uint64_t below = (1ull << lane) - 1ull;
+        const uint64_t mine = wave == 0 ? b0 : b1;
+        if ((mine >> lane) & 1ull) LLIVE[(wave == 0 ? 0u : (uint32_t)__popcll(b0)) + __popcll(mine & below)] = st;
+        if (tid == 0) LLIVE[kMaxSteps16 + 1] = (uint32_t)(__popcll(b0) + __popcll(b1));
     }
     __syncthreads();
     const uint32_t nlive = __builtin_amdgcn_readfirstlane(LLIVE[kMaxSteps16 + 1]);

@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             const uint32_t gs = c_begin + st * G::SC + cg * 64;
             uint32_t bit = 1;
             if (active && gs < c_end) {
-                const float4 *cb = a.cbox + 2 * (cb0 + st * (uint32_t)(G::SC / 64));
+                const float4 *cb = a.cbox + 2 * kBoxBlocks * (cb0 + st * (uint32_t)(G::SC / 64));
                 bit = __builtin_amdgcn_readfirstlane((int)(box_gap2(qlo, qhi, cb[0], cb[1]) > tbox));
             }
             if (bit) {
