@@ -101,21 +101,24 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         atomicAdd(&nin[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], (unsigned long long)s_hits);
 }
 
-// position of the r-th (0-based) set bit of w; r < popcount(w)
+// position of the r-th (0-based) set bit of w; r < popcount(w).  Halving
+// search in 32-bit pieces: at each width the low half's bit count decides
+// which half holds the bit.
 __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
 {
-    int pos = 0;
+    const uint32_t lo = (uint32_t)w;
+    uint32_t c = (uint32_t)__popc(lo);
+    const bool up = r >= c;
+    uint32_t v = up ? (uint32_t)(w >> 32) : lo;
+    int pos = up ? 32 : 0;
+    r = up ? r - c : r;
 #pragma unroll
-    for (int sh = 32; sh > 0; sh >>= 1) {
-        const uint64_t low = (1ull << sh) - 1ull;
-        const uint32_t c = __popcll(w & low);
-        if (r >= c) {
-            r -= c;
-            w >>= sh;
-            pos += sh;
-        } else {
-            w &= low;
-        }
+    for (int sh = 16; sh > 0; sh >>= 1) {
+        c = (uint32_t)__popc(v & ((1u << sh) - 1u));
+        const bool u = r >= c;
+        v = u ? v >> sh : v;
+        pos += u ? sh : 0;
+        r = u ? r - c : r;
     }
     return pos;
 }
@@ -128,9 +131,12 @@ __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
 // row-then-unit order.  The listed units are then taken 64 at a time: each
 // thread loads one of their 256 words, a workgroup prefix sum of the words'
 // bit counts places every set bit, and the bits are dealt to the threads in
-// turn (thread i takes bits i, i + 256, ...).  A row's pairs fill its output
-// range in candidate order; its next output position is kept in LDS from one
-// batch of units to the next.
+// turn (thread i takes bits i, i + 256, ...).  A bit finds its word through
+// a bit map of the words' first output bits and, per 64 output bits, the
+// word that holds the first; a word's range of the cell's list is looked up
+// once per word.  A row's pairs fill its output range in candidate order;
+// its next output position is kept in LDS from one batch of units to the
+// next.
 constexpr uint32_t kFlagPass = 4096;   // flag bytes read per pass
 constexpr uint32_t kUnitBatch = 64;    // listed units expanded per batch (256 words)
 static_assert(kTileRows < 255, "rows of a tile are held in bytes (0xff: no row)");
@@ -176,10 +182,17 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     __shared__ uint16_t s_list[kFlagPass];   // pass-relative byte offsets of flagged units
     __shared__ uint32_t s_ftot[16];          // flagged bytes per (load k, wave)
     __shared__ uint32_t s_wtot[4];
-    __shared__ uint64_t s_word[256];
-    __shared__ uint32_t s_excl[256];
-    __shared__ uint32_t s_wi[256];
     __shared__ uint8_t s_row[256];
+    // the batch's non-empty words in output order (index e), and the bit map
+    // of their first output bits (256 x 64 bits: a batch holds at most 16384)
+    __shared__ uint64_t s_word[256];
+    __shared__ uint64_t s_starts[256];
+    __shared__ uint32_t s_wi[256];       // word index in its row
+    __shared__ uint32_t s_goff[256];     // point - candidate in the range of the word's first candidate
+    __shared__ uint32_t s_gend[256];     // end of that range
+    __shared__ uint16_t s_excl[256];     // first output bit
+    __shared__ uint16_t s_first[256];    // non-empty word holding output bit 64 c
+    __shared__ uint8_t s_erow[256];
     __shared__ uint64_t s_rpos[kTileRows];   // next output position of each row
     __shared__ uint64_t s_rbase[kTileRows];  // output position of the batch's bit 0, per row
     __shared__ uint32_t s_qid[kTileRows];
@@ -195,7 +208,6 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
         s_qid[tid] = qorig[q];
         s_rpos[tid] = roff[q - row_base];
     }
-    const int wave = tid >> 6, lane = tid & 63;
     const uint64_t tbase = toff[t] - wbase;         // first word of the tile (a multiple of 8)
     const uint64_t fb = tbase >> 2;                  // its first flag byte
     const uint32_t fstride = tl.words >> 2;          // flag bytes per row
@@ -205,6 +217,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     const uint32_t *gf32 = (const uint32_t *)gflag;  // 4-byte loads from the aligned dword below fb
     const uint64_t d0 = fb >> 2, d1 = (fb + nbytes + 3) >> 2;
     const bool al8 = ((uintptr_t)pairs & 7u) == 0;  // a pair in one 8-byte store
+    const int wave = tid >> 6, lane = tid & 63;
     const uint64_t below = (1ull << lane) - 1ull;
     __syncthreads();
     for (uint64_t c = d0; c < d1; c += kFlagPass / 4) {
@@ -282,29 +295,43 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
             if (i0 + kUnitBatch < nl) load_word(i0 + kUnitBatch, &m_next, &wi_next, &row_next);
             const uint32_t pc = __popcll(m);
             s_row[tid] = (uint8_t)row;
-            uint32_t total;
-            const uint32_t excl = block_excl_scan(pc, s_wtot, &total);
+            s_starts[tid] = 0ull;
+            // one scan for both the bit offsets (low 16 bits, at most 16384)
+            // and the ranks of the non-empty words (high bits)
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan(pc | (pc != 0u ? 1u << 16 : 0u), s_wtot, &tot);
+            const uint32_t excl = ex & 0xffffu, e = ex >> 16, total = tot & 0xffffu;
             const bool first = row != 0xffu && (tid == 0 || s_row[tid - 1] != row);
             const bool last = row != 0xffu && (tid == 255 || s_row[tid + 1] != row);
-            s_word[tid] = m;
-            s_excl[tid] = excl;
-            s_wi[tid] = wi;
             if (first) s_rbase[row] = s_rpos[row] - excl;
+            if (pc != 0u) {
+                s_word[e] = m;
+                s_wi[e] = wi;
+                s_excl[e] = (uint16_t)excl;
+                s_erow[e] = (uint8_t)row;
+                const int g = range_of(s_pref, nr, wi * 64);
+                s_goff[e] = s_start[g] - s_pref[g];
+                s_gend[e] = s_pref[g + 1];
+                atomicOr((unsigned long long *)&s_starts[excl >> 6], 1ull << (excl & 63u));
+                const uint32_t c = (excl + 63u) >> 6;  // a 64-bit boundary inside the word's bits
+                if (64u * c < excl + pc) s_first[c] = (uint16_t)e;
+            }
             __syncthreads();
             if (last) s_rpos[row] = s_rbase[row] + excl + pc;
-            // bit j of the batch -> (output position, query id, point); two
-            // bits per thread at a time, so two gathers of orig are in flight
+            // bit j of the batch -> (output position, query id, point): its
+            // word is the last one starting at or before j, counted from the
+            // word that holds bit 64 (j / 64); two bits per thread at a
+            // time, so two gathers of orig are in flight
             auto locate = [&](uint32_t j, uint64_t *pos, uint32_t *qid, uint32_t *x) __attribute__((always_inline)) {
-                int lo = 0, hi = 255;  // the last slot with s_excl[slot] <= j
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) >> 1;
-                    if (s_excl[mid] <= j) lo = mid;
-                    else hi = mid - 1;
-                }
-                const uint32_t p = s_wi[lo] * 64 + nth_bit(s_word[lo], j - s_excl[lo]);
-                const int g = range_of(s_pref, nr, p);
-                *x = s_start[g] + (p - s_pref[g]);
-                const uint32_t r = s_row[lo];
+                const uint32_t c = j >> 6, b = j & 63u;
+                const uint64_t after = ((2ull << b) - 1ull) & ~1ull;  // bits 1..b
+                const uint32_t e = s_first[c] + (uint32_t)__popcll(s_starts[c] & after);
+                const uint32_t p = s_wi[e] * 64 + (uint32_t)nth_bit(s_word[e], j - s_excl[e]);
+                *x = p < s_gend[e] ? p + s_goff[e] : [&]() {
+                    const int g = range_of(s_pref, nr, p);
+                    return s_start[g] + (p - s_pref[g]);
+                }();
+                const uint32_t r = s_erow[e];
                 *qid = s_qid[r];
                 *pos = s_rbase[r] + j;
             };
