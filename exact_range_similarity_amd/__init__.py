@@ -15,7 +15,9 @@ import os
 import torch  # loads the HIP runtime the library must share with torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libersj.so")
+# ERSJ_LIBRARY selects another build of the same library (for example the
+# host-sanitized one that exact_range_similarity_amd.build makes on request)
+LIB_PATH = os.environ.get("ERSJ_LIBRARY") or os.path.join(_HERE, "libersj.so")
 
 OK = 0
 ERR_INVALID_ARG = -1
@@ -104,7 +106,7 @@ class KnnInfo(ctypes.Structure):
 SYMBOLS = ("ersj_default_options", "ersj_build_index", "ersj_set_queries", "ersj_count_pass",
            "ersj_plan_batches", "ersj_fill_pass", "ersj_fill_pass_host", "ersj_fill_pass_noalloc",
            "ersj_host_sync",
-           "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_last_error", "ersj_knn")
+           "ersj_batch_info", "ersj_get_stats", "ersj_free", "ersj_release_cached", "ersj_last_error", "ersj_knn")
 
 
 def lib():
@@ -133,6 +135,7 @@ def lib():
                                   ctypes.POINTER(u64)]
     L.ersj_get_stats.argtypes = [vp, ctypes.POINTER(Stats)]
     L.ersj_free.argtypes = [vp]
+    L.ersj_release_cached.argtypes = [i32, ctypes.POINTER(u64)]
     L.ersj_knn.argtypes = [vp, i64, i32, i64, vp, i64, i64, i32, dbl, dbl, ctypes.POINTER(Options),
                            vp, vp, ctypes.POINTER(KnnInfo), vp]
     L.ersj_free.restype = None
@@ -365,6 +368,24 @@ def free(h: Index):
     h.free()
 
 
+def release_cached(device: int = -1) -> int:
+    """Return the device memory the library keeps for reuse to the HIP runtime;
+    the bytes freed."""
+    out = ctypes.c_uint64()
+    _check(lib().ersj_release_cached(device, ctypes.byref(out)))
+    return out.value
+
+
+def _empty_pairs(m: int, dev):
+    # memory the library keeps for reuse is invisible to torch's allocator:
+    # give it back once before failing
+    try:
+        return torch.empty((m, 2), dtype=torch.int32, device=dev)
+    except torch.OutOfMemoryError:
+        release_cached(dev.index if dev.index is not None else -1)
+        return torch.empty((m, 2), dtype=torch.int32, device=dev)
+
+
 def iter_batches(h: Index, n_batches: int, stream=None):
     """Yield each batch's pairs as an int32 CUDA tensor [m, 2] (uint32 ids)."""
     dev = torch.device("cuda", torch.cuda.current_device())
@@ -375,7 +396,7 @@ def iter_batches(h: Index, n_batches: int, stream=None):
             if e.code != ERR_CAPACITY:
                 raise
             m = e.required
-        out = torch.empty((m, 2), dtype=torch.int32, device=dev)
+        out = _empty_pairs(m, dev)
         if m:
             fill_pass(h, b, out, m, stream)
         yield out

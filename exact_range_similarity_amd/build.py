@@ -50,5 +50,47 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer build of the
+# API layer (argument validation, handle state, planning and the host
+# bookkeeping of every entry point), linked with the ordinary kernel
+# objects.  Load it through ERSJ_LIBRARY with the clang ASan runtime
+# preloaded into the interpreter (SANITIZER_RUNTIME).
+SAN_LIB = os.path.join(OBJ, "libersj_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-shared-libsan", "-g", "-O1"]
+SANITIZER_RUNTIME = os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang")
+
+
+def sanitizer_runtime() -> str:
+    """Path of the clang ASan runtime that a sanitized library needs preloaded."""
+    for ver in sorted(os.listdir(SANITIZER_RUNTIME), reverse=True):
+        p = os.path.join(SANITIZER_RUNTIME, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise FileNotFoundError("clang ASan runtime not found under " + SANITIZER_RUNTIME)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    api = os.path.join(OBJ, "ersj_api_san.o")
+    cmd = [HIPCC, *COMMON, *SAN_FLAGS, "-c", os.path.join(CSRC, "ersj_api.cpp"), "-o", api]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libsan", "-Xarch_host",
+           "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", *objs, api, "-o", SAN_LIB]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

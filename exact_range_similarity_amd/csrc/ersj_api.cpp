@@ -854,6 +854,15 @@ int do_count(ersj_index *h, hipStream_t s)
     return ERSJ_OK;
 }
 
+// band-list entries a handle under max_device_bytes starts with: 1/64 of
+// the cap, at least 4096 and at most 2^20 (the list still grows on
+// overflow, within the cap)
+uint64_t capped_band_entries(const ersj_index *h)
+{
+    const uint64_t e = h->opt.max_device_bytes / 64 / sizeof(Boundary);
+    return std::min<uint64_t>(std::max<uint64_t>(e, 4096), 1ull << 20);
+}
+
 int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
 {
     release_plan(h);
@@ -865,8 +874,14 @@ int do_plan(ersj_index *h, uint64_t budget_bytes, hipStream_t s)
         uint64_t b = (uint64_t)fr / 4 * 3;
         budget_bytes = b > extra ? b - extra : 8;
         if (h->opt.max_device_bytes) {
+            // beside the mask and its flags a batch holds row counts, offsets
+            // and their scan (24 bytes a row at most), the counters and the
+            // band list
             const uint64_t room = h->opt.max_device_bytes > h->bytes ? h->opt.max_device_bytes - h->bytes : 0;
-            budget_bytes = std::min<uint64_t>(budget_bytes, room / 4 * 3);
+            // (each buffer above 1 MiB is rounded up to 2 MiB by the pool)
+            const uint64_t bl = h->opt.boundary_capacity ? h->opt.boundary_capacity : capped_band_entries(h);
+            const uint64_t reserve = (uint64_t)h->nq * 24 + bl * sizeof(Boundary) + (10ull << 20);
+            budget_bytes = std::min<uint64_t>(budget_bytes, room > reserve ? room - reserve : 0);
         }
     }
     // a mask word costs 8 bytes plus a quarter byte of unit flags
@@ -937,6 +952,7 @@ std::atomic<uint64_t> g_bcap_hint{0};
 uint64_t initial_bcap(const ersj_index *h)
 {
     if (h->opt.boundary_capacity) return h->opt.boundary_capacity;
+    if (h->opt.max_device_bytes) return capped_band_entries(h);
     uint64_t maxc = 0;
     for (int32_t b = 0; b < h->nbatch; ++b) maxc = std::max(maxc, h->hcands[b + 1] - h->hcands[b]);
     uint64_t cap = std::min<uint64_t>(std::max<uint64_t>(maxc / 4096, 1ull << 20), 1ull << 27);
@@ -1317,6 +1333,42 @@ void ersj_default_options(ersj_options *opt)
 }
 
 const char *ersj_last_error(void) { return g_err.c_str(); }
+
+int ersj_release_cached(int32_t device, uint64_t *released)
+{
+    g_err.clear();
+    if (released) *released = 0;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess) {
+        (void)hipGetLastError();
+        ndev = 0;
+    }
+    int dev = device;
+    if (dev == -1) {
+        if (hipGetDevice(&dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ERSJ_ERR_HIP, "no current HIP device");
+        }
+    }
+    if (dev < 0 || dev >= ndev) return fail(ERSJ_ERR_INVALID_ARG, "device = %d is not a HIP device (%d present)", device, ndev);
+    DeviceGuard g(dev);
+    if (!g.ok()) return fail(ERSJ_ERR_HIP, "cannot select device %d", dev);
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    auto it = g_pools.find(dev);
+    if (it == g_pools.end()) return ERSJ_OK;
+    DevicePool &pl = it->second;
+    if (!pl.blocks.empty()) (void)hipDeviceSynchronize();
+    uint64_t bytes = 0;
+    for (const PoolBlock &b : pl.blocks) {
+        (void)hipFree(b.p);
+        bytes += b.bytes;
+    }
+    (void)hipGetLastError();
+    pl.blocks.clear();
+    pl.cached = 0;
+    if (released) *released = bytes;
+    return ERSJ_OK;
+}
 
 void ersj_free(ersj_index *h)
 {

@@ -301,8 +301,22 @@ int ersj_batch_info(const ersj_index *h, int32_t batch, uint64_t *first_row, uin
 /* Counters and phase times of the handle (host out). */
 int ersj_get_stats(const ersj_index *h, ersj_stats *out);
 
-/* Release the handle and all device memory it owns.  NULL is a no-op. */
+/* Release the handle and all device memory it owns.  NULL is a no-op.  The
+ * library keeps released blocks (per device, up to half of its memory) and
+ * hands them out again to allocations of the same size; ersj_release_cached
+ * returns them to the HIP runtime. */
 void ersj_free(ersj_index *h);
+
+/* Return the device memory that the library keeps for reuse on a device
+ * (blocks released by ersj_free and by earlier passes) to the HIP runtime, so
+ * that other allocators (torch's included) can use it.  Handles stay valid:
+ * memory they own is not touched.
+ *  device   : HIP device ordinal, or -1 for the calling thread's current one.
+ *  released : host out (may be NULL): bytes freed.
+ * Waits for the device to finish enqueued work first (a released block may
+ * still be read by it).  Errors: ERSJ_ERR_INVALID_ARG for an ordinal that is
+ * not a device, ERSJ_ERR_HIP if the device cannot be selected. */
+int ersj_release_cached(int32_t device, uint64_t *released);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *ersj_last_error(void);

@@ -92,6 +92,15 @@ def test_knn_rejects_bad_arguments(kw):
     assert ersj.lib().ersj_last_error()
 
 
+def test_release_cached_rejects_a_missing_device():
+    L = ersj.lib()
+    out = ctypes.c_uint64(7)
+    assert L.ersj_release_cached(-2, ctypes.byref(out)) == ersj.ERR_INVALID_ARG
+    assert out.value == 0
+    assert L.ersj_release_cached(1 << 20, None) == ersj.ERR_INVALID_ARG
+    assert "not a HIP device" in L.ersj_last_error().decode()
+
+
 def test_error_message_is_per_call():
     rc, _ = build(d=0)
     assert rc == ersj.ERR_INVALID_ARG
