@@ -52,7 +52,8 @@ class Options(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("refine_kernel", ctypes.c_int32),
                 ("cell_width_scale", ctypes.c_double), ("max_device_bytes", ctypes.c_uint64),
                 ("boundary_capacity", ctypes.c_uint64), ("timing", ctypes.c_int32),
-                ("grid_reach", ctypes.c_int32), ("block_prune", ctypes.c_int32)]
+                ("grid_reach", ctypes.c_int32), ("block_prune", ctypes.c_int32),
+                ("cell_order", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):

@@ -131,6 +131,7 @@ struct ersj_index {
     uint64_t refined_cand = 0, skipped_cand = 0;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t kernel_used = ERSJ_REFINE_DIRECT;
+    bool box_order = false;  // rows of a cell in Morton order over its 8-dimension box
     bool use_m16 = false;  // split-fp16 form on the whole-tile kernel (33 <= d <= 64)
     bool use_g16 = false;  // split-fp16 form on operands prepared per point (d > 64)
     std::vector<double> mean;  // per input dimension (binary64 statistics of the points)
@@ -398,11 +399,15 @@ bool mfma_feasible(const ersj_index *h, const char **why)
 // 2^-25 covers subnormal parts).  Then s^2 q'x' = hi.hi + hi.lo + lo.hi + r
 // with |r| <= 3 * 2^-22 |s^2 q'x'| plus absolute terms below
 // 2^-25 (|q's| + |x's|) * 1.01 per dimension.  The fp16 products are exact in
-// fp32; each k = 16 MFMA adds 16 products and the accumulator, 17 additions,
-// each taken to err by less than one ulp (2u): 34u per instruction (a probe
-// of v_mfma_f32_32x32x16_f16 on the GPU measured at most 22.3u of
-// sum |ab| + |c|); the band charges 36u for each of the 3 ceil(d_pad / 16)
-// instructions of a tile, on top of the fp32 kernel's K.  With
+// fp32 (11-bit significands, exponents well inside fp32's range); each
+// k = 16 MFMA sums 16 products and the accumulator, 17 terms, with at most
+// 16 additions on any term's path whatever order the hardware takes.  Taking
+// each addition only to be faithful (error below one ulp of its result, 2u
+// relative), a term's relative error is below (1 + 2u)^16 - 1 < 32.1u, so an
+// instruction errs by less than 32.1u (sum |ab| + |c|), and |c| is at most
+// the sum of the earlier |ab| (to first order).  The band charges 36u for
+// each of the 3 ceil(d_pad / 16) instructions of a tile, on top of the fp32
+// kernel's K (a probe of v_mfma_f32_32x32x16_f16 measured at most 22.3u).  With
 // sum |q'_k x'_k| <= (Nq + Nx) / 2 the relative part fits the
 // norm-proportional band.  Norms come from the scaled coordinates and the
 // thresholds are those of fl(eps^2) s^2 (s^2 a power of two, so the rounding
@@ -542,9 +547,10 @@ void release_plan(ersj_index *h)
 }
 
 // Rows binned into the grid (A4-A7): Morton keys of their cells (clamped as
-// points or as queries), stable radix sort, gather into the
-// dimension-blocked variance-ordered layout, runs of equal keys = cells and
-// their boxes on the grid axes.
+// points or as queries), stable radix sort, runs of equal keys = cells, the
+// rows of each cell put in their order (cell_order), gather into the
+// dimension-blocked variance-ordered layout, and the cells' boxes on the grid
+// axes.
 struct Binned {
     float4 *xs = nullptr;
     float *xr = nullptr;
@@ -574,12 +580,6 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     int32_t *dperm = nullptr;
     TRY(tmp.get(&dperm, (size_t)d, "perm"));
     HIPC(hipMemcpyAsync(dperm, h->perm.data(), sizeof(int32_t) * d, hipMemcpyHostToDevice, s), "perm copy");
-    TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
-    HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
-    // row-major copy in sorted order for the binary64 re-check, which sums
-    // in the input's dimension order
-    TRY(dalloc(h, &out->xr, (size_t)n * recheck_stride(d), "rows"));
-    HIPC(launch_gather_rows(x, ld, out->orig, (uint64_t)n, d, recheck_stride(d), out->xr, s), "row gather kernel");
 
     uint32_t *flags = nullptr;
     uint64_t *cid = nullptr;
@@ -596,6 +596,22 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     TRY(dalloc(h, &out->lo_bits, (size_t)M * 3, "cells"));
     TRY(dalloc(h, &out->hi_bits, (size_t)M * 3, "cells"));
     HIPC(launch_cell_scatter(k0, 3 * h->gp.sub, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
+    if (h->box_order) {
+        // rows of each cell re-sorted by their Morton key in the cell's box
+        uint32_t *blo = nullptr, *bhi = nullptr;
+        TRY(tmp.get(&blo, (size_t)M * kOrderDims, "cell order"));
+        TRY(tmp.get(&bhi, (size_t)M * kOrderDims, "cell order"));
+        HIPC(launch_cell_order_keys(x, n, d, ld, out->orig, dperm, cid, (int64_t)M, blo, bhi, k0, s),
+             "cell order kernels");
+        HIPC(radix_sort(k0, out->orig, k1, v1, n, 24 + ceil_log2(M + 1), hist, stmp, s), "cell order sort");
+    }
+
+    TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
+    HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
+    // row-major copy in sorted order for the binary64 re-check, which sums
+    // in the input's dimension order
+    TRY(dalloc(h, &out->xr, (size_t)n * recheck_stride(d), "rows"));
+    HIPC(launch_gather_rows(x, ld, out->orig, (uint64_t)n, d, recheck_stride(d), out->xr, s), "row gather kernel");
     HIPC(launch_cell_aabb(out->xs, cid, n, (int64_t)M, out->lo_bits, out->hi_bits, s), "cell boxes");
     TRY(sync(s, "bin"));
     return ERSJ_OK;
@@ -694,10 +710,19 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
         bits = std::max(bits, ceil_log2((uint64_t)gp.G[a] + 2));
     }
     gp.bits = bits;
-    // rows within a cell follow a Morton curve over 8 x 8 x 8 sub-cells (fewer
-    // when the grid is near its 2^21 cap), so a block of consecutive rows is
-    // spatially compact and its bounding box prunes refinement work
-    gp.sub = std::min(3, 21 - bits);
+    // rows within a cell follow a Morton curve, so a block of consecutive rows
+    // is compact and its bounding box prunes refinement work: over the cell's
+    // own box in the first 8 dimensions (ordered after the cells are known,
+    // so the cell key carries no sub-cell bits), or over 8 x 8 x 8 sub-cells
+    // on the grid axes (fewer when the grid is near its 2^21 cap)
+    // automatic: the box order where an MFMA kernel will refine (their box
+    // test covers those 8 dimensions with 32-row and 64-candidate groups);
+    // the direct kernel's 256-candidate groups stay compact on the grid axes
+    // only under the sub-cell order
+    const char *why_not = "";
+    h->box_order = h->opt.cell_order == 2 ||
+                   (h->opt.cell_order == 0 && h->opt.refine_kernel != ERSJ_REFINE_DIRECT && coords_feasible(h, &why_not));
+    gp.sub = h->box_order ? 0 : std::min(3, 21 - bits);
     h->gp = gp;
 
     // A4-A7 for the points.
@@ -1417,6 +1442,8 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
             return fail(ERSJ_ERR_INVALID_ARG, "grid_reach must be 0, 1 or 2 (got %d)", o.grid_reach);
         if (o.block_prune < -1 || o.block_prune > 1)
             return fail(ERSJ_ERR_INVALID_ARG, "block_prune must be -1, 0 or 1 (got %d)", o.block_prune);
+        if (o.cell_order < 0 || o.cell_order > 2)
+            return fail(ERSJ_ERR_INVALID_ARG, "cell_order must be 0, 1 or 2 (got %d)", o.cell_order);
     }
     int dev = 0;
     HIPC(hipGetDevice(&dev), "hipGetDevice");

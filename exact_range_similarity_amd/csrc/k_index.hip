@@ -404,6 +404,80 @@ __global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restr
     if (i == n - 1) cell_start[cid[n]] = (uint32_t)n;
 }
 
+// ------------------------------------------------- order within a cell --
+// Rows of a cell in Morton order over the cell's own box in the first
+// kOrderDims dimensions of the variance order (3 bits per dimension), so
+// that runs of consecutive rows - the refinement's 32-row query blocks and
+// 64-candidate chunks - are compact in those dimensions and not only on the
+// grid axes.  The box test of the refinement covers the same dimensions.
+
+// Box of each cell over the first kOrderDims layout dimensions (ordered
+// float bits; box must hold 0xffffffff / 0 before): a wave per 64
+// consecutive sorted rows, reduced in the wave when they share a cell.
+__global__ __launch_bounds__(kBlock) void k_cell_box8(const float *__restrict__ x, int64_t ld,
+                                                      const uint32_t *__restrict__ orig,
+                                                      const int32_t *__restrict__ perm, int nd,
+                                                      const uint64_t *__restrict__ cid, int64_t n,
+                                                      uint32_t *__restrict__ lo_bits,
+                                                      uint32_t *__restrict__ hi_bits)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    if (i - lane >= n) return;  // whole wave
+    const bool valid = i < n;
+    const int64_t cell = valid ? (int64_t)cid[i + 1] - 1 : -1;
+    const int64_t c0 = __shfl(cell, 0, 64);
+    const bool shared = __ballot(valid && cell != c0) == 0;  // lanes past n hold no row
+    const uint64_t row = valid ? (uint64_t)orig[i] * (uint64_t)ld : 0;
+    for (int a = 0; a < nd; ++a) {
+        const uint32_t o = valid ? f2ord(x[row + perm[a]]) : 0u;
+        if (shared) {
+            uint32_t lo = valid ? o : 0xffffffffu, hi = o;
+            for (int k = 1; k < 64; k <<= 1) {
+                lo = min(lo, (uint32_t)__shfl_xor((int)lo, k, 64));
+                hi = max(hi, (uint32_t)__shfl_xor((int)hi, k, 64));
+            }
+            if (lane == 0) {
+                atomicMin(&lo_bits[c0 * kOrderDims + a], lo);
+                atomicMax(&hi_bits[c0 * kOrderDims + a], hi);
+            }
+        } else if (valid) {
+            atomicMin(&lo_bits[cell * kOrderDims + a], o);
+            atomicMax(&hi_bits[cell * kOrderDims + a], o);
+        }
+    }
+}
+
+// key = (cell << 24) | Morton interleave of the row's 3-bit positions in its
+// cell's box (most significant bits first, dimension 0 first at each level)
+__global__ __launch_bounds__(kBlock) void k_order_keys(const float *__restrict__ x, int64_t ld,
+                                                       const uint32_t *__restrict__ orig,
+                                                       const int32_t *__restrict__ perm, int nd,
+                                                       const uint64_t *__restrict__ cid, int64_t n,
+                                                       const uint32_t *__restrict__ lo_bits,
+                                                       const uint32_t *__restrict__ hi_bits,
+                                                       uint64_t *__restrict__ keys)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint64_t cell = cid[i + 1] - 1;
+    const uint64_t row = (uint64_t)orig[i] * (uint64_t)ld;
+    uint32_t q[kOrderDims];
+    for (int a = 0; a < kOrderDims; ++a) {
+        q[a] = 0;
+        if (a >= nd) continue;
+        const float lo = ord2f(lo_bits[cell * kOrderDims + a]), hi = ord2f(hi_bits[cell * kOrderDims + a]);
+        const float v = x[row + perm[a]];
+        const float w = hi - lo;  // may be 0 or overflow to inf: then every row takes 0
+        const float t = w > 0.f && w < INFINITY ? (v - lo) / w * 8.0f : 0.0f;
+        q[a] = t >= 7.0f ? 7u : (t > 0.0f ? (uint32_t)t : 0u);
+    }
+    uint32_t m = 0;
+    for (int b = 2; b >= 0; --b)
+        for (int a = 0; a < kOrderDims; ++a) m = (m << 1) | ((q[a] >> b) & 1u);
+    keys[i] = (cell << 24) | m;
+}
+
 constexpr int kAabbSteps = 8;  // 64-point steps per wave
 
 // A wave per 512 consecutive sorted points, 64 at a time (coalesced loads).
@@ -952,6 +1026,23 @@ hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, in
         e = hipMemcpyAsync(v0, vi, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return e;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_cell_order_keys(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
+                                  const int32_t *perm, const uint64_t *cid, int64_t M, uint32_t *box_lo,
+                                  uint32_t *box_hi, uint64_t *keys, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    const int nd = d < kOrderDims ? d : kOrderDims;
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_lo, 0xffffffffu,
+                       (int64_t)kOrderDims * M);
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_hi, 0u,
+                       (int64_t)kOrderDims * M);
+    hipLaunchKernelGGL(k_cell_box8, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
+                       box_hi);
+    hipLaunchKernelGGL(k_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
+                       box_hi, keys);
     return hipGetLastError();
 }
 

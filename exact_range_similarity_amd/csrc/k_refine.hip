@@ -78,19 +78,19 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
     Boundary *__restrict__ blist = band_list(a.blist, a.lcap);
     unsigned long long *__restrict__ bcount = band_counter(a.bcount);
 
-    // the wave's query box on the grid axes (rows past srows repeat the last)
-    float qlo[3], qhi[3];
-    {
-        const float4 q0 = xq[qrow[0]];
-        qlo[0] = qhi[0] = q0.x;
-        qlo[1] = qhi[1] = q0.y;
-        qlo[2] = qhi[2] = q0.z;
+    // the wave's query box over the first kBoxBlocks layout blocks (rows past
+    // srows repeat the last; blocks past nb are zero padding)
+    const uint64_t nqr = a.nqr;
+    const int nb = a.nb;
+    float4 qlo[kBoxBlocks], qhi[kBoxBlocks];
+#pragma unroll
+    for (int b = 0; b < kBoxBlocks; ++b) {
+        qlo[b] = qhi[b] = b < nb ? xq[(uint64_t)b * nqr + qrow[0]] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int k = 1; k < kQW; ++k) {
-            const float4 q = xq[qrow[k]];
-            qlo[0] = fminf(qlo[0], q.x); qhi[0] = fmaxf(qhi[0], q.x);
-            qlo[1] = fminf(qlo[1], q.y); qhi[1] = fmaxf(qhi[1], q.y);
-            qlo[2] = fminf(qlo[2], q.z); qhi[2] = fmaxf(qhi[2], q.z);
+            const float4 q = b < nb ? xq[(uint64_t)b * nqr + qrow[k]] : make_float4(0.f, 0.f, 0.f, 0.f);
+            qlo[b] = make_float4(fminf(qlo[b].x, q.x), fminf(qlo[b].y, q.y), fminf(qlo[b].z, q.z), fminf(qlo[b].w, q.w));
+            qhi[b] = make_float4(fmaxf(qhi[b].x, q.x), fmaxf(qhi[b].y, q.y), fmaxf(qhi[b].z, q.z), fmaxf(qhi[b].w, q.w));
         }
     }
     const float tbox = a.tbox;
@@ -109,18 +109,22 @@ __global__ __launch_bounds__(256) void k_refine_direct(RefineArgs a)
             xi[j] = s_start[g] + (pp - s_pref[g]);
         }
         {
-            float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), hi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
+            float g2 = 0.f;
 #pragma unroll
-            for (int j = 0; j < kCW; ++j) {
-                if (xv[j]) {
-                    const float4 v = xs[xi[j]];
-                    lo.x = fminf(lo.x, v.x); hi.x = fmaxf(hi.x, v.x);
-                    lo.y = fminf(lo.y, v.y); hi.y = fmaxf(hi.y, v.y);
-                    lo.z = fminf(lo.z, v.z); hi.z = fmaxf(hi.z, v.z);
+            for (int b = 0; b < kBoxBlocks; ++b) {
+                float4 lo = make_float4(INFINITY, INFINITY, INFINITY, INFINITY);
+                float4 hi = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+                for (int j = 0; j < kCW; ++j) {
+                    if (xv[j]) {
+                        const float4 v = b < nb ? xs[(uint64_t)b * n + xi[j]] : make_float4(0.f, 0.f, 0.f, 0.f);
+                        lo = make_float4(fminf(lo.x, v.x), fminf(lo.y, v.y), fminf(lo.z, v.z), fminf(lo.w, v.w));
+                        hi = make_float4(fmaxf(hi.x, v.x), fmaxf(hi.y, v.y), fmaxf(hi.z, v.z), fmaxf(hi.w, v.w));
+                    }
                 }
+                wave_box4(lo, hi);
+                g2 = gap4(qlo[b], qhi[b], lo, hi, g2);
             }
-            wave_box(lo, hi);
-            const float g2 = box_gap2(qlo, qhi, lo, hi);
             if (__builtin_amdgcn_readfirstlane((int)(g2 > tbox)) != 0) {
                 nskip += (uint64_t)nq * min((uint32_t)kChunk, c_end - c);
                 if (lane < kQW * kCW) {

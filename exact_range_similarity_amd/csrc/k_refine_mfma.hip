@@ -227,23 +227,22 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
     const int col = lane & 31, hi = lane >> 5;
     const int qb = wave % QB, cg = wave / QB;
     const bool active = (uint32_t)(qb * 32) < nrows;  // wave-uniform
-    // the wave's query block box on the grid axes (raw coordinates, valid
-    // rows only), held wave-uniform
-    float qlo[3], qhi[3];
+    // the wave's query block box over the first kBoxBlocks layout blocks (raw
+    // coordinates, valid rows only; blocks past nb are zero padding), the
+    // same in every lane
+    float4 qlo[kBoxBlocks], qhi[kBoxBlocks];
     {
         const uint32_t i = (uint32_t)(qb * 32 + (lane & 31));
-        float4 lo = make_float4(INFINITY, INFINITY, INFINITY, 0.f), hi = make_float4(-INFINITY, -INFINITY, -INFINITY, 0.f);
-        if (i < nrows) {
-            lo = xq[row0 + i];
-            hi = lo;
+#pragma unroll
+        for (int b = 0; b < kBoxBlocks; ++b) {
+            qlo[b] = make_float4(INFINITY, INFINITY, INFINITY, INFINITY);
+            qhi[b] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            if (i < nrows) {
+                qlo[b] = b < a.nb ? xq[(uint64_t)b * a.nqr + row0 + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                qhi[b] = qlo[b];
+            }
+            wave_box4(qlo[b], qhi[b]);
         }
-        wave_box(lo, hi);
-        qlo[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.x)));
-        qlo[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.y)));
-        qlo[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lo.z)));
-        qhi[0] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.x)));
-        qhi[1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.y)));
-        qhi[2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(hi.z)));
     }
     const float kp = a.kp, km = a.km;
     // the split-fp16 form classifies in the scaled domain (coordinates, norms
@@ -289,7 +288,10 @@ __global__ __launch_bounds__(256, QB == 4 ? 4 : 1) void k_refine_mfma(RefineArgs
             uint32_t bit = 1;
             if (active && gs < c_end) {
                 const float4 *cb = a.cbox + 2 * kBoxBlocks * (cb0 + st * (uint32_t)(G::SC / 64));
-                bit = __builtin_amdgcn_readfirstlane((int)(box_gap2(qlo, qhi, cb[0], cb[1]) > tbox));
+                float g2 = 0.f;
+#pragma unroll
+                for (int b = 0; b < kBoxBlocks; ++b) g2 = gap4(qlo[b], qhi[b], cb[2 * b], cb[2 * b + 1], g2);
+                bit = __builtin_amdgcn_readfirstlane((int)(g2 > tbox));
             }
             if (bit) {
                 const uint32_t m = 1u << (st & 31);

@@ -85,10 +85,18 @@ typedef struct ersj_options {
     int32_t grid_reach;         /* 0 or 1: cells of width >= eps and the 27-cell stencil; 2: cells of
                                    width >= eps/2 and a 5x5x5 stencil, fewer candidates (tighter
                                    pruning, more cells) with the same result */
-    int32_t block_prune;        /* 0 or 1: a block of queries and a group of candidates (MFMA kernel:
-                                   32 x 64, direct kernel: 8 x 256) whose bounding boxes on the grid
-                                   axes are farther apart than eps skip their distance computations
-                                   and get zero mask bits; -1: off.  Same result. */
+    int32_t block_prune;        /* 0 or 1: a block of queries and a group of candidates (MFMA kernels:
+                                   32 x 64, direct kernel: 8 x 256) whose bounding boxes over the
+                                   first 8 dimensions of the variance order are farther apart than
+                                   eps skip their distance computations and get zero mask bits;
+                                   -1: off.  Same result. */
+    int32_t cell_order;         /* order of the rows within a cell (Sec. IV-B groups points so that
+                                   each group has a tight box): 1 = Morton order of 8 x 8 x 8
+                                   sub-cells on the grid axes; 2 = Morton order over the cell's own
+                                   box in the first 8 dimensions of the variance order (3 bits per
+                                   dimension), which lets the MFMA kernels' block box test prune
+                                   more; 0 = 2 where an MFMA kernel can refine, else 1.  Same
+                                   result. */
 } ersj_options;
 
 typedef struct ersj_stats {

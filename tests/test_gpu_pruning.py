@@ -150,3 +150,22 @@ def test_norm_test_on_clusters_apart_off_the_grid_axes():
     X = X[rng.permutation(len(X))]
     check_against_oracle(X, 1.0, "families apart on a fourth axis")
     check_against_oracle(X, math.nextafter(1.0, 0.0), "families apart, eps just below 1")
+
+
+@pytest.mark.parametrize("name,n", [("c2", 20000), ("c3", 12000), ("c4", 30011), ("c1", 5000)])
+def test_cell_order_keeps_pairs_and_prunes_more(name, n):
+    # rows of a cell in Morton order over the cell's box in the first 8
+    # dimensions (cell_order 2, the default for the MFMA kernels) against
+    # 8 x 8 x 8 sub-cells on the grid axes (1): the same pairs and the same
+    # candidates (the pruning each order gets at full size is measured by
+    # the benchmark)
+    X = make_config(name, n)
+    eps, _, _ = oracle.calibrate_eps(X, min(1000, n), 32)
+    want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
+    st = {}
+    for order in (2, 1):
+        got, st[order] = _join(X, eps, ersj.REFINE_MFMA16, cell_order=order)
+        say(f"[gpu] {name} n={n} cell_order={order}: candidates {st[order]['refined_candidates']}, "
+            f"box-settled {st[order]['skipped_candidates']}")
+        assert np.array_equal(got, want), f"{name} cell_order={order}"
+    assert st[2]["refined_candidates"] == st[1]["refined_candidates"]
