@@ -1,12 +1,24 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
 times (default options; the d=64 workload with a budget that forces at
-least four memory-limited batches).
+least four memory-limited batches), compared with the oracle's stored
+neighbour fingerprints (tests/golden/make_digests.py, oracle only).
 
-The oracle cannot join these in seconds, so parity is checked on sampled
-rows (each row's neighbour list equal to the oracle's, computed row by
-row) and on properties that hold at any size: rows 0..999 carry exactly
-the neighbour count epsilon was calibrated for, every point pairs with
-itself, no pair is duplicated, and the pair multiset is symmetric.
+The result is the self-join of "RT-HiSS: Ray Tracing Accelerated High
+Dimensional Vector Similarity Searches", Sec. II-A.  Per query row the GPU
+pairs give a count and a fingerprint (sum of mix64 of the neighbour ids,
+tests/digest_util.py), equal to the oracle's exactly when the row's
+neighbour list is (up to a 2^-64 chance):
+
+* d=16 and d=32 workloads: every one of their 20,000 and 10^6 rows,
+  compared through per-block folds of 64 rows (a differing block is diffed
+  row by row against the oracle, so a failure names the rows and pairs);
+* the others: the stored sample (rows 0..999, 10,000 seeded rows, every row
+  of the largest cluster, and for the background mixture 2,000 background
+  rows), row by row.
+
+Properties that hold at any size are checked as well: rows 0..999 carry
+exactly the neighbour count epsilon was calibrated for, every point pairs
+with itself, no pair is duplicated, and the pair multiset is symmetric.
 """
 import json
 import os
@@ -19,6 +31,7 @@ import exact_range_similarity_amd as ersj
 import oracle
 from workloads import CONFIGS, make_config, x_digest
 
+from digest_util import block_fold, row_digests, u32
 from gpu_util import say
 
 pytestmark = pytest.mark.gpu
@@ -31,10 +44,6 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     ersj.lib()
-
-
-def u32(t):
-    return t.to(torch.int64) & 0xffffffff
 
 
 def chunks(parts):
@@ -89,11 +98,69 @@ def run_full(name, budget_div=0.0):
     del xt
     total = sum(p.shape[0] for p in parts)
     say(f"[gpu-full] {name}: batches={nb} cells={st['cells']} candidates={st['total_candidates']} "
-        f"pairs={total}")
+        f"pairs={total} band pairs re-checked (last batch)={st['last_boundary_pairs']}")
     return X, eps, rec, spec, parts, nb, total
 
 
-def check_common(name, X, eps, rec, spec, parts, total, n_sample=48, symmetric=True):
+def diff_rows(X, eps, parts, rows, label):
+    """Message naming the rows whose GPU list differs from the oracle's."""
+    rows = [int(r) for r in rows][:8]
+    got = rows_of(parts, rows)
+    colptr, cols = oracle.join_rows(X, eps, np.array(rows))
+    e2 = oracle.e64(eps)
+    lines = []
+    for k, r in enumerate(rows):
+        want = cols[colptr[k]:colptr[k + 1]].tolist()
+        if got[r] == want:
+            continue
+        extra = sorted(set(got[r]) - set(want))[:4]
+        missing = sorted(set(want) - set(got[r]))[:4]
+        dup = len(got[r]) - len(set(got[r]))
+        dd = [f"{j}: D64={oracle.d64(X[r], X[j])!r}" for j in extra + missing]
+        lines.append(f"row {r}: gpu {len(got[r])} oracle {len(want)} dup {dup} extra {extra} missing {missing} "
+                     f"E64={e2!r} {dd}")
+    return f"{label}: rows differ\n" + "\n".join(lines)
+
+
+def check_digests(name, X, eps, rec, parts):
+    with open(os.path.join(GOLDEN, "digests.json")) as f:
+        meta = json.load(f)[name]
+    z = np.load(os.path.join(GOLDEN, f"digests_{name}.npz"))
+    assert meta["eps"] == rec["eps"] and meta["x_sha256"] == rec["x_sha256"]
+    assert meta["oracle_version"] == oracle.version()
+    n = X.shape[0]
+    if meta["mode"] == "full":
+        cnt, dig = row_digests(parts, n)
+        bc, fp = block_fold(cnt, dig, meta["block"])
+        want_c = torch.from_numpy(z["block_count"].view(np.int64)).cuda()
+        want_f = torch.from_numpy(z["block_digest"].view(np.int64)).cuda()
+        bad = torch.nonzero((bc != want_c) | (fp != want_f)).flatten().cpu().numpy()
+        if bad.size:
+            blk = int(bad[0])
+            rows = np.arange(blk * meta["block"], min(n, (blk + 1) * meta["block"]))
+            oc, od, _ = oracle.digest_rows(X, eps, rows)
+            c = cnt[blk * meta["block"]:(blk + 1) * meta["block"]].cpu().numpy()
+            d = dig[blk * meta["block"]:(blk + 1) * meta["block"]].cpu().numpy().view(np.uint64)
+            diff = rows[(c != oc) | (d != od)]
+            raise AssertionError(f"{len(bad)} blocks differ; " + diff_rows(X, eps, parts, diff, name))
+        assert int(cnt.sum()) == meta["pairs"]
+        verified = n
+    else:
+        rows = torch.from_numpy(z["rows"].astype(np.int64)).cuda()
+        cnt, dig = row_digests(parts, n, rows)
+        want_c = torch.from_numpy(z["count"].astype(np.int64)).cuda()
+        want_d = torch.from_numpy(z["digest"].view(np.int64)).cuda()
+        bad = torch.nonzero((cnt != want_c) | (dig != want_d)).flatten().cpu().numpy()
+        if bad.size:
+            raise AssertionError(f"{len(bad)} rows differ; "
+                                 + diff_rows(X, eps, parts, z["rows"][bad], name))
+        verified = rows.numel()
+    say(f"[gpu-full] {name}: {verified} rows equal to the oracle ({meta['mode']}); oracle band pairs "
+        f"(|D64 - E64| <= {meta['band_rel']} E64) among them: {meta['band_pairs']}")
+    return verified
+
+
+def check_common(name, X, rec, spec, parts, symmetric=True):
     n = X.shape[0]
     # calibration identity over rows 0..nq-1
     nq = rec["nq"]
@@ -104,44 +171,59 @@ def check_common(name, X, eps, rec, spec, parts, total, n_sample=48, symmetric=T
         self_pairs += int((q == x).sum())
     assert cnt == nq * (spec.k + 1), (cnt, nq * (spec.k + 1))
     assert self_pairs == n
-    # sampled rows against the oracle, row by row
-    rng = np.random.default_rng(1234)
-    rows = np.unique(np.concatenate([np.arange(16), rng.integers(0, n, n_sample)]))
-    got = rows_of(parts, rows)
-    colptr, cols = oracle.join_rows(X, eps, rows)
-    for r_i, r in enumerate(rows):
-        want = cols[colptr[r_i]:colptr[r_i + 1]].tolist()
-        assert got[int(r)] == want, f"{name}: row {r} differs ({len(got[int(r)])} vs {len(want)})"
     if symmetric:
         fwd, rev = sym_hash(parts)
         assert fwd == rev, f"{name}: pair set is not symmetric"
 
 
-def check_unique(parts):
-    keys = torch.cat([(q << 32) | x for q, x in chunks(parts)])
-    s = torch.sort(keys).values
-    assert bool((s[1:] != s[:-1]).all())
+def check_unique(parts, n, rows_per_pass=None):
+    """No pair twice: keys sorted per range of query rows (one range when
+    rows_per_pass is None), so the largest results need not sort at once."""
+    step = n if rows_per_pass is None else rows_per_pass
+    for a in range(0, n, step):
+        keys = []
+        for q, x in chunks(parts):
+            sel = (q >= a) & (q < a + step)
+            if bool(sel.any()):
+                keys.append((q[sel] << 32) | x[sel])
+        if not keys:
+            continue
+        s = torch.sort(torch.cat(keys)).values
+        del keys
+        assert bool((s[1:] != s[:-1]).all()), f"duplicate pair among query rows {a}..{a + step - 1}"
+
+
+def test_full_c1():
+    X, eps, rec, spec, parts, nb, total = run_full("c1")
+    check_common("c1", X, rec, spec, parts)
+    check_unique(parts, X.shape[0])
+    assert check_digests("c1", X, eps, rec, parts) == X.shape[0]
 
 
 def test_full_c2():
     X, eps, rec, spec, parts, nb, total = run_full("c2")
-    check_common("c2", X, eps, rec, spec, parts, total)
-    check_unique(parts)
+    check_common("c2", X, rec, spec, parts)
+    check_unique(parts, X.shape[0])
+    assert check_digests("c2", X, eps, rec, parts) == X.shape[0]
 
 
 def test_full_c3_four_plus_batches():
     X, eps, rec, spec, parts, nb, total = run_full("c3", budget_div=4.5)
     assert nb >= 4
-    check_common("c3", X, eps, rec, spec, parts, total, n_sample=32)
-    check_unique(parts)
+    check_common("c3", X, rec, spec, parts)
+    check_unique(parts, X.shape[0])
+    assert check_digests("c3", X, eps, rec, parts) >= 11000
 
 
 def test_full_c4():
     X, eps, rec, spec, parts, nb, total = run_full("c4")
-    check_common("c4", X, eps, rec, spec, parts, total, n_sample=32)
+    check_common("c4", X, rec, spec, parts)
+    check_unique(parts, X.shape[0], rows_per_pass=1_000_000)
+    assert check_digests("c4", X, eps, rec, parts) >= 11000
 
 
 def test_full_c5():
     X, eps, rec, spec, parts, nb, total = run_full("c5")
-    check_common("c5", X, eps, rec, spec, parts, total, n_sample=24)
-    check_unique(parts)
+    check_common("c5", X, rec, spec, parts)
+    check_unique(parts, X.shape[0])
+    assert check_digests("c5", X, eps, rec, parts) >= 11000
