@@ -186,10 +186,14 @@ def main():
     mask_bytes = 8.0 * st["total_mask_words"] / max(1, st["n_batches"])
     hbm_bytes = mask_bytes + 4.0 * dpad * (X.shape[0] + (Q.shape[0] if semi else 0))
     hbm_gbs = hbm_bytes / (avg_launch_ms * 1e-3) / 1e9
-    kname = "k_refine_mfma" if mfma else "k_refine_direct"  # one kernel template, both MFMA forms
+    # the kernel that ran: the split-fp16 form on the whole-tile kernel up to
+    # 64 dimensions and on prepared operands above; the fp32 MFMA form; the
+    # direct form
+    nb = (d + 3) // 4
+    kname = ("k_refine_m16" if nb <= 16 else "k_refine_g16") if f16 else \
+        "k_refine_mfma" if mfma else "k_refine_direct"
     traffic = None
-    form = kname.replace("k_", "") + ("16" if f16 else "")
-    tfile = os.path.join(ROOT, "profiles", f"{form}_{args.workload}_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", f"{kname[2:]}_{args.workload}_traffic.json")
     if os.path.exists(tfile):
         import hashlib
         with open(tfile) as f:
