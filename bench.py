@@ -446,7 +446,8 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
         "phase_ms": phases,
         "roofline": {
             "bound": "mfma" if mfma else "alu",
-            "kernel": "k_refine_mfma" if mfma else "k_refine_direct",
+            "kernel": (("k_refine_m16" if (d + 3) // 4 <= 16 else "k_refine_g16") if f16
+                       else "k_refine_mfma" if mfma else "k_refine_direct"),
             "mfma_dtype": "f16 (hi/lo split), f32 accumulate" if f16 else "f32" if mfma else None,
             "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak, "traffic": None,

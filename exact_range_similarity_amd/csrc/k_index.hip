@@ -450,13 +450,13 @@ __global__ __launch_bounds__(kBlock) void k_cell_box8(const float *__restrict__ 
 
 // key = (cell << 24) | Morton interleave of the row's 3-bit positions in its
 // cell's box (most significant bits first, dimension 0 first at each level)
-__global__ __launch_bounds__(kBlock) void k_order_keys(const float *__restrict__ x, int64_t ld,
-                                                       const uint32_t *__restrict__ orig,
-                                                       const int32_t *__restrict__ perm, int nd,
-                                                       const uint64_t *__restrict__ cid, int64_t n,
-                                                       const uint32_t *__restrict__ lo_bits,
-                                                       const uint32_t *__restrict__ hi_bits,
-                                                       uint64_t *__restrict__ keys)
+__global__ __launch_bounds__(kBlock) void k_cell_order_keys(const float *__restrict__ x, int64_t ld,
+                                                            const uint32_t *__restrict__ orig,
+                                                            const int32_t *__restrict__ perm, int nd,
+                                                            const uint64_t *__restrict__ cid, int64_t n,
+                                                            const uint32_t *__restrict__ lo_bits,
+                                                            const uint32_t *__restrict__ hi_bits,
+                                                            uint64_t *__restrict__ keys)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -1041,7 +1041,7 @@ hipError_t launch_cell_order_keys(const float *x, int64_t n, int32_t d, int64_t 
                        (int64_t)kOrderDims * M);
     hipLaunchKernelGGL(k_cell_box8, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
                        box_hi);
-    hipLaunchKernelGGL(k_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
+    hipLaunchKernelGGL(k_cell_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
                        box_hi, keys);
     return hipGetLastError();
 }
