@@ -596,18 +596,25 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     TRY(dalloc(h, &out->lo_bits, (size_t)M * 3, "cells"));
     TRY(dalloc(h, &out->hi_bits, (size_t)M * 3, "cells"));
     HIPC(launch_cell_scatter(k0, 3 * h->gp.sub, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
+    TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
     if (h->box_order) {
-        // rows of each cell re-sorted by their Morton key in the cell's box
-        uint32_t *blo = nullptr, *bhi = nullptr;
+        // rows gathered in cell order first, then each cell's rows re-sorted
+        // by their Morton key in the cell's box and moved into place
+        float4 *xs1 = nullptr;
+        uint32_t *blo = nullptr, *bhi = nullptr, *orig1 = nullptr, *pos = nullptr;
+        TRY(tmp.get(&xs1, (size_t)h->nb * n, "cell order"));
         TRY(tmp.get(&blo, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&bhi, (size_t)M * kOrderDims, "cell order"));
-        HIPC(launch_cell_order_keys(x, n, d, ld, out->orig, dperm, cid, (int64_t)M, blo, bhi, k0, s),
-             "cell order kernels");
-        HIPC(radix_sort(k0, out->orig, k1, v1, n, 24 + ceil_log2(M + 1), hist, stmp, s), "cell order sort");
+        TRY(tmp.get(&orig1, (size_t)n, "cell order"));
+        TRY(tmp.get(&pos, (size_t)n, "cell order"));
+        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, xs1, s), "gather kernel");
+        HIPC(launch_cell_order_keys(xs1, n, h->nb, cid, (int64_t)M, blo, bhi, k0, pos, s), "cell order kernels");
+        HIPC(radix_sort(k0, pos, k1, v1, n, 24 + ceil_log2(M + 1), hist, stmp, s), "cell order sort");
+        HIPC(hipMemcpyAsync(orig1, out->orig, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s), "copy");
+        HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
+    } else {
+        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
     }
-
-    TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
-    HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
     // row-major copy in sorted order for the binary64 re-check, which sums
     // in the input's dimension order
     TRY(dalloc(h, &out->xr, (size_t)n * recheck_stride(d), "rows"));

@@ -412,12 +412,11 @@ __global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restr
 // grid axes.  The box test of the refinement covers the same dimensions.
 
 // Box of each cell over the first kOrderDims layout dimensions (ordered
-// float bits; box must hold 0xffffffff / 0 before): a wave per 64
-// consecutive sorted rows, reduced in the wave when they share a cell.
-__global__ __launch_bounds__(kBlock) void k_cell_box8(const float *__restrict__ x, int64_t ld,
-                                                      const uint32_t *__restrict__ orig,
-                                                      const int32_t *__restrict__ perm, int nd,
-                                                      const uint64_t *__restrict__ cid, int64_t n,
+// float bits; box must hold 0xffffffff / 0 before), from the rows gathered in
+// cell order (dimension-blocked, first two blocks): a wave per 64
+// consecutive rows, reduced in the wave when they share a cell.
+__global__ __launch_bounds__(kBlock) void k_cell_box8(const float4 *__restrict__ xs, int64_t n, int nb,
+                                                      const uint64_t *__restrict__ cid,
                                                       uint32_t *__restrict__ lo_bits,
                                                       uint32_t *__restrict__ hi_bits)
 {
@@ -428,54 +427,73 @@ __global__ __launch_bounds__(kBlock) void k_cell_box8(const float *__restrict__ 
     const int64_t cell = valid ? (int64_t)cid[i + 1] - 1 : -1;
     const int64_t c0 = __shfl(cell, 0, 64);
     const bool shared = __ballot(valid && cell != c0) == 0;  // lanes past n hold no row
-    const uint64_t row = valid ? (uint64_t)orig[i] * (uint64_t)ld : 0;
-    for (int a = 0; a < nd; ++a) {
-        const uint32_t o = valid ? f2ord(x[row + perm[a]]) : 0u;
-        if (shared) {
-            uint32_t lo = valid ? o : 0xffffffffu, hi = o;
-            for (int k = 1; k < 64; k <<= 1) {
-                lo = min(lo, (uint32_t)__shfl_xor((int)lo, k, 64));
-                hi = max(hi, (uint32_t)__shfl_xor((int)hi, k, 64));
+    for (int b = 0; b < kOrderDims / 4; ++b) {
+        const float4 v = valid && b < nb ? xs[(uint64_t)b * n + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float c[4] = {v.x, v.y, v.z, v.w};
+        for (int k = 0; k < 4; ++k) {
+            const int a = 4 * b + k;
+            const uint32_t o = valid ? f2ord(c[k]) : 0u;
+            if (shared) {
+                uint32_t lo = valid ? o : 0xffffffffu, hi = o;
+                for (int m = 1; m < 64; m <<= 1) {
+                    lo = min(lo, (uint32_t)__shfl_xor((int)lo, m, 64));
+                    hi = max(hi, (uint32_t)__shfl_xor((int)hi, m, 64));
+                }
+                if (lane == 0) {
+                    atomicMin(&lo_bits[c0 * kOrderDims + a], lo);
+                    atomicMax(&hi_bits[c0 * kOrderDims + a], hi);
+                }
+            } else if (valid) {
+                atomicMin(&lo_bits[cell * kOrderDims + a], o);
+                atomicMax(&hi_bits[cell * kOrderDims + a], o);
             }
-            if (lane == 0) {
-                atomicMin(&lo_bits[c0 * kOrderDims + a], lo);
-                atomicMax(&hi_bits[c0 * kOrderDims + a], hi);
-            }
-        } else if (valid) {
-            atomicMin(&lo_bits[cell * kOrderDims + a], o);
-            atomicMax(&hi_bits[cell * kOrderDims + a], o);
         }
     }
 }
 
 // key = (cell << 24) | Morton interleave of the row's 3-bit positions in its
-// cell's box (most significant bits first, dimension 0 first at each level)
-__global__ __launch_bounds__(kBlock) void k_cell_order_keys(const float *__restrict__ x, int64_t ld,
-                                                            const uint32_t *__restrict__ orig,
-                                                            const int32_t *__restrict__ perm, int nd,
-                                                            const uint64_t *__restrict__ cid, int64_t n,
+// cell's box (most significant bits first, dimension 0 first at each level);
+// value = the row's position in cell order
+__global__ __launch_bounds__(kBlock) void k_cell_order_keys(const float4 *__restrict__ xs, int64_t n, int nb,
+                                                            const uint64_t *__restrict__ cid,
                                                             const uint32_t *__restrict__ lo_bits,
                                                             const uint32_t *__restrict__ hi_bits,
-                                                            uint64_t *__restrict__ keys)
+                                                            uint64_t *__restrict__ keys,
+                                                            uint32_t *__restrict__ vals)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const uint64_t cell = cid[i + 1] - 1;
-    const uint64_t row = (uint64_t)orig[i] * (uint64_t)ld;
     uint32_t q[kOrderDims];
-    for (int a = 0; a < kOrderDims; ++a) {
-        q[a] = 0;
-        if (a >= nd) continue;
-        const float lo = ord2f(lo_bits[cell * kOrderDims + a]), hi = ord2f(hi_bits[cell * kOrderDims + a]);
-        const float v = x[row + perm[a]];
-        const float w = hi - lo;  // may be 0 or overflow to inf: then every row takes 0
-        const float t = w > 0.f && w < INFINITY ? (v - lo) / w * 8.0f : 0.0f;
-        q[a] = t >= 7.0f ? 7u : (t > 0.0f ? (uint32_t)t : 0u);
+    for (int b = 0; b < kOrderDims / 4; ++b) {
+        const float4 v4 = b < nb ? xs[(uint64_t)b * n + i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float c[4] = {v4.x, v4.y, v4.z, v4.w};
+        for (int k = 0; k < 4; ++k) {
+            const int a = 4 * b + k;
+            const float lo = ord2f(lo_bits[cell * kOrderDims + a]), hi = ord2f(hi_bits[cell * kOrderDims + a]);
+            const float w = hi - lo;  // may be 0 or overflow to inf: then every row takes 0
+            const float t = w > 0.f && w < INFINITY ? (c[k] - lo) / w * 8.0f : 0.0f;
+            q[a] = t >= 7.0f ? 7u : (t > 0.0f ? (uint32_t)t : 0u);
+        }
     }
     uint32_t m = 0;
     for (int b = 2; b >= 0; --b)
         for (int a = 0; a < kOrderDims; ++a) m = (m << 1) | ((q[a] >> b) & 1u);
     keys[i] = (cell << 24) | m;
+    vals[i] = (uint32_t)i;
+}
+
+// Rows put in their final order: thread i takes cell-order row perm[i]
+// (every dimension block, and its input row id).
+__global__ __launch_bounds__(kBlock) void k_permute_rows(const float4 *__restrict__ src, const uint32_t *__restrict__ orig_src,
+                                                         const uint32_t *__restrict__ perm, int64_t n, int nb,
+                                                         float4 *__restrict__ dst, uint32_t *__restrict__ orig_dst)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t j = perm[i];
+    orig_dst[i] = orig_src[j];
+    for (int b = 0; b < nb; ++b) dst[(uint64_t)b * n + i] = src[(uint64_t)b * n + j];
 }
 
 constexpr int kAabbSteps = 8;  // 64-point steps per wave
@@ -1029,20 +1047,26 @@ hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, in
     return hipGetLastError();
 }
 
-hipError_t launch_cell_order_keys(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
-                                  const int32_t *perm, const uint64_t *cid, int64_t M, uint32_t *box_lo,
-                                  uint32_t *box_hi, uint64_t *keys, hipStream_t s)
+hipError_t launch_cell_order_keys(const float4 *xs, int64_t n, int nb, const uint64_t *cid, int64_t M,
+                                  uint32_t *box_lo, uint32_t *box_hi, uint64_t *keys, uint32_t *vals, hipStream_t s)
 {
     if (n == 0) return hipSuccess;
-    const int nd = d < kOrderDims ? d : kOrderDims;
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_lo, 0xffffffffu,
                        (int64_t)kOrderDims * M);
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_hi, 0u,
                        (int64_t)kOrderDims * M);
-    hipLaunchKernelGGL(k_cell_box8, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
-                       box_hi);
-    hipLaunchKernelGGL(k_cell_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, x, ld, orig, perm, nd, cid, n, box_lo,
-                       box_hi, keys);
+    hipLaunchKernelGGL(k_cell_box8, dim3(grid_for(n)), dim3(kBlock), 0, s, xs, n, nb, cid, box_lo, box_hi);
+    hipLaunchKernelGGL(k_cell_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, xs, n, nb, cid, box_lo, box_hi,
+                       keys, vals);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const float4 *src, const uint32_t *orig_src, const uint32_t *perm, int64_t n, int nb,
+                               float4 *dst, uint32_t *orig_dst, hipStream_t s)
+{
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_permute_rows, dim3(grid_for(n)), dim3(kBlock), 0, s, src, orig_src, perm, n, nb, dst,
+                       orig_dst);
     return hipGetLastError();
 }
 
