@@ -599,16 +599,19 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
     if (h->box_order) {
         // rows gathered in cell order first, then each cell's rows re-sorted
-        // by their Morton key in the cell's box and moved into place
+        // by their code in the cell's box (midpoint splits of the widest
+        // extent) and moved into place
         float4 *xs1 = nullptr;
-        uint32_t *blo = nullptr, *bhi = nullptr, *orig1 = nullptr, *pos = nullptr;
+        uint32_t *blo = nullptr, *bhi = nullptr, *bmask = nullptr, *orig1 = nullptr, *pos = nullptr;
         TRY(tmp.get(&xs1, (size_t)h->nb * n, "cell order"));
         TRY(tmp.get(&blo, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&bhi, (size_t)M * kOrderDims, "cell order"));
+        TRY(tmp.get(&bmask, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&orig1, (size_t)n, "cell order"));
         TRY(tmp.get(&pos, (size_t)n, "cell order"));
         HIPC(launch_gather(x, n, d, ld, out->orig, dperm, xs1, s), "gather kernel");
-        HIPC(launch_cell_order_keys(xs1, n, h->nb, cid, (int64_t)M, blo, bhi, k0, pos, s), "cell order kernels");
+        HIPC(launch_cell_order_keys(xs1, n, h->nb, cid, (int64_t)M, blo, bhi, bmask, k0, pos, s),
+             "cell order kernels");
         HIPC(radix_sort(k0, pos, k1, v1, n, 24 + ceil_log2(M + 1), hist, stmp, s), "cell order sort");
         HIPC(hipMemcpyAsync(orig1, out->orig, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s), "copy");
         HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
@@ -722,13 +725,17 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     // own box in the first 8 dimensions (ordered after the cells are known,
     // so the cell key carries no sub-cell bits), or over 8 x 8 x 8 sub-cells
     // on the grid axes (fewer when the grid is near its 2^21 cap)
-    // automatic: the box order where an MFMA kernel will refine (their box
-    // test covers those 8 dimensions with 32-row and 64-candidate groups);
-    // the direct kernel's 256-candidate groups stay compact on the grid axes
-    // only under the sub-cell order
+    // automatic: the box order where an MFMA kernel with the box test will
+    // refine (it covers those 8 dimensions with 32-row and 64-candidate
+    // groups): the fp32 form, or the split form up to 64 dimensions; the
+    // direct kernel's 256-candidate groups stay compact on the grid axes only
+    // under the sub-cell order, and the split form above 64 dimensions has no
+    // box test
     const char *why_not = "";
+    const int rk = h->opt.refine_kernel;
     h->box_order = h->opt.cell_order == 2 ||
-                   (h->opt.cell_order == 0 && h->opt.refine_kernel != ERSJ_REFINE_DIRECT && coords_feasible(h, &why_not));
+                   (h->opt.cell_order == 0 && coords_feasible(h, &why_not) &&
+                    (rk == ERSJ_REFINE_MFMA || (rk != ERSJ_REFINE_DIRECT && h->nb <= 16)));
     gp.sub = h->box_order ? 0 : std::min(3, 21 - bits);
     h->gp = gp;
 

@@ -185,15 +185,17 @@ hipError_t launch_chunk_counts(const uint32_t *rpref, const uint32_t *nrng, int6
 // cbox: exact box of every 64-candidate chunk of every cell's candidate
 // list, from the group boxes and the points of partial groups
 // Order of the rows within each cell, from the rows gathered in cell order
-// (xs, dimension-blocked): key (cell << 24) | Morton code of the row's 3-bit
-// position in its cell's box over the first kOrderDims layout dimensions,
-// value = the row's position (box_lo/box_hi: [M][kOrderDims] temporaries;
-// cid: the cell scan, cell of position i = cid[i + 1] - 1).  Sorting the
-// keys gives perm; launch_permute_rows then moves every block of row perm[i]
-// and its input id to position i.
+// (xs, dimension-blocked): key (cell << 24) | the row's 24-bit code in its
+// cell's box over the first kOrderDims layout dimensions, the bits in the
+// order midpoint splits of the widest extent take them, value = the row's
+// position (box_lo/box_hi/masks: [M][kOrderDims] temporaries; cid: the cell
+// scan, cell of position i = cid[i + 1] - 1).  Sorting the keys gives perm;
+// launch_permute_rows then moves every block of row perm[i] and its input id
+// to position i.
 constexpr int kOrderDims = 8;
 hipError_t launch_cell_order_keys(const float4 *xs, int64_t n, int nb, const uint64_t *cid, int64_t M,
-                                  uint32_t *box_lo, uint32_t *box_hi, uint64_t *keys, uint32_t *vals, hipStream_t s);
+                                  uint32_t *box_lo, uint32_t *box_hi, uint32_t *masks, uint64_t *keys, uint32_t *vals,
+                                  hipStream_t s);
 hipError_t launch_permute_rows(const float4 *src, const uint32_t *orig_src, const uint32_t *perm, int64_t n, int nb,
                                float4 *dst, uint32_t *orig_dst, hipStream_t s);
 hipError_t launch_point_boxes(const float4 *xs, uint64_t n, int nb, float4 *pbox, hipStream_t s);

@@ -405,9 +405,10 @@ __global__ __launch_bounds__(kBlock) void k_cell_scatter(const uint64_t *__restr
 }
 
 // ------------------------------------------------- order within a cell --
-// Rows of a cell in Morton order over the cell's own box in the first
-// kOrderDims dimensions of the variance order (3 bits per dimension), so
-// that runs of consecutive rows - the refinement's 32-row query blocks and
+// Rows of a cell ordered as the leaves of a kd-tree with midpoint splits of
+// the cell's own box in the first kOrderDims dimensions of the variance
+// order (each split halves the widest remaining extent; 24 levels), so that
+// runs of consecutive rows - the refinement's 32-row query blocks and
 // 64-candidate chunks - are compact in those dimensions and not only on the
 // grid axes.  The box test of the refinement covers the same dimensions.
 
@@ -451,35 +452,89 @@ __global__ __launch_bounds__(kBlock) void k_cell_box8(const float4 *__restrict__
     }
 }
 
-// key = (cell << 24) | Morton interleave of the row's 3-bit positions in its
-// cell's box (most significant bits first, dimension 0 first at each level);
-// value = the row's position in cell order
+// The order of the key bits of a cell's rows, as a kd-tree with midpoint
+// splits would cut the cell's box: 24 times, the dimension whose current
+// width (extent / 2^(bits already taken)) is largest takes the next bit
+// (ties: the lower dimension).  masks[c][a] holds the key positions of
+// dimension a's bits (bit 23 first).  A thread per cell.
+__global__ __launch_bounds__(kBlock) void k_cell_split(const uint32_t *__restrict__ lo_bits,
+                                                       const uint32_t *__restrict__ hi_bits, int64_t M,
+                                                       uint32_t *__restrict__ masks)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= M) return;
+    float ext[kOrderDims];
+    uint32_t m[kOrderDims];
+    int nbits[kOrderDims];
+#pragma unroll
+    for (int a = 0; a < kOrderDims; ++a) {
+        const float e = ord2f(hi_bits[c * kOrderDims + a]) - ord2f(lo_bits[c * kOrderDims + a]);
+        ext[a] = e > 0.f ? e : 0.f;  // inf stays inf (never split past it)
+        m[a] = 0;
+        nbits[a] = 0;
+    }
+    for (int t = 23; t >= 0; --t) {
+        int best = 0;
+        float bw = -1.f;
+#pragma unroll
+        for (int a = 0; a < kOrderDims; ++a) {
+            const float w = ldexpf(ext[a], -nbits[a]);
+            if (w > bw) {
+                bw = w;
+                best = a;
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < kOrderDims; ++a) {
+            if (a == best) {
+                m[a] |= 1u << t;
+                ++nbits[a];
+            }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < kOrderDims; ++a) masks[c * kOrderDims + a] = m[a];
+}
+
+// key = (cell << 24) | the row's position in its cell's box, each dimension
+// quantised to as many bits as k_cell_split gave it and its bits placed at
+// that dimension's key positions; value = the row's position in cell order
 __global__ __launch_bounds__(kBlock) void k_cell_order_keys(const float4 *__restrict__ xs, int64_t n, int nb,
                                                             const uint64_t *__restrict__ cid,
                                                             const uint32_t *__restrict__ lo_bits,
                                                             const uint32_t *__restrict__ hi_bits,
+                                                            const uint32_t *__restrict__ masks,
                                                             uint64_t *__restrict__ keys,
                                                             uint32_t *__restrict__ vals)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const uint64_t cell = cid[i + 1] - 1;
-    uint32_t q[kOrderDims];
+    uint32_t key = 0;
+#pragma unroll
     for (int b = 0; b < kOrderDims / 4; ++b) {
         const float4 v4 = b < nb ? xs[(uint64_t)b * n + i] : make_float4(0.f, 0.f, 0.f, 0.f);
         const float c[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int a = 4 * b + k;
+            uint32_t pm = masks[cell * kOrderDims + a];
+            const int nbits = __popc(pm);
+            if (nbits == 0) continue;
             const float lo = ord2f(lo_bits[cell * kOrderDims + a]), hi = ord2f(hi_bits[cell * kOrderDims + a]);
-            const float w = hi - lo;  // may be 0 or overflow to inf: then every row takes 0
-            const float t = w > 0.f && w < INFINITY ? (c[k] - lo) / w * 8.0f : 0.0f;
-            q[a] = t >= 7.0f ? 7u : (t > 0.0f ? (uint32_t)t : 0u);
+            const float w = hi - lo;  // 0 (a one-point cell) or inf: every row takes 0
+            const float t = w > 0.f && w < INFINITY ? (c[k] - lo) / w * (float)(1u << nbits) : 0.0f;
+            const uint32_t top = (1u << nbits) - 1u;
+            const uint32_t q = t >= (float)top ? top : (t > 0.0f ? (uint32_t)t : 0u);
+            // deposit q's bits, most significant first, at the positions of pm
+            for (int j = nbits - 1; j >= 0; --j) {
+                const int pos = 31 - __clz(pm);
+                key |= ((q >> j) & 1u) << pos;
+                pm &= ~(1u << pos);
+            }
         }
     }
-    uint32_t m = 0;
-    for (int b = 2; b >= 0; --b)
-        for (int a = 0; a < kOrderDims; ++a) m = (m << 1) | ((q[a] >> b) & 1u);
-    keys[i] = (cell << 24) | m;
+    keys[i] = (cell << 24) | key;
     vals[i] = (uint32_t)i;
 }
 
@@ -1048,7 +1103,8 @@ hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, in
 }
 
 hipError_t launch_cell_order_keys(const float4 *xs, int64_t n, int nb, const uint64_t *cid, int64_t M,
-                                  uint32_t *box_lo, uint32_t *box_hi, uint64_t *keys, uint32_t *vals, hipStream_t s)
+                                  uint32_t *box_lo, uint32_t *box_hi, uint32_t *masks, uint64_t *keys, uint32_t *vals,
+                                  hipStream_t s)
 {
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_lo, 0xffffffffu,
@@ -1056,8 +1112,9 @@ hipError_t launch_cell_order_keys(const float4 *xs, int64_t n, int nb, const uin
     hipLaunchKernelGGL(k_fill_u32, dim3(grid_for(kOrderDims * M)), dim3(kBlock), 0, s, box_hi, 0u,
                        (int64_t)kOrderDims * M);
     hipLaunchKernelGGL(k_cell_box8, dim3(grid_for(n)), dim3(kBlock), 0, s, xs, n, nb, cid, box_lo, box_hi);
+    hipLaunchKernelGGL(k_cell_split, dim3(grid_for(M)), dim3(kBlock), 0, s, box_lo, box_hi, M, masks);
     hipLaunchKernelGGL(k_cell_order_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, xs, n, nb, cid, box_lo, box_hi,
-                       keys, vals);
+                       masks, keys, vals);
     return hipGetLastError();
 }
 

@@ -92,10 +92,12 @@ typedef struct ersj_options {
                                    -1: off.  Same result. */
     int32_t cell_order;         /* order of the rows within a cell (Sec. IV-B groups points so that
                                    each group has a tight box): 1 = Morton order of 8 x 8 x 8
-                                   sub-cells on the grid axes; 2 = Morton order over the cell's own
-                                   box in the first 8 dimensions of the variance order (3 bits per
-                                   dimension), which lets the MFMA kernels' block box test prune
-                                   more; 0 = 2 where an MFMA kernel can refine, else 1.  Same
+                                   sub-cells on the grid axes; 2 = the leaf order of a kd-tree over
+                                   the cell's own box in the first 8 dimensions of the variance
+                                   order, each of its 24 levels halving the widest remaining
+                                   extent, which lets the MFMA kernels' block box test prune more;
+                                   0 = 2 where an MFMA kernel with the box test refines (the fp32
+                                   form, or the split form up to 64 dimensions), else 1.  Same
                                    result. */
 } ersj_options;
 
