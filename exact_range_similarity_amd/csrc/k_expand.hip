@@ -134,9 +134,8 @@ __device__ __forceinline__ int nth_bit(uint64_t w, uint32_t r)
 // turn (thread i takes bits i, i + 256, ...).  A bit finds its word through
 // a bit map of the words' first output bits and, per 64 output bits, the
 // word that holds the first; a word's range of the cell's list is looked up
-// once per word.  A row's pairs fill its output range in candidate order;
-// its next output position is kept in LDS from one batch of units to the
-// next.
+// once per word.  The tile's pairs fill its output range in row-then-
+// candidate order, so bit j of a batch goes to the running offset + j.
 constexpr uint32_t kFlagPass = 4096;   // flag bytes read per pass
 constexpr uint32_t kUnitBatch = 64;    // listed units expanded per batch (256 words)
 static_assert(kTileRows < 255, "rows of a tile are held in bytes (0xff: no row)");
@@ -182,7 +181,6 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     __shared__ uint16_t s_list[kFlagPass];   // pass-relative byte offsets of flagged units
     __shared__ uint32_t s_ftot[16];          // flagged bytes per (load k, wave)
     __shared__ uint32_t s_wtot[4];
-    __shared__ uint8_t s_row[256];
     // the batch's non-empty words in output order (index e), and the bit map
     // of their first output bits (256 x 64 bits: a batch holds at most 16384)
     __shared__ uint64_t s_word[256];
@@ -193,8 +191,6 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     __shared__ uint16_t s_excl[256];     // first output bit
     __shared__ uint16_t s_first[256];    // non-empty word holding output bit 64 c
     __shared__ uint8_t s_erow[256];
-    __shared__ uint64_t s_rpos[kTileRows];   // next output position of each row
-    __shared__ uint64_t s_rbase[kTileRows];  // output position of the batch's bit 0, per row
     __shared__ uint32_t s_qid[kTileRows];
     const uint32_t t = t0 + blockIdx.x;
     const Tile tl = tiles[t];
@@ -203,11 +199,12 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     const uint32_t tid = threadIdx.x;
     if (tid <= kMaxRanges) s_pref[tid] = tid <= nr ? rpref[(uint64_t)A * (kMaxRanges + 1) + tid] : 0xffffffffu;
     if (tid < kMaxRanges) s_start[tid] = rstart[(uint64_t)A * kMaxRanges + tid];
-    if (tid < tl.nrows) {
-        const uint32_t q = tl.row0 + tid;
-        s_qid[tid] = qorig[q];
-        s_rpos[tid] = roff[q - row_base];
-    }
+    if (tid < tl.nrows) s_qid[tid] = qorig[tl.row0 + tid];
+    // the tile's rows own one contiguous output range, filled in row order
+    // (a row's bits all lie in its flagged units, counted in its row count):
+    // the batches' bits, taken in row-then-candidate order, land at
+    // consecutive positions from the first row's offset
+    uint64_t pos0 = roff[tl.row0 - row_base];
     const uint64_t tbase = toff[t] - wbase;         // first word of the tile (a multiple of 8)
     const uint64_t fb = tbase >> 2;                  // its first flag byte
     const uint32_t fstride = tl.words >> 2;          // flag bytes per row
@@ -294,16 +291,12 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
             const uint32_t wi = wi_next, row = row_next;
             if (i0 + kUnitBatch < nl) load_word(i0 + kUnitBatch, &m_next, &wi_next, &row_next);
             const uint32_t pc = __popcll(m);
-            s_row[tid] = (uint8_t)row;
             s_starts[tid] = 0ull;
             // one scan for both the bit offsets (low 16 bits, at most 16384)
             // and the ranks of the non-empty words (high bits)
             uint32_t tot;
             const uint32_t ex = block_excl_scan(pc | (pc != 0u ? 1u << 16 : 0u), s_wtot, &tot);
             const uint32_t excl = ex & 0xffffu, e = ex >> 16, total = tot & 0xffffu;
-            const bool first = row != 0xffu && (tid == 0 || s_row[tid - 1] != row);
-            const bool last = row != 0xffu && (tid == 255 || s_row[tid + 1] != row);
-            if (first) s_rbase[row] = s_rpos[row] - excl;
             if (pc != 0u) {
                 s_word[e] = m;
                 s_wi[e] = wi;
@@ -317,7 +310,6 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 if (64u * c < excl + pc) s_first[c] = (uint16_t)e;
             }
             __syncthreads();
-            if (last) s_rpos[row] = s_rbase[row] + excl + pc;
             // bit j of the batch -> (output position, query id, point): its
             // word is the last one starting at or before j, counted from the
             // word that holds bit 64 (j / 64); two bits per thread at a
@@ -331,9 +323,8 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                     const int g = range_of(s_pref, nr, p);
                     return s_start[g] + (p - s_pref[g]);
                 }();
-                const uint32_t r = s_erow[e];
-                *qid = s_qid[r];
-                *pos = s_rbase[r] + j;
+                *qid = s_qid[s_erow[e]];
+                *pos = pos0 + j;
             };
             auto put = [&](uint64_t pos, uint32_t qid, uint32_t id) __attribute__((always_inline)) {
                 if (al8) {
@@ -354,6 +345,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 put(pa, qa, ia);
                 if (two) put(pb, qb, ib);
             }
+            pos0 += total;
             __syncthreads();
         }
     }
