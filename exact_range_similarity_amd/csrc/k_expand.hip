@@ -208,6 +208,15 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
     const uint64_t tbase = toff[t] - wbase;         // first word of the tile (a multiple of 8)
     const uint64_t fb = tbase >> 2;                  // its first flag byte
     const uint32_t fstride = tl.words >> 2;          // flag bytes per row
+    // o / fstride for a tile byte o (quotient < kTileRows): a float estimate,
+    // off by at most one, then corrected
+    const float frcp = 1.0f / (float)fstride;
+    auto row_of = [&](uint32_t o) __attribute__((always_inline)) {
+        uint32_t r = (uint32_t)((float)o * frcp);
+        r = r * fstride > o ? r - 1 : r;
+        r = (r + 1) * fstride <= o ? r + 1 : r;
+        return r;
+    };
     const uint32_t nunits = (tl.used + 3) >> 2;      // units that hold candidates
     const uint64_t nbytes = (uint64_t)tl.nrows * fstride;  // below 2^32 (rows <= kTileRows)
     if (nbytes == 0) return;                           // uniform: no barrier passed yet
@@ -236,7 +245,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
                 for (int b = 0; b < 4; ++b) {
                     const int64_t o = (int64_t)(4 * di + b) - (int64_t)fb;
                     if (((f[k] >> (8 * b)) & 0xffu) != 0u && o >= 0 && (uint64_t)o < nbytes &&
-                        (uint32_t)o % fstride < nunits)
+                        (uint32_t)o - row_of((uint32_t)o) * fstride < nunits)
                         m |= 1u << b;
                 }
             }
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(256) void k_expand(const Tile *__restrict__ tiles, 
             *row = 0xffu;
             if (e < nl) {
                 const uint32_t o = (uint32_t)(4 * c + s_list[e] - fb);
-                *row = o / fstride;
+                *row = row_of(o);
                 *wi = (o - *row * fstride) * 4 + (tid & 3);
                 if (*wi < tl.used) *m = mask[tbase + (uint64_t)*row * tl.words + *wi];
             }
