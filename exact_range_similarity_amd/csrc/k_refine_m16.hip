@@ -78,7 +78,7 @@ struct M16 {
     static constexpr size_t BYTES = WORDS + (size_t)WB * kRows * 8 * 8;
 };
 
-template <int NS, int QBW>
+template <int NS, int QBW, bool PK>
 __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs a)
 {
     using G = M16<NS, QBW>;
@@ -158,6 +158,35 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
         float nq = 0.f;
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) {
+            if (PK && sl == NS - 1) {
+                // the last slab holds one dimension block (4 dimensions): its
+                // three products share one instruction, k 0-3 h.h, 4-7 h.l,
+                // 8-11 l.h (row operand: h, h | l, 0)
+                const int b = sl * 4;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (valid) {
+                    const float4 x = xq[(uint64_t)b * nqr + row0 + r];
+                    const float4 nr4 = LNRS[b];
+                    v = make_float4(fmaf(x.x, s16, nr4.x), fmaf(x.y, s16, nr4.y), fmaf(x.z, s16, nr4.z),
+                                    fmaf(x.w, s16, nr4.w));
+                }
+                if (hi == 0) {  // the row's norm takes the block once
+                    nq = fmaf(v.x, v.x, nq);
+                    nq = fmaf(v.y, v.y, nq);
+                    nq = fmaf(v.z, v.z, nq);
+                    nq = fmaf(v.w, v.w, nq);
+                }
+                half4 hh, ll;
+                split16(v, hh, ll);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    ah[i][sl][k] = hi == 0 ? hh[k] : ll[k];
+                    ah[i][sl][4 + k] = hi == 0 ? hh[k] : (_Float16)0.0f;
+                    al[i][sl][k] = (_Float16)0.0f;
+                    al[i][sl][4 + k] = (_Float16)0.0f;
+                }
+                continue;
+            }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int b = sl * 4 + hi * 2 + h2;
@@ -380,10 +409,17 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
             s2 = fmaf(v.w, v.w, s2);
             half4 hh, ll;
             split16(v, hh, ll);
-            // slab b / 4, [hi k 0-7, hi k 8-15, lo k 0-7, lo k 8-15][candidate], 8 bytes per block
+            // slab b / 4, [hi k 0-7, hi k 8-15, lo k 0-7, lo k 8-15][candidate], 8 bytes per block;
+            // a packed last slab: [h, l | h, 0] in parts 0 and 1 (k 12-15 stay zero)
             const int sl = b >> 2, p = (b & 3) >> 1, o = (b & 1) * 8;
-            *(half4 *)(xb + ((size_t)(sl * 4 + p) * kStep + lc) * 16 + o) = hh;
-            *(half4 *)(xb + ((size_t)(sl * 4 + 2 + p) * kStep + lc) * 16 + o) = ll;
+            if (PK && sl == NS - 1) {
+                *(half4 *)(xb + ((size_t)(sl * 4) * kStep + lc) * 16) = hh;
+                *(half4 *)(xb + ((size_t)(sl * 4) * kStep + lc) * 16 + 8) = ll;
+                *(half4 *)(xb + ((size_t)(sl * 4 + 1) * kStep + lc) * 16) = hh;
+            } else {
+                *(half4 *)(xb + ((size_t)(sl * 4 + p) * kStep + lc) * 16 + o) = hh;
+                *(half4 *)(xb + ((size_t)(sl * 4 + 2 + p) * kStep + lc) * 16 + o) = ll;
+            }
         }
         LNXP[(buf * G::TPC + lh) * kStep + lc] = s2;
         if (lh == 0) LXI[buf * kStep + lc] = ldi;
@@ -401,6 +437,7 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
                                  *(const half8 *)&xb[(sl * 4 + 2 + hi) * kStep + c0 + 32]};
             const floatx16 z = {};
             // three products, each accumulator touched every 2 QBW instructions
+            // (one for a packed last slab)
 #pragma unroll
             for (int i = 0; i < QBW; ++i) {
                 if (!dq[i]) continue;
@@ -409,6 +446,7 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
                     acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i][sl], bh[tt], sl == 0 ? z : acc[i][tt],
                                                                         0, 0, 0);
             }
+            if (PK && sl == NS - 1) continue;
 #pragma unroll
             for (int i = 0; i < QBW; ++i) {
                 if (!dq[i]) continue;
@@ -550,13 +588,17 @@ __global__ __launch_bounds__(256, QBW == 1 ? 4 : 2) void k_refine_m16(RefineArgs
 // three slabs on (the query halves fill the registers anyway)
 constexpr int qbw_of(int ns) { return ns <= 2 ? 1 : 2; }
 
-const void *m16_kernel(int ns)
+// one block in the last slab (nb % 4 == 1): that slab's products packed
+// into one instruction
+const void *m16_kernel(int nb)
 {
+    const int ns = (nb + 3) / 4;
+    const bool pk = nb % 4 == 1;
     switch (ns) {
-    case 1: return (const void *)k_refine_m16<1, 1>;
-    case 2: return (const void *)k_refine_m16<2, 1>;
-    case 3: return (const void *)k_refine_m16<3, 2>;
-    case 4: return (const void *)k_refine_m16<4, 2>;
+    case 1: return pk ? (const void *)k_refine_m16<1, 1, true> : (const void *)k_refine_m16<1, 1, false>;
+    case 2: return pk ? (const void *)k_refine_m16<2, 1, true> : (const void *)k_refine_m16<2, 1, false>;
+    case 3: return pk ? (const void *)k_refine_m16<3, 2, true> : (const void *)k_refine_m16<3, 2, false>;
+    case 4: return pk ? (const void *)k_refine_m16<4, 2, true> : (const void *)k_refine_m16<4, 2, false>;
     default: return nullptr;
     }
 }
@@ -576,15 +618,13 @@ uint32_t m16_step(int ns) { return (uint32_t)(64 * qbw_of(ns)); }
 
 }  // namespace
 
-// Used for three and four slabs (33 to 64 dimensions).  With one or two
-// slabs its two waves per SIMD (179 registers) hide load latency worse than
-// k_refine_mfma's four, which is then faster (c2: 9.3 against 13.4 ms).
+// The split form for up to 64 dimensions.
 bool refine_m16_supported(int nb) { return nb >= 1 && nb <= 16; }
 
 hipError_t prepare_refine_m16(int nb)
 {
     const int ns = (nb + 3) / 4;
-    const void *k = m16_kernel(ns);
+    const void *k = m16_kernel(nb);
     if (!k) return hipErrorInvalidValue;
     return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)m16_lds(ns));
 }
@@ -592,7 +632,7 @@ hipError_t prepare_refine_m16(int nb)
 hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s)
 {
     const int ns = (a.nb + 3) / 4;
-    const void *k = m16_kernel(ns);
+    const void *k = m16_kernel(a.nb);
     if (!k) return hipErrorInvalidValue;
     if (a.seg_len % kGroupCands != 0 || a.seg_len > 8192u || a.seg_len % m16_step(ns) != 0)
         return hipErrorInvalidValue;
