@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--no-block-prune", action="store_true",
                     help="switch off the MFMA kernel's query-block/candidate-group box test")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
+    ap.add_argument("--mfma-products", type=int, default=0, choices=(0, 1, 3),
+                    help="split-fp16 form above 64 dimensions: products per slab (0 = the library's choice)")
     ap.add_argument("--no-host", action="store_true",
                     help="skip the timing of the join delivered to pinned host memory")
     args = ap.parse_args()
@@ -126,7 +128,8 @@ def main():
     def step(timing):
         opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine,
                                     grid_reach=args.grid_reach,
-                                    block_prune=-1 if args.no_block_prune else 0)
+                                    block_prune=-1 if args.no_block_prune else 0,
+                                mfma_products=args.mfma_products)
         h = ersj.build_index(xt, eps, opts, stream)
         if semi:
             ersj.set_queries(h, qt, stream)
@@ -168,10 +171,11 @@ def main():
     kern = st["refine_kernel"]
     mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
     f16 = kern == ersj.REFINE_MFMA16
+    prods = st["mfma_products"]  # fp16 products per slab of the split form (1 or 3)
     # algorithmic flops per computed candidate: 2d + 3 for the expanded
     # form (a d-term dot product and the combination with the two norms),
     # 3d for the direct form (difference, square, sum per dimension); the
-    # split-fp16 form executes three fp16 products per dimension but is
+    # split-fp16 form executes one or three fp16 products per dimension but is
     # priced, like the others, by the work the distance needs
     per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
     flops_per_launch = per_cand * evaluated / max(1, launches)
@@ -201,6 +205,7 @@ def main():
         with open(os.path.join(ROOT, trec["source"]), "rb") as f:
             cur = hashlib.sha256(f.read()).hexdigest()
         if cur == trec["source_sha256"] and trec["workload"] == args.workload and not budget and not semi \
+                and trec.get("mfma_products", prods) == prods \
                 and args.grid_reach == 1 and not args.no_block_prune:
             traffic = trec["hbm_bytes_per_launch"]
     phases = {k: sum(s[k] for s in stats) / args.steps
@@ -217,7 +222,7 @@ def main():
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f16x3/f32" if f16 else "f32",
+        "dtype": (f"f16x{prods}/f32" if prods > 1 else "f16/f32") if f16 else "f32",
         "data": "synthetic",
         "config": {
             "workload": (f"{args.workload}: {spec.desc}; eps for a mean of {spec.k} neighbours/point"
@@ -228,6 +233,7 @@ def main():
             "batches": st["n_batches"], "budget_bytes": budget, "grid_reach": args.grid_reach,
             "block_prune": not args.no_block_prune,
             "refine_kernel": {1: "direct", 2: "mfma", 3: "mfma16"}.get(kern, "?"),
+            "mfma_products": prods,
         },
         "join_wall_s": wall,
         "result_pairs": npairs,
@@ -246,7 +252,9 @@ def main():
         "roofline": {
             "bound": "mfma" if mfma else "alu",
             "kernel": kname,
-            "mfma_dtype": "f16 (hi/lo split), f32 accumulate" if f16 else "f32" if mfma else None,
+            "mfma_dtype": ("f16 (hi/lo split), f32 accumulate" if prods == 3 else
+                           "f16 (high halves; binary64 re-check of the wider band), f32 accumulate")
+                          if f16 else "f32" if mfma else None,
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
@@ -357,7 +365,8 @@ def sample_mismatches(args, ersj, xt, qt, eps, budget, stream, nrows, colptr, co
     import numpy as np
     import torch
     opts = ersj.default_options(refine_kernel=args.refine, grid_reach=args.grid_reach,
-                                block_prune=-1 if args.no_block_prune else 0)
+                                block_prune=-1 if args.no_block_prune else 0,
+                                mfma_products=args.mfma_products)
     h = ersj.build_index(xt, eps, opts, stream)
     if qt is not None:
         ersj.set_queries(h, qt, stream)
@@ -390,7 +399,8 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
     k = args.k if args.k > 0 else spec.k
     eps0 = eps * args.eps0_scale
     opts = ersj.default_options(timing=1, refine_kernel=args.refine, grid_reach=args.grid_reach,
-                                block_prune=-1 if args.no_block_prune else 0)
+                                block_prune=-1 if args.no_block_prune else 0,
+                                mfma_products=args.mfma_products)
     ids = None
     for w in range(args.warmup):
         ids, _, info = ersj.knn(xt, k, eps0, growth=args.growth, options=opts, stream=stream)
@@ -413,6 +423,9 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
     kern = info["refine_kernel"]
     mfma = kern in (ersj.REFINE_MFMA, ersj.REFINE_MFMA16)
     f16 = kern == ersj.REFINE_MFMA16
+    # products per slab of the split form: three up to 64 dimensions, above
+    # them the option's choice (high halves alone by default)
+    prods = 3 if (d + 3) // 4 <= 16 or args.mfma_products == 3 else 1
     per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
     avg_launch_ms = refine_ms / max(1, launches)
     flops_per_launch = per_cand * computed / max(1, launches)
@@ -431,7 +444,7 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f16x3/f32" if f16 else "f32",
+        "dtype": (f"f16x{prods}/f32" if prods > 1 else "f16/f32") if f16 else "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {spec.desc}; exact kNN of every point, k={k}, first "
                                f"radius {args.eps0_scale} x the workload's eps",
@@ -448,7 +461,9 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
             "bound": "mfma" if mfma else "alu",
             "kernel": (("k_refine_m16" if (d + 3) // 4 <= 16 else "k_refine_g16") if f16
                        else "k_refine_mfma" if mfma else "k_refine_direct"),
-            "mfma_dtype": "f16 (hi/lo split), f32 accumulate" if f16 else "f32" if mfma else None,
+            "mfma_dtype": ("f16 (hi/lo split), f32 accumulate" if prods == 3 else
+                           "f16 (high halves; binary64 re-check of the wider band), f32 accumulate")
+                          if f16 else "f32" if mfma else None,
             "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak, "traffic": None,
             "flops_per_launch": flops_per_launch, "avg_launch_ms": avg_launch_ms, "launches": launches,

@@ -53,7 +53,7 @@ class Options(ctypes.Structure):
                 ("cell_width_scale", ctypes.c_double), ("max_device_bytes", ctypes.c_uint64),
                 ("boundary_capacity", ctypes.c_uint64), ("timing", ctypes.c_int32),
                 ("grid_reach", ctypes.c_int32), ("block_prune", ctypes.c_int32),
-                ("cell_order", ctypes.c_int32)]
+                ("cell_order", ctypes.c_int32), ("mfma_products", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -70,7 +70,7 @@ class Stats(ctypes.Structure):
                 ("recheck_ms", ctypes.c_double), ("expand_ms", ctypes.c_double),
                 ("refine_launches", ctypes.c_int64), ("refined_candidates", ctypes.c_uint64),
                 ("n_queries", ctypes.c_int64), ("last_skipped", ctypes.c_uint64),
-                ("skipped_candidates", ctypes.c_uint64)]
+                ("skipped_candidates", ctypes.c_uint64), ("mfma_products", ctypes.c_int32)]
 
     def as_dict(self):
         out = {}

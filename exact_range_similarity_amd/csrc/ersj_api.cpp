@@ -134,6 +134,7 @@ struct ersj_index {
     bool box_order = false;  // rows of a cell in Morton order over its 8-dimension box
     bool use_m16 = false;  // split-fp16 form on the whole-tile kernel (33 <= d <= 64)
     bool use_g16 = false;  // split-fp16 form on operands prepared per point (d > 64)
+    bool g16_hh = false;   // ... with the high-half products alone
     std::vector<double> mean;  // per input dimension (binary64 statistics of the points)
     float4 *tref = nullptr;  // per row tile: reference point of the MFMA kernels' centring
     uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
@@ -477,8 +478,21 @@ int choose_kernel(ersj_index *h)
     }
     h->use_m16 = k == ERSJ_REFINE_MFMA16 && refine_m16_supported(h->nb);
     h->use_g16 = k == ERSJ_REFINE_MFMA16 && h->nb > 16;
+    h->g16_hh = h->use_g16 && h->opt.mfma_products != 3;
+    if (h->g16_hh) {
+        // High-half products alone (k_refine_g16.hip): the dropped products
+        // move s^2 q'.x' by at most 2^-10 (1 + 2^-12) sum |v_q v_x| (in the
+        // squared distance at most twice that, <= 2^-10 (1 + 2^-12) (Nq + Nx))
+        // plus absolute parts within tabs; one MFMA per slab (padded to an
+        // even count) at 36u each, and the fp32 form's 4 (d_pad + 8) u.
+        const double u = std::ldexp(1.0, -24);
+        const double K = 4.0 * (4.0 * h->nb + 8.0) * u + std::ldexp(1.0 + std::ldexp(1.0, -12), -10) +
+                         36.0 * u * 2.0 * g16_stages(h->nb, true) * 1.01;
+        h->kp = (float)(1.0 + K);
+        h->km = (float)(1.0 - K);
+    }
     if (h->use_m16) HIPC(prepare_refine_m16(h->nb), "MFMA kernel LDS attribute");
-    else if (h->use_g16) HIPC(prepare_refine_g16(), "MFMA kernel LDS attribute");
+    else if (h->use_g16) HIPC(prepare_refine_g16(h->g16_hh), "MFMA kernel LDS attribute");
     else if (k == ERSJ_REFINE_MFMA16) HIPC(prepare_refine_mfma(h->nb, true), "MFMA kernel LDS attribute");
     return ERSJ_OK;
 }
@@ -800,7 +814,7 @@ void release_queries(ersj_index *h)
 // variance order; padded dimensions 0), scaled by s16, split, with norms.
 int prepare_operands(ersj_index *h, hipStream_t s)
 {
-    const int nb = h->nb, ns = (nb + 3) / 4;
+    const int nb = h->nb, ns = g16_stages(nb, h->g16_hh);
     std::vector<float> nrs((size_t)nb * 4, 0.0f);
     for (int j = 0; j < h->d; ++j) nrs[j] = -((float)h->mean[h->perm[j]] * h->s16);
     Scratch tmp(h);
@@ -809,11 +823,13 @@ int prepare_operands(ersj_index *h, hipStream_t s)
     HIPC(hipMemcpyAsync(dnrs, nrs.data(), sizeof(float) * nrs.size(), hipMemcpyHostToDevice, s), "copy");
     TRY(dalloc(h, &h->p16, (size_t)ns * 4 * (size_t)h->n, "prepared operands"));
     TRY(dalloc(h, &h->n16, (size_t)h->n, "prepared operands"));
-    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->p16, h->n16, s), "operand preparation");
+    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->n16, s),
+         "operand preparation");
     if (h->semi) {
         TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->nq, "prepared operands"));
         TRY(dalloc(h, &h->n16q, (size_t)h->nq, "prepared operands"));
-        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->p16q, h->n16q, s), "operand preparation");
+        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->g16_hh, h->p16q, h->n16q, s),
+             "operand preparation");
     } else {
         h->p16q = h->p16;
         h->n16q = h->n16;
@@ -1131,7 +1147,7 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         HIPC(launch_fill_u64((uint64_t *)fb.counters, 0, (int64_t)ncount, s), "clear counters");
         HIPC(launch_fill_u32(fb.rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
-        HIPC(h->use_g16   ? launch_refine_g16(a, s)
+        HIPC(h->use_g16   ? launch_refine_g16(a, h->g16_hh, s)
              : h->use_m16 ? launch_refine_m16(a, s)
              : mfma       ? launch_refine_mfma(a, f16, s)
                           : launch_refine_direct(a, s),
@@ -1458,6 +1474,8 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
             return fail(ERSJ_ERR_INVALID_ARG, "block_prune must be -1, 0 or 1 (got %d)", o.block_prune);
         if (o.cell_order < 0 || o.cell_order > 2)
             return fail(ERSJ_ERR_INVALID_ARG, "cell_order must be 0, 1 or 2 (got %d)", o.cell_order);
+        if (o.mfma_products != 0 && o.mfma_products != 1 && o.mfma_products != 3)
+            return fail(ERSJ_ERR_INVALID_ARG, "mfma_products must be 0, 1 or 3 (got %d)", o.mfma_products);
     }
     int dev = 0;
     HIPC(hipGetDevice(&dev), "hipGetDevice");
@@ -1732,6 +1750,7 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     o->refined_candidates = h->refined_cand;
     o->last_skipped = h->last_skip;
     o->skipped_candidates = h->skipped_cand;
+    o->mfma_products = h->kernel_used != ERSJ_REFINE_MFMA16 ? 0 : h->g16_hh ? 1 : 3;
     return ERSJ_OK;
 }
 

@@ -384,12 +384,19 @@ hipError_t prepare_refine_m16(int nb);
 hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 
 // k_refine_g16.hip: split-fp16 refinement for nb > 16 on operands prepared by
-// launch_prep16 (rows of xs centred by -nrs / s, scaled by s, split; P needs
-// ceil(nb / 4) * 4 * n uint4, N n floats); nsub = 1, seg_len a multiple of 512
-hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, uint4 *P, float *N,
-                         hipStream_t st);
-hipError_t prepare_refine_g16();
-hipError_t launch_refine_g16(const RefineArgs &a, hipStream_t s);
+// launch_prep16 (rows of xs centred by -nrs / s, scaled by s, split; N n
+// floats; P needs g16_stages(nb, hh) * 4 * n uint4); nsub = 1, seg_len a
+// multiple of 512.  hh: high halves only (one product per slab, the wider
+// band of the high-part form), for both calls alike.
+inline int g16_stages(int nb, bool hh)
+{
+    const int ns = (nb + 3) / 4;
+    return hh ? (ns + 1) / 2 : ns;
+}
+hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
+                         float *N, hipStream_t st);
+hipError_t prepare_refine_g16(bool hh);
+hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
 // Band-list bookkeeping after a refinement launch: out[0] = entries kept

@@ -28,6 +28,17 @@
 // run: one barrier per slab.  After the last slab the accumulators are
 // classified (classify_block, same band and thresholds as k_refine_mfma) and
 // mask words leave every 512 candidates as aligned 64-byte row pieces.
+//
+// High parts only (HH): the dot product is the sum of the high-half
+// products alone, one MFMA per slab instead of three.  Dropping h.l + l.h +
+// l.l changes s^2 q'.x' by at most 2^-10 (1 + 2^-12) sum |v_q v_x| plus
+// 2^-25 (|v_q| + |v_x|) (1 + 2^-11) + 2^-50 per dimension (|v - h| <=
+// 2^-11 |v| + 2^-25), so the band grows by 2^-10 (1 + 2^-12) (Nq + Nx) and
+// more pairs go to the binary64 re-check; the absolute part stays within
+// the split form's absolute widening.  The prepared operands then hold the
+// high halves only, two slabs in place of one slab's four parts, so a stage
+// covers 32 dimensions with the same loads and LDS traffic as a 16-dimension
+// stage of the three-product form, and runs 16 MFMAs per wave instead of 24.
 #include "refine_mfma_common.h"
 
 namespace ersj {
@@ -55,10 +66,11 @@ struct G16 {
 
 // Operands of one point set: centred, scaled, split, in slab-major parts
 // (part 0: high halves of a slab's dimensions 0-7, 1: high 8-15, 2 and 3:
-// the low halves), and the norms.
+// the low halves), and the norms.  High parts only (hh): parts 0 and 1 of
+// each slab, an odd slab count padded with one zero slab.
 __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, uint64_t n, int nb, int ns,
-                                                const float4 *__restrict__ nrs, float s, uint4 *__restrict__ P,
-                                                float *__restrict__ N)
+                                                const float4 *__restrict__ nrs, float s, bool hh,
+                                                uint4 *__restrict__ P, float *__restrict__ N)
 {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -91,14 +103,26 @@ __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, u
                 }
             }
         }
-        P[((uint64_t)sl * 4 + 0) * n + i] = *(const uint4 *)&h0;
-        P[((uint64_t)sl * 4 + 1) * n + i] = *(const uint4 *)&h1;
-        P[((uint64_t)sl * 4 + 2) * n + i] = *(const uint4 *)&l0;
-        P[((uint64_t)sl * 4 + 3) * n + i] = *(const uint4 *)&l1;
+        if (hh) {
+            P[((uint64_t)sl * 2 + 0) * n + i] = *(const uint4 *)&h0;
+            P[((uint64_t)sl * 2 + 1) * n + i] = *(const uint4 *)&h1;
+        } else {
+            P[((uint64_t)sl * 4 + 0) * n + i] = *(const uint4 *)&h0;
+            P[((uint64_t)sl * 4 + 1) * n + i] = *(const uint4 *)&h1;
+            P[((uint64_t)sl * 4 + 2) * n + i] = *(const uint4 *)&l0;
+            P[((uint64_t)sl * 4 + 3) * n + i] = *(const uint4 *)&l1;
+        }
+    }
+    if (hh && (ns & 1)) {
+        P[((uint64_t)ns * 2 + 0) * n + i] = make_uint4(0u, 0u, 0u, 0u);
+        P[((uint64_t)ns * 2 + 1) * n + i] = make_uint4(0u, 0u, 0u, 0u);
     }
     N[i] = nrm;
 }
 
+// HH: a stage's four parts are the high halves of two slabs (parts 0, 1 of
+// slab 2j and of slab 2j + 1); otherwise the four parts of one slab.
+template <bool HH>
 __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
 {
     using G = G16;
@@ -116,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     const uint32_t c_end = min(U, c_begin + a.seg_len);
     const uint32_t nrows = min((uint32_t)kRowsG, tl.nrows);
     const uint32_t row0 = tl.row0;
-    const int ns = (a.nb + 3) / 4;
+    const int ns = HH ? ((a.nb + 3) / 4 + 1) / 2 : (a.nb + 3) / 4;  // stages per step
 
     extern __shared__ __align__(16) unsigned char smemg[];
     uint4 *const LA = (uint4 *)(smemg + G::A);
@@ -234,6 +258,18 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             for (int tt = 0; tt < 4; ++tt)
                 acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], fresh ? z : acc[i][tt], 0, 0, 0);
         }
+        if (HH) {
+            // second slab of the stage: its high halves sit where the
+            // three-product form keeps the low ones
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (!(i == 0 ? do0 : do1)) continue;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bl[tt], acc[i][tt], 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (!(i == 0 ? do0 : do1)) continue;
@@ -326,24 +362,24 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
 
 }  // namespace
 
-hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, uint4 *P, float *N,
-                         hipStream_t st)
+hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
+                         float *N, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
     const int ns = (nb + 3) / 4;
     const uint64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, P, N);
+    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, hh, P, N);
     return hipGetLastError();
 }
 
-hipError_t prepare_refine_g16()
+hipError_t prepare_refine_g16(bool hh)
 {
-    return hipFuncSetAttribute((const void *)k_refine_g16, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)G16::BYTES);
+    return hipFuncSetAttribute(hh ? (const void *)k_refine_g16<true> : (const void *)k_refine_g16<false>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)G16::BYTES);
 }
 
-hipError_t launch_refine_g16(const RefineArgs &a, hipStream_t s)
+hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s)
 {
     if (a.seg_len % kGroupCands != 0 || a.seg_len / kStepG > (uint32_t)kMaxStepsG) return hipErrorInvalidValue;
     if (!a.p16 || !a.p16q || !a.n16 || !a.n16q) return hipErrorInvalidValue;
@@ -352,7 +388,8 @@ hipError_t launch_refine_g16(const RefineArgs &a, hipStream_t s)
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     RefineArgs args = a;
     void *params[] = {&args};
-    return hipLaunchKernel((const void *)k_refine_g16, dim3((unsigned)blocks), dim3(256), params, G16::BYTES, s);
+    return hipLaunchKernel(hh ? (const void *)k_refine_g16<true> : (const void *)k_refine_g16<false>,
+                           dim3((unsigned)blocks), dim3(256), params, G16::BYTES, s);
 }
 
 }  // namespace ersj

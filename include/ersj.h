@@ -99,6 +99,11 @@ typedef struct ersj_options {
                                    0 = 2 where an MFMA kernel with the box test refines (the fp32
                                    form, or the split form up to 64 dimensions), else 1.  Same
                                    result. */
+    int32_t mfma_products;      /* split-fp16 form above 64 dimensions: 3 = the three products
+                                   hi.hi + hi.lo + lo.hi of each 16-dimension slab; 1 = hi.hi alone,
+                                   a third of the matrix work and half the operand traffic, with a
+                                   band about 4.5 times as wide (more pairs re-checked in binary64);
+                                   0 = 1.  Same result. */
 } ersj_options;
 
 typedef struct ersj_stats {
@@ -126,6 +131,7 @@ typedef struct ersj_stats {
     int64_t n_queries;           /* query rows: n for the self-join, nq after ersj_set_queries */
     uint64_t last_skipped;       /* comparisons of the last fill_pass decided by the block box test */
     uint64_t skipped_candidates; /* the same, over the launches timed in refine_ms */
+    int32_t mfma_products;       /* products per slab of the split-fp16 form (1 or 3; 0: other forms) */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */

@@ -64,6 +64,10 @@ def test_build_rejects_bad_options():
         o = ersj.default_options(cell_order=order)
         assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
         assert "cell_order" in ersj.lib().ersj_last_error().decode()
+    for products in (-1, 2, 4):
+        o = ersj.default_options(mfma_products=products)
+        assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
+        assert "mfma_products" in ersj.lib().ersj_last_error().decode()
 
 
 def test_null_handle_paths():

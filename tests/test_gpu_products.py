@@ -1,0 +1,101 @@
+"""The split-fp16 form above 64 dimensions with one or three products per slab.
+
+The high-parts-only form (mfma_products = 1, the default there) sums the
+high-half products alone and widens its band by the dropped terms' bound;
+the three-product form (3) keeps hi.lo and lo.hi.  Both must return exactly
+the oracle's pair set (RT-HiSS Sec. II-A), for the self-join and the
+semi-join, on an odd slab count (a zero-padded slab), ragged sizes and the
+d = 384 workload's shape; the wider band sends at least as many pairs to the
+binary64 re-check."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_range_similarity_amd as ersj
+import oracle
+from workloads import make_config, make_queries
+
+from gpu_util import assert_same_pairs, keys_of, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ersj.lib()
+
+
+def _join_stats(X, eps, products):
+    opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products)
+    h = ersj.build_index(torch.from_numpy(X).cuda(), eps, opts)
+    ersj.count_pass(h)
+    nb = ersj.plan_batches(h, 0)
+    parts = list(ersj.iter_batches(h, nb))
+    st = ersj.get_stats(h)
+    h.free()
+    return ersj.pairs_to_numpy(parts), st
+
+
+@pytest.mark.parametrize("name,n,d", [("c5", 6000, None), ("rand", 3001, 129), ("rand", 700, 68),
+                                      ("rand", 1500, 200)])
+def test_both_forms_match_the_oracle(name, n, d):
+    if name == "rand":
+        rng = np.random.default_rng(n + d)
+        X = rng.random((n, d), dtype=np.float32)
+        eps = 0.33 * math.sqrt(d / 6.0)
+    else:
+        X = make_config(name, n)
+        eps, _, _ = oracle.calibrate_eps(X, min(1000, n), 50)
+    want = oracle.selfjoin_pairs(X, eps)
+    band = {}
+    for products in (1, 3):
+        say(f"[gpu] products={products} {name} n={n} d={X.shape[1]} eps={eps!r}")
+        got, st = _join_stats(X, eps, products)
+        assert st["mfma_products"] == products
+        assert_same_pairs(X, eps, got, want, f"{name} products={products}")
+        band[products] = st["last_boundary_pairs"]
+    say(f"[gpu] {name}: band pairs {band}")
+    assert band[1] >= band[3]
+
+
+def test_default_is_high_parts_above_64_dimensions():
+    rng = np.random.default_rng(5)
+    for d, expect in ((64, 3), (65, 1), (384, 1)):
+        X = rng.random((300, d), dtype=np.float32)
+        h = ersj.build_index(torch.from_numpy(X).cuda(), 0.5,
+                             ersj.default_options(refine_kernel=ersj.REFINE_MFMA16))
+        st = ersj.get_stats(h)
+        h.free()
+        assert st["mfma_products"] == expect, (d, st["mfma_products"])
+
+
+@pytest.mark.parametrize("products", [1, 3])
+@pytest.mark.parametrize("nq,n,d", [(600, 900, 100), (257, 1300, 133)])
+def test_semi_join_both_forms(nq, n, d, products):
+    rng = np.random.default_rng(nq + n + d)
+    X = rng.random((n, d), dtype=np.float32)
+    Q = np.concatenate([rng.random((nq - 40, d), dtype=np.float32),
+                        X[:40] + np.float32(0.01)])
+    eps = 0.33 * math.sqrt(d / 6.0)
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products)
+    parts = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts)
+    got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+    say(f"[gpu] semi-join products={products} nq={nq} n={n} d={d}: {got.size} pairs")
+    assert np.array_equal(got, want)
+
+
+def test_c5_shape_semijoin_queries_from_the_same_centres():
+    X = make_config("c5", 5000)
+    Q = make_queries("c5", 1500, 9, 5000)
+    eps, _, _ = oracle.calibrate_eps(X, 1000, 50)
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    for products in (1, 3):
+        opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products)
+        parts = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts)
+        got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+        assert np.array_equal(got, want), products
