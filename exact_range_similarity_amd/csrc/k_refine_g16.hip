@@ -204,37 +204,49 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         }
         return LSTART[g] - LPREF[g] + p;
     };
-    uint4 ra0, ra1, rb[4];
+    // the next stage's operands in flight (named registers: an array here
+    // ends up in scratch memory)
+    uint4 ra0, ra1, rb0, rb1, rb2, rb3;
     uint32_t ci = idx0;
     float cn = 0.f;
-    auto issue = [&](uint32_t u) __attribute__((always_inline)) {
-        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
+    auto issue = [&](uint32_t st, uint32_t sl) __attribute__((always_inline)) {
         if (sl == 0) {
             ci = cand_index(st);
             cn = NP[ci];
         }
         ra0 = PQ[((uint64_t)sl * 4 + wave) * nqr + qa];
         ra1 = PQ[((uint64_t)sl * 4 + wave) * nqr + qb2];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) rb[p] = P[((uint64_t)sl * 4 + p) * n + ci];
+        const uint4 *pc = P + (uint64_t)sl * 4 * n + ci;
+        rb0 = pc[0];
+        rb1 = pc[n];
+        rb2 = pc[2 * n];
+        rb3 = pc[3 * n];
     };
-    auto deposit = [&](uint32_t u) __attribute__((always_inline)) {
+    auto deposit = [&](uint32_t u, uint32_t st, uint32_t sl) __attribute__((always_inline)) {
         const int buf = (int)(u & 1);
-        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
         uint4 *la = LA + (size_t)buf * 4 * kRowsG;
         uint4 *lb = LB + (size_t)buf * 4 * kStepG;
         la[wave * kRowsG + lane] = ra0;
         la[wave * kRowsG + 64 + lane] = ra1;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) lb[p * kStepG + wave * 64 + lane] = rb[p];
+        lb[0 * kStepG + wave * 64 + lane] = rb0;
+        lb[1 * kStepG + wave * 64 + lane] = rb1;
+        lb[2 * kStepG + wave * 64 + lane] = rb2;
+        lb[3 * kStepG + wave * 64 + lane] = rb3;
         if (sl == 0) {
             LXI[(st & 1) * kStepG + wave * 64 + lane] = ci;
             LNX[(st & 1) * kStepG + wave * 64 + lane] = cn;
         }
     };
 
+    // accumulators start at zero and are cleared after each step's
+    // classification (a select per stage would cost a vector instruction per
+    // accumulator register)
     floatx16 acc[2][4];
-    auto mma = [&](int buf, bool fresh) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
+    auto mma = [&](int buf) __attribute__((always_inline)) {
         const uint4 *la = LA + (size_t)buf * 4 * kRowsG;
         const uint4 *lb = LB + (size_t)buf * 4 * kStepG;
         half8 ah[2], al[2], bh[4], bl[4];
@@ -250,13 +262,12 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             bh[tt] = *(const half8 *)&lb[hi * kStepG + c];
             bl[tt] = *(const half8 *)&lb[(2 + hi) * kStepG + c];
         }
-        const floatx16 z = {};
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (!(i == 0 ? do0 : do1)) continue;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
-                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], fresh ? z : acc[i][tt], 0, 0, 0);
+                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], acc[i][tt], 0, 0, 0);
         }
         if (HH) {
             // second slab of the stage: its high halves sit where the
@@ -336,24 +347,35 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     };
 
     if (units > 0) {
-        issue(0);
-        deposit(0);
+        issue(0, 0);
+        deposit(0, 0, 0);
     }
     __syncthreads();
+    // stage u = (step st, stage sl of the step); (nst, nsl) is stage u + 1
+    uint32_t st = 0, sl = 0;
     for (uint32_t u = 0; u < units; ++u) {
-        const uint32_t st = u / (uint32_t)ns, sl = u - st * (uint32_t)ns;
+        const bool last_sl = sl + 1 == (uint32_t)ns;
+        const uint32_t nst = last_sl ? st + 1 : st, nsl = last_sl ? 0 : sl + 1;
         const bool more = u + 1 < units;
-        if (more) issue(u + 1);
+        if (more) issue(nst, nsl);
         if (do0 || do1) {
-            mma((int)(u & 1), sl == 0);
-            if (sl + 1 == (uint32_t)ns) classify(st);
+            mma((int)(u & 1));
+            if (sl + 1 == (uint32_t)ns) {
+                classify(st);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
+            }
         }
-        if (more) deposit(u + 1);
+        if (more) deposit(u + 1, nst, nsl);
         __syncthreads();
         if (sl + 1 == (uint32_t)ns && (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps)) {
             flush(st / kGroupStepsG);
             wsel ^= 1;
         }
+        st = nst;
+        sl = nsl;
     }
     __syncthreads();
     for (int i = tid; i < (int)nrows; i += 256)
