@@ -75,6 +75,8 @@ def main():
     ap.add_argument("--no-block-prune", action="store_true",
                     help="switch off the MFMA kernel's query-block/candidate-group box test")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
+    ap.add_argument("--cell-order", type=int, default=0, choices=(0, 1, 2),
+                    help="order of the rows within a cell (0 = the library's choice)")
     ap.add_argument("--mfma-products", type=int, default=0, choices=(0, 1, 3),
                     help="split-fp16 form above 64 dimensions: products per slab (0 = the library's choice)")
     ap.add_argument("--no-host", action="store_true",
@@ -129,7 +131,7 @@ def main():
         opts = ersj.default_options(timing=int(timing), refine_kernel=args.refine,
                                     grid_reach=args.grid_reach,
                                     block_prune=-1 if args.no_block_prune else 0,
-                                mfma_products=args.mfma_products)
+                                mfma_products=args.mfma_products, cell_order=args.cell_order)
         h = ersj.build_index(xt, eps, opts, stream)
         if semi:
             ersj.set_queries(h, qt, stream)
@@ -177,12 +179,16 @@ def main():
     # 3d for the direct form (difference, square, sum per dimension); the
     # split-fp16 form executes one or three fp16 products per dimension but is
     # priced, like the others, by the work the distance needs
+    # comparisons the d > 64 kernel settled from its first 64 dimensions
+    # (the squared distance over them already exceeds the band) are priced
+    # at 2 * 64 + 3 flops, the work that decided them
+    partial = sum(s["partial_candidates"] for s in stats)
     per_cand = (2.0 * d + 3.0) if mfma else 3.0 * d
-    flops_per_launch = per_cand * evaluated / max(1, launches)
+    flops_per_launch = (per_cand * (evaluated - partial) + (2.0 * 64 + 3.0) * partial) / max(1, launches)
     achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
     # against the peak of the dtype the contraction runs in
     peak = FP16_PEAK_TFLOPS if f16 else FP32_PEAK_TFLOPS
-    fp32_equiv = (2.0 * d + 3.0) * evaluated / max(1, launches) / (avg_launch_ms * 1e-3) / 1e12
+    fp32_equiv = achieved
     # algorithmic HBM bytes of a launch: its result mask written once, and
     # the candidate and query rows read once (dimension-blocked, d padded to
     # a multiple of four)
@@ -244,6 +250,7 @@ def main():
         "candidates_per_s": cand / wall,
         "candidate_fraction_of_n2": cand / float(X.shape[0]) ** 2,
         "evaluated_fraction": evaluated / max(1, refined),
+        "partial_fraction": partial / max(1, evaluated),
         "cells": st["cells"],
         "grid": st["grid"],
         "boundary_pairs": st["last_boundary_pairs"],
@@ -366,7 +373,7 @@ def sample_mismatches(args, ersj, xt, qt, eps, budget, stream, nrows, colptr, co
     import torch
     opts = ersj.default_options(refine_kernel=args.refine, grid_reach=args.grid_reach,
                                 block_prune=-1 if args.no_block_prune else 0,
-                                mfma_products=args.mfma_products)
+                                mfma_products=args.mfma_products, cell_order=args.cell_order)
     h = ersj.build_index(xt, eps, opts, stream)
     if qt is not None:
         ersj.set_queries(h, qt, stream)
@@ -400,7 +407,7 @@ def run_knn(args, spec, rec, eps, X, xt, stream):
     eps0 = eps * args.eps0_scale
     opts = ersj.default_options(timing=1, refine_kernel=args.refine, grid_reach=args.grid_reach,
                                 block_prune=-1 if args.no_block_prune else 0,
-                                mfma_products=args.mfma_products)
+                                mfma_products=args.mfma_products, cell_order=args.cell_order)
     ids = None
     for w in range(args.warmup):
         ids, _, info = ersj.knn(xt, k, eps0, growth=args.growth, options=opts, stream=stream)

@@ -125,10 +125,10 @@ struct ersj_index {
     int32_t ready_batch = -1;
     uint64_t ready_pairs = 0;
     // stats
-    uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0, last_skip = 0;
+    uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0, last_skip = 0, last_part = 0;
     double ms_build = 0, ms_count = 0, ms_plan = 0, ms_refine = 0, ms_recheck = 0, ms_expand = 0;
     int64_t refine_launches = 0;
-    uint64_t refined_cand = 0, skipped_cand = 0;
+    uint64_t refined_cand = 0, skipped_cand = 0, partial_cand = 0;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t kernel_used = ERSJ_REFINE_DIRECT;
     bool box_order = false;  // rows of a cell in Morton order over its 8-dimension box
@@ -139,6 +139,7 @@ struct ersj_index {
     float4 *tref = nullptr;  // per row tile: reference point of the MFMA kernels' centring
     uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
     float *n16 = nullptr, *n16q = nullptr;
+    float *np16 = nullptr, *np16q = nullptr;  // their norms over the first kPartialDims dimensions
     // host delivery: two device staging buffers, alternated by batch, drained
     // into the caller's host memory on a copy stream of its own
     hipStream_t copy_stream = nullptr;
@@ -529,6 +530,9 @@ void release_prepared(ersj_index *h)
 {
     if (h->p16q != h->p16) dfree(h, h->p16q);
     if (h->n16q != h->n16) dfree(h, h->n16q);
+    if (h->np16q != h->np16) dfree(h, h->np16q);
+    h->np16q = nullptr;
+    dfree(h, h->np16);
     h->p16q = nullptr;
     h->n16q = nullptr;
     dfree(h, h->p16);
@@ -739,17 +743,17 @@ int do_build(ersj_index *h, const float *x, int64_t ld, hipStream_t s)
     // own box in the first 8 dimensions (ordered after the cells are known,
     // so the cell key carries no sub-cell bits), or over 8 x 8 x 8 sub-cells
     // on the grid axes (fewer when the grid is near its 2^21 cap)
-    // automatic: the box order where an MFMA kernel with the box test will
-    // refine (it covers those 8 dimensions with 32-row and 64-candidate
-    // groups): the fp32 form, or the split form up to 64 dimensions; the
+    // automatic: the box order wherever an MFMA kernel will refine: the
+    // fp32 form and the split form up to 64 dimensions cover those 8
+    // dimensions with 32-row and 64-candidate groups in their box test, and
+    // above 64 dimensions the split form's partial test settles more 32 x 32
+    // blocks when a block's rows lie close in the leading dimensions; the
     // direct kernel's 256-candidate groups stay compact on the grid axes only
-    // under the sub-cell order, and the split form above 64 dimensions has no
-    // box test
+    // under the sub-cell order
     const char *why_not = "";
     const int rk = h->opt.refine_kernel;
     h->box_order = h->opt.cell_order == 2 ||
-                   (h->opt.cell_order == 0 && coords_feasible(h, &why_not) &&
-                    (rk == ERSJ_REFINE_MFMA || (rk != ERSJ_REFINE_DIRECT && h->nb <= 16)));
+                   (h->opt.cell_order == 0 && coords_feasible(h, &why_not) && rk != ERSJ_REFINE_DIRECT);
     gp.sub = h->box_order ? 0 : std::min(3, 21 - bits);
     h->gp = gp;
 
@@ -823,16 +827,19 @@ int prepare_operands(ersj_index *h, hipStream_t s)
     HIPC(hipMemcpyAsync(dnrs, nrs.data(), sizeof(float) * nrs.size(), hipMemcpyHostToDevice, s), "copy");
     TRY(dalloc(h, &h->p16, (size_t)ns * 4 * (size_t)h->n, "prepared operands"));
     TRY(dalloc(h, &h->n16, (size_t)h->n, "prepared operands"));
-    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->n16, s),
+    TRY(dalloc(h, &h->np16, (size_t)h->n, "prepared operands"));
+    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->n16, h->np16, s),
          "operand preparation");
     if (h->semi) {
         TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->nq, "prepared operands"));
         TRY(dalloc(h, &h->n16q, (size_t)h->nq, "prepared operands"));
-        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->g16_hh, h->p16q, h->n16q, s),
+        TRY(dalloc(h, &h->np16q, (size_t)h->nq, "prepared operands"));
+        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->g16_hh, h->p16q, h->n16q, h->np16q, s),
              "operand preparation");
     } else {
         h->p16q = h->p16;
         h->n16q = h->n16;
+        h->np16q = h->np16;
     }
     TRY(sync(s, "operand preparation"));  // the host copy of nrs and dnrs must outlive the kernels
     return ERSJ_OK;
@@ -1034,7 +1041,7 @@ int ensure_fill_buffers(ersj_index *h)
         TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
         h->rows_cap = h->maxrows;
     }
-    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)(kBandLists + 2 * kHitSlots) * kBandStride, "counters"));
+    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)(kBandLists + 3 * kHitSlots) * kBandStride, "counters"));
     if (!h->lpref) TRY(dalloc(h, &h->lpref, (size_t)kBandLists + 3, "band list prefix"));
     if (!h->blist) {
         const uint64_t cap = initial_bcap(h);
@@ -1101,6 +1108,8 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     a.p16q = h->p16q;
     a.n16 = h->n16;
     a.n16q = h->n16q;
+    a.np16 = h->np16;
+    a.np16q = h->np16q;
     a.tref = h->tref;
     const uint64_t rows_items = (uint64_t)ntiles * a.nsub;
     uint32_t seg = 8192;
@@ -1125,12 +1134,14 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         a.tlo = h->tlo16;
         a.thi = h->thi16;
     }
-    // band sub-list counters, re-check hit slots, skipped-comparison slots
-    const size_t ncount = (size_t)(kBandLists + 2 * kHitSlots) * kBandStride;
+    // band sub-list counters, re-check hit slots, skipped-comparison slots,
+    // slots of comparisons decided from the first dimensions
+    const size_t ncount = (size_t)(kBandLists + 3 * kHitSlots) * kBandStride;
     unsigned long long *const hits = fb.counters + (size_t)kBandLists * kBandStride;
     unsigned long long *const skipped = hits + (size_t)kHitSlots * kBandStride;
     a.tbox = h->tbox;
     a.skipped = skipped;
+    a.partial = skipped + (size_t)kHitSlots * kBandStride;
     a.rowcnt = fb.rowcnt;
     a.row_base = h->hrows[b];
     a.cbox = h->cbox;
@@ -1193,20 +1204,24 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     timer_start(h, s);
     HIPC(scan_u32(fb.rowcnt, fb.roff, (int64_t)rows, fb.rscan, s), "row scan");
     uint64_t tot = 0;  // pairs
-    uint64_t hs[2 * kHitSlots * kBandStride];  // re-check hit slots, skipped-comparison slots
+    uint64_t hs[3 * kHitSlots * kBandStride];  // re-check hits, skipped comparisons, partial decisions
     HIPC(hipMemcpyAsync(&tot, fb.roff + rows, sizeof tot, hipMemcpyDeviceToHost, s), "copy");
     HIPC(hipMemcpyAsync(hs, hits, sizeof hs, hipMemcpyDeviceToHost, s), "copy");
     TRY(sync(s, "row count"));
     for (uint32_t k = 1; k < kHitSlots; ++k) hs[0] += hs[k * kBandStride];
     uint64_t skip = 0;
+    uint64_t part = 0;
     for (uint32_t k = 0; k < kHitSlots; ++k) skip += hs[(kHitSlots + k) * kBandStride];
+    for (uint32_t k = 0; k < kHitSlots; ++k) part += hs[(2 * kHitSlots + k) * kBandStride];
     hs[1] = skip;
     h->ms_expand += timer_stop(h, s);
     h->last_cand = h->hcands[b + 1] - h->hcands[b];
     h->last_bnd = bcount;
     h->last_in = hs[0];
     h->last_skip = hs[1];
+    h->last_part = part;
     if (h->opt.timing) h->skipped_cand += hs[1];
+    if (h->opt.timing) h->partial_cand += part;
     h->last_pairs = tot;
     *pairs = tot;
     return ERSJ_OK;
@@ -1262,7 +1277,7 @@ int noalloc_bufs(ersj_index *h, int32_t b, FillBufs *fb)
     const uint64_t o_rcnt = take(rows * 4);
     const uint64_t o_roff = take((rows + 1) * 8);
     const uint64_t o_scan = take(scan_tmp_entries((int64_t)rows + 1) * 8);
-    const uint64_t o_cnt = take((uint64_t)(kBandLists + 2 * kHitSlots) * kBandStride * 8);
+    const uint64_t o_cnt = take((uint64_t)(kBandLists + 3 * kHitSlots) * kBandStride * 8);
     const uint64_t o_lpref = take((uint64_t)(kBandLists + 3) * 8);
     const uint64_t min_band = (uint64_t)kBandLists * 64 * sizeof(Boundary);
     if (off + min_band > kNoallocScratchBytes)
@@ -1751,6 +1766,8 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     o->last_skipped = h->last_skip;
     o->skipped_candidates = h->skipped_cand;
     o->mfma_products = h->kernel_used != ERSJ_REFINE_MFMA16 ? 0 : h->g16_hh ? 1 : 3;
+    o->last_partial = h->last_part;
+    o->partial_candidates = h->partial_cand;
     return ERSJ_OK;
 }
 

@@ -319,9 +319,12 @@ struct RefineArgs {
     uint32_t *rowcnt;             // per query row of the batch: neighbours set in the mask (added)
     uint64_t row_base;            // first query row of the batch
     // split-fp16 operands prepared once per point (k_refine_g16): points and
-    // query rows, [slabs][4 parts][rows] x 16 bytes, and their norms
+    // query rows, [slabs][4 parts][rows] x 16 bytes, their norms and their
+    // norms over the first kPartialDims dimensions of the layout
     const uint4 *p16, *p16q;
     const float *n16, *n16q;
+    const float *np16, *np16q;
+    unsigned long long *partial;  // comparisons decided from those dimensions alone (kHitSlots slots)
     // MFMA kernels that centre per row tile: reference of tile t at
     // tref[t * nb .. t * nb + nb - 1] (the first query row of the tile when NULL)
     const float4 *tref;
@@ -388,13 +391,17 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 // floats; P needs g16_stages(nb, hh) * 4 * n uint4); nsub = 1, seg_len a
 // multiple of 512.  hh: high halves only (one product per slab, the wider
 // band of the high-part form), for both calls alike.
+// k_refine_g16 tests every 32 x 32 block after the first kPartialDims
+// dimensions: the squared distance over a subset of the dimensions bounds
+// the full one from below
+constexpr int kPartialDims = 64;
 inline int g16_stages(int nb, bool hh)
 {
     const int ns = (nb + 3) / 4;
     return hh ? (ns + 1) / 2 : ns;
 }
 hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
-                         float *N, hipStream_t st);
+                         float *N, float *NP, hipStream_t st);
 hipError_t prepare_refine_g16(bool hh);
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
 

@@ -39,6 +39,15 @@
 // high halves only, two slabs in place of one slab's four parts, so a stage
 // covers 32 dimensions with the same loads and LDS traffic as a 16-dimension
 // stage of the three-product form, and runs 16 MFMAs per wave instead of 24.
+//
+// Partial test: the squared distance over the first kPartialDims dimensions
+// of the layout bounds the full one from below.  After the stage that ends
+// with dimension kPartialDims - 1, every 32 x 32 block is tested with the
+// "out" rule of the classification, with the norms over those dimensions in
+// place of the full ones (the same band coefficient: the partial value has
+// fewer terms and fewer MFMA instructions behind it).  A block whose pairs
+// are all out keeps zero bits and runs no further MFMA; a step whose blocks
+// are all out loads and stages no further operand.
 #include "refine_mfma_common.h"
 
 namespace ersj {
@@ -60,7 +69,10 @@ struct G16 {
     static constexpr size_t RCNT = QOUT + (size_t)kRowsG * 4;             // [kRowsG] u32
     static constexpr size_t PREF = RCNT + (size_t)kRowsG * 4;             // [kMaxRanges + 1] u32
     static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;  // [kMaxRanges] u32
-    static constexpr size_t WORDS = (START + (size_t)kMaxRanges * 4 + 63) & ~(size_t)63;  // [2][kRowsG][8] u64
+    static constexpr size_t QOUTP = START + (size_t)kMaxRanges * 4;          // [kRowsG] f32
+    static constexpr size_t NXP = QOUTP + (size_t)kRowsG * 4;               // [2][kStepG] f32
+    static constexpr size_t ALIVE = NXP + (size_t)2 * kStepG * 4;           // [4] u32
+    static constexpr size_t WORDS = (ALIVE + 16 + 63) & ~(size_t)63;        // [2][kRowsG][8] u64
     static constexpr size_t BYTES = WORDS + (size_t)2 * kRowsG * 8 * 8;
 };
 
@@ -70,7 +82,8 @@ struct G16 {
 // each slab, an odd slab count padded with one zero slab.
 __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, uint64_t n, int nb, int ns,
                                                 const float4 *__restrict__ nrs, float s, bool hh,
-                                                uint4 *__restrict__ P, float *__restrict__ N)
+                                                uint4 *__restrict__ P, float *__restrict__ N,
+                                                float *__restrict__ NP)
 {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -103,6 +116,7 @@ __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, u
                 }
             }
         }
+        if (sl * 16 + 16 == kPartialDims) NP[i] = nrm;
         if (hh) {
             P[((uint64_t)sl * 2 + 0) * n + i] = *(const uint4 *)&h0;
             P[((uint64_t)sl * 2 + 1) * n + i] = *(const uint4 *)&h1;
@@ -141,6 +155,9 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     const uint32_t nrows = min((uint32_t)kRowsG, tl.nrows);
     const uint32_t row0 = tl.row0;
     const int ns = HH ? ((a.nb + 3) / 4 + 1) / 2 : (a.nb + 3) / 4;  // stages per step
+    // the stage that ends with dimension kPartialDims - 1 (nb > 16: a later
+    // stage always follows)
+    constexpr uint32_t chk = HH ? kPartialDims / 32 - 1 : kPartialDims / 16 - 1;
 
     extern __shared__ __align__(16) unsigned char smemg[];
     uint4 *const LA = (uint4 *)(smemg + G::A);
@@ -149,6 +166,9 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     float *const LNX = (float *)(smemg + G::NX);
     float *const LQIN = (float *)(smemg + G::QIN);
     float *const LQOUT = (float *)(smemg + G::QOUT);
+    float *const LQOUTP = (float *)(smemg + G::QOUTP);
+    float *const LNXP = (float *)(smemg + G::NXP);
+    uint32_t *const LALIVE = (uint32_t *)(smemg + G::ALIVE);
     uint32_t *const LRCNT = (uint32_t *)(smemg + G::RCNT);
     uint32_t *const LPREF = (uint32_t *)(smemg + G::PREF);
     uint32_t *const LSTART = (uint32_t *)(smemg + G::START);
@@ -170,6 +190,8 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         const float nq = valid ? a.n16q[row0 + tid] : 0.f;
         LQIN[tid] = valid ? a.tlo - a.kp * nq - a.tabs : -INFINITY;
         LQOUT[tid] = valid ? a.thi - a.km * nq + a.tabs : -INFINITY;
+        const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
+        LQOUTP[tid] = valid ? a.thi - a.km * nqp + a.tabs : -INFINITY;
         LRCNT[tid] = 0;
     }
     for (int e = tid; e < 2 * kRowsG * 8; e += 256) LWORDS[e] = 0ull;
@@ -208,11 +230,12 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     // ends up in scratch memory)
     uint4 ra0, ra1, rb0, rb1, rb2, rb3;
     uint32_t ci = idx0;
-    float cn = 0.f;
+    float cn = 0.f, cnp = 0.f;
     auto issue = [&](uint32_t st, uint32_t sl) __attribute__((always_inline)) {
         if (sl == 0) {
             ci = cand_index(st);
             cn = NP[ci];
+            cnp = a.np16[ci];
         }
         ra0 = PQ[((uint64_t)sl * 4 + wave) * nqr + qa];
         ra1 = PQ[((uint64_t)sl * 4 + wave) * nqr + qb2];
@@ -235,6 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         if (sl == 0) {
             LXI[(st & 1) * kStepG + wave * 64 + lane] = ci;
             LNX[(st & 1) * kStepG + wave * 64 + lane] = cn;
+            LNXP[(st & 1) * kStepG + wave * 64 + lane] = cnp;
         }
     };
 
@@ -246,6 +270,11 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
+    // blocks (bit 4 i + tt: rows rh 64 + 32 i, candidates cg 128 + 32 tt of
+    // the step) not yet settled by the partial test (wave-uniform)
+    uint32_t alive = 0xffu;
+    bool step_dead = false;  // every block of the workgroup settled (uniform)
+    unsigned long long npart = 0;  // comparisons settled by the partial test
     auto mma = [&](int buf) __attribute__((always_inline)) {
         const uint4 *la = LA + (size_t)buf * 4 * kRowsG;
         const uint4 *lb = LB + (size_t)buf * 4 * kStepG;
@@ -267,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             if (!(i == 0 ? do0 : do1)) continue;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
-                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], acc[i][tt], 0, 0, 0);
+                if ((alive >> (i * 4 + tt)) & 1u) acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[tt], acc[i][tt], 0, 0, 0);
         }
         if (HH) {
             // second slab of the stage: its high halves sit where the
@@ -277,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
                 if (!(i == 0 ? do0 : do1)) continue;
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
-                    acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bl[tt], acc[i][tt], 0, 0, 0);
+                    if ((alive >> (i * 4 + tt)) & 1u) acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bl[tt], acc[i][tt], 0, 0, 0);
             }
             return;
         }
@@ -286,15 +315,51 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             if (!(i == 0 ? do0 : do1)) continue;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
-                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bl[tt], acc[i][tt], 0, 0, 0);
+                if ((alive >> (i * 4 + tt)) & 1u) acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bl[tt], acc[i][tt], 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (!(i == 0 ? do0 : do1)) continue;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
-                acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bh[tt], acc[i][tt], 0, 0, 0);
+                if ((alive >> (i * 4 + tt)) & 1u) acc[i][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[i], bh[tt], acc[i][tt], 0, 0, 0);
         }
+    };
+
+    // partial test of the wave's live blocks; out-rule of classify_block
+    // with the norms over the first kPartialDims dimensions
+    auto partial_check = [&](uint32_t st) __attribute__((always_inline)) {
+        uint32_t nal = 0;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int cl = cg * 128 + tt * 32 + col;
+            const uint32_t c0 = c_begin + st * kStepG + cg * 128 + tt * 32;
+            const float xo = c0 + col < c_end ? a.km * LNXP[(st & 1) * kStepG + cl] : __builtin_nanf("");
+            const uint32_t ncol = c0 < c_end ? min(32u, c_end - c0) : 0u;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (!((alive >> (i * 4 + tt)) & 1u)) continue;
+                const int qb = rh * 2 + i;
+                const float4 *qo4 = (const float4 *)LQOUTP + qb * 8 + hi;
+                bool nout = false;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 qo = qo4[g * 2];
+                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 0], xo) <= qo.x;
+                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 1], xo) <= qo.y;
+                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 2], xo) <= qo.z;
+                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 3], xo) <= qo.w;
+                }
+                if (__ballot(nout) != 0) {
+                    nal |= 1u << (i * 4 + tt);
+                } else {
+                    const uint32_t r0 = (uint32_t)(rh * 64 + i * 32);
+                    const uint32_t nrow = r0 < nrows ? min(32u, nrows - r0) : 0u;
+                    npart += (unsigned long long)nrow * ncol;
+                }
+            }
+        }
+        alive = nal;
     };
 
     int wsel = 0;  // group buffer of the current 512-candidate group (toggles at each flush)
@@ -319,7 +384,9 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             for (int i = 0; i < 2; ++i) {
                 if (!(i == 0 ? do0 : do1)) continue;
                 const int qb = rh * 2 + i;
-                classify_block(&acc[i][w2 * 2], xin, xout, LQIN, LQOUT, qb, lane, cw, 3u, bsink,
+                const uint32_t live = (alive >> (i * 4 + w2 * 2)) & 3u;
+                if (live == 0) continue;
+                classify_block(&acc[i][w2 * 2], xin, xout, LQIN, LQOUT, qb, lane, cw, live, bsink,
                                [&](int t2) { return xid[t2]; }, wg + (qb * 32 + col) * 8 + wi);
             }
         }
@@ -356,27 +423,38 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     for (uint32_t u = 0; u < units; ++u) {
         const bool last_sl = sl + 1 == (uint32_t)ns;
         const uint32_t nst = last_sl ? st + 1 : st, nsl = last_sl ? 0 : sl + 1;
-        const bool more = u + 1 < units;
+        // a settled step's later stages are neither loaded nor staged
+        const bool more = u + 1 < units && !(step_dead && nst == st);
         if (more) issue(nst, nsl);
-        if (do0 || do1) {
-            mma((int)(u & 1));
-            if (sl + 1 == (uint32_t)ns) {
-                classify(st);
+        if ((do0 || do1) && alive != 0) mma((int)(u & 1));
+        if (sl == chk) {
+            if (do0 || do1) partial_check(st);
+            else alive = 0;
+            if (lane == 0) LALIVE[wave] = alive;
+        }
+        if (last_sl) {
+            if ((do0 || do1) && alive != 0) classify(st);
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
-            }
+                for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
         }
         if (more) deposit(u + 1, nst, nsl);
         __syncthreads();
-        if (sl + 1 == (uint32_t)ns && (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps)) {
+        if (sl == chk) step_dead = (LALIVE[0] | LALIVE[1] | LALIVE[2] | LALIVE[3]) == 0u;
+        if (last_sl) {
+            alive = 0xffu;
+            step_dead = false;
+        }
+        if (last_sl && (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps)) {
             flush(st / kGroupStepsG);
             wsel ^= 1;
         }
         st = nst;
         sl = nsl;
     }
+    if (lane == 0 && npart != 0)
+        atomicAdd(&a.partial[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], npart);
     __syncthreads();
     for (int i = tid; i < (int)nrows; i += 256)
         if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
@@ -385,13 +463,14 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
 }  // namespace
 
 hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
-                         float *N, hipStream_t st)
+                         float *N, float *NP, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
+    if (4 * nb <= kPartialDims) return hipErrorInvalidValue;
     const int ns = (nb + 3) / 4;
     const uint64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, hh, P, N);
+    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, hh, P, N, NP);
     return hipGetLastError();
 }
 

@@ -95,10 +95,9 @@ typedef struct ersj_options {
                                    sub-cells on the grid axes; 2 = the leaf order of a kd-tree over
                                    the cell's own box in the first 8 dimensions of the variance
                                    order, each of its 24 levels halving the widest remaining
-                                   extent, which lets the MFMA kernels' block box test prune more;
-                                   0 = 2 where an MFMA kernel with the box test refines (the fp32
-                                   form, or the split form up to 64 dimensions), else 1.  Same
-                                   result. */
+                                   extent, which lets the MFMA kernels' block box test (and above
+                                   64 dimensions the split form's partial test) settle more;
+                                   0 = 2 where an MFMA kernel refines, else 1.  Same result. */
     int32_t mfma_products;      /* split-fp16 form above 64 dimensions: 3 = the three products
                                    hi.hi + hi.lo + lo.hi of each 16-dimension slab; 1 = hi.hi alone,
                                    a third of the matrix work and half the operand traffic, with a
@@ -132,6 +131,9 @@ typedef struct ersj_stats {
     uint64_t last_skipped;       /* comparisons of the last fill_pass decided by the block box test */
     uint64_t skipped_candidates; /* the same, over the launches timed in refine_ms */
     int32_t mfma_products;       /* products per slab of the split-fp16 form (1 or 3; 0: other forms) */
+    uint64_t last_partial;       /* comparisons of the last fill_pass decided "out" from the first 64
+                                    dimensions alone (split form above 64 dimensions) */
+    uint64_t partial_candidates; /* the same, over the launches timed in refine_ms */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */

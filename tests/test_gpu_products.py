@@ -6,7 +6,10 @@ the three-product form (3) keeps hi.lo and lo.hi.  Both must return exactly
 the oracle's pair set (RT-HiSS Sec. II-A), for the self-join and the
 semi-join, on an odd slab count (a zero-padded slab), ragged sizes and the
 d = 384 workload's shape; the wider band sends at least as many pairs to the
-binary64 re-check."""
+binary64 re-check.  The partial test (a 32 x 32 block whose pairs are all
+farther than the band over the first 64 dimensions of the variance order is
+settled there) is checked with pairs whose difference lies in those 64
+dimensions alone, at the band's edges.""" 
 import math
 
 import numpy as np
@@ -58,6 +61,10 @@ def test_both_forms_match_the_oracle(name, n, d):
         assert st["mfma_products"] == products
         assert_same_pairs(X, eps, got, want, f"{name} products={products}")
         band[products] = st["last_boundary_pairs"]
+        say(f"[gpu] {name} products={products}: {st['last_partial']} comparisons settled from the first "
+            f"64 dimensions")
+        if name == "c5":  # clusters far apart: most blocks are settled early
+            assert st["last_partial"] > 0
     say(f"[gpu] {name}: band pairs {band}")
     assert band[1] >= band[3]
 
@@ -99,3 +106,33 @@ def test_c5_shape_semijoin_queries_from_the_same_centres():
         parts = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts)
         got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
         assert np.array_equal(got, want), products
+
+
+@pytest.mark.parametrize("products", [1, 3])
+def test_partial_test_with_differences_in_the_leading_dimensions(products):
+    # dimensions 0..63 spread widely (they lead the variance order), the rest
+    # nearly constant; each pair differs in dimensions 0..63 only, so its
+    # distance over them is its full distance, placed around eps^2 at
+    # relative offsets from 1e-6 to 1e-1 on both sides
+    rng = np.random.default_rng(77 + products)
+    d, eps = 100, 0.5
+    E = eps * eps
+    base = np.zeros((3000, d))
+    base[:, :64] = rng.random((3000, 64)) * 4.0
+    base[:, 64:] = rng.normal(0.0, 0.01, (3000, d - 64))
+    rows = [base]
+    for rel in (1e-6, 1e-5, 1e-4, 1e-3, 3e-3, 1e-2, 1e-1):
+        for sgn in (-1.0, 1.0):
+            for _ in range(6):
+                q = base[rng.integers(0, 3000)].copy()
+                v = np.zeros(d)
+                v[:64] = rng.normal(0.0, 1.0, 64)
+                v *= np.sqrt(E * (1.0 + sgn * rel)) / np.linalg.norm(v)
+                rows.append(np.stack([q, q + v]))
+    X = np.concatenate(rows).astype(np.float32)
+    want = oracle.selfjoin_pairs(X, eps)
+    got, st = _join_stats(X, eps, products)
+    say(f"[gpu] leading-dimension pairs products={products}: {len(got)} pairs, "
+        f"{st['last_partial']} comparisons settled from the first 64 dimensions")
+    assert st["last_partial"] > 0
+    assert_same_pairs(X, eps, got, want, f"leading-dimension pairs products={products}")
