@@ -117,6 +117,8 @@ struct ersj_index {
     uint64_t mask_cap = 0;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;
+    uint2 *dlist = nullptr;  // blocks the d > 64 kernel hands on (kBandLists sub-lists)
+    uint64_t dcap = 0;       // entries per sub-list
     unsigned long long *counters = nullptr;  // band sub-list counters, then re-check hits
     uint64_t *lpref = nullptr;               // [kBandLists + 1] prefix, [2] kept / max count
     uint32_t *rowcnt = nullptr;
@@ -1041,7 +1043,8 @@ int ensure_fill_buffers(ersj_index *h)
         TRY(dalloc(h, &h->rscan, scan_tmp_entries((int64_t)h->maxrows + 1), "row scan"));
         h->rows_cap = h->maxrows;
     }
-    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)(kBandLists + 3 * kHitSlots) * kBandStride, "counters"));
+    if (!h->counters) TRY(dalloc(h, &h->counters, (size_t)(2 * kBandLists + 3 * kHitSlots) * kBandStride, "counters"));
+
     if (!h->lpref) TRY(dalloc(h, &h->lpref, (size_t)kBandLists + 3, "band list prefix"));
     if (!h->blist) {
         const uint64_t cap = initial_bcap(h);
@@ -1059,6 +1062,8 @@ struct FillBufs {
     uint8_t *gflag = nullptr;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;                         // band-list entries over all sub-lists
+    uint2 *dlist = nullptr;                    // handed-on blocks (null: none)
+    uint64_t dcap = 0;                         // entries per sub-list
     unsigned long long *counters = nullptr;    // band sub-list counters, then re-check hit slots
     uint64_t *lpref = nullptr;
     uint32_t *rowcnt = nullptr;
@@ -1073,6 +1078,8 @@ FillBufs handle_bufs(ersj_index *h)
     fb.gflag = h->gflag;
     fb.blist = h->blist;
     fb.bcap = h->bcap;
+    fb.dlist = h->dlist;
+    fb.dcap = h->dcap;
     fb.counters = h->counters;
     fb.lpref = h->lpref;
     fb.rowcnt = h->rowcnt;
@@ -1118,6 +1125,22 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     while (rows_items * nseg_of(seg) > 0x7fffffffull) seg *= 2;
     a.seg_len = seg;
     a.nseg = std::max<uint32_t>(1, nseg_of(seg));
+    if (h->use_g16 && fb.grow && !h->opt.max_device_bytes) {
+        // hand-on list of the d > 64 kernel: kHandOn blocks per step, at most
+        // kStepsG16 steps per work item, the work items dealt to kBandLists
+        // sub-lists (8 bytes an entry; about 1.2% of the batch's mask)
+        const uint64_t items = (uint64_t)ntiles * a.nseg;
+        const uint64_t need = (uint64_t)kHandOn * kStepsG16 * ((items + kBandLists - 1) / kBandLists);
+        if (h->dcap < need) {
+            dfree(h, h->dlist);
+            h->dlist = nullptr;
+            h->dcap = 0;
+            if (dalloc(h, &h->dlist, (size_t)(need * kBandLists), "hand-on block list") == ERSJ_OK) h->dcap = need;
+            else h->dlist = nullptr;  // refine without it
+        }
+        fb.dlist = h->dlist;
+        fb.dcap = h->dcap;
+    }
     a.rstart = h->rstart;
     a.rpref = h->rpref;
     a.nrng = h->nrng;
@@ -1135,13 +1158,17 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         a.thi = h->thi16;
     }
     // band sub-list counters, re-check hit slots, skipped-comparison slots,
-    // slots of comparisons decided from the first dimensions
-    const size_t ncount = (size_t)(kBandLists + 3 * kHitSlots) * kBandStride;
+    // slots of comparisons decided from the first dimensions, handed-on block
+    // sub-list counters
+    const size_t ncount = (size_t)(2 * kBandLists + 3 * kHitSlots) * kBandStride;
     unsigned long long *const hits = fb.counters + (size_t)kBandLists * kBandStride;
     unsigned long long *const skipped = hits + (size_t)kHitSlots * kBandStride;
     a.tbox = h->tbox;
     a.skipped = skipped;
     a.partial = skipped + (size_t)kHitSlots * kBandStride;
+    a.dcount = a.partial + (size_t)kHitSlots * kBandStride;
+    a.dlist = fb.dlist;
+    a.dcap = fb.dlist ? fb.dcap : 0;
     a.rowcnt = fb.rowcnt;
     a.row_base = h->hrows[b];
     a.cbox = h->cbox;
@@ -1163,6 +1190,7 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
              : mfma       ? launch_refine_mfma(a, f16, s)
                           : launch_refine_direct(a, s),
              "refine kernel");
+        if (h->use_g16) HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
         h->ms_refine += timer_stop(h, s);
         if (h->opt.timing) {
             h->refine_launches += 1;
@@ -1170,7 +1198,17 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         }
         HIPC(launch_band_prefix(fb.counters, lcap, fb.lpref, fb.lpref + kBandLists + 1, s), "band prefix");
         HIPC(hipMemcpyAsync(bres, fb.lpref + kBandLists + 1, sizeof bres, hipMemcpyDeviceToHost, s), "copy");
+        std::vector<unsigned long long> dc;
+        if (a.dlist) {
+            dc.resize((size_t)kBandLists * kBandStride);
+            HIPC(hipMemcpyAsync(dc.data(), a.dcount, dc.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost, s),
+                 "copy");
+        }
         TRY(sync(s, "refine"));
+        for (uint32_t k = 0; k < dc.size() / kBandStride; ++k)
+            if (dc[(size_t)k * kBandStride] > a.dcap)
+                return fail(ERSJ_ERR_INTERNAL, "hand-on sub-list %u holds %llu blocks, more than its %llu", k,
+                            (unsigned long long)dc[(size_t)k * kBandStride], (unsigned long long)a.dcap);
         bcount = bres[0];
         if (bres[1] <= lcap) break;
         // A band sub-list overflowed: grow them all and refine the batch
@@ -1277,7 +1315,7 @@ int noalloc_bufs(ersj_index *h, int32_t b, FillBufs *fb)
     const uint64_t o_rcnt = take(rows * 4);
     const uint64_t o_roff = take((rows + 1) * 8);
     const uint64_t o_scan = take(scan_tmp_entries((int64_t)rows + 1) * 8);
-    const uint64_t o_cnt = take((uint64_t)(kBandLists + 3 * kHitSlots) * kBandStride * 8);
+    const uint64_t o_cnt = take((uint64_t)(2 * kBandLists + 3 * kHitSlots) * kBandStride * 8);
     const uint64_t o_lpref = take((uint64_t)(kBandLists + 3) * 8);
     const uint64_t min_band = (uint64_t)kBandLists * 64 * sizeof(Boundary);
     if (off + min_band > kNoallocScratchBytes)

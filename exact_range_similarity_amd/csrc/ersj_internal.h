@@ -325,6 +325,14 @@ struct RefineArgs {
     const float *n16, *n16q;
     const float *np16, *np16q;
     unsigned long long *partial;  // comparisons decided from those dimensions alone (kHitSlots slots)
+    // k_refine_g16: 32 x 32 blocks still live after that test, handed to
+    // k_refine_g16_blocks: kBandLists sub-lists of dcap entries {tile,
+    // (candidate position / 32) << 2 | query block}, sub-list c counted at
+    // dcount[c * kBandStride] (may exceed dcap: entries past it were not
+    // written, their blocks were finished in place); null: none handed on
+    uint2 *dlist;
+    unsigned long long *dcount;
+    uint64_t dcap;
     // MFMA kernels that centre per row tile: reference of tile t at
     // tref[t * nb .. t * nb + nb - 1] (the first query row of the tile when NULL)
     const float4 *tref;
@@ -393,8 +401,12 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 // band of the high-part form), for both calls alike.
 // k_refine_g16 tests every 32 x 32 block after the first kPartialDims
 // dimensions: the squared distance over a subset of the dimensions bounds
-// the full one from below
+// the full one from below; a workgroup step with at most kHandOn blocks
+// still live hands them to k_refine_g16_blocks and ends there (a step has
+// at most kStepsG16 of them per work item)
 constexpr int kPartialDims = 64;
+constexpr uint32_t kHandOn = 6;
+constexpr uint32_t kStepsG16 = 32;
 inline int g16_stages(int nb, bool hh)
 {
     const int ns = (nb + 3) / 4;
@@ -404,6 +416,8 @@ hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs
                          float *N, float *NP, hipStream_t st);
 hipError_t prepare_refine_g16(bool hh);
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
+// the blocks k_refine_g16 handed on (a.dlist), after it, on the same stream
+hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----
 // Band-list bookkeeping after a refinement launch: out[0] = entries kept

@@ -46,8 +46,17 @@
 // "out" rule of the classification, with the norms over those dimensions in
 // place of the full ones (the same band coefficient: the partial value has
 // fewer terms and fewer MFMA instructions behind it).  A block whose pairs
-// are all out keeps zero bits and runs no further MFMA; a step whose blocks
-// are all out loads and stages no further operand.
+// are all out keeps zero bits and runs no further MFMA.  A step with at most
+// kHandOn blocks still live hands them to k_refine_g16_blocks (a list) and
+// ends at the test; the check stage loads the next step's first stage in
+// advance for that.  A step with more live blocks continues in place.
+//
+// k_refine_g16_blocks: one wave per handed-on 32 x 32 block, operand
+// fragments read straight from the prepared arrays (the slab layout is the
+// MFMA operand layout: lane l takes row or candidate l % 32, half l / 32 of a
+// slab), all slabs summed in one accumulator, classified like the tiles of
+// k_refine_g16; its bits are ORed into the mask words (which k_refine_g16
+// stored with that half-word zero), with the unit flags and row counts.
 #include "refine_mfma_common.h"
 
 namespace ersj {
@@ -203,7 +212,6 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     const int rh = wave & 1, cg = wave >> 1;
     const bool do0 = (uint32_t)(rh * 64) < nrows, do1 = (uint32_t)(rh * 64 + 32) < nrows;
     const uint32_t nsteps = (c_end - c_begin + kStepG - 1) / kStepG;  // <= kMaxStepsG
-    const uint32_t units = nsteps * (uint32_t)ns;
     const BandSink bsink{band_list(a.blist, a.lcap), band_counter(a.bcount), a.lcap, row0, mbase, W};
 
     // loader: lane l of wave w copies part w of query rows l and 64 + l, and
@@ -341,16 +349,17 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
                 if (!((alive >> (i * 4 + tt)) & 1u)) continue;
                 const int qb = rh * 2 + i;
                 const float4 *qo4 = (const float4 *)LQOUTP + qb * 8 + hi;
-                bool nout = false;
+                // one ballot per register, OR-ed as wave masks
+                uint64_t nout = 0;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const float4 qo = qo4[g * 2];
-                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 0], xo) <= qo.x;
-                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 1], xo) <= qo.y;
-                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 2], xo) <= qo.z;
-                    nout |= fmaf(-2.0f, acc[i][tt][4 * g + 3], xo) <= qo.w;
+                    nout |= __ballot(fmaf(-2.0f, acc[i][tt][4 * g + 0], xo) <= qo.x);
+                    nout |= __ballot(fmaf(-2.0f, acc[i][tt][4 * g + 1], xo) <= qo.y);
+                    nout |= __ballot(fmaf(-2.0f, acc[i][tt][4 * g + 2], xo) <= qo.z);
+                    nout |= __ballot(fmaf(-2.0f, acc[i][tt][4 * g + 3], xo) <= qo.w);
                 }
-                if (__ballot(nout) != 0) {
+                if (nout != 0) {
                     nal |= 1u << (i * 4 + tt);
                 } else {
                     const uint32_t r0 = (uint32_t)(rh * 64 + i * 32);
@@ -360,6 +369,29 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
             }
         }
         alive = nal;
+    };
+
+    // hand the wave's live blocks on.  A workgroup hands on at most
+    // kHandOn blocks a step and the host sizes each sub-list for all steps of
+    // the workgroups that use it; the host also checks the counts, so an
+    // entry past dcap (never expected) fails the batch instead of losing a
+    // block.
+    auto defer_blocks = [&](uint32_t st) __attribute__((always_inline)) {
+        const uint32_t cnt = __popc(alive);
+        unsigned long long base = 0;
+        if (lane == 0) base = atomicAdd(&a.dcount[(uint64_t)(blockIdx.x % kBandLists) * kBandStride], (unsigned long long)cnt);
+        base = __shfl(base, 0, 64);
+        uint2 *dl = a.dlist + (uint64_t)(blockIdx.x % kBandLists) * a.dcap;
+        uint32_t j = 0;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (!((alive >> b) & 1u)) continue;
+            const uint32_t c0 = c_begin + st * kStepG + cg * 128 + (b & 3) * 32;
+            const uint32_t rb = (uint32_t)(rh * 2 + (b >> 2));
+            if (lane == 0 && base + j < a.dcap) dl[base + j] = make_uint2(t, ((c0 >> 5) << 2) | rb);
+            ++j;
+        }
+        alive = 0;
     };
 
     int wsel = 0;  // group buffer of the current 512-candidate group (toggles at each flush)
@@ -413,51 +445,232 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         }
     };
 
-    if (units > 0) {
+    if (nsteps > 0) {
         issue(0, 0);
         deposit(0, 0, 0);
     }
     __syncthreads();
-    // stage u = (step st, stage sl of the step); (nst, nsl) is stage u + 1
-    uint32_t st = 0, sl = 0;
-    for (uint32_t u = 0; u < units; ++u) {
+    // Stage (st, sl), it-th in order (LDS buffer it & 1).  With the hand-on
+    // list, the check stage loads the next step's first stage instead of its
+    // own next one: most steps end there (a barrier tells every wave how many
+    // blocks are still live: none, or up to kHandOn handed on).  A step with
+    // more live blocks continues in place and loads its next stage late.
+    const bool handon = a.dlist != nullptr;
+    uint32_t st = 0, sl = 0, it = 0;
+    while (st < nsteps) {
         const bool last_sl = sl + 1 == (uint32_t)ns;
-        const uint32_t nst = last_sl ? st + 1 : st, nsl = last_sl ? 0 : sl + 1;
-        // a settled step's later stages are neither loaded nor staged
-        const bool more = u + 1 < units && !(step_dead && nst == st);
+        const bool at_chk = sl == chk;
+        const bool spec = at_chk && handon;
+        uint32_t nst = last_sl || spec ? st + 1 : st, nsl = last_sl || spec ? 0 : sl + 1;
+        // without the hand-on list a settled step's later stages are neither
+        // loaded nor staged
+        bool more = nst < nsteps && !(step_dead && nst == st);
+        uint32_t ci_keep = ci;
+        float cn_keep = cn, cnp_keep = cnp;
         if (more) issue(nst, nsl);
-        if ((do0 || do1) && alive != 0) mma((int)(u & 1));
-        if (sl == chk) {
+        if ((do0 || do1) && alive != 0) mma((int)(it & 1));
+        bool done = false;  // the step ends with this stage
+        if (at_chk) {
             if (do0 || do1) partial_check(st);
             else alive = 0;
             if (lane == 0) LALIVE[wave] = alive;
+            if (spec) {
+                __syncthreads();
+                // (LALIVE is written again only after this stage's barrier)
+                const uint32_t live = __popc(LALIVE[0]) + __popc(LALIVE[1]) + __popc(LALIVE[2]) + __popc(LALIVE[3]);
+                if (live <= kHandOn) {
+                    if (alive != 0) defer_blocks(st);
+                    done = true;
+                } else {
+                    // continue in place: this step's next stage after all
+                    ci = ci_keep;
+                    cn = cn_keep;
+                    cnp = cnp_keep;
+                    nst = st;
+                    nsl = sl + 1;
+                    more = true;
+                    issue(nst, nsl);
+                }
+            }
         }
-        if (last_sl) {
+        if (last_sl || done) {
             if ((do0 || do1) && alive != 0) classify(st);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) acc[i][tt] = floatx16{};
         }
-        if (more) deposit(u + 1, nst, nsl);
+        if (more) deposit(it + 1, nst, nsl);
         __syncthreads();
-        if (sl == chk) step_dead = (LALIVE[0] | LALIVE[1] | LALIVE[2] | LALIVE[3]) == 0u;
-        if (last_sl) {
+        if (at_chk && !handon) step_dead = (LALIVE[0] | LALIVE[1] | LALIVE[2] | LALIVE[3]) == 0u;
+        if (last_sl || done) {
             alive = 0xffu;
             step_dead = false;
+            if (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps) {
+                flush(st / kGroupStepsG);
+                wsel ^= 1;
+            }
         }
-        if (last_sl && (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps)) {
-            flush(st / kGroupStepsG);
-            wsel ^= 1;
+        if (!more && !(last_sl || done)) {
+            // a settled step without the hand-on list: its remaining stages
+            // have nothing to do
+            nst = st;
+            nsl = sl + 1;
         }
         st = nst;
         sl = nsl;
+        ++it;
     }
     if (lane == 0 && npart != 0)
         atomicAdd(&a.partial[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], npart);
     __syncthreads();
     for (int i = tid; i < (int)nrows; i += 256)
         if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
+}
+
+// One wave per handed-on block (see the file comment).  Grid: kBandLists x
+// kDeferGroups workgroups; workgroup g reads sub-list g % kBandLists.
+constexpr uint32_t kDeferGroups = 16;
+template <bool HH>
+__global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
+{
+    __shared__ __align__(16) float LQI[4][32];
+    __shared__ __align__(16) float LQO[4][32];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+    const uint32_t sub = blockIdx.x % kBandLists, j0 = blockIdx.x / kBandLists, nj = gridDim.x / kBandLists;
+    const unsigned long long cnt0 = a.dcount[(uint64_t)sub * kBandStride];
+    const uint64_t cnt = cnt0 < a.dcap ? cnt0 : a.dcap;
+    const uint2 *dl = a.dlist + (uint64_t)sub * a.dcap;
+    const uint64_t n = a.n, nqr = a.nqr;
+    const int nsl = HH ? 2 * (((a.nb + 3) / 4 + 1) / 2) : (a.nb + 3) / 4;  // slabs (high parts: padded even)
+    const int pp = HH ? 2 : 4;                                            // parts per slab
+    constexpr int kChunk = HH ? 6 : 3;  // slabs whose operands are loaded together
+    for (uint64_t e = (uint64_t)j0 * 4 + wave; e < cnt; e += (uint64_t)nj * 4) {
+        const uint2 ent = dl[e];
+        const uint32_t t = ent.x, rb = ent.y & 3u, c0 = (ent.y >> 2) << 5;
+        const Tile tl = a.tiles[t];
+        const uint32_t A = tl.cell, nr = a.nrng[A];
+        const uint32_t *pref = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+        const uint32_t U = pref[nr];
+        const uint32_t nrows = min((uint32_t)kTileRows, tl.nrows);
+        const uint32_t r = rb * 32 + (uint32_t)col;
+        const bool vr = r < nrows;
+        const uint32_t q = tl.row0 + (vr ? r : nrows - 1);
+        const uint32_t p = c0 + (uint32_t)col;
+        const bool vc = p < U;
+        // the lane's candidate: range g with pref[g] <= p < pref[g + 1]
+        uint32_t g = 0;
+        if (vc) {
+            uint32_t lo = 0, up = nr;  // pref[lo] <= p < pref[up]
+            while (up - lo > 1) {
+                const uint32_t mid = (lo + up) >> 1;
+                if (pref[mid] <= p) lo = mid;
+                else up = mid;
+            }
+            g = lo;
+        }
+        const uint32_t ci = a.rstart[(uint64_t)A * kMaxRanges + g] + (vc ? p - pref[g] : 0u);
+        if (lane < 32) {
+            const float nq = a.n16q[q];
+            LQI[wave][col] = vr ? a.tlo - a.kp * nq - a.tabs : -INFINITY;
+            LQO[wave][col] = vr ? a.thi - a.km * nq + a.tabs : -INFINITY;
+        }
+        const float nx = a.n16[ci];
+        floatx16 acc = {};
+        const uint4 *pq = a.p16q + (uint64_t)hi * nqr + q;
+        const uint4 *pc = a.p16 + (uint64_t)hi * n + ci;
+#pragma unroll 1
+        for (int s0 = 0; s0 < nsl; s0 += kChunk) {
+            const int m = nsl - s0 < kChunk ? nsl - s0 : kChunk;
+            uint4 fa[kChunk], fb[kChunk], ga[kChunk], gb[kChunk];
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                if (k < m) {
+                    const uint64_t o = (uint64_t)(s0 + k) * pp;
+                    fa[k] = pq[o * nqr];
+                    fb[k] = pc[o * n];
+                    if (!HH) {
+                        ga[k] = pq[(o + 2) * nqr];
+                        gb[k] = pc[(o + 2) * n];
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kChunk; ++k) {
+                if (k < m) {
+                    const half8 ah = *(const half8 *)&fa[k], bh = *(const half8 *)&fb[k];
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
+                    if (!HH) {
+                        const half8 al = *(const half8 *)&ga[k], bl = *(const half8 *)&gb[k];
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
+                    }
+                }
+            }
+        }
+        // the row thresholds written by this wave's lanes are read by all
+        // of its lanes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // one 32 x 32 block: register v of lane l holds row 8 (v / 4) + v % 4
+        // + 4 (l / 32), column l % 32 (the rules of classify_block)
+        const float xin = vc ? a.kp * nx : __builtin_nanf(""), xout = vc ? a.km * nx : __builtin_nanf("");
+        int wbits = 0;  // lane r < 32: the block's 32 bits of row r
+        uint64_t band = 0;
+        static_for(std::make_integer_sequence<int, 16>{}, [&](auto V) {
+            constexpr int v = decltype(V)::value, i0 = 8 * (v / 4) + v % 4;
+            const int row = i0 + 4 * hi;
+            const float d2 = acc[v];
+            const uint64_t bin = __ballot(fmaf(-2.0f, d2, xin) <= LQI[wave][row]);
+            const uint64_t bno = __ballot(fmaf(-2.0f, d2, xout) <= LQO[wave][row]);
+            band |= bno & ~bin;
+            wbits = write_lane<i0>(wbits, (uint32_t)bin);
+            wbits = write_lane<i0 + 4>(wbits, (uint32_t)(bin >> 32));
+        });
+        const uint64_t mbase = a.toff[t] - a.wbase;
+        if (band != 0) {
+            // rare: the band pairs, appended for the binary64 re-check
+            Boundary *bl = band_list(a.blist, a.lcap);
+            unsigned long long *bc = band_counter(a.bcount);
+#pragma unroll 1
+            for (int v = 0; v < 16; ++v) {
+                const int row = 8 * (v >> 2) + (v & 3) + 4 * hi;
+                const float d2 = acc[v];
+                const bool bd = !(fmaf(-2.0f, d2, xin) <= LQI[wave][row]) && fmaf(-2.0f, d2, xout) <= LQO[wave][row];
+                const uint64_t bb = __ballot(bd);
+                if (bb == 0) continue;
+                const int first = __ffsll((unsigned long long)bb) - 1;
+                unsigned long long base = 0;
+                if (lane == first) base = atomicAdd(bc, (unsigned long long)__popcll(bb));
+                base = __shfl(base, first, 64);
+                if (bd) {
+                    const uint64_t below = lane == 0 ? 0ull : (bb & (~0ull >> (64 - lane)));
+                    const uint64_t idx = base + __popcll(below);
+                    if (idx < a.lcap) {
+                        Boundary e;
+                        e.q = tl.row0 + rb * 32 + (uint32_t)row;
+                        e.x = ci;
+                        e.bit = (mbase + (uint64_t)(rb * 32 + row) * tl.words) * 64 + c0 + (uint32_t)col;
+                        bl[idx] = e;
+                    }
+                }
+            }
+        }
+        const uint64_t w = (uint64_t)(uint32_t)wbits << (c0 & 32u);
+        if (lane < 32) {
+            if (w != 0 && vr) {
+                const uint64_t wi = mbase + (uint64_t)r * tl.words + (c0 >> 6);
+                atomicOr((unsigned long long *)&a.mask[wi], (unsigned long long)w);
+                a.gflag[wi >> 2] = 1;
+                atomicAdd(&a.rowcnt[tl.row0 + r - a.row_base], (uint32_t)__popcll(w));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 }
 
 }  // namespace
@@ -478,6 +691,15 @@ hipError_t prepare_refine_g16(bool hh)
 {
     return hipFuncSetAttribute(hh ? (const void *)k_refine_g16<true> : (const void *)k_refine_g16<false>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)G16::BYTES);
+}
+
+hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
+{
+    if (!a.dlist || a.dcap == 0) return hipSuccess;
+    const dim3 grid(kBandLists * kDeferGroups);
+    if (hh) hipLaunchKernelGGL(k_refine_g16_blocks<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_refine_g16_blocks<false>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s)

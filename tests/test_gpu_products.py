@@ -136,3 +136,18 @@ def test_partial_test_with_differences_in_the_leading_dimensions(products):
         f"{st['last_partial']} comparisons settled from the first 64 dimensions")
     assert st["last_partial"] > 0
     assert_same_pairs(X, eps, got, want, f"leading-dimension pairs products={products}")
+
+
+def test_dense_steps_continue_in_place():
+    # about a tenth of all pairs are neighbours, so nearly every 32 x 32
+    # block is still live after the first 64 dimensions: a step with more
+    # live blocks than it may hand to the second kernel finishes them itself
+    rng = np.random.default_rng(91)
+    n, d = 12000, 96
+    X = rng.random((n, d), dtype=np.float32)
+    eps, _, _ = oracle.calibrate_eps(X, 500, 1200)
+    want = oracle.selfjoin_pairs(X, eps)
+    for products in (1, 3):
+        got, st = _join_stats(X, eps, products)
+        say(f"[gpu] dense d={d} products={products}: {len(got)} pairs, {st['last_partial']} settled early")
+        assert_same_pairs(X, eps, got, want, f"dense d={d} products={products}")
