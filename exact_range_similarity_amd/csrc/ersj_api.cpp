@@ -117,7 +117,7 @@ struct ersj_index {
     uint64_t mask_cap = 0;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;
-    uint2 *dlist = nullptr;  // blocks the d > 64 kernel hands on (kBandLists sub-lists)
+    uint4 *dlist = nullptr;  // blocks the d > 64 filter hands on (kBandLists sub-lists)
     uint64_t dcap = 0;       // entries per sub-list
     unsigned long long *counters = nullptr;  // band sub-list counters, then re-check hits
     uint64_t *lpref = nullptr;               // [kBandLists + 1] prefix, [2] kept / max count
@@ -137,6 +137,7 @@ struct ersj_index {
     bool use_m16 = false;  // split-fp16 form on the whole-tile kernel (33 <= d <= 64)
     bool use_g16 = false;  // split-fp16 form on operands prepared per point (d > 64)
     bool g16_hh = false;   // ... with the high-half products alone
+    bool g16_tiled = false;  // a batch overflowed the hand-on list: the tiled kernel alone from then on
     std::vector<double> mean;  // per input dimension (binary64 statistics of the points)
     float4 *tref = nullptr;  // per row tile: reference point of the MFMA kernels' centring
     uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
@@ -495,7 +496,10 @@ int choose_kernel(ersj_index *h)
         h->km = (float)(1.0 - K);
     }
     if (h->use_m16) HIPC(prepare_refine_m16(h->nb), "MFMA kernel LDS attribute");
-    else if (h->use_g16) HIPC(prepare_refine_g16(h->g16_hh), "MFMA kernel LDS attribute");
+    else if (h->use_g16) {
+        HIPC(prepare_refine_g16(h->g16_hh), "MFMA kernel LDS attribute");
+        HIPC(prepare_filter16(), "MFMA kernel LDS attribute");
+    }
     else if (k == ERSJ_REFINE_MFMA16) HIPC(prepare_refine_mfma(h->nb, true), "MFMA kernel LDS attribute");
     return ERSJ_OK;
 }
@@ -1062,7 +1066,7 @@ struct FillBufs {
     uint8_t *gflag = nullptr;
     Boundary *blist = nullptr;
     uint64_t bcap = 0;                         // band-list entries over all sub-lists
-    uint2 *dlist = nullptr;                    // handed-on blocks (null: none)
+    uint4 *dlist = nullptr;                    // handed-on blocks (null: none)
     uint64_t dcap = 0;                         // entries per sub-list
     unsigned long long *counters = nullptr;    // band sub-list counters, then re-check hit slots
     uint64_t *lpref = nullptr;
@@ -1125,12 +1129,14 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     while (rows_items * nseg_of(seg) > 0x7fffffffull) seg *= 2;
     a.seg_len = seg;
     a.nseg = std::max<uint32_t>(1, nseg_of(seg));
-    if (h->use_g16 && fb.grow && !h->opt.max_device_bytes) {
-        // hand-on list of the d > 64 kernel: kHandOn blocks per step, at most
-        // kStepsG16 steps per work item, the work items dealt to kBandLists
-        // sub-lists (8 bytes an entry; about 1.2% of the batch's mask)
-        const uint64_t items = (uint64_t)ntiles * a.nseg;
-        const uint64_t need = (uint64_t)kHandOn * kStepsG16 * ((items + kBandLists - 1) / kBandLists);
+    if (h->use_g16 && fb.grow && !h->opt.max_device_bytes && !h->g16_tiled) {
+        // hand-on list of the d > 64 filter: room for a sixteenth of the
+        // batch's 32 x 32 blocks (8 bytes an entry, 1/256 of its mask), at
+        // least 2^20 entries; a batch with more live blocks is refined again
+        // by the tiled kernel
+        const uint64_t cand = h->hcands[b + 1] - h->hcands[b];
+        const uint64_t want = std::max<uint64_t>(cand / 1024 / 16, 1ull << 20);
+        const uint64_t need = (want + kBandLists - 1) / kBandLists;
         if (h->dcap < need) {
             dfree(h, h->dlist);
             h->dlist = nullptr;
@@ -1182,15 +1188,21 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         a.blist = fb.blist;
         a.bcount = fb.counters;
         a.lcap = lcap;
+        // d > 64: the filter and the block kernel, or the tiled kernel alone
+        const bool filter = h->use_g16 && a.dlist != nullptr;
         HIPC(launch_fill_u64((uint64_t *)fb.counters, 0, (int64_t)ncount, s), "clear counters");
         HIPC(launch_fill_u32(fb.rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
-        HIPC(h->use_g16   ? launch_refine_g16(a, h->g16_hh, s)
-             : h->use_m16 ? launch_refine_m16(a, s)
-             : mfma       ? launch_refine_mfma(a, f16, s)
-                          : launch_refine_direct(a, s),
-             "refine kernel");
-        if (h->use_g16) HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
+        if (filter) {
+            HIPC(launch_filter16(a, h->g16_hh, s), "filter kernel");
+            HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
+        } else {
+            HIPC(h->use_g16   ? launch_refine_g16(a, h->g16_hh, s)
+                 : h->use_m16 ? launch_refine_m16(a, s)
+                 : mfma       ? launch_refine_mfma(a, f16, s)
+                              : launch_refine_direct(a, s),
+                 "refine kernel");
+        }
         h->ms_refine += timer_stop(h, s);
         if (h->opt.timing) {
             h->refine_launches += 1;
@@ -1199,16 +1211,27 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         HIPC(launch_band_prefix(fb.counters, lcap, fb.lpref, fb.lpref + kBandLists + 1, s), "band prefix");
         HIPC(hipMemcpyAsync(bres, fb.lpref + kBandLists + 1, sizeof bres, hipMemcpyDeviceToHost, s), "copy");
         std::vector<unsigned long long> dc;
-        if (a.dlist) {
+        if (filter) {
             dc.resize((size_t)kBandLists * kBandStride);
             HIPC(hipMemcpyAsync(dc.data(), a.dcount, dc.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost, s),
                  "copy");
         }
         TRY(sync(s, "refine"));
-        for (uint32_t k = 0; k < dc.size() / kBandStride; ++k)
-            if (dc[(size_t)k * kBandStride] > a.dcap)
-                return fail(ERSJ_ERR_INTERNAL, "hand-on sub-list %u holds %llu blocks, more than its %llu", k,
-                            (unsigned long long)dc[(size_t)k * kBandStride], (unsigned long long)a.dcap);
+        bool over = false;
+        for (uint32_t k = 0; k < dc.size() / kBandStride; ++k) over |= dc[(size_t)k * kBandStride] > a.dcap;
+        if (over) {
+            // more live blocks than the hand-on list holds: this batch and the
+            // later ones with the tiled kernel (every mask word is rewritten)
+            h->g16_tiled = true;
+            a.dlist = nullptr;
+            a.dcap = 0;
+            if (h->opt.timing) {
+                h->refine_launches -= 1;
+                h->refined_cand -= h->hcands[b + 1] - h->hcands[b];
+            }
+            --attempt;
+            continue;
+        }
         bcount = bres[0];
         if (bres[1] <= lcap) break;
         // A band sub-list overflowed: grow them all and refine the batch

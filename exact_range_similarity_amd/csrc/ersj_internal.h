@@ -325,12 +325,15 @@ struct RefineArgs {
     const float *n16, *n16q;
     const float *np16, *np16q;
     unsigned long long *partial;  // comparisons decided from those dimensions alone (kHitSlots slots)
-    // k_refine_g16: 32 x 32 blocks still live after that test, handed to
+    // k_filter16: 32 x 32 blocks still live after that test, handed to
     // k_refine_g16_blocks: kBandLists sub-lists of dcap entries {tile,
-    // (candidate position / 32) << 2 | query block}, sub-list c counted at
-    // dcount[c * kBandStride] (may exceed dcap: entries past it were not
-    // written, their blocks were finished in place); null: none handed on
-    uint2 *dlist;
+    // (candidate position / 32) << 2 | query block, point index of the
+    // block's first candidate when its candidates are consecutive points
+    // (else ~0), valid candidates of the block (1 .. 32)}, sub-list c counted
+    // at dcount[c * kBandStride] (a
+    // count past dcap means entries were lost and the batch must be refined
+    // again by the tiled kernel)
+    uint4 *dlist;
     unsigned long long *dcount;
     uint64_t dcap;
     // MFMA kernels that centre per row tile: reference of tile t at
@@ -399,14 +402,10 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 // floats; P needs g16_stages(nb, hh) * 4 * n uint4); nsub = 1, seg_len a
 // multiple of 512.  hh: high halves only (one product per slab, the wider
 // band of the high-part form), for both calls alike.
-// k_refine_g16 tests every 32 x 32 block after the first kPartialDims
-// dimensions: the squared distance over a subset of the dimensions bounds
-// the full one from below; a workgroup step with at most kHandOn blocks
-// still live hands them to k_refine_g16_blocks and ends there (a step has
-// at most kStepsG16 of them per work item)
+// k_refine_g16 and k_filter16 test every 32 x 32 block after the first
+// kPartialDims dimensions: the squared distance over a subset of the
+// dimensions bounds the full one from below
 constexpr int kPartialDims = 64;
-constexpr uint32_t kHandOn = 6;
-constexpr uint32_t kStepsG16 = 32;
 inline int g16_stages(int nb, bool hh)
 {
     const int ns = (nb + 3) / 4;
@@ -416,7 +415,11 @@ hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs
                          float *N, float *NP, hipStream_t st);
 hipError_t prepare_refine_g16(bool hh);
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
-// the blocks k_refine_g16 handed on (a.dlist), after it, on the same stream
+// filter over the first kPartialDims dimensions: every 32 x 32 block settled
+// there or handed on (a.dlist, required); the batch's mask words zeroed
+hipError_t prepare_filter16();
+hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s);
+// the blocks handed on (a.dlist), after the filter, on the same stream
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----

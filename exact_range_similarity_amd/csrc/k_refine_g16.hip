@@ -46,12 +46,14 @@
 // "out" rule of the classification, with the norms over those dimensions in
 // place of the full ones (the same band coefficient: the partial value has
 // fewer terms and fewer MFMA instructions behind it).  A block whose pairs
-// are all out keeps zero bits and runs no further MFMA.  A step with at most
-// kHandOn blocks still live hands them to k_refine_g16_blocks (a list) and
-// ends at the test; the check stage loads the next step's first stage in
-// advance for that.  A step with more live blocks continues in place.
+// are all out keeps zero bits and runs no further MFMA; a step whose blocks
+// are all out loads and stages no further operand.
 //
-// k_refine_g16_blocks: one wave per handed-on 32 x 32 block, operand
+// The default path splits that work in two.  k_filter16 computes only the
+// first kPartialDims dimensions, with each wave's query block held in
+// registers for the whole work item and the candidates streamed through LDS,
+// tests every block and hands the live ones on in a list; then
+// k_refine_g16_blocks takes one wave per handed-on 32 x 32 block, operand
 // fragments read straight from the prepared arrays (the slab layout is the
 // MFMA operand layout: lane l takes row or candidate l % 32, half l / 32 of a
 // slab), all slabs summed in one accumulator, classified like the tiles of
@@ -371,29 +373,6 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         alive = nal;
     };
 
-    // hand the wave's live blocks on.  A workgroup hands on at most
-    // kHandOn blocks a step and the host sizes each sub-list for all steps of
-    // the workgroups that use it; the host also checks the counts, so an
-    // entry past dcap (never expected) fails the batch instead of losing a
-    // block.
-    auto defer_blocks = [&](uint32_t st) __attribute__((always_inline)) {
-        const uint32_t cnt = __popc(alive);
-        unsigned long long base = 0;
-        if (lane == 0) base = atomicAdd(&a.dcount[(uint64_t)(blockIdx.x % kBandLists) * kBandStride], (unsigned long long)cnt);
-        base = __shfl(base, 0, 64);
-        uint2 *dl = a.dlist + (uint64_t)(blockIdx.x % kBandLists) * a.dcap;
-        uint32_t j = 0;
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (!((alive >> b) & 1u)) continue;
-            const uint32_t c0 = c_begin + st * kStepG + cg * 128 + (b & 3) * 32;
-            const uint32_t rb = (uint32_t)(rh * 2 + (b >> 2));
-            if (lane == 0 && base + j < a.dcap) dl[base + j] = make_uint2(t, ((c0 >> 5) << 2) | rb);
-            ++j;
-        }
-        alive = 0;
-    };
-
     int wsel = 0;  // group buffer of the current 512-candidate group (toggles at each flush)
     auto classify = [&](uint32_t st) __attribute__((always_inline)) {
         uint64_t *wg = LWORDS + (size_t)wsel * kRowsG * 8;
@@ -450,50 +429,21 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         deposit(0, 0, 0);
     }
     __syncthreads();
-    // Stage (st, sl), it-th in order (LDS buffer it & 1).  With the hand-on
-    // list, the check stage loads the next step's first stage instead of its
-    // own next one: most steps end there (a barrier tells every wave how many
-    // blocks are still live: none, or up to kHandOn handed on).  A step with
-    // more live blocks continues in place and loads its next stage late.
-    const bool handon = a.dlist != nullptr;
+    // stage (st, sl), it-th in order (LDS buffer it & 1)
     uint32_t st = 0, sl = 0, it = 0;
     while (st < nsteps) {
         const bool last_sl = sl + 1 == (uint32_t)ns;
-        const bool at_chk = sl == chk;
-        const bool spec = at_chk && handon;
-        uint32_t nst = last_sl || spec ? st + 1 : st, nsl = last_sl || spec ? 0 : sl + 1;
-        // without the hand-on list a settled step's later stages are neither
-        // loaded nor staged
-        bool more = nst < nsteps && !(step_dead && nst == st);
-        uint32_t ci_keep = ci;
-        float cn_keep = cn, cnp_keep = cnp;
+        const uint32_t nst = last_sl ? st + 1 : st, nsl = last_sl ? 0 : sl + 1;
+        // a settled step's later stages are neither loaded nor staged
+        const bool more = nst < nsteps && !(step_dead && nst == st);
         if (more) issue(nst, nsl);
         if ((do0 || do1) && alive != 0) mma((int)(it & 1));
-        bool done = false;  // the step ends with this stage
-        if (at_chk) {
+        if (sl == chk) {
             if (do0 || do1) partial_check(st);
             else alive = 0;
             if (lane == 0) LALIVE[wave] = alive;
-            if (spec) {
-                __syncthreads();
-                // (LALIVE is written again only after this stage's barrier)
-                const uint32_t live = __popc(LALIVE[0]) + __popc(LALIVE[1]) + __popc(LALIVE[2]) + __popc(LALIVE[3]);
-                if (live <= kHandOn) {
-                    if (alive != 0) defer_blocks(st);
-                    done = true;
-                } else {
-                    // continue in place: this step's next stage after all
-                    ci = ci_keep;
-                    cn = cn_keep;
-                    cnp = cnp_keep;
-                    nst = st;
-                    nsl = sl + 1;
-                    more = true;
-                    issue(nst, nsl);
-                }
-            }
         }
-        if (last_sl || done) {
+        if (last_sl) {
             if ((do0 || do1) && alive != 0) classify(st);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -502,20 +452,14 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         }
         if (more) deposit(it + 1, nst, nsl);
         __syncthreads();
-        if (at_chk && !handon) step_dead = (LALIVE[0] | LALIVE[1] | LALIVE[2] | LALIVE[3]) == 0u;
-        if (last_sl || done) {
+        if (sl == chk) step_dead = (LALIVE[0] | LALIVE[1] | LALIVE[2] | LALIVE[3]) == 0u;
+        if (last_sl) {
             alive = 0xffu;
             step_dead = false;
             if (st % kGroupStepsG == kGroupStepsG - 1 || st + 1 == nsteps) {
                 flush(st / kGroupStepsG);
                 wsel ^= 1;
             }
-        }
-        if (!more && !(last_sl || done)) {
-            // a settled step without the hand-on list: its remaining stages
-            // have nothing to do
-            nst = st;
-            nsl = sl + 1;
         }
         st = nst;
         sl = nsl;
@@ -526,6 +470,226 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     __syncthreads();
     for (int i = tid; i < (int)nrows; i += 256)
         if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
+}
+
+// Filter over the first kPartialDims dimensions: work item as k_refine_g16;
+// wave w holds query block w (rows 32 w .. 32 w + 31 of the tile) in
+// registers, the high halves of its first kPartialDims dimensions, and the
+// item's candidates pass through LDS kStepF at a time (one barrier a step).
+// Each 32 x 32 block gets the partial test; a live block goes to the
+// hand-on list, a settled one keeps zero bits.  The item's mask words are
+// written here as zeros, with their unit flags.
+constexpr int kStepF = 128;
+constexpr int kSlabsF = kPartialDims / 16;
+
+struct F16 {
+    static constexpr size_t B = 0;                                          // [2][2 kSlabsF][kStepF] x 16 B
+    static constexpr size_t NXP = B + (size_t)2 * 2 * kSlabsF * kStepF * 16;  // [2][kStepF] f32
+    static constexpr size_t QOUTP = NXP + (size_t)2 * kStepF * 4;           // [kRowsG] f32
+    static constexpr size_t PREF = QOUTP + (size_t)kRowsG * 4;              // [kMaxRanges + 1] u32
+    static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;    // [kMaxRanges] u32
+    static constexpr size_t BYTES = START + (size_t)kMaxRanges * 4;
+};
+
+// PP: parts per slab of the prepared arrays (2: high halves only, 4: high
+// and low); the filter reads the high ones
+template <int PP>
+__global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
+{
+    uint32_t rk, seg;
+    work_item(blockIdx.x, a.ntiles, a.nseg, &rk, &seg);
+    const uint32_t t = a.order[a.ord0 + rk];
+    const Tile tl = a.tiles[t];
+    const uint32_t A = tl.cell, nr = a.nrng[A];
+    const uint32_t *pref_g = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+    const uint32_t U = pref_g[nr];
+    const uint32_t c_begin = seg * a.seg_len;
+    if (c_begin >= U) return;
+    const uint32_t c_end = min(U, c_begin + a.seg_len);
+    const uint32_t nrows = min((uint32_t)kRowsG, tl.nrows), row0 = tl.row0;
+
+    extern __shared__ __align__(16) unsigned char smemf[];
+    uint4 *const LB = (uint4 *)(smemf + F16::B);
+    float *const LNXP = (float *)(smemf + F16::NXP);
+    float *const LQOUTP = (float *)(smemf + F16::QOUTP);
+    uint32_t *const LPREF = (uint32_t *)(smemf + F16::PREF);
+    uint32_t *const LSTART = (uint32_t *)(smemf + F16::START);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, col = lane & 31, hi = lane >> 5;
+    const uint64_t n = a.n, nqr = a.nqr;
+    if (tid <= kMaxRanges) LPREF[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
+    if (tid < kMaxRanges) LSTART[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
+    if (tid < kRowsG) {
+        const bool valid = (uint32_t)tid < nrows;
+        const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
+        LQOUTP[tid] = valid ? a.thi - a.km * nqp + a.tabs : -INFINITY;
+    }
+    // the wave's query fragments: row 32 wave + l % 32, half l / 32 of each slab
+    const uint32_t nrow_w = (uint32_t)(wave * 32) < nrows ? min(32u, nrows - (uint32_t)(wave * 32)) : 0u;
+    const uint32_t q = row0 + min((uint32_t)(wave * 32 + col), nrows - 1);
+    half8 af[kSlabsF];
+#pragma unroll
+    for (int s = 0; s < kSlabsF; ++s) {
+        const uint4 v = a.p16q[((uint64_t)s * PP + hi) * nqr + q];
+        af[s] = *(const half8 *)&v;
+    }
+    const uint64_t mbase = a.toff[t] - a.wbase;
+    const uint32_t W = tl.words;
+    const uint32_t nsteps = (c_end - c_begin + kStepF - 1) / kStepF;
+    __syncthreads();
+
+    // loader: thread tid stages candidate tid % kStepF of the step, parts
+    // 4 (tid / kStepF) .. + 3 (part = 2 slab + half)
+    const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)tid / kStepF) * 4;
+    const uint32_t idx0 = [&]() {
+        const int g = range_of(LPREF, nr, c_begin);
+        return LSTART[g] + (c_begin - LPREF[g]);
+    }();
+    uint32_t g_u = 0;
+    auto cand_index = [&](uint32_t st) __attribute__((always_inline)) -> uint32_t {
+        const uint32_t P0 = c_begin + st * kStepF;
+        while (P0 >= (uint32_t)__builtin_amdgcn_readfirstlane(LPREF[g_u + 1])) ++g_u;
+        const uint32_t p = P0 + lc;
+        if (p >= c_end) return idx0;
+        uint32_t g = g_u;
+        const uint32_t nxt = __builtin_amdgcn_readfirstlane(LPREF[g_u + 1]);
+        if (P0 + kStepF > nxt) {
+            while (p >= LPREF[g + 1]) ++g;
+        }
+        return LSTART[g] - LPREF[g] + p;
+    };
+    // a step's operands in flight, loaded two steps ahead into two register
+    // sets used alternately (named sets: an indexed array ends up in scratch
+    // memory).  The loads are issued on every step (a repeat of the last
+    // step's past the end, never deposited) so that the number in flight is
+    // the same on every path and the wait before a deposit drains only the
+    // older set.
+    struct Ops {
+        uint4 r0, r1, r2, r3;
+        float cnp;
+    };
+    auto issue = [&](uint32_t st) __attribute__((always_inline)) -> Ops {
+        const uint32_t ci = cand_index(st < nsteps ? st : nsteps - 1);
+        Ops o;
+        o.cnp = a.np16[ci];
+        const uint4 *pc = a.p16 + ci;
+        // part p = 2 slab + half: prepared part slab * PP + half
+        auto src = [&](uint32_t p) { return pc[((uint64_t)(p >> 1) * PP + (p & 1)) * n]; };
+        o.r0 = src(lp0);
+        o.r1 = src(lp0 + 1);
+        o.r2 = src(lp0 + 2);
+        o.r3 = src(lp0 + 3);
+        return o;
+    };
+    auto deposit = [&](const Ops o, uint32_t buf) __attribute__((always_inline)) {
+        uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
+        lb[(lp0 + 0) * kStepF + lc] = o.r0;
+        lb[(lp0 + 1) * kStepF + lc] = o.r1;
+        lb[(lp0 + 2) * kStepF + lc] = o.r2;
+        lb[(lp0 + 3) * kStepF + lc] = o.r3;
+        if (tid < kStepF) LNXP[buf * kStepF + lc] = o.cnp;
+    };
+    unsigned long long npart = 0;
+    uint4 *const dl = a.dlist + (uint64_t)(blockIdx.x % kBandLists) * a.dcap;
+    unsigned long long *const dc = &a.dcount[(uint64_t)(blockIdx.x % kBandLists) * kBandStride];
+
+    if (nsteps == 0) return;
+    // the query fragments arrive before any operand load is in flight, so
+    // that no wait in the loop has to count them
+    __builtin_amdgcn_s_waitcnt(0);
+    Ops S0 = issue(0), S1 = issue(1);
+    deposit(S0, 0);
+    __syncthreads();
+    // step st: operands of step st + 2 requested into the set step st was
+    // deposited from (S0 for even st), step st + 1 deposited from the other.
+    // The request follows the hand-on, whose atomic returns through the same
+    // counter as the loads: placed before it, its wait would drain them.
+    auto step = [&](uint32_t st, auto odd) __attribute__((always_inline)) {
+        const uint32_t buf = st & 1;
+        // the step's mask words, zero, and their unit flags: row tid / 2,
+        // word tid % 2 of the step
+        {
+            const uint32_t row = (uint32_t)tid >> 1, c0 = c_begin + st * kStepF + ((uint32_t)tid & 1u) * 64;
+            if (row < nrows && c0 < c_end) {
+                const uint64_t wi = mbase + (uint64_t)row * W + (c0 >> 6);
+                a.mask[wi] = 0ull;
+                if (((c0 >> 6) & 3u) == 0) a.gflag[wi >> 2] = 0;
+            }
+        }
+        if (nrow_w != 0) {
+            floatx16 acc[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[tt] = floatx16{};
+            const uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
+#pragma unroll
+            for (int s = 0; s < kSlabsF; ++s) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const half8 bf = *(const half8 *)&lb[(s * 2 + hi) * kStepF + tt * 32 + col];
+                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s], bf, acc[tt], 0, 0, 0);
+                }
+            }
+            // partial test of the wave's four blocks
+            const float4 *qo4 = (const float4 *)LQOUTP + wave * 8 + hi;
+            uint32_t live = 0;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const uint32_t cb = c_begin + st * kStepF + tt * 32;
+                const float xo = cb + col < c_end ? a.km * LNXP[buf * kStepF + tt * 32 + col] : __builtin_nanf("");
+                uint64_t nout = 0;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 qo = qo4[g * 2];
+                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 0], xo) <= qo.x);
+                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 1], xo) <= qo.y);
+                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 2], xo) <= qo.z);
+                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 3], xo) <= qo.w);
+                }
+                if (nout != 0) live |= 1u << tt;
+                else if (cb < c_end) npart += (unsigned long long)nrow_w * min(32u, c_end - cb);
+            }
+            if (live != 0) {
+                // hand the live blocks on
+                unsigned long long base = 0;
+                if (lane == 0) base = atomicAdd(dc, (unsigned long long)__popc(live));
+                base = __shfl(base, 0, 64);
+                uint32_t j = 0;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    if (!((live >> tt) & 1u)) continue;
+                    const uint32_t c0 = c_begin + st * kStepF + tt * 32;
+                    if (lane == 0 && base + j < a.dcap) {
+                        // the block's candidates are consecutive points when
+                        // its valid positions lie in one range of the list
+                        const int g = range_of(LPREF, nr, c0);
+                        const bool one = min(c0 + 32u, U) <= LPREF[g + 1];
+                        const uint32_t ci0 = one ? LSTART[g] - LPREF[g] + c0 : 0xffffffffu;
+                        dl[base + j] = make_uint4(t, ((c0 >> 5) << 2) | (uint32_t)wave, ci0, min(32u, U - c0));
+                    }
+                    ++j;
+                }
+            }
+        }
+        if constexpr (decltype(odd)::value) S1 = issue(st + 2);
+        else S0 = issue(st + 2);
+        // deposited on every step (past the end into a buffer nobody reads),
+        // for the same reason the loads are issued on every step
+        if constexpr (decltype(odd)::value) deposit(S0, buf ^ 1);
+        else deposit(S1, buf ^ 1);
+        __syncthreads();
+    };
+    // pairs of steps (every trip of the loop passes both, so the waits it
+    // needs do not depend on a skipped odd step), then an even tail
+    uint32_t st = 0;
+    for (; st + 1 < nsteps; st += 2) {
+        step(st, std::integral_constant<bool, false>{});
+        step(st + 1, std::integral_constant<bool, true>{});
+    }
+    if (st < nsteps) step(st, std::integral_constant<bool, false>{});
+    if (lane == 0 && npart != 0)
+        atomicAdd(&a.partial[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], npart);
 }
 
 // One wave per handed-on block (see the file comment).  Grid: kBandLists x
@@ -541,36 +705,47 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
     const uint32_t sub = blockIdx.x % kBandLists, j0 = blockIdx.x / kBandLists, nj = gridDim.x / kBandLists;
     const unsigned long long cnt0 = a.dcount[(uint64_t)sub * kBandStride];
     const uint64_t cnt = cnt0 < a.dcap ? cnt0 : a.dcap;
-    const uint2 *dl = a.dlist + (uint64_t)sub * a.dcap;
+    const uint4 *dl = a.dlist + (uint64_t)sub * a.dcap;
     const uint64_t n = a.n, nqr = a.nqr;
     const int nsl = HH ? 2 * (((a.nb + 3) / 4 + 1) / 2) : (a.nb + 3) / 4;  // slabs (high parts: padded even)
     const int pp = HH ? 2 : 4;                                            // parts per slab
-    constexpr int kChunk = HH ? 6 : 3;  // slabs whose operands are loaded together
+    // slabs whose operands are loaded together; the next chunk's loads are
+    // in flight while a chunk's MFMAs run.  Every chunk loads all its slabs
+    // (an index past the last slab repeats the last one and is not used), so
+    // the loads in flight do not depend on the slab count.
+    constexpr int kChunk = HH ? 4 : 2;
+    struct Chunk {
+        uint4 fa[kChunk], fb[kChunk], ga[kChunk], gb[kChunk];
+    };
     for (uint64_t e = (uint64_t)j0 * 4 + wave; e < cnt; e += (uint64_t)nj * 4) {
-        const uint2 ent = dl[e];
+        const uint4 ent = dl[e];
         const uint32_t t = ent.x, rb = ent.y & 3u, c0 = (ent.y >> 2) << 5;
         const Tile tl = a.tiles[t];
-        const uint32_t A = tl.cell, nr = a.nrng[A];
-        const uint32_t *pref = a.rpref + (uint64_t)A * (kMaxRanges + 1);
-        const uint32_t U = pref[nr];
         const uint32_t nrows = min((uint32_t)kTileRows, tl.nrows);
         const uint32_t r = rb * 32 + (uint32_t)col;
         const bool vr = r < nrows;
         const uint32_t q = tl.row0 + (vr ? r : nrows - 1);
         const uint32_t p = c0 + (uint32_t)col;
-        const bool vc = p < U;
-        // the lane's candidate: range g with pref[g] <= p < pref[g + 1]
-        uint32_t g = 0;
-        if (vc) {
-            uint32_t lo = 0, up = nr;  // pref[lo] <= p < pref[up]
-            while (up - lo > 1) {
-                const uint32_t mid = (lo + up) >> 1;
-                if (pref[mid] <= p) lo = mid;
-                else up = mid;
+        const bool vc = (uint32_t)col < ent.w;
+        uint32_t ci;
+        if (ent.z != 0xffffffffu) {
+            ci = ent.z + (vc ? (uint32_t)col : 0u);  // consecutive points
+        } else {
+            // the lane's candidate: range g with pref[g] <= p < pref[g + 1]
+            const uint32_t A = tl.cell, nr = a.nrng[A];
+            const uint32_t *pref = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+            uint32_t g = 0;
+            if (vc) {
+                uint32_t lo = 0, up = nr;  // pref[lo] <= p < pref[up]
+                while (up - lo > 1) {
+                    const uint32_t mid = (lo + up) >> 1;
+                    if (pref[mid] <= p) lo = mid;
+                    else up = mid;
+                }
+                g = lo;
             }
-            g = lo;
+            ci = a.rstart[(uint64_t)A * kMaxRanges + g] + (vc ? p - pref[g] : 0u);
         }
-        const uint32_t ci = a.rstart[(uint64_t)A * kMaxRanges + g] + (vc ? p - pref[g] : 0u);
         if (lane < 32) {
             const float nq = a.n16q[q];
             LQI[wave][col] = vr ? a.tlo - a.kp * nq - a.tabs : -INFINITY;
@@ -580,34 +755,38 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
         floatx16 acc = {};
         const uint4 *pq = a.p16q + (uint64_t)hi * nqr + q;
         const uint4 *pc = a.p16 + (uint64_t)hi * n + ci;
-#pragma unroll 1
-        for (int s0 = 0; s0 < nsl; s0 += kChunk) {
-            const int m = nsl - s0 < kChunk ? nsl - s0 : kChunk;
-            uint4 fa[kChunk], fb[kChunk], ga[kChunk], gb[kChunk];
+        auto load = [&](int s0) __attribute__((always_inline)) -> Chunk {
+            Chunk c;
 #pragma unroll
             for (int k = 0; k < kChunk; ++k) {
-                if (k < m) {
-                    const uint64_t o = (uint64_t)(s0 + k) * pp;
-                    fa[k] = pq[o * nqr];
-                    fb[k] = pc[o * n];
-                    if (!HH) {
-                        ga[k] = pq[(o + 2) * nqr];
-                        gb[k] = pc[(o + 2) * n];
-                    }
+                const int sl = s0 + k < nsl ? s0 + k : nsl - 1;
+                const uint64_t o = (uint64_t)sl * pp;
+                c.fa[k] = pq[o * nqr];
+                c.fb[k] = pc[o * n];
+                if (!HH) {
+                    c.ga[k] = pq[(o + 2) * nqr];
+                    c.gb[k] = pc[(o + 2) * n];
                 }
             }
+            return c;
+        };
+        Chunk X = load(0);
+#pragma unroll 1
+        for (int s0 = 0; s0 < nsl; s0 += kChunk) {
+            const Chunk Y = load(s0 + kChunk);
 #pragma unroll
             for (int k = 0; k < kChunk; ++k) {
-                if (k < m) {
-                    const half8 ah = *(const half8 *)&fa[k], bh = *(const half8 *)&fb[k];
+                if (s0 + k < nsl) {
+                    const half8 ah = *(const half8 *)&X.fa[k], bh = *(const half8 *)&X.fb[k];
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc, 0, 0, 0);
                     if (!HH) {
-                        const half8 al = *(const half8 *)&ga[k], bl = *(const half8 *)&gb[k];
+                        const half8 al = *(const half8 *)&X.ga[k], bl = *(const half8 *)&X.gb[k];
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc, 0, 0, 0);
                         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc, 0, 0, 0);
                     }
                 }
             }
+            X = Y;
         }
         // the row thresholds written by this wave's lanes are read by all
         // of its lanes
@@ -691,6 +870,28 @@ hipError_t prepare_refine_g16(bool hh)
 {
     return hipFuncSetAttribute(hh ? (const void *)k_refine_g16<true> : (const void *)k_refine_g16<false>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)G16::BYTES);
+}
+
+hipError_t prepare_filter16()
+{
+    hipError_t e = hipFuncSetAttribute((const void *)k_filter16<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)F16::BYTES);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void *)k_filter16<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)F16::BYTES);
+}
+
+hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
+{
+    if (!a.dlist || !a.np16 || !a.np16q) return hipErrorInvalidValue;
+    if (a.seg_len % kGroupCands != 0) return hipErrorInvalidValue;
+    const uint64_t blocks = (uint64_t)a.ntiles * a.nseg;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    RefineArgs args = a;
+    void *params[] = {&args};
+    return hipLaunchKernel(hh ? (const void *)k_filter16<2> : (const void *)k_filter16<4>, dim3((unsigned)blocks),
+                           dim3(256), params, F16::BYTES, s);
 }
 
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)

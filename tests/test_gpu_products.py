@@ -151,3 +151,19 @@ def test_dense_steps_continue_in_place():
         got, st = _join_stats(X, eps, products)
         say(f"[gpu] dense d={d} products={products}: {len(got)} pairs, {st['last_partial']} settled early")
         assert_same_pairs(X, eps, got, want, f"dense d={d} products={products}")
+
+
+def test_more_live_blocks_than_the_hand_on_list_holds():
+    # equal spread in all 160 dimensions and a radius for a few neighbours
+    # per point: the distance over the first 64 dimensions settles almost no
+    # block, so the 1.2 M blocks of this join overflow the hand-on list
+    # (2^20 entries at this size) and the batch is refined again by the
+    # tiled kernel
+    rng = np.random.default_rng(97)
+    n, d = 36000, 160
+    X = rng.random((n, d), dtype=np.float32)
+    eps, _, _ = oracle.calibrate_eps(X, 300, 4)
+    want = oracle.selfjoin_pairs(X, eps)
+    got, st = _join_stats(X, eps, 0)
+    say(f"[gpu] overflowing hand-on list n={n} d={d}: {len(got)} pairs, {st['last_partial']} settled early")
+    assert_same_pairs(X, eps, got, want, f"overflowing hand-on list n={n} d={d}")
