@@ -200,10 +200,12 @@ def main():
     # 64 dimensions and on prepared operands above; the fp32 MFMA form; the
     # direct form
     nb = (d + 3) // 4
-    kname = ("k_refine_m16" if nb <= 16 else "k_refine_g16") if f16 else \
+    kname = ("k_refine_m16" if nb <= 16 else
+             "k_filter16+k_refine_g16_blocks" if st["last_filtered"] else "k_refine_g16") if f16 else \
         "k_refine_mfma" if mfma else "k_refine_direct"
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", f"{kname[2:]}_{args.workload}_traffic.json")
+    tname = "filter16_blocks" if "+" in kname else kname[2:]
+    tfile = os.path.join(ROOT, "profiles", f"{tname}_{args.workload}_traffic.json")
     if os.path.exists(tfile):
         import hashlib
         with open(tfile) as f:

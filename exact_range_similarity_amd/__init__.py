@@ -71,7 +71,8 @@ class Stats(ctypes.Structure):
                 ("refine_launches", ctypes.c_int64), ("refined_candidates", ctypes.c_uint64),
                 ("n_queries", ctypes.c_int64), ("last_skipped", ctypes.c_uint64),
                 ("skipped_candidates", ctypes.c_uint64), ("mfma_products", ctypes.c_int32),
-                ("last_partial", ctypes.c_uint64), ("partial_candidates", ctypes.c_uint64)]
+                ("last_partial", ctypes.c_uint64), ("partial_candidates", ctypes.c_uint64),
+                ("last_filtered", ctypes.c_int32)]
 
     def as_dict(self):
         out = {}

@@ -128,6 +128,7 @@ struct ersj_index {
     uint64_t ready_pairs = 0;
     // stats
     uint64_t last_cand = 0, last_pairs = 0, last_bnd = 0, last_in = 0, last_skip = 0, last_part = 0;
+    bool last_filtered = false;  // the last batch went through the filter and the block kernel
     double ms_build = 0, ms_count = 0, ms_plan = 0, ms_refine = 0, ms_recheck = 0, ms_expand = 0;
     int64_t refine_launches = 0;
     uint64_t refined_cand = 0, skipped_cand = 0, partial_cand = 0;
@@ -1233,6 +1234,7 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
             continue;
         }
         bcount = bres[0];
+        h->last_filtered = filter;
         if (bres[1] <= lcap) break;
         // A band sub-list overflowed: grow them all and refine the batch
         // again (every mask word is rewritten, so the first result is
@@ -1828,6 +1830,7 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     o->skipped_candidates = h->skipped_cand;
     o->mfma_products = h->kernel_used != ERSJ_REFINE_MFMA16 ? 0 : h->g16_hh ? 1 : 3;
     o->last_partial = h->last_part;
+    o->last_filtered = h->last_filtered ? 1 : 0;
     o->partial_candidates = h->partial_cand;
     return ERSJ_OK;
 }

@@ -134,6 +134,8 @@ typedef struct ersj_stats {
     uint64_t last_partial;       /* comparisons of the last fill_pass decided "out" from the first 64
                                     dimensions alone (split form above 64 dimensions) */
     uint64_t partial_candidates; /* the same, over the launches timed in refine_ms */
+    int32_t last_filtered;       /* 1: the last fill_pass refined with the 64-dimension filter and the
+                                    block kernel (above 64 dimensions), 0: with one kernel */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */
