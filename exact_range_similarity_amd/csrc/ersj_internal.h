@@ -429,7 +429,7 @@ hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
 hipError_t launch_band_prefix(const unsigned long long *bcount, uint64_t lcap, uint64_t *lpref,
                               uint64_t *out, hipStream_t s);
 // xr, xqr: points and query rows in sorted order, input dimension order,
-// row-major (d floats per row).
+// row-major, ldr = recheck_stride(d) floats per row, the floats past d zero.
 hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpref, uint64_t cnt,
                           const float *xr, const float *xqr, int32_t d, int32_t ldr, double e64, uint64_t *mask,
                           uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,

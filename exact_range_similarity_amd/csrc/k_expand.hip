@@ -42,14 +42,19 @@ __global__ __launch_bounds__(kBandLists) void k_band_prefix(const unsigned long 
 // operation separately rounded (no contraction): the exact definition the
 // result set is specified by.  Pairs at or below fl(eps*eps) get their bit.
 // Both rows are read from row-major copies in sorted order, rows ldr
-// floats apart (ldr: d rounded up to 4), in 16-byte pieces: a row's d floats
-// are contiguous, a few cache lines and d / 4 loads per pair.  Entry i of the kept
+// floats apart (ldr: d rounded up to 4, the floats past d zero in both
+// copies, so that their terms add an exact +0 to a sum that is never
+// negative).  A lane takes its two rows 32 floats (one 128-byte line each)
+// at a time: the 16 loads of a line pair are issued together, then its 32
+// terms are summed in order.  The last chunk re-reads the row's last float4
+// in place of those past its end and skips their terms.  Entry i of the kept
 // band pairs lives in sub-list c (lpref[c] <= i < lpref[c+1]) at offset
 // i - lpref[c].
+constexpr int kRecheckChunk = 8;  // float4 per row per chunk
 __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl, uint64_t lcap,
                                                  const uint64_t *__restrict__ lpref, uint64_t cnt,
                                                  const float *__restrict__ xr, const float *__restrict__ xqr,
-                                                 int32_t d, int32_t ldr, double e64, uint64_t *__restrict__ mask,
+                                                 int32_t ldr, double e64, uint64_t *__restrict__ mask,
                                                  uint8_t *__restrict__ gflag,
                                                  unsigned long long *__restrict__ nin,
                                                  uint32_t *__restrict__ rowcnt, uint64_t row_base)
@@ -72,16 +77,45 @@ __global__ __launch_bounds__(256) void k_recheck(const Boundary *__restrict__ bl
         const Boundary e = bl[(uint64_t)lo * lcap + (i - spref[lo])];
         const float4 *qa = (const float4 *)(xqr + (uint64_t)e.q * (uint64_t)ldr);
         const float4 *xb = (const float4 *)(xr + (uint64_t)e.x * (uint64_t)ldr);
+        const int n4 = ldr >> 2;
         double s = 0.0;
-        for (int k4 = 0; 4 * k4 < d; ++k4) {
-            const float4 qv = qa[k4], xv = xb[k4];
-            const float qc[4] = {qv.x, qv.y, qv.z, qv.w}, xc[4] = {xv.x, xv.y, xv.z, xv.w};
+        auto term = [&](float a, float b) __attribute__((always_inline)) {
+            const double t = (double)a - (double)b;
+            const double tt = t * t;
+            s = s + tt;
+        };
+        int k4 = 0;
+#pragma unroll 1
+        for (; k4 + kRecheckChunk <= n4; k4 += kRecheckChunk) {
+            float4 qv[kRecheckChunk], xv[kRecheckChunk];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (4 * k4 + c < d) {
-                    const double t = (double)qc[c] - (double)xc[c];
-                    const double tt = t * t;
-                    s = s + tt;
+            for (int c = 0; c < kRecheckChunk; ++c) {
+                qv[c] = qa[k4 + c];
+                xv[c] = xb[k4 + c];
+            }
+#pragma unroll
+            for (int c = 0; c < kRecheckChunk; ++c) {
+                term(qv[c].x, xv[c].x);
+                term(qv[c].y, xv[c].y);
+                term(qv[c].z, xv[c].z);
+                term(qv[c].w, xv[c].w);
+            }
+        }
+        if (k4 < n4) {
+            float4 qv[kRecheckChunk], xv[kRecheckChunk];
+#pragma unroll
+            for (int c = 0; c < kRecheckChunk; ++c) {
+                const int k = k4 + c < n4 ? k4 + c : n4 - 1;
+                qv[c] = qa[k];
+                xv[c] = xb[k];
+            }
+#pragma unroll
+            for (int c = 0; c < kRecheckChunk; ++c) {
+                if (k4 + c < n4) {
+                    term(qv[c].x, xv[c].x);
+                    term(qv[c].y, xv[c].y);
+                    term(qv[c].z, xv[c].z);
+                    term(qv[c].w, xv[c].w);
                 }
             }
         }
@@ -374,11 +408,11 @@ hipError_t launch_recheck(const Boundary *bl, uint64_t lcap, const uint64_t *lpr
                           uint8_t *gflag, unsigned long long *nin, uint32_t *rowcnt, uint64_t row_base,
                           hipStream_t s)
 {
-    if (ldr < d || (ldr & 3) != 0) return hipErrorInvalidValue;
+    if (ldr < d || (ldr & 3) != 0 || ldr <= 0) return hipErrorInvalidValue;
     if (cnt == 0) return hipSuccess;
     const uint64_t blocks = (cnt + 255) / 256;
     hipLaunchKernelGGL(k_recheck, dim3((unsigned)blocks), dim3(256), 0, s, bl, lcap, lpref, cnt, xr, xqr,
-                       d, ldr, e64, mask, gflag, nin, rowcnt, row_base);
+                       ldr, e64, mask, gflag, nin, rowcnt, row_base);
     return hipGetLastError();
 }
 
