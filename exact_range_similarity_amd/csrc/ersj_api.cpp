@@ -66,6 +66,7 @@ struct ersj_index {
     float tlo = 0.0f, thi = 0.0f;
     float tbox = INFINITY;  // block box test threshold (inf: off)
     float kp = 1.0f, km = 1.0f;
+    float kmf = 1.0f;  // the d > 64 filter's partial test
     float s16 = 1.0f, tlo16 = 0.0f, thi16 = 0.0f, tabs = 0.0f;  // split-fp16 form (scaled domain)
     double maxabs = 0.0;
     GridParams gp{};
@@ -484,17 +485,23 @@ int choose_kernel(ersj_index *h)
     h->use_m16 = k == ERSJ_REFINE_MFMA16 && refine_m16_supported(h->nb);
     h->use_g16 = k == ERSJ_REFINE_MFMA16 && h->nb > 16;
     h->g16_hh = h->use_g16 && h->opt.mfma_products != 3;
-    if (h->g16_hh) {
+    if (h->use_g16) {
         // High-half products alone (k_refine_g16.hip): the dropped products
         // move s^2 q'.x' by at most 2^-10 (1 + 2^-12) sum |v_q v_x| (in the
         // squared distance at most twice that, <= 2^-10 (1 + 2^-12) (Nq + Nx))
         // plus absolute parts within tabs; one MFMA per slab (padded to an
-        // even count) at 36u each, and the fp32 form's 4 (d_pad + 8) u.
+        // even count) at 36u each, and the fp32 form's 4 (d_pad + 8) u.  The
+        // filter's partial test forms high-half products alone with either
+        // product count, so it always takes this coefficient (over its 64
+        // dimensions it is larger than needed).
         const double u = std::ldexp(1.0, -24);
         const double K = 4.0 * (4.0 * h->nb + 8.0) * u + std::ldexp(1.0 + std::ldexp(1.0, -12), -10) +
                          36.0 * u * 2.0 * g16_stages(h->nb, true) * 1.01;
-        h->kp = (float)(1.0 + K);
-        h->km = (float)(1.0 - K);
+        h->kmf = (float)(1.0 - K);
+        if (h->g16_hh) {
+            h->kp = (float)(1.0 + K);
+            h->km = (float)(1.0 - K);
+        }
     }
     if (h->use_m16) HIPC(prepare_refine_m16(h->nb), "MFMA kernel LDS attribute");
     else if (h->use_g16) {
@@ -1158,6 +1165,7 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     a.thi = h->thi;
     a.kp = h->kp;
     a.km = h->km;
+    a.kmf = h->kmf;
     a.s16 = h->s16;
     a.tabs = h->tabs;
     if (f16) {

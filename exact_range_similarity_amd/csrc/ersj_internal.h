@@ -303,6 +303,7 @@ struct RefineArgs {
     uint64_t *mask;
     float tlo, thi;      // fp32 classification thresholds
     float kp, km;        // 1 + K and 1 - K of the MFMA kernel's norm-proportional band
+    float kmf;           // 1 - K of the d > 64 filter's partial test (high-half products alone)
     float s16;           // split-fp16 form: power-of-two scale of the centred coordinates
                          // (tlo, thi are then the scaled thresholds)
     float tabs;          // absolute widening of its thresholds (fp16 subnormal parts)

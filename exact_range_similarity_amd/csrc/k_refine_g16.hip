@@ -52,7 +52,9 @@
 // The default path splits that work in two.  k_filter16 computes only the
 // first kPartialDims dimensions, with each wave's query block held in
 // registers for the whole work item and the candidates streamed through LDS,
-// tests every block and hands the live ones on in a list; then
+// tests every block and hands the live ones on in a list (its partial dot
+// product is the high-half one with either product count, so its "out" rule
+// takes the high-half band coefficient); then
 // k_refine_g16_blocks takes one wave per handed-on 32 x 32 block, operand
 // fragments read straight from the prepared arrays (the slab layout is the
 // MFMA operand layout: lane l takes row or candidate l % 32, half l / 32 of a
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     if (tid < kRowsG) {
         const bool valid = (uint32_t)tid < nrows;
         const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
-        LQOUTP[tid] = valid ? a.thi - a.km * nqp + a.tabs : -INFINITY;
+        LQOUTP[tid] = valid ? a.thi - a.kmf * nqp + a.tabs : -INFINITY;
     }
     // the wave's query fragments: row 32 wave + l % 32, half l / 32 of each slab
     const uint32_t nrow_w = (uint32_t)(wave * 32) < nrows ? min(32u, nrows - (uint32_t)(wave * 32)) : 0u;
@@ -637,7 +639,7 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const uint32_t cb = c_begin + st * kStepF + tt * 32;
-                const float xo = cb + col < c_end ? a.km * LNXP[buf * kStepF + tt * 32 + col] : __builtin_nanf("");
+                const float xo = cb + col < c_end ? a.kmf * LNXP[buf * kStepF + tt * 32 + col] : __builtin_nanf("");
                 uint64_t nout = 0;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {

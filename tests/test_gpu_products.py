@@ -167,3 +167,56 @@ def test_more_live_blocks_than_the_hand_on_list_holds():
     got, st = _join_stats(X, eps, 0)
     say(f"[gpu] overflowing hand-on list n={n} d={d}: {len(got)} pairs, {st['last_partial']} settled early")
     assert_same_pairs(X, eps, got, want, f"overflowing hand-on list n={n} d={d}")
+
+
+def _coherent_semijoin_case(seed=3):
+    # Every coordinate of the first 64 dimensions is 4 m + 1.75 or 4 m + 2.25
+    # (m an integer, 1024 <= m < 2048) after the kernels' scaling by 2^14
+    # (the largest magnitude, below 0.5, sets that scale; the points are
+    # mirrored so that their mean, the reference, is exactly 0).  fp16 has
+    # spacing 4 there, so every high half rounds down by 1.75 (or up by
+    # 1.75) in all 64 dimensions of both rows of a pair: the dropped
+    # low-half products add up instead of cancelling, and the high-half dot
+    # product is off by about 0.6 E, most of the high-half band 2^-10 (Nq + Nx)
+    # and far beyond the three-product band.  Each query has one partner, at
+    # S = E (1 + rho) for rho from -0.3 to 0.3; a semi-join, so that no
+    # zero-distance self pair keeps a block live.
+    rng = np.random.default_rng(seed)
+    d, scale, Es = 100, 16384.0, 4.0e6
+    Q, X = [], []
+    for off in (1.75, 2.25):
+        for rho in (-0.3, -0.1, -0.03, -0.01, -0.001, 0.001, 0.01, 0.03, 0.1, 0.3):
+            a = rng.integers(0, 600, 64)
+            base = rng.random(64) + 0.5
+            j = np.round(math.sqrt(Es * (1 + rho) / 16 / np.sum(base ** 2)) * base).astype(np.int64)
+            q, x = np.zeros(d), np.zeros(d)
+            q[:64] = (4 * (1024 + a) + off) / scale
+            x[:64] = (4 * (1024 + a + j) + off) / scale
+            Q.append(q)
+            X.append(x)
+    Q = np.array(Q, dtype=np.float32)
+    X = np.array(X, dtype=np.float32)
+    assert np.abs(X).max() < 0.5 and np.abs(Q).max() < 0.5 and np.abs(X).max() >= 0.25
+    Q = np.concatenate([Q, -Q])
+    X = np.concatenate([X, -X])
+    return Q, X, math.sqrt(Es) / scale
+
+
+@pytest.mark.parametrize("products", [1, 3])
+@pytest.mark.parametrize("tiled", [False, True])
+def test_high_halves_that_all_round_one_way(products, tiled):
+    Q, X, eps = _coherent_semijoin_case()
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    assert want.size == 20  # the ten pairs below eps and their mirror images
+    # a device-memory cap keeps the hand-on list unallocated: the tiled kernel
+    opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products,
+                                max_device_bytes=(1 << 34) if tiled else 0)
+    parts, h = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts,
+                              return_index=True)
+    st = ersj.get_stats(h)
+    h.free()
+    got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+    say(f"[gpu] coherent rounding products={products} tiled={tiled}: {got.size} pairs, "
+        f"filtered={st['last_filtered']}, band pairs {st['last_boundary_pairs']}")
+    assert st["last_filtered"] == (0 if tiled else 1)
+    assert np.array_equal(got, want)
