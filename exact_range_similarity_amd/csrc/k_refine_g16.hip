@@ -474,6 +474,28 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
         if (LRCNT[i] != 0) atomicAdd(&a.rowcnt[row0 + i - a.row_base], LRCNT[i]);
 }
 
+// The filter's "out" rule, rearranged so that the MFMAs add each row's term.
+// The classification's rule for a pair is out iff fl(xo - 2 s) > qo (s the
+// accumulated dot product, xo = fl(km Nx), qo the row threshold); its proof
+// starts from xo - 2 s* > qo - 2 E_s, s* the exact sum of the products and
+// E_s the accumulation error the band charges.  Here the accumulator starts
+// at c = filter_row_start(qo) >= qo / 2 + 2^-16 |qo / 2| (rounded up) and a
+// pair is out iff acc < filter_col_bound(xo) <= xo / 2.  A start value adds
+// at most 32.1u |c| to each instruction's error (the accumulation bound:
+// 17 faithfully rounded terms, the accumulator one of them), 128.4u |c| over
+// the four instructions of 64 dimensions, less than the slack: acc < xo / 2
+// gives s* + qo / 2 < xo / 2 + E_s, the proof's premise.  An invalid row
+// starts at -inf and an invalid column compares with NaN: out either way.
+__device__ __forceinline__ float filter_row_start(float qo)
+{
+    if (!(qo > -INFINITY)) return -INFINITY;
+    const double h = 0.5 * (double)qo;
+    return __double2float_ru(h + fabs(h) * 0x1p-16 + 0x1p-140);
+}
+
+// xo / 2, exact for xo >= 2^-125; 0 (below it) under 2^-120
+__device__ __forceinline__ float filter_col_bound(float xo) { return xo >= 0x1p-120f ? xo * 0.5f : 0.0f; }
+
 // Filter over the first kPartialDims dimensions: work item as k_refine_g16;
 // wave w holds query block w (rows 32 w .. 32 w + 31 of the tile) in
 // registers, the high halves of its first kPartialDims dimensions, and the
@@ -526,7 +548,7 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     if (tid < kRowsG) {
         const bool valid = (uint32_t)tid < nrows;
         const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
-        LQOUTP[tid] = valid ? a.thi - a.kmf * nqp + a.tabs : -INFINITY;
+        LQOUTP[tid] = valid ? filter_row_start(a.thi - a.kmf * nqp + a.tabs) : -INFINITY;
     }
     // the wave's query fragments: row 32 wave + l % 32, half l / 32 of each slab
     const uint32_t nrow_w = (uint32_t)(wave * 32) < nrows ? min(32u, nrows - (uint32_t)(wave * 32)) : 0u;
@@ -604,6 +626,20 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     Ops S0 = issue(0), S1 = issue(1);
     deposit(S0, 0);
     __syncthreads();
+    // the accumulators' start: register v of lane l holds row 8 (v / 4) +
+    // v % 4 + 4 (l / 32) of the wave's block
+    floatx16 crow;
+    {
+        const float4 *c4 = (const float4 *)LQOUTP + wave * 8 + hi;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 c = c4[g * 2];
+            crow[4 * g + 0] = c.x;
+            crow[4 * g + 1] = c.y;
+            crow[4 * g + 2] = c.z;
+            crow[4 * g + 3] = c.w;
+        }
+    }
     // step st: operands of step st + 2 requested into the set step st was
     // deposited from (S0 for even st), step st + 1 deposited from the other.
     // The request follows the hand-on, whose atomic returns through the same
@@ -622,34 +658,30 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
         }
         if (nrow_w != 0) {
             floatx16 acc[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) acc[tt] = floatx16{};
             const uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
 #pragma unroll
             for (int s = 0; s < kSlabsF; ++s) {
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const half8 bf = *(const half8 *)&lb[(s * 2 + hi) * kStepF + tt * 32 + col];
-                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s], bf, acc[tt], 0, 0, 0);
+                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s], bf, s == 0 ? crow : acc[tt], 0, 0, 0);
                 }
             }
-            // partial test of the wave's four blocks
-            const float4 *qo4 = (const float4 *)LQOUTP + wave * 8 + hi;
+            // partial test of the wave's four blocks: a lane's 16 registers
+            // share its column, so the block is live iff some lane's largest
+            // register reaches the lane's column bound
             uint32_t live = 0;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const uint32_t cb = c_begin + st * kStepF + tt * 32;
-                const float xo = cb + col < c_end ? a.kmf * LNXP[buf * kStepF + tt * 32 + col] : __builtin_nanf("");
-                uint64_t nout = 0;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 qo = qo4[g * 2];
-                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 0], xo) <= qo.x);
-                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 1], xo) <= qo.y);
-                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 2], xo) <= qo.z);
-                    nout |= __ballot(fmaf(-2.0f, acc[tt][4 * g + 3], xo) <= qo.w);
-                }
-                if (nout != 0) live |= 1u << tt;
+                const float xb = cb + col < c_end ? filter_col_bound(a.kmf * LNXP[buf * kStepF + tt * 32 + col])
+                                                  : __builtin_nanf("");
+                const floatx16 v = acc[tt];
+                const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+                const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+                const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+                const float m = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15]));
+                if (__ballot(m >= xb) != 0) live |= 1u << tt;
                 else if (cb < c_end) npart += (unsigned long long)nrow_w * min(32u, c_end - cb);
             }
             if (live != 0) {
