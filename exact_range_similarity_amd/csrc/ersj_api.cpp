@@ -1203,6 +1203,10 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
         HIPC(launch_fill_u32(fb.rowcnt, 0, (int64_t)rows, s), "clear row counts");
         timer_start(h, s);
         if (filter) {
+            // unit flags cleared here; the filter zeroes the mask units of
+            // live blocks only
+            const uint64_t words = h->hwords[b + 1] - h->hwords[b];
+            HIPC(launch_fill_u64((uint64_t *)fb.gflag, 0, (int64_t)((words / 4 + 7) / 8), s), "clear unit flags");
             HIPC(launch_filter16(a, h->g16_hh, s), "filter kernel");
             HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
         } else {

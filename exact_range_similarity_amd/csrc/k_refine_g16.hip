@@ -501,8 +501,10 @@ __device__ __forceinline__ float filter_col_bound(float xo) { return xo >= 0x1p-
 // registers, the high halves of its first kPartialDims dimensions, and the
 // item's candidates pass through LDS kStepF at a time (one barrier a step).
 // Each 32 x 32 block gets the partial test; a live block goes to the
-// hand-on list, a settled one keeps zero bits.  The item's mask words are
-// written here as zeros, with their unit flags.
+// hand-on list, a settled one keeps zero bits.  The unit flags of the
+// batch are cleared before the launch; a step with a live block zeroes the
+// 4-word mask unit it covers in the block's rows, the only units whose
+// words the block kernel, the re-check and the compaction touch.
 constexpr int kStepF = 128;
 constexpr int kSlabsF = kPartialDims / 16;
 
@@ -646,16 +648,6 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     // counter as the loads: placed before it, its wait would drain them.
     auto step = [&](uint32_t st, auto odd) __attribute__((always_inline)) {
         const uint32_t buf = st & 1;
-        // the step's mask words, zero, and their unit flags: row tid / 2,
-        // word tid % 2 of the step
-        {
-            const uint32_t row = (uint32_t)tid >> 1, c0 = c_begin + st * kStepF + ((uint32_t)tid & 1u) * 64;
-            if (row < nrows && c0 < c_end) {
-                const uint64_t wi = mbase + (uint64_t)row * W + (c0 >> 6);
-                a.mask[wi] = 0ull;
-                if (((c0 >> 6) & 3u) == 0) a.gflag[wi >> 2] = 0;
-            }
-        }
         if (nrow_w != 0) {
             floatx16 acc[4];
             const uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
@@ -685,6 +677,18 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
                 else if (cb < c_end) npart += (unsigned long long)nrow_w * min(32u, c_end - cb);
             }
             if (live != 0) {
+                // the step's two mask words lie in one 4-word unit of each
+                // row (rows start on 8-word boundaries, steps on 2-word
+                // ones, items on 512-candidate ones); a flagged unit is read
+                // whole, so the unit is zeroed for the wave's rows (lane l:
+                // row l % 32, bytes 16 (l / 32) .. + 15)
+                {
+                    const uint32_t r = (uint32_t)col;
+                    if (r < nrow_w) {
+                        const uint64_t wu = (mbase + (uint64_t)(wave * 32 + r) * W + ((c_begin + st * kStepF) >> 6)) & ~3ull;
+                        ((uint4 *)(a.mask + wu))[hi] = make_uint4(0u, 0u, 0u, 0u);
+                    }
+                }
                 // hand the live blocks on
                 unsigned long long base = 0;
                 if (lane == 0) base = atomicAdd(dc, (unsigned long long)__popc(live));
