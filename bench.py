@@ -75,7 +75,7 @@ def main():
     ap.add_argument("--no-block-prune", action="store_true",
                     help="switch off the MFMA kernel's query-block/candidate-group box test")
     ap.add_argument("--nq", type=int, default=0, help="semi-join query rows (0 = as many as points)")
-    ap.add_argument("--cell-order", type=int, default=0, choices=(0, 1, 2),
+    ap.add_argument("--cell-order", type=int, default=0, choices=(0, 1, 2, 3),
                     help="order of the rows within a cell (0 = the library's choice)")
     ap.add_argument("--mfma-products", type=int, default=0, choices=(0, 1, 3),
                     help="split-fp16 form above 64 dimensions: products per slab (0 = the library's choice)")

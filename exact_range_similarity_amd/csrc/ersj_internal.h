@@ -196,6 +196,24 @@ constexpr int kOrderDims = 8;
 hipError_t launch_cell_order_keys(const float4 *xs, int64_t n, int nb, const uint64_t *cid, int64_t M,
                                   uint32_t *box_lo, uint32_t *box_hi, uint32_t *masks, uint64_t *keys, uint32_t *vals,
                                   hipStream_t s);
+// Balanced tree order of the rows within each cell (k_index.hip): the
+// leaves of a binary tree whose nodes split at 32-row multiples by the
+// dimension of largest sampled variance among the first kTreeDims layout
+// dimensions.  launch_tree_roots makes a node per cell (nstart/nsize [M]),
+// pos = 0..n-1 and *maxsz the largest cell; each launch_tree_level (while
+// *maxsz > kTreeLeaf) sorts pos within the K nodes and writes the next
+// level's nodes (ostart/osize; their count is off[K], off from the counts
+// cnt[K]) and their largest size.  Node arrays hold up to n + 1 entries; k0,
+// k1, v1, hist, stmp as for radix_sort over n rows.  pos ends as the
+// permutation for launch_permute_rows.
+constexpr int kTreeLeaf = 32;
+constexpr int kTreeDims = 64;
+hipError_t launch_tree_roots(const uint32_t *cell_start, int64_t M, uint32_t *nstart, uint32_t *nsize,
+                             uint32_t *pos, int64_t n, uint32_t *maxsz, hipStream_t s);
+hipError_t launch_tree_level(const float4 *xs, int64_t n, int nb, uint32_t *pos, const uint32_t *nstart,
+                             const uint32_t *nsize, uint32_t K, uint32_t *ndim, uint64_t *k0, uint64_t *k1,
+                             uint32_t *v1, uint64_t *hist, uint64_t *stmp, uint32_t *cnt, uint64_t *off,
+                             uint32_t *ostart, uint32_t *osize, uint32_t *maxsz, hipStream_t s);
 hipError_t launch_permute_rows(const float4 *src, const uint32_t *orig_src, const uint32_t *perm, int64_t n, int nb,
                                float4 *dst, uint32_t *orig_dst, hipStream_t s);
 hipError_t launch_point_boxes(const float4 *xs, uint64_t n, int nb, float4 *pbox, hipStream_t s);

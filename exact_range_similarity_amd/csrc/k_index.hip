@@ -14,6 +14,7 @@
 // used to drop neighbour cells is the one of "JZ-tree", Sec. III-B, eq. (15).
 #include "ersj_internal.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cfloat>
 
@@ -549,6 +550,153 @@ __global__ __launch_bounds__(kBlock) void k_permute_rows(const float4 *__restric
     const uint32_t j = perm[i];
     orig_dst[i] = orig_src[j];
     for (int b = 0; b < nb; ++b) dst[(uint64_t)b * n + i] = src[(uint64_t)b * n + j];
+}
+
+// ------------------------------------------------- balanced tree order --
+// Rows of a cell ordered as the leaves of a balanced binary tree, the
+// equal-count grouping of the kd-tree of Sec. IV-B (about the same number of
+// points per leaf).  A node is a run of consecutive rows.  A node of more
+// than kTreeLeaf rows splits into a first child of 32 floor(size / 64) rows
+// (size / 2 below 64) and a second child of the rest, by the rows' values
+// in the node's split dimension: of the first kTreeDims layout dimensions,
+// the one whose values vary most over up to 256 of the node's rows sampled
+// at equal strides.  Children start on 32-row boundaries from the cell's
+// first row, so the refinement's 32-row query blocks are leaves (or
+// sub-runs of the last, smaller ones).  A level is built from a key per row,
+// (node << 32) | the row's value as ordered bits (0 in a leaf), and a stable
+// radix sort of the keys with the rows' cell-order positions.
+
+// one workgroup per node: its split dimension, 0xffffffff for a leaf.
+// Thread t sums dimension t % 64 over samples t / 64, t / 64 + 4, ...,
+// shifted by the first sample's value.
+__global__ __launch_bounds__(kBlock) void k_tree_dims(const float4 *__restrict__ xs, int64_t n, int nb,
+                                                      const uint32_t *__restrict__ pos,
+                                                      const uint32_t *__restrict__ nstart,
+                                                      const uint32_t *__restrict__ nsize,
+                                                      uint32_t *__restrict__ ndim)
+{
+    __shared__ float s1[4][64], s2[4][64];
+    const uint32_t k = blockIdx.x, t = threadIdx.x;
+    const uint32_t st = nstart[k], sz = nsize[k];
+    if (sz <= (uint32_t)kTreeLeaf) {
+        if (t == 0) ndim[k] = 0xffffffffu;
+        return;
+    }
+    const int D = min(4 * nb, kTreeDims);
+    const int a = (int)(t & 63u), g = (int)(t >> 6);
+    const uint32_t m = min(sz, 256u);
+    auto value = [&](uint32_t j) -> float {
+        const uint32_t p = st + (uint32_t)((uint64_t)j * sz / m);
+        const float4 v = xs[(uint64_t)(a >> 2) * (uint64_t)n + pos[p]];
+        const int c = a & 3;
+        return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+    };
+    float a1 = 0.f, a2 = 0.f;
+    if (a < D) {
+        const float sh = value(0);
+        for (uint32_t j = (uint32_t)g; j < m; j += 4) {
+            const float y = value(j) - sh;
+            a1 += y;
+            a2 = fmaf(y, y, a2);
+        }
+    }
+    s1[g][a] = a1;
+    s2[g][a] = a2;
+    __syncthreads();
+    if (t < 64) {
+        const float q1 = s1[0][t] + s1[1][t] + s1[2][t] + s1[3][t];
+        const float q2 = s2[0][t] + s2[1][t] + s2[2][t] + s2[3][t];
+        const float mu = q1 / (float)m;
+        float var = (int)t < D ? q2 / (float)m - mu * mu : -1.0f;
+        if (!(var >= 0.0f)) var = (int)t < D ? 0.0f : -1.0f;  // rounding below 0, or overflow
+        uint32_t best = t;
+        // largest variance, ties to the lower dimension
+        for (int o = 1; o < 64; o <<= 1) {
+            const float ov = __shfl_xor(var, o, 64);
+            const uint32_t ob = (uint32_t)__shfl_xor((int)best, o, 64);
+            if (ov > var || (ov == var && ob < best)) {
+                var = ov;
+                best = ob;
+            }
+        }
+        if (t == 0) ndim[k] = best;
+    }
+}
+
+// key of position p: node k (largest with nstart[k] <= p) in the high word,
+// the row's value in k's split dimension as ordered bits in the low word
+__global__ __launch_bounds__(kBlock) void k_tree_keys(const float4 *__restrict__ xs, int64_t n,
+                                                      const uint32_t *__restrict__ pos,
+                                                      const uint32_t *__restrict__ nstart, uint32_t K,
+                                                      const uint32_t *__restrict__ ndim,
+                                                      uint64_t *__restrict__ keys)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n) return;
+    uint32_t lo = 0, hi = K;  // nstart[lo] <= p < nstart[hi] (nstart[K] taken as n)
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if ((int64_t)nstart[mid] <= p) lo = mid;
+        else hi = mid;
+    }
+    const uint32_t dm = ndim[lo];
+    uint32_t v = 0;
+    if (dm != 0xffffffffu) {
+        const float4 x = xs[(uint64_t)(dm >> 2) * (uint64_t)n + pos[p]];
+        const uint32_t c = dm & 3u;
+        v = f2ord(c == 0 ? x.x : c == 1 ? x.y : c == 2 ? x.z : x.w);
+    }
+    keys[p] = ((uint64_t)lo << 32) | v;
+}
+
+__global__ __launch_bounds__(kBlock) void k_tree_counts(const uint32_t *__restrict__ nsize, uint32_t K,
+                                                        uint32_t *__restrict__ cnt)
+{
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < K) cnt[k] = nsize[k] > (uint32_t)kTreeLeaf ? 2u : 1u;
+}
+
+// the next level's nodes at off[k] (exclusive scan of the counts); the
+// largest next-level size into *maxsz (must hold 0 before)
+__global__ __launch_bounds__(kBlock) void k_tree_next(const uint32_t *__restrict__ nstart,
+                                                      const uint32_t *__restrict__ nsize, uint32_t K,
+                                                      const uint64_t *__restrict__ off,
+                                                      uint32_t *__restrict__ ostart, uint32_t *__restrict__ osize,
+                                                      uint32_t *__restrict__ maxsz)
+{
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= K) return;
+    const uint32_t st = nstart[k], sz = nsize[k];
+    const uint64_t o = off[k];
+    uint32_t big = sz;
+    if (sz > (uint32_t)kTreeLeaf) {
+        const uint32_t h = sz >= 64u ? sz / 64u * 32u : sz / 2u;
+        ostart[o] = st;
+        osize[o] = h;
+        ostart[o + 1] = st + h;
+        osize[o + 1] = sz - h;
+        big = max(h, sz - h);
+    } else {
+        ostart[o] = st;
+        osize[o] = sz;
+    }
+    atomicMax(maxsz, big);
+}
+
+// level 0: a node per cell; the largest cell size into *maxsz (0 before)
+__global__ __launch_bounds__(kBlock) void k_tree_roots(const uint32_t *__restrict__ cell_start, int64_t M,
+                                                       uint32_t *__restrict__ nstart, uint32_t *__restrict__ nsize,
+                                                       uint32_t *__restrict__ pos_identity, int64_t n,
+                                                       uint32_t *__restrict__ maxsz)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) pos_identity[i] = (uint32_t)i;
+    if (i < M) {
+        const uint32_t st = cell_start[i], sz = cell_start[i + 1] - st;
+        nstart[i] = st;
+        nsize[i] = sz;
+        atomicMax(maxsz, sz);
+    }
 }
 
 constexpr int kAabbSteps = 8;  // 64-point steps per wave
@@ -1124,6 +1272,39 @@ hipError_t launch_permute_rows(const float4 *src, const uint32_t *orig_src, cons
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(k_permute_rows, dim3(grid_for(n)), dim3(kBlock), 0, s, src, orig_src, perm, n, nb, dst,
                        orig_dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_roots(const uint32_t *cell_start, int64_t M, uint32_t *nstart, uint32_t *nsize,
+                             uint32_t *pos, int64_t n, uint32_t *maxsz, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(kBlock), 0, s, maxsz, 0u, (int64_t)1);
+    const int64_t m = std::max<int64_t>(n, M);
+    if (m == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_tree_roots, dim3(grid_for(m)), dim3(kBlock), 0, s, cell_start, M, nstart, nsize, pos, n,
+                       maxsz);
+    return hipGetLastError();
+}
+
+hipError_t launch_tree_level(const float4 *xs, int64_t n, int nb, uint32_t *pos, const uint32_t *nstart,
+                             const uint32_t *nsize, uint32_t K, uint32_t *ndim, uint64_t *k0, uint64_t *k1,
+                             uint32_t *v1, uint64_t *hist, uint64_t *stmp, uint32_t *cnt, uint64_t *off,
+                             uint32_t *ostart, uint32_t *osize, uint32_t *maxsz, hipStream_t s)
+{
+    if (n == 0 || K == 0) return hipSuccess;
+    if (K > 0x7fffffffu || (uint64_t)K > (uint64_t)n) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_tree_dims, dim3(K), dim3(kBlock), 0, s, xs, n, nb, pos, nstart, nsize, ndim);
+    hipLaunchKernelGGL(k_tree_keys, dim3(grid_for(n)), dim3(kBlock), 0, s, xs, n, pos, nstart, K, ndim, k0);
+    int kb = 0;
+    while (kb < 32 && (1ull << kb) < (uint64_t)K) ++kb;
+    hipError_t e = radix_sort(k0, pos, k1, v1, n, 32 + kb, hist, stmp, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_tree_counts, dim3(grid_for(K)), dim3(kBlock), 0, s, nsize, K, cnt);
+    e = scan_u32(cnt, off, K, stmp, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(kBlock), 0, s, maxsz, 0u, (int64_t)1);
+    hipLaunchKernelGGL(k_tree_next, dim3(grid_for(K)), dim3(kBlock), 0, s, nstart, nsize, K, off, ostart, osize,
+                       maxsz);
     return hipGetLastError();
 }
 

@@ -97,7 +97,13 @@ typedef struct ersj_options {
                                    order, each of its 24 levels halving the widest remaining
                                    extent, which lets the MFMA kernels' block box test (and above
                                    64 dimensions the split form's partial test) settle more;
-                                   0 = 2 where an MFMA kernel refines, else 1.  Same result. */
+                                   3 = the leaf order of a balanced binary tree (the equal-count
+                                   grouping of the Sec. IV-B kd-tree): each node splits at a
+                                   multiple of 32 rows by the dimension, among the first 64 of the
+                                   variance order, whose values vary most over the node's rows, so
+                                   32-row blocks of clustered data in many dimensions hold few
+                                   clusters; 0 = 3 above 64 dimensions and 2 up to 64 where an MFMA
+                                   kernel refines, else 1.  Same result. */
     int32_t mfma_products;      /* split-fp16 form above 64 dimensions: 3 = the three products
                                    hi.hi + hi.lo + lo.hi of each 16-dimension slab; 1 = hi.hi alone,
                                    a third of the matrix work and half the operand traffic, with a

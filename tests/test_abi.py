@@ -60,7 +60,7 @@ def test_build_rejects_bad_options():
     for reach in (-1, 3):
         o = ersj.default_options(grid_reach=reach)
         assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
-    for order in (-1, 3):
+    for order in (-1, 4):
         o = ersj.default_options(cell_order=order)
         assert build(opt=ctypes.byref(o))[0] == ersj.ERR_INVALID_ARG
         assert "cell_order" in ersj.lib().ersj_last_error().decode()

@@ -173,3 +173,55 @@ def test_cell_order_keeps_pairs_and_prunes_more(name, n):
             f"box-settled {st[order]['skipped_candidates']}")
         assert np.array_equal(got, want), f"{name} cell_order={order}"
     assert st[2]["refined_candidates"] == st[1]["refined_candidates"]
+
+
+@pytest.mark.parametrize("case", ["c5", "rand100", "dups80", "tiny", "one_cell_large"])
+def test_tree_order_keeps_pairs(case):
+    # rows of each cell as the leaves of a balanced tree (cell_order 3, the
+    # default above 64 dimensions) against the 8-dimension kd order (2): the
+    # same pairs; the tree's 32-row blocks of clustered data are purer, so
+    # at least as many comparisons are settled by the partial test
+    rng = np.random.default_rng(len(case))
+    if case == "c5":
+        X = make_config("c5", 6000)
+        eps, _, _ = oracle.calibrate_eps(X, 1000, 50)
+    elif case == "rand100":
+        X = rng.random((3001, 100), dtype=np.float32)
+        eps = 0.33 * math.sqrt(100 / 6.0)
+    elif case == "dups80":
+        # many equal rows and equal values in every dimension: zero sampled
+        # variance in most nodes, ties everywhere in the sort
+        base = rng.integers(0, 3, size=(60, 80)).astype(np.float32)
+        X = base[rng.integers(0, 60, 2500)]
+        eps = 1.5
+    elif case == "tiny":
+        X = rng.random((45, 70), dtype=np.float32)
+        eps = 1.2
+    else:
+        # one cell far larger than the 2^k leaf sizes, ragged at its end
+        X = rng.normal(0.0, 1.0, (5003, 66)).astype(np.float32)
+        eps = 9.0
+    want = np.sort(keys_of(oracle.selfjoin_pairs(X, eps)))
+    st = {}
+    for order in (3, 2):
+        got, st[order] = _join(X, eps, ersj.REFINE_MFMA16, cell_order=order)
+        say(f"[gpu] tree order {case} n={X.shape[0]} d={X.shape[1]} cell_order={order}: {got.size} pairs, "
+            f"settled from 64 dimensions {st[order]['last_partial']}")
+        assert np.array_equal(got, want), f"{case} cell_order={order}"
+    auto, st0 = _join(X, eps, ersj.REFINE_MFMA16)
+    assert np.array_equal(auto, want)
+    assert st0["last_partial"] == st[3]["last_partial"]  # the default above 64 dimensions
+    if case == "c5":
+        assert st[3]["last_partial"] >= st[2]["last_partial"]
+
+
+def test_tree_order_semi_join():
+    X = make_config("c5", 6000)
+    Q = make_queries("c5", 2500, 11, 6000)
+    eps, _, _ = oracle.calibrate_eps(X, 1000, 50)
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    for order in (3, 1):
+        opts = ersj.default_options(cell_order=order)
+        parts = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts)
+        got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+        assert np.array_equal(got, want), order
