@@ -609,13 +609,17 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
         o.r3 = src(lp0 + 3);
         return o;
     };
-    auto deposit = [&](const Ops o, uint32_t buf) __attribute__((always_inline)) {
+    // step st's operands into LDS buffer buf, with each candidate's column
+    // bound (NaN past the item's end: never live)
+    auto deposit = [&](const Ops o, uint32_t buf, uint32_t st) __attribute__((always_inline)) {
         uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
         lb[(lp0 + 0) * kStepF + lc] = o.r0;
         lb[(lp0 + 1) * kStepF + lc] = o.r1;
         lb[(lp0 + 2) * kStepF + lc] = o.r2;
         lb[(lp0 + 3) * kStepF + lc] = o.r3;
-        if (tid < kStepF) LNXP[buf * kStepF + lc] = o.cnp;
+        if (tid < kStepF)
+            LNXP[buf * kStepF + lc] =
+                c_begin + st * kStepF + lc < c_end ? filter_col_bound(a.kmf * o.cnp) : __builtin_nanf("");
     };
     unsigned long long npart = 0;
     uint4 *const dl = a.dlist + (uint64_t)(blockIdx.x % kBandLists) * a.dcap;
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     // that no wait in the loop has to count them
     __builtin_amdgcn_s_waitcnt(0);
     Ops S0 = issue(0), S1 = issue(1);
-    deposit(S0, 0);
+    deposit(S0, 0, 0);
     __syncthreads();
     // the accumulators' start: register v of lane l holds row 8 (v / 4) +
     // v % 4 + 4 (l / 32) of the wave's block
@@ -665,16 +669,25 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
             uint32_t live = 0;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const uint32_t cb = c_begin + st * kStepF + tt * 32;
-                const float xb = cb + col < c_end ? filter_col_bound(a.kmf * LNXP[buf * kStepF + tt * 32 + col])
-                                                  : __builtin_nanf("");
+                const float xb = LNXP[buf * kStepF + tt * 32 + col];
                 const floatx16 v = acc[tt];
                 const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
                 const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
                 const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
                 const float m = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15]));
                 if (__ballot(m >= xb) != 0) live |= 1u << tt;
-                else if (cb < c_end) npart += (unsigned long long)nrow_w * min(32u, c_end - cb);
+            }
+            // comparisons settled here: the step's valid columns less those
+            // of its live blocks
+            {
+                const uint32_t s0 = c_begin + st * kStepF;
+                uint32_t cols = min((uint32_t)kStepF, c_end - s0);
+                if (live != 0) {
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+                        if ((live >> tt) & 1u) cols -= min(32u, c_end - (s0 + tt * 32));
+                }
+                npart += (unsigned long long)nrow_w * cols;
             }
             if (live != 0) {
                 // the step's two mask words lie in one 4-word unit of each
@@ -714,8 +727,8 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
         else S0 = issue(st + 2);
         // deposited on every step (past the end into a buffer nobody reads),
         // for the same reason the loads are issued on every step
-        if constexpr (decltype(odd)::value) deposit(S0, buf ^ 1);
-        else deposit(S1, buf ^ 1);
+        if constexpr (decltype(odd)::value) deposit(S0, buf ^ 1, st + 1);
+        else deposit(S1, buf ^ 1, st + 1);
         __syncthreads();
     };
     // pairs of steps (every trip of the loop passes both, so the waits it
