@@ -146,6 +146,7 @@ struct ersj_index {
     uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
     float *n16 = nullptr, *n16q = nullptr;
     float *np16 = nullptr, *np16q = nullptr;  // their norms over the first kPartialDims dimensions
+    float *xb16 = nullptr;  // the filter's column bound of each point (n + 1)
     // host delivery: two device staging buffers, alternated by batch, drained
     // into the caller's host memory on a copy stream of its own
     hipStream_t copy_stream = nullptr;
@@ -548,6 +549,7 @@ void release_prepared(ersj_index *h)
     if (h->np16q != h->np16) dfree(h, h->np16q);
     h->np16q = nullptr;
     dfree(h, h->np16);
+    dfree(h, h->xb16);
     h->p16q = nullptr;
     h->n16q = nullptr;
     dfree(h, h->p16);
@@ -889,6 +891,8 @@ int prepare_operands(ersj_index *h, hipStream_t s)
     TRY(dalloc(h, &h->np16, (size_t)h->n, "prepared operands"));
     HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->n16, h->np16, s),
          "operand preparation");
+    TRY(dalloc(h, &h->xb16, (size_t)h->n + 1, "prepared operands"));
+    HIPC(launch_col_bounds16(h->np16, (uint64_t)h->n, h->kmf, h->xb16, s), "operand preparation");
     if (h->semi) {
         TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->nq, "prepared operands"));
         TRY(dalloc(h, &h->n16q, (size_t)h->nq, "prepared operands"));
@@ -1174,6 +1178,7 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     a.n16q = h->n16q;
     a.np16 = h->np16;
     a.np16q = h->np16q;
+    a.xb16 = h->xb16;
     a.tref = h->tref;
     const uint64_t rows_items = (uint64_t)ntiles * a.nsub;
     uint32_t seg = 8192;

@@ -343,6 +343,7 @@ struct RefineArgs {
     const uint4 *p16, *p16q;
     const float *n16, *n16q;
     const float *np16, *np16q;
+    const float *xb16;  // k_filter16's column bound of each point, n + 1 entries (the last NaN)
     unsigned long long *partial;  // comparisons decided from those dimensions alone (kHitSlots slots)
     // k_filter16: 32 x 32 blocks still live after that test, handed to
     // k_refine_g16_blocks: kBandLists sub-lists of dcap entries {tile,
@@ -437,6 +438,9 @@ hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
 // filter over the first kPartialDims dimensions: every 32 x 32 block settled
 // there or handed on (a.dlist, required); the batch's mask words zeroed
 hipError_t prepare_filter16();
+// xb[i] = the filter's column bound of point i (from its norm over the
+// first kPartialDims dimensions and 1 - K), xb[n] = NaN
+hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *xb, hipStream_t st);
 hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s);
 // the blocks handed on (a.dlist), after the filter, on the same stream
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s);

@@ -505,22 +505,29 @@ __device__ __forceinline__ float filter_col_bound(float xo) { return xo >= 0x1p-
 // batch are cleared before the launch; a step with a live block zeroes the
 // 4-word mask unit it covers in the block's rows, the only units whose
 // words the block kernel, the re-check and the compaction touch.
+//
+// Operands go from global memory straight into LDS (16 bytes a lane, lane l
+// at the wave's base + 16 l): while a step's MFMAs read one buffer, the next
+// step's operands and column bounds arrive in the other.  Two buffers in
+// separate LDS arrays, the steps in pairs, so that every access names its
+// buffer and the only wait for the loads is the one before the barrier.
 constexpr int kStepF = 128;
 constexpr int kSlabsF = kPartialDims / 16;
 
-struct F16 {
-    static constexpr size_t B = 0;                                          // [2][2 kSlabsF][kStepF] x 16 B
-    static constexpr size_t NXP = B + (size_t)2 * 2 * kSlabsF * kStepF * 16;  // [2][kStepF] f32
-    static constexpr size_t QOUTP = NXP + (size_t)2 * kStepF * 4;           // [kRowsG] f32
-    static constexpr size_t PREF = QOUTP + (size_t)kRowsG * 4;              // [kMaxRanges + 1] u32
-    static constexpr size_t START = PREF + (size_t)(kMaxRanges + 1) * 4;    // [kMaxRanges] u32
-    static constexpr size_t BYTES = START + (size_t)kMaxRanges * 4;
-};
+// xb[i] = filter_col_bound(kmf NP[i]) for the n points, xb[n] = NaN (the
+// bound of a position past a work item's end: never live)
+__global__ __launch_bounds__(256) void k_col_bounds16(const float *__restrict__ NP, uint64_t n, float kmf,
+                                                      float *__restrict__ xb)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) xb[i] = filter_col_bound(kmf * NP[i]);
+    else if (i == n) xb[i] = __builtin_nanf("");
+}
 
 // PP: parts per slab of the prepared arrays (2: high halves only, 4: high
 // and low); the filter reads the high ones
 template <int PP>
-__global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
+__global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
 {
     uint32_t rk, seg;
     work_item(blockIdx.x, a.ntiles, a.nseg, &rk, &seg);
@@ -534,12 +541,12 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     const uint32_t c_end = min(U, c_begin + a.seg_len);
     const uint32_t nrows = min((uint32_t)kRowsG, tl.nrows), row0 = tl.row0;
 
-    extern __shared__ __align__(16) unsigned char smemf[];
-    uint4 *const LB = (uint4 *)(smemf + F16::B);
-    float *const LNXP = (float *)(smemf + F16::NXP);
-    float *const LQOUTP = (float *)(smemf + F16::QOUTP);
-    uint32_t *const LPREF = (uint32_t *)(smemf + F16::PREF);
-    uint32_t *const LSTART = (uint32_t *)(smemf + F16::START);
+    // operand buffers: part p (= 2 slab + half) of candidate c at [p][c];
+    // column bounds at [copy][c] (waves 0-1 and 2-3 each load a copy)
+    __shared__ __align__(16) uint4 LB0[2 * kSlabsF * kStepF], LB1[2 * kSlabsF * kStepF];
+    __shared__ __align__(16) float LX0[2 * kStepF], LX1[2 * kStepF];
+    __shared__ __align__(16) float LQOUTP[kRowsG];
+    __shared__ uint32_t LPREF[kMaxRanges + 1], LSTART[kMaxRanges];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -566,9 +573,10 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
     const uint32_t nsteps = (c_end - c_begin + kStepF - 1) / kStepF;
     __syncthreads();
 
-    // loader: thread tid stages candidate tid % kStepF of the step, parts
-    // 4 (tid / kStepF) .. + 3 (part = 2 slab + half)
-    const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)tid / kStepF) * 4;
+    // loader: lane l of wave w stages candidate lc = 64 (w % 2) + l of the
+    // step, parts 4 (w / 2) .. + 3
+    const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)wave >> 1) * 4;
+    const uint32_t lbase = (uint32_t)(wave & 1) * 64;  // the wave's first candidate
     const uint32_t idx0 = [&]() {
         const int g = range_of(LPREF, nr, c_begin);
         return LSTART[g] + (c_begin - LPREF[g]);
@@ -586,51 +594,31 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
         }
         return LSTART[g] - LPREF[g] + p;
     };
-    // a step's operands in flight, loaded two steps ahead into two register
-    // sets used alternately (named sets: an indexed array ends up in scratch
-    // memory).  The loads are issued on every step (a repeat of the last
-    // step's past the end, never deposited) so that the number in flight is
-    // the same on every path and the wait before a deposit drains only the
-    // older set.
-    struct Ops {
-        uint4 r0, r1, r2, r3;
-        float cnp;
-    };
-    auto issue = [&](uint32_t st) __attribute__((always_inline)) -> Ops {
+    // step st's operands and column bounds into buffer lb / lx: five loads
+    // a lane on every call (a step past the end repeats the last step's
+    // candidates, with NaN bounds, into a buffer nobody reads)
+    auto issue = [&](uint32_t st, uint4 *lb, float *lx) __attribute__((always_inline)) {
         const uint32_t ci = cand_index(st < nsteps ? st : nsteps - 1);
-        Ops o;
-        o.cnp = a.np16[ci];
+        const uint32_t cx = c_begin + st * kStepF + lc < c_end ? ci : (uint32_t)n;
         const uint4 *pc = a.p16 + ci;
-        // part p = 2 slab + half: prepared part slab * PP + half
-        auto src = [&](uint32_t p) { return pc[((uint64_t)(p >> 1) * PP + (p & 1)) * n]; };
-        o.r0 = src(lp0);
-        o.r1 = src(lp0 + 1);
-        o.r2 = src(lp0 + 2);
-        o.r3 = src(lp0 + 3);
-        return o;
-    };
-    // step st's operands into LDS buffer buf, with each candidate's column
-    // bound (NaN past the item's end: never live)
-    auto deposit = [&](const Ops o, uint32_t buf, uint32_t st) __attribute__((always_inline)) {
-        uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
-        lb[(lp0 + 0) * kStepF + lc] = o.r0;
-        lb[(lp0 + 1) * kStepF + lc] = o.r1;
-        lb[(lp0 + 2) * kStepF + lc] = o.r2;
-        lb[(lp0 + 3) * kStepF + lc] = o.r3;
-        if (tid < kStepF)
-            LNXP[buf * kStepF + lc] =
-                c_begin + st * kStepF + lc < c_end ? filter_col_bound(a.kmf * o.cnp) : __builtin_nanf("");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t p = lp0 + (uint32_t)k;
+            __builtin_amdgcn_global_load_lds((const void *)(pc + ((uint64_t)(p >> 1) * PP + (p & 1)) * n),
+                                             (__attribute__((address_space(3))) void *)(lb + p * kStepF + lbase),
+                                             16, 0, 0);
+        }
+        __builtin_amdgcn_global_load_lds((const void *)(a.xb16 + cx),
+                                         (__attribute__((address_space(3))) void *)(lx + (wave >> 1) * kStepF + lbase),
+                                         4, 0, 0);
     };
     unsigned long long npart = 0;
     uint4 *const dl = a.dlist + (uint64_t)(blockIdx.x % kBandLists) * a.dcap;
     unsigned long long *const dc = &a.dcount[(uint64_t)(blockIdx.x % kBandLists) * kBandStride];
 
     if (nsteps == 0) return;
-    // the query fragments arrive before any operand load is in flight, so
-    // that no wait in the loop has to count them
+    issue(0, LB0, LX0);
     __builtin_amdgcn_s_waitcnt(0);
-    Ops S0 = issue(0), S1 = issue(1);
-    deposit(S0, 0, 0);
     __syncthreads();
     // the accumulators' start: register v of lane l holds row 8 (v / 4) +
     // v % 4 + 4 (l / 32) of the wave's block
@@ -646,15 +634,12 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
             crow[4 * g + 3] = c.w;
         }
     }
-    // step st: operands of step st + 2 requested into the set step st was
-    // deposited from (S0 for even st), step st + 1 deposited from the other.
-    // The request follows the hand-on, whose atomic returns through the same
-    // counter as the loads: placed before it, its wait would drain them.
-    auto step = [&](uint32_t st, auto odd) __attribute__((always_inline)) {
-        const uint32_t buf = st & 1;
+    // step st reads (lb, lx) while step st + 1's operands load into (nb, nx)
+    auto step = [&](uint32_t st, const uint4 *lb, const float *lx, uint4 *nb, float *nx)
+                    __attribute__((always_inline)) {
+        issue(st + 1, nb, nx);
         if (nrow_w != 0) {
             floatx16 acc[4];
-            const uint4 *lb = LB + (size_t)buf * 2 * kSlabsF * kStepF;
 #pragma unroll
             for (int s = 0; s < kSlabsF; ++s) {
 #pragma unroll
@@ -669,7 +654,7 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
             uint32_t live = 0;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const float xb = LNXP[buf * kStepF + tt * 32 + col];
+                const float xb = lx[tt * 32 + col];
                 const floatx16 v = acc[tt];
                 const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
                 const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
@@ -723,22 +708,17 @@ __global__ __launch_bounds__(256, 3) void k_filter16(RefineArgs a)
                 }
             }
         }
-        if constexpr (decltype(odd)::value) S1 = issue(st + 2);
-        else S0 = issue(st + 2);
-        // deposited on every step (past the end into a buffer nobody reads),
-        // for the same reason the loads are issued on every step
-        if constexpr (decltype(odd)::value) deposit(S0, buf ^ 1, st + 1);
-        else deposit(S1, buf ^ 1, st + 1);
+        // the next step's operands are in LDS, and every wave is done with
+        // this step's buffer, before the next step starts
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    // pairs of steps (every trip of the loop passes both, so the waits it
-    // needs do not depend on a skipped odd step), then an even tail
     uint32_t st = 0;
     for (; st + 1 < nsteps; st += 2) {
-        step(st, std::integral_constant<bool, false>{});
-        step(st + 1, std::integral_constant<bool, true>{});
+        step(st, LB0, LX0, LB1, LX1);
+        step(st + 1, LB1, LX1, LB0, LX0);
     }
-    if (st < nsteps) step(st, std::integral_constant<bool, false>{});
+    if (st < nsteps) step(st, LB0, LX0, LB1, LX1);
     if (lane == 0 && npart != 0)
         atomicAdd(&a.partial[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], npart);
 }
@@ -923,18 +903,19 @@ hipError_t prepare_refine_g16(bool hh)
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)G16::BYTES);
 }
 
-hipError_t prepare_filter16()
+hipError_t prepare_filter16() { return hipSuccess; }
+
+hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *xb, hipStream_t st)
 {
-    hipError_t e = hipFuncSetAttribute((const void *)k_filter16<2>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)F16::BYTES);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void *)k_filter16<4>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)F16::BYTES);
+    const uint64_t grid = (n + 1 + 255) / 256;
+    if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_col_bounds16, dim3((unsigned)grid), dim3(256), 0, st, np16, n, kmf, xb);
+    return hipGetLastError();
 }
 
 hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
 {
-    if (!a.dlist || !a.np16 || !a.np16q) return hipErrorInvalidValue;
+    if (!a.dlist || !a.np16 || !a.np16q || !a.xb16) return hipErrorInvalidValue;
     if (a.seg_len % kGroupCands != 0) return hipErrorInvalidValue;
     const uint64_t blocks = (uint64_t)a.ntiles * a.nseg;
     if (blocks == 0) return hipSuccess;
@@ -942,7 +923,7 @@ hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
     RefineArgs args = a;
     void *params[] = {&args};
     return hipLaunchKernel(hh ? (const void *)k_filter16<2> : (const void *)k_filter16<4>, dim3((unsigned)blocks),
-                           dim3(256), params, F16::BYTES, s);
+                           dim3(256), params, 0, s);
 }
 
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
