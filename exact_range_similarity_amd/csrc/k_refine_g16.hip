@@ -577,22 +577,29 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     // step, parts 4 (w / 2) .. + 3
     const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)wave >> 1) * 4;
     const uint32_t lbase = (uint32_t)(wave & 1) * 64;  // the wave's first candidate
-    const uint32_t idx0 = [&]() {
-        const int g = range_of(LPREF, nr, c_begin);
-        return LSTART[g] + (c_begin - LPREF[g]);
-    }();
-    uint32_t g_u = 0;
+    // the range of the candidate list holding the step's first position,
+    // kept in scalar registers: [r_lo, r_hi) of the list are points r_st ..
+    uint32_t g_u = (uint32_t)__builtin_amdgcn_readfirstlane(range_of(LPREF, nr, c_begin));
+    uint32_t r_lo = __builtin_amdgcn_readfirstlane(LPREF[g_u]), r_hi = __builtin_amdgcn_readfirstlane(LPREF[g_u + 1]);
+    uint32_t r_st = __builtin_amdgcn_readfirstlane(LSTART[g_u]);
+    const uint32_t idx0 = r_st + (c_begin - r_lo);
     auto cand_index = [&](uint32_t st) __attribute__((always_inline)) -> uint32_t {
         const uint32_t P0 = c_begin + st * kStepF;
-        while (P0 >= (uint32_t)__builtin_amdgcn_readfirstlane(LPREF[g_u + 1])) ++g_u;
-        const uint32_t p = P0 + lc;
-        if (p >= c_end) return idx0;
-        uint32_t g = g_u;
-        const uint32_t nxt = __builtin_amdgcn_readfirstlane(LPREF[g_u + 1]);
-        if (P0 + kStepF > nxt) {
-            while (p >= LPREF[g + 1]) ++g;
+        while (P0 >= r_hi) {
+            ++g_u;
+            r_lo = r_hi;
+            r_hi = __builtin_amdgcn_readfirstlane(LPREF[g_u + 1]);
+            r_st = __builtin_amdgcn_readfirstlane(LSTART[g_u]);
         }
-        return LSTART[g] - LPREF[g] + p;
+        const uint32_t p = P0 + lc;
+        uint32_t ci = r_st - r_lo + p;
+        if (P0 + kStepF > r_hi) {
+            // a step across the end of a range (rare): each lane finds its own
+            uint32_t g = g_u;
+            while (p >= LPREF[g + 1]) ++g;
+            ci = LSTART[g] - LPREF[g] + p;
+        }
+        return p < c_end ? ci : idx0;
     };
     // step st's operands and column bounds into buffer lb / lx: five loads
     // a lane on every call (a step past the end repeats the last step's
