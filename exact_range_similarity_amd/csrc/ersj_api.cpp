@@ -1258,7 +1258,44 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
             const uint64_t words = h->hwords[b + 1] - h->hwords[b];
             HIPC(launch_fill_u64((uint64_t *)fb.gflag, 0, (int64_t)((words / 4 + 7) / 8), s), "clear unit flags");
             HIPC(launch_filter16(a, h->g16_hh, s), "filter kernel");
-            HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
+            // the live blocks, sorted by their candidates' first point, so
+            // that the block kernel's waves on one XCD share candidate
+            // operands in its L2 (a full sub-list sends the batch to the
+            // tiled kernel below, without the block kernel)
+            std::vector<unsigned long long> dh((size_t)kBandLists * kBandStride);
+            HIPC(hipMemcpyAsync(dh.data(), a.dcount, dh.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost, s),
+                 "copy");
+            TRY(sync(s, "filter"));
+            std::vector<uint64_t> pref(kBandLists + 1, 0);
+            bool full = false;
+            for (uint32_t k = 0; k < kBandLists; ++k) {
+                const unsigned long long c = dh[(size_t)k * kBandStride];
+                full |= c > a.dcap;
+                pref[k + 1] = pref[k] + std::min<uint64_t>(c, a.dcap);
+            }
+            const uint64_t total = pref[kBandLists];
+            Scratch stmp(h);
+            a.dorder = nullptr;
+            a.dtotal = 0;
+            if (!full && total > 0 && (uint64_t)kBandLists * a.dcap <= 0xffffffffull) {
+                uint64_t *dpref = nullptr, *k0 = nullptr, *k1 = nullptr, *hist = nullptr, *sc = nullptr;
+                uint32_t *v0 = nullptr, *v1 = nullptr;
+                const size_t hent = radix_hist_entries((int64_t)total);
+                if (stmp.get(&dpref, kBandLists + 1, "block order") == ERSJ_OK &&
+                    stmp.get(&k0, total, "block order") == ERSJ_OK && stmp.get(&k1, total, "block order") == ERSJ_OK &&
+                    stmp.get(&v0, total, "block order") == ERSJ_OK && stmp.get(&v1, total, "block order") == ERSJ_OK &&
+                    stmp.get(&hist, hent, "block order") == ERSJ_OK &&
+                    stmp.get(&sc, scan_tmp_entries((int64_t)hent), "block order") == ERSJ_OK) {
+                    HIPC(hipMemcpyAsync(dpref, pref.data(), sizeof(uint64_t) * pref.size(), hipMemcpyHostToDevice, s),
+                         "copy");
+                    HIPC(launch_handon_keys(a.dlist, a.dcap, dpref, total, k0, v0, s), "block order keys");
+                    HIPC(radix_sort(k0, v0, k1, v1, (int64_t)total, 32, hist, sc, s), "block order sort");
+                    a.dorder = v0;
+                    a.dtotal = total;
+                }
+            }
+            if (!full) HIPC(launch_refine_g16_blocks(a, h->g16_hh, s), "block refine kernel");
+            TRY(sync(s, "block refine"));  // the pref copy and the sort buffers outlive the kernels
         } else {
             HIPC(h->use_g16   ? launch_refine_g16(a, h->g16_hh, s)
                  : h->use_m16 ? launch_refine_m16(a, s)

@@ -356,6 +356,8 @@ struct RefineArgs {
     uint4 *dlist;
     unsigned long long *dcount;
     uint64_t dcap;
+    const uint32_t *dorder;  // k_refine_g16_blocks: entries in this order (dtotal of them), or null
+    uint64_t dtotal;
     // MFMA kernels that centre per row tile: reference of tile t at
     // tref[t * nb .. t * nb + nb - 1] (the first query row of the tile when NULL)
     const float4 *tref;
@@ -436,13 +438,22 @@ hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs
 hipError_t prepare_refine_g16(bool hh);
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
 // filter over the first kPartialDims dimensions: every 32 x 32 block settled
-// there or handed on (a.dlist, required); the batch's mask words zeroed
+// there or handed on (a.dlist, required); the mask units of steps with a
+// live block zeroed (the batch's unit flags must be clear before)
 hipError_t prepare_filter16();
 // xb[i] = the filter's column bound of point i (from its norm over the
 // first kPartialDims dimensions and 1 - K), xb[n] = NaN
 hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *xb, hipStream_t st);
 hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s);
-// the blocks handed on (a.dlist), after the filter, on the same stream
+// sort keys of the total handed-on blocks (pref: device copy of the
+// exclusive prefix of the sub-lists' kept counts, kBandLists + 1 entries):
+// the first point of each block's candidates, with its index in dlist
+// (kBandLists * dcap must fit 32 bits)
+hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, uint64_t *keys,
+                              uint32_t *vals, hipStream_t st);
+// the blocks handed on (a.dlist), after the filter, on the same stream: in
+// the order a.dorder (a.dtotal entries, indices into dlist) when given, else
+// sub-list by sub-list
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s);
 
 // ---- re-check and compaction (k_expand.hip) ----

@@ -730,6 +730,28 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
         atomicAdd(&a.partial[(uint64_t)(blockIdx.x % kHitSlots) * kBandStride], npart);
 }
 
+// Sort keys of the handed-on blocks: entry e of the sub-lists taken in
+// order (pref: exclusive prefix of their kept counts, kBandLists + 1
+// entries) gets key = the point index of its block's first candidate
+// (0xffffffff when the candidates are not consecutive points) and value =
+// its index in dlist.
+__global__ __launch_bounds__(256) void k_handon_keys(const uint4 *__restrict__ dl, uint64_t dcap,
+                                                     const uint64_t *__restrict__ pref, uint64_t total,
+                                                     uint64_t *__restrict__ keys, uint32_t *__restrict__ vals)
+{
+    const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    uint32_t lo = 0, hi = kBandLists;  // largest sub-list k with pref[k] <= e
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (pref[mid] <= e) lo = mid;
+        else hi = mid;
+    }
+    const uint64_t idx = (uint64_t)lo * dcap + (e - pref[lo]);
+    keys[e] = dl[idx].z;
+    vals[e] = (uint32_t)idx;
+}
+
 // One wave per handed-on block (see the file comment).  Grid: kBandLists x
 // kDeferGroups workgroups; workgroup g reads sub-list g % kBandLists.
 constexpr uint32_t kDeferGroups = 16;
@@ -740,10 +762,28 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
     __shared__ __align__(16) float LQO[4][32];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
-    const uint32_t sub = blockIdx.x % kBandLists, j0 = blockIdx.x / kBandLists, nj = gridDim.x / kBandLists;
-    const unsigned long long cnt0 = a.dcount[(uint64_t)sub * kBandStride];
-    const uint64_t cnt = cnt0 < a.dcap ? cnt0 : a.dcap;
-    const uint4 *dl = a.dlist + (uint64_t)sub * a.dcap;
+    // the entries of this workgroup: with a sorted order, chunk c of it,
+    // the chunks of one XCD (workgroups b with the same b % kXcds)
+    // consecutive; else sub-list b % kBandLists, strided over the workgroups
+    // that share it
+    uint64_t e_first, e_end, e_step;
+    const uint4 *dl;
+    if (a.dorder) {
+        const uint32_t G = gridDim.x, per = G / kXcds;
+        const uint64_t len = (a.dtotal + G - 1) / G;
+        const uint64_t c0 = ((uint64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds) * len;
+        e_first = c0 + (uint64_t)wave;
+        e_end = c0 + len < a.dtotal ? c0 + len : a.dtotal;
+        e_step = 4;
+        dl = a.dlist;
+    } else {
+        const uint32_t sub = blockIdx.x % kBandLists, j0 = blockIdx.x / kBandLists, nj = gridDim.x / kBandLists;
+        const unsigned long long cnt0 = a.dcount[(uint64_t)sub * kBandStride];
+        e_first = (uint64_t)j0 * 4 + wave;
+        e_end = cnt0 < a.dcap ? cnt0 : a.dcap;
+        e_step = (uint64_t)nj * 4;
+        dl = a.dlist + (uint64_t)sub * a.dcap;
+    }
     const uint64_t n = a.n, nqr = a.nqr;
     const int nsl = HH ? 2 * (((a.nb + 3) / 4 + 1) / 2) : (a.nb + 3) / 4;  // slabs (high parts: padded even)
     const int pp = HH ? 2 : 4;                                            // parts per slab
@@ -755,8 +795,8 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
     struct Chunk {
         uint4 fa[kChunk], fb[kChunk], ga[kChunk], gb[kChunk];
     };
-    for (uint64_t e = (uint64_t)j0 * 4 + wave; e < cnt; e += (uint64_t)nj * 4) {
-        const uint4 ent = dl[e];
+    for (uint64_t e = e_first; e < e_end; e += e_step) {
+        const uint4 ent = a.dorder ? dl[a.dorder[e]] : dl[e];
         const uint32_t t = ent.x, rb = ent.y & 3u, c0 = (ent.y >> 2) << 5;
         const Tile tl = a.tiles[t];
         const uint32_t nrows = min((uint32_t)kTileRows, tl.nrows);
@@ -931,6 +971,17 @@ hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
     void *params[] = {&args};
     return hipLaunchKernel(hh ? (const void *)k_filter16<2> : (const void *)k_filter16<4>, dim3((unsigned)blocks),
                            dim3(256), params, 0, s);
+}
+
+hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, uint64_t *keys,
+                              uint32_t *vals, hipStream_t st)
+{
+    if (total == 0) return hipSuccess;
+    if ((uint64_t)kBandLists * dcap > 0xffffffffull) return hipErrorInvalidValue;
+    const uint64_t grid = (total + 255) / 256;
+    if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_handon_keys, dim3((unsigned)grid), dim3(256), 0, st, dl, dcap, pref, total, keys, vals);
+    return hipGetLastError();
 }
 
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
