@@ -633,32 +633,44 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
     HIPC(launch_cell_scatter(k0, 3 * h->gp.sub, flags, cid, n, out->cell_start, out->cell_key, s), "cell scatter");
     TRY(dalloc(h, &out->xs, (size_t)h->nb * n, "points"));
     if (h->box_order) {
-        // rows gathered in cell order first, then each cell's rows re-sorted
-        // by their code in the cell's box (midpoint splits of the widest
-        // extent) and moved into place
+        // rows gathered in cell order (up to 64 dimensions all of them,
+        // above only the first kOrderDims), each cell's rows re-sorted by
+        // their code in the cell's box (midpoint splits of the widest
+        // extent), then moved (or, above 64 dimensions, gathered again) into
+        // that order
+        const bool wide = d > 64;
+        const int nbw = wide ? std::min(h->nb, kOrderDims / 4) : h->nb;
         float4 *xs1 = nullptr;
         uint32_t *blo = nullptr, *bhi = nullptr, *bmask = nullptr, *orig1 = nullptr, *pos = nullptr;
-        TRY(tmp.get(&xs1, (size_t)h->nb * n, "cell order"));
+        TRY(tmp.get(&xs1, (size_t)nbw * n, "cell order"));
         TRY(tmp.get(&blo, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&bhi, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&bmask, (size_t)M * kOrderDims, "cell order"));
         TRY(tmp.get(&orig1, (size_t)n, "cell order"));
         TRY(tmp.get(&pos, (size_t)n, "cell order"));
-        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, xs1, s), "gather kernel");
-        HIPC(launch_cell_order_keys(xs1, n, h->nb, cid, (int64_t)M, blo, bhi, bmask, k0, pos, s),
+        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, nbw, xs1, s), "gather kernel");
+        HIPC(launch_cell_order_keys(xs1, n, std::min(nbw, kOrderDims / 4), cid, (int64_t)M, blo, bhi, bmask, k0, pos, s),
              "cell order kernels");
         HIPC(radix_sort(k0, pos, k1, v1, n, 24 + ceil_log2(M + 1), hist, stmp, s), "cell order sort");
         HIPC(hipMemcpyAsync(orig1, out->orig, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s), "copy");
-        HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
+        if (wide) {
+            HIPC(launch_permute_rows(nullptr, orig1, pos, n, 0, nullptr, out->orig, s), "row order");
+            HIPC(launch_gather(x, n, d, ld, out->orig, dperm, h->nb, out->xs, s), "gather kernel");
+        } else {
+            HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
+        }
     } else if (h->tree_order) {
-        // rows gathered in cell order first, then each cell's rows sorted
-        // level by level into the leaf order of a balanced tree and moved
-        // into place
+        // rows gathered in cell order (up to 64 dimensions all of them,
+        // above only the first kTreeDims), each cell's rows sorted level by
+        // level into the leaf order of a balanced tree, then moved (or,
+        // above 64 dimensions, gathered again) into that order
+        const bool wide = d > 64;
+        const int nbw = wide ? std::min(h->nb, kTreeDims / 4) : h->nb;
         float4 *xs1 = nullptr;
         uint32_t *orig1 = nullptr, *pos = nullptr, *ndim = nullptr, *cnt = nullptr, *maxsz = nullptr;
         uint32_t *nst[2] = {nullptr, nullptr}, *nsz[2] = {nullptr, nullptr};
         uint64_t *off = nullptr;
-        TRY(tmp.get(&xs1, (size_t)h->nb * n, "tree order"));
+        TRY(tmp.get(&xs1, (size_t)nbw * n, "tree order"));
         TRY(tmp.get(&orig1, (size_t)n, "tree order"));
         TRY(tmp.get(&pos, (size_t)n, "tree order"));
         for (int k = 0; k < 2; ++k) {
@@ -669,7 +681,7 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
         TRY(tmp.get(&cnt, (size_t)n + 1, "tree order"));
         TRY(tmp.get(&off, (size_t)n + 2, "tree order"));
         TRY(tmp.get(&maxsz, 1, "tree order"));
-        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, xs1, s), "gather kernel");
+        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, nbw, xs1, s), "gather kernel");
         HIPC(launch_tree_roots(out->cell_start, (int64_t)M, nst[0], nsz[0], pos, n, maxsz, s), "tree roots");
         uint32_t big = 0;
         HIPC(hipMemcpyAsync(&big, maxsz, sizeof big, hipMemcpyDeviceToHost, s), "copy");
@@ -679,7 +691,7 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
         // every split leaves both children smaller than their parent
         for (int level = 0; big > (uint32_t)kTreeLeaf; ++level) {
             if (level >= 64 || K > (uint64_t)n) return fail(ERSJ_ERR_INTERNAL, "tree order did not converge");
-            HIPC(launch_tree_level(xs1, n, h->nb, pos, nst[cur], nsz[cur], (uint32_t)K, ndim, k0, k1, v1, hist, stmp,
+            HIPC(launch_tree_level(xs1, n, std::min(nbw, kTreeDims / 4), pos, nst[cur], nsz[cur], (uint32_t)K, ndim, k0, k1, v1, hist, stmp,
                                    cnt, off, nst[cur ^ 1], nsz[cur ^ 1], maxsz, s),
                  "tree level");
             HIPC(hipMemcpyAsync(&K, off + K, sizeof K, hipMemcpyDeviceToHost, s), "copy");
@@ -688,9 +700,14 @@ int bin_rows(ersj_index *h, const float *x, int64_t n, int64_t ld, bool queries,
             cur ^= 1;
         }
         HIPC(hipMemcpyAsync(orig1, out->orig, sizeof(uint32_t) * n, hipMemcpyDeviceToDevice, s), "copy");
-        HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
+        if (wide) {
+            HIPC(launch_permute_rows(nullptr, orig1, pos, n, 0, nullptr, out->orig, s), "row order");
+            HIPC(launch_gather(x, n, d, ld, out->orig, dperm, h->nb, out->xs, s), "gather kernel");
+        } else {
+            HIPC(launch_permute_rows(xs1, orig1, pos, n, h->nb, out->xs, out->orig, s), "row permute kernel");
+        }
     } else {
-        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, out->xs, s), "gather kernel");
+        HIPC(launch_gather(x, n, d, ld, out->orig, dperm, h->nb, out->xs, s), "gather kernel");
     }
     // row-major copy in sorted order for the binary64 re-check, which sums
     // in the input's dimension order

@@ -154,8 +154,10 @@ size_t radix_hist_entries(int64_t n);
 hipError_t radix_sort(uint64_t *k0, uint32_t *v0, uint64_t *k1, uint32_t *v1, int64_t n, int bits,
                       uint64_t *hist, uint64_t *scan_tmp, hipStream_t s);
 
+// rows orig[i] of x into the dimension-blocked layout xs (n rows per
+// block, layout dimension k = input dimension perm[k]), blocks [0, nbw)
 hipError_t launch_gather(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
-                         const int32_t *perm, float4 *xs, hipStream_t s);
+                         const int32_t *perm, int nbw, float4 *xs, hipStream_t s);
 
 // Exclusive scan: out[i] = sum in[0..i), out[n] = total.  tmp needs
 // scan_tmp_entries(n) u64.

@@ -358,25 +358,87 @@ hipError_t scan_impl(const T *in, uint64_t *out, int64_t n, uint64_t *tmp, hipSt
 }
 
 // ---------------------------------------------------------------- gather --
-__global__ __launch_bounds__(kBlock) void k_gather(const float *__restrict__ x, int64_t n, int32_t d,
-                                                   int64_t ld, const uint32_t *__restrict__ orig,
-                                                   const int32_t *__restrict__ perm,
-                                                   float4 *__restrict__ xs)
+// Rows orig[i] of x (row-major, stride ld) into the dimension-blocked,
+// variance-ordered layout: block b of row i holds input dimensions
+// perm[4b .. 4b + 3] (0 past d).
+//
+// Narrow rows (up to 64 dimensions): a thread per output row, its blocks
+// in turn (the row's few cache lines serve all of them).
+__global__ __launch_bounds__(kBlock) void k_gather_narrow(const float *__restrict__ x, int64_t n, int32_t d,
+                                                          int64_t ld, const uint32_t *__restrict__ orig,
+                                                          const int32_t *__restrict__ perm, int nbw,
+                                                          float4 *__restrict__ xs)
 {
-    __shared__ int32_t sp[kMaxDim + 4];
-    const int nb = (d + 3) / 4;
-    for (int k = threadIdx.x; k < nb * 4; k += blockDim.x) sp[k] = k < d ? perm[k] : -1;
+    __shared__ int32_t sp[64];
+    for (int k = threadIdx.x; k < 64; k += blockDim.x) sp[k] = k < d ? perm[k] : -1;
     __syncthreads();
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
     const float *row = x + (int64_t)orig[i] * ld;
-    for (int b = 0; b < nb; ++b) {
+    for (int b = 0; b < nbw; ++b) {
         float4 v;
         v.x = sp[4 * b + 0] >= 0 ? row[sp[4 * b + 0]] : 0.0f;
         v.y = sp[4 * b + 1] >= 0 ? row[sp[4 * b + 1]] : 0.0f;
         v.z = sp[4 * b + 2] >= 0 ? row[sp[4 * b + 2]] : 0.0f;
         v.w = sp[4 * b + 3] >= 0 ? row[sp[4 * b + 3]] : 0.0f;
         xs[(int64_t)b * n + i] = v;
+    }
+}
+
+// Wider rows: a workgroup takes gather_rows_per_group(d)
+// consecutive output rows: their input rows are read whole into LDS (each
+// row's floats by consecutive threads), then every block of the rows is
+// written as consecutive float4 of the rows (LDS row stride d + 1 floats,
+// odd, so that threads reading one dimension of consecutive rows hit
+// distinct banks).  Only blocks [0, nbw) are written.
+constexpr int kGatherLds = 12288;  // floats of LDS for the staged rows
+__host__ __device__ inline int gather_rows_per_group(int32_t d)
+{
+    const int r = kGatherLds / (d + 1);
+    return r > kBlock ? kBlock : (r < 1 ? 1 : r);
+}
+
+__global__ __launch_bounds__(kBlock) void k_gather(const float *__restrict__ x, int64_t n, int32_t d,
+                                                   int64_t ld, const uint32_t *__restrict__ orig,
+                                                   const int32_t *__restrict__ perm, int nbw,
+                                                   float4 *__restrict__ xs)
+{
+    __shared__ float sx[kGatherLds];
+    const int R = gather_rows_per_group(d), ldl = d + 1;
+    const int64_t r0 = (int64_t)blockIdx.x * R;
+    const int rows = (int)(n - r0 < R ? n - r0 : R);
+    const int tid = threadIdx.x;
+    if (d >= 128) {
+        for (int r = 0; r < rows; ++r) {
+            const float *row = x + (int64_t)orig[r0 + r] * ld;
+            for (int k = tid; k < d; k += kBlock) sx[r * ldl + k] = row[k];
+        }
+    } else {
+        // rows * d < 12288: element idx is dimension idx - r d of row r
+        const float rd = 1.0f / (float)d;
+        for (int idx = tid; idx < rows * d; idx += kBlock) {
+            int r = (int)((float)idx * rd);
+            r = r * d > idx ? r - 1 : r;
+            r = (r + 1) * d <= idx ? r + 1 : r;
+            const int k = idx - r * d;
+            sx[r * ldl + k] = x[(int64_t)orig[r0 + r] * ld + k];
+        }
+    }
+    __syncthreads();
+    // thread tid: row tid % Rp of the group, blocks tid / Rp + j (256 / Rp)
+    // (Rp: R rounded up to a power of two)
+    int Rp = 1;
+    while (Rp < R) Rp <<= 1;
+    const int r = tid & (Rp - 1), bstep = kBlock / Rp;
+    if (r >= rows) return;
+    for (int b = tid / Rp; b < nbw; b += bstep) {
+        float c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int k = 4 * b + q;
+            c[q] = k < d ? sx[r * ldl + perm[k]] : 0.0f;
+        }
+        xs[(int64_t)b * n + r0 + r] = make_float4(c[0], c[1], c[2], c[3]);
     }
 }
 
@@ -1309,9 +1371,18 @@ hipError_t launch_tree_level(const float4 *xs, int64_t n, int nb, uint32_t *pos,
 }
 
 hipError_t launch_gather(const float *x, int64_t n, int32_t d, int64_t ld, const uint32_t *orig,
-                         const int32_t *perm, float4 *xs, hipStream_t s)
+                         const int32_t *perm, int nbw, float4 *xs, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, d, ld, orig, perm, xs);
+    if (n == 0 || nbw <= 0) return hipSuccess;
+    if (d < 1 || d > kMaxDim || nbw > (d + 3) / 4) return hipErrorInvalidValue;
+    if (d <= 64) {
+        hipLaunchKernelGGL(k_gather_narrow, dim3(grid_for(n)), dim3(kBlock), 0, s, x, n, d, ld, orig, perm, nbw, xs);
+        return hipGetLastError();
+    }
+    const int R = gather_rows_per_group(d);
+    const int64_t groups = (n + R - 1) / R;
+    if (groups > 0x7fffffffll) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_gather, dim3((unsigned)groups), dim3(kBlock), 0, s, x, n, d, ld, orig, perm, nbw, xs);
     return hipGetLastError();
 }
 
