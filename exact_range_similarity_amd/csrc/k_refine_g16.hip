@@ -762,19 +762,21 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
     __shared__ __align__(16) float LQO[4][32];
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
-    // the entries of this workgroup: with a sorted order, chunk c of it,
-    // the chunks of one XCD (workgroups b with the same b % kXcds)
-    // consecutive; else sub-list b % kBandLists, strided over the workgroups
-    // that share it
+    // the entries of this wave: with a sorted order, XCD x (workgroups b
+    // with b % kXcds = x) takes the x-th eighth of it, swept by all its
+    // waves together (the grid is what the device holds at once, so the
+    // waves of an XCD work on a window of consecutive entries and share
+    // candidate operands in its L2); else sub-list b % kBandLists, strided
+    // over the workgroups that share it
     uint64_t e_first, e_end, e_step;
     const uint4 *dl;
     if (a.dorder) {
-        const uint32_t G = gridDim.x, per = G / kXcds;
-        const uint64_t len = (a.dtotal + G - 1) / G;
-        const uint64_t c0 = ((uint64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds) * len;
-        e_first = c0 + (uint64_t)wave;
-        e_end = c0 + len < a.dtotal ? c0 + len : a.dtotal;
-        e_step = 4;
+        const uint32_t per = gridDim.x / kXcds, x = blockIdx.x % kXcds;
+        const uint64_t len = (a.dtotal + kXcds - 1) / kXcds;
+        const uint64_t x0 = (uint64_t)x * len;
+        e_first = x0 + (uint64_t)(blockIdx.x / kXcds) * 4 + (uint64_t)wave;
+        e_end = x0 + len < a.dtotal ? x0 + len : a.dtotal;
+        e_step = (uint64_t)per * 4;
         dl = a.dlist;
     } else {
         const uint32_t sub = blockIdx.x % kBandLists, j0 = blockIdx.x / kBandLists, nj = gridDim.x / kBandLists;
@@ -987,7 +989,14 @@ hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pr
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
 {
     if (!a.dlist || a.dcap == 0) return hipSuccess;
-    const dim3 grid(kBandLists * kDeferGroups);
+    // sorted order: as many workgroups as the device holds at once (three
+    // per CU), a multiple of kXcds
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const uint32_t resident = ((uint32_t)cus * 3 + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid(a.dorder ? resident : kBandLists * kDeferGroups);
     if (hh) hipLaunchKernelGGL(k_refine_g16_blocks<true>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_refine_g16_blocks<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
