@@ -144,6 +144,7 @@ struct ersj_index {
     std::vector<double> mean;  // per input dimension (binary64 statistics of the points)
     float4 *tref = nullptr;  // per row tile: reference point of the MFMA kernels' centring
     uint4 *p16 = nullptr, *p16q = nullptr;  // prepared operands of points and query rows
+    uint64_t ps16 = 0, ps16q = 0;           // their part strides
     float *n16 = nullptr, *n16q = nullptr;
     float *np16 = nullptr, *np16q = nullptr;  // their norms over the first kPartialDims dimensions
     float *xb16 = nullptr;  // the filter's column bound of each point (n + 1)
@@ -903,21 +904,25 @@ int prepare_operands(ersj_index *h, hipStream_t s)
     float4 *dnrs = nullptr;
     TRY(tmp.get(&dnrs, (size_t)nb, "operand preparation"));
     HIPC(hipMemcpyAsync(dnrs, nrs.data(), sizeof(float) * nrs.size(), hipMemcpyHostToDevice, s), "copy");
-    TRY(dalloc(h, &h->p16, (size_t)ns * 4 * (size_t)h->n, "prepared operands"));
+    h->ps16 = prep16_stride((uint64_t)h->n);
+    TRY(dalloc(h, &h->p16, (size_t)ns * 4 * (size_t)h->ps16, "prepared operands"));
     TRY(dalloc(h, &h->n16, (size_t)h->n, "prepared operands"));
     TRY(dalloc(h, &h->np16, (size_t)h->n, "prepared operands"));
-    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->n16, h->np16, s),
+    HIPC(launch_prep16(h->xs, (uint64_t)h->n, nb, dnrs, h->s16, h->g16_hh, h->p16, h->ps16, h->n16, h->np16, s),
          "operand preparation");
     TRY(dalloc(h, &h->xb16, (size_t)h->n + 1, "prepared operands"));
     HIPC(launch_col_bounds16(h->np16, (uint64_t)h->n, h->kmf, h->xb16, s), "operand preparation");
     if (h->semi) {
-        TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->nq, "prepared operands"));
+        h->ps16q = prep16_stride((uint64_t)h->nq);
+        TRY(dalloc(h, &h->p16q, (size_t)ns * 4 * (size_t)h->ps16q, "prepared operands"));
         TRY(dalloc(h, &h->n16q, (size_t)h->nq, "prepared operands"));
         TRY(dalloc(h, &h->np16q, (size_t)h->nq, "prepared operands"));
-        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->g16_hh, h->p16q, h->n16q, h->np16q, s),
+        HIPC(launch_prep16(h->xq, (uint64_t)h->nq, nb, dnrs, h->s16, h->g16_hh, h->p16q, h->ps16q, h->n16q,
+                           h->np16q, s),
              "operand preparation");
     } else {
         h->p16q = h->p16;
+        h->ps16q = h->ps16;
         h->n16q = h->n16;
         h->np16q = h->np16;
     }
@@ -1191,6 +1196,8 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     a.nsub = h->use_m16 || h->use_g16 ? 1u : (uint32_t)(kTileRows / (mfma ? 32 * refine_mfma_qblocks(h->nb) : 32));
     a.p16 = h->p16;
     a.p16q = h->p16q;
+    a.ps = h->ps16;
+    a.psq = h->ps16q;
     a.n16 = h->n16;
     a.n16q = h->n16q;
     a.np16 = h->np16;
@@ -1305,8 +1312,13 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
                     stmp.get(&sc, scan_tmp_entries((int64_t)hent), "block order") == ERSJ_OK) {
                     HIPC(hipMemcpyAsync(dpref, pref.data(), sizeof(uint64_t) * pref.size(), hipMemcpyHostToDevice, s),
                          "copy");
-                    HIPC(launch_handon_keys(a.dlist, a.dcap, dpref, total, k0, v0, s), "block order keys");
-                    HIPC(radix_sort(k0, v0, k1, v1, (int64_t)total, 32, hist, sc, s), "block order sort");
+                    // key bits: the query block (tile << 2 | block) below
+                    // the 1024-point group of the first candidate
+                    const int qbits = std::max(2, ceil_log2((uint64_t)h->T * 4));
+                    const uint32_t gend = (uint32_t)((uint64_t)h->n >> 10) + 1;
+                    const int kbits = qbits + ceil_log2((uint64_t)gend + 1);
+                    HIPC(launch_handon_keys(a.dlist, a.dcap, dpref, total, qbits, gend, k0, v0, s), "block order keys");
+                    HIPC(radix_sort(k0, v0, k1, v1, (int64_t)total, kbits, hist, sc, s), "block order sort");
                     a.dorder = v0;
                     a.dtotal = total;
                 }

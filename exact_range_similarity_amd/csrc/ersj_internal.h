@@ -343,6 +343,7 @@ struct RefineArgs {
     // query rows, [slabs][4 parts][rows] x 16 bytes, their norms and their
     // norms over the first kPartialDims dimensions of the layout
     const uint4 *p16, *p16q;
+    uint64_t ps, psq;  // their part strides (uint4 elements, prep16_stride of n and nqr)
     const float *n16, *n16q;
     const float *np16, *np16q;
     const float *xb16;  // k_filter16's column bound of each point, n + 1 entries (the last NaN)
@@ -423,8 +424,8 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 
 // k_refine_g16.hip: split-fp16 refinement for nb > 16 on operands prepared by
 // launch_prep16 (rows of xs centred by -nrs / s, scaled by s, split; N n
-// floats; P needs g16_stages(nb, hh) * 4 * n uint4); nsub = 1, seg_len a
-// multiple of 512.  hh: high halves only (one product per slab, the wider
+// floats; P needs g16_stages(nb, hh) * 4 * ps uint4, part k of row i at
+// P[k * ps + i], ps = prep16_stride(n)); nsub = 1, seg_len a multiple of 512.  hh: high halves only (one product per slab, the wider
 // band of the high-part form), for both calls alike.
 // k_refine_g16 and k_filter16 test every 32 x 32 block after the first
 // kPartialDims dimensions: the squared distance over a subset of the
@@ -435,8 +436,9 @@ inline int g16_stages(int nb, bool hh)
     const int ns = (nb + 3) / 4;
     return hh ? (ns + 1) / 2 : ns;
 }
+uint64_t prep16_stride(uint64_t n);
 hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
-                         float *N, float *NP, hipStream_t st);
+                         uint64_t ps, float *N, float *NP, hipStream_t st);
 hipError_t prepare_refine_g16(bool hh);
 hipError_t launch_refine_g16(const RefineArgs &a, bool hh, hipStream_t s);
 // filter over the first kPartialDims dimensions: every 32 x 32 block settled
@@ -449,10 +451,12 @@ hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *
 hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s);
 // sort keys of the total handed-on blocks (pref: device copy of the
 // exclusive prefix of the sub-lists' kept counts, kBandLists + 1 entries):
-// the first point of each block's candidates, with its index in dlist
-// (kBandLists * dcap must fit 32 bits)
-hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, uint64_t *keys,
-                              uint32_t *vals, hipStream_t st);
+// (first candidate point >> 10, gend for a block whose candidates are not
+// consecutive points) << qbits | (tile << 2 | query block), qbits covering
+// 4 x the tile count, with each entry's index in dlist (kBandLists * dcap
+// must fit 32 bits)
+hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, int qbits,
+                              uint32_t gend, uint64_t *keys, uint32_t *vals, hipStream_t st);
 // the blocks handed on (a.dlist), after the filter, on the same stream: in
 // the order a.dorder (a.dtotal entries, indices into dlist) when given, else
 // sub-list by sub-list

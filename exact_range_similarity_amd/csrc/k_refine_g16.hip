@@ -95,7 +95,7 @@ struct G16 {
 // each slab, an odd slab count padded with one zero slab.
 __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, uint64_t n, int nb, int ns,
                                                 const float4 *__restrict__ nrs, float s, bool hh,
-                                                uint4 *__restrict__ P, float *__restrict__ N,
+                                                uint4 *__restrict__ P, uint64_t ps, float *__restrict__ N,
                                                 float *__restrict__ NP)
 {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -131,18 +131,18 @@ __global__ __launch_bounds__(256) void k_prep16(const float4 *__restrict__ xs, u
         }
         if (sl * 16 + 16 == kPartialDims) NP[i] = nrm;
         if (hh) {
-            P[((uint64_t)sl * 2 + 0) * n + i] = *(const uint4 *)&h0;
-            P[((uint64_t)sl * 2 + 1) * n + i] = *(const uint4 *)&h1;
+            P[((uint64_t)sl * 2 + 0) * ps + i] = *(const uint4 *)&h0;
+            P[((uint64_t)sl * 2 + 1) * ps + i] = *(const uint4 *)&h1;
         } else {
-            P[((uint64_t)sl * 4 + 0) * n + i] = *(const uint4 *)&h0;
-            P[((uint64_t)sl * 4 + 1) * n + i] = *(const uint4 *)&h1;
-            P[((uint64_t)sl * 4 + 2) * n + i] = *(const uint4 *)&l0;
-            P[((uint64_t)sl * 4 + 3) * n + i] = *(const uint4 *)&l1;
+            P[((uint64_t)sl * 4 + 0) * ps + i] = *(const uint4 *)&h0;
+            P[((uint64_t)sl * 4 + 1) * ps + i] = *(const uint4 *)&h1;
+            P[((uint64_t)sl * 4 + 2) * ps + i] = *(const uint4 *)&l0;
+            P[((uint64_t)sl * 4 + 3) * ps + i] = *(const uint4 *)&l1;
         }
     }
     if (hh && (ns & 1)) {
-        P[((uint64_t)ns * 2 + 0) * n + i] = make_uint4(0u, 0u, 0u, 0u);
-        P[((uint64_t)ns * 2 + 1) * n + i] = make_uint4(0u, 0u, 0u, 0u);
+        P[((uint64_t)ns * 2 + 0) * ps + i] = make_uint4(0u, 0u, 0u, 0u);
+        P[((uint64_t)ns * 2 + 1) * ps + i] = make_uint4(0u, 0u, 0u, 0u);
     }
     N[i] = nrm;
 }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256, 2) void k_refine_g16(RefineArgs a)
     uint64_t *const LWORDS = (uint64_t *)(smemg + G::WORDS);
 
     const int tid = threadIdx.x;
-    const uint64_t n = a.n, nqr = a.nqr;
+    const uint64_t n = a.ps, nqr = a.psq;  // part strides of the prepared arrays
     const uint4 *__restrict__ P = a.p16;
     const uint4 *__restrict__ PQ = a.p16q;
     const float *__restrict__ NP = a.n16;
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, col = lane & 31, hi = lane >> 5;
-    const uint64_t n = a.n, nqr = a.nqr;
+    const uint64_t ps = a.ps, psq = a.psq;  // part strides of the prepared arrays
     if (tid <= kMaxRanges) LPREF[tid] = tid <= (int)nr ? pref_g[tid] : 0xffffffffu;
     if (tid < kMaxRanges) LSTART[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
     if (tid < kRowsG) {
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     half8 af[kSlabsF];
 #pragma unroll
     for (int s = 0; s < kSlabsF; ++s) {
-        const uint4 v = a.p16q[((uint64_t)s * PP + hi) * nqr + q];
+        const uint4 v = a.p16q[((uint64_t)s * PP + hi) * psq + q];
         af[s] = *(const half8 *)&v;
     }
     const uint64_t mbase = a.toff[t] - a.wbase;
@@ -606,12 +606,12 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     // candidates, with NaN bounds, into a buffer nobody reads)
     auto issue = [&](uint32_t st, uint4 *lb, float *lx) __attribute__((always_inline)) {
         const uint32_t ci = cand_index(st < nsteps ? st : nsteps - 1);
-        const uint32_t cx = c_begin + st * kStepF + lc < c_end ? ci : (uint32_t)n;
+        const uint32_t cx = c_begin + st * kStepF + lc < c_end ? ci : (uint32_t)a.n;
         const uint4 *pc = a.p16 + ci;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t p = lp0 + (uint32_t)k;
-            __builtin_amdgcn_global_load_lds((const void *)(pc + ((uint64_t)(p >> 1) * PP + (p & 1)) * n),
+            __builtin_amdgcn_global_load_lds((const void *)(pc + ((uint64_t)(p >> 1) * PP + (p & 1)) * ps),
                                              (__attribute__((address_space(3))) void *)(lb + p * kStepF + lbase),
                                              16, 0, 0);
         }
@@ -732,12 +732,16 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
 
 // Sort keys of the handed-on blocks: entry e of the sub-lists taken in
 // order (pref: exclusive prefix of their kept counts, kBandLists + 1
-// entries) gets key = the point index of its block's first candidate
-// (0xffffffff when the candidates are not consecutive points) and value =
-// its index in dlist.
+// entries) gets key = (the group of 1024 points holding its block's first
+// candidate, gend when the candidates are not consecutive points) << qbits
+// | (tile << 2 | query block), and value = its index in dlist.  In
+// that order a group's candidate blocks (768 KB of operands at d = 384)
+// serve every query block live against them while that query block's
+// entries are consecutive.
 __global__ __launch_bounds__(256) void k_handon_keys(const uint4 *__restrict__ dl, uint64_t dcap,
-                                                     const uint64_t *__restrict__ pref, uint64_t total,
-                                                     uint64_t *__restrict__ keys, uint32_t *__restrict__ vals)
+                                                     const uint64_t *__restrict__ pref, uint64_t total, int qbits,
+                                                     uint32_t gend, uint64_t *__restrict__ keys,
+                                                     uint32_t *__restrict__ vals)
 {
     const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= total) return;
@@ -748,8 +752,82 @@ __global__ __launch_bounds__(256) void k_handon_keys(const uint4 *__restrict__ d
         else hi = mid;
     }
     const uint64_t idx = (uint64_t)lo * dcap + (e - pref[lo]);
-    keys[e] = dl[idx].z;
+    const uint4 ent = dl[idx];
+    const uint32_t grp = ent.z == 0xffffffffu ? gend : ent.z >> 10;
+    keys[e] = ((uint64_t)grp << qbits) | ((uint64_t)ent.x << 2 | (ent.y & 3u));
     vals[e] = (uint32_t)idx;
+}
+
+// The end of a handed-on block's refinement (k_refine_g16_blocks and
+// k_refine_g16_runs): classification of its accumulated 32 x 32 block
+// against the row thresholds this wave wrote to lqi / lqo (register v of
+// lane l: row 8 (v / 4) + v % 4 + 4 (l / 32), column l % 32, the rules of
+// classify_block), band pairs to the band list, bits ORed into the mask
+// words with their unit flags and row counts.
+__device__ __forceinline__ void g16_block_finish(const RefineArgs &a, const floatx16 &acc, uint32_t t,
+                                                 const Tile &tl, uint32_t rb, uint32_t c0, uint32_t r, bool vr,
+                                                 bool vc, uint32_t ci, float nx, const float *lqi,
+                                                 const float *lqo)
+{
+    const int lane = threadIdx.x & 63, col = lane & 31, hi = lane >> 5;
+    // the row thresholds written by this wave's lanes are read by all
+    // of its lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // one 32 x 32 block: register v of lane l holds row 8 (v / 4) + v % 4
+    // + 4 (l / 32), column l % 32 (the rules of classify_block)
+    const float xin = vc ? a.kp * nx : __builtin_nanf(""), xout = vc ? a.km * nx : __builtin_nanf("");
+    int wbits = 0;  // lane r < 32: the block's 32 bits of row r
+    uint64_t band = 0;
+    static_for(std::make_integer_sequence<int, 16>{}, [&](auto V) {
+        constexpr int v = decltype(V)::value, i0 = 8 * (v / 4) + v % 4;
+        const int row = i0 + 4 * hi;
+        const float d2 = acc[v];
+        const uint64_t bin = __ballot(fmaf(-2.0f, d2, xin) <= lqi[row]);
+        const uint64_t bno = __ballot(fmaf(-2.0f, d2, xout) <= lqo[row]);
+        band |= bno & ~bin;
+        wbits = write_lane<i0>(wbits, (uint32_t)bin);
+        wbits = write_lane<i0 + 4>(wbits, (uint32_t)(bin >> 32));
+    });
+    const uint64_t mbase = a.toff[t] - a.wbase;
+    if (band != 0) {
+        // rare: the band pairs, appended for the binary64 re-check
+        Boundary *bl = band_list(a.blist, a.lcap);
+        unsigned long long *bc = band_counter(a.bcount);
+#pragma unroll 1
+        for (int v = 0; v < 16; ++v) {
+            const int row = 8 * (v >> 2) + (v & 3) + 4 * hi;
+            const float d2 = acc[v];
+            const bool bd = !(fmaf(-2.0f, d2, xin) <= lqi[row]) && fmaf(-2.0f, d2, xout) <= lqo[row];
+            const uint64_t bb = __ballot(bd);
+            if (bb == 0) continue;
+            const int first = __ffsll((unsigned long long)bb) - 1;
+            unsigned long long base = 0;
+            if (lane == first) base = atomicAdd(bc, (unsigned long long)__popcll(bb));
+            base = __shfl(base, first, 64);
+            if (bd) {
+                const uint64_t below = lane == 0 ? 0ull : (bb & (~0ull >> (64 - lane)));
+                const uint64_t idx = base + __popcll(below);
+                if (idx < a.lcap) {
+                    Boundary e;
+                    e.q = tl.row0 + rb * 32 + (uint32_t)row;
+                    e.x = ci;
+                    e.bit = (mbase + (uint64_t)(rb * 32 + row) * tl.words) * 64 + c0 + (uint32_t)col;
+                    bl[idx] = e;
+                }
+            }
+        }
+    }
+    const uint64_t w = (uint64_t)(uint32_t)wbits << (c0 & 32u);
+    if (lane < 32) {
+        if (w != 0 && vr) {
+            const uint64_t wi = mbase + (uint64_t)r * tl.words + (c0 >> 6);
+            atomicOr((unsigned long long *)&a.mask[wi], (unsigned long long)w);
+            a.gflag[wi >> 2] = 1;
+            atomicAdd(&a.rowcnt[tl.row0 + r - a.row_base], (uint32_t)__popcll(w));
+        }
+    }
 }
 
 // One wave per handed-on block (see the file comment).  Grid: kBandLists x
@@ -786,7 +864,7 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
         e_step = (uint64_t)nj * 4;
         dl = a.dlist + (uint64_t)sub * a.dcap;
     }
-    const uint64_t n = a.n, nqr = a.nqr;
+    const uint64_t n = a.ps, nqr = a.psq;  // part strides of the prepared arrays
     const int nsl = HH ? 2 * (((a.nb + 3) / 4 + 1) / 2) : (a.nb + 3) / 4;  // slabs (high parts: padded even)
     const int pp = HH ? 2 : 4;                                            // parts per slab
     // slabs whose operands are loaded together; the next chunk's loads are
@@ -868,81 +946,133 @@ __global__ __launch_bounds__(256, 3) void k_refine_g16_blocks(RefineArgs a)
             }
             X = Y;
         }
-        // the row thresholds written by this wave's lanes are read by all
-        // of its lanes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // one 32 x 32 block: register v of lane l holds row 8 (v / 4) + v % 4
-        // + 4 (l / 32), column l % 32 (the rules of classify_block)
-        const float xin = vc ? a.kp * nx : __builtin_nanf(""), xout = vc ? a.km * nx : __builtin_nanf("");
-        int wbits = 0;  // lane r < 32: the block's 32 bits of row r
-        uint64_t band = 0;
-        static_for(std::make_integer_sequence<int, 16>{}, [&](auto V) {
-            constexpr int v = decltype(V)::value, i0 = 8 * (v / 4) + v % 4;
-            const int row = i0 + 4 * hi;
-            const float d2 = acc[v];
-            const uint64_t bin = __ballot(fmaf(-2.0f, d2, xin) <= LQI[wave][row]);
-            const uint64_t bno = __ballot(fmaf(-2.0f, d2, xout) <= LQO[wave][row]);
-            band |= bno & ~bin;
-            wbits = write_lane<i0>(wbits, (uint32_t)bin);
-            wbits = write_lane<i0 + 4>(wbits, (uint32_t)(bin >> 32));
-        });
-        const uint64_t mbase = a.toff[t] - a.wbase;
-        if (band != 0) {
-            // rare: the band pairs, appended for the binary64 re-check
-            Boundary *bl = band_list(a.blist, a.lcap);
-            unsigned long long *bc = band_counter(a.bcount);
-#pragma unroll 1
-            for (int v = 0; v < 16; ++v) {
-                const int row = 8 * (v >> 2) + (v & 3) + 4 * hi;
-                const float d2 = acc[v];
-                const bool bd = !(fmaf(-2.0f, d2, xin) <= LQI[wave][row]) && fmaf(-2.0f, d2, xout) <= LQO[wave][row];
-                const uint64_t bb = __ballot(bd);
-                if (bb == 0) continue;
-                const int first = __ffsll((unsigned long long)bb) - 1;
-                unsigned long long base = 0;
-                if (lane == first) base = atomicAdd(bc, (unsigned long long)__popcll(bb));
-                base = __shfl(base, first, 64);
-                if (bd) {
-                    const uint64_t below = lane == 0 ? 0ull : (bb & (~0ull >> (64 - lane)));
-                    const uint64_t idx = base + __popcll(below);
-                    if (idx < a.lcap) {
-                        Boundary e;
-                        e.q = tl.row0 + rb * 32 + (uint32_t)row;
-                        e.x = ci;
-                        e.bit = (mbase + (uint64_t)(rb * 32 + row) * tl.words) * 64 + c0 + (uint32_t)col;
-                        bl[idx] = e;
-                    }
-                }
-            }
-        }
-        const uint64_t w = (uint64_t)(uint32_t)wbits << (c0 & 32u);
-        if (lane < 32) {
-            if (w != 0 && vr) {
-                const uint64_t wi = mbase + (uint64_t)r * tl.words + (c0 >> 6);
-                atomicOr((unsigned long long *)&a.mask[wi], (unsigned long long)w);
-                a.gflag[wi >> 2] = 1;
-                atomicAdd(&a.rowcnt[tl.row0 + r - a.row_base], (uint32_t)__popcll(w));
-            }
-        }
+        g16_block_finish(a, acc, t, tl, rb, c0, r, vr, vc, ci, nx, LQI[wave], LQO[wave]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 }
 
+// The sorted hand-on list in the high-half form up to 24 slabs (384
+// dimensions): each wave takes runs of kRunLen consecutive entries of its
+// XCD's eighth of the order (the XCD's waves on consecutive runs, so that
+// they share candidate operands in its L2).  The sort key puts the entries
+// of one query block next to each other, so the wave keeps that block's
+// fragments of every slab in registers and loads them again only when the
+// query block changes; the candidate fragments stream through a ring of
+// three registers, two slabs ahead.  NS: slabs held (8, 16 or 24, at
+// least the operands' slab count; loads past the last slab repeat it and
+// their MFMAs are skipped).
+constexpr uint32_t kRunLen = 16;
+template <int NS>
+__global__ __launch_bounds__(256, NS > 16 ? 2 : 3) void k_refine_g16_runs(RefineArgs a)
+{
+    __shared__ __align__(16) float LQI[4][32];
+    __shared__ __align__(16) float LQO[4][32];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 31, hi = lane >> 5;
+    const uint32_t per = gridDim.x / kXcds, xcd = blockIdx.x % kXcds;
+    const uint64_t len = (a.dtotal + kXcds - 1) / kXcds;
+    const uint64_t x0 = (uint64_t)xcd * len, x1 = x0 + len < a.dtotal ? x0 + len : a.dtotal;
+    const uint64_t gw = (uint64_t)(blockIdx.x / kXcds) * 4 + (uint64_t)wave, nw = (uint64_t)per * 4;
+    const uint64_t n = a.ps, nqr = a.psq;  // part strides of the prepared arrays
+    const int nsl = 2 * (((a.nb + 3) / 4 + 1) / 2);  // slabs of high halves (padded even), <= NS
+    half8 qf[NS];
+    uint32_t qkey = 0xffffffffu;
+    for (uint64_t r0 = x0 + gw * kRunLen; r0 < x1; r0 += nw * kRunLen) {
+        const uint64_t r1 = r0 + kRunLen < x1 ? r0 + kRunLen : x1;
+        for (uint64_t e = r0; e < r1; ++e) {
+            const uint4 ent = a.dlist[a.dorder[e]];
+            const uint32_t t = ent.x, rb = ent.y & 3u, c0 = (ent.y >> 2) << 5;
+            const Tile tl = a.tiles[t];
+            const uint32_t nrows = min((uint32_t)kTileRows, tl.nrows);
+            const uint32_t r = rb * 32 + (uint32_t)col;
+            const bool vr = r < nrows;
+            const uint32_t q = tl.row0 + (vr ? r : nrows - 1);
+            const uint32_t p = c0 + (uint32_t)col;
+            const bool vc = (uint32_t)col < ent.w;
+            uint32_t ci;
+            if (ent.z != 0xffffffffu) {
+                ci = ent.z + (vc ? (uint32_t)col : 0u);  // consecutive points
+            } else {
+                // the lane's candidate: range g with pref[g] <= p < pref[g + 1]
+                const uint32_t A = tl.cell, nr = a.nrng[A];
+                const uint32_t *pref = a.rpref + (uint64_t)A * (kMaxRanges + 1);
+                uint32_t g = 0;
+                if (vc) {
+                    uint32_t lo = 0, up = nr;
+                    while (up - lo > 1) {
+                        const uint32_t mid = (lo + up) >> 1;
+                        if (pref[mid] <= p) lo = mid;
+                        else up = mid;
+                    }
+                    g = lo;
+                }
+                ci = a.rstart[(uint64_t)A * kMaxRanges + g] + (vc ? p - pref[g] : 0u);
+            }
+            const uint32_t key = t << 2 | rb;
+            if (key != qkey) {
+                // a new query block: its fragments and row thresholds
+                qkey = key;
+                const uint4 *pq = a.p16q + (uint64_t)hi * nqr + q;
+                // (non-temporal: a query block is read once per run and
+                // would only push candidate operands out of L2)
+                static_for(std::make_integer_sequence<int, NS>{}, [&](auto S) {
+                    constexpr int sl = decltype(S)::value;
+                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+                    const u32x4 v = __builtin_nontemporal_load(
+                        (const u32x4 *)(pq + (uint64_t)(sl < nsl ? sl : nsl - 1) * 2 * nqr));
+                    qf[sl] = *(const half8 *)&v;
+                });
+                if (lane < 32) {
+                    const float nq = a.n16q[q];
+                    LQI[wave][col] = vr ? a.tlo - a.kp * nq - a.tabs : -INFINITY;
+                    LQO[wave][col] = vr ? a.thi - a.km * nq + a.tabs : -INFINITY;
+                }
+            }
+            const float nx = a.n16[ci];
+            const uint4 *pc = a.p16 + (uint64_t)hi * n + ci;
+            auto cload = [&](int sl) __attribute__((always_inline)) {
+                return pc[(uint64_t)(sl < nsl ? sl : nsl - 1) * 2 * n];
+            };
+            uint4 ring[3];
+            ring[0] = cload(0);
+            ring[1] = cload(1);
+            floatx16 acc = {};
+            static_for(std::make_integer_sequence<int, NS>{}, [&](auto S) {
+                constexpr int sl = decltype(S)::value;
+                ring[(sl + 2) % 3] = cload(sl + 2);
+                if (sl < nsl)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[sl], *(const half8 *)&ring[sl % 3], acc, 0, 0, 0);
+            });
+            g16_block_finish(a, acc, t, tl, rb, c0, r, vr, vc, ci, nx, LQI[wave], LQO[wave]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+}
+
 }  // namespace
 
+uint64_t prep16_stride(uint64_t n)
+{
+    // an odd number of 4 KiB pieces plus 128 bytes: the same row of
+    // consecutive parts falls in different L2 channels and sets (a stride of
+    // a power of two times 4 KiB put a block's 48 part lines in one set)
+    const uint64_t units = (n + 511) / 512;  // 512 x 16 B = 8 KiB
+    return (2 * units + 1) * 256 + 8;
+}
+
 hipError_t launch_prep16(const float4 *xs, uint64_t n, int nb, const float4 *nrs, float s, bool hh, uint4 *P,
-                         float *N, float *NP, hipStream_t st)
+                         uint64_t ps, float *N, float *NP, hipStream_t st)
 {
     if (n == 0) return hipSuccess;
-    if (4 * nb <= kPartialDims) return hipErrorInvalidValue;
+    if (4 * nb <= kPartialDims || ps < n) return hipErrorInvalidValue;
     const int ns = (nb + 3) / 4;
     const uint64_t grid = (n + 255) / 256;
     if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, hh, P, N, NP);
+    hipLaunchKernelGGL(k_prep16, dim3((unsigned)grid), dim3(256), 0, st, xs, n, nb, ns, nrs, s, hh, P, ps, N, NP);
     return hipGetLastError();
 }
 
@@ -975,20 +1105,22 @@ hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
                            dim3(256), params, 0, s);
 }
 
-hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, uint64_t *keys,
-                              uint32_t *vals, hipStream_t st)
+hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, int qbits,
+                              uint32_t gend, uint64_t *keys, uint32_t *vals, hipStream_t st)
 {
     if (total == 0) return hipSuccess;
-    if ((uint64_t)kBandLists * dcap > 0xffffffffull) return hipErrorInvalidValue;
+    if ((uint64_t)kBandLists * dcap > 0xffffffffull || qbits < 2 || qbits > 40) return hipErrorInvalidValue;
     const uint64_t grid = (total + 255) / 256;
     if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(k_handon_keys, dim3((unsigned)grid), dim3(256), 0, st, dl, dcap, pref, total, keys, vals);
+    hipLaunchKernelGGL(k_handon_keys, dim3((unsigned)grid), dim3(256), 0, st, dl, dcap, pref, total, qbits, gend,
+                       keys, vals);
     return hipGetLastError();
 }
 
 hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
 {
     if (!a.dlist || a.dcap == 0) return hipSuccess;
+    const int nsl = 2 * (((a.nb + 3) / 4 + 1) / 2);
     // sorted order: as many workgroups as the device holds at once (three
     // per CU), a multiple of kXcds
     int dev = 0, cus = 0;
@@ -996,6 +1128,16 @@ hipError_t launch_refine_g16_blocks(const RefineArgs &a, bool hh, hipStream_t s)
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const uint32_t resident = ((uint32_t)cus * 3 + kXcds - 1) / kXcds * kXcds;
+    if (a.dorder && hh && nsl <= 24) {
+        // runs with the query block held in registers (24 slabs: two
+        // workgroups per CU, the registers of three)
+        if (a.dtotal == 0) return hipSuccess;
+        const uint32_t two = ((uint32_t)cus * 2 + kXcds - 1) / kXcds * kXcds;
+        if (nsl <= 8) hipLaunchKernelGGL(k_refine_g16_runs<8>, dim3(resident), dim3(256), 0, s, a);
+        else if (nsl <= 16) hipLaunchKernelGGL(k_refine_g16_runs<16>, dim3(resident), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_refine_g16_runs<24>, dim3(two), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid(a.dorder ? resident : kBandLists * kDeferGroups);
     if (hh) hipLaunchKernelGGL(k_refine_g16_blocks<true>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_refine_g16_blocks<false>, grid, dim3(256), 0, s, a);
