@@ -200,11 +200,15 @@ def main():
     # 64 dimensions and on prepared operands above; the fp32 MFMA form; the
     # direct form
     nb = (d + 3) // 4
+    # above 64 dimensions the filter hands live blocks to the run kernel
+    # (high halves, up to 24 slabs of 16 dimensions) or the block kernel
+    nsl = 2 * (((nb + 3) // 4 + 1) // 2)
+    second = "k_refine_g16_runs" if prods == 1 and nsl <= 24 else "k_refine_g16_blocks"
     kname = ("k_refine_m16" if nb <= 16 else
-             "k_filter16+k_refine_g16_blocks" if st["last_filtered"] else "k_refine_g16") if f16 else \
+             f"k_filter16+{second}" if st["last_filtered"] else "k_refine_g16") if f16 else \
         "k_refine_mfma" if mfma else "k_refine_direct"
     traffic = None
-    tname = "filter16_blocks" if "+" in kname else kname[2:]
+    tname = ("filter16_" + second.split("_")[-1]) if "+" in kname else kname[2:]
     tfile = os.path.join(ROOT, "profiles", f"{tname}_{args.workload}_traffic.json")
     if os.path.exists(tfile):
         import hashlib
