@@ -53,7 +53,8 @@ class Options(ctypes.Structure):
                 ("cell_width_scale", ctypes.c_double), ("max_device_bytes", ctypes.c_uint64),
                 ("boundary_capacity", ctypes.c_uint64), ("timing", ctypes.c_int32),
                 ("grid_reach", ctypes.c_int32), ("block_prune", ctypes.c_int32),
-                ("cell_order", ctypes.c_int32), ("mfma_products", ctypes.c_int32)]
+                ("cell_order", ctypes.c_int32), ("mfma_products", ctypes.c_int32),
+                ("filter_bits", ctypes.c_int32)]
 
 
 class Stats(ctypes.Structure):
@@ -72,7 +73,7 @@ class Stats(ctypes.Structure):
                 ("n_queries", ctypes.c_int64), ("last_skipped", ctypes.c_uint64),
                 ("skipped_candidates", ctypes.c_uint64), ("mfma_products", ctypes.c_int32),
                 ("last_partial", ctypes.c_uint64), ("partial_candidates", ctypes.c_uint64),
-                ("last_filtered", ctypes.c_int32)]
+                ("last_filtered", ctypes.c_int32), ("filter_bits", ctypes.c_int32)]
 
     def as_dict(self):
         out = {}

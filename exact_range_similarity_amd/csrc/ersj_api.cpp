@@ -148,6 +148,11 @@ struct ersj_index {
     float *n16 = nullptr, *n16q = nullptr;
     float *np16 = nullptr, *np16q = nullptr;  // their norms over the first kPartialDims dimensions
     float *xb16 = nullptr;  // the filter's column bound of each point (n + 1)
+    // the filter's int8 form (null: the fp16 form): operands of points and
+    // query rows, part strides, column bounds (n + 1) and row starts
+    uint4 *p8 = nullptr, *p8q = nullptr;
+    uint64_t ps8 = 0, ps8q = 0;
+    int *xb8 = nullptr, *qs8 = nullptr;
     // host delivery: two device staging buffers, alternated by batch, drained
     // into the caller's host memory on a copy stream of its own
     hipStream_t copy_stream = nullptr;
@@ -555,6 +560,11 @@ void release_prepared(ersj_index *h)
     h->n16q = nullptr;
     dfree(h, h->p16);
     dfree(h, h->n16);
+    if (h->p8q != h->p8) dfree(h, h->p8q);
+    h->p8q = nullptr;
+    dfree(h, h->p8);
+    dfree(h, h->xb8);
+    dfree(h, h->qs8);
 }
 
 void release_count(ersj_index *h)
@@ -895,6 +905,54 @@ void release_queries(ersj_index *h)
 // Split-fp16 operands of the points and the query rows for k_refine_g16:
 // centred on the points' per-dimension mean r (fp32, in the layout's
 // variance order; padded dimensions 0), scaled by s16, split, with norms.
+// The d > 64 filter's int8 operands (k_refine_g16.hip derives the test):
+// centred on the layout's means as fp32, scaled by S = 127 / M, M the largest
+// |x_i - r_i| over the first kPartialDims dimensions of both point sets,
+// raised by 2^-20 over its fp32 evaluation; E the squared radius widened by
+// the binary64 reference's rounding.  Left unset (the fp16 form runs) when
+// M is not finite and positive.
+int prepare_int8_filter(ersj_index *h, hipStream_t s)
+{
+    std::vector<float> ref(kPartialDims);
+    for (int j = 0; j < kPartialDims; ++j) ref[j] = (float)h->mean[h->perm[j]];
+    Scratch tmp(h);
+    float4 *dref = nullptr;
+    unsigned int *dmx = nullptr;
+    TRY(tmp.get(&dref, (size_t)kPartialDims / 4, "int8 filter operands"));
+    TRY(tmp.get(&dmx, 1, "int8 filter operands"));
+    HIPC(hipMemcpyAsync(dref, ref.data(), sizeof(float) * ref.size(), hipMemcpyHostToDevice, s), "copy");
+    HIPC(hipMemsetAsync(dmx, 0, sizeof(unsigned int), s), "clear");
+    HIPC(launch_maxabs8(h->xs, (uint64_t)h->n, dref, dmx, s), "int8 filter operands");
+    if (h->semi) HIPC(launch_maxabs8(h->xq, (uint64_t)h->nq, dref, dmx, s), "int8 filter operands");
+    unsigned int bits = 0;
+    HIPC(hipMemcpyAsync(&bits, dmx, sizeof bits, hipMemcpyDeviceToHost, s), "copy");
+    TRY(sync(s, "int8 filter operands"));
+    float mf = 0.0f;
+    std::memcpy(&mf, &bits, sizeof mf);
+    const double M = (double)mf * (1.0 + std::ldexp(1.0, -20));
+    if (!(M > 0.0) || !std::isfinite(M)) return ERSJ_OK;
+    const double S = 127.0 / M;
+    const double g = std::max(std::ldexp(1.0, -30), 4.0 * gamma_n(h->d + 2, std::ldexp(1.0, -53)));
+    const double E = std::isinf(h->e64) ? INFINITY : h->e64 * (1.0 + g);
+    h->ps8 = prep16_stride((uint64_t)h->n);
+    TRY(dalloc(h, &h->p8, (size_t)4 * (size_t)h->ps8, "int8 filter operands"));
+    TRY(dalloc(h, &h->xb8, (size_t)h->n + 1, "int8 filter operands"));
+    TRY(dalloc(h, &h->qs8, (size_t)h->nq, "int8 filter operands"));
+    HIPC(launch_prep8(h->xs, (uint64_t)h->n, dref, S, E, h->p8, h->ps8, h->semi ? nullptr : h->qs8, h->xb8, s),
+         "int8 filter operands");
+    if (h->semi) {
+        h->ps8q = prep16_stride((uint64_t)h->nq);
+        TRY(dalloc(h, &h->p8q, (size_t)4 * (size_t)h->ps8q, "int8 filter operands"));
+        HIPC(launch_prep8(h->xq, (uint64_t)h->nq, dref, S, E, h->p8q, h->ps8q, h->qs8, nullptr, s),
+             "int8 filter operands");
+    } else {
+        h->p8q = h->p8;
+        h->ps8q = h->ps8;
+    }
+    TRY(sync(s, "int8 filter operands"));  // ref and dref must outlive the kernels
+    return ERSJ_OK;
+}
+
 int prepare_operands(ersj_index *h, hipStream_t s)
 {
     const int nb = h->nb, ns = g16_stages(nb, h->g16_hh);
@@ -927,6 +985,7 @@ int prepare_operands(ersj_index *h, hipStream_t s)
         h->np16q = h->np16;
     }
     TRY(sync(s, "operand preparation"));  // the host copy of nrs and dnrs must outlive the kernels
+    if (h->opt.filter_bits != 16) TRY(prepare_int8_filter(h, s));
     return ERSJ_OK;
 }
 
@@ -1203,6 +1262,14 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
     a.np16 = h->np16;
     a.np16q = h->np16q;
     a.xb16 = h->xb16;
+    if (h->p8) {
+        a.p8 = h->p8;
+        a.p8q = h->p8q;
+        a.ps8 = h->ps8;
+        a.ps8q = h->ps8q;
+        a.xb8 = h->xb8;
+        a.qs8 = h->qs8;
+    }
     a.tref = h->tref;
     const uint64_t rows_items = (uint64_t)ntiles * a.nsub;
     uint32_t seg = 8192;
@@ -1682,6 +1749,8 @@ int ersj_build_index(const float *d_x, int64_t n, int32_t d, int64_t ld, double 
             return fail(ERSJ_ERR_INVALID_ARG, "cell_order must be 0, 1, 2 or 3 (got %d)", o.cell_order);
         if (o.mfma_products != 0 && o.mfma_products != 1 && o.mfma_products != 3)
             return fail(ERSJ_ERR_INVALID_ARG, "mfma_products must be 0, 1 or 3 (got %d)", o.mfma_products);
+        if (o.filter_bits != 0 && o.filter_bits != 8 && o.filter_bits != 16)
+            return fail(ERSJ_ERR_INVALID_ARG, "filter_bits must be 0, 8 or 16 (got %d)", o.filter_bits);
     }
     int dev = 0;
     HIPC(hipGetDevice(&dev), "hipGetDevice");
@@ -1959,6 +2028,7 @@ int ersj_get_stats(const ersj_index *h, ersj_stats *o)
     o->mfma_products = h->kernel_used != ERSJ_REFINE_MFMA16 ? 0 : h->g16_hh ? 1 : 3;
     o->last_partial = h->last_part;
     o->last_filtered = h->last_filtered ? 1 : 0;
+    o->filter_bits = h->p8 ? 8 : h->use_g16 ? 16 : 0;
     o->partial_candidates = h->partial_cand;
     return ERSJ_OK;
 }

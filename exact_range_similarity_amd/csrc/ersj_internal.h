@@ -347,6 +347,13 @@ struct RefineArgs {
     const float *n16, *n16q;
     const float *np16, *np16q;
     const float *xb16;  // k_filter16's column bound of each point, n + 1 entries (the last NaN)
+    // the filter's int8 form (k_prep8; all four set, or all null for the
+    // fp16 form): points' and query rows' operands [4 parts][rows] x 16
+    // bytes with part strides ps8, ps8q; column bounds (n + 1 entries, the
+    // last INT_MAX) and row starts
+    const uint4 *p8, *p8q;
+    uint64_t ps8, ps8q;
+    const int *xb8, *qs8;
     unsigned long long *partial;  // comparisons decided from those dimensions alone (kHitSlots slots)
     // k_filter16: 32 x 32 blocks still live after that test, handed to
     // k_refine_g16_blocks: kBandLists sub-lists of dcap entries {tile,
@@ -448,6 +455,14 @@ hipError_t prepare_filter16();
 // xb[i] = the filter's column bound of point i (from its norm over the
 // first kPartialDims dimensions and 1 - K), xb[n] = NaN
 hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *xb, hipStream_t st);
+// the filter's int8 form: mx = bits of max |x_i - ref_i| over the first
+// kPartialDims dimensions (fp32; maxed into *mx, which starts at 0); the
+// operands of a point set scaled by S (|x_i - ref_i| S <= 127 for all rows),
+// row starts (start, may be null) and column bounds (bound, n + 1 entries,
+// may be null) against squared radius E; P needs 4 * ps uint4, ps >= n
+hipError_t launch_maxabs8(const float4 *xs, uint64_t n, const float4 *ref, unsigned int *mx, hipStream_t st);
+hipError_t launch_prep8(const float4 *xs, uint64_t n, const float4 *ref, double S, double E, uint4 *P, uint64_t ps,
+                        int *start, int *bound, hipStream_t st);
 hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s);
 // sort keys of the total handed-on blocks (pref: device copy of the
 // exclusive prefix of the sub-lists' kept counts, kBandLists + 1 entries):

@@ -63,6 +63,9 @@
 // stored with that half-word zero), with the unit flags and row counts.
 #include "refine_mfma_common.h"
 
+#include <climits>
+#include <type_traits>
+
 namespace ersj {
 
 namespace {
@@ -524,11 +527,105 @@ __global__ __launch_bounds__(256) void k_col_bounds16(const float *__restrict__ 
     else if (i == n) xb[i] = __builtin_nanf("");
 }
 
+// Integer form of the partial test.  Over the first kPartialDims dimensions
+// of the layout, d_i = x_i - r_i (r: the layout's means as fp32, the same
+// for both point sets) rounds to q_i = rint(S d_i), S = 127 / M with M at
+// least every |d_i| of both sets, so |q_i| <= 127 and d_i = q_i / S + e_i
+// with |e_i| <= D = (1/2 + 2^-30) / S (the fp64 product S d_i is within
+// 2^-46 of exact).  For two points, with N the exact squared norm of d and
+// A = sum |q_i| of each,
+//   |dq - dx|^2 = Nq + Nx - 2 dq.dx
+//              >= Nq + Nx - 2 sum qq_i qx_i / S^2 - 2 D (Aq + Ax) / S - 128 D^2,
+// since dq.dx = sum (qq_i / S + eq_i)(qx_i / S + ex_i).  The pair's squared
+// distance exceeds E (and it is no neighbour) when, with T = S^2 / 2,
+//   sum qq_i qx_i < T (Nq - 2 D Aq / S - 64 D^2 - E) + T (Nx - 2 D Ax / S - 64 D^2).
+// The row term, evaluated in fp64, lowered by a relative 2^-40 of its
+// magnitude and 2, and rounded down, is negated into the int32 accumulator's
+// start (qs8); the column term, lowered the same way and rounded down, is
+// the bound (xb8).  The int8 MFMA's sum is exact, so a block whose every
+// accumulator stays below its column's bound is settled.  Ranges: the
+// column term lies in [-4160, T 64 M^2 = 516128]; a row start above 2^30
+// (a huge E) is clamped to 2^30, live against every bound; sums stay within
+// 64 * 127^2 of the start, far from int32 overflow.
+
+// bits of max |x_i - r_i| over the first kPartialDims dimensions of the
+// rows (fp32 difference, within 2^-24 of exact), atomically maxed into *mx
+__global__ __launch_bounds__(256) void k_maxabs8(const float4 *__restrict__ xs, uint64_t n,
+                                                 const float4 *__restrict__ ref, unsigned int *__restrict__ mx)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    float m = 0.f;
+    if (i < n) {
+#pragma unroll 4
+        for (int b = 0; b < kPartialDims / 4; ++b) {
+            const float4 x = xs[(uint64_t)b * n + i], r = ref[b];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(x.x - r.x), fabsf(x.y - r.y)), fmaxf(fabsf(x.z - r.z), fabsf(x.w - r.w))));
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if ((threadIdx.x & 63) == 0 && m > 0.f) atomicMax(mx, __float_as_uint(m));
+}
+
+// int8 operands of one point set: part p (dimensions 16 p .. 16 p + 15, slab
+// p / 2 of 32, half p % 2) of row i at P[p * ps + i], one byte a dimension;
+// the row start (rows) and the column bound (cols, with bound[n] = INT_MAX
+// past the end) as derived above
+__global__ __launch_bounds__(256) void k_prep8(const float4 *__restrict__ xs, uint64_t n,
+                                               const float4 *__restrict__ ref, double S, double E,
+                                               uint4 *__restrict__ P, uint64_t ps, int *__restrict__ start,
+                                               int *__restrict__ bound)
+{
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) {
+        if (i == n && bound) bound[n] = INT_MAX;
+        return;
+    }
+    double N = 0.0, A = 0.0;
+#pragma unroll 1
+    for (int p = 0; p < kPartialDims / 16; ++p) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 x = xs[(uint64_t)(4 * p + j) * n + i], r = ref[4 * p + j];
+            const double dv[4] = {(double)x.x - (double)r.x, (double)x.y - (double)r.y, (double)x.z - (double)r.z,
+                                  (double)x.w - (double)r.w};
+            uint32_t word = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                N = fma(dv[c], dv[c], N);
+                const double qv = fmin(fmax(rint(dv[c] * S), -127.0), 127.0);
+                A += fabs(qv);
+                word |= ((uint32_t)(int)qv & 0xffu) << (8 * c);
+            }
+            w[j] = word;
+        }
+        P[(uint64_t)p * ps + i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    const double D = (0.5 + 0x1p-30) / S, T = 0.5 * S * S;
+    const double base = N - 2.0 * D * A / S - 64.0 * D * D;
+    const double mag = N + 2.0 * D * A / S + 64.0 * D * D;  // bounds the terms' rounding
+    if (bound) bound[i] = (int)fmin(floor(T * base - T * mag * 0x1p-40 - 2.0), 0x1p29);
+    if (start) {
+        const double v = T * (base - E) - T * (mag + E) * 0x1p-40 - 2.0;
+        start[i] = v > -0x1p30 ? -(int)floor(v) : (1 << 30);  // (NaN from E = inf: 2^30)
+    }
+}
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx16 __attribute__((ext_vector_type(16)));
+
 // PP: parts per slab of the prepared arrays (2: high halves only, 4: high
-// and low); the filter reads the high ones
-template <int PP>
+// and low); the fp16 form reads the high ones.  I8: the integer form of the
+// same test (k_prep8's operands, row starts and column bounds; two int8
+// MFMAs of 32 dimensions per block, exact int32 sums).
+template <int PP, bool I8>
 __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
 {
+    using Acc = std::conditional_t<I8, intx16, floatx16>;
+    // parts of a candidate in LDS: fp16 high halves of 4 slabs of 16
+    // dimensions, or int8 values of 2 slabs of 32, two parts a slab
+    constexpr int kParts = I8 ? 4 : 2 * kSlabsF;
+    constexpr int kSl = kParts / 2;
     uint32_t rk, seg;
     work_item(blockIdx.x, a.ntiles, a.nseg, &rk, &seg);
     const uint32_t t = a.order[a.ord0 + rk];
@@ -543,9 +640,9 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
 
     // operand buffers: part p (= 2 slab + half) of candidate c at [p][c];
     // column bounds at [copy][c] (waves 0-1 and 2-3 each load a copy)
-    __shared__ __align__(16) uint4 LB0[2 * kSlabsF * kStepF], LB1[2 * kSlabsF * kStepF];
-    __shared__ __align__(16) float LX0[2 * kStepF], LX1[2 * kStepF];
-    __shared__ __align__(16) float LQOUTP[kRowsG];
+    __shared__ __align__(16) uint4 LB0[kParts * kStepF], LB1[kParts * kStepF];
+    __shared__ __align__(16) float LX0[2 * kStepF], LX1[2 * kStepF];  // int bounds in the int8 form
+    __shared__ __align__(16) float LQOUTP[kRowsG];                     // int starts in the int8 form
     __shared__ uint32_t LPREF[kMaxRanges + 1], LSTART[kMaxRanges];
 
     const int tid = threadIdx.x;
@@ -556,17 +653,23 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     if (tid < kMaxRanges) LSTART[tid] = a.rstart[(uint64_t)A * kMaxRanges + tid];
     if (tid < kRowsG) {
         const bool valid = (uint32_t)tid < nrows;
-        const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
-        LQOUTP[tid] = valid ? filter_row_start(a.thi - a.kmf * nqp + a.tabs) : -INFINITY;
+        if constexpr (I8) {
+            // an invalid row starts far below every bound (-2^30 + 2^20 < -4160)
+            LQOUTP[tid] = __builtin_bit_cast(float, valid ? a.qs8[row0 + tid] : -(1 << 30));
+        } else {
+            const float nqp = valid ? a.np16q[row0 + tid] : 0.f;
+            LQOUTP[tid] = valid ? filter_row_start(a.thi - a.kmf * nqp + a.tabs) : -INFINITY;
+        }
     }
     // the wave's query fragments: row 32 wave + l % 32, half l / 32 of each slab
     const uint32_t nrow_w = (uint32_t)(wave * 32) < nrows ? min(32u, nrows - (uint32_t)(wave * 32)) : 0u;
     const uint32_t q = row0 + min((uint32_t)(wave * 32 + col), nrows - 1);
-    half8 af[kSlabsF];
+    using Frag = std::conditional_t<I8, intx4, half8>;
+    Frag af[kSl];
 #pragma unroll
-    for (int s = 0; s < kSlabsF; ++s) {
-        const uint4 v = a.p16q[((uint64_t)s * PP + hi) * psq + q];
-        af[s] = *(const half8 *)&v;
+    for (int s = 0; s < kSl; ++s) {
+        const uint4 v = I8 ? a.p8q[((uint64_t)s * 2 + hi) * a.ps8q + q] : a.p16q[((uint64_t)s * PP + hi) * psq + q];
+        af[s] = __builtin_bit_cast(Frag, v);
     }
     const uint64_t mbase = a.toff[t] - a.wbase;
     const uint32_t W = tl.words;
@@ -574,8 +677,8 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     __syncthreads();
 
     // loader: lane l of wave w stages candidate lc = 64 (w % 2) + l of the
-    // step, parts 4 (w / 2) .. + 3
-    const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)wave >> 1) * 4;
+    // step, parts kSl (w / 2) .. + kSl - 1
+    const uint32_t lc = (uint32_t)tid & (kStepF - 1), lp0 = ((uint32_t)wave >> 1) * kSl;
     const uint32_t lbase = (uint32_t)(wave & 1) * 64;  // the wave's first candidate
     // the range of the candidate list holding the step's first position,
     // kept in scalar registers: [r_lo, r_hi) of the list are points r_st ..
@@ -607,16 +710,17 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     auto issue = [&](uint32_t st, uint4 *lb, float *lx) __attribute__((always_inline)) {
         const uint32_t ci = cand_index(st < nsteps ? st : nsteps - 1);
         const uint32_t cx = c_begin + st * kStepF + lc < c_end ? ci : (uint32_t)a.n;
-        const uint4 *pc = a.p16 + ci;
+        const uint4 *pc = (I8 ? a.p8 : a.p16) + ci;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kSl; ++k) {
             const uint32_t p = lp0 + (uint32_t)k;
-            __builtin_amdgcn_global_load_lds((const void *)(pc + ((uint64_t)(p >> 1) * PP + (p & 1)) * ps),
+            const uint64_t off = I8 ? (uint64_t)p * a.ps8 : ((uint64_t)(p >> 1) * PP + (p & 1)) * ps;
+            __builtin_amdgcn_global_load_lds((const void *)(pc + off),
                                              (__attribute__((address_space(3))) void *)(lb + p * kStepF + lbase),
                                              16, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds((const void *)(a.xb16 + cx),
-                                         (__attribute__((address_space(3))) void *)(lx + (wave >> 1) * kStepF + lbase),
+        const void *xsrc = I8 ? (const void *)(a.xb8 + cx) : (const void *)(a.xb16 + cx);
+        __builtin_amdgcn_global_load_lds(xsrc, (__attribute__((address_space(3))) void *)(lx + (wave >> 1) * kStepF + lbase),
                                          4, 0, 0);
     };
     unsigned long long npart = 0;
@@ -629,16 +733,23 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
     __syncthreads();
     // the accumulators' start: register v of lane l holds row 8 (v / 4) +
     // v % 4 + 4 (l / 32) of the wave's block
-    floatx16 crow;
+    Acc crow;
     {
         const float4 *c4 = (const float4 *)LQOUTP + wave * 8 + hi;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const float4 c = c4[g * 2];
-            crow[4 * g + 0] = c.x;
-            crow[4 * g + 1] = c.y;
-            crow[4 * g + 2] = c.z;
-            crow[4 * g + 3] = c.w;
+            if constexpr (I8) {
+                crow[4 * g + 0] = __builtin_bit_cast(int, c.x);
+                crow[4 * g + 1] = __builtin_bit_cast(int, c.y);
+                crow[4 * g + 2] = __builtin_bit_cast(int, c.z);
+                crow[4 * g + 3] = __builtin_bit_cast(int, c.w);
+            } else {
+                crow[4 * g + 0] = c.x;
+                crow[4 * g + 1] = c.y;
+                crow[4 * g + 2] = c.z;
+                crow[4 * g + 3] = c.w;
+            }
         }
     }
     // step st reads (lb, lx) while step st + 1's operands load into (nb, nx)
@@ -646,13 +757,16 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
                     __attribute__((always_inline)) {
         issue(st + 1, nb, nx);
         if (nrow_w != 0) {
-            floatx16 acc[4];
+            Acc acc[4];
 #pragma unroll
-            for (int s = 0; s < kSlabsF; ++s) {
+            for (int s = 0; s < kSl; ++s) {
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const half8 bf = *(const half8 *)&lb[(s * 2 + hi) * kStepF + tt * 32 + col];
-                    acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s], bf, s == 0 ? crow : acc[tt], 0, 0, 0);
+                    const Frag bf = *(const Frag *)&lb[(s * 2 + hi) * kStepF + tt * 32 + col];
+                    if constexpr (I8)
+                        acc[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[s], bf, s == 0 ? crow : acc[tt], 0, 0, 0);
+                    else
+                        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s], bf, s == 0 ? crow : acc[tt], 0, 0, 0);
                 }
             }
             // partial test of the wave's four blocks: a lane's 16 registers
@@ -661,13 +775,22 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
             uint32_t live = 0;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
-                const float xb = lx[tt * 32 + col];
-                const floatx16 v = acc[tt];
-                const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
-                const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
-                const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
-                const float m = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15]));
-                if (__ballot(m >= xb) != 0) live |= 1u << tt;
+                const Acc v = acc[tt];
+                bool hit;
+                if constexpr (I8) {
+                    const int xb = __builtin_bit_cast(int, lx[tt * 32 + col]);
+                    const int m0 = max(max(v[0], v[1]), v[2]), m1 = max(max(v[3], v[4]), v[5]);
+                    const int m2 = max(max(v[6], v[7]), v[8]), m3 = max(max(v[9], v[10]), v[11]);
+                    const int m4 = max(max(v[12], v[13]), v[14]);
+                    hit = max(max(max(m0, m1), m2), max(max(m3, m4), v[15])) >= xb;
+                } else {
+                    const float xb = lx[tt * 32 + col];
+                    const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+                    const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+                    const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+                    hit = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15])) >= xb;
+                }
+                if (__ballot(hit) != 0) live |= 1u << tt;
             }
             // comparisons settled here: the step's valid columns less those
             // of its live blocks
@@ -1084,6 +1207,25 @@ hipError_t prepare_refine_g16(bool hh)
 
 hipError_t prepare_filter16() { return hipSuccess; }
 
+hipError_t launch_maxabs8(const float4 *xs, uint64_t n, const float4 *ref, unsigned int *mx, hipStream_t st)
+{
+    if (n == 0) return hipSuccess;
+    const uint64_t grid = (n + 255) / 256;
+    if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_maxabs8, dim3((unsigned)grid), dim3(256), 0, st, xs, n, ref, mx);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep8(const float4 *xs, uint64_t n, const float4 *ref, double S, double E, uint4 *P, uint64_t ps,
+                        int *start, int *bound, hipStream_t st)
+{
+    if (ps < n || !(S > 0.0)) return hipErrorInvalidValue;
+    const uint64_t grid = (n + 1 + 255) / 256;
+    if (grid > 0x7fffffffull) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(k_prep8, dim3((unsigned)grid), dim3(256), 0, st, xs, n, ref, S, E, P, ps, start, bound);
+    return hipGetLastError();
+}
+
 hipError_t launch_col_bounds16(const float *np16, uint64_t n, float kmf, float *xb, hipStream_t st)
 {
     const uint64_t grid = (n + 1 + 255) / 256;
@@ -1101,8 +1243,10 @@ hipError_t launch_filter16(const RefineArgs &a, bool hh, hipStream_t s)
     if (blocks > 0x7fffffffull) return hipErrorInvalidConfiguration;
     RefineArgs args = a;
     void *params[] = {&args};
-    return hipLaunchKernel(hh ? (const void *)k_filter16<2> : (const void *)k_filter16<4>, dim3((unsigned)blocks),
-                           dim3(256), params, 0, s);
+    const bool i8 = a.p8 && a.p8q && a.xb8 && a.qs8;
+    const void *k = i8 ? (const void *)k_filter16<2, true>
+                       : hh ? (const void *)k_filter16<2, false> : (const void *)k_filter16<4, false>;
+    return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), params, 0, s);
 }
 
 hipError_t launch_handon_keys(const uint4 *dl, uint64_t dcap, const uint64_t *pref, uint64_t total, int qbits,

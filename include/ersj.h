@@ -109,6 +109,12 @@ typedef struct ersj_options {
                                    a third of the matrix work and half the operand traffic, with a
                                    band about 4.5 times as wide (more pairs re-checked in binary64);
                                    0 = 1.  Same result. */
+    int32_t filter_bits;        /* operands of the 64-dimension filter above 64 dimensions: 8 = int8
+                                   values of the centred, scaled coordinates (two int8 MFMAs of 32
+                                   dimensions a 32 x 32 block, exact integer sums, a wider but
+                                   rigorous bound); 16 = the fp16 high halves (four MFMAs a block);
+                                   0 = 8 (16 where the coordinates' range is not finite).  Same
+                                   result. */
 } ersj_options;
 
 typedef struct ersj_stats {
@@ -142,6 +148,7 @@ typedef struct ersj_stats {
     uint64_t partial_candidates; /* the same, over the launches timed in refine_ms */
     int32_t last_filtered;       /* 1: the last fill_pass refined with the 64-dimension filter and the
                                     block kernel (above 64 dimensions), 0: with one kernel */
+    int32_t filter_bits;         /* operands of that filter: 8 (int8), 16 (fp16); 0: no filter */
 } ersj_stats;
 
 /* Fill *opt with the defaults (struct_size set). */

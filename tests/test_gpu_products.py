@@ -32,8 +32,8 @@ def _gpu():
     ersj.lib()
 
 
-def _join_stats(X, eps, products):
-    opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products)
+def _join_stats(X, eps, products, bits=0):
+    opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, mfma_products=products, filter_bits=bits)
     h = ersj.build_index(torch.from_numpy(X).cuda(), eps, opts)
     ersj.count_pass(h)
     nb = ersj.plan_batches(h, 0)
@@ -43,9 +43,10 @@ def _join_stats(X, eps, products):
     return ersj.pairs_to_numpy(parts), st
 
 
+@pytest.mark.parametrize("bits", [8, 16])
 @pytest.mark.parametrize("name,n,d", [("c5", 6000, None), ("rand", 3001, 129), ("rand", 700, 68),
                                       ("rand", 1500, 200)])
-def test_both_forms_match_the_oracle(name, n, d):
+def test_both_forms_match_the_oracle(name, n, d, bits):
     if name == "rand":
         rng = np.random.default_rng(n + d)
         X = rng.random((n, d), dtype=np.float32)
@@ -57,8 +58,8 @@ def test_both_forms_match_the_oracle(name, n, d):
     band = {}
     for products in (1, 3):
         say(f"[gpu] products={products} {name} n={n} d={X.shape[1]} eps={eps!r}")
-        got, st = _join_stats(X, eps, products)
-        assert st["mfma_products"] == products
+        got, st = _join_stats(X, eps, products, bits)
+        assert st["mfma_products"] == products and st["filter_bits"] == bits
         assert_same_pairs(X, eps, got, want, f"{name} products={products}")
         band[products] = st["last_boundary_pairs"]
         say(f"[gpu] {name} products={products}: {st['last_partial']} comparisons settled from the first "
@@ -108,8 +109,9 @@ def test_c5_shape_semijoin_queries_from_the_same_centres():
         assert np.array_equal(got, want), products
 
 
+@pytest.mark.parametrize("bits", [8, 16])
 @pytest.mark.parametrize("products", [1, 3])
-def test_partial_test_with_differences_in_the_leading_dimensions(products):
+def test_partial_test_with_differences_in_the_leading_dimensions(products, bits):
     # dimensions 0..63 spread widely (they lead the variance order), the rest
     # nearly constant; each pair differs in dimensions 0..63 only, so its
     # distance over them is its full distance, placed around eps^2 at
@@ -131,11 +133,11 @@ def test_partial_test_with_differences_in_the_leading_dimensions(products):
                 rows.append(np.stack([q, q + v]))
     X = np.concatenate(rows).astype(np.float32)
     want = oracle.selfjoin_pairs(X, eps)
-    got, st = _join_stats(X, eps, products)
-    say(f"[gpu] leading-dimension pairs products={products}: {len(got)} pairs, "
+    got, st = _join_stats(X, eps, products, bits)
+    say(f"[gpu] leading-dimension pairs products={products} filter bits={bits}: {len(got)} pairs, "
         f"{st['last_partial']} comparisons settled from the first 64 dimensions")
-    assert st["last_partial"] > 0
-    assert_same_pairs(X, eps, got, want, f"leading-dimension pairs products={products}")
+    assert st["last_partial"] > 0 and st["filter_bits"] == bits
+    assert_same_pairs(X, eps, got, want, f"leading-dimension pairs products={products} bits={bits}")
 
 
 def test_dense_steps_continue_in_place():
@@ -220,3 +222,63 @@ def test_high_halves_that_all_round_one_way(products, tiled):
         f"filtered={st['last_filtered']}, band pairs {st['last_boundary_pairs']}")
     assert st["last_filtered"] == (0 if tiled else 1)
     assert np.array_equal(got, want)
+
+
+def _int8_coherent_case(f, rhos, seed=5):
+    # The int8 filter centres on the mean (exactly 0: the points are
+    # mirrored) and scales by S = 127 / (M (1 + 2^-20)), M the largest
+    # coordinate of the first 64 dimensions.  Every such coordinate here is
+    # (a_i + f) / S with a_i an integer: each rounds to a_i, off by f / S
+    # in the same direction in all 64 dimensions of both rows of a pair, so
+    # the dropped parts add up and the test's bound is nearly tight.  One
+    # partner per query, differing in those dimensions by integer steps j_i,
+    # at S^2 |x - q|^2 = sum j_i^2 around E S^2 (1 + rho), every pair of a case
+    # at one rho, so that a block holding a pair just inside the radius holds
+    # no other kind; a semi-join, so no self pair keeps a block live.  Pairs
+    # of different queries lie about 1.8 E apart, mirror images far apart.
+    # Dimensions 64..99 are 0.
+    rng = np.random.default_rng(seed)
+    d, M = 100, np.float32(0.4375)
+    S = 127.0 / (float(M) * (1.0 + 2.0 ** -20))
+    eps = 0.5
+    E = eps * eps
+    Q, X = [], []
+    for rho in rhos:
+        for _ in range(40):
+            a = rng.integers(10, 50, 64)  # one sign: the rounding errors' products add up too
+            j = rng.normal(0.0, 1.0, 64)
+            j = np.round(j * math.sqrt(E * S * S * (1 + rho) / np.sum(j * j))).astype(np.int64)
+            j = np.clip(j, -100 - a, 110 - a)
+            q, x = np.zeros(d), np.zeros(d)
+            q[:64] = (a + f) / S
+            x[:64] = (a + j + f) / S
+            Q.append(q)
+            X.append(x)
+    edge = np.zeros(d)
+    edge[0] = M  # sets the scale
+    Q, X = np.array(Q + [edge]), np.array(X + [edge])
+    Q = np.concatenate([Q, -Q]).astype(np.float32)
+    X = np.concatenate([X, -X]).astype(np.float32)
+    assert np.abs(Q).max() == M and np.abs(X).max() == M
+    return Q, X, eps
+
+
+@pytest.mark.parametrize("rho", [-0.05, -0.01, -0.002, 0.3])
+@pytest.mark.parametrize("f", [0.499, -0.499, 0.25])
+def test_int8_filter_with_rounding_all_one_way(f, rho):
+    Q, X, eps = _int8_coherent_case(f, (rho,))
+    want = np.sort(keys_of(oracle.semijoin_pairs(Q, X, eps)))
+    assert want.size >= (0 if rho > 0 else 40)
+    for bits in (8, 16):
+        opts = ersj.default_options(refine_kernel=ersj.REFINE_MFMA16, filter_bits=bits)
+        parts, h = ersj.semi_join(torch.from_numpy(Q).cuda(), torch.from_numpy(X).cuda(), eps, 0, opts,
+                                  return_index=True)
+        st = ersj.get_stats(h)
+        h.free()
+        got = np.sort(keys_of(ersj.pairs_to_numpy(parts)))
+        say(f"[gpu] int8 rounding one way f={f} bits={bits}: {got.size} pairs (oracle {want.size}), "
+            f"filtered={st['last_filtered']}, settled early {st['last_partial']}")
+        assert st["filter_bits"] == bits and st["last_filtered"] == 1
+        if rho > 0:
+            assert st["last_partial"] > 0  # the bound settles blocks here
+        assert np.array_equal(got, want), (f, rho, bits)
