@@ -1104,8 +1104,11 @@ __global__ __launch_bounds__(256, NS > 16 ? 2 : 3) void k_refine_g16_runs(Refine
     uint32_t qkey = 0xffffffffu;
     for (uint64_t r0 = x0 + gw * kRunLen; r0 < x1; r0 += nw * kRunLen) {
         const uint64_t r1 = r0 + kRunLen < x1 ? r0 + kRunLen : x1;
+        // the next entry is fetched while this one is refined
+        uint4 nent = a.dlist[a.dorder[r0]];
         for (uint64_t e = r0; e < r1; ++e) {
-            const uint4 ent = a.dlist[a.dorder[e]];
+            const uint4 ent = nent;
+            if (e + 1 < r1) nent = a.dlist[a.dorder[e + 1]];
             const uint32_t t = ent.x, rb = ent.y & 3u, c0 = (ent.y >> 2) << 5;
             const Tile tl = a.tiles[t];
             const uint32_t nrows = min((uint32_t)kTileRows, tl.nrows);
@@ -1158,15 +1161,22 @@ __global__ __launch_bounds__(256, NS > 16 ? 2 : 3) void k_refine_g16_runs(Refine
             auto cload = [&](int sl) __attribute__((always_inline)) {
                 return pc[(uint64_t)(sl < nsl ? sl : nsl - 1) * 2 * n];
             };
-            uint4 ring[3];
-            ring[0] = cload(0);
-            ring[1] = cload(1);
+            // candidate fragments through a ring, kAhead slabs ahead (as deep
+            // as the registers of the kernel's occupancy allow: a block's
+            // loads come mostly from beyond L2, and only two or three waves
+            // per SIMD hide their latency)
+            constexpr int kAhead = NS == 24 ? 11 : NS == 16 ? 6 : 4;
+            uint4 ring[kAhead + 1];
+            static_for(std::make_integer_sequence<int, kAhead>{}, [&](auto S) {
+                constexpr int sl = decltype(S)::value;
+                ring[sl] = cload(sl);
+            });
             floatx16 acc = {};
             static_for(std::make_integer_sequence<int, NS>{}, [&](auto S) {
                 constexpr int sl = decltype(S)::value;
-                ring[(sl + 2) % 3] = cload(sl + 2);
+                if constexpr (sl + kAhead < NS) ring[(sl + kAhead) % (kAhead + 1)] = cload(sl + kAhead);
                 if (sl < nsl)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[sl], *(const half8 *)&ring[sl % 3], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[sl], *(const half8 *)&ring[sl % (kAhead + 1)], acc, 0, 0, 0);
             });
             g16_block_finish(a, acc, t, tl, rb, c0, r, vr, vc, ci, nx, LQI[wave], LQO[wave]);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
