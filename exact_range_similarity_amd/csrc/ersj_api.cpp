@@ -1380,9 +1380,9 @@ int refine_into(ersj_index *h, int32_t b, hipStream_t s, FillBufs &fb, uint64_t 
                     HIPC(hipMemcpyAsync(dpref, pref.data(), sizeof(uint64_t) * pref.size(), hipMemcpyHostToDevice, s),
                          "copy");
                     // key bits: the query block (tile << 2 | block) below
-                    // the 1024-point group of the first candidate
+                    // the 2^kHandonGroupBits-point group of the first candidate
                     const int qbits = std::max(2, ceil_log2((uint64_t)h->T * 4));
-                    const uint32_t gend = (uint32_t)((uint64_t)h->n >> 10) + 1;
+                    const uint32_t gend = (uint32_t)((uint64_t)h->n >> kHandonGroupBits) + 1;
                     const int kbits = qbits + ceil_log2((uint64_t)gend + 1);
                     HIPC(launch_handon_keys(a.dlist, a.dcap, dpref, total, qbits, gend, k0, v0, s), "block order keys");
                     HIPC(radix_sort(k0, v0, k1, v1, (int64_t)total, kbits, hist, sc, s), "block order sort");

@@ -438,6 +438,9 @@ hipError_t launch_refine_m16(const RefineArgs &a, hipStream_t s);
 // kPartialDims dimensions: the squared distance over a subset of the
 // dimensions bounds the full one from below
 constexpr int kPartialDims = 64;
+// the run kernel's order: handed-on blocks grouped by the 2^kHandonGroupBits
+// consecutive points holding their first candidate, then by query block
+constexpr int kHandonGroupBits = 12;
 inline int g16_stages(int nb, bool hh)
 {
     const int ns = (nb + 3) / 4;

@@ -855,12 +855,12 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
 
 // Sort keys of the handed-on blocks: entry e of the sub-lists taken in
 // order (pref: exclusive prefix of their kept counts, kBandLists + 1
-// entries) gets key = (the group of 1024 points holding its block's first
-// candidate, gend when the candidates are not consecutive points) << qbits
-// | (tile << 2 | query block), and value = its index in dlist.  In
-// that order a group's candidate blocks (768 KB of operands at d = 384)
-// serve every query block live against them while that query block's
-// entries are consecutive.
+// entries) gets key = (the group of 2^kHandonGroupBits points holding its
+// block's first candidate, gend when the candidates are not consecutive
+// points) << qbits | (tile << 2 | query block), and value = its index in
+// dlist.  In that order a group's candidate blocks (3 MB of operands at
+// d = 384, within one XCD's L2) serve every query block live against them
+// while that query block's entries are consecutive.
 __global__ __launch_bounds__(256) void k_handon_keys(const uint4 *__restrict__ dl, uint64_t dcap,
                                                      const uint64_t *__restrict__ pref, uint64_t total, int qbits,
                                                      uint32_t gend, uint64_t *__restrict__ keys,
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(256) void k_handon_keys(const uint4 *__restrict__ d
     }
     const uint64_t idx = (uint64_t)lo * dcap + (e - pref[lo]);
     const uint4 ent = dl[idx];
-    const uint32_t grp = ent.z == 0xffffffffu ? gend : ent.z >> 10;
+    const uint32_t grp = ent.z == 0xffffffffu ? gend : ent.z >> kHandonGroupBits;
     keys[e] = ((uint64_t)grp << qbits) | ((uint64_t)ent.x << 2 | (ent.y & 3u));
     vals[e] = (uint32_t)idx;
 }
@@ -1141,13 +1141,9 @@ __global__ __launch_bounds__(256, NS > 16 ? 2 : 3) void k_refine_g16_runs(Refine
                 // a new query block: its fragments and row thresholds
                 qkey = key;
                 const uint4 *pq = a.p16q + (uint64_t)hi * nqr + q;
-                // (non-temporal: a query block is read once per run and
-                // would only push candidate operands out of L2)
                 static_for(std::make_integer_sequence<int, NS>{}, [&](auto S) {
                     constexpr int sl = decltype(S)::value;
-                    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-                    const u32x4 v = __builtin_nontemporal_load(
-                        (const u32x4 *)(pq + (uint64_t)(sl < nsl ? sl : nsl - 1) * 2 * nqr));
+                    const uint4 v = pq[(uint64_t)(sl < nsl ? sl : nsl - 1) * 2 * nqr];
                     qf[sl] = *(const half8 *)&v;
                 });
                 if (lane < 32) {
