@@ -282,3 +282,36 @@ def test_int8_filter_with_rounding_all_one_way(f, rho):
         if rho > 0:
             assert st["last_partial"] > 0  # the bound settles blocks here
         assert np.array_equal(got, want), (f, rho, bits)
+
+
+@pytest.mark.parametrize("case", ["eps0_duplicates", "eps_inf", "one_far_outlier", "constant_leading_dims"])
+def test_int8_filter_degenerate_inputs(case):
+    # eps = 0 with repeated rows (only exact duplicates pair up), eps = inf
+    # (every row start clamped: nothing settled), one row far from all others
+    # (it sets the int8 scale, so the others' integers are small and the
+    # bound wide), and 70 of 80 dimensions constant (the variance order puts
+    # the 10 that vary first, so the filter's 64 dimensions are mostly
+    # zero after centring); both filter forms against the oracle
+    rng = np.random.default_rng(len(case))
+    d = 80
+    if case == "eps0_duplicates":
+        base = rng.random((300, d), dtype=np.float32)
+        X = base[rng.integers(0, 300, 900)]
+        eps = 0.0
+    elif case == "eps_inf":
+        X = rng.random((400, d), dtype=np.float32)
+        eps = math.inf
+    elif case == "one_far_outlier":
+        X = rng.random((2000, d), dtype=np.float32)
+        X[17] += np.float32(500.0)
+        eps = 0.33 * math.sqrt(d / 6.0)
+    else:
+        X = np.full((1500, d), np.float32(0.25))
+        X[:, 70:] = rng.random((1500, 10), dtype=np.float32)
+        eps = 0.4
+    want = oracle.selfjoin_pairs(X, eps)
+    for bits in (8, 16):
+        got, st = _join_stats(X, eps, 0, bits)
+        say(f"[gpu] int8 degenerate {case} bits={bits}: {len(got)} pairs (oracle {len(want)}), "
+            f"filter bits used {st['filter_bits']}, settled early {st['last_partial']}")
+        assert_same_pairs(X, eps, got, want, f"{case} bits={bits}")
