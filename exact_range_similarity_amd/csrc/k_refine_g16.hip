@@ -772,11 +772,11 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
             // partial test of the wave's four blocks: a lane's 16 registers
             // share its column, so the block is live iff some lane's largest
             // register reaches the lane's column bound
-            uint32_t live = 0;
+            bool hits[4];
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 const Acc v = acc[tt];
-                bool hit;
+                bool &hit = hits[tt];
                 if constexpr (I8) {
                     const int xb = __builtin_bit_cast(int, lx[tt * 32 + col]);
                     const int m0 = max(max(v[0], v[1]), v[2]), m1 = max(max(v[3], v[4]), v[5]);
@@ -790,7 +790,13 @@ __global__ __launch_bounds__(256, 4) void k_filter16(RefineArgs a)
                     const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
                     hit = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15])) >= xb;
                 }
-                if (__ballot(hit) != 0) live |= 1u << tt;
+            }
+            // one ballot settles the common step with no live block
+            uint32_t live = 0;
+            if (__ballot(hits[0] || hits[1] || hits[2] || hits[3]) != 0) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+                    if (__ballot(hits[tt]) != 0) live |= 1u << tt;
             }
             // comparisons settled here: the step's valid columns less those
             // of its live blocks
